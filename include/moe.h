@@ -1,0 +1,262 @@
+/*
+ * moe.h — C-ABI of the deterministic MoE layer on one MI355X (gfx950).
+ *
+ * The layer, as the pages state the problem: a router sends each token to a
+ * selection of experts, each a small feed-forward net with up, gate and down
+ * projections (sebask.de, "Mixture-of-Kittens: Cursors Open-Source-Ansatz für
+ * effizientes MoE-Training auf NVL72", introduction), the experts are SwiGLU
+ * (stamatios.com, "Cursor abre código de megakernel MoE para GPUs NVL72",
+ * § Outras características); tokens are dispatched to their experts and the
+ * results combined back (sebask.de, § Das Kernproblem); one schedule table, built
+ * on the GPU without sorting, serves all four movement operations (forward
+ * dispatch and combine, backward reverse-combine and reverse-dispatch)
+ * (sebask.de, § Push oder Pull; stamatios.com, § Escolha da direção de
+ * comunicação); the operation order is fixed so that outputs are bitwise
+ * reproducible (sebask.de, § Determinismus und MXFP8-Unterstützung;
+ * stamatios.com, § Outras características).
+ *
+ * Conventions for every entry point
+ *  - Every array pointer is a DEVICE pointer owned by the caller.  The library
+ *    allocates and frees nothing, keeps no state between calls (apart from
+ *    the optional per-thread timing trace below), never synchronises the host
+ *    and enqueues all work on `stream` (NULL = the null stream).  Outputs are valid once the caller has synchronised the stream.
+ *  - Matrices are row-major and contiguous.  Per-expert weights are stacked
+ *    [E, out, in] (nn.Linear layout): w_gate, w_up [E, I, H]; w_down [E, H, I].
+ *    Shared-expert weights: s_gate, s_up [I_shared, H]; s_down [H, I_shared].
+ *  - "bf16" data is passed as `void*` (IEEE bfloat16, 2 bytes), fp32 as float*.
+ *  - Every pointer must be 16-byte aligned.
+ *  - Arguments are checked on the host before anything is enqueued; a failed
+ *    check returns a status other than MOE_OK and enqueues nothing.
+ *  - A data error that only the device can see (an expert id outside [0, E))
+ *    sets the plan's err_flag: the pair is left out of the plan (its pos is -1)
+ *    and the layer runs on the remaining pairs.
+ *  - Calls on one stream are ordered; concurrent calls sharing output or
+ *    workspace buffers on different streams race.
+ *  - Results are bitwise identical across repeated calls with the same inputs.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_E_NULL = 1,        /* a required pointer is NULL */
+  MOE_E_SHAPE = 2,       /* a size is out of range or not a supported multiple */
+  MOE_E_ALIGN = 3,       /* a pointer is not 16-byte aligned */
+  MOE_E_WORKSPACE = 4,   /* workspace smaller than moe_workspace_bytes() */
+  MOE_E_UNSUPPORTED = 5, /* valid request that this build does not implement */
+  MOE_E_HIP = 6          /* a HIP launch failed (hipGetLastError) */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2 } moe_dtype;
+
+/* T tokens, H hidden, I expert intermediate, E experts, k experts per token,
+ * I_shared intermediate of the always-on shared expert (0 = none),
+ * T_minibatch tokens per minibatch (0 = T).
+ * Limits: 0 <= T, T*k < 2^31, 1 <= E <= 1024, 1 <= k <= min(E, 32);
+ * H, I and I_shared multiples of 128 for the expert GEMMs. */
+typedef struct {
+  int32_t T, H, I, E, k;
+  int32_t I_shared;
+  int32_t T_minibatch;
+} moe_shape;
+
+/* Where each array of the schedule table sits inside the plan buffer (byte
+ * offsets from its start; all 256-byte aligned).  With R = T*k:
+ *   counts    int32 [E]      rows routed to each expert
+ *   offsets   int32 [E+1]    exclusive prefix of counts; offsets[E] = valid rows
+ *   src_token int32 [R]      pull list: token of row r (-1 past offsets[E])
+ *   src_slot  int32 [R]      pull list: slot j of row r (-1 past offsets[E])
+ *   pos       int32 [T, k]   inverse: row of pair (t, j), -1 if left out
+ *   tiles     int32 [max_tiles, 2]  (expert, first row) per tile_m rows of each
+ *                            expert, experts in id order; n_tiles entries valid
+ *   n_tiles   int32 [1]
+ *   err_flag  int32 [1]      1 if some expert id was outside [0, E), else 0
+ *   scratch   per-chunk histograms used while building the plan */
+typedef struct {
+  size_t counts, offsets, src_token, src_slot, pos, tiles, n_tiles, err_flag, scratch;
+  size_t total_bytes;
+  int32_t tile_m, max_tiles, chunk_pairs, n_chunks;
+} moe_plan_layout;
+
+const char* moe_status_str(moe_status s);
+
+/* Per-kernel timing.  While a trace is set on a host thread, every kernel that a
+ * call from that thread enqueues is bracketed by events[2 i] (before) and
+ * events[2 i + 1] (after), recorded on the call's stream, and names[i] is set to
+ * the kernel's name (a static string); i runs from the trace's `count`, which the
+ * library increments, up to `capacity` (later kernels are not recorded).  The
+ * caller creates the 2 * capacity events and reads them with hipEventElapsedTime
+ * after synchronising.  moe_trace_set(NULL) stops tracing.  This is the only
+ * state the library keeps, and it is per host thread. */
+typedef struct moe_trace {
+  hipEvent_t* events;
+  const char** names;
+  int32_t capacity;
+  int32_t count;
+} moe_trace;
+
+void moe_trace_set(moe_trace* trace);
+
+/* Layout and size of the plan buffer for `shape` (T, k, E are used). */
+moe_status moe_plan_layout_of(const moe_shape* shape, moe_plan_layout* out);
+size_t moe_plan_bytes(const moe_shape* shape);
+
+/* Bytes of activations the forward keeps for the backward (`saved`):
+ * Z = (A | B) bf16/f32 [T*k, 2I] (gate and up pre-activations of every routed
+ * row) followed by Zs [T, 2*I_shared] for the shared expert. */
+size_t moe_saved_bytes(const moe_shape* shape, moe_dtype dtype);
+
+/* Scratch bytes of moe_forward_* (backward = 0) or moe_backward_* (backward = 1). */
+size_t moe_workspace_bytes(const moe_shape* shape, moe_dtype dtype, int backward);
+
+/* ---------------------------------------------------------------- router */
+
+/* Router scores of the fp32 workload: logits [T, E] = x [T, H] * w_router[E, H]^T.
+ * (sebask.de, introduction: a router distributes tokens to experts.) */
+moe_status moe_router_logits_f32(const moe_shape* shape, const float* x, const float* w_router,
+                                 float* logits, hipStream_t stream);
+
+/* Top-k routing (sebask.de, introduction).  For each token the k experts with
+ * the largest logits are taken in order (logit descending, expert id ascending;
+ * -0.0 ties with +0.0), and topk_w holds the softmax of the k selected logits.
+ *   logits   fp32 [T, E]   in
+ *   topk_idx int32 [T, k]  out
+ *   topk_w   fp32 [T, k]   out
+ * NaN logits are not supported. */
+moe_status moe_route(const moe_shape* shape, const float* logits, int32_t* topk_idx,
+                     float* topk_w, hipStream_t stream);
+
+/* Gradient of the logits from the gradient of the gates: for selected experts
+ * d_logits[t, e_j] = w_j (d_w_j - sum_i w_i d_w_i), 0 elsewhere.
+ *   d_topk_w fp32 [T, k] in; d_logits fp32 [T, E] out (overwritten). */
+moe_status moe_route_backward(const moe_shape* shape, const int32_t* topk_idx,
+                              const float* topk_w, const float* d_topk_w, float* d_logits,
+                              hipStream_t stream);
+
+/* Backward of moe_router_logits_f32: dw_router [E, H] = d_logits^T x
+ * (overwritten) and dx [T, H] += d_logits w_router (accumulated in place). */
+moe_status moe_router_backward_f32(const moe_shape* shape, const float* x,
+                                   const float* w_router, const float* d_logits,
+                                   float* dw_router, float* dx, hipStream_t stream);
+
+/* ------------------------------------------------------------------ plan */
+
+/* Build the schedule table from the routing (sebask.de, § Das Scheduling: the
+ * pull schedule is a list of sources whose order follows from the routing and
+ * is built entirely on the GPU; stamatios.com, § Escolha da direção: built once,
+ * reused by the four operations, no sorting).  A counting sort: rows of expert
+ * e are its pairs in ascending t*k + j.  `plan` is a buffer of
+ * moe_plan_bytes(shape) bytes laid out as moe_plan_layout_of() reports.
+ *   topk_idx int32 [T, k] in. */
+moe_status moe_plan(const moe_shape* shape, const int32_t* topk_idx, void* plan,
+                    hipStream_t stream);
+
+/* ---------------------------------------------------- row movement (bf16/f32)
+ * Building blocks of the four movement operations, one GPU's share.  The
+ * layer entry points fuse dispatch and reverse-combine into the loaders of the
+ * expert GEMMs; these exported forms are the same gathers, materialised. */
+
+/* Dispatch, pull form (sebask.de, § Push oder Pull: dispatch pulls):
+ * X[r, :] = x[src_token[r], :] for the valid rows r < offsets[E].
+ * x [T, H] in; X [T*k, H] out (rows past offsets[E] untouched). */
+moe_status moe_dispatch_bf16(const moe_shape* shape, const void* plan, const void* x, void* X,
+                             hipStream_t stream);
+moe_status moe_dispatch_f32(const moe_shape* shape, const void* plan, const float* x, float* X,
+                            hipStream_t stream);
+
+/* Combine in token order (sebask.de, § Push oder Pull: combine keeps the token
+ * order; stamatios.com, § Outras características: fixed order):
+ * y[t, :] = round( sum_{j=0..k-1} topk_w[t, j] * Y[pos[t, j], :]  + shared_out[t, :] ),
+ * accumulated in fp32 from zero in ascending j, the shared term added last,
+ * one rounding to the output type.  Y [T*k, H] in; shared_out [T, H] in or NULL;
+ * y [T, H] out. */
+moe_status moe_combine_bf16(const moe_shape* shape, const void* plan, const void* Y,
+                            const float* topk_w, const void* shared_out, void* y,
+                            hipStream_t stream);
+moe_status moe_combine_f32(const moe_shape* shape, const void* plan, const float* Y,
+                           const float* topk_w, const float* shared_out, float* y,
+                           hipStream_t stream);
+
+/* Reverse-combine, pull form (stamatios.com, § Escolha da direção: pull for the
+ * backward reverse-combine): dYu[r, :] = dy[src_token[r], :].  Same gather as
+ * dispatch; dy [T, H] in, dYu [T*k, H] out. */
+moe_status moe_reverse_combine_bf16(const moe_shape* shape, const void* plan, const void* dy,
+                                    void* dYu, hipStream_t stream);
+
+/* Reverse-dispatch in fixed order (sebask.de, § Push oder Pull: the four
+ * operations): dx[t, :] = round( sum_{j ascending} dX[pos[t, j], :] + shared_dx[t, :] )
+ * in fp32.  dX [T*k, H] in; shared_dx [T, H] in or NULL; dx [T, H] out. */
+moe_status moe_reverse_dispatch_bf16(const moe_shape* shape, const void* plan, const void* dX,
+                                     const void* shared_dx, void* dx, hipStream_t stream);
+
+/* ------------------------------------------------------------ layer, bf16 */
+
+/* Forward of the expert part of the layer (sebask.de, introduction; stamatios.com,
+ * § Outras características: SwiGLU experts, shared expert):
+ *   per routed row r of expert e:  A = X_r W_g[e]^T, B = X_r W_u[e]^T,
+ *   h = silu(A) * B, Y_r = h W_d[e]^T, with X_r = x[src_token[r]] gathered in the
+ *   GEMM loader; shared expert S(x) = (silu(x S_g^T) * (x S_u^T)) S_d^T;
+ *   y = combine(Y) + S(x) as in moe_combine_bf16.
+ * bf16 operands, fp32 accumulation; A, B, h and Y are rounded to bf16, h is
+ * computed from the rounded A and B.
+ *   plan   from moe_plan on the same topk_idx
+ *   x [T, H], topk_w fp32 [T, k], weights as in the conventions
+ *   s_gate, s_up, s_down: NULL when shape->I_shared == 0
+ *   y [T, H] out; saved [moe_saved_bytes] out; ws [ws_bytes >= moe_workspace_bytes(.., 0)].
+ * T_minibatch must be 0 or T in this variant. */
+moe_status moe_forward_bf16(const moe_shape* shape, const void* plan, const void* x,
+                            const float* topk_w, const void* w_gate, const void* w_up,
+                            const void* w_down, const void* s_gate, const void* s_up,
+                            const void* s_down, void* y, void* saved, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/* Backward, the mirror of the forward (sebask.de, § Push oder Pull: reverse-combine
+ * and reverse-dispatch; stamatios.com, § Outras características: router-weight
+ * gradient fused into the SwiGLU backward):
+ *   dh' = dy[src_token[r]] W_d[e]       (reverse-combine gathered in the loader)
+ *   d_topk_w[t, j] = <dh'_r, h_r>       (= <dy_t, Y_r>), reduced in fixed order
+ *   dh = w dh'; dA = dh B silu'(A); dB = dh silu(A)   (h, A, B from `saved`)
+ *   dW_d[e] = sum_r dy_r (x) (w h)_r;  dW_g[e] = dA^T X_e;  dW_u[e] = dB^T X_e
+ *   dX_r = dA W_g[e] + dB W_u[e];  dx = reverse-dispatch(dX) + shared dx
+ * Outputs are overwritten: dx [T, H]; dw_* like the weights (experts with no
+ * rows get zeros); ds_* like the shared weights (NULL without a shared expert);
+ * d_topk_w fp32 [T, k] (0 for pairs left out of the plan).
+ * ws [ws_bytes >= moe_workspace_bytes(.., 1)]. */
+moe_status moe_backward_bf16(const moe_shape* shape, const void* plan, const void* x,
+                             const float* topk_w, const void* w_gate, const void* w_up,
+                             const void* w_down, const void* s_gate, const void* s_up,
+                             const void* s_down, const void* saved, const void* dy, void* dx,
+                             void* dw_gate, void* dw_up, void* dw_down, void* ds_gate,
+                             void* ds_up, void* ds_down, float* d_topk_w, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------- layer, fp32
+ * The same computation with fp32 operands and outputs (fp32 MFMA, fp32
+ * intermediates); arguments as the bf16 forms with float pointers. */
+moe_status moe_forward_f32(const moe_shape* shape, const void* plan, const float* x,
+                           const float* topk_w, const float* w_gate, const float* w_up,
+                           const float* w_down, const float* s_gate, const float* s_up,
+                           const float* s_down, float* y, void* saved, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+moe_status moe_backward_f32(const moe_shape* shape, const void* plan, const float* x,
+                            const float* topk_w, const float* w_gate, const float* w_up,
+                            const float* w_down, const float* s_gate, const float* s_up,
+                            const float* s_down, const void* saved, const float* dy, float* dx,
+                            float* dw_gate, float* dw_up, float* dw_down, float* ds_gate,
+                            float* ds_up, float* ds_down, float* d_topk_w, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,320 @@
+"""ctypes binding of libmoe.so (include/moe.h), same names as the C entry points.
+
+Marshalling only: torch tensors become device pointers, ``None`` becomes NULL and
+the current torch stream becomes the hipStream_t.  Every step of the layer runs in
+the library's HIP kernels; there is no Python or CPU fallback.  A missing library
+raises ``MoeLibraryMissing``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
+DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8}
+
+
+class MoeLibraryMissing(RuntimeError):
+    pass
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn}: status {code} ({msg})")
+        self.code = code
+
+
+class moe_shape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("I_shared", ctypes.c_int32),
+                ("T_minibatch", ctypes.c_int32)]
+
+
+class moe_plan_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("counts", "offsets", "src_token", "src_slot", "pos",
+                                                "tiles", "n_tiles", "err_flag", "scratch",
+                                                "total_bytes")] + \
+               [(n, ctypes.c_int32) for n in ("tile_m", "max_tiles", "chunk_pairs", "n_chunks")]
+
+
+_P = ctypes.c_void_p
+_S = ctypes.POINTER(moe_shape)
+_Z = ctypes.c_size_t
+_I = ctypes.c_int
+
+class moe_trace(ctypes.Structure):
+    _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p)),
+                ("names", ctypes.POINTER(ctypes.c_char_p)),
+                ("capacity", ctypes.c_int32), ("count", ctypes.c_int32)]
+
+
+# name -> (restype, argtypes)
+_SIGS = {
+    "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_trace_set": (None, [ctypes.POINTER(moe_trace)]),
+    "moe_plan_layout_of": (ctypes.c_int, [_S, ctypes.POINTER(moe_plan_layout)]),
+    "moe_plan_bytes": (_Z, [_S]),
+    "moe_saved_bytes": (_Z, [_S, _I]),
+    "moe_workspace_bytes": (_Z, [_S, _I, _I]),
+    "moe_router_logits_f32": (_I, [_S, _P, _P, _P, _P]),
+    "moe_route": (_I, [_S, _P, _P, _P, _P]),
+    "moe_route_backward": (_I, [_S, _P, _P, _P, _P, _P]),
+    "moe_router_backward_f32": (_I, [_S, _P, _P, _P, _P, _P, _P]),
+    "moe_plan": (_I, [_S, _P, _P, _P]),
+    "moe_dispatch_bf16": (_I, [_S, _P, _P, _P, _P]),
+    "moe_dispatch_f32": (_I, [_S, _P, _P, _P, _P]),
+    "moe_combine_bf16": (_I, [_S, _P, _P, _P, _P, _P, _P]),
+    "moe_combine_f32": (_I, [_S, _P, _P, _P, _P, _P, _P]),
+    "moe_reverse_combine_bf16": (_I, [_S, _P, _P, _P, _P]),
+    "moe_reverse_dispatch_bf16": (_I, [_S, _P, _P, _P, _P, _P]),
+    "moe_forward_bf16": (_I, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "moe_forward_f32": (_I, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "moe_backward_bf16": (_I, [_S] + [_P] * 20 + [_Z, _P]),
+    "moe_backward_f32": (_I, [_S] + [_P] * 20 + [_Z, _P]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MoeLibraryMissing(
+                f"{LIB_PATH} is missing: build it with `python -m mixture_experts_layer_plan_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def exported_names() -> list[str]:
+    return list(_SIGS)
+
+
+def shape(T, H, I, E, k, I_shared=0, T_minibatch=0) -> moe_shape:
+    return moe_shape(int(T), int(H), int(I), int(E), int(k), int(I_shared), int(T_minibatch))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _call(name, *args):
+    rc = getattr(lib(), name)(*args)
+    if rc != 0:
+        raise MoeError(name, rc, lib().moe_status_str(rc).decode())
+
+
+def moe_status_str(code: int) -> str:
+    return lib().moe_status_str(code).decode()
+
+
+def moe_plan_layout_of(s: moe_shape) -> moe_plan_layout:
+    out = moe_plan_layout()
+    _call("moe_plan_layout_of", ctypes.byref(s), ctypes.byref(out))
+    return out
+
+
+def moe_plan_bytes(s: moe_shape) -> int:
+    return lib().moe_plan_bytes(ctypes.byref(s))
+
+
+def moe_saved_bytes(s: moe_shape, dtype: int) -> int:
+    return lib().moe_saved_bytes(ctypes.byref(s), dtype)
+
+
+def moe_workspace_bytes(s: moe_shape, dtype: int, backward: bool) -> int:
+    return lib().moe_workspace_bytes(ctypes.byref(s), dtype, int(backward))
+
+
+def moe_router_logits_f32(s, x, w_router, logits, stream=None):
+    _call("moe_router_logits_f32", ctypes.byref(s), _ptr(x), _ptr(w_router), _ptr(logits),
+          _stream(stream))
+
+
+def moe_route(s, logits, topk_idx, topk_w, stream=None):
+    _call("moe_route", ctypes.byref(s), _ptr(logits), _ptr(topk_idx), _ptr(topk_w),
+          _stream(stream))
+
+
+def moe_route_backward(s, topk_idx, topk_w, d_topk_w, d_logits, stream=None):
+    _call("moe_route_backward", ctypes.byref(s), _ptr(topk_idx), _ptr(topk_w), _ptr(d_topk_w),
+          _ptr(d_logits), _stream(stream))
+
+
+def moe_router_backward_f32(s, x, w_router, d_logits, dw_router, dx, stream=None):
+    _call("moe_router_backward_f32", ctypes.byref(s), _ptr(x), _ptr(w_router), _ptr(d_logits),
+          _ptr(dw_router), _ptr(dx), _stream(stream))
+
+
+def moe_plan(s, topk_idx, plan, stream=None):
+    _call("moe_plan", ctypes.byref(s), _ptr(topk_idx), _ptr(plan), _stream(stream))
+
+
+def moe_dispatch_bf16(s, plan, x, X, stream=None):
+    _call("moe_dispatch_bf16", ctypes.byref(s), _ptr(plan), _ptr(x), _ptr(X), _stream(stream))
+
+
+def moe_dispatch_f32(s, plan, x, X, stream=None):
+    _call("moe_dispatch_f32", ctypes.byref(s), _ptr(plan), _ptr(x), _ptr(X), _stream(stream))
+
+
+def moe_combine_bf16(s, plan, Y, topk_w, shared_out, y, stream=None):
+    _call("moe_combine_bf16", ctypes.byref(s), _ptr(plan), _ptr(Y), _ptr(topk_w),
+          _ptr(shared_out), _ptr(y), _stream(stream))
+
+
+def moe_combine_f32(s, plan, Y, topk_w, shared_out, y, stream=None):
+    _call("moe_combine_f32", ctypes.byref(s), _ptr(plan), _ptr(Y), _ptr(topk_w),
+          _ptr(shared_out), _ptr(y), _stream(stream))
+
+
+def moe_reverse_combine_bf16(s, plan, dy, dYu, stream=None):
+    _call("moe_reverse_combine_bf16", ctypes.byref(s), _ptr(plan), _ptr(dy), _ptr(dYu),
+          _stream(stream))
+
+
+def moe_reverse_dispatch_bf16(s, plan, dX, shared_dx, dx, stream=None):
+    _call("moe_reverse_dispatch_bf16", ctypes.byref(s), _ptr(plan), _ptr(dX), _ptr(shared_dx),
+          _ptr(dx), _stream(stream))
+
+
+def _fwd(name, s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down, y, saved, ws,
+         stream):
+    _call(name, ctypes.byref(s), _ptr(plan), _ptr(x), _ptr(topk_w), _ptr(w_gate), _ptr(w_up),
+          _ptr(w_down), _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(y), _ptr(saved), _ptr(ws),
+          0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+
+
+def moe_forward_bf16(s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down, y, saved,
+                     ws, stream=None):
+    _fwd("moe_forward_bf16", s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down, y,
+         saved, ws, stream)
+
+
+def moe_forward_f32(s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down, y, saved,
+                    ws, stream=None):
+    _fwd("moe_forward_f32", s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down, y,
+         saved, ws, stream)
+
+
+def _bwd(name, s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down, saved, dy, dx,
+         dw_gate, dw_up, dw_down, ds_gate, ds_up, ds_down, d_topk_w, ws, stream):
+    _call(name, ctypes.byref(s), _ptr(plan), _ptr(x), _ptr(topk_w), _ptr(w_gate), _ptr(w_up),
+          _ptr(w_down), _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(saved), _ptr(dy), _ptr(dx),
+          _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _ptr(ds_gate), _ptr(ds_up), _ptr(ds_down),
+          _ptr(d_topk_w), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+          _stream(stream))
+
+
+def moe_backward_bf16(s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down, saved, dy,
+                      dx, dw_gate, dw_up, dw_down, ds_gate, ds_up, ds_down, d_topk_w, ws,
+                      stream=None):
+    _bwd("moe_backward_bf16", s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down,
+         saved, dy, dx, dw_gate, dw_up, dw_down, ds_gate, ds_up, ds_down, d_topk_w, ws, stream)
+
+
+def moe_backward_f32(s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down, saved, dy,
+                     dx, dw_gate, dw_up, dw_down, ds_gate, ds_up, ds_down, d_topk_w, ws,
+                     stream=None):
+    _bwd("moe_backward_f32", s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down,
+         saved, dy, dx, dw_gate, dw_up, dw_down, ds_gate, ds_up, ds_down, d_topk_w, ws, stream)
+
+
+# ------------------------------------------------------------ kernel timing
+_hip = None
+
+
+def _hiprt():
+    global _hip
+    if _hip is None:
+        h = ctypes.CDLL("libamdhip64.so")
+        h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                          ctypes.c_void_p]
+        _hip = h
+    return _hip
+
+
+class KernelTrace:
+    """Per-kernel HIP events around every launch the library makes from this
+    thread while active (``with KernelTrace(n) as tr: ...``); ``records()`` gives
+    (name, milliseconds) per launch after the stream has been synchronised."""
+
+    def __init__(self, capacity: int):
+        h = _hiprt()
+        self.capacity = capacity
+        self._events = (ctypes.c_void_p * (2 * capacity))()
+        for i in range(2 * capacity):
+            if h.hipEventCreate(ctypes.byref(self._events, i * ctypes.sizeof(ctypes.c_void_p))) != 0:
+                raise RuntimeError("hipEventCreate failed")
+        self._names = (ctypes.c_char_p * capacity)()
+        self.t = moe_trace(ctypes.cast(self._events, ctypes.POINTER(ctypes.c_void_p)),
+                           ctypes.cast(self._names, ctypes.POINTER(ctypes.c_char_p)),
+                           capacity, 0)
+
+    def __enter__(self):
+        self.t.count = 0
+        lib().moe_trace_set(ctypes.byref(self.t))
+        return self
+
+    def __exit__(self, *exc):
+        lib().moe_trace_set(None)
+        return False
+
+    def records(self):
+        h = _hiprt()
+        out = []
+        ms = ctypes.c_float()
+        for i in range(self.t.count):
+            if h.hipEventElapsedTime(ctypes.byref(ms), self._events[2 * i], self._events[2 * i + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append((self._names[i].decode(), ms.value))
+        return out
+
+    def close(self):
+        h = _hiprt()
+        for i in range(2 * self.capacity):
+            h.hipEventDestroy(self._events[i])
+        self.capacity = 0
+
+
+# ------------------------------------------------------------ buffer helpers
+def plan_views(s: moe_shape, plan: torch.Tensor) -> dict:
+    """int32 views of the arrays inside a plan buffer (uint8 tensor)."""
+    L = moe_plan_layout_of(s)
+    R = s.T * s.k
+
+    def view(off, n):
+        return plan[off:off + 4 * n].view(torch.int32)
+
+    return {"counts": view(L.counts, s.E), "offsets": view(L.offsets, s.E + 1),
+            "src_token": view(L.src_token, R), "src_slot": view(L.src_slot, R),
+            "pos": view(L.pos, R).view(s.T, s.k), "tiles": view(L.tiles, 2 * L.max_tiles).view(-1, 2),
+            "n_tiles": view(L.n_tiles, 1), "err_flag": view(L.err_flag, 1),
+            "tile_m": L.tile_m}

@@ -1,0 +1,502 @@
+// C-ABI of the MoE layer (include/moe.h): argument checks, buffer layouts and the
+// enqueue sequences of the forward and backward passes.  Nothing here allocates,
+// synchronises or keeps state; every kernel goes onto the caller's stream.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "internal.hpp"
+
+using namespace moe;
+
+namespace moe {
+
+thread_local ::moe_trace* tls_trace = nullptr;
+
+void trace_before(hipStream_t s, const char* name) {
+  moe_trace* t = tls_trace;
+  if (!t || t->count >= t->capacity) return;
+  t->names[t->count] = name;
+  (void)hipEventRecord(t->events[2 * t->count], s);
+}
+
+void trace_after(hipStream_t s) {
+  moe_trace* t = tls_trace;
+  if (!t || t->count >= t->capacity) return;
+  (void)hipEventRecord(t->events[2 * t->count + 1], s);
+  ++t->count;
+}
+
+}  // namespace moe
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+
+size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Carves consecutive 256-byte-aligned regions out of one buffer.
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off += up(bytes);
+    return o;
+  }
+};
+
+moe_status check_shape(const moe_shape* s, bool need_gemm_dims) {
+  if (!s) return MOE_E_NULL;
+  if (s->T < 0 || s->E < 1 || s->E > MOE_MAX_E || s->k < 1 || s->k > s->E || s->k > MOE_MAX_K)
+    return MOE_E_SHAPE;
+  if ((int64_t)s->T * s->k >= (int64_t)1 << 31) return MOE_E_SHAPE;
+  if (s->H < 128 || s->H % 128) return MOE_E_SHAPE;
+  if (need_gemm_dims) {
+    if (s->I < 128 || s->I % 128) return MOE_E_SHAPE;
+    if (s->I_shared < 0 || s->I_shared % 128) return MOE_E_SHAPE;
+    if (s->T_minibatch < 0) return MOE_E_SHAPE;
+  }
+  return MOE_OK;
+}
+
+moe_plan_layout plan_layout(const moe_shape* s) {
+  moe_plan_layout L;
+  memset(&L, 0, sizeof(L));
+  const int64_t R = (int64_t)s->T * s->k;
+  L.tile_m = GEMM_TILE_M;
+  L.max_tiles = (int32_t)(R / GEMM_TILE_M + (R < s->E ? R : s->E) + 1);
+  L.chunk_pairs = PLAN_CHUNK;
+  L.n_chunks = (int32_t)((R + PLAN_CHUNK - 1) / PLAN_CHUNK);
+  Carve c;
+  L.counts = c.take(sizeof(int32_t) * s->E);
+  L.offsets = c.take(sizeof(int32_t) * (s->E + 1));
+  L.src_token = c.take(sizeof(int32_t) * R);
+  L.src_slot = c.take(sizeof(int32_t) * R);
+  L.pos = c.take(sizeof(int32_t) * R);
+  L.tiles = c.take(sizeof(int32_t) * 2 * (size_t)L.max_tiles);
+  L.n_tiles = c.take(sizeof(int32_t));
+  L.err_flag = c.take(sizeof(int32_t));
+  L.scratch = c.take(sizeof(int32_t) * ((size_t)L.n_chunks * s->E + L.n_chunks));
+  L.total_bytes = c.off;
+  return L;
+}
+
+template <typename P>
+P* at(void* base, size_t off) {
+  return (P*)((char*)base + off);
+}
+template <typename P>
+const P* at(const void* base, size_t off) {
+  return (const P*)((const char*)base + off);
+}
+
+struct PlanView {
+  const int32_t *counts, *offsets, *src_token, *src_slot, *pos, *tiles, *n_tiles;
+  int max_tiles;
+};
+
+PlanView view_plan(const moe_shape* s, const void* plan) {
+  const moe_plan_layout L = plan_layout(s);
+  PlanView v;
+  v.counts = at<int32_t>(plan, L.counts);
+  v.offsets = at<int32_t>(plan, L.offsets);
+  v.src_token = at<int32_t>(plan, L.src_token);
+  v.src_slot = at<int32_t>(plan, L.src_slot);
+  v.pos = at<int32_t>(plan, L.pos);
+  v.tiles = at<int32_t>(plan, L.tiles);
+  v.n_tiles = at<int32_t>(plan, L.n_tiles);
+  v.max_tiles = L.max_tiles;
+  return v;
+}
+
+GroupInfo grouped(const moe_shape* s, const PlanView& v) {
+  GroupInfo g;
+  g.tiles = v.tiles;
+  g.n_tiles = v.n_tiles;
+  g.offsets = v.offsets;
+  g.src_token = v.src_token;
+  g.src_slot = v.src_slot;
+  g.max_tiles = v.max_tiles;
+  g.dense_rows = 0;
+  g.E = s->E;
+  return g;
+}
+
+GroupInfo dense(int rows) {
+  GroupInfo g;
+  memset(&g, 0, sizeof(g));
+  g.dense_rows = rows;
+  g.E = 1;
+  return g;
+}
+
+size_t esize(moe_dtype dt) { return dt == MOE_F32 ? 4 : 2; }
+
+// saved: Z [R, 2I] then Zs [T, 2 Is]
+struct SavedLayout {
+  size_t Z, Zs, total;
+};
+SavedLayout saved_layout(const moe_shape* s, moe_dtype dt) {
+  const size_t R = (size_t)s->T * s->k, es = esize(dt);
+  Carve c;
+  SavedLayout L;
+  L.Z = c.take(R * 2 * s->I * es);
+  L.Zs = c.take((size_t)s->T * 2 * s->I_shared * es);
+  L.total = c.off;
+  return L;
+}
+
+// forward workspace: h [R, I], Y [R, H], hs [T, Is], ys [T, H]
+struct FwdWs {
+  size_t h, Y, hs, ys, total;
+};
+FwdWs fwd_ws(const moe_shape* s, moe_dtype dt) {
+  const size_t R = (size_t)s->T * s->k, es = esize(dt), T = s->T;
+  Carve c;
+  FwdWs L;
+  L.h = c.take(R * s->I * es);
+  L.Y = c.take(R * s->H * es);
+  L.hs = c.take(T * s->I_shared * es);
+  L.ys = c.take(s->I_shared ? T * s->H * es : 0);
+  L.total = c.off;
+  return L;
+}
+
+// backward workspace: dZ [R, 2I], gh [R, I], dgp fp32 [R, I/128], dX [R, H],
+// dZs [T, 2Is], hs [T, Is], dxs [T, H]
+struct BwdWs {
+  size_t dZ, gh, dgp, dX, dZs, hs, dxs, total;
+};
+BwdWs bwd_ws(const moe_shape* s, moe_dtype dt) {
+  const size_t R = (size_t)s->T * s->k, es = esize(dt), T = s->T;
+  Carve c;
+  BwdWs L;
+  L.dZ = c.take(R * 2 * s->I * es);
+  L.gh = c.take(R * s->I * es);
+  L.dgp = c.take(R * (s->I / 128) * sizeof(float));
+  L.dX = c.take(R * s->H * es);
+  L.dZs = c.take(T * 2 * s->I_shared * es);
+  L.hs = c.take(T * s->I_shared * es);
+  L.dxs = c.take(s->I_shared ? T * s->H * es : 0);
+  L.total = c.off;
+  return L;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E_HIP; }
+
+#define MOE_TRY(expr)                         \
+  do {                                        \
+    const hipError_t e_ = (expr);             \
+    if (e_ != hipSuccess) return MOE_E_HIP;   \
+  } while (0)
+
+bool all_aligned(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p && !aligned16(p)) return false;
+  return true;
+}
+
+bool any_null(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!p) return true;
+  return false;
+}
+
+moe_status forward_impl(moe_dtype dt, const moe_shape* s, const void* plan, const void* x,
+                        const float* topk_w, const void* wg, const void* wu, const void* wd,
+                        const void* sg, const void* su, const void* sd, void* y, void* saved,
+                        void* ws, size_t ws_bytes, hipStream_t st) {
+  moe_status rc = check_shape(s, true);
+  if (rc != MOE_OK) return rc;
+  if (s->T_minibatch != 0 && s->T_minibatch != s->T) return MOE_E_UNSUPPORTED;
+  if (any_null({plan, x, topk_w, wg, wu, wd, y, saved}) || (s->T > 0 && !ws)) return MOE_E_NULL;
+  if (s->I_shared && any_null({sg, su, sd})) return MOE_E_NULL;
+  if (!all_aligned({plan, x, topk_w, wg, wu, wd, sg, su, sd, y, saved, ws})) return MOE_E_ALIGN;
+  const FwdWs W = fwd_ws(s, dt);
+  if (ws_bytes < W.total) return MOE_E_WORKSPACE;
+  if (s->T == 0) return MOE_OK;
+  const int d = dt == MOE_BF16 ? 1 : 0;
+  const PlanView v = view_plan(s, plan);
+  const SavedLayout S = saved_layout(s, dt);
+  const GroupInfo g = grouped(s, v);
+  void* Z = at<char>(saved, S.Z);
+  void* h = at<char>(ws, W.h);
+  void* Y = at<char>(ws, W.Y);
+  MOE_TRY(launch_gemm_up_swiglu(d, g, x, wg, wu, s->H, s->I, Z, h, st));
+  MOE_TRY(launch_gemm_down(d, g, h, wd, s->H, s->I, Y, st));
+  void* ys = nullptr;
+  if (s->I_shared) {
+    const GroupInfo gs = dense(s->T);
+    void* Zs = at<char>(saved, S.Zs);
+    void* hs = at<char>(ws, W.hs);
+    ys = at<char>(ws, W.ys);
+    MOE_TRY(launch_gemm_up_swiglu(d, gs, x, sg, su, s->H, s->I_shared, Zs, hs, st));
+    MOE_TRY(launch_gemm_down(d, gs, hs, sd, s->H, s->I_shared, ys, st));
+  }
+  if (d)
+    MOE_TRY(launch_combine_bf16(Y, v.pos, topk_w, ys, y, s->T, s->k, s->H, st));
+  else
+    MOE_TRY(launch_combine_f32((const float*)Y, v.pos, topk_w, (const float*)ys, (float*)y, s->T,
+                               s->k, s->H, st));
+  return MOE_OK;
+}
+
+moe_status backward_impl(moe_dtype dt, const moe_shape* s, const void* plan, const void* x,
+                         const float* topk_w, const void* wg, const void* wu, const void* wd,
+                         const void* sg, const void* su, const void* sd, const void* saved,
+                         const void* dy, void* dx, void* dwg, void* dwu, void* dwd, void* dsg,
+                         void* dsu, void* dsd, float* d_topk_w, void* ws, size_t ws_bytes,
+                         hipStream_t st) {
+  moe_status rc = check_shape(s, true);
+  if (rc != MOE_OK) return rc;
+  if (s->T_minibatch != 0 && s->T_minibatch != s->T) return MOE_E_UNSUPPORTED;
+  if (any_null({plan, x, topk_w, wg, wu, wd, saved, dy, dx, dwg, dwu, dwd, d_topk_w}) ||
+      (s->T > 0 && !ws))
+    return MOE_E_NULL;
+  if (s->I_shared && any_null({sg, su, sd, dsg, dsu, dsd})) return MOE_E_NULL;
+  if (!all_aligned({plan, x, topk_w, wg, wu, wd, sg, su, sd, saved, dy, dx, dwg, dwu, dwd, dsg, dsu,
+                    dsd, d_topk_w, ws}))
+    return MOE_E_ALIGN;
+  const BwdWs W = bwd_ws(s, dt);
+  if (ws_bytes < W.total) return MOE_E_WORKSPACE;
+  const int d = dt == MOE_BF16 ? 1 : 0;
+  const PlanView v = view_plan(s, plan);
+  const SavedLayout S = saved_layout(s, dt);
+  const GroupInfo g = grouped(s, v);
+  const int H = s->H, I = s->I, R = s->T * s->k;
+  const void* Z = at<char>(saved, S.Z);
+  void* dZ = at<char>(ws, W.dZ);
+  void* gh = at<char>(ws, W.gh);
+  float* dgp = at<float>(ws, W.dgp);
+  void* dX = at<char>(ws, W.dX);
+  // reverse-combine (gathered in the loader) + dgrad-down + SwiGLU backward + dg partials
+  MOE_TRY(launch_gemm_dgrad_down(d, g, dy, wd, Z, topk_w, H, I, s->k, dZ, gh, dgp, st));
+  MOE_TRY(launch_dg_reduce(dgp, v.pos, R, I / 128, d_topk_w, st));
+  MOE_TRY(launch_gemm_wgrad_down(d, g, dy, gh, H, I, dwd, st));
+  MOE_TRY(launch_gemm_dgrad_up(d, g, dZ, wg, wu, H, I, dX, st));
+  MOE_TRY(launch_gemm_wgrad_up(d, g, dZ, x, H, I, dwg, dwu, st));
+  void* dxs = nullptr;
+  if (s->I_shared) {
+    const int Is = s->I_shared;
+    const GroupInfo gs = dense(s->T);
+    const void* Zs = at<char>(saved, S.Zs);
+    void* dZs = at<char>(ws, W.dZs);
+    void* hs = at<char>(ws, W.hs);
+    dxs = at<char>(ws, W.dxs);
+    MOE_TRY(launch_gemm_dgrad_down(d, gs, dy, sd, Zs, nullptr, H, Is, 1, dZs, hs, nullptr, st));
+    MOE_TRY(launch_gemm_wgrad_down(d, gs, dy, hs, H, Is, dsd, st));
+    MOE_TRY(launch_gemm_dgrad_up(d, gs, dZs, sg, su, H, Is, dxs, st));
+    MOE_TRY(launch_gemm_wgrad_up(d, gs, dZs, x, H, Is, dsg, dsu, st));
+  }
+  if (d)
+    MOE_TRY(launch_combine_bf16(dX, v.pos, nullptr, dxs, dx, s->T, s->k, H, st));
+  else
+    MOE_TRY(launch_combine_f32((const float*)dX, v.pos, nullptr, (const float*)dxs, (float*)dx,
+                               s->T, s->k, H, st));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void moe_trace_set(moe_trace* trace) { moe::tls_trace = trace; }
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_E_NULL: return "a required pointer is NULL";
+    case MOE_E_SHAPE: return "shape out of range or not a supported multiple";
+    case MOE_E_ALIGN: return "pointer not 16-byte aligned";
+    case MOE_E_WORKSPACE: return "workspace too small";
+    case MOE_E_UNSUPPORTED: return "not supported by this build";
+    case MOE_E_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+moe_status moe_plan_layout_of(const moe_shape* shape, moe_plan_layout* out) {
+  if (!out) return MOE_E_NULL;
+  const moe_status rc = check_shape(shape, false);
+  if (rc != MOE_OK) return rc;
+  *out = plan_layout(shape);
+  return MOE_OK;
+}
+
+size_t moe_plan_bytes(const moe_shape* shape) {
+  if (check_shape(shape, false) != MOE_OK) return 0;
+  return plan_layout(shape).total_bytes;
+}
+
+size_t moe_saved_bytes(const moe_shape* shape, moe_dtype dtype) {
+  if (check_shape(shape, true) != MOE_OK || dtype == MOE_MXFP8) return 0;
+  return saved_layout(shape, dtype).total;
+}
+
+size_t moe_workspace_bytes(const moe_shape* shape, moe_dtype dtype, int backward) {
+  if (check_shape(shape, true) != MOE_OK || dtype == MOE_MXFP8) return 0;
+  return backward ? bwd_ws(shape, dtype).total : fwd_ws(shape, dtype).total;
+}
+
+moe_status moe_router_logits_f32(const moe_shape* s, const float* x, const float* w_router,
+                                 float* logits, hipStream_t st) {
+  moe_status rc = check_shape(s, false);
+  if (rc != MOE_OK) return rc;
+  if (any_null({x, w_router, logits})) return MOE_E_NULL;
+  if (!all_aligned({x, w_router, logits})) return MOE_E_ALIGN;
+  return hip_status(launch_router_logits_f32(x, w_router, s->T, s->H, s->E, logits, st));
+}
+
+moe_status moe_route(const moe_shape* s, const float* logits, int32_t* topk_idx, float* topk_w,
+                     hipStream_t st) {
+  moe_status rc = check_shape(s, false);
+  if (rc != MOE_OK) return rc;
+  if (any_null({logits, topk_idx, topk_w})) return MOE_E_NULL;
+  if (!all_aligned({logits, topk_idx, topk_w})) return MOE_E_ALIGN;
+  return hip_status(launch_route(logits, s->T, s->E, s->k, topk_idx, topk_w, st));
+}
+
+moe_status moe_route_backward(const moe_shape* s, const int32_t* topk_idx, const float* topk_w,
+                              const float* d_topk_w, float* d_logits, hipStream_t st) {
+  moe_status rc = check_shape(s, false);
+  if (rc != MOE_OK) return rc;
+  if (any_null({topk_idx, topk_w, d_topk_w, d_logits})) return MOE_E_NULL;
+  if (!all_aligned({topk_idx, topk_w, d_topk_w, d_logits})) return MOE_E_ALIGN;
+  return hip_status(
+      launch_route_backward(topk_idx, topk_w, d_topk_w, s->T, s->E, s->k, d_logits, st));
+}
+
+moe_status moe_router_backward_f32(const moe_shape* s, const float* x, const float* w_router,
+                                   const float* d_logits, float* dw_router, float* dx,
+                                   hipStream_t st) {
+  moe_status rc = check_shape(s, false);
+  if (rc != MOE_OK) return rc;
+  if (any_null({x, w_router, d_logits, dw_router, dx})) return MOE_E_NULL;
+  if (!all_aligned({x, w_router, d_logits, dw_router, dx})) return MOE_E_ALIGN;
+  return hip_status(
+      launch_router_backward_f32(x, w_router, d_logits, s->T, s->H, s->E, dw_router, dx, st));
+}
+
+moe_status moe_plan(const moe_shape* s, const int32_t* topk_idx, void* plan, hipStream_t st) {
+  moe_status rc = check_shape(s, false);
+  if (rc != MOE_OK) return rc;
+  if (any_null({topk_idx, plan})) return MOE_E_NULL;
+  if (!all_aligned({topk_idx, plan})) return MOE_E_ALIGN;
+  const moe_plan_layout L = plan_layout(s);
+  PlanPtrs p;
+  p.counts = at<int32_t>(plan, L.counts);
+  p.offsets = at<int32_t>(plan, L.offsets);
+  p.src_token = at<int32_t>(plan, L.src_token);
+  p.src_slot = at<int32_t>(plan, L.src_slot);
+  p.pos = at<int32_t>(plan, L.pos);
+  p.tiles = at<int32_t>(plan, L.tiles);
+  p.n_tiles = at<int32_t>(plan, L.n_tiles);
+  p.err_flag = at<int32_t>(plan, L.err_flag);
+  p.chunk_hist = at<int32_t>(plan, L.scratch);
+  p.chunk_invalid = p.chunk_hist + (size_t)L.n_chunks * s->E;
+  p.n_chunks = L.n_chunks;
+  p.max_tiles = L.max_tiles;
+  return hip_status(launch_plan(topk_idx, s->T, s->k, s->E, p, st));
+}
+
+static moe_status gather_impl(const moe_shape* s, const void* plan, const void* src, void* dst,
+                              size_t es, hipStream_t st) {
+  moe_status rc = check_shape(s, false);
+  if (rc != MOE_OK) return rc;
+  if (any_null({plan, src, dst})) return MOE_E_NULL;
+  if (!all_aligned({plan, src, dst})) return MOE_E_ALIGN;
+  const PlanView v = view_plan(s, plan);
+  return hip_status(launch_gather_rows(src, dst, v.src_token, v.offsets + s->E, s->T * s->k,
+                                       (int)(s->H * es), st));
+}
+
+moe_status moe_dispatch_bf16(const moe_shape* s, const void* plan, const void* x, void* X,
+                             hipStream_t st) {
+  return gather_impl(s, plan, x, X, 2, st);
+}
+moe_status moe_dispatch_f32(const moe_shape* s, const void* plan, const float* x, float* X,
+                            hipStream_t st) {
+  return gather_impl(s, plan, x, X, 4, st);
+}
+moe_status moe_reverse_combine_bf16(const moe_shape* s, const void* plan, const void* dy,
+                                    void* dYu, hipStream_t st) {
+  return gather_impl(s, plan, dy, dYu, 2, st);
+}
+
+moe_status moe_combine_bf16(const moe_shape* s, const void* plan, const void* Y,
+                            const float* topk_w, const void* shared_out, void* y,
+                            hipStream_t st) {
+  moe_status rc = check_shape(s, false);
+  if (rc != MOE_OK) return rc;
+  if (any_null({plan, Y, topk_w, y})) return MOE_E_NULL;
+  if (!all_aligned({plan, Y, topk_w, shared_out, y})) return MOE_E_ALIGN;
+  const PlanView v = view_plan(s, plan);
+  return hip_status(launch_combine_bf16(Y, v.pos, topk_w, shared_out, y, s->T, s->k, s->H, st));
+}
+
+moe_status moe_combine_f32(const moe_shape* s, const void* plan, const float* Y,
+                           const float* topk_w, const float* shared_out, float* y,
+                           hipStream_t st) {
+  moe_status rc = check_shape(s, false);
+  if (rc != MOE_OK) return rc;
+  if (any_null({plan, Y, topk_w, y})) return MOE_E_NULL;
+  if (!all_aligned({plan, Y, topk_w, shared_out, y})) return MOE_E_ALIGN;
+  const PlanView v = view_plan(s, plan);
+  return hip_status(launch_combine_f32(Y, v.pos, topk_w, shared_out, y, s->T, s->k, s->H, st));
+}
+
+moe_status moe_reverse_dispatch_bf16(const moe_shape* s, const void* plan, const void* dX,
+                                     const void* shared_dx, void* dx, hipStream_t st) {
+  moe_status rc = check_shape(s, false);
+  if (rc != MOE_OK) return rc;
+  if (any_null({plan, dX, dx})) return MOE_E_NULL;
+  if (!all_aligned({plan, dX, shared_dx, dx})) return MOE_E_ALIGN;
+  const PlanView v = view_plan(s, plan);
+  return hip_status(launch_combine_bf16(dX, v.pos, nullptr, shared_dx, dx, s->T, s->k, s->H, st));
+}
+
+moe_status moe_forward_bf16(const moe_shape* s, const void* plan, const void* x,
+                            const float* topk_w, const void* w_gate, const void* w_up,
+                            const void* w_down, const void* s_gate, const void* s_up,
+                            const void* s_down, void* y, void* saved, void* ws, size_t ws_bytes,
+                            hipStream_t st) {
+  return forward_impl(MOE_BF16, s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down, y,
+                      saved, ws, ws_bytes, st);
+}
+
+moe_status moe_forward_f32(const moe_shape* s, const void* plan, const float* x,
+                           const float* topk_w, const float* w_gate, const float* w_up,
+                           const float* w_down, const float* s_gate, const float* s_up,
+                           const float* s_down, float* y, void* saved, void* ws, size_t ws_bytes,
+                           hipStream_t st) {
+  return forward_impl(MOE_F32, s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down, y,
+                      saved, ws, ws_bytes, st);
+}
+
+moe_status moe_backward_bf16(const moe_shape* s, const void* plan, const void* x,
+                             const float* topk_w, const void* w_gate, const void* w_up,
+                             const void* w_down, const void* s_gate, const void* s_up,
+                             const void* s_down, const void* saved, const void* dy, void* dx,
+                             void* dw_gate, void* dw_up, void* dw_down, void* ds_gate,
+                             void* ds_up, void* ds_down, float* d_topk_w, void* ws,
+                             size_t ws_bytes, hipStream_t st) {
+  return backward_impl(MOE_BF16, s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down,
+                       saved, dy, dx, dw_gate, dw_up, dw_down, ds_gate, ds_up, ds_down, d_topk_w,
+                       ws, ws_bytes, st);
+}
+
+moe_status moe_backward_f32(const moe_shape* s, const void* plan, const float* x,
+                            const float* topk_w, const float* w_gate, const float* w_up,
+                            const float* w_down, const float* s_gate, const float* s_up,
+                            const float* s_down, const void* saved, const float* dy, float* dx,
+                            float* dw_gate, float* dw_up, float* dw_down, float* ds_gate,
+                            float* ds_up, float* ds_down, float* d_topk_w, void* ws,
+                            size_t ws_bytes, hipStream_t st) {
+  return backward_impl(MOE_F32, s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down,
+                       saved, dy, dx, dw_gate, dw_up, dw_down, ds_gate, ds_up, ds_down, d_topk_w,
+                       ws, ws_bytes, st);
+}
+
+}  // extern "C"

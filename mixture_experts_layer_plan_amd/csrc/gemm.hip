@@ -1,0 +1,658 @@
+// Grouped expert GEMMs on MFMA (gfx950), with the layer's epilogues fused.
+//
+// The experts are SwiGLU feed-forward nets (up, gate, down projections) run as
+// grouped GEMMs over all experts at once (sebask.de, "Mixture-of-Kittens: Cursors
+// Open-Source-Ansatz für effizientes MoE-Training auf NVL72", introduction;
+// stamatios.com, "Cursor abre código de megakernel MoE para GPUs NVL72",
+// § Granularidade do overlap and § Outras características: SwiGLU, router-weight
+// gradient fused into the SwiGLU backward).
+//
+// One workgroup (256 threads = 4 wavefronts in 2 x 2) computes a 128 x 128 output
+// tile; each wavefront owns 64 x 64 = 2 x 2 blocks of the 32 x 32 MFMA
+// (v_mfma_f32_32x32x16_bf16 for bf16, 8 x v_mfma_f32_32x32x2_f32 per 16-deep step
+// for fp32).  Operands are staged through LDS as 128 rows x 128 bytes (64 bf16 or
+// 32 fp32 of K per row), 16-byte chunks XOR-swizzled by row so that the MFMA
+// fragment reads and the staging writes spread over the banks; two LDS buffers
+// and a register prefetch overlap the next tile's global loads with the current
+// tile's MFMAs.  An operand stored K-contiguous ("K-major") is copied chunk by
+// chunk; one stored with K as the outer dimension ("MN-major": the wgrad operands
+// and the weights of the dgrad GEMMs) is loaded as 4 x VEC blocks and transposed
+// in registers on its way into LDS.
+//
+// Grouping: a "rows-grouped" GEMM (forward GEMMs and dgrads) walks the plan's
+// tile list (expert, first row) so a tile never mixes experts; a "K-grouped" GEMM
+// (wgrads) takes one expert per grid z and runs K over that expert's rows.  The
+// gathers of dispatch (x rows) and reverse-combine (dy rows) happen in the A/B
+// loaders through the plan's src_token list, so X and dYu are never written to
+// HBM.  Every output element is produced by one workgroup with a fixed K order:
+// results are bitwise reproducible and independent of the grid.
+//
+// Epilogues stage the fp32 accumulator tile in LDS (64 KiB, swizzled) and then
+// work on rows of 8 consecutive columns with 16-byte global accesses.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace moe {
+
+constexpr int TM = 128, TN = 128, NTHR = 256;
+constexpr int ROWB = 128;            // bytes per LDS operand row
+constexpr int TILEB = 128 * ROWB;    // one operand tile: 16 KiB
+constexpr int LDS_BYTES = 4 * TILEB; // 2 buffers x (A, B) = 64 KiB = the staged C tile
+
+template <typename T> struct Tr;
+template <> struct Tr<bf16_t> { static constexpr int BK = 64, VEC = 8; };
+template <> struct Tr<float> { static constexpr int BK = 32, VEC = 4; };
+
+// byte offset of 16-byte chunk `chunk` of operand row `row`
+MOE_DEV int swz(int row, int chunk) { return row * ROWB + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4); }
+
+// float offset of element (row, col) in the staged 128 x 128 fp32 C tile
+MOE_DEV int cidx(int row, int col) { return row * 128 + ((((col >> 3) ^ (row & 15))) << 3) + (col & 7); }
+
+MOE_DEV uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+// ------------------------------------------------------------------ loaders
+// K-major operand: thread t loads chunk (t & 7) of tile rows (t >> 3) + 32 s.
+template <typename T>
+struct KLoad {
+  const T* rp[4];
+  MOE_DEV void load(int kt, uint4 (&r)[4]) const {
+    const int k = kt * Tr<T>::BK + (threadIdx.x & 7) * Tr<T>::VEC;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) r[s] = rp[s] ? *(const uint4*)(rp[s] + k) : zero4();
+  }
+  MOE_DEV void store(char* t, const uint4 (&r)[4]) const {
+    const int row = threadIdx.x >> 3, ch = threadIdx.x & 7;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) *(uint4*)(t + swz(row + 32 * s, ch)) = r[s];
+  }
+};
+
+// MN-major operand: element (k, i) of the tile at kr(k)[i]; kr returns nullptr
+// for K rows outside the operand (they load as zeros).
+// bf16: thread t owns k = 4 (t >> 4) .. +3, i = 8 (t & 15) .. +7.
+// fp32: thread t owns k = 4 (t >> 5) .. +3, i = 4 (t & 31) .. +3.
+template <typename T, class KR>
+struct MNLoad {
+  KR kr;
+  static constexpr int IB = 128 / Tr<T>::VEC;  // i-blocks per row of 128
+  MOE_DEV void load(int kt, uint4 (&r)[4]) const {
+    const int kb = threadIdx.x / IB, ib = threadIdx.x % IB;
+    const int k0 = kt * Tr<T>::BK + 4 * kb;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const T* p = kr(k0 + kk);
+      r[kk] = p ? *(const uint4*)(p + ib * Tr<T>::VEC) : zero4();
+    }
+  }
+  MOE_DEV void store(char* t, const uint4 (&r)[4]) const;
+};
+
+MOE_DEV uint32_t u4_word(const uint4& v, int w) {
+  return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
+}
+
+template <typename T, class KR>
+MOE_DEV void MNLoad<T, KR>::store(char* t, const uint4 (&r)[4]) const {
+  const int kb = threadIdx.x / IB, ib = threadIdx.x % IB;
+  if constexpr (sizeof(T) == 2) {
+    // 4 k x 8 i bf16 -> 8 rows (i) of 4 k values (8 bytes)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int sh = (i & 1) * 16;
+      const uint32_t e0 = (u4_word(r[0], i >> 1) >> sh) & 0xffffu;
+      const uint32_t e1 = (u4_word(r[1], i >> 1) >> sh) & 0xffffu;
+      const uint32_t e2 = (u4_word(r[2], i >> 1) >> sh) & 0xffffu;
+      const uint32_t e3 = (u4_word(r[3], i >> 1) >> sh) & 0xffffu;
+      const int row = ib * 8 + i;
+      *(uint2*)(t + swz(row, kb >> 1) + (kb & 1) * 8) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+    }
+  } else {
+    // 4 k x 4 i fp32 -> 4 rows (i) of 4 k values (16 bytes)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = ib * 4 + i;
+      *(uint4*)(t + swz(row, kb)) =
+          make_uint4(u4_word(r[0], i), u4_word(r[1], i), u4_word(r[2], i), u4_word(r[3], i));
+    }
+  }
+}
+
+// ------------------------------------------------------------- MFMA on a tile
+// acc[mb][nb]: wave rows arow + 32 mb, B-tile rows brow[nb]; lane l supplies row
+// (l & 31) and the 8 K values of chunk half (l >> 5) of each 16-deep step.
+template <typename T>
+MOE_DEV void mma_tile(const char* ta, const char* tb, f32x16_t (&acc)[2][2], int arow,
+                      const int (&brow)[2], int lane);
+
+template <>
+MOE_DEV void mma_tile<bf16_t>(const char* ta, const char* tb, f32x16_t (&acc)[2][2], int arow,
+                              const int (&brow)[2], int lane) {
+  const int r = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int ch = ks * 2 + hi;
+    const bf16x8_t a0 = *(const bf16x8_t*)(ta + swz(arow + r, ch));
+    const bf16x8_t a1 = *(const bf16x8_t*)(ta + swz(arow + 32 + r, ch));
+    const bf16x8_t b0 = *(const bf16x8_t*)(tb + swz(brow[0] + r, ch));
+    const bf16x8_t b1 = *(const bf16x8_t*)(tb + swz(brow[1] + r, ch));
+    acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
+    acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
+    acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
+    acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
+  }
+}
+
+template <>
+MOE_DEV void mma_tile<float>(const char* ta, const char* tb, f32x16_t (&acc)[2][2], int arow,
+                             const int (&brow)[2], int lane) {
+  const int r = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int ch = ks * 4 + hi * 2;
+    float a[2][8], b[2][8];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      *(uint4*)&a[0][4 * q] = *(const uint4*)(ta + swz(arow + r, ch + q));
+      *(uint4*)&a[1][4 * q] = *(const uint4*)(ta + swz(arow + 32 + r, ch + q));
+      *(uint4*)&b[0][4 * q] = *(const uint4*)(tb + swz(brow[0] + r, ch + q));
+      *(uint4*)&b[1][4 * q] = *(const uint4*)(tb + swz(brow[1] + r, ch + q));
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0][s], b[0][s], acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0][s], b[1][s], acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[1][s], b[0][s], acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[1][s], b[1][s], acc[1][1], 0, 0, 0);
+    }
+  }
+}
+
+// ----------------------------------------------------------------- main loop
+template <typename T, class LA, class LB>
+MOE_DEV void gemm_main(char* lds, const LA& la, const LB& lb, int nk, f32x16_t (&acc)[2][2],
+                       int arow, const int (&brow)[2], int lane) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  if (nk <= 0) return;
+  uint4 ra[4], rb[4];
+  la.load(0, ra);
+  lb.load(0, rb);
+  la.store(lds, ra);
+  lb.store(lds + TILEB, rb);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    char* cur = lds + (kt & 1) * 2 * TILEB;
+    char* nxt = lds + ((kt + 1) & 1) * 2 * TILEB;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      la.load(kt + 1, ra);
+      lb.load(kt + 1, rb);
+    }
+    mma_tile<T>(cur, cur + TILEB, acc, arow, brow, lane);
+    if (more) {
+      la.store(nxt, ra);
+      lb.store(nxt + TILEB, rb);
+    }
+    __syncthreads();
+  }
+}
+
+// Accumulators -> staged C tile.  Output element of acc[mb][nb][v] in lane l:
+// row arow + 32 mb + 8 (v >> 2) + 4 (l >> 5) + (v & 3), column brow[nb] + (l & 31).
+MOE_DEV void stage_acc(float* C, const f32x16_t (&acc)[2][2], int arow, const int (&brow)[2],
+                       int lane) {
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = arow + 32 * mb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        C[cidx(row, brow[nb] + (lane & 31))] = acc[mb][nb][v];
+      }
+}
+
+MOE_DEV void read8(const float* C, int row, int col, float* f) {
+  const float4 a = *(const float4*)(C + cidx(row, col));
+  const float4 b = *(const float4*)(C + cidx(row, col) + 4);
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+// 8 values -> 8 elements of T at p (16-byte aligned)
+MOE_DEV void store8(bf16_t* p, const float* f) { *(uint4*)p = pack8(f); }
+MOE_DEV void store8(float* p, const float* f) {
+  *(float4*)p = make_float4(f[0], f[1], f[2], f[3]);
+  *(float4*)(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
+}
+MOE_DEV void load8(const bf16_t* p, float* f) { unpack8(*(const uint4*)p, f); }
+MOE_DEV void load8(const float* p, float* f) {
+  const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+// value as stored in T (bf16 rounds, fp32 is exact)
+MOE_DEV float as_stored(bf16_t, float v) { return bf16_to_f32(f32_to_bf16(v)); }
+MOE_DEV float as_stored(float, float v) { return v; }
+
+// Plain epilogue: the 128 x 128 tile to out_row(r) + n0 for valid rows.
+template <typename T, class RowPtr>
+MOE_DEV void epi_store(const float* C, const RowPtr& out_row, int n_valid_rows) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int r = (threadIdx.x >> 4) + 16 * s, c = threadIdx.x & 15;
+    if (r < n_valid_rows) {
+      float f[8];
+      read8(C, r, 8 * c, f);
+      store8(out_row(r) + 8 * c, f);
+    }
+  }
+}
+
+// --------------------------------------------------------------- tile decode
+struct RowTile {
+  int e, row0, row_end;
+};
+
+// Rows-grouped tile for blockIdx.y; false when past the last tile.
+MOE_DEV bool rows_tile(const GroupInfo& g, RowTile& t) {
+  const int mt = blockIdx.y;
+  if (g.tiles) {
+    if (mt >= g.n_tiles[0]) return false;
+    t.e = g.tiles[2 * mt];
+    t.row0 = g.tiles[2 * mt + 1];
+    t.row_end = min(t.row0 + TM, g.offsets[t.e + 1]);
+  } else {
+    t.e = 0;
+    t.row0 = mt * TM;
+    if (t.row0 >= g.dense_rows) return false;
+    t.row_end = min(t.row0 + TM, g.dense_rows);
+  }
+  return true;
+}
+
+MOE_DEV int token_of(const GroupInfo& g, int r) { return g.src_token ? g.src_token[r] : r; }
+
+MOE_DEV void wave_coords(int& arow, int (&brow)[2], bool swiglu) {
+  const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  arow = wm * 64;
+  if (swiglu) {
+    brow[0] = wn * 32;        // gate columns i0 + 32 wn ..
+    brow[1] = 64 + wn * 32;   // up columns, same i
+  } else {
+    brow[0] = wn * 64;
+    brow[1] = wn * 64 + 32;
+  }
+}
+
+// ------------------------------------------------------------------ kernels
+// GEMM1 + SwiGLU.  Tile n covers i in [64 n, 64 n + 64): B-tile rows 0..63 are
+// W_g[e] rows, 64..127 the W_u[e] rows of the same i.
+template <typename T>
+__global__ __launch_bounds__(NTHR, 2) void k_up_swiglu(GroupInfo g, const T* __restrict__ x,
+                                                       const T* __restrict__ wg,
+                                                       const T* __restrict__ wu, int H, int I,
+                                                       T* __restrict__ Z, T* __restrict__ hout) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  RowTile t;
+  if (!rows_tile(g, t)) return;
+  const int i0 = blockIdx.x * 64;
+  const size_t wofs = (size_t)t.e * I * H;
+  KLoad<T> la, lb;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int rr = (threadIdx.x >> 3) + 32 * s;
+    const int r = t.row0 + rr;
+    la.rp[s] = r < t.row_end ? x + (size_t)token_of(g, r) * H : nullptr;
+    lb.rp[s] = rr < 64 ? wg + wofs + (size_t)(i0 + rr) * H : wu + wofs + (size_t)(i0 + rr - 64) * H;
+  }
+  int arow, brow[2];
+  wave_coords(arow, brow, true);
+  const int lane = threadIdx.x & 63;
+  f32x16_t acc[2][2];
+  gemm_main<T>(lds, la, lb, H / Tr<T>::BK, acc, arow, brow, lane);
+  float* C = (float*)lds;
+  stage_acc(C, acc, arow, brow, lane);
+  __syncthreads();
+  const int nrows = t.row_end - t.row0;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int r = (threadIdx.x >> 3) + 32 * s, c = threadIdx.x & 7;
+    if (r < nrows) {
+      float a[8], b[8], h[8];
+      read8(C, r, 8 * c, a);
+      read8(C, r, 64 + 8 * c, b);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        a[q] = as_stored(T(), a[q]);
+        b[q] = as_stored(T(), b[q]);
+        h[q] = silu_f(a[q]) * b[q];
+      }
+      T* zr = Z + (size_t)(t.row0 + r) * (2 * I);
+      store8(zr + i0 + 8 * c, a);
+      store8(zr + I + i0 + 8 * c, b);
+      store8(hout + (size_t)(t.row0 + r) * I + i0 + 8 * c, h);
+    }
+  }
+}
+
+// GEMM2: Y[r, n] = sum_i h[r, i] W_d[e][n, i]
+template <typename T>
+__global__ __launch_bounds__(NTHR, 2) void k_down(GroupInfo g, const T* __restrict__ h,
+                                                  const T* __restrict__ wd, int H, int I,
+                                                  T* __restrict__ Y) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  RowTile t;
+  if (!rows_tile(g, t)) return;
+  const int n0 = blockIdx.x * TN;
+  const size_t wofs = (size_t)t.e * H * I;
+  KLoad<T> la, lb;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int rr = (threadIdx.x >> 3) + 32 * s;
+    const int r = t.row0 + rr;
+    la.rp[s] = r < t.row_end ? h + (size_t)r * I : nullptr;
+    lb.rp[s] = wd + wofs + (size_t)(n0 + rr) * I;
+  }
+  int arow, brow[2];
+  wave_coords(arow, brow, false);
+  const int lane = threadIdx.x & 63;
+  f32x16_t acc[2][2];
+  gemm_main<T>(lds, la, lb, I / Tr<T>::BK, acc, arow, brow, lane);
+  float* C = (float*)lds;
+  stage_acc(C, acc, arow, brow, lane);
+  __syncthreads();
+  auto out = [&](int r) { return Y + (size_t)(t.row0 + r) * H + n0; };
+  epi_store<T>(C, out, t.row_end - t.row0);
+}
+
+// K-row pointer of a plain row-major matrix: element (k, i) at base[k * ld + i]
+template <typename T>
+struct KRowPlain {
+  const T* base;
+  size_t ld;
+  MOE_DEV const T* operator()(int k) const { return base + (size_t)k * ld; }
+};
+
+// dgrad-down: dh'[r, i] = sum_n dy[tok(r), n] W_d[e][n, i]; epilogue: SwiGLU backward
+// and the router-weight-gradient partial of this tile's 128 columns.
+template <typename T>
+__global__ __launch_bounds__(NTHR, 2) void k_dgrad_down(GroupInfo g, const T* __restrict__ dy,
+                                                        const T* __restrict__ wd,
+                                                        const T* __restrict__ Z,
+                                                        const float* __restrict__ topk_w, int H,
+                                                        int I, int k, T* __restrict__ dZ,
+                                                        T* __restrict__ gh,
+                                                        float* __restrict__ dgp) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  RowTile t;
+  if (!rows_tile(g, t)) return;
+  const int i0 = blockIdx.x * TN;
+  KLoad<T> la;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int r = t.row0 + (threadIdx.x >> 3) + 32 * s;
+    la.rp[s] = r < t.row_end ? dy + (size_t)token_of(g, r) * H : nullptr;
+  }
+  MNLoad<T, KRowPlain<T>> lb{{wd + (size_t)t.e * H * I + i0, (size_t)I}};
+  int arow, brow[2];
+  wave_coords(arow, brow, false);
+  const int lane = threadIdx.x & 63;
+  f32x16_t acc[2][2];
+  gemm_main<T>(lds, la, lb, H / Tr<T>::BK, acc, arow, brow, lane);
+  float* C = (float*)lds;
+  stage_acc(C, acc, arow, brow, lane);
+  __syncthreads();
+  const int nrows = t.row_end - t.row0;
+  const int n_parts = I / TN;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int r = (threadIdx.x >> 4) + 16 * s, c = threadIdx.x & 15;
+    const bool ok = r < nrows;
+    float part = 0.0f;
+    if (ok) {
+      const int row = t.row0 + r;
+      const float gate = g.src_token ? topk_w[(size_t)g.src_token[row] * k + g.src_slot[row]] : 1.0f;
+      float d[8], a[8], b[8], da[8], db[8], gh8[8];
+      read8(C, r, 8 * c, d);
+      const T* zr = Z + (size_t)row * (2 * I);
+      load8(zr + i0 + 8 * c, a);
+      load8(zr + I + i0 + 8 * c, b);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float sg = 1.0f / (1.0f + expf(-a[q]));
+        const float sl = a[q] * sg;
+        const float hv = sl * b[q];
+        part = fmaf(d[q], hv, part);
+        const float dh = gate * d[q];
+        da[q] = dh * b[q] * (sg * (1.0f + a[q] * (1.0f - sg)));
+        db[q] = dh * sl;
+        gh8[q] = gate * hv;
+      }
+      T* dzr = dZ + (size_t)row * (2 * I);
+      store8(dzr + i0 + 8 * c, da);
+      store8(dzr + I + i0 + 8 * c, db);
+      store8(gh + (size_t)row * I + i0 + 8 * c, gh8);
+    }
+    // fixed-order sum over the 16 lanes holding this row's 128 columns
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
+    if (ok && c == 0 && dgp) dgp[(size_t)(t.row0 + r) * n_parts + blockIdx.x] = part;
+  }
+}
+
+// Weights of dgrad-up as one [2I, H] operand: rows < I from W_g[e], the rest W_u[e]
+template <typename T>
+struct KRowCat {
+  const T* wg;
+  const T* wu;
+  int I, H;
+  MOE_DEV const T* operator()(int k) const {
+    return k < I ? wg + (size_t)k * H : wu + (size_t)(k - I) * H;
+  }
+};
+
+// dgrad-up: dX[r, n] = sum_{k < 2I} dZ[r, k] Wcat[k, n]
+template <typename T>
+__global__ __launch_bounds__(NTHR, 2) void k_dgrad_up(GroupInfo g, const T* __restrict__ dZ,
+                                                      const T* __restrict__ wg,
+                                                      const T* __restrict__ wu, int H, int I,
+                                                      T* __restrict__ dX) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  RowTile t;
+  if (!rows_tile(g, t)) return;
+  const int n0 = blockIdx.x * TN;
+  const size_t wofs = (size_t)t.e * I * H + n0;
+  KLoad<T> la;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int r = t.row0 + (threadIdx.x >> 3) + 32 * s;
+    la.rp[s] = r < t.row_end ? dZ + (size_t)r * (2 * I) : nullptr;
+  }
+  MNLoad<T, KRowCat<T>> lb{{wg + wofs, wu + wofs, I, H}};
+  int arow, brow[2];
+  wave_coords(arow, brow, false);
+  const int lane = threadIdx.x & 63;
+  f32x16_t acc[2][2];
+  gemm_main<T>(lds, la, lb, (2 * I) / Tr<T>::BK, acc, arow, brow, lane);
+  float* C = (float*)lds;
+  stage_acc(C, acc, arow, brow, lane);
+  __syncthreads();
+  auto out = [&](int r) { return dX + (size_t)(t.row0 + r) * H + n0; };
+  epi_store<T>(C, out, t.row_end - t.row0);
+}
+
+// K rows of a K-grouped operand: segment row seg0 + k (valid below seg1) of a
+// row-major matrix, optionally gathered through src_token.
+template <typename T>
+struct KRowSeg {
+  const T* base;
+  const int32_t* gather;
+  size_t ld;
+  int seg0, seg1;
+  MOE_DEV const T* operator()(int k) const {
+    const int r = seg0 + k;
+    if (r >= seg1) return nullptr;
+    return base + (size_t)(gather ? gather[r] : r) * ld;
+  }
+};
+
+MOE_DEV void k_segment(const GroupInfo& g, int e, int& seg0, int& seg1) {
+  if (g.offsets) {
+    seg0 = g.offsets[e];
+    seg1 = g.offsets[e + 1];
+  } else {
+    seg0 = 0;
+    seg1 = g.dense_rows;
+  }
+}
+
+// wgrad-down: dW_d[e][m, n] = sum_r dy[tok(r), m] gh[r, n]  (M = H, N = I, K = rows of e)
+template <typename T>
+__global__ __launch_bounds__(NTHR, 2) void k_wgrad_down(GroupInfo g, const T* __restrict__ dy,
+                                                        const T* __restrict__ gh, int H, int I,
+                                                        T* __restrict__ dwd) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  const int n0 = blockIdx.x * TN, m0 = blockIdx.y * TM, e = blockIdx.z;
+  int seg0, seg1;
+  k_segment(g, e, seg0, seg1);
+  MNLoad<T, KRowSeg<T>> la{{dy + m0, g.src_token, (size_t)H, seg0, seg1}};
+  MNLoad<T, KRowSeg<T>> lb{{gh + n0, nullptr, (size_t)I, seg0, seg1}};
+  int arow, brow[2];
+  wave_coords(arow, brow, false);
+  const int lane = threadIdx.x & 63;
+  f32x16_t acc[2][2];
+  const int nk = (seg1 - seg0 + Tr<T>::BK - 1) / Tr<T>::BK;
+  gemm_main<T>(lds, la, lb, nk, acc, arow, brow, lane);
+  float* C = (float*)lds;
+  stage_acc(C, acc, arow, brow, lane);
+  __syncthreads();
+  T* base = dwd + (size_t)e * H * I + (size_t)m0 * I + n0;
+  auto out = [&](int r) { return base + (size_t)r * I; };
+  epi_store<T>(C, out, TM);
+}
+
+// wgrad-up: [dW_g; dW_u][e][m, n] = sum_r dZ[r, m] x[tok(r), n]  (M = 2I, N = H)
+template <typename T>
+__global__ __launch_bounds__(NTHR, 2) void k_wgrad_up(GroupInfo g, const T* __restrict__ dZ,
+                                                      const T* __restrict__ x, int H, int I,
+                                                      T* __restrict__ dwg, T* __restrict__ dwu) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  const int n0 = blockIdx.x * TN, m0 = blockIdx.y * TM, e = blockIdx.z;
+  int seg0, seg1;
+  k_segment(g, e, seg0, seg1);
+  MNLoad<T, KRowSeg<T>> la{{dZ + m0, nullptr, (size_t)(2 * I), seg0, seg1}};
+  MNLoad<T, KRowSeg<T>> lb{{x + n0, g.src_token, (size_t)H, seg0, seg1}};
+  int arow, brow[2];
+  wave_coords(arow, brow, false);
+  const int lane = threadIdx.x & 63;
+  f32x16_t acc[2][2];
+  const int nk = (seg1 - seg0 + Tr<T>::BK - 1) / Tr<T>::BK;
+  gemm_main<T>(lds, la, lb, nk, acc, arow, brow, lane);
+  float* C = (float*)lds;
+  stage_acc(C, acc, arow, brow, lane);
+  __syncthreads();
+  T* base = (m0 < I ? dwg + (size_t)e * I * H + (size_t)m0 * H
+                    : dwu + (size_t)e * I * H + (size_t)(m0 - I) * H) + n0;
+  auto out = [&](int r) { return base + (size_t)r * H; };
+  epi_store<T>(C, out, TM);
+}
+
+// ------------------------------------------------------------------ launchers
+static unsigned row_tiles(const GroupInfo& g) {
+  return g.tiles ? (unsigned)g.max_tiles : (unsigned)((g.dense_rows + TM - 1) / TM);
+}
+
+template <typename T>
+static hipError_t up_swiglu_t(const GroupInfo& g, const void* x, const void* wg, const void* wu,
+                              int H, int I, void* Z, void* h, hipStream_t s) {
+  const unsigned ty = row_tiles(g);
+  if (ty == 0) return hipSuccess;
+  return MOE_LAUNCH(g.tiles ? "gemm_up_swiglu" : "gemm_up_swiglu_shared", s,
+                    k_up_swiglu<T><<<dim3(I / 64, ty), NTHR, 0, s>>>(
+                        g, (const T*)x, (const T*)wg, (const T*)wu, H, I, (T*)Z, (T*)h));
+}
+
+template <typename T>
+static hipError_t down_t(const GroupInfo& g, const void* h, const void* wd, int H, int I, void* Y,
+                         hipStream_t s) {
+  const unsigned ty = row_tiles(g);
+  if (ty == 0) return hipSuccess;
+  return MOE_LAUNCH(g.tiles ? "gemm_down" : "gemm_down_shared", s,
+                    k_down<T><<<dim3(H / TN, ty), NTHR, 0, s>>>(g, (const T*)h, (const T*)wd, H,
+                                                                 I, (T*)Y));
+}
+
+template <typename T>
+static hipError_t dgrad_down_t(const GroupInfo& g, const void* dy, const void* wd, const void* Z,
+                               const float* topk_w, int H, int I, int k, void* dZ, void* gh,
+                               float* dgp, hipStream_t s) {
+  const unsigned ty = row_tiles(g);
+  if (ty == 0) return hipSuccess;
+  return MOE_LAUNCH(g.tiles ? "gemm_dgrad_down" : "gemm_dgrad_down_shared", s,
+                    k_dgrad_down<T><<<dim3(I / TN, ty), NTHR, 0, s>>>(
+                        g, (const T*)dy, (const T*)wd, (const T*)Z, topk_w, H, I, k, (T*)dZ,
+                        (T*)gh, dgp));
+}
+
+template <typename T>
+static hipError_t dgrad_up_t(const GroupInfo& g, const void* dZ, const void* wg, const void* wu,
+                             int H, int I, void* dX, hipStream_t s) {
+  const unsigned ty = row_tiles(g);
+  if (ty == 0) return hipSuccess;
+  return MOE_LAUNCH(g.tiles ? "gemm_dgrad_up" : "gemm_dgrad_up_shared", s,
+                    k_dgrad_up<T><<<dim3(H / TN, ty), NTHR, 0, s>>>(
+                        g, (const T*)dZ, (const T*)wg, (const T*)wu, H, I, (T*)dX));
+}
+
+template <typename T>
+static hipError_t wgrad_down_t(const GroupInfo& g, const void* dy, const void* gh, int H, int I,
+                               void* dwd, hipStream_t s) {
+  return MOE_LAUNCH(g.offsets ? "gemm_wgrad_down" : "gemm_wgrad_down_shared", s,
+                    k_wgrad_down<T><<<dim3(I / TN, H / TM, g.E), NTHR, 0, s>>>(
+                        g, (const T*)dy, (const T*)gh, H, I, (T*)dwd));
+}
+
+template <typename T>
+static hipError_t wgrad_up_t(const GroupInfo& g, const void* dZ, const void* x, int H, int I,
+                             void* dwg, void* dwu, hipStream_t s) {
+  return MOE_LAUNCH(g.offsets ? "gemm_wgrad_up" : "gemm_wgrad_up_shared", s,
+                    k_wgrad_up<T><<<dim3(H / TN, (2 * I) / TM, g.E), NTHR, 0, s>>>(
+                        g, (const T*)dZ, (const T*)x, H, I, (T*)dwg, (T*)dwu));
+}
+
+hipError_t launch_gemm_up_swiglu(int dt, const GroupInfo& g, const void* x, const void* wg,
+                                 const void* wu, int H, int I, void* Z, void* h, hipStream_t s) {
+  return dt ? up_swiglu_t<bf16_t>(g, x, wg, wu, H, I, Z, h, s)
+            : up_swiglu_t<float>(g, x, wg, wu, H, I, Z, h, s);
+}
+hipError_t launch_gemm_down(int dt, const GroupInfo& g, const void* h, const void* wd, int H,
+                            int I, void* Y, hipStream_t s) {
+  return dt ? down_t<bf16_t>(g, h, wd, H, I, Y, s) : down_t<float>(g, h, wd, H, I, Y, s);
+}
+hipError_t launch_gemm_dgrad_down(int dt, const GroupInfo& g, const void* dy, const void* wd,
+                                  const void* Z, const float* topk_w, int H, int I, int k,
+                                  void* dZ, void* gh, float* dgp, hipStream_t s) {
+  return dt ? dgrad_down_t<bf16_t>(g, dy, wd, Z, topk_w, H, I, k, dZ, gh, dgp, s)
+            : dgrad_down_t<float>(g, dy, wd, Z, topk_w, H, I, k, dZ, gh, dgp, s);
+}
+hipError_t launch_gemm_dgrad_up(int dt, const GroupInfo& g, const void* dZ, const void* wg,
+                                const void* wu, int H, int I, void* dX, hipStream_t s) {
+  return dt ? dgrad_up_t<bf16_t>(g, dZ, wg, wu, H, I, dX, s)
+            : dgrad_up_t<float>(g, dZ, wg, wu, H, I, dX, s);
+}
+hipError_t launch_gemm_wgrad_down(int dt, const GroupInfo& g, const void* dy, const void* gh,
+                                  int H, int I, void* dwd, hipStream_t s) {
+  return dt ? wgrad_down_t<bf16_t>(g, dy, gh, H, I, dwd, s)
+            : wgrad_down_t<float>(g, dy, gh, H, I, dwd, s);
+}
+hipError_t launch_gemm_wgrad_up(int dt, const GroupInfo& g, const void* dZ, const void* x,
+                                int H, int I, void* dwg, void* dwu, hipStream_t s) {
+  return dt ? wgrad_up_t<bf16_t>(g, dZ, x, H, I, dwg, dwu, s)
+            : wgrad_up_t<float>(g, dZ, x, H, I, dwg, dwu, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,100 @@
+// Launch functions of the gfx950 kernels, called by the C-ABI layer (api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define MOE_MAX_E 1024
+#define MOE_MAX_K 32
+
+struct moe_trace;
+
+namespace moe {
+
+// Optional per-thread kernel timing (moe_trace_set in the C-ABI).
+extern thread_local ::moe_trace* tls_trace;
+void trace_before(hipStream_t s, const char* name);
+void trace_after(hipStream_t s);
+
+// Enqueue one kernel launch between trace events; evaluates to hipGetLastError().
+#define MOE_LAUNCH(name, stream, ...)   \
+  (::moe::trace_before((stream), (name)), (__VA_ARGS__), ::moe::trace_after(stream), \
+   hipGetLastError())
+
+// plan construction
+constexpr int PLAN_CHUNK = 512;      // pairs per wavefront chunk
+constexpr int GEMM_TILE_M = 128;     // rows per grouped-GEMM tile (plan tile list)
+
+// router
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                        hipStream_t s);
+hipError_t launch_route_backward(const int32_t* idx, const float* w, const float* dw, int T,
+                                 int E, int k, float* dL, hipStream_t s);
+hipError_t launch_router_logits_f32(const float* x, const float* wr, int T, int H, int E,
+                                    float* logits, hipStream_t s);
+hipError_t launch_router_backward_f32(const float* x, const float* wr, const float* dL, int T,
+                                      int H, int E, float* dwr, float* dx, hipStream_t s);
+
+// plan
+struct PlanPtrs {
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* src_token;
+  int32_t* src_slot;
+  int32_t* pos;
+  int32_t* tiles;
+  int32_t* n_tiles;
+  int32_t* err_flag;
+  int32_t* chunk_hist;     // [n_chunks, E]
+  int32_t* chunk_invalid;  // [n_chunks]
+  int n_chunks;
+  int max_tiles;
+};
+hipError_t launch_plan(const int32_t* topk_idx, int T, int k, int E, const PlanPtrs& p,
+                       hipStream_t s);
+
+// row movement
+hipError_t launch_gather_rows(const void* src, void* dst, const int32_t* src_token,
+                              const int32_t* n_valid, int R, int row_bytes, hipStream_t s);
+hipError_t launch_combine_bf16(const void* Y, const int32_t* pos, const float* w,
+                               const void* shared, void* y, int T, int k, int H, hipStream_t s);
+hipError_t launch_combine_f32(const float* Y, const int32_t* pos, const float* w,
+                              const float* shared, float* y, int T, int k, int H, hipStream_t s);
+hipError_t launch_dg_reduce(const float* dgp, const int32_t* pos, int R, int n_parts,
+                            float* d_topk_w, hipStream_t s);
+
+// grouped GEMMs (gemm.hip); `dt` 0 = fp32, 1 = bf16
+struct GroupInfo {
+  const int32_t* tiles;      // rows-grouped: plan tile list (NULL: dense over dense_rows)
+  const int32_t* n_tiles;
+  const int32_t* offsets;    // expert row offsets [E+1] (NULL: dense)
+  const int32_t* src_token;  // token of each row (NULL: rows are tokens)
+  const int32_t* src_slot;
+  int max_tiles;             // grid bound for rows-grouped launches
+  int dense_rows;            // row count in dense mode
+  int E;
+};
+
+// GEMM1 + SwiGLU: Z[:, i] = A, Z[:, I + i] = B, h = silu(A) * B, with
+// A = X W_g[e]^T, B = X W_u[e]^T and X rows gathered from x through src_token.
+hipError_t launch_gemm_up_swiglu(int dt, const GroupInfo& g, const void* x, const void* wg,
+                                 const void* wu, int H, int I, void* Z, void* h, hipStream_t s);
+// GEMM2: Y = h W_d[e]^T
+hipError_t launch_gemm_down(int dt, const GroupInfo& g, const void* h, const void* wd, int H,
+                            int I, void* Y, hipStream_t s);
+// dgrad-down + SwiGLU backward + router-weight-gradient partials
+hipError_t launch_gemm_dgrad_down(int dt, const GroupInfo& g, const void* dy, const void* wd,
+                                  const void* Z, const float* topk_w, int H, int I, int k,
+                                  void* dZ, void* gh, float* dgp, hipStream_t s);
+// dgrad-up: dX = dZ[:, :I] W_g[e] + dZ[:, I:] W_u[e]
+hipError_t launch_gemm_dgrad_up(int dt, const GroupInfo& g, const void* dZ, const void* wg,
+                                const void* wu, int H, int I, void* dX, hipStream_t s);
+// wgrad-down: dW_d[e] = sum_r dy[src_token[r]] (x) gh[r]
+hipError_t launch_gemm_wgrad_down(int dt, const GroupInfo& g, const void* dy, const void* gh,
+                                  int H, int I, void* dwd, hipStream_t s);
+// wgrad-up: dW_g[e] = sum_r dZ[r, :I] (x) x[src_token[r]], dW_u[e] likewise with dZ[r, I:]
+hipError_t launch_gemm_wgrad_up(int dt, const GroupInfo& g, const void* dZ, const void* x,
+                                int H, int I, void* dwg, void* dwu, hipStream_t s);
+
+}  // namespace moe

@@ -286,11 +286,11 @@ def layer_backward(cache: dict, dy) -> dict:
     dWg, dWu, dWd = [], [], []
     for e in range(E):
         r0, r1 = int(off[e]), int(off[e + 1])
-        Wg_e, Wu_e, Wd_e = _f64(w_gate[e]), _f64(w_up[e]), _f64(w_down[e])
-        if r1 == r0:
-            dWg.append(np.zeros_like(Wg_e)); dWu.append(np.zeros_like(Wu_e))
-            dWd.append(np.zeros_like(Wd_e))
+        if r1 == r0:                         # no rows: zero gradients, weights not read
+            dWg.append(np.zeros(tuple(w_gate[e].shape))); dWu.append(np.zeros(tuple(w_up[e].shape)))
+            dWd.append(np.zeros(tuple(w_down[e].shape)))
             continue
+        Wg_e, Wu_e, Wd_e = _f64(w_gate[e]), _f64(w_up[e]), _f64(w_down[e])
         A, B, h = cache["A"][r0:r1], cache["B"][r0:r1], cache["h"][r0:r1]
         dhp = dYu[r0:r1] @ Wd_e
         dg_rows[r0:r1] = np.sum(dhp * h, axis=1)

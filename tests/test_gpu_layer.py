@@ -1,0 +1,202 @@
+"""GPU parity of the whole layer (forward and backward) against the fp64 oracle.
+
+Small shapes that span several tiles with ragged tails are compared element by
+element on every output; the full-size workloads are compared on sampled tokens,
+sampled weight-gradient slices and exact properties (plan, routing, zero
+gradients of empty experts, bitwise repeatability)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import digest, np_, say, shared_of, to_dev
+from synth import CONFIGS, Shape, make_inputs
+from tolerance import check
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "ragged_bf16": Shape(T=300, H=384, I=256, E=8, k=2),
+    "skew_shared_bf16": Shape(T=517, H=256, I=384, E=16, k=4, I_shared=256, zipf_s=1.2),
+    "dense_E1_bf16": Shape(T=129, H=256, I=128, E=1, k=1),
+    "k_eq_E_bf16": Shape(T=70, H=128, I=128, E=4, k=4),
+    "one_token_bf16": Shape(T=1, H=128, I=128, E=8, k=2, I_shared=128),
+    "hot_expert_bf16": Shape(T=700, H=256, I=256, E=32, k=2, zipf_s=4.0),
+    "tiny_f32": CONFIGS["tiny_f32"],
+    "ragged_f32": Shape(T=200, H=256, I=256, E=6, k=3, I_shared=128, dtype="f32"),
+}
+
+
+def gpu_run(shape: Shape, inp_dev: dict, backward=True):
+    from mixture_experts_layer_plan_amd import LayerBuffers, run_layer
+    b = LayerBuffers(shape.T, shape.H, shape.I, shape.E, shape.k, shape.I_shared,
+                     dtype=shape.dtype, backward=backward, router_gemm=shape.router == "gemm")
+    run_layer(b, inp_dev, backward=backward)
+    torch.cuda.synchronize()
+    return b
+
+
+def router_margin_ok(L, k):
+    """Top-k decisions of fp32 router logits can only be compared where the
+    k-th and (k+1)-th logits are further apart than the fp32 GEMM error."""
+    s = -np.sort(-L, axis=1)
+    if L.shape[1] == k:
+        return np.ones(L.shape[0], bool)
+    return (s[:, k - 1] - s[:, k]) > 1e-4
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_small_all_outputs(name):
+    shape = SMALL[name]
+    kind = shape.dtype
+    say(f"layer {name}: {shape}")
+    inp = make_inputs(shape, seed=0, device="cpu", with_dy=True)
+    b = gpu_run(shape, to_dev(inp))
+    c = oracle.layer_forward(inp["x"], inp.get("logits"), shape.k, inp["w_gate"], inp["w_up"],
+                             inp["w_down"], shared=shared_of(inp), w_router=inp.get("w_router"))
+    g = oracle.layer_backward(c, inp["dy"])
+    if shape.router == "gemm":
+        assert router_margin_ok(c["logits"], shape.k).all(), "seed has a near-tie in the router"
+        check(b.logits, c["logits"], kind, "logits")
+    np.testing.assert_array_equal(np_(b.topk_idx), c["topk_idx"])
+    check(b.topk_w, c["topk_w"], "f32" if kind == "f32" else "bf16", "topk_w")
+    pv = b.plan_views()
+    np.testing.assert_array_equal(np_(pv["src_token"]), c["plan"]["src_token"])
+    np.testing.assert_array_equal(np_(pv["pos"]), c["plan"]["pos"])
+    check(b.y, c["y"], kind, "y")
+    # saved Z = (A | B) of every routed row
+    R, I = shape.R, shape.I
+    Z = b.saved[: R * 2 * I * (4 if kind == "f32" else 2)].view(b.tdt).view(R, 2 * I)
+    check(Z[:, :I], c["A"], kind, "saved A")
+    check(Z[:, I:], c["B"], kind, "saved B")
+    check(b.dx, g["dx"], kind, "dx")
+    check(b.d_topk_w, g["dg"], kind, "d_topk_w")
+    check(b.d_logits, g["dlogits"], kind, "d_logits")
+    for e in range(shape.E):
+        for n in ("dw_gate", "dw_up", "dw_down"):
+            check(getattr(b, n)[e], g[n][e], kind, f"{n}[{e}]")
+    if shape.I_shared:
+        for n in ("ds_gate", "ds_up", "ds_down"):
+            check(getattr(b, n), g[n], kind, n)
+    if shape.router == "gemm":
+        check(b.dw_router, g["dw_router"], kind, "dw_router")
+
+
+def test_layer_bitwise_repeatable_and_buffer_independent():
+    shape = SMALL["skew_shared_bf16"]
+    say("determinism: 3 runs, 2 buffer sets")
+    inp = to_dev(make_inputs(shape, seed=1, device="cpu", with_dy=True))
+    outs = []
+    for rep in range(3):
+        b = gpu_run(shape, inp)
+        outs.append(digest(b.y, b.dx, b.dw_gate, b.dw_up, b.dw_down, b.ds_gate, b.ds_up, b.ds_down,
+                           b.d_topk_w, b.d_logits, b.topk_idx, b.topk_w))
+        del b
+    assert outs[0] == outs[1] == outs[2]
+
+
+# --------------------------------------------------------------- full sizes
+class ExpertCache:
+    """fp64 host copies of single experts of a device weight stack, on demand."""
+
+    def __init__(self, w):
+        self.w, self.c = w, {}
+
+    def __getitem__(self, e):
+        e = int(e)
+        if e not in self.c:
+            self.c[e] = self.w[e].to("cpu", torch.float64).numpy()
+        return self.c[e]
+
+
+def full_size(name, backward):
+    shape = CONFIGS[name]
+    say(f"full size {name}: generating inputs on the device")
+    inp = make_inputs(shape, seed=0, device="cuda", with_dy=backward)
+    say(f"full size {name}: running the layer")
+    b = gpu_run(shape, inp, backward=backward)
+    return shape, inp, b
+
+
+def sampled_tokens(T, n=8):
+    return np.unique(np.linspace(0, T - 1, n).astype(int))
+
+
+@pytest.mark.parametrize("name", ["mid_bf16_fwd", "kimi_bf16_fwd"])
+def test_full_size_forward_sampled(name):
+    shape, inp, b = full_size(name, backward=False)
+    L = np_(inp["logits"])
+    idx, w = oracle.route(L, shape.k)
+    np.testing.assert_array_equal(np_(b.topk_idx), idx)
+    ref_plan = oracle.build_plan(idx, shape.E)
+    pv = b.plan_views()
+    for key in ("counts", "offsets", "src_token", "src_slot", "pos"):
+        np.testing.assert_array_equal(np_(pv[key]), ref_plan[key], err_msg=key)
+    Wg, Wu, Wd = ExpertCache(inp["w_gate"]), ExpertCache(inp["w_up"]), ExpertCache(inp["w_down"])
+    toks = sampled_tokens(shape.T)
+    got = np_(b.y.double())[toks]
+    ref = np.stack([oracle.token_forward(inp["x"][t], idx[t], w[t], Wg, Wu, Wd) for t in toks])
+    check(got, ref, "bf16", f"{name} y (sampled tokens)")
+
+
+def test_full_size_forward_backward_sampled():
+    name = "kimi_bf16_fwdbwd"
+    shape, inp, b = full_size(name, backward=True)
+    L = np_(inp["logits"])
+    idx, w = oracle.route(L, shape.k)
+    np.testing.assert_array_equal(np_(b.topk_idx), idx)
+    plan = oracle.build_plan(idx, shape.E)
+    pv = b.plan_views()
+    for key in ("counts", "offsets", "src_token", "src_slot", "pos"):
+        np.testing.assert_array_equal(np_(pv[key]), plan[key], err_msg=key)
+    Wg, Wu, Wd = ExpertCache(inp["w_gate"]), ExpertCache(inp["w_up"]), ExpertCache(inp["w_down"])
+    sh = shared_of(inp)
+    toks = sampled_tokens(shape.T, 6)
+    say(f"{name}: oracle on {len(toks)} sampled tokens")
+    y_ref, dx_ref, dg_ref, dl_ref = [], [], [], []
+    for t in toks:
+        y_ref.append(oracle.token_forward(inp["x"][t], idx[t], w[t], Wg, Wu, Wd, shared=sh))
+        dx_t, dg_t = oracle.token_backward(inp["x"][t], idx[t], w[t], inp["dy"][t], Wg, Wu, Wd,
+                                           shared=sh)
+        dx_ref.append(dx_t)
+        dg_ref.append(dg_t)
+        dl_ref.append(oracle.route_backward(idx[t:t + 1], w[t:t + 1], dg_t[None], shape.E)[0])
+    check(np_(b.y.double())[toks], np.stack(y_ref), "bf16", "y (sampled)")
+    check(np_(b.dx.double())[toks], np.stack(dx_ref), "bf16", "dx (sampled)")
+    check(np_(b.d_topk_w)[toks], np.stack(dg_ref), "bf16", "d_topk_w (sampled)")
+    check(np_(b.d_logits)[toks], np.stack(dl_ref), "bf16", "d_logits (sampled)")
+    # weight-gradient slices of a hot, a median, a single-row and an empty expert
+    counts = plan["counts"]
+    order = np.argsort(-counts, kind="stable")
+    picks = [int(order[0]), int(order[len(order) // 4])]
+    ones = np.nonzero(counts == 1)[0]
+    zeros = np.nonzero(counts == 0)[0]
+    picks += [int(ones[0])] if len(ones) else []
+    cols = [0, 777, shape.I - 1]
+    x64 = inp["x"]
+    for e in picks:
+        seg = slice(plan["offsets"][e], plan["offsets"][e + 1])
+        tok, slot = plan["src_token"][seg], plan["src_slot"][seg]
+        say(f"{name}: dW slices of expert {e} ({counts[e]} rows)")
+        ti = torch.as_tensor(tok, device="cuda")
+        dg_, du_, dd_ = oracle.expert_weight_grad_slices(
+            x64[ti], inp["dy"][ti], w[tok, slot], Wg[e], Wu[e], Wd[e], cols)
+        check(np_(b.dw_gate[e].double())[cols], dg_, "bf16", f"dw_gate[{e}] rows")
+        check(np_(b.dw_up[e].double())[cols], du_, "bf16", f"dw_up[{e}] rows")
+        check(np_(b.dw_down[e].double())[:, cols], dd_, "bf16", f"dw_down[{e}] cols")
+    for e in zeros[:3]:
+        assert not b.dw_gate[int(e)].any() and not b.dw_up[int(e)].any() and not b.dw_down[int(e)].any()
+    say(f"{name}: shared-expert gradient slices")
+    ones_g = np.ones(shape.T)
+    sg_, su_, sd_ = oracle.expert_weight_grad_slices(x64, inp["dy"], ones_g, sh[0], sh[1], sh[2],
+                                                     cols)
+    check(np_(b.ds_gate.double())[cols], sg_, "bf16", "ds_gate rows")
+    check(np_(b.ds_up.double())[cols], su_, "bf16", "ds_up rows")
+    check(np_(b.ds_down.double())[:, cols], sd_, "bf16", "ds_down cols")
+    # bitwise repeatability at full size
+    say(f"{name}: repeat for bitwise equality")
+    d1 = digest(b.y, b.dx, b.d_topk_w, b.dw_gate, b.dw_down)
+    from mixture_experts_layer_plan_amd import run_layer
+    run_layer(b, inp, backward=True)
+    torch.cuda.synchronize()
+    assert digest(b.y, b.dx, b.d_topk_w, b.dw_gate, b.dw_down) == d1

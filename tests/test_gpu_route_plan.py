@@ -1,0 +1,138 @@
+"""GPU parity of the router and the schedule table: bit-exact against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import np_, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    from mixture_experts_layer_plan_amd import binding
+    return binding
+
+
+def run_route(B, L, k):
+    T, E = L.shape
+    s = B.shape(T, 128, 128, E, k)
+    Ld = torch.as_tensor(L, dtype=torch.float32).cuda()
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    B.moe_route(s, Ld, idx, w)
+    torch.cuda.synchronize()
+    return np_(idx), np_(w)
+
+
+@pytest.mark.parametrize("T,E,k,kind", [(1, 4, 1, "n"), (37, 8, 2, "n"), (300, 64, 6, "n"),
+                                        (129, 256, 8, "zipf"), (70, 1024, 32, "n"),
+                                        (200, 16, 16, "int"), (65, 5, 3, "int"), (33, 1000, 7, "n")])
+def test_route_bitexact(B, T, E, k, kind):
+    say(f"route T={T} E={E} k={k} {kind}")
+    rng = np.random.default_rng(T * 7 + E)
+    if kind == "int":
+        L = rng.integers(-2, 3, size=(T, E)).astype(np.float32)   # heavy ties
+        L[L == 0] = np.where(rng.random((L == 0).sum()) < 0.5, -0.0, 0.0)
+    else:
+        L = rng.standard_normal((T, E)).astype(np.float32)
+        if kind == "zipf":
+            L += (-1.2 * np.log(rng.permutation(E) + 1.0)).astype(np.float32)
+    idx, w = run_route(B, L, k)
+    ridx, rw = oracle.route(L, k)
+    np.testing.assert_array_equal(idx, ridx)
+    np.testing.assert_allclose(w, rw, rtol=2e-6, atol=1e-7)
+
+
+def build_plan(B, idx, E):
+    T, k = idx.shape
+    s = B.shape(T, 128, 128, E, k)
+    plan = torch.empty(max(B.moe_plan_bytes(s), 1), dtype=torch.uint8, device="cuda")
+    d_idx = torch.as_tensor(idx, dtype=torch.int32).cuda()
+    B.moe_plan(s, d_idx, plan)
+    torch.cuda.synchronize()
+    v = B.plan_views(s, plan)
+    return {n: (np_(t) if isinstance(t, torch.Tensor) else t) for n, t in v.items()}, plan
+
+
+def check_plan(B, idx, E):
+    idx = np.asarray(idx, dtype=np.int32)
+    got, _ = build_plan(B, idx, E)
+    ref = oracle.build_plan(idx, E)
+    for n in ("counts", "offsets", "src_token", "src_slot", "pos"):
+        np.testing.assert_array_equal(got[n], ref[n], err_msg=n)
+    tl = oracle.tile_list(ref["counts"], ref["offsets"], got["tile_m"])
+    assert got["n_tiles"][0] == len(tl)
+    np.testing.assert_array_equal(got["tiles"][:len(tl)], tl)
+    assert got["err_flag"][0] == int(ref["err"])
+    return got
+
+
+def rand_idx(rng, T, E, k, skew=0.0):
+    if skew:
+        L = rng.standard_normal((T, E)) - skew * np.log(rng.permutation(E) + 1.0)
+    else:
+        L = rng.standard_normal((T, E))
+    return oracle.route(L, k)[0]
+
+
+@pytest.mark.parametrize("T,E,k,skew", [(1, 4, 1, 0), (16, 4, 2, 0), (300, 8, 2, 0),
+                                        (517, 16, 4, 1.2), (1000, 64, 6, 0), (2048, 256, 8, 1.1),
+                                        (4096, 256, 8, 1.2), (777, 1024, 3, 0), (64, 8, 8, 0)])
+def test_plan_bitexact(B, T, E, k, skew):
+    say(f"plan T={T} E={E} k={k} skew={skew}")
+    rng = np.random.default_rng(T + E + k)
+    check_plan(B, rand_idx(rng, T, E, k, skew), E)
+
+
+def test_plan_all_tokens_on_same_experts(B):
+    say("plan degenerate: every token on experts 5,2,7")
+    idx = np.tile(np.array([[5, 2, 7]], dtype=np.int32), (1500, 1))
+    got = check_plan(B, idx, 9)
+    assert got["counts"][5] == 1500 and got["counts"][0] == 0
+
+
+def test_plan_exhaustive_small_routings(B):
+    """All 12^3 ordered routings of T=3 tokens onto E=4 experts with k=2, in one launch
+    each would be slow; instead the 1728 routings are stacked as independent T=3
+    problems and checked one by one on a sample, plus the stacked whole."""
+    say("plan exhaustive T=3 E=4 k=2 (stacked)")
+    import itertools
+    choices = list(itertools.permutations(range(4), 2))
+    rows = [np.array(r) for r in itertools.product(choices, repeat=3)]
+    stacked = np.concatenate(rows).astype(np.int32)       # 5184 tokens
+    check_plan(B, stacked, 4)
+    for r in rows[::97]:
+        check_plan(B, r.astype(np.int32), 4)
+
+
+def test_plan_invalid_ids_set_flag(B):
+    say("plan with out-of-range expert ids")
+    idx = np.array([[0, 5], [-1, 1], [1, 0], [2, 2000]], dtype=np.int32)
+    got = check_plan(B, idx, 3)
+    assert got["err_flag"][0] == 1
+    np.testing.assert_array_equal(got["pos"], [[0, -1], [-1, 2], [3, 1], [4, -1]])
+
+
+def test_plan_empty_batch(B):
+    say("plan T=0")
+    s = B.shape(0, 128, 128, 8, 2)
+    plan = torch.full((B.moe_plan_bytes(s),), 0x7f, dtype=torch.uint8, device="cuda")
+    B.moe_plan(s, torch.empty((0, 2), dtype=torch.int32, device="cuda"), plan)
+    torch.cuda.synchronize()
+    v = B.plan_views(s, plan)
+    assert int(v["n_tiles"][0]) == 0 and int(v["err_flag"][0]) == 0
+    assert np.all(np_(v["counts"]) == 0) and np.all(np_(v["offsets"]) == 0)
+
+
+def test_plan_is_deterministic(B):
+    say("plan determinism")
+    rng = np.random.default_rng(3)
+    idx = rand_idx(rng, 3000, 128, 8, 1.2)
+    a, _ = build_plan(B, idx, 128)
+    b, _ = build_plan(B, idx, 128)
+    n = int(a["n_tiles"][0])
+    for key in ("counts", "offsets", "src_token", "src_slot", "pos", "n_tiles", "err_flag"):
+        np.testing.assert_array_equal(a[key], b[key])
+    np.testing.assert_array_equal(a["tiles"][:n], b["tiles"][:n])
