@@ -24,7 +24,9 @@
  *    [E, out, in] (nn.Linear layout): w_gate, w_up [E, I, H]; w_down [E, H, I].
  *    Shared-expert weights: s_gate, s_up [I_shared, H]; s_down [H, I_shared].
  *  - "bf16" data is passed as `void*` (IEEE bfloat16, 2 bytes), fp32 as float*.
- *  - Every pointer must be 16-byte aligned.
+ *  - Every pointer must be 16-byte aligned.  With T == 0, arrays whose size is a
+ *    multiple of T may be NULL (weights, weight gradients and the plan may not;
+ *    the backward still overwrites the weight gradients with zeros).
  *  - Arguments are checked on the host before anything is enqueued; a failed
  *    check returns a status other than MOE_OK and enqueues nothing.
  *  - A data error that only the device can see (an expert id outside [0, E))
@@ -111,8 +113,10 @@ moe_status moe_plan_layout_of(const moe_shape* shape, moe_plan_layout* out);
 size_t moe_plan_bytes(const moe_shape* shape);
 
 /* Bytes of activations the forward keeps for the backward (`saved`):
- * Z = (A | B) bf16/f32 [T*k, 2I] (gate and up pre-activations of every routed
- * row) followed by Zs [T, 2*I_shared] for the shared expert. */
+ * Z = (A | B) fp32 [T*k, 2I] (gate and up pre-activations of every routed row)
+ * followed by Zs fp32 [T, 2*I_shared] for the shared expert.  They stay fp32 in
+ * every variant: the SwiGLU backward multiplies by silu'(A), which magnifies a
+ * rounding of A near its zero. */
 size_t moe_saved_bytes(const moe_shape* shape, moe_dtype dtype);
 
 /* Scratch bytes of moe_forward_* (backward = 0) or moe_backward_* (backward = 1). */
@@ -206,8 +210,8 @@ moe_status moe_reverse_dispatch_bf16(const moe_shape* shape, const void* plan, c
  *   h = silu(A) * B, Y_r = h W_d[e]^T, with X_r = x[src_token[r]] gathered in the
  *   GEMM loader; shared expert S(x) = (silu(x S_g^T) * (x S_u^T)) S_d^T;
  *   y = combine(Y) + S(x) as in moe_combine_bf16.
- * bf16 operands, fp32 accumulation; A, B, h and Y are rounded to bf16, h is
- * computed from the rounded A and B.
+ * bf16 operands, fp32 accumulation; A and B are kept in fp32 (`saved`), h is
+ * formed from them in fp32 and rounded to bf16, as is Y.
  *   plan   from moe_plan on the same topk_idx
  *   x [T, H], topk_w fp32 [T, k], weights as in the conventions
  *   s_gate, s_up, s_down: NULL when shape->I_shared == 0

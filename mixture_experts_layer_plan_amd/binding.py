@@ -270,9 +270,11 @@ class KernelTrace:
         h = _hiprt()
         self.capacity = capacity
         self._events = (ctypes.c_void_p * (2 * capacity))()
+        ev = ctypes.c_void_p()
         for i in range(2 * capacity):
-            if h.hipEventCreate(ctypes.byref(self._events, i * ctypes.sizeof(ctypes.c_void_p))) != 0:
+            if h.hipEventCreate(ctypes.byref(ev)) != 0:
                 raise RuntimeError("hipEventCreate failed")
+            self._events[i] = ev.value
         self._names = (ctypes.c_char_p * capacity)()
         self.t = moe_trace(ctypes.cast(self._events, ctypes.POINTER(ctypes.c_void_p)),
                            ctypes.cast(self._names, ctypes.POINTER(ctypes.c_char_p)),

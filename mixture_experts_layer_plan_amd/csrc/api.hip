@@ -134,16 +134,16 @@ GroupInfo dense(int rows) {
 
 size_t esize(moe_dtype dt) { return dt == MOE_F32 ? 4 : 2; }
 
-// saved: Z [R, 2I] then Zs [T, 2 Is]
+// saved: Z fp32 [R, 2I] then Zs fp32 [T, 2 Is] (gate | up pre-activations)
 struct SavedLayout {
   size_t Z, Zs, total;
 };
-SavedLayout saved_layout(const moe_shape* s, moe_dtype dt) {
-  const size_t R = (size_t)s->T * s->k, es = esize(dt);
+SavedLayout saved_layout(const moe_shape* s, moe_dtype) {
+  const size_t R = (size_t)s->T * s->k;
   Carve c;
   SavedLayout L;
-  L.Z = c.take(R * 2 * s->I * es);
-  L.Zs = c.take((size_t)s->T * 2 * s->I_shared * es);
+  L.Z = c.take(R * 2 * s->I * sizeof(float));
+  L.Zs = c.take((size_t)s->T * 2 * s->I_shared * sizeof(float));
   L.total = c.off;
   return L;
 }
@@ -204,6 +204,11 @@ bool any_null(std::initializer_list<const void*> ps) {
   return false;
 }
 
+// Arrays whose size is a multiple of T may be NULL when T == 0.
+bool any_null_rows(const moe_shape* s, std::initializer_list<const void*> ps) {
+  return s->T > 0 && any_null(ps);
+}
+
 moe_status forward_impl(moe_dtype dt, const moe_shape* s, const void* plan, const void* x,
                         const float* topk_w, const void* wg, const void* wu, const void* wd,
                         const void* sg, const void* su, const void* sd, void* y, void* saved,
@@ -211,7 +216,8 @@ moe_status forward_impl(moe_dtype dt, const moe_shape* s, const void* plan, cons
   moe_status rc = check_shape(s, true);
   if (rc != MOE_OK) return rc;
   if (s->T_minibatch != 0 && s->T_minibatch != s->T) return MOE_E_UNSUPPORTED;
-  if (any_null({plan, x, topk_w, wg, wu, wd, y, saved}) || (s->T > 0 && !ws)) return MOE_E_NULL;
+  if (any_null({plan, wg, wu, wd}) || any_null_rows(s, {x, topk_w, y, saved, ws}))
+    return MOE_E_NULL;
   if (s->I_shared && any_null({sg, su, sd})) return MOE_E_NULL;
   if (!all_aligned({plan, x, topk_w, wg, wu, wd, sg, su, sd, y, saved, ws})) return MOE_E_ALIGN;
   const FwdWs W = fwd_ws(s, dt);
@@ -252,8 +258,8 @@ moe_status backward_impl(moe_dtype dt, const moe_shape* s, const void* plan, con
   moe_status rc = check_shape(s, true);
   if (rc != MOE_OK) return rc;
   if (s->T_minibatch != 0 && s->T_minibatch != s->T) return MOE_E_UNSUPPORTED;
-  if (any_null({plan, x, topk_w, wg, wu, wd, saved, dy, dx, dwg, dwu, dwd, d_topk_w}) ||
-      (s->T > 0 && !ws))
+  if (any_null({plan, wg, wu, wd, dwg, dwu, dwd}) ||
+      any_null_rows(s, {x, topk_w, saved, dy, dx, d_topk_w, ws}))
     return MOE_E_NULL;
   if (s->I_shared && any_null({sg, su, sd, dsg, dsu, dsd})) return MOE_E_NULL;
   if (!all_aligned({plan, x, topk_w, wg, wu, wd, sg, su, sd, saved, dy, dx, dwg, dwu, dwd, dsg, dsu,
@@ -344,7 +350,7 @@ moe_status moe_router_logits_f32(const moe_shape* s, const float* x, const float
                                  float* logits, hipStream_t st) {
   moe_status rc = check_shape(s, false);
   if (rc != MOE_OK) return rc;
-  if (any_null({x, w_router, logits})) return MOE_E_NULL;
+  if (!w_router || any_null_rows(s, {x, logits})) return MOE_E_NULL;
   if (!all_aligned({x, w_router, logits})) return MOE_E_ALIGN;
   return hip_status(launch_router_logits_f32(x, w_router, s->T, s->H, s->E, logits, st));
 }
@@ -353,7 +359,7 @@ moe_status moe_route(const moe_shape* s, const float* logits, int32_t* topk_idx,
                      hipStream_t st) {
   moe_status rc = check_shape(s, false);
   if (rc != MOE_OK) return rc;
-  if (any_null({logits, topk_idx, topk_w})) return MOE_E_NULL;
+  if (any_null_rows(s, {logits, topk_idx, topk_w})) return MOE_E_NULL;
   if (!all_aligned({logits, topk_idx, topk_w})) return MOE_E_ALIGN;
   return hip_status(launch_route(logits, s->T, s->E, s->k, topk_idx, topk_w, st));
 }
@@ -362,7 +368,7 @@ moe_status moe_route_backward(const moe_shape* s, const int32_t* topk_idx, const
                               const float* d_topk_w, float* d_logits, hipStream_t st) {
   moe_status rc = check_shape(s, false);
   if (rc != MOE_OK) return rc;
-  if (any_null({topk_idx, topk_w, d_topk_w, d_logits})) return MOE_E_NULL;
+  if (any_null_rows(s, {topk_idx, topk_w, d_topk_w, d_logits})) return MOE_E_NULL;
   if (!all_aligned({topk_idx, topk_w, d_topk_w, d_logits})) return MOE_E_ALIGN;
   return hip_status(
       launch_route_backward(topk_idx, topk_w, d_topk_w, s->T, s->E, s->k, d_logits, st));
@@ -373,7 +379,7 @@ moe_status moe_router_backward_f32(const moe_shape* s, const float* x, const flo
                                    hipStream_t st) {
   moe_status rc = check_shape(s, false);
   if (rc != MOE_OK) return rc;
-  if (any_null({x, w_router, d_logits, dw_router, dx})) return MOE_E_NULL;
+  if (any_null({w_router, dw_router}) || any_null_rows(s, {x, d_logits, dx})) return MOE_E_NULL;
   if (!all_aligned({x, w_router, d_logits, dw_router, dx})) return MOE_E_ALIGN;
   return hip_status(
       launch_router_backward_f32(x, w_router, d_logits, s->T, s->H, s->E, dw_router, dx, st));
@@ -382,7 +388,7 @@ moe_status moe_router_backward_f32(const moe_shape* s, const float* x, const flo
 moe_status moe_plan(const moe_shape* s, const int32_t* topk_idx, void* plan, hipStream_t st) {
   moe_status rc = check_shape(s, false);
   if (rc != MOE_OK) return rc;
-  if (any_null({topk_idx, plan})) return MOE_E_NULL;
+  if (!plan || any_null_rows(s, {topk_idx})) return MOE_E_NULL;
   if (!all_aligned({topk_idx, plan})) return MOE_E_ALIGN;
   const moe_plan_layout L = plan_layout(s);
   PlanPtrs p;
@@ -405,7 +411,7 @@ static moe_status gather_impl(const moe_shape* s, const void* plan, const void* 
                               size_t es, hipStream_t st) {
   moe_status rc = check_shape(s, false);
   if (rc != MOE_OK) return rc;
-  if (any_null({plan, src, dst})) return MOE_E_NULL;
+  if (!plan || any_null_rows(s, {src, dst})) return MOE_E_NULL;
   if (!all_aligned({plan, src, dst})) return MOE_E_ALIGN;
   const PlanView v = view_plan(s, plan);
   return hip_status(launch_gather_rows(src, dst, v.src_token, v.offsets + s->E, s->T * s->k,
@@ -430,7 +436,7 @@ moe_status moe_combine_bf16(const moe_shape* s, const void* plan, const void* Y,
                             hipStream_t st) {
   moe_status rc = check_shape(s, false);
   if (rc != MOE_OK) return rc;
-  if (any_null({plan, Y, topk_w, y})) return MOE_E_NULL;
+  if (!plan || any_null_rows(s, {Y, topk_w, y})) return MOE_E_NULL;
   if (!all_aligned({plan, Y, topk_w, shared_out, y})) return MOE_E_ALIGN;
   const PlanView v = view_plan(s, plan);
   return hip_status(launch_combine_bf16(Y, v.pos, topk_w, shared_out, y, s->T, s->k, s->H, st));
@@ -441,7 +447,7 @@ moe_status moe_combine_f32(const moe_shape* s, const void* plan, const float* Y,
                            hipStream_t st) {
   moe_status rc = check_shape(s, false);
   if (rc != MOE_OK) return rc;
-  if (any_null({plan, Y, topk_w, y})) return MOE_E_NULL;
+  if (!plan || any_null_rows(s, {Y, topk_w, y})) return MOE_E_NULL;
   if (!all_aligned({plan, Y, topk_w, shared_out, y})) return MOE_E_ALIGN;
   const PlanView v = view_plan(s, plan);
   return hip_status(launch_combine_f32(Y, v.pos, topk_w, shared_out, y, s->T, s->k, s->H, st));
@@ -451,7 +457,7 @@ moe_status moe_reverse_dispatch_bf16(const moe_shape* s, const void* plan, const
                                      const void* shared_dx, void* dx, hipStream_t st) {
   moe_status rc = check_shape(s, false);
   if (rc != MOE_OK) return rc;
-  if (any_null({plan, dX, dx})) return MOE_E_NULL;
+  if (!plan || any_null_rows(s, {dX, dx})) return MOE_E_NULL;
   if (!all_aligned({plan, dX, shared_dx, dx})) return MOE_E_ALIGN;
   const PlanView v = view_plan(s, plan);
   return hip_status(launch_combine_bf16(dX, v.pos, nullptr, shared_dx, dx, s->T, s->k, s->H, st));

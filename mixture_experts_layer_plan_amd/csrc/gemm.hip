@@ -234,9 +234,6 @@ MOE_DEV void load8(const float* p, float* f) {
   const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
   f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
-// value as stored in T (bf16 rounds, fp32 is exact)
-MOE_DEV float as_stored(bf16_t, float v) { return bf16_to_f32(f32_to_bf16(v)); }
-MOE_DEV float as_stored(float, float v) { return v; }
 
 // Plain epilogue: the 128 x 128 tile to out_row(r) + n0 for valid rows.
 template <typename T, class RowPtr>
@@ -290,12 +287,14 @@ MOE_DEV void wave_coords(int& arow, int (&brow)[2], bool swiglu) {
 
 // ------------------------------------------------------------------ kernels
 // GEMM1 + SwiGLU.  Tile n covers i in [64 n, 64 n + 64): B-tile rows 0..63 are
-// W_g[e] rows, 64..127 the W_u[e] rows of the same i.
+// W_g[e] rows, 64..127 the W_u[e] rows of the same i.  The pre-activations A and B
+// are kept in fp32 (Z) for the backward; h = silu(A) * B is formed from them in
+// fp32 and rounded once to T.
 template <typename T>
 __global__ __launch_bounds__(NTHR, 2) void k_up_swiglu(GroupInfo g, const T* __restrict__ x,
                                                        const T* __restrict__ wg,
                                                        const T* __restrict__ wu, int H, int I,
-                                                       T* __restrict__ Z, T* __restrict__ hout) {
+                                                       float* __restrict__ Z, T* __restrict__ hout) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   RowTile t;
   if (!rows_tile(g, t)) return;
@@ -326,12 +325,8 @@ __global__ __launch_bounds__(NTHR, 2) void k_up_swiglu(GroupInfo g, const T* __r
       read8(C, r, 8 * c, a);
       read8(C, r, 64 + 8 * c, b);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        a[q] = as_stored(T(), a[q]);
-        b[q] = as_stored(T(), b[q]);
-        h[q] = silu_f(a[q]) * b[q];
-      }
-      T* zr = Z + (size_t)(t.row0 + r) * (2 * I);
+      for (int q = 0; q < 8; ++q) h[q] = silu_f(a[q]) * b[q];
+      float* zr = Z + (size_t)(t.row0 + r) * (2 * I);
       store8(zr + i0 + 8 * c, a);
       store8(zr + I + i0 + 8 * c, b);
       store8(hout + (size_t)(t.row0 + r) * I + i0 + 8 * c, h);
@@ -382,7 +377,7 @@ struct KRowPlain {
 template <typename T>
 __global__ __launch_bounds__(NTHR, 2) void k_dgrad_down(GroupInfo g, const T* __restrict__ dy,
                                                         const T* __restrict__ wd,
-                                                        const T* __restrict__ Z,
+                                                        const float* __restrict__ Z,
                                                         const float* __restrict__ topk_w, int H,
                                                         int I, int k, T* __restrict__ dZ,
                                                         T* __restrict__ gh,
@@ -418,7 +413,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_dgrad_down(GroupInfo g, const T* __
       const float gate = g.src_token ? topk_w[(size_t)g.src_token[row] * k + g.src_slot[row]] : 1.0f;
       float d[8], a[8], b[8], da[8], db[8], gh8[8];
       read8(C, r, 8 * c, d);
-      const T* zr = Z + (size_t)row * (2 * I);
+      const float* zr = Z + (size_t)row * (2 * I);
       load8(zr + i0 + 8 * c, a);
       load8(zr + I + i0 + 8 * c, b);
 #pragma unroll
@@ -573,7 +568,7 @@ static hipError_t up_swiglu_t(const GroupInfo& g, const void* x, const void* wg,
   if (ty == 0) return hipSuccess;
   return MOE_LAUNCH(g.tiles ? "gemm_up_swiglu" : "gemm_up_swiglu_shared", s,
                     k_up_swiglu<T><<<dim3(I / 64, ty), NTHR, 0, s>>>(
-                        g, (const T*)x, (const T*)wg, (const T*)wu, H, I, (T*)Z, (T*)h));
+                        g, (const T*)x, (const T*)wg, (const T*)wu, H, I, (float*)Z, (T*)h));
 }
 
 template <typename T>
@@ -594,7 +589,7 @@ static hipError_t dgrad_down_t(const GroupInfo& g, const void* dy, const void* w
   if (ty == 0) return hipSuccess;
   return MOE_LAUNCH(g.tiles ? "gemm_dgrad_down" : "gemm_dgrad_down_shared", s,
                     k_dgrad_down<T><<<dim3(I / TN, ty), NTHR, 0, s>>>(
-                        g, (const T*)dy, (const T*)wd, (const T*)Z, topk_w, H, I, k, (T*)dZ,
+                        g, (const T*)dy, (const T*)wd, (const float*)Z, topk_w, H, I, k, (T*)dZ,
                         (T*)gh, dgp));
 }
 

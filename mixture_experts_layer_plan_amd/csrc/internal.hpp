@@ -76,7 +76,7 @@ struct GroupInfo {
   int E;
 };
 
-// GEMM1 + SwiGLU: Z[:, i] = A, Z[:, I + i] = B, h = silu(A) * B, with
+// GEMM1 + SwiGLU: Z (fp32) [:, i] = A, Z[:, I + i] = B, h = silu(A) * B, with
 // A = X W_g[e]^T, B = X W_u[e]^T and X rows gathered from x through src_token.
 hipError_t launch_gemm_up_swiglu(int dt, const GroupInfo& g, const void* x, const void* wg,
                                  const void* wu, int H, int I, void* Z, void* h, hipStream_t s);

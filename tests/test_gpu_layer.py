@@ -66,7 +66,7 @@ def test_layer_small_all_outputs(name):
     check(b.y, c["y"], kind, "y")
     # saved Z = (A | B) of every routed row
     R, I = shape.R, shape.I
-    Z = b.saved[: R * 2 * I * (4 if kind == "f32" else 2)].view(b.tdt).view(R, 2 * I)
+    Z = b.saved[: R * 2 * I * 4].view(torch.float32).view(R, 2 * I)
     check(Z[:, :I], c["A"], kind, "saved A")
     check(Z[:, I:], c["B"], kind, "saved B")
     check(b.dx, g["dx"], kind, "dx")
@@ -200,3 +200,17 @@ def test_full_size_forward_backward_sampled():
     run_layer(b, inp, backward=True)
     torch.cuda.synchronize()
     assert digest(b.y, b.dx, b.d_topk_w, b.dw_gate, b.dw_down) == d1
+
+
+def test_empty_batch_zeroes_weight_gradients():
+    say("layer T=0: forward is a no-op, backward overwrites dW with zeros")
+    from mixture_experts_layer_plan_amd import LayerBuffers, run_layer
+    shape = Shape(T=0, H=256, I=128, E=4, k=2, I_shared=128)
+    inp = to_dev(make_inputs(shape, seed=0, device="cpu", with_dy=True))
+    b = LayerBuffers(0, 256, 128, 4, 2, 128, "bf16", backward=True)
+    for t in (b.dw_gate, b.dw_up, b.dw_down, b.ds_gate, b.ds_up, b.ds_down):
+        t.fill_(1.0)
+    run_layer(b, inp, backward=True)
+    torch.cuda.synchronize()
+    for t in (b.dw_gate, b.dw_up, b.dw_down, b.ds_gate, b.ds_up, b.ds_down):
+        assert not t.any()
