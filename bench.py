@@ -34,18 +34,23 @@ def kernel_work(name, sh, counts, es=2):
     w = {
         "route": (T * E * 4 + T * k * 8, 0),
         "plan_hist": (R * 4, 0), "plan_scan": (E * 12, 0), "plan_scatter": (R * 16, 0),
-        "gemm_up_swiglu": (Et * 2 * I * H * es + R * H * es + R * 3 * I * es, 2 * R * H * 2 * I),
+        # saved pre-activations Z are fp32 (4 bytes), h bf16
+        "gemm_up_swiglu": (Et * 2 * I * H * es + R * H * es + R * 2 * I * 4 + R * I * es,
+                           2 * R * H * 2 * I),
         "gemm_down": (Et * H * I * es + R * I * es + R * H * es, 2 * R * I * H),
-        "gemm_up_swiglu_shared": (2 * Is * H * es + T * H * es + T * 3 * Is * es, 2 * T * H * 2 * Is),
+        "gemm_up_swiglu_shared": (2 * Is * H * es + T * H * es + T * 2 * Is * 4 + T * Is * es,
+                                  2 * T * H * 2 * Is),
         "gemm_down_shared": (Is * H * es + T * Is * es + T * H * es, 2 * T * Is * H),
         "combine_bf16": (R * H * es + 2 * T * H * es + T * k * 8, 0),
-        "gemm_dgrad_down": (Et * H * I * es + R * H * es + R * 5 * I * es + R * (I // 128) * 4,
-                            2 * R * H * I),
+        "gemm_dgrad_down": (Et * H * I * es + R * H * es + R * 2 * I * 4 + R * 3 * I * es
+                            + R * (I // 128) * 4, 2 * R * H * I),
         "dg_reduce": (R * (I // 128) * 4 + R * 8, 0),
-        "gemm_wgrad_down": (R * H * es + R * I * es + E * H * I * es, 2 * R * H * I),
+        "zero_empty_experts": ((E - Et) * 3 * I * H * es, 0),
+        "gemm_wgrad_down": (R * H * es + R * I * es + Et * H * I * es, 2 * R * H * I),
         "gemm_dgrad_up": (Et * 2 * I * H * es + R * 2 * I * es + R * H * es, 2 * R * 2 * I * H),
-        "gemm_wgrad_up": (R * 2 * I * es + R * H * es + E * 2 * I * H * es, 2 * R * 2 * I * H),
-        "gemm_dgrad_down_shared": (Is * H * es + T * H * es + T * 5 * Is * es, 2 * T * H * Is),
+        "gemm_wgrad_up": (R * 2 * I * es + R * H * es + Et * 2 * I * H * es, 2 * R * 2 * I * H),
+        "gemm_dgrad_down_shared": (Is * H * es + T * H * es + T * 2 * Is * 4 + T * 3 * Is * es,
+                                   2 * T * H * Is),
         "gemm_wgrad_down_shared": (T * H * es + T * Is * es + H * Is * es, 2 * T * H * Is),
         "gemm_dgrad_up_shared": (2 * Is * H * es + T * 2 * Is * es + T * H * es, 2 * T * 2 * Is * H),
         "gemm_wgrad_up_shared": (T * 2 * Is * es + T * H * es + 2 * Is * H * es, 2 * T * 2 * Is * H),
@@ -92,6 +97,8 @@ def main():
     ap.add_argument("--config", default="kimi_bf16_fwdbwd")
     ap.add_argument("--cpu-tokens", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one plain 1 GiB device copy first (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -113,6 +120,13 @@ def main():
     log(f"[bench] generating {args.config} inputs on the device")
     inp = make_inputs(sh, seed=0, device="cuda", with_dy=True)
     b = LayerBuffers(sh.T, sh.H, sh.I, sh.E, sh.k, sh.I_shared, "bf16", backward=True)
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         run_layer(b, inp, backward=True)

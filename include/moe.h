@@ -82,9 +82,12 @@ typedef struct {
  *                            expert, experts in id order; n_tiles entries valid
  *   n_tiles   int32 [1]
  *   err_flag  int32 [1]      1 if some expert id was outside [0, E), else 0
+ *   active    int32 [E]      ids of the experts with rows, ascending; n_active valid
+ *   n_active  int32 [1]
  *   scratch   per-chunk histograms used while building the plan */
 typedef struct {
-  size_t counts, offsets, src_token, src_slot, pos, tiles, n_tiles, err_flag, scratch;
+  size_t counts, offsets, src_token, src_slot, pos, tiles, n_tiles, err_flag, active, n_active,
+      scratch;
   size_t total_bytes;
   int32_t tile_m, max_tiles, chunk_pairs, n_chunks;
 } moe_plan_layout;

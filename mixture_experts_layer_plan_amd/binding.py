@@ -37,8 +37,8 @@ class moe_shape(ctypes.Structure):
 
 class moe_plan_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("counts", "offsets", "src_token", "src_slot", "pos",
-                                                "tiles", "n_tiles", "err_flag", "scratch",
-                                                "total_bytes")] + \
+                                                "tiles", "n_tiles", "err_flag", "active",
+                                                "n_active", "scratch", "total_bytes")] + \
                [(n, ctypes.c_int32) for n in ("tile_m", "max_tiles", "chunk_pairs", "n_chunks")]
 
 
@@ -319,4 +319,5 @@ def plan_views(s: moe_shape, plan: torch.Tensor) -> dict:
             "src_token": view(L.src_token, R), "src_slot": view(L.src_slot, R),
             "pos": view(L.pos, R).view(s.T, s.k), "tiles": view(L.tiles, 2 * L.max_tiles).view(-1, 2),
             "n_tiles": view(L.n_tiles, 1), "err_flag": view(L.err_flag, 1),
+            "active": view(L.active, s.E), "n_active": view(L.n_active, 1),
             "tile_m": L.tile_m}

@@ -78,6 +78,8 @@ moe_plan_layout plan_layout(const moe_shape* s) {
   L.tiles = c.take(sizeof(int32_t) * 2 * (size_t)L.max_tiles);
   L.n_tiles = c.take(sizeof(int32_t));
   L.err_flag = c.take(sizeof(int32_t));
+  L.active = c.take(sizeof(int32_t) * s->E);
+  L.n_active = c.take(sizeof(int32_t));
   L.scratch = c.take(sizeof(int32_t) * ((size_t)L.n_chunks * s->E + L.n_chunks));
   L.total_bytes = c.off;
   return L;
@@ -93,7 +95,8 @@ const P* at(const void* base, size_t off) {
 }
 
 struct PlanView {
-  const int32_t *counts, *offsets, *src_token, *src_slot, *pos, *tiles, *n_tiles;
+  const int32_t *counts, *offsets, *src_token, *src_slot, *pos, *tiles, *n_tiles, *active,
+      *n_active;
   int max_tiles;
 };
 
@@ -107,6 +110,8 @@ PlanView view_plan(const moe_shape* s, const void* plan) {
   v.pos = at<int32_t>(plan, L.pos);
   v.tiles = at<int32_t>(plan, L.tiles);
   v.n_tiles = at<int32_t>(plan, L.n_tiles);
+  v.active = at<int32_t>(plan, L.active);
+  v.n_active = at<int32_t>(plan, L.n_active);
   v.max_tiles = L.max_tiles;
   return v;
 }
@@ -118,6 +123,9 @@ GroupInfo grouped(const moe_shape* s, const PlanView& v) {
   g.offsets = v.offsets;
   g.src_token = v.src_token;
   g.src_slot = v.src_slot;
+  g.active = v.active;
+  g.n_active = v.n_active;
+  g.counts = v.counts;
   g.max_tiles = v.max_tiles;
   g.dense_rows = 0;
   g.E = s->E;
@@ -280,6 +288,12 @@ moe_status backward_impl(moe_dtype dt, const moe_shape* s, const void* plan, con
   // reverse-combine (gathered in the loader) + dgrad-down + SwiGLU backward + dg partials
   MOE_TRY(launch_gemm_dgrad_down(d, g, dy, wd, Z, topk_w, H, I, s->k, dZ, gh, dgp, st));
   MOE_TRY(launch_dg_reduce(dgp, v.pos, R, I / 128, d_topk_w, st));
+  {
+    const size_t es = dt == MOE_BF16 ? 2 : 4;
+    void* bufs[3] = {dwg, dwu, dwd};
+    const size_t stride[3] = {(size_t)I * H * es, (size_t)I * H * es, (size_t)H * I * es};
+    MOE_TRY(launch_zero_empty_experts(v.counts, s->E, bufs, stride, st));
+  }
   MOE_TRY(launch_gemm_wgrad_down(d, g, dy, gh, H, I, dwd, st));
   MOE_TRY(launch_gemm_dgrad_up(d, g, dZ, wg, wu, H, I, dX, st));
   MOE_TRY(launch_gemm_wgrad_up(d, g, dZ, x, H, I, dwg, dwu, st));
@@ -400,6 +414,8 @@ moe_status moe_plan(const moe_shape* s, const int32_t* topk_idx, void* plan, hip
   p.tiles = at<int32_t>(plan, L.tiles);
   p.n_tiles = at<int32_t>(plan, L.n_tiles);
   p.err_flag = at<int32_t>(plan, L.err_flag);
+  p.active = at<int32_t>(plan, L.active);
+  p.n_active = at<int32_t>(plan, L.n_active);
   p.chunk_hist = at<int32_t>(plan, L.scratch);
   p.chunk_invalid = p.chunk_hist + (size_t)L.n_chunks * s->E;
   p.n_chunks = L.n_chunks;

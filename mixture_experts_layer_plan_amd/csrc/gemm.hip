@@ -21,7 +21,9 @@
 //
 // Grouping: a "rows-grouped" GEMM (forward GEMMs and dgrads) walks the plan's
 // tile list (expert, first row) so a tile never mixes experts; a "K-grouped" GEMM
-// (wgrads) takes one expert per grid z and runs K over that expert's rows.  The
+// (wgrads) is persistent: its workgroups walk (expert with rows, output tile) items
+// and run K over that expert's rows; experts without rows get zeros from a
+// separate full-bandwidth fill.  The
 // gathers of dispatch (x rows) and reverse-combine (dy rows) happen in the A/B
 // loaders through the plan's src_token list, so X and dYu are never written to
 // HBM.  Every output element is produced by one workgroup with a fixed K order:
@@ -505,55 +507,87 @@ MOE_DEV void k_segment(const GroupInfo& g, int e, int& seg0, int& seg1) {
   }
 }
 
-// wgrad-down: dW_d[e][m, n] = sum_r dy[tok(r), m] gh[r, n]  (M = H, N = I, K = rows of e)
+// Work item w of a K-grouped GEMM over an M_tiles x N_tiles output per expert:
+// experts with rows only (the plan's active list), tiles in row-major order.
+struct KTile {
+  int e, m0, n0;
+};
+MOE_DEV KTile k_tile(const GroupInfo& g, int w, int mt_count, int nt_count) {
+  const int per = mt_count * nt_count;
+  const int a = w / per, rem = w - a * per;
+  const int mt = rem / nt_count;
+  KTile t;
+  t.e = g.active ? g.active[a] : 0;
+  t.m0 = mt * TM;
+  t.n0 = (rem - mt * nt_count) * TN;
+  return t;
+}
+
+MOE_DEV int k_work_items(const GroupInfo& g, int mt_count, int nt_count) {
+  return (g.active ? g.n_active[0] : 1) * mt_count * nt_count;
+}
+
+// wgrad-down: dW_d[e][m, n] = sum_r dy[tok(r), m] gh[r, n]  (M = H, N = I, K = rows of e).
+// Persistent: each workgroup walks work items blockIdx.x, + gridDim.x, ...; experts
+// without rows are not visited (their gradients are zeroed by a separate fill).
 template <typename T>
 __global__ __launch_bounds__(NTHR, 2) void k_wgrad_down(GroupInfo g, const T* __restrict__ dy,
                                                         const T* __restrict__ gh, int H, int I,
                                                         T* __restrict__ dwd) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
-  const int n0 = blockIdx.x * TN, m0 = blockIdx.y * TM, e = blockIdx.z;
-  int seg0, seg1;
-  k_segment(g, e, seg0, seg1);
-  MNLoad<T, KRowSeg<T>> la{{dy + m0, g.src_token, (size_t)H, seg0, seg1}};
-  MNLoad<T, KRowSeg<T>> lb{{gh + n0, nullptr, (size_t)I, seg0, seg1}};
+  const int MT = H / TM, NT = I / TN;
+  const int total = k_work_items(g, MT, NT);
   int arow, brow[2];
   wave_coords(arow, brow, false);
   const int lane = threadIdx.x & 63;
-  f32x16_t acc[2][2];
-  const int nk = (seg1 - seg0 + Tr<T>::BK - 1) / Tr<T>::BK;
-  gemm_main<T>(lds, la, lb, nk, acc, arow, brow, lane);
-  float* C = (float*)lds;
-  stage_acc(C, acc, arow, brow, lane);
-  __syncthreads();
-  T* base = dwd + (size_t)e * H * I + (size_t)m0 * I + n0;
-  auto out = [&](int r) { return base + (size_t)r * I; };
-  epi_store<T>(C, out, TM);
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const KTile t = k_tile(g, w, MT, NT);
+    int seg0, seg1;
+    k_segment(g, t.e, seg0, seg1);
+    MNLoad<T, KRowSeg<T>> la{{dy + t.m0, g.src_token, (size_t)H, seg0, seg1}};
+    MNLoad<T, KRowSeg<T>> lb{{gh + t.n0, nullptr, (size_t)I, seg0, seg1}};
+    f32x16_t acc[2][2];
+    const int nk = (seg1 - seg0 + Tr<T>::BK - 1) / Tr<T>::BK;
+    gemm_main<T>(lds, la, lb, nk, acc, arow, brow, lane);
+    float* C = (float*)lds;
+    stage_acc(C, acc, arow, brow, lane);
+    __syncthreads();
+    T* base = dwd + (size_t)t.e * H * I + (size_t)t.m0 * I + t.n0;
+    auto out = [&](int r) { return base + (size_t)r * I; };
+    epi_store<T>(C, out, TM);
+    __syncthreads();
+  }
 }
 
-// wgrad-up: [dW_g; dW_u][e][m, n] = sum_r dZ[r, m] x[tok(r), n]  (M = 2I, N = H)
+// wgrad-up: [dW_g; dW_u][e][m, n] = sum_r dZ[r, m] x[tok(r), n]  (M = 2I, N = H); persistent.
 template <typename T>
 __global__ __launch_bounds__(NTHR, 2) void k_wgrad_up(GroupInfo g, const T* __restrict__ dZ,
                                                       const T* __restrict__ x, int H, int I,
                                                       T* __restrict__ dwg, T* __restrict__ dwu) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
-  const int n0 = blockIdx.x * TN, m0 = blockIdx.y * TM, e = blockIdx.z;
-  int seg0, seg1;
-  k_segment(g, e, seg0, seg1);
-  MNLoad<T, KRowSeg<T>> la{{dZ + m0, nullptr, (size_t)(2 * I), seg0, seg1}};
-  MNLoad<T, KRowSeg<T>> lb{{x + n0, g.src_token, (size_t)H, seg0, seg1}};
+  const int MT = (2 * I) / TM, NT = H / TN;
+  const int total = k_work_items(g, MT, NT);
   int arow, brow[2];
   wave_coords(arow, brow, false);
   const int lane = threadIdx.x & 63;
-  f32x16_t acc[2][2];
-  const int nk = (seg1 - seg0 + Tr<T>::BK - 1) / Tr<T>::BK;
-  gemm_main<T>(lds, la, lb, nk, acc, arow, brow, lane);
-  float* C = (float*)lds;
-  stage_acc(C, acc, arow, brow, lane);
-  __syncthreads();
-  T* base = (m0 < I ? dwg + (size_t)e * I * H + (size_t)m0 * H
-                    : dwu + (size_t)e * I * H + (size_t)(m0 - I) * H) + n0;
-  auto out = [&](int r) { return base + (size_t)r * H; };
-  epi_store<T>(C, out, TM);
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const KTile t = k_tile(g, w, MT, NT);
+    int seg0, seg1;
+    k_segment(g, t.e, seg0, seg1);
+    MNLoad<T, KRowSeg<T>> la{{dZ + t.m0, nullptr, (size_t)(2 * I), seg0, seg1}};
+    MNLoad<T, KRowSeg<T>> lb{{x + t.n0, g.src_token, (size_t)H, seg0, seg1}};
+    f32x16_t acc[2][2];
+    const int nk = (seg1 - seg0 + Tr<T>::BK - 1) / Tr<T>::BK;
+    gemm_main<T>(lds, la, lb, nk, acc, arow, brow, lane);
+    float* C = (float*)lds;
+    stage_acc(C, acc, arow, brow, lane);
+    __syncthreads();
+    T* base = (t.m0 < I ? dwg + (size_t)t.e * I * H + (size_t)t.m0 * H
+                        : dwu + (size_t)t.e * I * H + (size_t)(t.m0 - I) * H) + t.n0;
+    auto out = [&](int r) { return base + (size_t)r * H; };
+    epi_store<T>(C, out, TM);
+    __syncthreads();
+  }
 }
 
 // ------------------------------------------------------------------ launchers
@@ -603,20 +637,31 @@ static hipError_t dgrad_up_t(const GroupInfo& g, const void* dZ, const void* wg,
                         g, (const T*)dZ, (const T*)wg, (const T*)wu, H, I, (T*)dX));
 }
 
+// Persistent grid: two resident workgroups per compute unit, at most one per item.
+static unsigned persistent_grid(long items) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const long g = 2L * (cus > 0 ? cus : 256);
+  return (unsigned)(items < g ? (items > 0 ? items : 1) : g);
+}
+
 template <typename T>
 static hipError_t wgrad_down_t(const GroupInfo& g, const void* dy, const void* gh, int H, int I,
                                void* dwd, hipStream_t s) {
+  const unsigned grid = persistent_grid((long)g.E * (H / TM) * (I / TN));
   return MOE_LAUNCH(g.offsets ? "gemm_wgrad_down" : "gemm_wgrad_down_shared", s,
-                    k_wgrad_down<T><<<dim3(I / TN, H / TM, g.E), NTHR, 0, s>>>(
-                        g, (const T*)dy, (const T*)gh, H, I, (T*)dwd));
+                    k_wgrad_down<T><<<grid, NTHR, 0, s>>>(g, (const T*)dy, (const T*)gh, H, I,
+                                                          (T*)dwd));
 }
 
 template <typename T>
 static hipError_t wgrad_up_t(const GroupInfo& g, const void* dZ, const void* x, int H, int I,
                              void* dwg, void* dwu, hipStream_t s) {
+  const unsigned grid = persistent_grid((long)g.E * ((2 * I) / TM) * (H / TN));
   return MOE_LAUNCH(g.offsets ? "gemm_wgrad_up" : "gemm_wgrad_up_shared", s,
-                    k_wgrad_up<T><<<dim3(H / TN, (2 * I) / TM, g.E), NTHR, 0, s>>>(
-                        g, (const T*)dZ, (const T*)x, H, I, (T*)dwg, (T*)dwu));
+                    k_wgrad_up<T><<<grid, NTHR, 0, s>>>(g, (const T*)dZ, (const T*)x, H, I,
+                                                        (T*)dwg, (T*)dwu));
 }
 
 hipError_t launch_gemm_up_swiglu(int dt, const GroupInfo& g, const void* x, const void* wg,

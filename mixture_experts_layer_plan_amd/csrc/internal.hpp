@@ -46,6 +46,8 @@ struct PlanPtrs {
   int32_t* tiles;
   int32_t* n_tiles;
   int32_t* err_flag;
+  int32_t* active;         // [E] experts with rows, ascending
+  int32_t* n_active;
   int32_t* chunk_hist;     // [n_chunks, E]
   int32_t* chunk_invalid;  // [n_chunks]
   int n_chunks;
@@ -61,6 +63,10 @@ hipError_t launch_combine_bf16(const void* Y, const int32_t* pos, const float* w
                                const void* shared, void* y, int T, int k, int H, hipStream_t s);
 hipError_t launch_combine_f32(const float* Y, const int32_t* pos, const float* w,
                               const float* shared, float* y, int T, int k, int H, hipStream_t s);
+// Zero the weight gradients of experts that received no rows: for each e with
+// counts[e] == 0, bytes [e * stride[i], (e + 1) * stride[i]) of buffer i (i < 3).
+hipError_t launch_zero_empty_experts(const int32_t* counts, int E, void* const* bufs,
+                                     const size_t* stride, hipStream_t s);
 hipError_t launch_dg_reduce(const float* dgp, const int32_t* pos, int R, int n_parts,
                             float* d_topk_w, hipStream_t s);
 
@@ -71,6 +77,9 @@ struct GroupInfo {
   const int32_t* offsets;    // expert row offsets [E+1] (NULL: dense)
   const int32_t* src_token;  // token of each row (NULL: rows are tokens)
   const int32_t* src_slot;
+  const int32_t* active;     // K-grouped: experts with rows (NULL: dense)
+  const int32_t* n_active;
+  const int32_t* counts;     // rows per expert (zero-fill of empty experts)
   int max_tiles;             // grid bound for rows-grouped launches
   int dense_rows;            // row count in dense mode
   int E;

@@ -14,7 +14,8 @@
 //      group's popcount to the chunk's LDS counter (no atomics).
 //   2. plan_scan: one workgroup reduces the chunk histograms to counts, takes the
 //      exclusive prefix over experts (offsets) and over chunks (each chunk's first
-//      row per expert), writes the GEMM tile list and the error flag.
+//      row per expert), writes the GEMM tile list, the list of experts that
+//      received rows, and the error flag.
 //   3. plan_scatter: each wavefront replays its chunk in pair order; a pair's row
 //      is its chunk base + the number of earlier same-expert pairs, so rows of an
 //      expert keep ascending pair order (stable) and the result does not depend on
@@ -77,9 +78,10 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
     int32_t* __restrict__ hist, const int32_t* __restrict__ chunk_invalid, int n_chunks, int E,
     int R, int tile_m, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles, int32_t* __restrict__ err_flag,
-    int32_t* __restrict__ src_token, int32_t* __restrict__ src_slot) {
-  __shared__ int32_t s_rows[1024];
-  __shared__ int32_t s_wave[2][16];
+    int32_t* __restrict__ src_token, int32_t* __restrict__ src_slot,
+    int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
+  __shared__ int32_t s_rows[1];
+  __shared__ int32_t s_wave[3][16];
   __shared__ int32_t s_bad;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   if (tid == 0) s_bad = 0;
@@ -87,20 +89,22 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
   if (tid < E)
     for (int c = 0; c < n_chunks; ++c) n += hist[(size_t)c * E + tid];
   const int nt = (n + tile_m - 1) / tile_m;
+  const int act = n > 0 ? 1 : 0;
   // inclusive scans inside each wavefront (Hillis-Steele over shuffles)
-  int a = n, b = nt;
+  int a = n, b = nt, c3 = act;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int ua = __shfl_up(a, o, 64), ub = __shfl_up(b, o, 64);
-    if (lane >= o) { a += ua; b += ub; }
+    const int ua = __shfl_up(a, o, 64), ub = __shfl_up(b, o, 64), uc = __shfl_up(c3, o, 64);
+    if (lane >= o) { a += ua; b += ub; c3 += uc; }
   }
-  if (lane == 63) { s_wave[0][wv] = a; s_wave[1][wv] = b; }
+  if (lane == 63) { s_wave[0][wv] = a; s_wave[1][wv] = b; s_wave[2][wv] = c3; }
   __syncthreads();
-  int base_a = 0, base_b = 0;
-  for (int i = 0; i < wv; ++i) { base_a += s_wave[0][i]; base_b += s_wave[1][i]; }
-  const int excl_rows = base_a + a - n, excl_tiles = base_b + b - nt;
+  int base_a = 0, base_b = 0, base_c = 0;
+  for (int i = 0; i < wv; ++i) { base_a += s_wave[0][i]; base_b += s_wave[1][i]; base_c += s_wave[2][i]; }
+  const int excl_rows = base_a + a - n, excl_tiles = base_b + b - nt, excl_act = base_c + c3 - act;
   if (tid < E) {
     counts[tid] = n;
+    if (act) active[excl_act] = tid;
     offsets[tid] = excl_rows;
     // first row of each chunk for this expert
     int run = excl_rows;
@@ -117,6 +121,7 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
   if (tid == E - 1) {
     offsets[E] = excl_rows + n;
     n_tiles[0] = excl_tiles + nt;
+    n_active[0] = excl_act + act;
     s_rows[0] = excl_rows + n;
   }
   for (int c = tid; c < n_chunks; c += 1024)
@@ -182,7 +187,7 @@ hipError_t launch_plan(const int32_t* topk_idx, int T, int k, int E, const PlanP
                               plan_scan_kernel<<<1, 1024, 0, s>>>(
                                   p.chunk_hist, p.chunk_invalid, p.n_chunks, E, R, GEMM_TILE_M,
                                   p.counts, p.offsets, p.tiles, p.n_tiles, p.err_flag,
-                                  p.src_token, p.src_slot));
+                                  p.src_token, p.src_slot, p.active, p.n_active));
   if (err != hipSuccess || p.n_chunks == 0) return err;
   return MOE_LAUNCH("plan_scatter", s,
                     plan_scatter_kernel<<<blocks, 256, lds, s>>>(topk_idx, R, E, k, nbits,

@@ -66,6 +66,9 @@ def check_plan(B, idx, E):
     assert got["n_tiles"][0] == len(tl)
     np.testing.assert_array_equal(got["tiles"][:len(tl)], tl)
     assert got["err_flag"][0] == int(ref["err"])
+    act = np.nonzero(ref["counts"])[0]
+    assert got["n_active"][0] == len(act)
+    np.testing.assert_array_equal(got["active"][:len(act)], act)
     return got
 
 
