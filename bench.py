@@ -55,6 +55,7 @@ def kernel_work(name, sh, counts, es=2):
         "gemm_dgrad_up_shared": (2 * Is * H * es + T * 2 * Is * es + T * H * es, 2 * T * 2 * Is * H),
         "gemm_wgrad_up_shared": (T * 2 * Is * es + T * H * es + 2 * Is * H * es, 2 * T * 2 * Is * H),
         "reverse_dispatch_bf16": (R * H * es + 2 * T * H * es, 0),
+        "gather_rows": (2 * R * H * es + R * 4, 0),
         "route_backward": (T * k * 12 + T * E * 4, 0),
     }
     return w.get(name, (0, 0))

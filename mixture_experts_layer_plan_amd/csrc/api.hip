@@ -173,9 +173,9 @@ FwdWs fwd_ws(const moe_shape* s, moe_dtype dt) {
 }
 
 // backward workspace: dZ [R, 2I], gh [R, I], dgp fp32 [R, I/128], dX [R, H],
-// dZs [T, 2Is], hs [T, Is], dxs [T, H]
+// X [R, H] and dYu [R, H] (replayed gathers), dZs [T, 2Is], hs [T, Is], dxs [T, H]
 struct BwdWs {
-  size_t dZ, gh, dgp, dX, dZs, hs, dxs, total;
+  size_t dZ, gh, dgp, dX, X, dYu, dZs, hs, dxs, total;
 };
 BwdWs bwd_ws(const moe_shape* s, moe_dtype dt) {
   const size_t R = (size_t)s->T * s->k, es = esize(dt), T = s->T;
@@ -185,6 +185,8 @@ BwdWs bwd_ws(const moe_shape* s, moe_dtype dt) {
   L.gh = c.take(R * s->I * es);
   L.dgp = c.take(R * (s->I / 128) * sizeof(float));
   L.dX = c.take(R * s->H * es);
+  L.X = c.take(R * s->H * es);
+  L.dYu = c.take(R * s->H * es);
   L.dZs = c.take(T * 2 * s->I_shared * es);
   L.hs = c.take(T * s->I_shared * es);
   L.dxs = c.take(s->I_shared ? T * s->H * es : 0);
@@ -285,8 +287,14 @@ moe_status backward_impl(moe_dtype dt, const moe_shape* s, const void* plan, con
   void* gh = at<char>(ws, W.gh);
   float* dgp = at<float>(ws, W.dgp);
   void* dX = at<char>(ws, W.dX);
-  // reverse-combine (gathered in the loader) + dgrad-down + SwiGLU backward + dg partials
-  MOE_TRY(launch_gemm_dgrad_down(d, g, dy, wd, Z, topk_w, H, I, s->k, dZ, gh, dgp, st));
+  void* X = at<char>(ws, W.X);
+  void* dYu = at<char>(ws, W.dYu);
+  const int es = d ? 2 : 4;
+  // reverse-combine: pull dy rows into expert order; replay the dispatch of x
+  MOE_TRY(launch_gather_rows(dy, dYu, v.src_token, v.offsets + s->E, R, H * es, st));
+  MOE_TRY(launch_gather_rows(x, X, v.src_token, v.offsets + s->E, R, H * es, st));
+  // dgrad-down + SwiGLU backward + router-weight-gradient partials
+  MOE_TRY(launch_gemm_dgrad_down(d, g, dYu, wd, Z, topk_w, H, I, s->k, dZ, gh, dgp, st));
   MOE_TRY(launch_dg_reduce(dgp, v.pos, R, I / 128, d_topk_w, st));
   {
     const size_t es = dt == MOE_BF16 ? 2 : 4;
@@ -294,9 +302,9 @@ moe_status backward_impl(moe_dtype dt, const moe_shape* s, const void* plan, con
     const size_t stride[3] = {(size_t)I * H * es, (size_t)I * H * es, (size_t)H * I * es};
     MOE_TRY(launch_zero_empty_experts(v.counts, s->E, bufs, stride, st));
   }
-  MOE_TRY(launch_gemm_wgrad_down(d, g, dy, gh, H, I, dwd, st));
+  MOE_TRY(launch_gemm_wgrad_down(d, g, dYu, gh, H, I, dwd, st));
   MOE_TRY(launch_gemm_dgrad_up(d, g, dZ, wg, wu, H, I, dX, st));
-  MOE_TRY(launch_gemm_wgrad_up(d, g, dZ, x, H, I, dwg, dwu, st));
+  MOE_TRY(launch_gemm_wgrad_up(d, g, dZ, X, H, I, dwg, dwu, st));
   void* dxs = nullptr;
   if (s->I_shared) {
     const int Is = s->I_shared;

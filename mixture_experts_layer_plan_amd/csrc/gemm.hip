@@ -25,8 +25,9 @@
 // and run K over that expert's rows; experts without rows get zeros from a
 // separate full-bandwidth fill.  The
 // gathers of dispatch (x rows) and reverse-combine (dy rows) happen in the A/B
-// loaders through the plan's src_token list, so X and dYu are never written to
-// HBM.  Every output element is produced by one workgroup with a fixed K order:
+// loader of GEMM1 through the plan's src_token list (X is not written in the
+// forward); the backward replays both gathers once into row-major buffers so that
+// the K rows of the wgrad operands are plain strided addresses.  Every output element is produced by one workgroup with a fixed K order:
 // results are bitwise reproducible and independent of the grid.
 //
 // Epilogues stage the fp32 accumulator tile in LDS (64 KiB, swizzled) and then
@@ -171,7 +172,14 @@ MOE_DEV void mma_tile<float>(const char* ta, const char* tb, f32x16_t (&acc)[2][
 }
 
 // ----------------------------------------------------------------- main loop
-template <typename T, class LA, class LB>
+// Prefetch distance 2: two register sets (r*0, r*1) and two LDS buffers.  While
+// the MFMAs consume K tile kt from LDS, tile kt + 1 (loaded one iteration earlier)
+// goes from registers into the other LDS buffer and tile kt + 2 is in flight from
+// memory, so each global load has a whole iteration to arrive.  The loop is
+// unrolled by two so that the register sets stay statically indexed.
+// DIST = 1 keeps one register set (fewer registers, for the short-K wgrads):
+// tile kt + 1 is loaded while tile kt is multiplied.
+template <typename T, int DIST = 2, class LA, class LB>
 MOE_DEV void gemm_main(char* lds, const LA& la, const LB& lb, int nk, f32x16_t (&acc)[2][2],
                        int arow, const int (&brow)[2], int lane) {
 #pragma unroll
@@ -181,24 +189,62 @@ MOE_DEV void gemm_main(char* lds, const LA& la, const LB& lb, int nk, f32x16_t (
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   if (nk <= 0) return;
-  uint4 ra[4], rb[4];
-  la.load(0, ra);
-  lb.load(0, rb);
-  la.store(lds, ra);
-  lb.store(lds + TILEB, rb);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    char* cur = lds + (kt & 1) * 2 * TILEB;
-    char* nxt = lds + ((kt + 1) & 1) * 2 * TILEB;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      la.load(kt + 1, ra);
-      lb.load(kt + 1, rb);
+  if constexpr (DIST == 1) {
+    uint4 ra[4], rb[4];
+    la.load(0, ra);
+    lb.load(0, rb);
+    la.store(lds, ra);
+    lb.store(lds + TILEB, rb);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      char* cur = lds + (kt & 1) * 2 * TILEB;
+      char* nxt = lds + ((kt + 1) & 1) * 2 * TILEB;
+      const bool more = kt + 1 < nk;
+      if (more) {
+        la.load(kt + 1, ra);
+        lb.load(kt + 1, rb);
+      }
+      mma_tile<T>(cur, cur + TILEB, acc, arow, brow, lane);
+      if (more) {
+        la.store(nxt, ra);
+        lb.store(nxt + TILEB, rb);
+      }
+      __syncthreads();
     }
-    mma_tile<T>(cur, cur + TILEB, acc, arow, brow, lane);
-    if (more) {
-      la.store(nxt, ra);
-      lb.store(nxt + TILEB, rb);
+    return;
+  }
+  char* buf0 = lds;
+  char* buf1 = lds + 2 * TILEB;
+  uint4 ra0[4], rb0[4], ra1[4], rb1[4];
+  la.load(0, ra0);
+  lb.load(0, rb0);
+  if (nk > 1) {
+    la.load(1, ra1);
+    lb.load(1, rb1);
+  }
+  la.store(buf0, ra0);
+  lb.store(buf0 + TILEB, rb0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    if (kt + 2 < nk) {
+      la.load(kt + 2, ra0);
+      lb.load(kt + 2, rb0);
+    }
+    mma_tile<T>(buf0, buf0 + TILEB, acc, arow, brow, lane);
+    if (kt + 1 < nk) {
+      la.store(buf1, ra1);
+      lb.store(buf1 + TILEB, rb1);
+    }
+    __syncthreads();
+    if (kt + 1 >= nk) break;
+    if (kt + 3 < nk) {
+      la.load(kt + 3, ra1);
+      lb.load(kt + 3, rb1);
+    }
+    mma_tile<T>(buf1, buf1 + TILEB, acc, arow, brow, lane);
+    if (kt + 2 < nk) {
+      la.store(buf0, ra0);
+      lb.store(buf0 + TILEB, rb0);
     }
     __syncthreads();
   }
@@ -256,18 +302,30 @@ struct RowTile {
   int e, row0, row_end;
 };
 
-// Rows-grouped tile for blockIdx.y; false when past the last tile.
-MOE_DEV bool rows_tile(const GroupInfo& g, RowTile& t) {
-  const int mt = blockIdx.y;
+constexpr int N_XCD = 8;  // MI355X: workgroup i is dispatched to XCD i mod 8
+
+// Rows-grouped launches use a 1-D grid over (row tile, column tile) pairs.  The
+// pairs that exist (n_tiles of the plan x nt_count) are renumbered so that the
+// workgroups one XCD receives (ids x, x + 8, x + 16, ...) cover a contiguous run
+// of pairs with the column tile fastest: a row tile's activations and an expert's
+// weight columns are then fetched into that XCD's L2 once, not once per XCD.
+// Returns false for workgroups past the last pair.
+MOE_DEV bool rows_tile(const GroupInfo& g, int nt_count, RowTile& t, int& nt) {
+  const int n_row_tiles = g.tiles ? g.n_tiles[0] : (g.dense_rows + TM - 1) / TM;
+  const int total = n_row_tiles * nt_count;
+  const int id = blockIdx.x;
+  if (id >= total) return false;
+  const int per = total / N_XCD, rem = total % N_XCD, x = id % N_XCD, local = id / N_XCD;
+  const int L = x < rem ? x * (per + 1) + local : rem * (per + 1) + (x - rem) * per + local;
+  const int mt = L / nt_count;
+  nt = L - mt * nt_count;
   if (g.tiles) {
-    if (mt >= g.n_tiles[0]) return false;
     t.e = g.tiles[2 * mt];
     t.row0 = g.tiles[2 * mt + 1];
     t.row_end = min(t.row0 + TM, g.offsets[t.e + 1]);
   } else {
     t.e = 0;
     t.row0 = mt * TM;
-    if (t.row0 >= g.dense_rows) return false;
     t.row_end = min(t.row0 + TM, g.dense_rows);
   }
   return true;
@@ -299,8 +357,9 @@ __global__ __launch_bounds__(NTHR, 2) void k_up_swiglu(GroupInfo g, const T* __r
                                                        float* __restrict__ Z, T* __restrict__ hout) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   RowTile t;
-  if (!rows_tile(g, t)) return;
-  const int i0 = blockIdx.x * 64;
+  int nt;
+  if (!rows_tile(g, I / 64, t, nt)) return;
+  const int i0 = nt * 64;
   const size_t wofs = (size_t)t.e * I * H;
   KLoad<T> la, lb;
 #pragma unroll
@@ -343,8 +402,9 @@ __global__ __launch_bounds__(NTHR, 2) void k_down(GroupInfo g, const T* __restri
                                                   T* __restrict__ Y) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   RowTile t;
-  if (!rows_tile(g, t)) return;
-  const int n0 = blockIdx.x * TN;
+  int nt;
+  if (!rows_tile(g, H / TN, t, nt)) return;
+  const int n0 = nt * TN;
   const size_t wofs = (size_t)t.e * H * I;
   KLoad<T> la, lb;
 #pragma unroll
@@ -374,10 +434,11 @@ struct KRowPlain {
   MOE_DEV const T* operator()(int k) const { return base + (size_t)k * ld; }
 };
 
-// dgrad-down: dh'[r, i] = sum_n dy[tok(r), n] W_d[e][n, i]; epilogue: SwiGLU backward
-// and the router-weight-gradient partial of this tile's 128 columns.
+// dgrad-down: dh'[r, i] = sum_n dYu[r, n] W_d[e][n, i] with dYu[r] = dy[tok(r)] (the
+// reverse-combined rows); epilogue: SwiGLU backward and the router-weight-gradient
+// partial of this tile's 128 columns.
 template <typename T>
-__global__ __launch_bounds__(NTHR, 2) void k_dgrad_down(GroupInfo g, const T* __restrict__ dy,
+__global__ __launch_bounds__(NTHR, 2) void k_dgrad_down(GroupInfo g, const T* __restrict__ dYu,
                                                         const T* __restrict__ wd,
                                                         const float* __restrict__ Z,
                                                         const float* __restrict__ topk_w, int H,
@@ -386,13 +447,14 @@ __global__ __launch_bounds__(NTHR, 2) void k_dgrad_down(GroupInfo g, const T* __
                                                         float* __restrict__ dgp) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   RowTile t;
-  if (!rows_tile(g, t)) return;
-  const int i0 = blockIdx.x * TN;
+  int nt;
+  if (!rows_tile(g, I / TN, t, nt)) return;
+  const int i0 = nt * TN;
   KLoad<T> la;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int r = t.row0 + (threadIdx.x >> 3) + 32 * s;
-    la.rp[s] = r < t.row_end ? dy + (size_t)token_of(g, r) * H : nullptr;
+    la.rp[s] = r < t.row_end ? dYu + (size_t)r * H : nullptr;
   }
   MNLoad<T, KRowPlain<T>> lb{{wd + (size_t)t.e * H * I + i0, (size_t)I}};
   int arow, brow[2];
@@ -437,7 +499,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_dgrad_down(GroupInfo g, const T* __
     // fixed-order sum over the 16 lanes holding this row's 128 columns
 #pragma unroll
     for (int o = 8; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
-    if (ok && c == 0 && dgp) dgp[(size_t)(t.row0 + r) * n_parts + blockIdx.x] = part;
+    if (ok && c == 0 && dgp) dgp[(size_t)(t.row0 + r) * n_parts + nt] = part;
   }
 }
 
@@ -460,8 +522,9 @@ __global__ __launch_bounds__(NTHR, 2) void k_dgrad_up(GroupInfo g, const T* __re
                                                       T* __restrict__ dX) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   RowTile t;
-  if (!rows_tile(g, t)) return;
-  const int n0 = blockIdx.x * TN;
+  int nt;
+  if (!rows_tile(g, H / TN, t, nt)) return;
+  const int n0 = nt * TN;
   const size_t wofs = (size_t)t.e * I * H + n0;
   KLoad<T> la;
 #pragma unroll
@@ -527,11 +590,11 @@ MOE_DEV int k_work_items(const GroupInfo& g, int mt_count, int nt_count) {
   return (g.active ? g.n_active[0] : 1) * mt_count * nt_count;
 }
 
-// wgrad-down: dW_d[e][m, n] = sum_r dy[tok(r), m] gh[r, n]  (M = H, N = I, K = rows of e).
+// wgrad-down: dW_d[e][m, n] = sum_r dYu[r, m] gh[r, n]  (M = H, N = I, K = rows of e).
 // Persistent: each workgroup walks work items blockIdx.x, + gridDim.x, ...; experts
 // without rows are not visited (their gradients are zeroed by a separate fill).
 template <typename T>
-__global__ __launch_bounds__(NTHR, 2) void k_wgrad_down(GroupInfo g, const T* __restrict__ dy,
+__global__ __launch_bounds__(NTHR, 2) void k_wgrad_down(GroupInfo g, const T* __restrict__ dYu,
                                                         const T* __restrict__ gh, int H, int I,
                                                         T* __restrict__ dwd) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
@@ -544,11 +607,11 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_down(GroupInfo g, const T* __
     const KTile t = k_tile(g, w, MT, NT);
     int seg0, seg1;
     k_segment(g, t.e, seg0, seg1);
-    MNLoad<T, KRowSeg<T>> la{{dy + t.m0, g.src_token, (size_t)H, seg0, seg1}};
+    MNLoad<T, KRowSeg<T>> la{{dYu + t.m0, nullptr, (size_t)H, seg0, seg1}};
     MNLoad<T, KRowSeg<T>> lb{{gh + t.n0, nullptr, (size_t)I, seg0, seg1}};
     f32x16_t acc[2][2];
     const int nk = (seg1 - seg0 + Tr<T>::BK - 1) / Tr<T>::BK;
-    gemm_main<T>(lds, la, lb, nk, acc, arow, brow, lane);
+    gemm_main<T, 1>(lds, la, lb, nk, acc, arow, brow, lane);
     float* C = (float*)lds;
     stage_acc(C, acc, arow, brow, lane);
     __syncthreads();
@@ -559,10 +622,11 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_down(GroupInfo g, const T* __
   }
 }
 
-// wgrad-up: [dW_g; dW_u][e][m, n] = sum_r dZ[r, m] x[tok(r), n]  (M = 2I, N = H); persistent.
+// wgrad-up: [dW_g; dW_u][e][m, n] = sum_r dZ[r, m] X[r, n] with X[r] = x[tok(r)] (the
+// dispatched rows, replayed)  (M = 2I, N = H); persistent.
 template <typename T>
 __global__ __launch_bounds__(NTHR, 2) void k_wgrad_up(GroupInfo g, const T* __restrict__ dZ,
-                                                      const T* __restrict__ x, int H, int I,
+                                                      const T* __restrict__ X, int H, int I,
                                                       T* __restrict__ dwg, T* __restrict__ dwu) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   const int MT = (2 * I) / TM, NT = H / TN;
@@ -575,10 +639,10 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_up(GroupInfo g, const T* __re
     int seg0, seg1;
     k_segment(g, t.e, seg0, seg1);
     MNLoad<T, KRowSeg<T>> la{{dZ + t.m0, nullptr, (size_t)(2 * I), seg0, seg1}};
-    MNLoad<T, KRowSeg<T>> lb{{x + t.n0, g.src_token, (size_t)H, seg0, seg1}};
+    MNLoad<T, KRowSeg<T>> lb{{X + t.n0, nullptr, (size_t)H, seg0, seg1}};
     f32x16_t acc[2][2];
     const int nk = (seg1 - seg0 + Tr<T>::BK - 1) / Tr<T>::BK;
-    gemm_main<T>(lds, la, lb, nk, acc, arow, brow, lane);
+    gemm_main<T, 1>(lds, la, lb, nk, acc, arow, brow, lane);
     float* C = (float*)lds;
     stage_acc(C, acc, arow, brow, lane);
     __syncthreads();
@@ -601,7 +665,7 @@ static hipError_t up_swiglu_t(const GroupInfo& g, const void* x, const void* wg,
   const unsigned ty = row_tiles(g);
   if (ty == 0) return hipSuccess;
   return MOE_LAUNCH(g.tiles ? "gemm_up_swiglu" : "gemm_up_swiglu_shared", s,
-                    k_up_swiglu<T><<<dim3(I / 64, ty), NTHR, 0, s>>>(
+                    k_up_swiglu<T><<<ty * (I / 64), NTHR, 0, s>>>(
                         g, (const T*)x, (const T*)wg, (const T*)wu, H, I, (float*)Z, (T*)h));
 }
 
@@ -611,7 +675,7 @@ static hipError_t down_t(const GroupInfo& g, const void* h, const void* wd, int 
   const unsigned ty = row_tiles(g);
   if (ty == 0) return hipSuccess;
   return MOE_LAUNCH(g.tiles ? "gemm_down" : "gemm_down_shared", s,
-                    k_down<T><<<dim3(H / TN, ty), NTHR, 0, s>>>(g, (const T*)h, (const T*)wd, H,
+                    k_down<T><<<ty * (H / TN), NTHR, 0, s>>>(g, (const T*)h, (const T*)wd, H,
                                                                  I, (T*)Y));
 }
 
@@ -622,7 +686,7 @@ static hipError_t dgrad_down_t(const GroupInfo& g, const void* dy, const void* w
   const unsigned ty = row_tiles(g);
   if (ty == 0) return hipSuccess;
   return MOE_LAUNCH(g.tiles ? "gemm_dgrad_down" : "gemm_dgrad_down_shared", s,
-                    k_dgrad_down<T><<<dim3(I / TN, ty), NTHR, 0, s>>>(
+                    k_dgrad_down<T><<<ty * (I / TN), NTHR, 0, s>>>(
                         g, (const T*)dy, (const T*)wd, (const float*)Z, topk_w, H, I, k, (T*)dZ,
                         (T*)gh, dgp));
 }
@@ -633,7 +697,7 @@ static hipError_t dgrad_up_t(const GroupInfo& g, const void* dZ, const void* wg,
   const unsigned ty = row_tiles(g);
   if (ty == 0) return hipSuccess;
   return MOE_LAUNCH(g.tiles ? "gemm_dgrad_up" : "gemm_dgrad_up_shared", s,
-                    k_dgrad_up<T><<<dim3(H / TN, ty), NTHR, 0, s>>>(
+                    k_dgrad_up<T><<<ty * (H / TN), NTHR, 0, s>>>(
                         g, (const T*)dZ, (const T*)wg, (const T*)wu, H, I, (T*)dX));
 }
 

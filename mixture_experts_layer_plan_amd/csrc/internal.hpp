@@ -92,18 +92,19 @@ hipError_t launch_gemm_up_swiglu(int dt, const GroupInfo& g, const void* x, cons
 // GEMM2: Y = h W_d[e]^T
 hipError_t launch_gemm_down(int dt, const GroupInfo& g, const void* h, const void* wd, int H,
                             int I, void* Y, hipStream_t s);
-// dgrad-down + SwiGLU backward + router-weight-gradient partials
-hipError_t launch_gemm_dgrad_down(int dt, const GroupInfo& g, const void* dy, const void* wd,
+// dgrad-down + SwiGLU backward + router-weight-gradient partials; dYu = rows of dy
+// in expert order (dy itself in dense mode)
+hipError_t launch_gemm_dgrad_down(int dt, const GroupInfo& g, const void* dYu, const void* wd,
                                   const void* Z, const float* topk_w, int H, int I, int k,
                                   void* dZ, void* gh, float* dgp, hipStream_t s);
 // dgrad-up: dX = dZ[:, :I] W_g[e] + dZ[:, I:] W_u[e]
 hipError_t launch_gemm_dgrad_up(int dt, const GroupInfo& g, const void* dZ, const void* wg,
                                 const void* wu, int H, int I, void* dX, hipStream_t s);
-// wgrad-down: dW_d[e] = sum_r dy[src_token[r]] (x) gh[r]
-hipError_t launch_gemm_wgrad_down(int dt, const GroupInfo& g, const void* dy, const void* gh,
+// wgrad-down: dW_d[e] = sum_r dYu[r] (x) gh[r]
+hipError_t launch_gemm_wgrad_down(int dt, const GroupInfo& g, const void* dYu, const void* gh,
                                   int H, int I, void* dwd, hipStream_t s);
-// wgrad-up: dW_g[e] = sum_r dZ[r, :I] (x) x[src_token[r]], dW_u[e] likewise with dZ[r, I:]
-hipError_t launch_gemm_wgrad_up(int dt, const GroupInfo& g, const void* dZ, const void* x,
+// wgrad-up: dW_g[e] = sum_r dZ[r, :I] (x) X[r], dW_u[e] likewise with dZ[r, I:]
+hipError_t launch_gemm_wgrad_up(int dt, const GroupInfo& g, const void* dZ, const void* X,
                                 int H, int I, void* dwg, void* dwu, hipStream_t s);
 
 }  // namespace moe

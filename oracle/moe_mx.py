@@ -1,0 +1,196 @@
+"""MXFP8 variant of the layer oracle.  TEST INFRASTRUCTURE ONLY (see the package
+docstring).
+
+MoK trains in MXFP8, with the conversion inside the kernel and the shared expert
+kept in BF16 (sebask.de, "Mixture-of-Kittens: Cursors Open-Source-Ansatz für
+effizientes MoE-Training auf NVL72", § Determinismus und MXFP8-Unterstützung;
+stamatios.com, "Cursor abre código de megakernel MoE para GPUs NVL72", § Outras
+características).  The pages do not say which operands are quantised or along
+which axis; the reading taken here: every operand of the six expert GEMMs is
+replaced by dequant(Q(.)) along that GEMM's contraction axis (blocks of 32, OCP
+rule in ``oracle.mx``), and everything else is the fp64 definition of
+``oracle.moe``:
+
+  forward   A = Q_H(X) Q_H(W_g)^T, B = Q_H(X) Q_H(W_u)^T, h = silu(A) B,
+            Y = Q_I(h) Q_I(W_d)^T                        (Q_H: along H, per row)
+  backward  dh' = Q_H(dYu) Q_H(W_d) (W_d blocked along H), dg = <dh', h>,
+            dA, dB as in the bf16 definition,
+            dX = Q_2I(dA|dB) [Q_I(W_g); Q_I(W_u)]      (weights blocked along I)
+            dW_d[e] = Q_t(dYu)^T Q_t(g h), dW_g[e] = Q_t(dA)^T Q_t(X),
+            dW_u[e] = Q_t(dB)^T Q_t(X)
+where Q_t blocks along the tokens of one expert's segment in one minibatch,
+32 rows at a time from the segment's first row, the last block zero-padded.
+
+Tokens are processed in consecutive minibatches of T_mb (the ring-buffer macro
+batch, stamatios.com § Ring token buffers); each minibatch has its own plan.
+Weight gradients sum the per-minibatch products (in fp64 the order is
+immaterial).  The shared expert is the exact bf16-input definition.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .moe import _f64, build_plan, combine, dense_swiglu, dsilu, route, route_backward, silu
+from .mx import mx_roundtrip
+
+
+def q_rows(a) -> np.ndarray:
+    """dequant(Q(a)) in blocks of 32 along the last axis."""
+    return mx_roundtrip(_f64(a), axis=-1)
+
+
+def q_cols(a) -> np.ndarray:
+    """dequant(Q(a)) in blocks of 32 along axis 0 (the length must be a multiple of 32)."""
+    return mx_roundtrip(_f64(a), axis=0)
+
+
+def q_tokens(a) -> np.ndarray:
+    """dequant(Q(a)) in blocks of 32 rows from the first row, last block zero-padded."""
+    a = _f64(a)
+    n = a.shape[0]
+    pad = (-n) % 32
+    if pad:
+        a = np.concatenate([a, np.zeros((pad,) + a.shape[1:])])
+    return mx_roundtrip(a, axis=0)[:n]
+
+
+class _QuantCache:
+    """Per-expert quantised weights, each orientation computed once."""
+
+    def __init__(self, w_gate, w_up, w_down):
+        self.w = (w_gate, w_up, w_down)
+        self.c = {}
+
+    def get(self, kind, e):
+        key = (kind, int(e))
+        if key not in self.c:
+            wg, wu, wd = self.w
+            if kind == "g_H":
+                v = q_rows(wg[e])            # [I, H] along H
+            elif kind == "u_H":
+                v = q_rows(wu[e])
+            elif kind == "d_I":
+                v = q_rows(wd[e])            # [H, I] along I
+            elif kind == "d_H":
+                v = q_cols(wd[e])            # [H, I] along H
+            elif kind == "g_I":
+                v = q_cols(wg[e])            # [I, H] along I
+            elif kind == "u_I":
+                v = q_cols(wu[e])
+            else:
+                raise KeyError(kind)
+            self.c[key] = v
+        return self.c[key]
+
+
+def minibatch_slices(T: int, T_mb: int):
+    T_mb = T_mb or T
+    return [slice(s, min(T, s + T_mb)) for s in range(0, T, T_mb)]
+
+
+def layer_forward_mx(x, logits, k, w_gate, w_up, w_down, shared=None, T_mb=0,
+                     qcache: _QuantCache | None = None) -> dict:
+    """Forward of the MXFP8 layer over consecutive minibatches of T_mb tokens."""
+    xf = _f64(x)
+    L = _f64(logits)
+    T, H = xf.shape
+    E = L.shape[1]
+    idx, g = route(L, k)
+    qc = qcache or _QuantCache(w_gate, w_up, w_down)
+    y = np.zeros((T, H))
+    mbs = []
+    for sl in minibatch_slices(T, T_mb):
+        plan = build_plan(idx[sl], E)
+        xq = q_rows(xf[sl])
+        n_rows = int(plan["offsets"][E])
+        X = xq[plan["src_token"][:n_rows]]
+        Y = np.zeros((n_rows, H))
+        A = B = h = None
+        for e in range(E):
+            r0, r1 = int(plan["offsets"][e]), int(plan["offsets"][e + 1])
+            if r1 == r0:
+                continue
+            Ae = X[r0:r1] @ qc.get("g_H", e).T
+            Be = X[r0:r1] @ qc.get("u_H", e).T
+            he = silu(Ae) * Be
+            if A is None:
+                I = Ae.shape[1]
+                A, B, h = np.zeros((n_rows, I)), np.zeros((n_rows, I)), np.zeros((n_rows, I))
+            A[r0:r1], B[r0:r1], h[r0:r1] = Ae, Be, he
+            Y[r0:r1] = q_rows(he) @ qc.get("d_I", e).T
+        shared_out = dense_swiglu(xf[sl], *shared)[3] if shared is not None else None
+        y[sl] = combine(Y, plan["pos"], g[sl], shared_out)
+        mbs.append({"slice": sl, "plan": plan, "A": A, "B": B, "h": h, "Y": Y})
+    return {"y": y, "topk_idx": idx, "topk_w": g, "minibatches": mbs, "x": xf, "E": E, "k": k,
+            "shared": shared, "qcache": qc, "w": (w_gate, w_up, w_down)}
+
+
+def layer_backward_mx(cache: dict, dy) -> dict:
+    """Backward of ``layer_forward_mx`` (selection held fixed)."""
+    dyf = _f64(dy)
+    xf = cache["x"]
+    T, H = xf.shape
+    E, k = cache["E"], cache["k"]
+    g = cache["topk_w"]
+    qc = cache["qcache"]
+    w_gate, w_up, w_down = cache["w"]
+    dWg = [None] * E
+    dWu = [None] * E
+    dWd = [None] * E
+    dx = np.zeros((T, H))
+    dg = np.zeros((T, k))
+    for mb in cache["minibatches"]:
+        sl, plan = mb["slice"], mb["plan"]
+        n_rows = int(plan["offsets"][E])
+        st = plan["src_token"][:n_rows]
+        ss = plan["src_slot"][:n_rows]
+        dyq = q_rows(dyf[sl])
+        dY_rows = dyf[sl][st]
+        X_rows = xf[sl][st]
+        g_rows = g[sl][st, ss]
+        dX = np.zeros((n_rows, H))
+        dg_rows = np.zeros(n_rows)
+        for e in range(E):
+            r0, r1 = int(plan["offsets"][e]), int(plan["offsets"][e + 1])
+            if r1 == r0:
+                continue
+            A, B, h = mb["A"][r0:r1], mb["B"][r0:r1], mb["h"][r0:r1]
+            dhp = dyq[st[r0:r1]] @ qc.get("d_H", e)
+            dg_rows[r0:r1] = np.sum(dhp * h, axis=1)
+            gr = g_rows[r0:r1][:, None]
+            dh = gr * dhp
+            dA = dh * B * dsilu(A)
+            dB = dh * silu(A)
+            dX[r0:r1] = q_rows(dA) @ qc.get("g_I", e) + q_rows(dB) @ qc.get("u_I", e)
+            Xt = q_tokens(X_rows[r0:r1])
+            parts = (q_tokens(dY_rows[r0:r1]).T @ q_tokens(gr * h),
+                     q_tokens(dA).T @ Xt, q_tokens(dB).T @ Xt)
+            for store, p in zip((dWd, dWg, dWu), parts):
+                store[e] = p if store[e] is None else store[e] + p
+        P = plan["pos"]
+        Tm = P.shape[0]
+        for t in range(Tm):
+            for j in range(k):
+                if P[t, j] >= 0:
+                    dx[sl.start + t] += dX[P[t, j]]
+                    dg[sl.start + t, j] = dg_rows[P[t, j]]
+    for e in range(E):
+        if dWg[e] is None:
+            dWg[e] = np.zeros(tuple(w_gate[e].shape))
+            dWu[e] = np.zeros(tuple(w_up[e].shape))
+            dWd[e] = np.zeros(tuple(w_down[e].shape))
+    out = {"dg": dg, "dw_gate": np.stack(dWg), "dw_up": np.stack(dWu), "dw_down": np.stack(dWd)}
+    if cache["shared"] is not None:
+        Sg, Su, Sd = (_f64(a) for a in cache["shared"])
+        As, Bs = xf @ Sg.T, xf @ Su.T
+        hs = silu(As) * Bs
+        dhs = dyf @ Sd
+        dAs = dhs * Bs * dsilu(As)
+        dBs = dhs * silu(As)
+        out["ds_down"] = dyf.T @ hs
+        out["ds_gate"] = dAs.T @ xf
+        out["ds_up"] = dBs.T @ xf
+        dx += dAs @ Sg + dBs @ Su
+    out["dx"] = dx
+    out["dlogits"] = route_backward(cache["topk_idx"], g, dg, E)
+    return out

@@ -1,0 +1,134 @@
+"""Pins of the MXFP8 layer oracle: row-local outputs do not depend on the minibatch
+size, the result stays within MX rounding of the exact layer, and each operand is
+blocked along its own contraction axis (operands whose rows or columns differ by
+many binades survive only when blocked along the right axis)."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import moe_mx
+
+
+def rand_layer(rng, T, H, I, E, std=0.3, shared=True):
+    d = {"x": rng.standard_normal((T, H)), "logits": rng.standard_normal((T, E)),
+         "w_gate": rng.standard_normal((E, I, H)) * std, "w_up": rng.standard_normal((E, I, H)) * std,
+         "w_down": rng.standard_normal((E, H, I)) * std, "dy": rng.standard_normal((T, H))}
+    d["shared"] = (rng.standard_normal((I, H)) * std, rng.standard_normal((I, H)) * std,
+                   rng.standard_normal((H, I)) * std) if shared else None
+    return d
+
+
+def run_mx(d, k, T_mb):
+    c = moe_mx.layer_forward_mx(d["x"], d["logits"], k, d["w_gate"], d["w_up"], d["w_down"],
+                                shared=d["shared"], T_mb=T_mb)
+    return c, moe_mx.layer_backward_mx(c, d["dy"])
+
+
+def test_row_local_outputs_do_not_depend_on_minibatch_size():
+    rng = np.random.default_rng(0)
+    d = rand_layer(rng, 96, 64, 64, 6)
+    ref_c, ref_g = run_mx(d, 2, 0)
+    for T_mb in (32, 40, 7):
+        c, g = run_mx(d, 2, T_mb)
+        np.testing.assert_allclose(c["y"], ref_c["y"], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(g["dx"], ref_g["dx"], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(g["dg"], ref_g["dg"], rtol=1e-11, atol=1e-12)
+
+
+def rel(a, b):
+    return np.linalg.norm(a - b) / np.linalg.norm(b)
+
+
+def test_within_mx_rounding_of_the_exact_layer():
+    rng = np.random.default_rng(1)
+    d = rand_layer(rng, 80, 64, 96, 5)
+    c, g = run_mx(d, 2, 32)
+    ce = oracle.layer_forward(d["x"], d["logits"], 2, d["w_gate"], d["w_up"], d["w_down"],
+                              shared=d["shared"])
+    ge = oracle.layer_backward(ce, d["dy"])
+    assert np.array_equal(c["topk_idx"], ce["topk_idx"])
+    # E4M3 keeps 3 mantissa bits: a few 2^-5 relative errors per product chain
+    for name, a, b in [("y", c["y"], ce["y"]), ("dx", g["dx"], ge["dx"]), ("dg", g["dg"], ge["dg"]),
+                       ("dw_gate", g["dw_gate"], ge["dw_gate"]), ("dw_down", g["dw_down"], ge["dw_down"]),
+                       ("ds_gate", g["ds_gate"], ge["ds_gate"])]:
+        r = rel(a, b)
+        assert r < 0.15, (name, r)
+        if name != "ds_gate":                 # the shared expert is not quantised
+            assert r > 1e-4, (name, r)
+        else:
+            assert r < 1e-12
+
+
+def binade_scaled(rng, shape, axis):
+    """Gaussian entries whose slices along `axis` differ by 2^+-10 from one to the next."""
+    a = rng.standard_normal(shape)
+    s = np.where(np.arange(shape[axis]) % 2 == 0, 2.0 ** 10, 2.0 ** -10)
+    sh = [1] * len(shape)
+    sh[axis] = shape[axis]
+    return a * s.reshape(sh)
+
+
+def test_forward_weights_are_blocked_along_H():
+    """W_g rows alternate by 2^20: per-row blocks (along H) keep every row."""
+    rng = np.random.default_rng(2)
+    T, H, I, E = 40, 64, 64, 1
+    d = rand_layer(rng, T, H, I, E, shared=False)
+    d["w_gate"][0] = binade_scaled(rng, (I, H), 0)
+    c, _ = run_mx(d, 1, 0)
+    A_exact = d["x"] @ d["w_gate"][0].T
+    A_mx = c["minibatches"][0]["A"]
+    col_err = np.linalg.norm(A_mx - A_exact, axis=0) / np.linalg.norm(A_exact, axis=0)
+    assert col_err.max() < 0.1
+
+
+def test_tokens_are_blocked_along_H_in_the_forward():
+    rng = np.random.default_rng(3)
+    T, H, I, E = 40, 64, 64, 1
+    d = rand_layer(rng, T, H, I, E, shared=False)
+    d["x"] = binade_scaled(rng, (T, H), 0)                 # tokens differ by 2^20
+    c, _ = run_mx(d, 1, 0)
+    A_exact = d["x"] @ d["w_gate"][0].T
+    A_mx = c["minibatches"][0]["A"]
+    row_err = np.linalg.norm(A_mx - A_exact, axis=1) / np.linalg.norm(A_exact, axis=1)
+    assert row_err.max() < 0.1
+
+
+def test_dgrad_up_weights_are_blocked_along_I():
+    """W_g columns alternate by 2^20: dX = dA W_g needs W_g blocked along I."""
+    rng = np.random.default_rng(4)
+    T, H, I, E = 40, 64, 64, 1
+    d = rand_layer(rng, T, H, I, E, shared=False)
+    d["w_gate"][0] = binade_scaled(rng, (I, H), 1)
+    d["w_up"][0] = binade_scaled(rng, (I, H), 1)
+    c, g = run_mx(d, 1, 0)
+    ce = oracle.layer_forward(d["x"], d["logits"], 1, d["w_gate"], d["w_up"], d["w_down"])
+    ge = oracle.layer_backward(ce, d["dy"])
+    col_err = np.linalg.norm(g["dx"] - ge["dx"], axis=0) / np.linalg.norm(ge["dx"], axis=0)
+    assert col_err.max() < 0.25
+
+
+def test_weight_gradients_are_blocked_along_tokens():
+    """Rows of x alternate by 2^20 across tokens; dW_g = Q_t(dA)^T Q_t(X) blocked along
+    tokens would flush the small tokens' contributions in a shared block, so each
+    block is checked to hold tokens of one binade: use 32 big then 32 small tokens."""
+    rng = np.random.default_rng(5)
+    T, H, I, E = 64, 64, 64, 1
+    d = rand_layer(rng, T, H, I, E, shared=False)
+    big = np.arange(T) < 32
+    d["x"] = d["x"] * np.where(big, 1.0, 2.0 ** -12)[:, None]
+    d["dy"] = d["dy"] * np.where(big, 2.0 ** -12, 1.0)[:, None]
+    c, g = run_mx(d, 1, 0)
+    ce = oracle.layer_forward(d["x"], d["logits"], 1, d["w_gate"], d["w_up"], d["w_down"])
+    ge = oracle.layer_backward(ce, d["dy"])
+    # both binades contribute comparably (x*dy ~ 2^-12 each); blocks of 32 tokens
+    # from the segment start keep each binade in its own block
+    assert rel(g["dw_gate"], ge["dw_gate"]) < 0.15
+
+
+def test_q_tokens_blocks_start_at_first_row():
+    a = np.ones((40, 4))
+    a[35] = 2.0 ** 20                       # one huge row in the second block
+    q = moe_mx.q_tokens(a)
+    assert np.all(q[:32] == 1.0)            # first block untouched by the huge row
+    assert np.all(q[32:35] == 0.0) and np.all(q[36:] == 0.0)
+    assert np.all(q[35] == 2.0 ** 20)
