@@ -64,7 +64,9 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2 } moe_dtype;
  * I_shared intermediate of the always-on shared expert (0 = none),
  * T_minibatch tokens per minibatch (0 = T).
  * Limits: 0 <= T, T*k < 2^31, 1 <= E <= 1024, 1 <= k <= min(E, 32);
- * H, I and I_shared multiples of 128 for the expert GEMMs. */
+ * H, I and I_shared multiples of 128 for the expert GEMMs; the bf16 and fp32
+ * layer calls take one minibatch (T_minibatch 0 or >= T), the MXFP8 calls at
+ * most 8. */
 typedef struct {
   int32_t T, H, I, E, k;
   int32_t I_shared;
@@ -84,12 +86,18 @@ typedef struct {
  *   err_flag  int32 [1]      1 if some expert id was outside [0, E), else 0
  *   active    int32 [E]      ids of the experts with rows, ascending; n_active valid
  *   n_active  int32 [1]
- *   scratch   per-chunk histograms used while building the plan */
+ *   tile_first int32 [E+1]   index of each expert's first entry in `tiles`
+ *   scratch   per-chunk histograms used while building the plan
+ * With T_minibatch in (0, T) the tokens form n_minibatch = ceil(T / T_minibatch)
+ * consecutive minibatches and the plan buffer holds one such table per minibatch
+ * (sized for T_minibatch tokens; minibatch m at byte m * sub_plan_bytes, covering
+ * tokens m * T_minibatch ..); R above is then T_minibatch * k.  Otherwise there is
+ * one table and T_minibatch reads T. */
 typedef struct {
   size_t counts, offsets, src_token, src_slot, pos, tiles, n_tiles, err_flag, active, n_active,
-      scratch;
-  size_t total_bytes;
-  int32_t tile_m, max_tiles, chunk_pairs, n_chunks;
+      tile_first, scratch;
+  size_t sub_plan_bytes, total_bytes;
+  int32_t tile_m, max_tiles, chunk_pairs, n_chunks, n_minibatch, T_minibatch;
 } moe_plan_layout;
 
 const char* moe_status_str(moe_status s);
@@ -261,6 +269,55 @@ moe_status moe_backward_f32(const moe_shape* shape, const void* plan, const floa
                             float* dw_gate, float* dw_up, float* dw_down, float* ds_gate,
                             float* ds_up, float* ds_down, float* d_topk_w, void* ws,
                             size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------ layer, MXFP8
+ * MXFP8 training with the conversion inside the kernels and the shared expert in
+ * BF16 (sebask.de, § Determinismus und MXFP8-Unterstützung; stamatios.com,
+ * § Outras características).  Every operand of the six expert GEMMs is E4M3 with
+ * one E8M0 scale per 32 elements along that GEMM's K (OCP MX v1.0 rule: scale
+ * exponent floor(log2 amax) - 8, elements rounded to nearest even and saturated):
+ * x and dy along H (quantised while they are gathered into the ring of minibatch
+ * slots), h along I, dZ = (dA | dB) along 2I, the weights along H or I (both
+ * orientations, from moe_quantize_weights_mxfp8), and the wgrad operands along
+ * the tokens of each expert's segment in each minibatch (blocks of 32 rows from
+ * the segment's first row, zero-padded).  Tokens run in minibatches of
+ * shape->T_minibatch (at most 8 per call; 0 = one minibatch) through a ring of two
+ * slots of T_minibatch * k dispatched rows (stamatios.com, § Ring token buffers
+ * and § Granularidade do overlap); the plan must come from moe_plan with the same
+ * shape.  Weight gradients are summed over all minibatches in one pass. */
+
+/* Bytes of the quantised expert weights (both orientations, codes and scales). */
+size_t moe_mx_weights_bytes(const moe_shape* shape);
+
+/* Quantise w_gate, w_up [E, I, H] and w_down [E, H, I] (bf16) into `wq`: w_gate
+ * and w_up along H, w_down along I (forward), w_down along H and w_gate, w_up along
+ * I (backward, stored transposed). */
+moe_status moe_quantize_weights_mxfp8(const moe_shape* shape, const void* w_gate,
+                                      const void* w_up, const void* w_down, void* wq,
+                                      hipStream_t stream);
+
+/* Quantise a bf16 matrix src [rows, cols].  axis = 1: blocks of 32 along cols,
+ * q [rows, cols], scales [rows, cols / 32].  axis = 0: blocks of 32 along rows,
+ * written transposed: q [cols, rows], scales [cols, rows / 32]. */
+moe_status moe_quantize_mxfp8(const void* src, int64_t rows, int64_t cols, int axis, uint8_t* q,
+                              uint8_t* scales, hipStream_t stream);
+
+/* As moe_forward_bf16 with the expert weights replaced by `wq`; the shared-expert
+ * weights s_* stay bf16.  saved: moe_saved_bytes(shape, MOE_MXFP8); ws:
+ * moe_workspace_bytes(shape, MOE_MXFP8, 0). */
+moe_status moe_forward_mxfp8(const moe_shape* shape, const void* plan, const void* x,
+                             const float* topk_w, const void* wq, const void* s_gate,
+                             const void* s_up, const void* s_down, void* y, void* saved, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+/* As moe_backward_bf16 with the expert weights replaced by `wq`; weight gradients
+ * are bf16 and overwritten. ws: moe_workspace_bytes(shape, MOE_MXFP8, 1). */
+moe_status moe_backward_mxfp8(const moe_shape* shape, const void* plan, const void* x,
+                              const float* topk_w, const void* wq, const void* s_gate,
+                              const void* s_up, const void* s_down, const void* saved,
+                              const void* dy, void* dx, void* dw_gate, void* dw_up, void* dw_down,
+                              void* ds_gate, void* ds_up, void* ds_down, float* d_topk_w, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

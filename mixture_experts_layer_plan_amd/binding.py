@@ -38,8 +38,10 @@ class moe_shape(ctypes.Structure):
 class moe_plan_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("counts", "offsets", "src_token", "src_slot", "pos",
                                                 "tiles", "n_tiles", "err_flag", "active",
-                                                "n_active", "scratch", "total_bytes")] + \
-               [(n, ctypes.c_int32) for n in ("tile_m", "max_tiles", "chunk_pairs", "n_chunks")]
+                                                "n_active", "tile_first", "scratch",
+                                                "sub_plan_bytes", "total_bytes")] + \
+               [(n, ctypes.c_int32) for n in ("tile_m", "max_tiles", "chunk_pairs", "n_chunks",
+                                              "n_minibatch", "T_minibatch")]
 
 
 _P = ctypes.c_void_p
@@ -76,6 +78,11 @@ _SIGS = {
     "moe_forward_f32": (_I, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "moe_backward_bf16": (_I, [_S] + [_P] * 20 + [_Z, _P]),
     "moe_backward_f32": (_I, [_S] + [_P] * 20 + [_Z, _P]),
+    "moe_mx_weights_bytes": (_Z, [_S]),
+    "moe_quantize_weights_mxfp8": (_I, [_S, _P, _P, _P, _P, _P]),
+    "moe_quantize_mxfp8": (_I, [_P, ctypes.c_int64, ctypes.c_int64, _I, _P, _P, _P]),
+    "moe_forward_mxfp8": (_I, [_S] + [_P] * 11 + [_Z, _P]),
+    "moe_backward_mxfp8": (_I, [_S] + [_P] * 18 + [_Z, _P]),
 }
 
 _lib = None
@@ -245,6 +252,34 @@ def moe_backward_f32(s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_d
          saved, dy, dx, dw_gate, dw_up, dw_down, ds_gate, ds_up, ds_down, d_topk_w, ws, stream)
 
 
+def moe_mx_weights_bytes(s: moe_shape) -> int:
+    return lib().moe_mx_weights_bytes(ctypes.byref(s))
+
+
+def moe_quantize_weights_mxfp8(s, w_gate, w_up, w_down, wq, stream=None):
+    _call("moe_quantize_weights_mxfp8", ctypes.byref(s), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+          _ptr(wq), _stream(stream))
+
+
+def moe_quantize_mxfp8(src, rows, cols, axis, q, scales, stream=None):
+    _call("moe_quantize_mxfp8", _ptr(src), int(rows), int(cols), int(axis), _ptr(q), _ptr(scales),
+          _stream(stream))
+
+
+def moe_forward_mxfp8(s, plan, x, topk_w, wq, s_gate, s_up, s_down, y, saved, ws, stream=None):
+    _call("moe_forward_mxfp8", ctypes.byref(s), _ptr(plan), _ptr(x), _ptr(topk_w), _ptr(wq),
+          _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(y), _ptr(saved), _ptr(ws),
+          0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+
+
+def moe_backward_mxfp8(s, plan, x, topk_w, wq, s_gate, s_up, s_down, saved, dy, dx, dw_gate,
+                       dw_up, dw_down, ds_gate, ds_up, ds_down, d_topk_w, ws, stream=None):
+    _call("moe_backward_mxfp8", ctypes.byref(s), _ptr(plan), _ptr(x), _ptr(topk_w), _ptr(wq),
+          _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(saved), _ptr(dy), _ptr(dx), _ptr(dw_gate),
+          _ptr(dw_up), _ptr(dw_down), _ptr(ds_gate), _ptr(ds_up), _ptr(ds_down), _ptr(d_topk_w),
+          _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+
+
 # ------------------------------------------------------------ kernel timing
 _hip = None
 
@@ -307,17 +342,20 @@ class KernelTrace:
 
 
 # ------------------------------------------------------------ buffer helpers
-def plan_views(s: moe_shape, plan: torch.Tensor) -> dict:
-    """int32 views of the arrays inside a plan buffer (uint8 tensor)."""
+def plan_views(s: moe_shape, plan: torch.Tensor, minibatch: int = 0) -> dict:
+    """int32 views of the arrays of one minibatch's table inside a plan buffer
+    (uint8 tensor); ``T`` is that minibatch's token count."""
     L = moe_plan_layout_of(s)
-    R = s.T * s.k
+    T = min(L.T_minibatch, s.T - minibatch * L.T_minibatch)
+    R = T * s.k
+    sub = plan[minibatch * L.sub_plan_bytes:(minibatch + 1) * L.sub_plan_bytes]
 
     def view(off, n):
-        return plan[off:off + 4 * n].view(torch.int32)
+        return sub[off:off + 4 * n].view(torch.int32)
 
     return {"counts": view(L.counts, s.E), "offsets": view(L.offsets, s.E + 1),
             "src_token": view(L.src_token, R), "src_slot": view(L.src_slot, R),
-            "pos": view(L.pos, R).view(s.T, s.k), "tiles": view(L.tiles, 2 * L.max_tiles).view(-1, 2),
+            "pos": view(L.pos, R).view(T, s.k), "tiles": view(L.tiles, 2 * L.max_tiles).view(-1, 2),
             "n_tiles": view(L.n_tiles, 1), "err_flag": view(L.err_flag, 1),
             "active": view(L.active, s.E), "n_active": view(L.n_active, 1),
-            "tile_m": L.tile_m}
+            "tile_first": view(L.tile_first, s.E + 1), "tile_m": L.tile_m, "T": T}

@@ -4,10 +4,14 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/moe.h"
 #include "internal.hpp"
 
 using namespace moe;
+
+typedef uint16_t bf16_t_host;  // bfloat16 bits on the host side
 
 namespace moe {
 
@@ -61,10 +65,19 @@ moe_status check_shape(const moe_shape* s, bool need_gemm_dims) {
   return MOE_OK;
 }
 
+// Minibatches: T_minibatch in (0, T) splits the tokens into ceil(T / T_minibatch)
+// consecutive minibatches, each with its own plan; otherwise one minibatch of T.
+int n_minibatches(const moe_shape* s) {
+  if (s->T_minibatch <= 0 || s->T_minibatch >= s->T) return 1;
+  return (s->T + s->T_minibatch - 1) / s->T_minibatch;
+}
+int minibatch_tokens(const moe_shape* s) { return n_minibatches(s) > 1 ? s->T_minibatch : s->T; }
+
+// Layout of one minibatch plan (sized for minibatch_tokens(s) tokens).
 moe_plan_layout plan_layout(const moe_shape* s) {
   moe_plan_layout L;
   memset(&L, 0, sizeof(L));
-  const int64_t R = (int64_t)s->T * s->k;
+  const int64_t R = (int64_t)minibatch_tokens(s) * s->k;
   L.tile_m = GEMM_TILE_M;
   L.max_tiles = (int32_t)(R / GEMM_TILE_M + (R < s->E ? R : s->E) + 1);
   L.chunk_pairs = PLAN_CHUNK;
@@ -80,8 +93,12 @@ moe_plan_layout plan_layout(const moe_shape* s) {
   L.err_flag = c.take(sizeof(int32_t));
   L.active = c.take(sizeof(int32_t) * s->E);
   L.n_active = c.take(sizeof(int32_t));
+  L.tile_first = c.take(sizeof(int32_t) * (s->E + 1));
   L.scratch = c.take(sizeof(int32_t) * ((size_t)L.n_chunks * s->E + L.n_chunks));
-  L.total_bytes = c.off;
+  L.sub_plan_bytes = c.off;
+  L.n_minibatch = n_minibatches(s);
+  L.T_minibatch = minibatch_tokens(s);
+  L.total_bytes = L.sub_plan_bytes * L.n_minibatch;
   return L;
 }
 
@@ -96,12 +113,14 @@ const P* at(const void* base, size_t off) {
 
 struct PlanView {
   const int32_t *counts, *offsets, *src_token, *src_slot, *pos, *tiles, *n_tiles, *active,
-      *n_active;
+      *n_active, *tile_first;
   int max_tiles;
 };
 
-PlanView view_plan(const moe_shape* s, const void* plan) {
+// View of minibatch m's plan.
+PlanView view_plan(const moe_shape* s, const void* plan_all, int m = 0) {
   const moe_plan_layout L = plan_layout(s);
+  const void* plan = (const char*)plan_all + (size_t)m * L.sub_plan_bytes;
   PlanView v;
   v.counts = at<int32_t>(plan, L.counts);
   v.offsets = at<int32_t>(plan, L.offsets);
@@ -112,6 +131,7 @@ PlanView view_plan(const moe_shape* s, const void* plan) {
   v.n_tiles = at<int32_t>(plan, L.n_tiles);
   v.active = at<int32_t>(plan, L.active);
   v.n_active = at<int32_t>(plan, L.n_active);
+  v.tile_first = at<int32_t>(plan, L.tile_first);
   v.max_tiles = L.max_tiles;
   return v;
 }
@@ -225,7 +245,7 @@ moe_status forward_impl(moe_dtype dt, const moe_shape* s, const void* plan, cons
                         void* ws, size_t ws_bytes, hipStream_t st) {
   moe_status rc = check_shape(s, true);
   if (rc != MOE_OK) return rc;
-  if (s->T_minibatch != 0 && s->T_minibatch != s->T) return MOE_E_UNSUPPORTED;
+  if (n_minibatches(s) != 1) return MOE_E_UNSUPPORTED;
   if (any_null({plan, wg, wu, wd}) || any_null_rows(s, {x, topk_w, y, saved, ws}))
     return MOE_E_NULL;
   if (s->I_shared && any_null({sg, su, sd})) return MOE_E_NULL;
@@ -267,7 +287,7 @@ moe_status backward_impl(moe_dtype dt, const moe_shape* s, const void* plan, con
                          hipStream_t st) {
   moe_status rc = check_shape(s, true);
   if (rc != MOE_OK) return rc;
-  if (s->T_minibatch != 0 && s->T_minibatch != s->T) return MOE_E_UNSUPPORTED;
+  if (n_minibatches(s) != 1) return MOE_E_UNSUPPORTED;
   if (any_null({plan, wg, wu, wd, dwg, dwu, dwd}) ||
       any_null_rows(s, {x, topk_w, saved, dy, dx, d_topk_w, ws}))
     return MOE_E_NULL;
@@ -326,6 +346,282 @@ moe_status backward_impl(moe_dtype dt, const moe_shape* s, const void* plan, con
   return MOE_OK;
 }
 
+moe_status plan_one(const moe_shape* s, const moe_plan_layout& L, int T_m,
+                           const int32_t* topk_idx, void* plan, hipStream_t st) {
+  PlanPtrs p;
+  p.counts = at<int32_t>(plan, L.counts);
+  p.offsets = at<int32_t>(plan, L.offsets);
+  p.src_token = at<int32_t>(plan, L.src_token);
+  p.src_slot = at<int32_t>(plan, L.src_slot);
+  p.pos = at<int32_t>(plan, L.pos);
+  p.tiles = at<int32_t>(plan, L.tiles);
+  p.n_tiles = at<int32_t>(plan, L.n_tiles);
+  p.err_flag = at<int32_t>(plan, L.err_flag);
+  p.active = at<int32_t>(plan, L.active);
+  p.n_active = at<int32_t>(plan, L.n_active);
+  p.tile_first = at<int32_t>(plan, L.tile_first);
+  p.chunk_hist = at<int32_t>(plan, L.scratch);
+  p.chunk_invalid = p.chunk_hist + (size_t)L.n_chunks * s->E;
+  p.n_chunks = (int)(((int64_t)T_m * s->k + PLAN_CHUNK - 1) / PLAN_CHUNK);
+  p.max_tiles = L.max_tiles;
+  return hip_status(launch_plan(topk_idx, T_m, s->k, s->E, p, st));
+}
+
+
+// ------------------------------------------------------------------ MXFP8
+// Quantised weights: forward orientation (blocks along each GEMM's K) and the
+// transposed backward orientation, each an E4M3 array plus its scale bytes.
+//   wg, wu [E, I, H] along H;  wd [E, H, I] along I;
+//   wdT [E, I, H] = W_d^T along H;  wgT, wuT [E, H, I] = W_g^T, W_u^T along I.
+struct MxWeights {
+  size_t wg8, wgs, wu8, wus, wd8, wds, wdT8, wdTs, wgT8, wgTs, wuT8, wuTs, total;
+};
+MxWeights mx_weights_layout(const moe_shape* s) {
+  const size_t n = (size_t)s->E * s->I * s->H, ns = n / 32;
+  Carve c;
+  MxWeights L;
+  L.wg8 = c.take(n); L.wgs = c.take(ns);
+  L.wu8 = c.take(n); L.wus = c.take(ns);
+  L.wd8 = c.take(n); L.wds = c.take(ns);
+  L.wdT8 = c.take(n); L.wdTs = c.take(ns);
+  L.wgT8 = c.take(n); L.wgTs = c.take(ns);
+  L.wuT8 = c.take(n); L.wuTs = c.take(ns);
+  L.total = c.off;
+  return L;
+}
+
+// Saved by the MX forward: Z fp32 of every minibatch (minibatch m's rows at
+// m * R_mb) and Zs fp32 [T, 2 Is].
+struct MxSaved {
+  size_t Z, Zs, total;
+};
+MxSaved mx_saved_layout(const moe_shape* s) {
+  const size_t R_mb = (size_t)minibatch_tokens(s) * s->k;
+  Carve c;
+  MxSaved L;
+  L.Z = c.take((size_t)n_minibatches(s) * R_mb * 2 * s->I * sizeof(float));
+  L.Zs = c.take((size_t)s->T * 2 * s->I_shared * sizeof(float));
+  L.total = c.off;
+  return L;
+}
+
+// Forward workspace: the ring of two minibatch slots of dispatched MX rows, the
+// quantised h, Y, and the shared expert's h and output of one minibatch.
+struct MxFwdWs {
+  size_t ring8[2], rings[2], hq, hs, Y, hs_sh, ys, total;
+};
+MxFwdWs mx_fwd_ws(const moe_shape* s) {
+  const size_t Tm = minibatch_tokens(s), R = Tm * s->k, H = s->H, I = s->I;
+  Carve c;
+  MxFwdWs L;
+  for (int i = 0; i < 2; ++i) {
+    L.ring8[i] = c.take(R * H);
+    L.rings[i] = c.take(R * H / 32);
+  }
+  L.hq = c.take(R * I);
+  L.hs = c.take(R * I / 32);
+  L.Y = c.take(R * H * 2);
+  L.hs_sh = c.take(Tm * s->I_shared * 2);
+  L.ys = c.take(s->I_shared ? Tm * H * 2 : 0);
+  L.total = c.off;
+  return L;
+}
+
+// Backward workspace: per-minibatch buffers (dYu ring, dZ bf16 and MX, g h, dg
+// partials, dX) and the token-quantised wgrad operands of all minibatches
+// (transposed, tile-padded token axis of Kp = n_mb * max_tiles * 128 bytes).
+struct MxBwdWs {
+  size_t ring8[2], rings[2], dZ, dZ8, dZs, gh, dgp, dX;
+  size_t dYuT8, dYuTs, ghT8, ghTs, dZT8, dZTs, XT8, XTs;
+  size_t counts_all, active, n_active;
+  size_t dZs_sh, hs_sh, dxs, total;
+  size_t Kp;
+};
+MxBwdWs mx_bwd_ws(const moe_shape* s) {
+  const moe_plan_layout P = plan_layout(s);
+  const size_t Tm = minibatch_tokens(s), R = Tm * s->k, H = s->H, I = s->I, T = s->T;
+  const size_t Kp = (size_t)n_minibatches(s) * P.max_tiles * 128;
+  Carve c;
+  MxBwdWs L;
+  for (int i = 0; i < 2; ++i) {
+    L.ring8[i] = c.take(R * H);
+    L.rings[i] = c.take(R * H / 32);
+  }
+  L.dZ = c.take(R * 2 * I * 2);
+  L.dZ8 = c.take(R * 2 * I);
+  L.dZs = c.take(R * 2 * I / 32);
+  L.gh = c.take(R * I * 2);
+  L.dgp = c.take(R * (I / 128) * sizeof(float));
+  L.dX = c.take(R * H * 2);
+  L.dYuT8 = c.take(H * Kp); L.dYuTs = c.take(H * Kp / 32);
+  L.ghT8 = c.take(I * Kp); L.ghTs = c.take(I * Kp / 32);
+  L.dZT8 = c.take(2 * I * Kp); L.dZTs = c.take(2 * I * Kp / 32);
+  L.XT8 = c.take(H * Kp); L.XTs = c.take(H * Kp / 32);
+  L.counts_all = c.take(sizeof(int32_t) * s->E);
+  L.active = c.take(sizeof(int32_t) * s->E);
+  L.n_active = c.take(sizeof(int32_t));
+  L.dZs_sh = c.take(T * 2 * s->I_shared * 2);
+  L.hs_sh = c.take(T * s->I_shared * 2);
+  L.dxs = c.take(s->I_shared ? T * H * 2 : 0);
+  L.total = c.off;
+  L.Kp = Kp;
+  return L;
+}
+
+moe_status check_mx(const moe_shape* s) {
+  moe_status rc = check_shape(s, true);
+  if (rc != MOE_OK) return rc;
+  if (n_minibatches(s) > MX_MAX_MB) return MOE_E_SHAPE;
+  return MOE_OK;
+}
+
+moe_status forward_mx_impl(const moe_shape* s, const void* plan, const void* x,
+                           const float* topk_w, const void* wq, const void* sg, const void* su,
+                           const void* sd, void* y, void* saved, void* ws, size_t ws_bytes,
+                           hipStream_t st) {
+  moe_status rc = check_mx(s);
+  if (rc != MOE_OK) return rc;
+  if (any_null({plan, wq}) || any_null_rows(s, {x, topk_w, y, saved, ws})) return MOE_E_NULL;
+  if (s->I_shared && any_null({sg, su, sd})) return MOE_E_NULL;
+  if (!all_aligned({plan, x, topk_w, wq, sg, su, sd, y, saved, ws})) return MOE_E_ALIGN;
+  const MxFwdWs W = mx_fwd_ws(s);
+  if (ws_bytes < W.total) return MOE_E_WORKSPACE;
+  if (s->T == 0) return MOE_OK;
+  const MxWeights Q = mx_weights_layout(s);
+  const MxSaved S = mx_saved_layout(s);
+  const int H = s->H, I = s->I, k = s->k, nmb = n_minibatches(s), Tmb = minibatch_tokens(s);
+  const uint8_t* q = (const uint8_t*)wq;
+  for (int m = 0; m < nmb; ++m) {
+    const int T_m = std::min(Tmb, s->T - m * Tmb), R_m = T_m * k;
+    const PlanView v = view_plan(s, plan, m);
+    const GroupInfo g = grouped(s, v);
+    const bf16_t_host* xm = (const bf16_t_host*)x + (size_t)m * Tmb * H;
+    uint8_t* X8 = at<uint8_t>(ws, W.ring8[m & 1]);
+    uint8_t* Xs = at<uint8_t>(ws, W.rings[m & 1]);
+    float* Z = at<float>(saved, S.Z) + (size_t)m * Tmb * k * 2 * I;
+    uint8_t* hq = at<uint8_t>(ws, W.hq);
+    uint8_t* hs = at<uint8_t>(ws, W.hs);
+    void* Y = at<char>(ws, W.Y);
+    // dispatch into the ring slot, quantised along H on the way
+    MOE_TRY(launch_quant_rows(1, xm, v.src_token, v.offsets + s->E, R_m, H, X8, Xs, st));
+    MOE_TRY(launch_mx_up_swiglu(g, X8, Xs, q + Q.wg8, q + Q.wgs, q + Q.wu8, q + Q.wus, H, I, Z,
+                                hq, hs, st));
+    MOE_TRY(launch_mx_down(g, hq, hs, q + Q.wd8, q + Q.wds, H, I, Y, st));
+    void* ys = nullptr;
+    if (s->I_shared) {
+      const GroupInfo gs = dense(T_m);
+      float* Zs = at<float>(saved, S.Zs) + (size_t)m * Tmb * 2 * s->I_shared;
+      void* hsh = at<char>(ws, W.hs_sh);
+      ys = at<char>(ws, W.ys);
+      MOE_TRY(launch_gemm_up_swiglu(1, gs, xm, sg, su, H, s->I_shared, Zs, hsh, st));
+      MOE_TRY(launch_gemm_down(1, gs, hsh, sd, H, s->I_shared, ys, st));
+    }
+    MOE_TRY(launch_combine_bf16(Y, v.pos, topk_w + (size_t)m * Tmb * k, ys,
+                                (bf16_t_host*)y + (size_t)m * Tmb * H, T_m, k, H, st));
+  }
+  return MOE_OK;
+}
+
+moe_status backward_mx_impl(const moe_shape* s, const void* plan, const void* x,
+                            const float* topk_w, const void* wq, const void* sg, const void* su,
+                            const void* sd, const void* saved, const void* dy, void* dx,
+                            void* dwg, void* dwu, void* dwd, void* dsg, void* dsu, void* dsd,
+                            float* d_topk_w, void* ws, size_t ws_bytes, hipStream_t st) {
+  moe_status rc = check_mx(s);
+  if (rc != MOE_OK) return rc;
+  if (any_null({plan, wq, dwg, dwu, dwd}) || any_null_rows(s, {x, topk_w, saved, dy, dx, d_topk_w, ws}))
+    return MOE_E_NULL;
+  if (s->I_shared && any_null({sg, su, sd, dsg, dsu, dsd})) return MOE_E_NULL;
+  if (!all_aligned({plan, x, topk_w, wq, sg, su, sd, saved, dy, dx, dwg, dwu, dwd, dsg, dsu, dsd,
+                    d_topk_w, ws}))
+    return MOE_E_ALIGN;
+  const MxBwdWs W = mx_bwd_ws(s);
+  if (ws_bytes < W.total) return MOE_E_WORKSPACE;
+  const MxWeights Q = mx_weights_layout(s);
+  const MxSaved S = mx_saved_layout(s);
+  const moe_plan_layout P = plan_layout(s);
+  const int H = s->H, I = s->I, k = s->k, nmb = n_minibatches(s), Tmb = minibatch_tokens(s);
+  const uint8_t* q = (const uint8_t*)wq;
+  // shared expert (bf16, dense over all tokens)
+  void* dxs = nullptr;
+  if (s->I_shared) {
+    const int Is = s->I_shared;
+    const GroupInfo gs = dense(s->T);
+    const float* Zs = at<float>(saved, S.Zs);
+    void* dZs = at<char>(ws, W.dZs_sh);
+    void* hsh = at<char>(ws, W.hs_sh);
+    dxs = at<char>(ws, W.dxs);
+    MOE_TRY(launch_gemm_dgrad_down(1, gs, dy, sd, Zs, nullptr, H, Is, 1, dZs, hsh, nullptr, st));
+    MOE_TRY(launch_gemm_wgrad_down(1, gs, dy, hsh, H, Is, dsd, st));
+    MOE_TRY(launch_gemm_dgrad_up(1, gs, dZs, sg, su, H, Is, dxs, st));
+    MOE_TRY(launch_gemm_wgrad_up(1, gs, dZs, x, H, Is, dsg, dsu, st));
+  }
+  const int32_t* counts[MX_MAX_MB];
+  MbPlans mp;
+  mp.n_mb = nmb;
+  mp.max_tiles = P.max_tiles;
+  for (int m = nmb - 1; m >= 0; --m) {
+    const int T_m = std::min(Tmb, s->T - m * Tmb), R_m = T_m * k;
+    const PlanView v = view_plan(s, plan, m);
+    counts[m] = v.counts;
+    mp.tile_first[m] = v.tile_first;
+    if (T_m <= 0) continue;
+    const GroupInfo g = grouped(s, v);
+    const size_t tok0 = (size_t)m * Tmb;
+    const bf16_t_host* dym = (const bf16_t_host*)dy + tok0 * H;
+    const bf16_t_host* xm = (const bf16_t_host*)x + tok0 * H;
+    uint8_t* dYu8 = at<uint8_t>(ws, W.ring8[m & 1]);
+    uint8_t* dYus = at<uint8_t>(ws, W.rings[m & 1]);
+    const float* Z = at<float>(saved, S.Z) + tok0 * k * 2 * I;
+    void* dZ = at<char>(ws, W.dZ);
+    uint8_t* dZ8 = at<uint8_t>(ws, W.dZ8);
+    uint8_t* dZsc = at<uint8_t>(ws, W.dZs);
+    void* gh = at<char>(ws, W.gh);
+    float* dgp = at<float>(ws, W.dgp);
+    void* dX = at<char>(ws, W.dX);
+    const size_t kofs = (size_t)m * P.max_tiles * 128;
+    // reverse-combine into the ring slot, quantised along H
+    MOE_TRY(launch_quant_rows(1, dym, v.src_token, v.offsets + s->E, R_m, H, dYu8, dYus, st));
+    MOE_TRY(launch_mx_dgrad_down(g, dYu8, dYus, q + Q.wdT8, q + Q.wdTs, Z, topk_w + tok0 * k, H,
+                                 I, k, dZ, dZ8, dZsc, gh, dgp, st));
+    MOE_TRY(launch_dg_reduce(dgp, v.pos, R_m, I / 128, d_topk_w + tok0 * k, st));
+    // wgrad operands of this minibatch, quantised along its tokens
+    MOE_TRY(launch_quant_tokens(dym, v.src_token, H, v.tiles, v.n_tiles, v.offsets, P.max_tiles,
+                                H, W.Kp, kofs, at<uint8_t>(ws, W.dYuT8), at<uint8_t>(ws, W.dYuTs),
+                                st));
+    MOE_TRY(launch_quant_tokens(xm, v.src_token, H, v.tiles, v.n_tiles, v.offsets, P.max_tiles, H,
+                                W.Kp, kofs, at<uint8_t>(ws, W.XT8), at<uint8_t>(ws, W.XTs), st));
+    MOE_TRY(launch_quant_tokens(gh, nullptr, I, v.tiles, v.n_tiles, v.offsets, P.max_tiles, I,
+                                W.Kp, kofs, at<uint8_t>(ws, W.ghT8), at<uint8_t>(ws, W.ghTs), st));
+    MOE_TRY(launch_quant_tokens(dZ, nullptr, 2 * I, v.tiles, v.n_tiles, v.offsets, P.max_tiles,
+                                2 * I, W.Kp, kofs, at<uint8_t>(ws, W.dZT8), at<uint8_t>(ws, W.dZTs),
+                                st));
+    MOE_TRY(launch_mx_dgrad_up(g, dZ8, dZsc, q + Q.wgT8, q + Q.wgTs, q + Q.wuT8, q + Q.wuTs, H, I,
+                               dX, st));
+    MOE_TRY(launch_combine_bf16(dX, v.pos, nullptr,
+                                dxs ? (const bf16_t_host*)dxs + tok0 * H : nullptr,
+                                (bf16_t_host*)dx + tok0 * H, T_m, k, H, st));
+  }
+  int32_t* counts_all = at<int32_t>(ws, W.counts_all);
+  int32_t* active = at<int32_t>(ws, W.active);
+  int32_t* n_active = at<int32_t>(ws, W.n_active);
+  MOE_TRY(launch_mb_union(counts, nmb, s->E, counts_all, active, n_active, st));
+  mp.active = active;
+  mp.n_active = n_active;
+  {
+    void* bufs[3] = {dwg, dwu, dwd};
+    const size_t stride[3] = {(size_t)I * H * 2, (size_t)I * H * 2, (size_t)H * I * 2};
+    MOE_TRY(launch_zero_empty_experts(counts_all, s->E, bufs, stride, st));
+  }
+  MOE_TRY(launch_mx_wgrad("mx_gemm_wgrad_down", mp, s->E, at<uint8_t>(ws, W.dYuT8),
+                          at<uint8_t>(ws, W.dYuTs), at<uint8_t>(ws, W.ghT8),
+                          at<uint8_t>(ws, W.ghTs), H, I, H, dwd, nullptr, st));
+  MOE_TRY(launch_mx_wgrad("mx_gemm_wgrad_up", mp, s->E, at<uint8_t>(ws, W.dZT8),
+                          at<uint8_t>(ws, W.dZTs), at<uint8_t>(ws, W.XT8), at<uint8_t>(ws, W.XTs),
+                          2 * I, H, I, dwg, dwu, st));
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -359,13 +655,75 @@ size_t moe_plan_bytes(const moe_shape* shape) {
 }
 
 size_t moe_saved_bytes(const moe_shape* shape, moe_dtype dtype) {
-  if (check_shape(shape, true) != MOE_OK || dtype == MOE_MXFP8) return 0;
+  if (check_shape(shape, true) != MOE_OK) return 0;
+  if (dtype == MOE_MXFP8) return check_mx(shape) == MOE_OK ? mx_saved_layout(shape).total : 0;
   return saved_layout(shape, dtype).total;
 }
 
 size_t moe_workspace_bytes(const moe_shape* shape, moe_dtype dtype, int backward) {
-  if (check_shape(shape, true) != MOE_OK || dtype == MOE_MXFP8) return 0;
+  if (check_shape(shape, true) != MOE_OK) return 0;
+  if (dtype == MOE_MXFP8) {
+    if (check_mx(shape) != MOE_OK) return 0;
+    return backward ? mx_bwd_ws(shape).total : mx_fwd_ws(shape).total;
+  }
   return backward ? bwd_ws(shape, dtype).total : fwd_ws(shape, dtype).total;
+}
+
+size_t moe_mx_weights_bytes(const moe_shape* shape) {
+  if (check_shape(shape, true) != MOE_OK) return 0;
+  return mx_weights_layout(shape).total;
+}
+
+moe_status moe_quantize_weights_mxfp8(const moe_shape* s, const void* w_gate, const void* w_up,
+                                      const void* w_down, void* wq, hipStream_t st) {
+  moe_status rc = check_shape(s, true);
+  if (rc != MOE_OK) return rc;
+  if (any_null({w_gate, w_up, w_down, wq})) return MOE_E_NULL;
+  if (!all_aligned({w_gate, w_up, w_down, wq})) return MOE_E_ALIGN;
+  const MxWeights L = mx_weights_layout(s);
+  uint8_t* q = (uint8_t*)wq;
+  const int E = s->E, H = s->H, I = s->I;
+  MOE_TRY(launch_quant_rows(1, w_gate, nullptr, nullptr, E * I, H, q + L.wg8, q + L.wgs, st));
+  MOE_TRY(launch_quant_rows(1, w_up, nullptr, nullptr, E * I, H, q + L.wu8, q + L.wus, st));
+  MOE_TRY(launch_quant_rows(1, w_down, nullptr, nullptr, E * H, I, q + L.wd8, q + L.wds, st));
+  MOE_TRY(launch_quant_cols(1, w_down, E, H, I, q + L.wdT8, q + L.wdTs, st));
+  MOE_TRY(launch_quant_cols(1, w_gate, E, I, H, q + L.wgT8, q + L.wgTs, st));
+  MOE_TRY(launch_quant_cols(1, w_up, E, I, H, q + L.wuT8, q + L.wuTs, st));
+  return MOE_OK;
+}
+
+moe_status moe_quantize_mxfp8(const void* src, int64_t rows, int64_t cols, int axis, uint8_t* q,
+                              uint8_t* scales, hipStream_t st) {
+  if (any_null({src, q, scales}) && rows * cols > 0) return MOE_E_NULL;
+  if (!all_aligned({src, q})) return MOE_E_ALIGN;
+  if (rows < 0 || cols < 0 || rows > INT32_MAX || cols > INT32_MAX) return MOE_E_SHAPE;
+  if (rows * cols == 0) return MOE_OK;
+  if (axis == 1) {
+    if (cols % 32) return MOE_E_SHAPE;
+    return hip_status(launch_quant_rows(1, src, nullptr, nullptr, (int)rows, (int)cols, q, scales, st));
+  }
+  if (axis == 0) {
+    if (rows % 32 || cols % 16) return MOE_E_SHAPE;
+    return hip_status(launch_quant_cols(1, src, 1, (int)rows, (int)cols, q, scales, st));
+  }
+  return MOE_E_SHAPE;
+}
+
+moe_status moe_forward_mxfp8(const moe_shape* s, const void* plan, const void* x,
+                             const float* topk_w, const void* wq, const void* s_gate,
+                             const void* s_up, const void* s_down, void* y, void* saved, void* ws,
+                             size_t ws_bytes, hipStream_t st) {
+  return forward_mx_impl(s, plan, x, topk_w, wq, s_gate, s_up, s_down, y, saved, ws, ws_bytes, st);
+}
+
+moe_status moe_backward_mxfp8(const moe_shape* s, const void* plan, const void* x,
+                              const float* topk_w, const void* wq, const void* s_gate,
+                              const void* s_up, const void* s_down, const void* saved,
+                              const void* dy, void* dx, void* dw_gate, void* dw_up, void* dw_down,
+                              void* ds_gate, void* ds_up, void* ds_down, float* d_topk_w, void* ws,
+                              size_t ws_bytes, hipStream_t st) {
+  return backward_mx_impl(s, plan, x, topk_w, wq, s_gate, s_up, s_down, saved, dy, dx, dw_gate,
+                          dw_up, dw_down, ds_gate, ds_up, ds_down, d_topk_w, ws, ws_bytes, st);
 }
 
 moe_status moe_router_logits_f32(const moe_shape* s, const float* x, const float* w_router,
@@ -413,22 +771,14 @@ moe_status moe_plan(const moe_shape* s, const int32_t* topk_idx, void* plan, hip
   if (!plan || any_null_rows(s, {topk_idx})) return MOE_E_NULL;
   if (!all_aligned({topk_idx, plan})) return MOE_E_ALIGN;
   const moe_plan_layout L = plan_layout(s);
-  PlanPtrs p;
-  p.counts = at<int32_t>(plan, L.counts);
-  p.offsets = at<int32_t>(plan, L.offsets);
-  p.src_token = at<int32_t>(plan, L.src_token);
-  p.src_slot = at<int32_t>(plan, L.src_slot);
-  p.pos = at<int32_t>(plan, L.pos);
-  p.tiles = at<int32_t>(plan, L.tiles);
-  p.n_tiles = at<int32_t>(plan, L.n_tiles);
-  p.err_flag = at<int32_t>(plan, L.err_flag);
-  p.active = at<int32_t>(plan, L.active);
-  p.n_active = at<int32_t>(plan, L.n_active);
-  p.chunk_hist = at<int32_t>(plan, L.scratch);
-  p.chunk_invalid = p.chunk_hist + (size_t)L.n_chunks * s->E;
-  p.n_chunks = L.n_chunks;
-  p.max_tiles = L.max_tiles;
-  return hip_status(launch_plan(topk_idx, s->T, s->k, s->E, p, st));
+  if (L.n_minibatch > MX_MAX_MB) return MOE_E_SHAPE;
+  for (int m = 0; m < L.n_minibatch; ++m) {
+    const int T_m = std::min(L.T_minibatch, s->T - m * L.T_minibatch);
+    void* sub = (char*)plan + (size_t)m * L.sub_plan_bytes;
+    const moe_status rc = plan_one(s, L, T_m, topk_idx + (size_t)m * L.T_minibatch * s->k, sub, st);
+    if (rc != MOE_OK) return rc;
+  }
+  return MOE_OK;
 }
 
 static moe_status gather_impl(const moe_shape* s, const void* plan, const void* src, void* dst,

@@ -1,0 +1,397 @@
+// Building blocks of the grouped MFMA GEMMs (bf16/fp32 in gemm.hip, MXFP8 in
+// gemm_mx.hip): LDS tile layout and swizzle, operand loaders, the pipelined main
+// loop, accumulator staging, tile rasterisation.  See gemm.hip for the design.
+#pragma once
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace moe {
+
+constexpr int TM = 128, TN = 128, NTHR = 256;
+constexpr int ROWB = 128;            // bytes per LDS operand row
+constexpr int TILEB = 128 * ROWB;    // one operand tile: 16 KiB
+constexpr int LDS_BYTES = 4 * TILEB; // 2 buffers x (A, B) = 64 KiB = the staged C tile
+
+template <typename T> struct Tr;
+template <> struct Tr<bf16_t> { static constexpr int BK = 64, VEC = 8; };
+template <> struct Tr<float> { static constexpr int BK = 32, VEC = 4; };
+
+// byte offset of 16-byte chunk `chunk` of operand row `row`
+MOE_DEV int swz(int row, int chunk) { return row * ROWB + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4); }
+
+// float offset of element (row, col) in the staged 128 x 128 fp32 C tile
+MOE_DEV int cidx(int row, int col) { return row * 128 + ((((col >> 3) ^ (row & 15))) << 3) + (col & 7); }
+
+MOE_DEV uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+// ------------------------------------------------------------------ loaders
+// Loads are branch-free: a row outside the operand reads a valid row and is
+// zeroed with a select afterwards.  (A load under a branch keeps the compiler from
+// counting outstanding loads, and it then waits for all of them before the next
+// LDS store, which removes the prefetch.)
+MOE_DEV uint4 keep_if(bool ok, const uint4& v) {
+  return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+}
+
+// K-major operand: thread t loads chunk (t & 7) of tile rows (t >> 3) + 32 s.
+// rp[s] must point at a readable row; ok[s] = false zeroes it.
+template <typename T>
+struct KLoad {
+  const T* rp[4];
+  bool ok[4];
+  MOE_DEV void set(int s, const T* p, bool valid, const T* fallback) {
+    rp[s] = valid ? p : fallback;
+    ok[s] = valid;
+  }
+  MOE_DEV void load(int kt, uint4 (&r)[4]) const {
+    const int k = kt * Tr<T>::BK + (threadIdx.x & 7) * Tr<T>::VEC;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) r[s] = keep_if(ok[s], *(const uint4*)(rp[s] + k));
+  }
+  MOE_DEV void store(char* t, const uint4 (&r)[4]) const {
+    const int row = threadIdx.x >> 3, ch = threadIdx.x & 7;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) *(uint4*)(t + swz(row + 32 * s, ch)) = r[s];
+  }
+};
+
+// MN-major operand: element (k, i) of the tile at kr(k)[i]; kr.valid(k) is false
+// for K rows outside the operand (kr(k) still points at a readable row; the data
+// is zeroed).
+// bf16: thread t owns k = 4 (t >> 4) .. +3, i = 8 (t & 15) .. +7.
+// fp32: thread t owns k = 4 (t >> 5) .. +3, i = 4 (t & 31) .. +3.
+template <typename T, class KR>
+struct MNLoad {
+  KR kr;
+  static constexpr int IB = 128 / Tr<T>::VEC;  // i-blocks per row of 128
+  MOE_DEV void load(int kt, uint4 (&r)[4]) const {
+    const int kb = threadIdx.x / IB, ib = threadIdx.x % IB;
+    const int k0 = kt * Tr<T>::BK + 4 * kb;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      r[kk] = keep_if(kr.valid(k0 + kk), *(const uint4*)(kr(k0 + kk) + ib * Tr<T>::VEC));
+  }
+  MOE_DEV void store(char* t, const uint4 (&r)[4]) const;
+};
+
+MOE_DEV uint32_t u4_word(const uint4& v, int w) {
+  return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
+}
+
+template <typename T, class KR>
+MOE_DEV void MNLoad<T, KR>::store(char* t, const uint4 (&r)[4]) const {
+  const int kb = threadIdx.x / IB, ib = threadIdx.x % IB;
+  if constexpr (sizeof(T) == 2) {
+    // 4 k x 8 i bf16 -> 8 rows (i) of 4 k values (8 bytes)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int sh = (i & 1) * 16;
+      const uint32_t e0 = (u4_word(r[0], i >> 1) >> sh) & 0xffffu;
+      const uint32_t e1 = (u4_word(r[1], i >> 1) >> sh) & 0xffffu;
+      const uint32_t e2 = (u4_word(r[2], i >> 1) >> sh) & 0xffffu;
+      const uint32_t e3 = (u4_word(r[3], i >> 1) >> sh) & 0xffffu;
+      const int row = ib * 8 + i;
+      *(uint2*)(t + swz(row, kb >> 1) + (kb & 1) * 8) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+    }
+  } else {
+    // 4 k x 4 i fp32 -> 4 rows (i) of 4 k values (16 bytes)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = ib * 4 + i;
+      *(uint4*)(t + swz(row, kb)) =
+          make_uint4(u4_word(r[0], i), u4_word(r[1], i), u4_word(r[2], i), u4_word(r[3], i));
+    }
+  }
+}
+
+// ------------------------------------------------------------- MFMA on a tile
+// acc[mb][nb]: wave rows arow + 32 mb, B-tile rows brow[nb]; lane l supplies row
+// (l & 31) and the 8 K values of chunk half (l >> 5) of each 16-deep step.
+template <typename T>
+MOE_DEV void mma_tile(const char* ta, const char* tb, f32x16_t (&acc)[2][2], int arow,
+                      const int (&brow)[2], int lane);
+
+template <>
+MOE_DEV void mma_tile<bf16_t>(const char* ta, const char* tb, f32x16_t (&acc)[2][2], int arow,
+                              const int (&brow)[2], int lane) {
+  const int r = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int ch = ks * 2 + hi;
+    const bf16x8_t a0 = *(const bf16x8_t*)(ta + swz(arow + r, ch));
+    const bf16x8_t a1 = *(const bf16x8_t*)(ta + swz(arow + 32 + r, ch));
+    const bf16x8_t b0 = *(const bf16x8_t*)(tb + swz(brow[0] + r, ch));
+    const bf16x8_t b1 = *(const bf16x8_t*)(tb + swz(brow[1] + r, ch));
+    acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
+    acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
+    acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
+    acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
+  }
+}
+
+template <>
+MOE_DEV void mma_tile<float>(const char* ta, const char* tb, f32x16_t (&acc)[2][2], int arow,
+                             const int (&brow)[2], int lane) {
+  const int r = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int ch = ks * 4 + hi * 2;
+    float a[2][8], b[2][8];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      *(uint4*)&a[0][4 * q] = *(const uint4*)(ta + swz(arow + r, ch + q));
+      *(uint4*)&a[1][4 * q] = *(const uint4*)(ta + swz(arow + 32 + r, ch + q));
+      *(uint4*)&b[0][4 * q] = *(const uint4*)(tb + swz(brow[0] + r, ch + q));
+      *(uint4*)&b[1][4 * q] = *(const uint4*)(tb + swz(brow[1] + r, ch + q));
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0][s], b[0][s], acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0][s], b[1][s], acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[1][s], b[0][s], acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[1][s], b[1][s], acc[1][1], 0, 0, 0);
+    }
+  }
+}
+
+// ----------------------------------------------------------------- main loop
+// Prefetch distance 2: two register sets (r*0, r*1) and two LDS buffers.  While
+// the MFMAs consume K tile kt from LDS, tile kt + 1 (loaded one iteration earlier)
+// goes from registers into the other LDS buffer and tile kt + 2 is in flight from
+// memory, so each global load has a whole iteration to arrive.  The loop is
+// unrolled by two so that the register sets stay statically indexed.
+// DIST = 1 keeps one register set (fewer registers, for the short-K wgrads):
+// tile kt + 1 is loaded while tile kt is multiplied.
+template <typename T, int DIST = 2, class LA, class LB>
+MOE_DEV void gemm_main(char* lds, const LA& la, const LB& lb, int nk, f32x16_t (&acc)[2][2],
+                       int arow, const int (&brow)[2], int lane) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  if (nk <= 0) return;
+  if constexpr (DIST == 1) {
+    uint4 ra[4], rb[4];
+    la.load(0, ra);
+    lb.load(0, rb);
+    la.store(lds, ra);
+    lb.store(lds + TILEB, rb);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      char* cur = lds + (kt & 1) * 2 * TILEB;
+      char* nxt = lds + ((kt + 1) & 1) * 2 * TILEB;
+      la.load(min(kt + 1, nk - 1), ra);
+      lb.load(min(kt + 1, nk - 1), rb);
+      mma_tile<T>(cur, cur + TILEB, acc, arow, brow, lane);
+      la.store(nxt, ra);
+      lb.store(nxt + TILEB, rb);
+      __syncthreads();
+    }
+    return;
+  }
+  char* buf0 = lds;
+  char* buf1 = lds + 2 * TILEB;
+  uint4 ra0[4], rb0[4], ra1[4], rb1[4];
+  const int last = nk - 1;
+  la.load(0, ra0);
+  lb.load(0, rb0);
+  la.load(min(1, last), ra1);
+  lb.load(min(1, last), rb1);
+  la.store(buf0, ra0);
+  lb.store(buf0 + TILEB, rb0);
+  __syncthreads();
+  // Every load is issued unconditionally (past the last tile it re-reads the last
+  // tile) so that the compiler can wait for exactly the older register set.
+  for (int kt = 0; kt < nk; kt += 2) {
+    la.load(min(kt + 2, last), ra0);
+    lb.load(min(kt + 2, last), rb0);
+    mma_tile<T>(buf0, buf0 + TILEB, acc, arow, brow, lane);
+    la.store(buf1, ra1);
+    lb.store(buf1 + TILEB, rb1);
+    __syncthreads();
+    if (kt + 1 >= nk) break;
+    la.load(min(kt + 3, last), ra1);
+    lb.load(min(kt + 3, last), rb1);
+    mma_tile<T>(buf1, buf1 + TILEB, acc, arow, brow, lane);
+    la.store(buf0, ra0);
+    lb.store(buf0 + TILEB, rb0);
+    __syncthreads();
+  }
+}
+
+// Accumulators -> staged C tile.  Output element of acc[mb][nb][v] in lane l:
+// row arow + 32 mb + 8 (v >> 2) + 4 (l >> 5) + (v & 3), column brow[nb] + (l & 31).
+MOE_DEV void stage_acc(float* C, const f32x16_t (&acc)[2][2], int arow, const int (&brow)[2],
+                       int lane) {
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = arow + 32 * mb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        C[cidx(row, brow[nb] + (lane & 31))] = acc[mb][nb][v];
+      }
+}
+
+MOE_DEV void read8(const float* C, int row, int col, float* f) {
+  const float4 a = *(const float4*)(C + cidx(row, col));
+  const float4 b = *(const float4*)(C + cidx(row, col) + 4);
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+// 8 values -> 8 elements of T at p (16-byte aligned)
+MOE_DEV void store8(bf16_t* p, const float* f) { *(uint4*)p = pack8(f); }
+MOE_DEV void store8(float* p, const float* f) {
+  *(float4*)p = make_float4(f[0], f[1], f[2], f[3]);
+  *(float4*)(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
+}
+MOE_DEV void load8(const bf16_t* p, float* f) { unpack8(*(const uint4*)p, f); }
+MOE_DEV void load8(const float* p, float* f) {
+  const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+// Plain epilogue: the 128 x 128 tile to out_row(r) + n0 for valid rows.
+template <typename T, class RowPtr>
+MOE_DEV void epi_store(const float* C, const RowPtr& out_row, int n_valid_rows) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int r = (threadIdx.x >> 4) + 16 * s, c = threadIdx.x & 15;
+    if (r < n_valid_rows) {
+      float f[8];
+      read8(C, r, 8 * c, f);
+      store8(out_row(r) + 8 * c, f);
+    }
+  }
+}
+
+// --------------------------------------------------------------- tile decode
+struct RowTile {
+  int e, row0, row_end;
+};
+
+constexpr int N_XCD = 8;  // MI355X: workgroup i is dispatched to XCD i mod 8
+
+// Rows-grouped launches use a 1-D grid over (row tile, column tile) pairs.  The
+// pairs that exist (n_tiles of the plan x nt_count) are renumbered so that the
+// workgroups one XCD receives (ids x, x + 8, x + 16, ...) cover a contiguous run
+// of pairs with the column tile fastest: a row tile's activations and an expert's
+// weight columns are then fetched into that XCD's L2 once, not once per XCD.
+// Returns false for workgroups past the last pair.
+MOE_DEV bool rows_tile(const GroupInfo& g, int nt_count, RowTile& t, int& nt) {
+  const int n_row_tiles = g.tiles ? g.n_tiles[0] : (g.dense_rows + TM - 1) / TM;
+  const int total = n_row_tiles * nt_count;
+  const int id = blockIdx.x;
+  if (id >= total) return false;
+  const int per = total / N_XCD, rem = total % N_XCD, x = id % N_XCD, local = id / N_XCD;
+  const int L = x < rem ? x * (per + 1) + local : rem * (per + 1) + (x - rem) * per + local;
+  const int mt = L / nt_count;
+  nt = L - mt * nt_count;
+  if (g.tiles) {
+    t.e = g.tiles[2 * mt];
+    t.row0 = g.tiles[2 * mt + 1];
+    t.row_end = min(t.row0 + TM, g.offsets[t.e + 1]);
+  } else {
+    t.e = 0;
+    t.row0 = mt * TM;
+    t.row_end = min(t.row0 + TM, g.dense_rows);
+  }
+  return true;
+}
+
+MOE_DEV int token_of(const GroupInfo& g, int r) { return g.src_token ? g.src_token[r] : r; }
+
+MOE_DEV void wave_coords(int& arow, int (&brow)[2], bool swiglu) {
+  const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  arow = wm * 64;
+  if (swiglu) {
+    brow[0] = wn * 32;        // gate columns i0 + 32 wn ..
+    brow[1] = 64 + wn * 32;   // up columns, same i
+  } else {
+    brow[0] = wn * 64;
+    brow[1] = wn * 64 + 32;
+  }
+}
+
+// K-row pointer of a plain row-major matrix: element (k, i) at base[k * ld + i]
+template <typename T>
+struct KRowPlain {
+  const T* base;
+  size_t ld;
+  MOE_DEV const T* operator()(int k) const { return base + (size_t)k * ld; }
+  MOE_DEV bool valid(int) const { return true; }
+};
+
+// Weights of dgrad-up as one [2I, H] operand: rows < I from W_g[e], the rest W_u[e]
+template <typename T>
+struct KRowCat {
+  const T* wg;
+  const T* wu;
+  int I, H;
+  MOE_DEV const T* operator()(int k) const {
+    return k < I ? wg + (size_t)k * H : wu + (size_t)(k - I) * H;
+  }
+  MOE_DEV bool valid(int) const { return true; }
+};
+
+// K rows of a K-grouped operand: segment row seg0 + k (valid below seg1) of a
+// row-major matrix, optionally gathered through src_token.
+template <typename T>
+struct KRowSeg {
+  const T* base;
+  const int32_t* gather;
+  size_t ld;
+  int seg0, seg1;
+  // rows past the segment read the segment's first row (callers only load when
+  // the segment is not empty) and are zeroed through valid()
+  MOE_DEV const T* operator()(int k) const {
+    const int r = seg0 + k < seg1 ? seg0 + k : seg0;
+    return base + (size_t)(gather ? gather[r] : r) * ld;
+  }
+  MOE_DEV bool valid(int k) const { return seg0 + k < seg1; }
+};
+
+MOE_DEV void k_segment(const GroupInfo& g, int e, int& seg0, int& seg1) {
+  if (g.offsets) {
+    seg0 = g.offsets[e];
+    seg1 = g.offsets[e + 1];
+  } else {
+    seg0 = 0;
+    seg1 = g.dense_rows;
+  }
+}
+
+// Work item w of a K-grouped GEMM over an M_tiles x N_tiles output per expert:
+// experts with rows only (the plan's active list), tiles in row-major order.
+struct KTile {
+  int e, m0, n0;
+};
+MOE_DEV KTile k_tile(const GroupInfo& g, int w, int mt_count, int nt_count) {
+  const int per = mt_count * nt_count;
+  const int a = w / per, rem = w - a * per;
+  const int mt = rem / nt_count;
+  KTile t;
+  t.e = g.active ? g.active[a] : 0;
+  t.m0 = mt * TM;
+  t.n0 = (rem - mt * nt_count) * TN;
+  return t;
+}
+
+MOE_DEV int k_work_items(const GroupInfo& g, int mt_count, int nt_count) {
+  return (g.active ? g.n_active[0] : 1) * mt_count * nt_count;
+}
+
+// Persistent grid: two resident workgroups per compute unit, at most one per item.
+inline unsigned persistent_grid(long items) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const long g = 2L * (cus > 0 ? cus : 256);
+  return (unsigned)(items < g ? (items > 0 ? items : 1) : g);
+}
+
+}  // namespace moe

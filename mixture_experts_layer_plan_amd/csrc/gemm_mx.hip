@@ -1,0 +1,536 @@
+// MXFP8 grouped expert GEMMs: E4M3 operands with one E8M0 scale per 32 along K,
+// on the scaled MFMA v_mfma_scale_f32_32x32x64_f8f6f4 (gfx950), fp32 accumulation.
+//
+// MoK trains in MXFP8 with the format handled inside the kernels (sebask.de,
+// "Mixture-of-Kittens: Cursors Open-Source-Ansatz für effizientes MoE-Training auf
+// NVL72", § Determinismus und MXFP8-Unterstützung; stamatios.com, "Cursor abre
+// código de megakernel MoE para GPUs NVL72", § Outras características).  Every
+// operand here is K-major: an E4M3 row of K bytes plus K/32 scale bytes.  The
+// operands whose contraction runs over the token axis (the wgrads) are produced
+// transposed by the token quantiser, and the weights exist in both orientations,
+// so no transposition happens inside these kernels.
+//
+// Lane layout of the scaled 32x32x64 instruction (established with an in-bounds
+// probe): lane i + 32 h holds row i; its bytes 0-15 lie in K block 0 and bytes
+// 16-31 in K block 1 of the 64-deep step; the scale of (row i, block c) comes
+// from lane i + 32 c.  Here lane (i, h) takes the 16-byte chunks 4 ks + h and
+// 4 ks + 2 + h of a 128-byte K tile row (blocks 2 ks and 2 ks + 1), so every
+// (lane half, byte) pair names one K index, the same for both operands.
+//
+// Tiles, LDS layout, swizzle, rasterisation and epilogue staging are those of the
+// bf16 GEMMs (gemm_common.hpp) with 128 bytes = 128 fp8 of K per LDS row.  Scale
+// words (4 blocks of one row per K tile) go straight from memory into the
+// registers of the lanes whose MFMA fragments use them.
+#include "gemm_common.hpp"
+#include "mx_common.hpp"
+
+namespace moe {
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+constexpr int MX_BK = 128;  // K bytes per tile row (4 scale blocks)
+
+// One K-major MX operand as seen by one thread: data rows for its loads (rows
+// (t >> 3) + 32 s of the tile), scale rows for its MFMA fragments (two 32-row
+// blocks).  A second source can take over at K >= ksplit (dgrad-up weights); its
+// pointers are pre-offset by -ksplit so that the same K offset applies.
+// Rows outside the operand are loaded from a readable row (the tile's first row)
+// and zeroed with a select: loads stay branch-free (see gemm_common.hpp).
+struct MxOp {
+  const uint8_t* d[4];
+  const uint8_t* d_hi[4];
+  const uint8_t* sc[2];
+  const uint8_t* sc_hi[2];
+  bool dok[4], sok[2];
+  long ksplit;
+};
+
+MOE_DEV void mx_op_clear(MxOp& o) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    o.d[s] = o.d_hi[s] = nullptr;
+    o.dok[s] = true;
+  }
+  o.sc[0] = o.sc[1] = o.sc_hi[0] = o.sc_hi[1] = nullptr;
+  o.sok[0] = o.sok[1] = true;
+  o.ksplit = 1L << 62;
+}
+
+MOE_DEV void mx_load(const MxOp& o, long koff, uint4 (&r)[4], uint32_t (&sw)[2]) {
+  const bool hi = koff >= o.ksplit;
+  const int ch = (threadIdx.x & 7) * 16;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    r[s] = keep_if(o.dok[s], *(const uint4*)((hi ? o.d_hi[s] : o.d[s]) + koff + ch));
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t w = *(const uint32_t*)((hi ? o.sc_hi[q] : o.sc[q]) + koff / 32);
+    sw[q] = o.sok[q] ? w : 0u;
+  }
+}
+
+MOE_DEV void mx_store(char* t, const uint4 (&r)[4]) {
+  const int row = threadIdx.x >> 3, ch = threadIdx.x & 7;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) *(uint4*)(t + swz(row + 32 * s, ch)) = r[s];
+}
+
+MOE_DEV i32x8_t mx_frag(const char* t, int row, int c0, int c1) {
+  const uint4 a = *(const uint4*)(t + swz(row, c0));
+  const uint4 b = *(const uint4*)(t + swz(row, c1));
+  i32x8_t v;
+  v[0] = (int)a.x; v[1] = (int)a.y; v[2] = (int)a.z; v[3] = (int)a.w;
+  v[4] = (int)b.x; v[5] = (int)b.y; v[6] = (int)b.z; v[7] = (int)b.w;
+  return v;
+}
+
+MOE_DEV void mma_tile_mx(const char* ta, const char* tb, const uint32_t (&sa)[2],
+                         const uint32_t (&sb)[2], f32x16_t (&acc)[2][2], int arow,
+                         const int (&brow)[2], int lane) {
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int c0 = 4 * ks + h, c1 = 4 * ks + 2 + h, sh = 8 * (2 * ks + h);
+    const i32x8_t a0 = mx_frag(ta, arow + r, c0, c1);
+    const i32x8_t a1 = mx_frag(ta, arow + 32 + r, c0, c1);
+    const i32x8_t b0 = mx_frag(tb, brow[0] + r, c0, c1);
+    const i32x8_t b1 = mx_frag(tb, brow[1] + r, c0, c1);
+    const int s_a0 = (int)((sa[0] >> sh) & 0xffu), s_a1 = (int)((sa[1] >> sh) & 0xffu);
+    const int s_b0 = (int)((sb[0] >> sh) & 0xffu), s_b1 = (int)((sb[1] >> sh) & 0xffu);
+    acc[0][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b0, acc[0][0], 0, 0, 0, s_a0, 0, s_b0);
+    acc[0][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b1, acc[0][1], 0, 0, 0, s_a0, 0, s_b1);
+    acc[1][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b0, acc[1][0], 0, 0, 0, s_a1, 0, s_b0);
+    acc[1][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1, acc[1][1], 0, 0, 0, s_a1, 0, s_b1);
+  }
+}
+
+// K offset (bytes) of K tile kt in a plain operand
+struct KLinear {
+  MOE_DEV long operator()(int kt) const { return (long)kt * MX_BK; }
+};
+
+// Main loop, prefetch distance 2 (as gemm_main); scale words travel with their
+// data: sX0/sX1 with the register sets, cX0/cX1 with the LDS buffers.
+template <class KM>
+MOE_DEV void gemm_main_mx(char* lds, const MxOp& A, const MxOp& B, const KM& km, int nk,
+                          f32x16_t (&acc)[2][2], int arow, const int (&brow)[2], int lane) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  if (nk <= 0) return;
+  char* buf0 = lds;
+  char* buf1 = lds + 2 * TILEB;
+  uint4 ra0[4], rb0[4], ra1[4], rb1[4];
+  uint32_t sa0[2], sb0[2], sa1[2], sb1[2], ca0[2], cb0[2], ca1[2], cb1[2];
+  const int last = nk - 1;
+  mx_load(A, km(0), ra0, sa0);
+  mx_load(B, km(0), rb0, sb0);
+  mx_load(A, km(min(1, last)), ra1, sa1);
+  mx_load(B, km(min(1, last)), rb1, sb1);
+  mx_store(buf0, ra0);
+  mx_store(buf0 + TILEB, rb0);
+  ca0[0] = sa0[0]; ca0[1] = sa0[1]; cb0[0] = sb0[0]; cb0[1] = sb0[1];
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    mx_load(A, km(min(kt + 2, last)), ra0, sa0);
+    mx_load(B, km(min(kt + 2, last)), rb0, sb0);
+    mma_tile_mx(buf0, buf0 + TILEB, ca0, cb0, acc, arow, brow, lane);
+    mx_store(buf1, ra1);
+    mx_store(buf1 + TILEB, rb1);
+    ca1[0] = sa1[0]; ca1[1] = sa1[1]; cb1[0] = sb1[0]; cb1[1] = sb1[1];
+    __syncthreads();
+    if (kt + 1 >= nk) break;
+    mx_load(A, km(min(kt + 3, last)), ra1, sa1);
+    mx_load(B, km(min(kt + 3, last)), rb1, sb1);
+    mma_tile_mx(buf1, buf1 + TILEB, ca1, cb1, acc, arow, brow, lane);
+    mx_store(buf0, ra0);
+    mx_store(buf0 + TILEB, rb0);
+    ca0[0] = sa0[0]; ca0[1] = sa0[1]; cb0[0] = sb0[0]; cb0[1] = sb0[1];
+    __syncthreads();
+  }
+}
+
+// Row-quantise 8 consecutive values held by each of 4 neighbouring lanes (one
+// 32-block): amax over the 4 lanes, codes to q (8 bytes), the scale from the
+// first lane of the group.  Every lane of the wavefront must call this.
+MOE_DEV void quant8_group4(const float* v, bool ok, uint8_t* q, uint8_t* sc, bool first) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  const int X = mx_exp_of_amax(amax);
+  if (ok) {
+    *(uint2*)q = mx_encode8(v, X);
+    if (first) *sc = (uint8_t)(X + 127);
+  }
+}
+
+// ------------------------------------------------------------------ kernels
+// GEMM1 + SwiGLU, MX: A = X8 rows (dispatched, quantised along H), B = W_g / W_u
+// quantised along H.  Epilogue: Z = (A | B) fp32, h = silu(A) B quantised along I.
+__global__ __launch_bounds__(NTHR, 2) void k_up_swiglu_mx(
+    GroupInfo g, const uint8_t* __restrict__ X8, const uint8_t* __restrict__ Xs,
+    const uint8_t* __restrict__ wg8, const uint8_t* __restrict__ wgs,
+    const uint8_t* __restrict__ wu8, const uint8_t* __restrict__ wus, int H, int I,
+    float* __restrict__ Z, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  RowTile t;
+  int nt;
+  if (!rows_tile(g, I / 64, t, nt)) return;
+  const int i0 = nt * 64, lane = threadIdx.x & 63, HS = H / 32;
+  int arow, brow[2];
+  wave_coords(arow, brow, true);
+  MxOp A, B;
+  mx_op_clear(A);
+  mx_op_clear(B);
+  const size_t we = (size_t)t.e * I;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int rr = (threadIdx.x >> 3) + 32 * s, r = t.row0 + rr;
+    A.dok[s] = r < t.row_end;
+    A.d[s] = X8 + (size_t)(A.dok[s] ? r : t.row0) * H;
+    B.d[s] = rr < 64 ? wg8 + (we + i0 + rr) * H : wu8 + (we + i0 + rr - 64) * H;
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = t.row0 + arow + 32 * q + (lane & 31);
+    A.sok[q] = r < t.row_end;
+    A.sc[q] = Xs + (size_t)(A.sok[q] ? r : t.row0) * HS;
+    const int n = brow[q] + (lane & 31);
+    B.sc[q] = n < 64 ? wgs + (we + i0 + n) * HS : wus + (we + i0 + n - 64) * HS;
+  }
+  f32x16_t acc[2][2];
+  gemm_main_mx(lds, A, B, KLinear(), H / MX_BK, acc, arow, brow, lane);
+  float* C = (float*)lds;
+  stage_acc(C, acc, arow, brow, lane);
+  __syncthreads();
+  const int nrows = t.row_end - t.row0;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int r = (threadIdx.x >> 3) + 32 * s, c = threadIdx.x & 7;
+    const bool ok = r < nrows;
+    float a[8], b[8], h[8];
+    read8(C, r, 8 * c, a);
+    read8(C, r, 64 + 8 * c, b);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) h[q] = ok ? silu_f(a[q]) * b[q] : 0.0f;
+    const size_t row = (size_t)(t.row0 + r);
+    if (ok) {
+      float* zr = Z + row * (2 * I);
+      store8(zr + i0 + 8 * c, a);
+      store8(zr + I + i0 + 8 * c, b);
+    }
+    quant8_group4(h, ok, hq + row * I + i0 + 8 * c, hs + row * (I / 32) + (i0 + 8 * c) / 32,
+                  (c & 3) == 0);
+  }
+}
+
+// GEMM2, MX: Y = Q_I(h) Q_I(W_d)^T, Y in bf16.
+__global__ __launch_bounds__(NTHR, 2) void k_down_mx(GroupInfo g, const uint8_t* __restrict__ hq,
+                                                     const uint8_t* __restrict__ hs,
+                                                     const uint8_t* __restrict__ wd8,
+                                                     const uint8_t* __restrict__ wds, int H, int I,
+                                                     bf16_t* __restrict__ Y) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  RowTile t;
+  int nt;
+  if (!rows_tile(g, H / TN, t, nt)) return;
+  const int n0 = nt * TN, lane = threadIdx.x & 63, IS = I / 32;
+  int arow, brow[2];
+  wave_coords(arow, brow, false);
+  MxOp A, B;
+  mx_op_clear(A);
+  mx_op_clear(B);
+  const size_t we = (size_t)t.e * H;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int rr = (threadIdx.x >> 3) + 32 * s, r = t.row0 + rr;
+    A.dok[s] = r < t.row_end;
+    A.d[s] = hq + (size_t)(A.dok[s] ? r : t.row0) * I;
+    B.d[s] = wd8 + (we + n0 + rr) * I;
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = t.row0 + arow + 32 * q + (lane & 31);
+    A.sok[q] = r < t.row_end;
+    A.sc[q] = hs + (size_t)(A.sok[q] ? r : t.row0) * IS;
+    B.sc[q] = wds + (we + n0 + brow[q] + (lane & 31)) * IS;
+  }
+  f32x16_t acc[2][2];
+  gemm_main_mx(lds, A, B, KLinear(), I / MX_BK, acc, arow, brow, lane);
+  float* C = (float*)lds;
+  stage_acc(C, acc, arow, brow, lane);
+  __syncthreads();
+  auto out = [&](int r) { return Y + (size_t)(t.row0 + r) * H + n0; };
+  epi_store<bf16_t>(C, out, t.row_end - t.row0);
+}
+
+// dgrad-down, MX: dh' = Q_H(dYu) Q_H(W_d) with W_d stored transposed [E, I, H];
+// epilogue as the bf16 kernel (SwiGLU backward from fp32 Z, router-weight
+// gradient partials, dZ and g h in bf16) plus dZ quantised along 2I for dgrad-up.
+__global__ __launch_bounds__(NTHR, 2) void k_dgrad_down_mx(
+    GroupInfo g, const uint8_t* __restrict__ dYu8, const uint8_t* __restrict__ dYus,
+    const uint8_t* __restrict__ wdT8, const uint8_t* __restrict__ wdTs,
+    const float* __restrict__ Z, const float* __restrict__ topk_w, int H, int I, int k,
+    bf16_t* __restrict__ dZ, uint8_t* __restrict__ dZ8, uint8_t* __restrict__ dZs,
+    bf16_t* __restrict__ gh, float* __restrict__ dgp) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  RowTile t;
+  int nt;
+  if (!rows_tile(g, I / TN, t, nt)) return;
+  const int i0 = nt * TN, lane = threadIdx.x & 63, HS = H / 32;
+  int arow, brow[2];
+  wave_coords(arow, brow, false);
+  MxOp A, B;
+  mx_op_clear(A);
+  mx_op_clear(B);
+  const size_t we = (size_t)t.e * I;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int rr = (threadIdx.x >> 3) + 32 * s, r = t.row0 + rr;
+    A.dok[s] = r < t.row_end;
+    A.d[s] = dYu8 + (size_t)(A.dok[s] ? r : t.row0) * H;
+    B.d[s] = wdT8 + (we + i0 + rr) * H;
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = t.row0 + arow + 32 * q + (lane & 31);
+    A.sok[q] = r < t.row_end;
+    A.sc[q] = dYus + (size_t)(A.sok[q] ? r : t.row0) * HS;
+    B.sc[q] = wdTs + (we + i0 + brow[q] + (lane & 31)) * HS;
+  }
+  f32x16_t acc[2][2];
+  gemm_main_mx(lds, A, B, KLinear(), H / MX_BK, acc, arow, brow, lane);
+  float* C = (float*)lds;
+  stage_acc(C, acc, arow, brow, lane);
+  __syncthreads();
+  const int nrows = t.row_end - t.row0, n_parts = I / TN, S2 = (2 * I) / 32;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int r = (threadIdx.x >> 4) + 16 * s, c = threadIdx.x & 15;
+    const bool ok = r < nrows;
+    const int row = t.row0 + r;
+    float part = 0.0f;
+    float da[8], db[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) da[q] = db[q] = 0.0f;
+    if (ok) {
+      const float gate = topk_w[(size_t)g.src_token[row] * k + g.src_slot[row]];
+      float d[8], a[8], b[8], gh8[8];
+      read8(C, r, 8 * c, d);
+      const float* zr = Z + (size_t)row * (2 * I);
+      load8(zr + i0 + 8 * c, a);
+      load8(zr + I + i0 + 8 * c, b);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float sg = 1.0f / (1.0f + expf(-a[q]));
+        const float sl = a[q] * sg;
+        const float hv = sl * b[q];
+        part = fmaf(d[q], hv, part);
+        const float dh = gate * d[q];
+        da[q] = dh * b[q] * (sg * (1.0f + a[q] * (1.0f - sg)));
+        db[q] = dh * sl;
+        gh8[q] = gate * hv;
+      }
+      bf16_t* dzr = dZ + (size_t)row * (2 * I);
+      store8(dzr + i0 + 8 * c, da);
+      store8(dzr + I + i0 + 8 * c, db);
+      store8(gh + (size_t)row * I + i0 + 8 * c, gh8);
+    }
+    const size_t qr = (size_t)(ok ? row : 0);
+    quant8_group4(da, ok, dZ8 + qr * (2 * I) + i0 + 8 * c, dZs + qr * S2 + (i0 + 8 * c) / 32,
+                  (c & 3) == 0);
+    quant8_group4(db, ok, dZ8 + qr * (2 * I) + I + i0 + 8 * c,
+                  dZs + qr * S2 + (I + i0 + 8 * c) / 32, (c & 3) == 0);
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
+    if (ok && c == 0) dgp[(size_t)row * n_parts + nt] = part;
+  }
+}
+
+// dgrad-up, MX: dX = Q_2I(dZ) [Q_I(W_g); Q_I(W_u)] with the weights stored
+// transposed [E, H, I]: B row h takes W_g^T[e][h] for K < I and W_u^T[e][h] after.
+__global__ __launch_bounds__(NTHR, 2) void k_dgrad_up_mx(
+    GroupInfo g, const uint8_t* __restrict__ dZ8, const uint8_t* __restrict__ dZs,
+    const uint8_t* __restrict__ wgT8, const uint8_t* __restrict__ wgTs,
+    const uint8_t* __restrict__ wuT8, const uint8_t* __restrict__ wuTs, int H, int I,
+    bf16_t* __restrict__ dX) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  RowTile t;
+  int nt;
+  if (!rows_tile(g, H / TN, t, nt)) return;
+  const int n0 = nt * TN, lane = threadIdx.x & 63, IS = I / 32, S2 = (2 * I) / 32;
+  int arow, brow[2];
+  wave_coords(arow, brow, false);
+  MxOp A, B;
+  mx_op_clear(A);
+  mx_op_clear(B);
+  const size_t we = (size_t)t.e * H;
+  B.ksplit = I;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int rr = (threadIdx.x >> 3) + 32 * s, r = t.row0 + rr;
+    A.dok[s] = r < t.row_end;
+    A.d[s] = dZ8 + (size_t)(A.dok[s] ? r : t.row0) * (2 * I);
+    B.d[s] = wgT8 + (we + n0 + rr) * I;
+    B.d_hi[s] = wuT8 + (we + n0 + rr) * I - I;
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = t.row0 + arow + 32 * q + (lane & 31);
+    A.sok[q] = r < t.row_end;
+    A.sc[q] = dZs + (size_t)(A.sok[q] ? r : t.row0) * S2;
+    const size_t n = we + n0 + brow[q] + (lane & 31);
+    B.sc[q] = wgTs + n * IS;
+    B.sc_hi[q] = wuTs + n * IS - IS;
+  }
+  f32x16_t acc[2][2];
+  gemm_main_mx(lds, A, B, KLinear(), (2 * I) / MX_BK, acc, arow, brow, lane);
+  float* C = (float*)lds;
+  stage_acc(C, acc, arow, brow, lane);
+  __syncthreads();
+  auto out = [&](int r) { return dX + (size_t)(t.row0 + r) * H + n0; };
+  epi_store<bf16_t>(C, out, t.row_end - t.row0);
+}
+
+// K tiles of one expert in the tile-padded token axis of all minibatches: tile j
+// of expert e in minibatch m sits at K offset (m * max_tiles + first_m[e] + j) * 128.
+struct KMinibatch {
+  int n_mb, max_tiles;
+  int first[MX_MAX_MB], cnt[MX_MAX_MB];
+  MOE_DEV long operator()(int kt) const {
+    long base = 0;
+#pragma unroll
+    for (int m = 0; m < MX_MAX_MB; ++m) {
+      if (m < n_mb) {
+        if (kt >= 0 && kt < cnt[m]) base = ((long)m * max_tiles + first[m] + kt) * MX_BK;
+        kt -= cnt[m];
+      }
+    }
+    return base;
+  }
+};
+
+MOE_DEV KMinibatch k_minibatch(const MbPlans& mp, int e, int& nk) {
+  KMinibatch km;
+  km.n_mb = mp.n_mb;
+  km.max_tiles = mp.max_tiles;
+  nk = 0;
+#pragma unroll
+  for (int m = 0; m < MX_MAX_MB; ++m) {
+    km.first[m] = 0;
+    km.cnt[m] = 0;
+    if (m < mp.n_mb) {
+      km.first[m] = mp.tile_first[m][e];
+      km.cnt[m] = mp.tile_first[m][e + 1] - km.first[m];
+      nk += km.cnt[m];
+    }
+  }
+  return km;
+}
+
+// wgrad, MX: out[e][m, n] = sum over the expert's padded token axis of
+// Q_t(A)[m, k] Q_t(B)[n, k]; A [M, Kp], B [N, Kp] (Kp = n_mb * max_tiles * 128).
+// Persistent over (expert with rows in some minibatch, output tile).  Output rows
+// m < split go to out0[e], the rest to out1[e] (dW_g / dW_u); split = M for one.
+__global__ __launch_bounds__(NTHR, 2) void k_wgrad_mx(MbPlans mp, const uint8_t* __restrict__ A8,
+                                                      const uint8_t* __restrict__ As,
+                                                      const uint8_t* __restrict__ B8,
+                                                      const uint8_t* __restrict__ Bs, int M, int N,
+                                                      int split, bf16_t* __restrict__ out0,
+                                                      bf16_t* __restrict__ out1) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  const int MT = M / TM, NT = N / TN, lane = threadIdx.x & 63;
+  const long Kp = (long)mp.n_mb * mp.max_tiles * MX_BK, KS = Kp / 32;
+  const int total = mp.n_active[0] * MT * NT;
+  int arow, brow[2];
+  wave_coords(arow, brow, false);
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int a = w / (MT * NT), rem = w - a * (MT * NT);
+    const int e = mp.active[a], mt = rem / NT, m0 = mt * TM, n0 = (rem - mt * NT) * TN;
+    int nk;
+    const KMinibatch km = k_minibatch(mp, e, nk);
+    MxOp oa, ob;
+    mx_op_clear(oa);
+    mx_op_clear(ob);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int rr = (threadIdx.x >> 3) + 32 * s;
+      oa.d[s] = A8 + (size_t)(m0 + rr) * Kp;
+      ob.d[s] = B8 + (size_t)(n0 + rr) * Kp;
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      oa.sc[q] = As + (size_t)(m0 + arow + 32 * q + (lane & 31)) * KS;
+      ob.sc[q] = Bs + (size_t)(n0 + brow[q] + (lane & 31)) * KS;
+    }
+    f32x16_t acc[2][2];
+    gemm_main_mx(lds, oa, ob, km, nk, acc, arow, brow, lane);
+    float* C = (float*)lds;
+    stage_acc(C, acc, arow, brow, lane);
+    __syncthreads();
+    bf16_t* base = (m0 < split ? out0 + (size_t)e * split * N + (size_t)m0 * N
+                               : out1 + (size_t)e * (M - split) * N + (size_t)(m0 - split) * N) + n0;
+    auto out = [&](int r) { return base + (size_t)r * N; };
+    epi_store<bf16_t>(C, out, TM);
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+hipError_t launch_mx_up_swiglu(const GroupInfo& g, const uint8_t* X8, const uint8_t* Xs,
+                               const uint8_t* wg8, const uint8_t* wgs, const uint8_t* wu8,
+                               const uint8_t* wus, int H, int I, float* Z, uint8_t* hq,
+                               uint8_t* hs, hipStream_t s) {
+  const unsigned ty = (unsigned)g.max_tiles;
+  if (ty == 0) return hipSuccess;
+  return MOE_LAUNCH("mx_gemm_up_swiglu", s,
+                    k_up_swiglu_mx<<<ty * (I / 64), NTHR, 0, s>>>(g, X8, Xs, wg8, wgs, wu8, wus, H,
+                                                                  I, Z, hq, hs));
+}
+
+hipError_t launch_mx_down(const GroupInfo& g, const uint8_t* hq, const uint8_t* hs,
+                          const uint8_t* wd8, const uint8_t* wds, int H, int I, void* Y,
+                          hipStream_t s) {
+  const unsigned ty = (unsigned)g.max_tiles;
+  if (ty == 0) return hipSuccess;
+  return MOE_LAUNCH("mx_gemm_down", s,
+                    k_down_mx<<<ty * (H / TN), NTHR, 0, s>>>(g, hq, hs, wd8, wds, H, I,
+                                                             (bf16_t*)Y));
+}
+
+hipError_t launch_mx_dgrad_down(const GroupInfo& g, const uint8_t* dYu8, const uint8_t* dYus,
+                                const uint8_t* wdT8, const uint8_t* wdTs, const float* Z,
+                                const float* topk_w, int H, int I, int k, void* dZ, uint8_t* dZ8,
+                                uint8_t* dZs, void* gh, float* dgp, hipStream_t s) {
+  const unsigned ty = (unsigned)g.max_tiles;
+  if (ty == 0) return hipSuccess;
+  return MOE_LAUNCH("mx_gemm_dgrad_down", s,
+                    k_dgrad_down_mx<<<ty * (I / TN), NTHR, 0, s>>>(
+                        g, dYu8, dYus, wdT8, wdTs, Z, topk_w, H, I, k, (bf16_t*)dZ, dZ8, dZs,
+                        (bf16_t*)gh, dgp));
+}
+
+hipError_t launch_mx_dgrad_up(const GroupInfo& g, const uint8_t* dZ8, const uint8_t* dZs,
+                              const uint8_t* wgT8, const uint8_t* wgTs, const uint8_t* wuT8,
+                              const uint8_t* wuTs, int H, int I, void* dX, hipStream_t s) {
+  const unsigned ty = (unsigned)g.max_tiles;
+  if (ty == 0) return hipSuccess;
+  return MOE_LAUNCH("mx_gemm_dgrad_up", s,
+                    k_dgrad_up_mx<<<ty * (H / TN), NTHR, 0, s>>>(g, dZ8, dZs, wgT8, wgTs, wuT8,
+                                                                 wuTs, H, I, (bf16_t*)dX));
+}
+
+hipError_t launch_mx_wgrad(const char* name, const MbPlans& mp, int E, const uint8_t* A8,
+                           const uint8_t* As, const uint8_t* B8, const uint8_t* Bs, int M, int N,
+                           int split, void* out0, void* out1, hipStream_t s) {
+  const unsigned grid = persistent_grid((long)E * (M / TM) * (N / TN));
+  return MOE_LAUNCH(name, s,
+                    k_wgrad_mx<<<grid, NTHR, 0, s>>>(mp, A8, As, B8, Bs, M, N, split,
+                                                     (bf16_t*)out0, (bf16_t*)out1));
+}
+
+}  // namespace moe

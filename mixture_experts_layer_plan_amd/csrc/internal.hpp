@@ -48,6 +48,7 @@ struct PlanPtrs {
   int32_t* err_flag;
   int32_t* active;         // [E] experts with rows, ascending
   int32_t* n_active;
+  int32_t* tile_first;     // [E + 1] first tile of each expert in the tile list
   int32_t* chunk_hist;     // [n_chunks, E]
   int32_t* chunk_invalid;  // [n_chunks]
   int n_chunks;
@@ -106,5 +107,54 @@ hipError_t launch_gemm_wgrad_down(int dt, const GroupInfo& g, const void* dYu, c
 // wgrad-up: dW_g[e] = sum_r dZ[r, :I] (x) X[r], dW_u[e] likewise with dZ[r, I:]
 hipError_t launch_gemm_wgrad_up(int dt, const GroupInfo& g, const void* dZ, const void* X,
                                 int H, int I, void* dwg, void* dwu, hipStream_t s);
+
+// ------------------------------------------------------------------ MXFP8
+#define MX_MAX_MB 8  // minibatches per macro batch in the MX path
+
+// Row quantisation: q[r] = E4M3 of src[gather ? gather[r] : r] (cols values) with
+// one scale per 32; rows r < min(n_rows, *n_rows_dev) (n_rows_dev may be NULL).
+hipError_t launch_quant_rows(int dt, const void* src, const int32_t* gather,
+                             const int32_t* n_rows_dev, int n_rows, int cols, uint8_t* q,
+                             uint8_t* sc, hipStream_t s);
+// Column quantisation of batch x [rows, cols] into batch x [cols, rows] (blocks along rows).
+hipError_t launch_quant_cols(int dt, const void* src, int batch, int rows, int cols, uint8_t* q,
+                             uint8_t* sc, hipStream_t s);
+// Token quantisation of plan tiles into the transposed, tile-padded token axis.
+hipError_t launch_quant_tokens(const void* src, const int32_t* gather, int ld,
+                               const int32_t* tiles, const int32_t* n_tiles,
+                               const int32_t* offsets, int max_tiles, int cols,
+                               size_t kpad_total, size_t kofs, uint8_t* q, uint8_t* sc,
+                               hipStream_t s);
+
+// Tile lists of the minibatch plans, for the wgrads that span all of them.
+struct MbPlans {
+  const int32_t* tile_first[MX_MAX_MB];
+  int n_mb, max_tiles;
+  const int32_t* active;     // union over minibatches of the experts with rows
+  const int32_t* n_active;
+};
+
+// counts_all[e] = sum over minibatch plans of counts[e]; active / n_active list the
+// experts with counts_all > 0 in ascending order.
+hipError_t launch_mb_union(const int32_t* const* counts, int n_mb, int E, int32_t* counts_all,
+                           int32_t* active, int32_t* n_active, hipStream_t s);
+
+hipError_t launch_mx_up_swiglu(const GroupInfo& g, const uint8_t* X8, const uint8_t* Xs,
+                               const uint8_t* wg8, const uint8_t* wgs, const uint8_t* wu8,
+                               const uint8_t* wus, int H, int I, float* Z, uint8_t* hq,
+                               uint8_t* hs, hipStream_t s);
+hipError_t launch_mx_down(const GroupInfo& g, const uint8_t* hq, const uint8_t* hs,
+                          const uint8_t* wd8, const uint8_t* wds, int H, int I, void* Y,
+                          hipStream_t s);
+hipError_t launch_mx_dgrad_down(const GroupInfo& g, const uint8_t* dYu8, const uint8_t* dYus,
+                                const uint8_t* wdT8, const uint8_t* wdTs, const float* Z,
+                                const float* topk_w, int H, int I, int k, void* dZ, uint8_t* dZ8,
+                                uint8_t* dZs, void* gh, float* dgp, hipStream_t s);
+hipError_t launch_mx_dgrad_up(const GroupInfo& g, const uint8_t* dZ8, const uint8_t* dZs,
+                              const uint8_t* wgT8, const uint8_t* wgTs, const uint8_t* wuT8,
+                              const uint8_t* wuTs, int H, int I, void* dX, hipStream_t s);
+hipError_t launch_mx_wgrad(const char* name, const MbPlans& mp, int E, const uint8_t* A8,
+                           const uint8_t* As, const uint8_t* B8, const uint8_t* Bs, int M, int N,
+                           int split, void* out0, void* out1, hipStream_t s);
 
 }  // namespace moe

@@ -1,0 +1,160 @@
+// MXFP8 conversion on the GPU: E4M3 elements with one E8M0 scale per 32.
+//
+// The pages name MXFP8 training with the conversion inside the kernels
+// (sebask.de, "Mixture-of-Kittens: Cursors Open-Source-Ansatz für effizientes
+// MoE-Training auf NVL72", § Determinismus und MXFP8-Unterstützung; stamatios.com,
+// "Cursor abre código de megakernel MoE para GPUs NVL72", § Outras
+// características) but no rule; the block rule is OCP MX v1.0: scale exponent
+// X = floor(log2 amax) - 8 (8 = exponent of E4M3's largest normal, 448), clamped
+// to [-127, 127], X = -127 for an all-zero block, scale byte X + 127; elements are
+// v / 2^X rounded to nearest even into E4M3 ("FN": no infinities) and saturated at
+// +-448; the input's sign bit is kept also when the magnitude rounds to zero.
+//
+// Kernels here: row quantisation (blocks along the contiguous axis, optionally
+// pulling rows through the plan's src_token list: the MX dispatch), column
+// quantisation with a transposed output (weights blocked along their outer
+// axis), and token quantisation (blocks of 32 rows inside each 128-row tile of
+// the plan, written transposed for the wgrad GEMMs).
+#include "common.hpp"
+#include "internal.hpp"
+#include "mx_common.hpp"
+
+namespace moe {
+
+// ------------------------------------------------------------------ rows
+// One wavefront per row, lane handles 32-element blocks b = lane, lane + 64, ...
+// q[r, c] = E4M3(src[g(r), c] / 2^X), s[r, c / 32] = X + 127.
+template <typename T>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ src,
+                                                         const int32_t* __restrict__ gather,
+                                                         const int32_t* __restrict__ n_rows_dev,
+                                                         int n_rows, int cols,
+                                                         uint8_t* __restrict__ q,
+                                                         uint8_t* __restrict__ sc) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int rows = n_rows_dev ? min(n_rows_dev[0], n_rows) : n_rows;
+  if (r >= rows) return;
+  const T* row = src + (size_t)(gather ? gather[r] : r) * cols;
+  const int nb = cols / 32;
+  for (int b = lane; b < nb; b += 64) {
+    float v[32];
+    load32(row + 32 * b, v);
+    const int X = mx_scale_exp(v);
+    uint4 lo, hi;
+    mx_encode32(v, X, lo, hi);
+    uint4* qd = (uint4*)(q + (size_t)r * cols + 32 * b);
+    qd[0] = lo;
+    qd[1] = hi;
+    sc[(size_t)r * nb + b] = (uint8_t)(X + 127);
+  }
+}
+
+// ------------------------------------------------------------ columns
+// Batched [batch, rows, cols] -> q [batch, cols, rows] with blocks of 32 along
+// rows: q[b, c, r] = E4M3(src[b, r, c] / 2^X(b, c, r / 32)).  A workgroup takes a
+// 32 x 256 slab (one row block, 256 columns) through LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void quant_cols_kernel(const T* __restrict__ src, int rows,
+                                                         int cols, uint8_t* __restrict__ q,
+                                                         uint8_t* __restrict__ sc) {
+  __shared__ float tile[32][257];
+  const int rb = blockIdx.x, c0 = blockIdx.y * 256, bat = blockIdx.z;
+  const T* s = src + (size_t)bat * rows * cols;
+  for (int i = threadIdx.x; i < 32 * 256; i += 256) {
+    const int rr = i / 256, cc = i % 256;
+    tile[rr][cc] = (c0 + cc < cols) ? to_f32(s[(size_t)(32 * rb + rr) * cols + c0 + cc]) : 0.0f;
+  }
+  __syncthreads();
+  const int c = c0 + threadIdx.x;
+  if (c >= cols) return;
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = tile[i][threadIdx.x];
+  const int X = mx_scale_exp(v);
+  uint4 lo, hi;
+  mx_encode32(v, X, lo, hi);
+  uint4* qd = (uint4*)(q + (size_t)bat * cols * rows + (size_t)c * rows + 32 * rb);
+  qd[0] = lo;
+  qd[1] = hi;
+  sc[(size_t)bat * cols * (rows / 32) + (size_t)c * (rows / 32) + rb] = (uint8_t)(X + 127);
+}
+
+// ------------------------------------------------------------- tokens
+// For plan tile t (expert e, rows row0 .. row_end-1, at most 128) and column c:
+// blocks of 32 rows from row0; the output is transposed into the tile-padded token
+// axis: q[c, kofs + 128 t + j] for local row j (rows past row_end are zero), with
+// scales s[c, (kofs + 128 t) / 32 + j / 32].  src rows are pulled through gather
+// when given.  One workgroup per (tile, 64 columns).
+template <typename T>
+__global__ __launch_bounds__(256) void quant_tokens_kernel(
+    const T* __restrict__ src, const int32_t* __restrict__ gather, int ld,
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
+    const int32_t* __restrict__ offsets, int cols, size_t kpad_total, size_t kofs,
+    uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
+  __shared__ float tile[128][65];
+  const int t = blockIdx.x, c0 = blockIdx.y * 64;
+  if (t >= n_tiles[0]) return;
+  const int e = tiles[2 * t], row0 = tiles[2 * t + 1];
+  const int row_end = min(row0 + 128, offsets[e + 1]);
+  for (int i = threadIdx.x; i < 128 * 64; i += 256) {
+    const int j = i / 64, cc = i % 64;
+    const int r = row0 + j;
+    tile[j][cc] = (r < row_end) ? to_f32(src[(size_t)(gather ? gather[r] : r) * ld + c0 + cc]) : 0.0f;
+  }
+  __syncthreads();
+  const int cc = threadIdx.x & 63, blk = threadIdx.x >> 6;
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = tile[32 * blk + i][cc];
+  const int X = mx_scale_exp(v);
+  uint4 lo, hi;
+  mx_encode32(v, X, lo, hi);
+  const size_t k = kofs + (size_t)128 * t + 32 * blk;
+  uint4* qd = (uint4*)(q + (size_t)(c0 + cc) * kpad_total + k);
+  qd[0] = lo;
+  qd[1] = hi;
+  sc[(size_t)(c0 + cc) * (kpad_total / 32) + k / 32] = (uint8_t)(X + 127);
+}
+
+// ----------------------------------------------------------- launchers
+hipError_t launch_quant_rows(int dt, const void* src, const int32_t* gather,
+                             const int32_t* n_rows_dev, int n_rows, int cols, uint8_t* q,
+                             uint8_t* sc, hipStream_t s) {
+  if (n_rows == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((n_rows + 3) / 4);
+  if (dt)
+    return MOE_LAUNCH("mx_quant_rows", s,
+                      quant_rows_kernel<bf16_t><<<grid, 256, 0, s>>>(
+                          (const bf16_t*)src, gather, n_rows_dev, n_rows, cols, q, sc));
+  return MOE_LAUNCH("mx_quant_rows", s,
+                    quant_rows_kernel<float><<<grid, 256, 0, s>>>(
+                        (const float*)src, gather, n_rows_dev, n_rows, cols, q, sc));
+}
+
+hipError_t launch_quant_cols(int dt, const void* src, int batch, int rows, int cols, uint8_t* q,
+                             uint8_t* sc, hipStream_t s) {
+  if (batch == 0 || rows == 0) return hipSuccess;
+  const dim3 grid(rows / 32, (cols + 255) / 256, batch);
+  if (dt)
+    return MOE_LAUNCH("mx_quant_cols", s,
+                      quant_cols_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)src, rows,
+                                                                     cols, q, sc));
+  return MOE_LAUNCH("mx_quant_cols", s,
+                    quant_cols_kernel<float><<<grid, 256, 0, s>>>((const float*)src, rows, cols,
+                                                                  q, sc));
+}
+
+hipError_t launch_quant_tokens(const void* src, const int32_t* gather, int ld,
+                               const int32_t* tiles, const int32_t* n_tiles,
+                               const int32_t* offsets, int max_tiles, int cols,
+                               size_t kpad_total, size_t kofs, uint8_t* q, uint8_t* sc,
+                               hipStream_t s) {
+  if (max_tiles == 0) return hipSuccess;
+  return MOE_LAUNCH("mx_quant_tokens", s,
+                    quant_tokens_kernel<bf16_t><<<dim3(max_tiles, cols / 64), 256, 0, s>>>(
+                        (const bf16_t*)src, gather, ld, tiles, n_tiles, offsets, cols, kpad_total,
+                        kofs, q, sc));
+}
+
+}  // namespace moe

@@ -26,6 +26,11 @@
 namespace moe {
 
 constexpr int PLAN_WAVES = 4;  // wavefronts (chunks) per workgroup
+
+struct MbCounts {
+  const int32_t* counts[MX_MAX_MB];
+  int n_mb;
+};
 constexpr int PLAN_STEPS = PLAN_CHUNK / 64;
 
 // Lanes whose expert id equals mine (only meaningful for lanes with ok == true).
@@ -79,7 +84,8 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
     int R, int tile_m, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles, int32_t* __restrict__ err_flag,
     int32_t* __restrict__ src_token, int32_t* __restrict__ src_slot,
-    int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
+    int32_t* __restrict__ active, int32_t* __restrict__ n_active,
+    int32_t* __restrict__ tile_first) {
   __shared__ int32_t s_rows[1];
   __shared__ int32_t s_wave[3][16];
   __shared__ int32_t s_bad;
@@ -104,6 +110,7 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
   const int excl_rows = base_a + a - n, excl_tiles = base_b + b - nt, excl_act = base_c + c3 - act;
   if (tid < E) {
     counts[tid] = n;
+    tile_first[tid] = excl_tiles;
     if (act) active[excl_act] = tid;
     offsets[tid] = excl_rows;
     // first row of each chunk for this expert
@@ -122,6 +129,7 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
     offsets[E] = excl_rows + n;
     n_tiles[0] = excl_tiles + nt;
     n_active[0] = excl_act + act;
+    tile_first[E] = excl_tiles + nt;
     s_rows[0] = excl_rows + n;
   }
   for (int c = tid; c < n_chunks; c += 1024)
@@ -187,12 +195,55 @@ hipError_t launch_plan(const int32_t* topk_idx, int T, int k, int E, const PlanP
                               plan_scan_kernel<<<1, 1024, 0, s>>>(
                                   p.chunk_hist, p.chunk_invalid, p.n_chunks, E, R, GEMM_TILE_M,
                                   p.counts, p.offsets, p.tiles, p.n_tiles, p.err_flag,
-                                  p.src_token, p.src_slot, p.active, p.n_active));
+                                  p.src_token, p.src_slot, p.active, p.n_active,
+                                  p.tile_first));
   if (err != hipSuccess || p.n_chunks == 0) return err;
   return MOE_LAUNCH("plan_scatter", s,
                     plan_scatter_kernel<<<blocks, 256, lds, s>>>(topk_idx, R, E, k, nbits,
                                                                  p.n_chunks, p.chunk_hist,
                                                                  p.src_token, p.src_slot, p.pos));
+}
+
+}  // namespace moe
+
+namespace moe {
+
+// Union of the minibatch plans' expert lists (one workgroup of 1024 threads).
+__global__ __launch_bounds__(1024) void mb_union_kernel(MbCounts mc, int E,
+                                                        int32_t* __restrict__ counts_all,
+                                                        int32_t* __restrict__ active,
+                                                        int32_t* __restrict__ n_active) {
+  __shared__ int32_t s_wave[16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int n = 0;
+  if (tid < E)
+    for (int m = 0; m < mc.n_mb; ++m) n += mc.counts[m][tid];
+  const int act = n > 0 ? 1 : 0;
+  int c = act;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(c, o, 64);
+    if (lane >= o) c += u;
+  }
+  if (lane == 63) s_wave[wv] = c;
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < wv; ++i) base += s_wave[i];
+  const int excl = base + c - act;
+  if (tid < E) {
+    counts_all[tid] = n;
+    if (act) active[excl] = tid;
+  }
+  if (tid == E - 1) n_active[0] = excl + act;
+}
+
+hipError_t launch_mb_union(const int32_t* const* counts, int n_mb, int E, int32_t* counts_all,
+                           int32_t* active, int32_t* n_active, hipStream_t s) {
+  MbCounts mc;
+  mc.n_mb = n_mb;
+  for (int m = 0; m < MX_MAX_MB; ++m) mc.counts[m] = m < n_mb ? counts[m] : nullptr;
+  return MOE_LAUNCH("mb_union", s,
+                    mb_union_kernel<<<1, 1024, 0, s>>>(mc, E, counts_all, active, n_active));
 }
 
 }  // namespace moe
