@@ -427,8 +427,8 @@ MxFwdWs mx_fwd_ws(const moe_shape* s) {
   return L;
 }
 
-// Backward workspace: per-minibatch buffers (dYu ring, dZ bf16 and MX, g h, dg
-// partials, dX) and the token-quantised wgrad operands of all minibatches
+// Backward workspace: per-minibatch buffers (dYu ring, dZ fp32 and MX, g h fp32,
+// dg partials, dX) and the token-quantised wgrad operands of all minibatches
 // (transposed, tile-padded token axis of Kp = n_mb * max_tiles * 128 bytes).
 struct MxBwdWs {
   size_t ring8[2], rings[2], dZ, dZ8, dZs, gh, dgp, dX;
@@ -447,10 +447,10 @@ MxBwdWs mx_bwd_ws(const moe_shape* s) {
     L.ring8[i] = c.take(R * H);
     L.rings[i] = c.take(R * H / 32);
   }
-  L.dZ = c.take(R * 2 * I * 2);
+  L.dZ = c.take(R * 2 * I * sizeof(float));
   L.dZ8 = c.take(R * 2 * I);
   L.dZs = c.take(R * 2 * I / 32);
-  L.gh = c.take(R * I * 2);
+  L.gh = c.take(R * I * sizeof(float));
   L.dgp = c.take(R * (I / 128) * sizeof(float));
   L.dX = c.take(R * H * 2);
   L.dYuT8 = c.take(H * Kp); L.dYuTs = c.take(H * Kp / 32);
@@ -586,14 +586,14 @@ moe_status backward_mx_impl(const moe_shape* s, const void* plan, const void* x,
                                  I, k, dZ, dZ8, dZsc, gh, dgp, st));
     MOE_TRY(launch_dg_reduce(dgp, v.pos, R_m, I / 128, d_topk_w + tok0 * k, st));
     // wgrad operands of this minibatch, quantised along its tokens
-    MOE_TRY(launch_quant_tokens(dym, v.src_token, H, v.tiles, v.n_tiles, v.offsets, P.max_tiles,
+    MOE_TRY(launch_quant_tokens(1, dym, v.src_token, H, v.tiles, v.n_tiles, v.offsets, P.max_tiles,
                                 H, W.Kp, kofs, at<uint8_t>(ws, W.dYuT8), at<uint8_t>(ws, W.dYuTs),
                                 st));
-    MOE_TRY(launch_quant_tokens(xm, v.src_token, H, v.tiles, v.n_tiles, v.offsets, P.max_tiles, H,
+    MOE_TRY(launch_quant_tokens(1, xm, v.src_token, H, v.tiles, v.n_tiles, v.offsets, P.max_tiles, H,
                                 W.Kp, kofs, at<uint8_t>(ws, W.XT8), at<uint8_t>(ws, W.XTs), st));
-    MOE_TRY(launch_quant_tokens(gh, nullptr, I, v.tiles, v.n_tiles, v.offsets, P.max_tiles, I,
+    MOE_TRY(launch_quant_tokens(0, gh, nullptr, I, v.tiles, v.n_tiles, v.offsets, P.max_tiles, I,
                                 W.Kp, kofs, at<uint8_t>(ws, W.ghT8), at<uint8_t>(ws, W.ghTs), st));
-    MOE_TRY(launch_quant_tokens(dZ, nullptr, 2 * I, v.tiles, v.n_tiles, v.offsets, P.max_tiles,
+    MOE_TRY(launch_quant_tokens(0, dZ, nullptr, 2 * I, v.tiles, v.n_tiles, v.offsets, P.max_tiles,
                                 2 * I, W.Kp, kofs, at<uint8_t>(ws, W.dZT8), at<uint8_t>(ws, W.dZTs),
                                 st));
     MOE_TRY(launch_mx_dgrad_up(g, dZ8, dZsc, q + Q.wgT8, q + Q.wgTs, q + Q.wuT8, q + Q.wuTs, H, I,
@@ -703,7 +703,7 @@ moe_status moe_quantize_mxfp8(const void* src, int64_t rows, int64_t cols, int a
     return hip_status(launch_quant_rows(1, src, nullptr, nullptr, (int)rows, (int)cols, q, scales, st));
   }
   if (axis == 0) {
-    if (rows % 32 || cols % 16) return MOE_E_SHAPE;
+    if (rows % 32) return MOE_E_SHAPE;
     return hip_status(launch_quant_cols(1, src, 1, (int)rows, (int)cols, q, scales, st));
   }
   return MOE_E_SHAPE;

@@ -270,13 +270,14 @@ __global__ __launch_bounds__(NTHR, 2) void k_down_mx(GroupInfo g, const uint8_t*
 
 // dgrad-down, MX: dh' = Q_H(dYu) Q_H(W_d) with W_d stored transposed [E, I, H];
 // epilogue as the bf16 kernel (SwiGLU backward from fp32 Z, router-weight
-// gradient partials, dZ and g h in bf16) plus dZ quantised along 2I for dgrad-up.
+// gradient partials) writing dZ = (dA | dB) and g h in fp32 for the token
+// quantiser, plus dZ quantised along 2I for dgrad-up.
 __global__ __launch_bounds__(NTHR, 2) void k_dgrad_down_mx(
     GroupInfo g, const uint8_t* __restrict__ dYu8, const uint8_t* __restrict__ dYus,
     const uint8_t* __restrict__ wdT8, const uint8_t* __restrict__ wdTs,
     const float* __restrict__ Z, const float* __restrict__ topk_w, int H, int I, int k,
-    bf16_t* __restrict__ dZ, uint8_t* __restrict__ dZ8, uint8_t* __restrict__ dZs,
-    bf16_t* __restrict__ gh, float* __restrict__ dgp) {
+    float* __restrict__ dZ, uint8_t* __restrict__ dZ8, uint8_t* __restrict__ dZs,
+    float* __restrict__ gh, float* __restrict__ dgp) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   RowTile t;
   int nt;
@@ -335,7 +336,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_dgrad_down_mx(
         db[q] = dh * sl;
         gh8[q] = gate * hv;
       }
-      bf16_t* dzr = dZ + (size_t)row * (2 * I);
+      float* dzr = dZ + (size_t)row * (2 * I);
       store8(dzr + i0 + 8 * c, da);
       store8(dzr + I + i0 + 8 * c, db);
       store8(gh + (size_t)row * I + i0 + 8 * c, gh8);
@@ -510,8 +511,8 @@ hipError_t launch_mx_dgrad_down(const GroupInfo& g, const uint8_t* dYu8, const u
   if (ty == 0) return hipSuccess;
   return MOE_LAUNCH("mx_gemm_dgrad_down", s,
                     k_dgrad_down_mx<<<ty * (I / TN), NTHR, 0, s>>>(
-                        g, dYu8, dYus, wdT8, wdTs, Z, topk_w, H, I, k, (bf16_t*)dZ, dZ8, dZs,
-                        (bf16_t*)gh, dgp));
+                        g, dYu8, dYus, wdT8, wdTs, Z, topk_w, H, I, k, (float*)dZ, dZ8, dZs,
+                        (float*)gh, dgp));
 }
 
 hipError_t launch_mx_dgrad_up(const GroupInfo& g, const uint8_t* dZ8, const uint8_t* dZs,

@@ -119,8 +119,9 @@ hipError_t launch_quant_rows(int dt, const void* src, const int32_t* gather,
 // Column quantisation of batch x [rows, cols] into batch x [cols, rows] (blocks along rows).
 hipError_t launch_quant_cols(int dt, const void* src, int batch, int rows, int cols, uint8_t* q,
                              uint8_t* sc, hipStream_t s);
-// Token quantisation of plan tiles into the transposed, tile-padded token axis.
-hipError_t launch_quant_tokens(const void* src, const int32_t* gather, int ld,
+// Token quantisation of plan tiles into the transposed, tile-padded token axis
+// (dt 1: bf16 source, 0: fp32 source).
+hipError_t launch_quant_tokens(int dt, const void* src, const int32_t* gather, int ld,
                                const int32_t* tiles, const int32_t* n_tiles,
                                const int32_t* offsets, int max_tiles, int cols,
                                size_t kpad_total, size_t kofs, uint8_t* q, uint8_t* sc,

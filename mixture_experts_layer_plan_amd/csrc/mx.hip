@@ -145,15 +145,21 @@ hipError_t launch_quant_cols(int dt, const void* src, int batch, int rows, int c
                                                                   q, sc));
 }
 
-hipError_t launch_quant_tokens(const void* src, const int32_t* gather, int ld,
+hipError_t launch_quant_tokens(int dt, const void* src, const int32_t* gather, int ld,
                                const int32_t* tiles, const int32_t* n_tiles,
                                const int32_t* offsets, int max_tiles, int cols,
                                size_t kpad_total, size_t kofs, uint8_t* q, uint8_t* sc,
                                hipStream_t s) {
   if (max_tiles == 0) return hipSuccess;
+  const dim3 grid(max_tiles, cols / 64);
+  if (dt)
+    return MOE_LAUNCH("mx_quant_tokens", s,
+                      quant_tokens_kernel<bf16_t><<<grid, 256, 0, s>>>(
+                          (const bf16_t*)src, gather, ld, tiles, n_tiles, offsets, cols,
+                          kpad_total, kofs, q, sc));
   return MOE_LAUNCH("mx_quant_tokens", s,
-                    quant_tokens_kernel<bf16_t><<<dim3(max_tiles, cols / 64), 256, 0, s>>>(
-                        (const bf16_t*)src, gather, ld, tiles, n_tiles, offsets, cols, kpad_total,
+                    quant_tokens_kernel<float><<<grid, 256, 0, s>>>(
+                        (const float*)src, gather, ld, tiles, n_tiles, offsets, cols, kpad_total,
                         kofs, q, sc));
 }
 

@@ -2,7 +2,7 @@
 
 ``LayerBuffers`` allocates (through torch, on the current device) every output,
 the plan, the saved activations and the workspaces that the C-ABI asks for.
-``run_layer`` enqueues route -> plan -> forward [-> backward -> router backward]
+``run_layer`` enqueues route -> plan -> [MX weight quantisation ->] forward [-> backward -> router backward]
 on the current stream.  Both only move pointers; the arithmetic is in libmoe.so.
 """
 from __future__ import annotations
@@ -14,12 +14,12 @@ from . import binding as B
 
 class LayerBuffers:
     def __init__(self, T, H, I, E, k, I_shared=0, dtype="bf16", backward=True,
-                 router_gemm=False, device="cuda"):
-        if dtype not in ("bf16", "f32"):
+                 router_gemm=False, device="cuda", T_minibatch=0):
+        if dtype not in ("bf16", "f32", "mxfp8"):
             raise ValueError(f"unsupported dtype {dtype}")
         self.dtype = dtype
         self.dt = B.DTYPES[dtype]
-        self.s = B.shape(T, H, I, E, k, I_shared)
+        self.s = B.shape(T, H, I, E, k, I_shared, T_minibatch)
         tdt = torch.float32 if dtype == "f32" else torch.bfloat16
         dev = torch.device(device)
         u8 = dict(dtype=torch.uint8, device=dev)
@@ -29,6 +29,7 @@ class LayerBuffers:
         self.plan = torch.empty(B.moe_plan_bytes(self.s), **u8)
         self.saved = torch.empty(B.moe_saved_bytes(self.s, self.dt), **u8)
         self.ws_fwd = torch.empty(B.moe_workspace_bytes(self.s, self.dt, False), **u8)
+        self.wq = torch.empty(B.moe_mx_weights_bytes(self.s), **u8) if dtype == "mxfp8" else None
         self.y = torch.empty((T, H), dtype=tdt, device=dev)
         self.logits = torch.empty((T, E), dtype=torch.float32, device=dev) if router_gemm else None
         self.backward = backward
@@ -61,6 +62,11 @@ def run_forward(b: LayerBuffers, inp: dict, stream=None):
         logits = inp["logits"]
     B.moe_route(s, logits, b.topk_idx, b.topk_w, stream)
     B.moe_plan(s, b.topk_idx, b.plan, stream)
+    if b.dtype == "mxfp8":
+        B.moe_quantize_weights_mxfp8(s, inp["w_gate"], inp["w_up"], inp["w_down"], b.wq, stream)
+        B.moe_forward_mxfp8(s, b.plan, inp["x"], b.topk_w, b.wq, inp.get("s_gate"),
+                            inp.get("s_up"), inp.get("s_down"), b.y, b.saved, b.ws_fwd, stream)
+        return
     fwd = B.moe_forward_bf16 if b.dtype == "bf16" else B.moe_forward_f32
     fwd(s, b.plan, inp["x"], b.topk_w, inp["w_gate"], inp["w_up"], inp["w_down"],
         inp.get("s_gate"), inp.get("s_up"), inp.get("s_down"), b.y, b.saved, b.ws_fwd, stream)
@@ -68,11 +74,17 @@ def run_forward(b: LayerBuffers, inp: dict, stream=None):
 
 def run_backward(b: LayerBuffers, inp: dict, stream=None):
     s = b.s
-    bwd = B.moe_backward_bf16 if b.dtype == "bf16" else B.moe_backward_f32
-    bwd(s, b.plan, inp["x"], b.topk_w, inp["w_gate"], inp["w_up"], inp["w_down"],
-        inp.get("s_gate"), inp.get("s_up"), inp.get("s_down"), b.saved, inp["dy"], b.dx,
-        b.dw_gate, b.dw_up, b.dw_down, b.ds_gate, b.ds_up, b.ds_down, b.d_topk_w, b.ws_bwd,
-        stream)
+    if b.dtype == "mxfp8":
+        B.moe_backward_mxfp8(s, b.plan, inp["x"], b.topk_w, b.wq, inp.get("s_gate"),
+                             inp.get("s_up"), inp.get("s_down"), b.saved, inp["dy"], b.dx,
+                             b.dw_gate, b.dw_up, b.dw_down, b.ds_gate, b.ds_up, b.ds_down,
+                             b.d_topk_w, b.ws_bwd, stream)
+    else:
+        bwd = B.moe_backward_bf16 if b.dtype == "bf16" else B.moe_backward_f32
+        bwd(s, b.plan, inp["x"], b.topk_w, inp["w_gate"], inp["w_up"], inp["w_down"],
+            inp.get("s_gate"), inp.get("s_up"), inp.get("s_down"), b.saved, inp["dy"], b.dx,
+            b.dw_gate, b.dw_up, b.dw_down, b.ds_gate, b.ds_up, b.ds_down, b.d_topk_w, b.ws_bwd,
+            stream)
     B.moe_route_backward(s, b.topk_idx, b.topk_w, b.d_topk_w, b.d_logits, stream)
     if "w_router" in inp:
         B.moe_router_backward_f32(s, inp["x"], inp["w_router"], b.d_logits, b.dw_router, b.dx,

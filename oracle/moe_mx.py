@@ -194,3 +194,38 @@ def layer_backward_mx(cache: dict, dy) -> dict:
     out["dx"] = dx
     out["dlogits"] = route_backward(cache["topk_idx"], g, dg, E)
     return out
+
+
+def token_mx(x_t, idx_t, w_t, dy_t, qc: _QuantCache, shared=None, backward=True):
+    """One token straight from the MX definition (no plan, no minibatch): returns
+    (y_t, dx_t, dg_t); dx_t and dg_t are None without ``backward``.  The
+    row-local quantisations (x and dy along H, h along I, dA and dB along I) do not
+    depend on the minibatch, so these equal the planned results row for row."""
+    v = q_rows(_f64(x_t)[None])[0]
+    g = _f64(w_t)
+    y = np.zeros_like(v)
+    dx = np.zeros_like(v) if backward else None
+    dg = np.zeros(len(idx_t)) if backward else None
+    d = q_rows(_f64(dy_t)[None])[0] if backward else None
+    for j, e in enumerate(np.asarray(idx_t).astype(int)):
+        A = qc.get("g_H", e) @ v
+        B = qc.get("u_H", e) @ v
+        h = silu(A) * B
+        y += g[j] * (qc.get("d_I", e) @ q_rows(h[None])[0])
+        if backward:
+            dhp = qc.get("d_H", e).T @ d
+            dg[j] = float(dhp @ h)
+            dh = g[j] * dhp
+            dA = dh * B * dsilu(A)
+            dB = dh * silu(A)
+            dx += qc.get("g_I", e).T @ q_rows(dA[None])[0] + qc.get("u_I", e).T @ q_rows(dB[None])[0]
+    if shared is not None:
+        Sg, Su, Sd = (_f64(a) for a in shared)
+        xf = _f64(x_t)
+        A = Sg @ xf
+        B = Su @ xf
+        y += Sd @ (silu(A) * B)
+        if backward:
+            dh = Sd.T @ _f64(dy_t)
+            dx += Sg.T @ (dh * B * dsilu(A)) + Su.T @ (dh * silu(A))
+    return y, dx, dg

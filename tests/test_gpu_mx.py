@@ -1,0 +1,175 @@
+"""GPU parity of the MXFP8 path: the quantisers bit-exact against the oracle's OCP
+MX quantiser, the layer (forward + backward over a ring of minibatches) against
+the MXFP8 oracle fed the same dequantised operands, and the properties that hold
+at any size (row-local outputs independent of the minibatch size, bitwise
+repeatability)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import digest, np_, say, shared_of, to_dev
+from oracle import moe_mx
+from oracle.mx import mx_quantize
+from synth import CONFIGS, Shape, make_inputs
+from tolerance import check
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    from mixture_experts_layer_plan_amd import binding
+    return binding
+
+
+def mx_input(rows, cols, seed):
+    g = torch.Generator().manual_seed(seed)
+    a = torch.randn((rows, cols), generator=g) * torch.exp(torch.randn((rows, 1), generator=g) * 3)
+    a[0, :32] = 0.0                                   # an all-zero block
+    a[1, :32] = -0.0
+    a[2, 5] = 1e30                                    # a block dominated by one huge value
+    a[3, :] = torch.randn(cols, generator=g) * 1e-38  # fp32 subnormal range
+    return a.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("rows,cols", [(64, 256), (96, 7168)])
+def test_quantise_rows_bitexact(B, rows, cols):
+    say(f"mx quantise rows {rows}x{cols}")
+    a = mx_input(rows, cols, 1)
+    q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+    s = torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda")
+    B.moe_quantize_mxfp8(a.cuda(), rows, cols, 1, q, s)
+    torch.cuda.synchronize()
+    rq, rs = mx_quantize(a.double().numpy(), axis=1)
+    np.testing.assert_array_equal(np_(s), rs)
+    np.testing.assert_array_equal(np_(q), rq)
+
+
+@pytest.mark.parametrize("rows,cols", [(64, 256), (2048, 300)])
+def test_quantise_cols_transposed_bitexact(B, rows, cols):
+    say(f"mx quantise cols {rows}x{cols}")
+    a = mx_input(rows, cols, 2)
+    q = torch.empty((cols, rows), dtype=torch.uint8, device="cuda")
+    s = torch.empty((cols, rows // 32), dtype=torch.uint8, device="cuda")
+    B.moe_quantize_mxfp8(a.cuda(), rows, cols, 0, q, s)
+    torch.cuda.synchronize()
+    rq, rs = mx_quantize(a.double().numpy(), axis=0)
+    np.testing.assert_array_equal(np_(q), rq.T)
+    np.testing.assert_array_equal(np_(s), rs.T)
+
+
+def test_weight_quantisation_all_orientations(B):
+    say("mx weight quantisation")
+    E, I, H = 3, 128, 256
+    shape = Shape(T=8, H=H, I=I, E=E, k=2)
+    inp = make_inputs(shape, seed=3, device="cpu")
+    s = B.shape(8, H, I, E, 2)
+    wq = torch.empty(B.moe_mx_weights_bytes(s), dtype=torch.uint8, device="cuda")
+    B.moe_quantize_weights_mxfp8(s, inp["w_gate"].cuda(), inp["w_up"].cuda(), inp["w_down"].cuda(), wq)
+    torch.cuda.synchronize()
+    buf = np_(wq)
+    n = E * I * H
+    off = 0
+
+    def take(nbytes):
+        nonlocal off
+        v = buf[off:off + nbytes]
+        off += -(-nbytes // 256) * 256
+        return v
+
+    wg, wu, wd = (inp[k].double().numpy() for k in ("w_gate", "w_up", "w_down"))
+    expect = [(wg, 2, False), (wu, 2, False), (wd, 2, False), (wd, 1, True), (wg, 1, True),
+              (wu, 1, True)]
+    for arr, axis, transposed in expect:
+        codes = take(n)
+        scales = take(n // 32)
+        rq, rs = mx_quantize(arr, axis=axis)
+        if transposed:
+            rq, rs = np.swapaxes(rq, 1, 2), np.swapaxes(rs, 1, 2)
+        np.testing.assert_array_equal(codes, rq.reshape(-1))
+        np.testing.assert_array_equal(scales, rs.reshape(-1))
+
+
+def gpu_mx(shape, inp, T_mb):
+    from mixture_experts_layer_plan_amd import LayerBuffers, run_layer
+    b = LayerBuffers(shape.T, shape.H, shape.I, shape.E, shape.k, shape.I_shared, "mxfp8",
+                     backward=True, T_minibatch=T_mb)
+    run_layer(b, inp, backward=True)
+    torch.cuda.synchronize()
+    return b
+
+
+SMALL_MX = {
+    "ring3_ragged": (Shape(T=300, H=256, I=256, E=8, k=2, I_shared=128, dtype="mxfp8"), 128),
+    "skew_ring": (Shape(T=512, H=384, I=256, E=16, k=4, I_shared=256, zipf_s=1.2, dtype="mxfp8"), 128),
+    "one_minibatch": (Shape(T=200, H=256, I=128, E=6, k=3, dtype="mxfp8"), 0),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL_MX))
+def test_mx_layer_small_all_outputs(name):
+    shape, T_mb = SMALL_MX[name]
+    say(f"mx layer {name}: {shape} T_mb={T_mb}")
+    inp = make_inputs(shape, seed=0, device="cpu", with_dy=True)
+    b = gpu_mx(shape, to_dev(inp), T_mb)
+    c = moe_mx.layer_forward_mx(inp["x"], inp["logits"], shape.k, inp["w_gate"], inp["w_up"],
+                                inp["w_down"], shared=shared_of(inp), T_mb=T_mb)
+    g = moe_mx.layer_backward_mx(c, inp["dy"])
+    np.testing.assert_array_equal(np_(b.topk_idx), c["topk_idx"])
+    check(b.y, c["y"], "mxfp8", "y")
+    check(b.dx, g["dx"], "mxfp8", "dx")
+    check(b.d_topk_w, g["dg"], "mxfp8", "d_topk_w")
+    check(b.d_logits, g["dlogits"], "mxfp8", "d_logits")
+    for e in range(shape.E):
+        for n in ("dw_gate", "dw_up", "dw_down"):
+            check(getattr(b, n)[e], g[n][e], "mxfp8", f"{n}[{e}]")
+    if shape.I_shared:
+        for n in ("ds_gate", "ds_up", "ds_down"):
+            check(getattr(b, n), g[n], "bf16", n)
+
+
+def test_mx_row_local_outputs_bitwise_independent_of_minibatch_size():
+    shape, _ = SMALL_MX["skew_ring"]
+    say("mx minibatch-size invariance of y, dx, d_topk_w")
+    inp = to_dev(make_inputs(shape, seed=4, device="cpu", with_dy=True))
+    outs = []
+    for T_mb in (0, 256, 128):
+        b = gpu_mx(shape, inp, T_mb)
+        outs.append(digest(b.y, b.dx, b.d_topk_w))
+    assert outs[0] == outs[1] == outs[2]
+
+
+def test_mx_bitwise_repeatable():
+    shape, T_mb = SMALL_MX["ring3_ragged"]
+    say("mx repeatability")
+    inp = to_dev(make_inputs(shape, seed=5, device="cpu", with_dy=True))
+    d = [digest(*(getattr(gpu_mx(shape, inp, T_mb), n) for n in
+                  ("y", "dx", "dw_gate", "dw_up", "dw_down", "d_topk_w"))) for _ in range(3)]
+    assert d[0] == d[1] == d[2]
+
+
+def test_mx_full_size_sampled():
+    name = "kimi_mxfp8_ring"
+    shape = CONFIGS[name]
+    say(f"{name}: inputs on the device")
+    inp = make_inputs(shape, seed=0, device="cuda", with_dy=True)
+    say(f"{name}: layer over {shape.T // shape.T_minibatch} minibatches")
+    b = gpu_mx(shape, inp, shape.T_minibatch)
+    L = np_(inp["logits"])
+    idx, w = oracle.route(L, shape.k)
+    np.testing.assert_array_equal(np_(b.topk_idx), idx)
+    qc = moe_mx._QuantCache(inp["w_gate"], inp["w_up"], inp["w_down"])
+    sh = shared_of(inp)
+    toks = [5, shape.T - 3]
+    say(f"{name}: oracle on tokens {toks}")
+    y_ref, dx_ref, dg_ref = [], [], []
+    for t in toks:
+        y_t, dx_t, dg_t = moe_mx.token_mx(inp["x"][t], idx[t], w[t], inp["dy"][t], qc, shared=sh,
+                                          backward=(t == toks[0]))
+        y_ref.append(y_t)
+        dx_ref.append(dx_t)
+        dg_ref.append(dg_t)
+    check(np_(b.y.double())[toks], np.stack(y_ref), "mxfp8", "y (sampled)")
+    check(np_(b.dx.double())[toks[0]], dx_ref[0], "mxfp8", "dx (sampled)")
+    check(np_(b.d_topk_w)[toks[0]], dg_ref[0], "mxfp8", "d_topk_w (sampled)")

@@ -132,3 +132,16 @@ def test_q_tokens_blocks_start_at_first_row():
     assert np.all(q[:32] == 1.0)            # first block untouched by the huge row
     assert np.all(q[32:35] == 0.0) and np.all(q[36:] == 0.0)
     assert np.all(q[35] == 2.0 ** 20)
+
+
+def test_per_token_mx_equals_planned_rows():
+    rng = np.random.default_rng(6)
+    d = rand_layer(rng, 48, 64, 64, 5)
+    c, g = run_mx(d, 2, 16)
+    qc = c["qcache"]
+    for t in (0, 17, 47):
+        y_t, dx_t, dg_t = moe_mx.token_mx(d["x"][t], c["topk_idx"][t], c["topk_w"][t], d["dy"][t],
+                                          qc, shared=d["shared"])
+        np.testing.assert_allclose(y_t, c["y"][t], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dx_t, g["dx"][t], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(dg_t, g["dg"][t], rtol=1e-11, atol=1e-12)
