@@ -61,6 +61,32 @@ def kernel_work(name, sh, counts, es=2):
     return w.get(name, (0, 0))
 
 
+def kernel_sources_sha256() -> str:
+    """Hash of the HIP sources of the library (kernels and their headers)."""
+    import hashlib
+    d = os.path.join(ROOT, "mixture_experts_layer_plan_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary of this workload, scaled by the copy-kernel calibration;
+    None when there is none or the kernel sources changed since it was taken."""
+    p = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    return None if k is None else int(k["fetch_bytes"] + k["write_bytes"])
+
+
 def cpu_baseline(sh, inp, n_tokens):
     """The fp64 oracle, as it stands, on the first n_tokens tokens of the workload
     (forward + backward with every expert's weights streamed from the device)."""
@@ -178,7 +204,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(byt / avg_s / 1e9, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom, args.config)
     roof["kernel"] = dom
     roof["algorithmic_bytes"] = byt
     roof["algorithmic_flops"] = flop

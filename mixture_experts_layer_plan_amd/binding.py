@@ -81,7 +81,7 @@ _SIGS = {
     "moe_mx_weights_bytes": (_Z, [_S]),
     "moe_quantize_weights_mxfp8": (_I, [_S, _P, _P, _P, _P, _P]),
     "moe_quantize_mxfp8": (_I, [_P, ctypes.c_int64, ctypes.c_int64, _I, _P, _P, _P]),
-    "moe_forward_mxfp8": (_I, [_S] + [_P] * 11 + [_Z, _P]),
+    "moe_forward_mxfp8": (_I, [_S] + [_P] * 10 + [_Z, _P]),
     "moe_backward_mxfp8": (_I, [_S] + [_P] * 18 + [_Z, _P]),
 }
 

@@ -58,11 +58,9 @@ __global__ __launch_bounds__(NTHR, 2) void k_up_swiglu(GroupInfo g, const T* __r
     const int rr = (threadIdx.x >> 3) + 32 * s;
     const int r = t.row0 + rr;
     const bool ok = r < t.row_end;
-    const T* xrow = x + (size_t)token_of(g, ok ? r : t.row0) * H;
-    la.set(s, xrow, ok, xrow);
-    const T* wrow =
-        rr < 64 ? wg + wofs + (size_t)(i0 + rr) * H : wu + wofs + (size_t)(i0 + rr - 64) * H;
-    lb.set(s, wrow, true, wrow);
+    la.set(s, ok ? x + (size_t)token_of(g, r) * H : nullptr, ok);
+    lb.set(s, rr < 64 ? wg + wofs + (size_t)(i0 + rr) * H : wu + wofs + (size_t)(i0 + rr - 64) * H,
+           true);
   }
   int arow, brow[2];
   wave_coords(arow, brow, true);
@@ -106,8 +104,8 @@ __global__ __launch_bounds__(NTHR, 2) void k_down(GroupInfo g, const T* __restri
   for (int s = 0; s < 4; ++s) {
     const int rr = (threadIdx.x >> 3) + 32 * s;
     const int r = t.row0 + rr;
-    la.set(s, h + (size_t)r * I, r < t.row_end, h + (size_t)t.row0 * I);
-    lb.set(s, wd + wofs + (size_t)(n0 + rr) * I, true, wd);
+    la.set(s, h + (size_t)r * I, r < t.row_end);
+    lb.set(s, wd + wofs + (size_t)(n0 + rr) * I, true);
   }
   int arow, brow[2];
   wave_coords(arow, brow, false);
@@ -141,7 +139,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_dgrad_down(GroupInfo g, const T* __
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int r = t.row0 + (threadIdx.x >> 3) + 32 * s;
-    la.set(s, dYu + (size_t)r * H, r < t.row_end, dYu + (size_t)t.row0 * H);
+    la.set(s, dYu + (size_t)r * H, r < t.row_end);
   }
   MNLoad<T, KRowPlain<T>> lb{{wd + (size_t)t.e * H * I + i0, (size_t)I}};
   int arow, brow[2];
@@ -206,7 +204,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_dgrad_up(GroupInfo g, const T* __re
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int r = t.row0 + (threadIdx.x >> 3) + 32 * s;
-    la.set(s, dZ + (size_t)r * (2 * I), r < t.row_end, dZ + (size_t)t.row0 * (2 * I));
+    la.set(s, dZ + (size_t)r * (2 * I), r < t.row_end);
   }
   MNLoad<T, KRowCat<T>> lb{{wg + wofs, wu + wofs, I, H}};
   int arow, brow[2];

@@ -26,28 +26,19 @@ MOE_DEV int cidx(int row, int col) { return row * 128 + ((((col >> 3) ^ (row & 1
 MOE_DEV uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
 // ------------------------------------------------------------------ loaders
-// Loads are branch-free: a row outside the operand reads a valid row and is
-// zeroed with a select afterwards.  (A load under a branch keeps the compiler from
-// counting outstanding loads, and it then waits for all of them before the next
-// LDS store, which removes the prefetch.)
-MOE_DEV uint4 keep_if(bool ok, const uint4& v) {
-  return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
-}
-
-// K-major operand: thread t loads chunk (t & 7) of tile rows (t >> 3) + 32 s.
-// rp[s] must point at a readable row; ok[s] = false zeroes it.
+// K-major operand: thread t loads chunk (t & 7) of tile rows (t >> 3) + 32 s; a
+// row outside the operand (rp = nullptr) loads as zeros.  (Measured on MI355X:
+// this branchy form beats a branch-free load-and-select, whose extra loads of
+// padding rows and re-reads of the last K tile cost more than the conservative
+// wait the branches cause.)
 template <typename T>
 struct KLoad {
   const T* rp[4];
-  bool ok[4];
-  MOE_DEV void set(int s, const T* p, bool valid, const T* fallback) {
-    rp[s] = valid ? p : fallback;
-    ok[s] = valid;
-  }
+  MOE_DEV void set(int s, const T* p, bool valid) { rp[s] = valid ? p : nullptr; }
   MOE_DEV void load(int kt, uint4 (&r)[4]) const {
     const int k = kt * Tr<T>::BK + (threadIdx.x & 7) * Tr<T>::VEC;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) r[s] = keep_if(ok[s], *(const uint4*)(rp[s] + k));
+    for (int s = 0; s < 4; ++s) r[s] = rp[s] ? *(const uint4*)(rp[s] + k) : zero4();
   }
   MOE_DEV void store(char* t, const uint4 (&r)[4]) const {
     const int row = threadIdx.x >> 3, ch = threadIdx.x & 7;
@@ -56,9 +47,8 @@ struct KLoad {
   }
 };
 
-// MN-major operand: element (k, i) of the tile at kr(k)[i]; kr.valid(k) is false
-// for K rows outside the operand (kr(k) still points at a readable row; the data
-// is zeroed).
+// MN-major operand: element (k, i) of the tile at kr(k)[i]; kr returns nullptr
+// for K rows outside the operand (they load as zeros).
 // bf16: thread t owns k = 4 (t >> 4) .. +3, i = 8 (t & 15) .. +7.
 // fp32: thread t owns k = 4 (t >> 5) .. +3, i = 4 (t & 31) .. +3.
 template <typename T, class KR>
@@ -69,8 +59,10 @@ struct MNLoad {
     const int kb = threadIdx.x / IB, ib = threadIdx.x % IB;
     const int k0 = kt * Tr<T>::BK + 4 * kb;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      r[kk] = keep_if(kr.valid(k0 + kk), *(const uint4*)(kr(k0 + kk) + ib * Tr<T>::VEC));
+    for (int kk = 0; kk < 4; ++kk) {
+      const T* p = kr(k0 + kk);
+      r[kk] = p ? *(const uint4*)(p + ib * Tr<T>::VEC) : zero4();
+    }
   }
   MOE_DEV void store(char* t, const uint4 (&r)[4]) const;
 };
@@ -183,11 +175,16 @@ MOE_DEV void gemm_main(char* lds, const LA& la, const LB& lb, int nk, f32x16_t (
     for (int kt = 0; kt < nk; ++kt) {
       char* cur = lds + (kt & 1) * 2 * TILEB;
       char* nxt = lds + ((kt + 1) & 1) * 2 * TILEB;
-      la.load(min(kt + 1, nk - 1), ra);
-      lb.load(min(kt + 1, nk - 1), rb);
+      const bool more = kt + 1 < nk;
+      if (more) {
+        la.load(kt + 1, ra);
+        lb.load(kt + 1, rb);
+      }
       mma_tile<T>(cur, cur + TILEB, acc, arow, brow, lane);
-      la.store(nxt, ra);
-      lb.store(nxt + TILEB, rb);
+      if (more) {
+        la.store(nxt, ra);
+        lb.store(nxt + TILEB, rb);
+      }
       __syncthreads();
     }
     return;
@@ -195,29 +192,36 @@ MOE_DEV void gemm_main(char* lds, const LA& la, const LB& lb, int nk, f32x16_t (
   char* buf0 = lds;
   char* buf1 = lds + 2 * TILEB;
   uint4 ra0[4], rb0[4], ra1[4], rb1[4];
-  const int last = nk - 1;
   la.load(0, ra0);
   lb.load(0, rb0);
-  la.load(min(1, last), ra1);
-  lb.load(min(1, last), rb1);
+  if (nk > 1) {
+    la.load(1, ra1);
+    lb.load(1, rb1);
+  }
   la.store(buf0, ra0);
   lb.store(buf0 + TILEB, rb0);
   __syncthreads();
-  // Every load is issued unconditionally (past the last tile it re-reads the last
-  // tile) so that the compiler can wait for exactly the older register set.
   for (int kt = 0; kt < nk; kt += 2) {
-    la.load(min(kt + 2, last), ra0);
-    lb.load(min(kt + 2, last), rb0);
+    if (kt + 2 < nk) {
+      la.load(kt + 2, ra0);
+      lb.load(kt + 2, rb0);
+    }
     mma_tile<T>(buf0, buf0 + TILEB, acc, arow, brow, lane);
-    la.store(buf1, ra1);
-    lb.store(buf1 + TILEB, rb1);
+    if (kt + 1 < nk) {
+      la.store(buf1, ra1);
+      lb.store(buf1 + TILEB, rb1);
+    }
     __syncthreads();
     if (kt + 1 >= nk) break;
-    la.load(min(kt + 3, last), ra1);
-    lb.load(min(kt + 3, last), rb1);
+    if (kt + 3 < nk) {
+      la.load(kt + 3, ra1);
+      lb.load(kt + 3, rb1);
+    }
     mma_tile<T>(buf1, buf1 + TILEB, acc, arow, brow, lane);
-    la.store(buf0, ra0);
-    lb.store(buf0 + TILEB, rb0);
+    if (kt + 2 < nk) {
+      la.store(buf0, ra0);
+      lb.store(buf0 + TILEB, rb0);
+    }
     __syncthreads();
   }
 }
@@ -323,7 +327,6 @@ struct KRowPlain {
   const T* base;
   size_t ld;
   MOE_DEV const T* operator()(int k) const { return base + (size_t)k * ld; }
-  MOE_DEV bool valid(int) const { return true; }
 };
 
 // Weights of dgrad-up as one [2I, H] operand: rows < I from W_g[e], the rest W_u[e]
@@ -335,7 +338,6 @@ struct KRowCat {
   MOE_DEV const T* operator()(int k) const {
     return k < I ? wg + (size_t)k * H : wu + (size_t)(k - I) * H;
   }
-  MOE_DEV bool valid(int) const { return true; }
 };
 
 // K rows of a K-grouped operand: segment row seg0 + k (valid below seg1) of a
@@ -346,13 +348,11 @@ struct KRowSeg {
   const int32_t* gather;
   size_t ld;
   int seg0, seg1;
-  // rows past the segment read the segment's first row (callers only load when
-  // the segment is not empty) and are zeroed through valid()
   MOE_DEV const T* operator()(int k) const {
-    const int r = seg0 + k < seg1 ? seg0 + k : seg0;
+    const int r = seg0 + k;
+    if (r >= seg1) return nullptr;
     return base + (size_t)(gather ? gather[r] : r) * ld;
   }
-  MOE_DEV bool valid(int k) const { return seg0 + k < seg1; }
 };
 
 MOE_DEV void k_segment(const GroupInfo& g, int e, int& seg0, int& seg1) {

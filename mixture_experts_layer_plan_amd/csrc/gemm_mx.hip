@@ -33,8 +33,7 @@ constexpr int MX_BK = 128;  // K bytes per tile row (4 scale blocks)
 // (t >> 3) + 32 s of the tile), scale rows for its MFMA fragments (two 32-row
 // blocks).  A second source can take over at K >= ksplit (dgrad-up weights); its
 // pointers are pre-offset by -ksplit so that the same K offset applies.
-// Rows outside the operand are loaded from a readable row (the tile's first row)
-// and zeroed with a select: loads stay branch-free (see gemm_common.hpp).
+// Rows outside the operand (dok / sok false) load as zeros.
 struct MxOp {
   const uint8_t* d[4];
   const uint8_t* d_hi[4];
@@ -60,12 +59,10 @@ MOE_DEV void mx_load(const MxOp& o, long koff, uint4 (&r)[4], uint32_t (&sw)[2])
   const int ch = (threadIdx.x & 7) * 16;
 #pragma unroll
   for (int s = 0; s < 4; ++s)
-    r[s] = keep_if(o.dok[s], *(const uint4*)((hi ? o.d_hi[s] : o.d[s]) + koff + ch));
+    r[s] = o.dok[s] ? *(const uint4*)((hi ? o.d_hi[s] : o.d[s]) + koff + ch) : zero4();
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const uint32_t w = *(const uint32_t*)((hi ? o.sc_hi[q] : o.sc[q]) + koff / 32);
-    sw[q] = o.sok[q] ? w : 0u;
-  }
+  for (int q = 0; q < 2; ++q)
+    sw[q] = o.sok[q] ? *(const uint32_t*)((hi ? o.sc_hi[q] : o.sc[q]) + koff / 32) : 0u;
 }
 
 MOE_DEV void mx_store(char* t, const uint4 (&r)[4]) {
@@ -124,30 +121,39 @@ MOE_DEV void gemm_main_mx(char* lds, const MxOp& A, const MxOp& B, const KM& km,
   char* buf1 = lds + 2 * TILEB;
   uint4 ra0[4], rb0[4], ra1[4], rb1[4];
   uint32_t sa0[2], sb0[2], sa1[2], sb1[2], ca0[2], cb0[2], ca1[2], cb1[2];
-  const int last = nk - 1;
   mx_load(A, km(0), ra0, sa0);
   mx_load(B, km(0), rb0, sb0);
-  mx_load(A, km(min(1, last)), ra1, sa1);
-  mx_load(B, km(min(1, last)), rb1, sb1);
+  if (nk > 1) {
+    mx_load(A, km(1), ra1, sa1);
+    mx_load(B, km(1), rb1, sb1);
+  }
   mx_store(buf0, ra0);
   mx_store(buf0 + TILEB, rb0);
   ca0[0] = sa0[0]; ca0[1] = sa0[1]; cb0[0] = sb0[0]; cb0[1] = sb0[1];
   __syncthreads();
   for (int kt = 0; kt < nk; kt += 2) {
-    mx_load(A, km(min(kt + 2, last)), ra0, sa0);
-    mx_load(B, km(min(kt + 2, last)), rb0, sb0);
+    if (kt + 2 < nk) {
+      mx_load(A, km(kt + 2), ra0, sa0);
+      mx_load(B, km(kt + 2), rb0, sb0);
+    }
     mma_tile_mx(buf0, buf0 + TILEB, ca0, cb0, acc, arow, brow, lane);
-    mx_store(buf1, ra1);
-    mx_store(buf1 + TILEB, rb1);
-    ca1[0] = sa1[0]; ca1[1] = sa1[1]; cb1[0] = sb1[0]; cb1[1] = sb1[1];
+    if (kt + 1 < nk) {
+      mx_store(buf1, ra1);
+      mx_store(buf1 + TILEB, rb1);
+      ca1[0] = sa1[0]; ca1[1] = sa1[1]; cb1[0] = sb1[0]; cb1[1] = sb1[1];
+    }
     __syncthreads();
     if (kt + 1 >= nk) break;
-    mx_load(A, km(min(kt + 3, last)), ra1, sa1);
-    mx_load(B, km(min(kt + 3, last)), rb1, sb1);
+    if (kt + 3 < nk) {
+      mx_load(A, km(kt + 3), ra1, sa1);
+      mx_load(B, km(kt + 3), rb1, sb1);
+    }
     mma_tile_mx(buf1, buf1 + TILEB, ca1, cb1, acc, arow, brow, lane);
-    mx_store(buf0, ra0);
-    mx_store(buf0 + TILEB, rb0);
-    ca0[0] = sa0[0]; ca0[1] = sa0[1]; cb0[0] = sb0[0]; cb0[1] = sb0[1];
+    if (kt + 2 < nk) {
+      mx_store(buf0, ra0);
+      mx_store(buf0 + TILEB, rb0);
+      ca0[0] = sa0[0]; ca0[1] = sa0[1]; cb0[0] = sb0[0]; cb0[1] = sb0[1];
+    }
     __syncthreads();
   }
 }
