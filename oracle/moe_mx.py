@@ -125,8 +125,13 @@ def layer_forward_mx(x, logits, k, w_gate, w_up, w_down, shared=None, T_mb=0,
             "shared": shared, "qcache": qc, "w": (w_gate, w_up, w_down)}
 
 
-def layer_backward_mx(cache: dict, dy) -> dict:
-    """Backward of ``layer_forward_mx`` (selection held fixed)."""
+def layer_backward_mx(cache: dict, dy, keep_operands: bool = False) -> dict:
+    """Backward of ``layer_forward_mx`` (selection held fixed).  With
+    ``keep_operands`` the result also holds the quantised operands of the three
+    weight-gradient products, ``wgrad_operands[e][name]`` = list over minibatches
+    of (a, b) with dW[e] = sum a^T b (names dw_down: (dYu, g h), dw_gate: (dA, X),
+    dw_up: (dB, X)), from which a test bounds what one quantisation step of a
+    single product term can move an element."""
     dyf = _f64(dy)
     xf = cache["x"]
     T, H = xf.shape
@@ -139,6 +144,7 @@ def layer_backward_mx(cache: dict, dy) -> dict:
     dWd = [None] * E
     dx = np.zeros((T, H))
     dg = np.zeros((T, k))
+    operands = {}
     for mb in cache["minibatches"]:
         sl, plan = mb["slice"], mb["plan"]
         n_rows = int(plan["offsets"][E])
@@ -163,10 +169,13 @@ def layer_backward_mx(cache: dict, dy) -> dict:
             dB = dh * silu(A)
             dX[r0:r1] = q_rows(dA) @ qc.get("g_I", e) + q_rows(dB) @ qc.get("u_I", e)
             Xt = q_tokens(X_rows[r0:r1])
-            parts = (q_tokens(dY_rows[r0:r1]).T @ q_tokens(gr * h),
-                     q_tokens(dA).T @ Xt, q_tokens(dB).T @ Xt)
-            for store, p in zip((dWd, dWg, dWu), parts):
+            ops = ((q_tokens(dY_rows[r0:r1]), q_tokens(gr * h)),
+                   (q_tokens(dA), Xt), (q_tokens(dB), Xt))
+            for store, name, (a, b) in zip((dWd, dWg, dWu), ("dw_down", "dw_gate", "dw_up"), ops):
+                p = a.T @ b
                 store[e] = p if store[e] is None else store[e] + p
+                if keep_operands:
+                    operands.setdefault(e, {}).setdefault(name, []).append((a, b))
         P = plan["pos"]
         Tm = P.shape[0]
         for t in range(Tm):
@@ -180,6 +189,8 @@ def layer_backward_mx(cache: dict, dy) -> dict:
             dWu[e] = np.zeros(tuple(w_up[e].shape))
             dWd[e] = np.zeros(tuple(w_down[e].shape))
     out = {"dg": dg, "dw_gate": np.stack(dWg), "dw_up": np.stack(dWu), "dw_down": np.stack(dWd)}
+    if keep_operands:
+        out["wgrad_operands"] = operands
     if cache["shared"] is not None:
         Sg, Su, Sd = (_f64(a) for a in cache["shared"])
         As, Bs = xf @ Sg.T, xf @ Su.T
