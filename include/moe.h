@@ -66,7 +66,8 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2 } moe_dtype;
  * Limits: 0 <= T, T*k < 2^31, 1 <= E <= 1024, 1 <= k <= min(E, 32);
  * H, I and I_shared multiples of 128 for the expert GEMMs; the bf16 and fp32
  * layer calls take one minibatch (T_minibatch 0 or >= T), the MXFP8 calls at
- * most 8. */
+ * most 8.  The bf16 layer calls also need T*k*max(H, 2I, 2 I_shared)*2 bytes and
+ * I*H*2, I_shared*H*2 bytes below 4 GiB (MOE_E_UNSUPPORTED otherwise). */
 typedef struct {
   int32_t T, H, I, E, k;
   int32_t I_shared;
@@ -87,6 +88,9 @@ typedef struct {
  *   active    int32 [E]      ids of the experts with rows, ascending; n_active valid
  *   n_active  int32 [1]
  *   tile_first int32 [E+1]   index of each expert's first entry in `tiles`
+ *   wtiles    int32 [max_wtiles, 2]  the same list for wtile_m-row tiles (the
+ *                            wide-tile bf16 GEMMs); n_wtiles entries valid
+ *   n_wtiles  int32 [1]
  *   scratch   per-chunk histograms used while building the plan
  * With T_minibatch in (0, T) the tokens form n_minibatch = ceil(T / T_minibatch)
  * consecutive minibatches and the plan buffer holds one such table per minibatch
@@ -95,9 +99,10 @@ typedef struct {
  * one table and T_minibatch reads T. */
 typedef struct {
   size_t counts, offsets, src_token, src_slot, pos, tiles, n_tiles, err_flag, active, n_active,
-      tile_first, scratch;
+      tile_first, wtiles, n_wtiles, scratch;
   size_t sub_plan_bytes, total_bytes;
   int32_t tile_m, max_tiles, chunk_pairs, n_chunks, n_minibatch, T_minibatch;
+  int32_t wtile_m, max_wtiles;
 } moe_plan_layout;
 
 const char* moe_status_str(moe_status s);

@@ -38,10 +38,12 @@ class moe_shape(ctypes.Structure):
 class moe_plan_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("counts", "offsets", "src_token", "src_slot", "pos",
                                                 "tiles", "n_tiles", "err_flag", "active",
-                                                "n_active", "tile_first", "scratch",
+                                                "n_active", "tile_first", "wtiles",
+                                                "n_wtiles", "scratch",
                                                 "sub_plan_bytes", "total_bytes")] + \
                [(n, ctypes.c_int32) for n in ("tile_m", "max_tiles", "chunk_pairs", "n_chunks",
-                                              "n_minibatch", "T_minibatch")]
+                                              "n_minibatch", "T_minibatch", "wtile_m",
+                                              "max_wtiles")]
 
 
 _P = ctypes.c_void_p
@@ -358,4 +360,6 @@ def plan_views(s: moe_shape, plan: torch.Tensor, minibatch: int = 0) -> dict:
             "pos": view(L.pos, R).view(T, s.k), "tiles": view(L.tiles, 2 * L.max_tiles).view(-1, 2),
             "n_tiles": view(L.n_tiles, 1), "err_flag": view(L.err_flag, 1),
             "active": view(L.active, s.E), "n_active": view(L.n_active, 1),
-            "tile_first": view(L.tile_first, s.E + 1), "tile_m": L.tile_m, "T": T}
+            "tile_first": view(L.tile_first, s.E + 1), "tile_m": L.tile_m,
+            "wtiles": view(L.wtiles, 2 * L.max_wtiles).view(-1, 2),
+            "n_wtiles": view(L.n_wtiles, 1), "wtile_m": L.wtile_m, "T": T}

@@ -51,6 +51,16 @@ struct Carve {
   }
 };
 
+// The bf16 GEMMs address activation rows and one expert's weights with 32-bit
+// byte offsets from a base: every such operand must be smaller than 4 GiB.
+bool bf16_offsets_fit(const moe_shape* s) {
+  const uint64_t R = (uint64_t)s->T * s->k;
+  const uint64_t w = std::max<uint64_t>({(uint64_t)s->H, 2ull * s->I, 2ull * s->I_shared});
+  const uint64_t lim = 1ull << 32;
+  return R * w * 2 < lim && (uint64_t)s->I * s->H * 2 < lim &&
+         (uint64_t)s->I_shared * s->H * 2 < lim;
+}
+
 moe_status check_shape(const moe_shape* s, bool need_gemm_dims) {
   if (!s) return MOE_E_NULL;
   if (s->T < 0 || s->E < 1 || s->E > MOE_MAX_E || s->k < 1 || s->k > s->E || s->k > MOE_MAX_K)
@@ -80,6 +90,8 @@ moe_plan_layout plan_layout(const moe_shape* s) {
   const int64_t R = (int64_t)minibatch_tokens(s) * s->k;
   L.tile_m = GEMM_TILE_M;
   L.max_tiles = (int32_t)(R / GEMM_TILE_M + (R < s->E ? R : s->E) + 1);
+  L.wtile_m = GEMM_WTILE_M;
+  L.max_wtiles = (int32_t)(R / GEMM_WTILE_M + (R < s->E ? R : s->E) + 1);
   L.chunk_pairs = PLAN_CHUNK;
   L.n_chunks = (int32_t)((R + PLAN_CHUNK - 1) / PLAN_CHUNK);
   Carve c;
@@ -94,6 +106,8 @@ moe_plan_layout plan_layout(const moe_shape* s) {
   L.active = c.take(sizeof(int32_t) * s->E);
   L.n_active = c.take(sizeof(int32_t));
   L.tile_first = c.take(sizeof(int32_t) * (s->E + 1));
+  L.wtiles = c.take(sizeof(int32_t) * 2 * (size_t)L.max_wtiles);
+  L.n_wtiles = c.take(sizeof(int32_t));
   L.scratch = c.take(sizeof(int32_t) * ((size_t)L.n_chunks * s->E + L.n_chunks));
   L.sub_plan_bytes = c.off;
   L.n_minibatch = n_minibatches(s);
@@ -113,8 +127,8 @@ const P* at(const void* base, size_t off) {
 
 struct PlanView {
   const int32_t *counts, *offsets, *src_token, *src_slot, *pos, *tiles, *n_tiles, *active,
-      *n_active, *tile_first;
-  int max_tiles;
+      *n_active, *tile_first, *wtiles, *n_wtiles;
+  int max_tiles, max_wtiles;
 };
 
 // View of minibatch m's plan.
@@ -132,7 +146,10 @@ PlanView view_plan(const moe_shape* s, const void* plan_all, int m = 0) {
   v.active = at<int32_t>(plan, L.active);
   v.n_active = at<int32_t>(plan, L.n_active);
   v.tile_first = at<int32_t>(plan, L.tile_first);
+  v.wtiles = at<int32_t>(plan, L.wtiles);
+  v.n_wtiles = at<int32_t>(plan, L.n_wtiles);
   v.max_tiles = L.max_tiles;
+  v.max_wtiles = L.max_wtiles;
   return v;
 }
 
@@ -146,7 +163,10 @@ GroupInfo grouped(const moe_shape* s, const PlanView& v) {
   g.active = v.active;
   g.n_active = v.n_active;
   g.counts = v.counts;
+  g.wtiles = v.wtiles;
+  g.n_wtiles = v.n_wtiles;
   g.max_tiles = v.max_tiles;
+  g.max_wtiles = v.max_wtiles;
   g.dense_rows = 0;
   g.E = s->E;
   return g;
@@ -246,6 +266,7 @@ moe_status forward_impl(moe_dtype dt, const moe_shape* s, const void* plan, cons
   moe_status rc = check_shape(s, true);
   if (rc != MOE_OK) return rc;
   if (n_minibatches(s) != 1) return MOE_E_UNSUPPORTED;
+  if (dt == MOE_BF16 && !bf16_offsets_fit(s)) return MOE_E_UNSUPPORTED;
   if (any_null({plan, wg, wu, wd}) || any_null_rows(s, {x, topk_w, y, saved, ws}))
     return MOE_E_NULL;
   if (s->I_shared && any_null({sg, su, sd})) return MOE_E_NULL;
@@ -288,6 +309,7 @@ moe_status backward_impl(moe_dtype dt, const moe_shape* s, const void* plan, con
   moe_status rc = check_shape(s, true);
   if (rc != MOE_OK) return rc;
   if (n_minibatches(s) != 1) return MOE_E_UNSUPPORTED;
+  if (dt == MOE_BF16 && !bf16_offsets_fit(s)) return MOE_E_UNSUPPORTED;
   if (any_null({plan, wg, wu, wd, dwg, dwu, dwd}) ||
       any_null_rows(s, {x, topk_w, saved, dy, dx, d_topk_w, ws}))
     return MOE_E_NULL;
@@ -360,6 +382,8 @@ moe_status plan_one(const moe_shape* s, const moe_plan_layout& L, int T_m,
   p.active = at<int32_t>(plan, L.active);
   p.n_active = at<int32_t>(plan, L.n_active);
   p.tile_first = at<int32_t>(plan, L.tile_first);
+  p.wtiles = at<int32_t>(plan, L.wtiles);
+  p.n_wtiles = at<int32_t>(plan, L.n_wtiles);
   p.chunk_hist = at<int32_t>(plan, L.scratch);
   p.chunk_invalid = p.chunk_hist + (size_t)L.n_chunks * s->E;
   p.n_chunks = (int)(((int64_t)T_m * s->k + PLAN_CHUNK - 1) / PLAN_CHUNK);

@@ -350,11 +350,12 @@ static hipError_t wgrad_up_t(const GroupInfo& g, const void* dZ, const void* x, 
 
 hipError_t launch_gemm_up_swiglu(int dt, const GroupInfo& g, const void* x, const void* wg,
                                  const void* wu, int H, int I, void* Z, void* h, hipStream_t s) {
-  return dt ? up_swiglu_t<bf16_t>(g, x, wg, wu, H, I, Z, h, s)
+  return dt ? launch_big_up_swiglu(g, x, wg, wu, H, I, Z, h, s)
             : up_swiglu_t<float>(g, x, wg, wu, H, I, Z, h, s);
 }
 hipError_t launch_gemm_down(int dt, const GroupInfo& g, const void* h, const void* wd, int H,
                             int I, void* Y, hipStream_t s) {
+  if (dt && !g.tiles) return launch_big_down(g, h, wd, H, I, Y, s);
   return dt ? down_t<bf16_t>(g, h, wd, H, I, Y, s) : down_t<float>(g, h, wd, H, I, Y, s);
 }
 hipError_t launch_gemm_dgrad_down(int dt, const GroupInfo& g, const void* dy, const void* wd,
@@ -365,7 +366,7 @@ hipError_t launch_gemm_dgrad_down(int dt, const GroupInfo& g, const void* dy, co
 }
 hipError_t launch_gemm_dgrad_up(int dt, const GroupInfo& g, const void* dZ, const void* wg,
                                 const void* wu, int H, int I, void* dX, hipStream_t s) {
-  return dt ? dgrad_up_t<bf16_t>(g, dZ, wg, wu, H, I, dX, s)
+  return dt ? launch_big_dgrad_up(g, dZ, wg, wu, H, I, dX, s)
             : dgrad_up_t<float>(g, dZ, wg, wu, H, I, dX, s);
 }
 hipError_t launch_gemm_wgrad_down(int dt, const GroupInfo& g, const void* dy, const void* gh,

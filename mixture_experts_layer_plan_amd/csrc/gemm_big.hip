@@ -1,0 +1,496 @@
+// Large-tile bf16 grouped GEMMs for gfx950 (MI355X): GEMM1 + SwiGLU, GEMM2 of the
+// dense shared expert, and dgrad-up, with their epilogues fused.
+//
+// The experts are SwiGLU feed-forward nets run as grouped GEMMs over all experts
+// at once (sebask.de, "Mixture-of-Kittens: Cursors Open-Source-Ansatz für
+// effizientes MoE-Training auf NVL72", introduction; stamatios.com, "Cursor abre
+// código de megakernel MoE para GPUs NVL72", § Outras características).
+//
+// Core (chosen from measurements on MI355X): one workgroup of eight wavefronts
+// (two per SIMD) computes a 256 x 256 output tile; wavefront (wm, wn) owns rows
+// 128 wm .. +127 and columns 64 wn .. +63 as 4 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16.  Both operands travel global -> LDS by the gfx950
+// direct-to-LDS load (global_load_lds_dwordx4: each lane's 16 bytes land at the
+// wavefront's LDS base + 16 * lane), so no registers stage them; two LDS stages of
+// 64 KiB each: the next K tile (64 deep) streams in while the current one is
+// multiplied.  MFMA fragments are read one 16-deep step ahead, and the tile
+// barrier sits before the last step's MFMAs so that the next tile's first
+// fragments load underneath them.  Against a 128 x 128 tile with register-staged
+// loads this halves LDS traffic per flop (32 flops per LDS byte) and frees the
+// registers that made the loop wait on every fragment read.  (The K-grouped
+// wgrads and dgrad-down stay on the 128 x 128 kernels of gemm.hip: with one
+// workgroup per CU their write-heavy epilogues no longer overlap other tiles'
+// loads, and they measured slower.)
+//
+// Operand layouts in LDS (one stage = 32 KiB per operand):
+//  * K-major (rows of K-contiguous data: tokens, and the weights of the forward
+//    GEMMs): 256 rows x 128 bytes, 16-byte chunks XOR-swizzled by row; fragments
+//    by 16-byte reads.
+//  * MN-major (K is the outer dimension: the weights of dgrad-up): 64 K rows x
+//    512 bytes as stored in memory, 16-byte chunks XOR-swizzled by K row;
+//    fragments by the gfx950 transposing LDS read ds_read_b64_tr_b16 (within each
+//    16-lane group, lane 4a + b receives element b of the 8-byte rows addressed by
+//    lanes a, a + 4, a + 8, a + 12), two reads per fragment.  No register
+//    transpose, no bank conflicts.
+//
+// Grouping: the kernels walk the plan's 256-row tile list (expert, first row); a
+// wavefront skips the MFMAs of 32-row blocks that lie past the expert's rows and
+// the token loads skip whole 64-row groups past them, so a tile of a small expert
+// costs what its rows need and is bound by its weight reads.  Every output element
+// is produced by one workgroup with a fixed K order: bitwise reproducible and
+// independent of the grid.
+#include "gemm_common.hpp"
+
+namespace moe {
+namespace big {
+
+constexpr int TILE = 256;
+constexpr int NTH = 512;
+constexpr int STAGE = 32768;     // one operand, one 64-deep K tile
+constexpr int LDS = 4 * STAGE;   // two stages of (A, B)
+
+typedef __attribute__((address_space(3))) void* lds_vptr;
+typedef const __attribute__((address_space(1))) void* gbl_vptr;
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+
+MOE_DEV void dma16(const char* src, char* dst) {
+  __builtin_amdgcn_global_load_lds((gbl_vptr)src, (lds_vptr)dst, 16, 0, 0);
+}
+
+MOE_DEV int wave() { return threadIdx.x >> 6; }
+MOE_DEV int lane() { return threadIdx.x & 63; }
+
+// Addresses are a wave-uniform base plus a 32-bit per-lane offset (and uniform
+// strides), so the loads use the scalar-base addressing form and few registers.
+
+// ------------------------------------------------------------ K-major operand
+// Instruction s (0..3) of wavefront w fills stage rows 64 s + 8 w .. +7: lane L
+// brings row kmaj_row(s) = 64 s + 8 w + L / 8 into physical chunk L % 8, i.e. its
+// logical chunk (L % 8) ^ swizzle(row) (the swizzle of gemm_common.hpp; it depends
+// on row % 64 only, so it is the same for the four instructions).
+MOE_DEV int kmaj_row(int s) { return 64 * s + 8 * wave() + (lane() >> 3); }
+MOE_DEV int kmaj_chunk() {
+  const int r = kmaj_row(0);
+  return (threadIdx.x & 7) ^ ((r ^ (r >> 3)) & 7);
+}
+MOE_DEV char* kmaj_dst(char* st, int s) { return st + (8 * s + wave()) * 1024; }
+
+// Rows gathered one by one (tokens through the plan's pull list).  Instructions
+// whose 64 rows all lie past the tile's `rows` are not issued: those LDS rows keep
+// stale data and feed only output rows that are neither multiplied (blocks_a) nor
+// stored.
+struct DmaKG {
+  const char* base;
+  uint32_t off[4];  // byte offset of this lane's row for instruction s, chunk included
+  int n;            // instructions issued
+  MOE_DEV void set(const bf16_t* b, int rows) {
+    base = (const char*)b;
+    n = (rows + 63) / 64;
+  }
+  MOE_DEV void row(int s, size_t row_elem_offset) {
+    off[s] = (uint32_t)(row_elem_offset * 2) + 16u * kmaj_chunk();
+  }
+  MOE_DEV void issue(int kt, char* st) const {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      if (s < n) dma16(base + (size_t)kt * 128 + off[s], kmaj_dst(st, s));
+  }
+};
+
+// Rows at a fixed stride (weights): row r at base + r * ld; rows past `rows` read
+// row 0 (only whole 64-row groups can lie past the operand, as rows % 64 == 0).
+struct DmaKS {
+  const char* base;
+  uint32_t off;   // this lane's offset for instruction 0
+  uint32_t step;  // 64 rows, bytes
+  int valid;      // instructions 0 .. valid-1 read their own rows
+  MOE_DEV void set(const bf16_t* b, size_t ld_elems, int rows) {
+    base = (const char*)b;
+    off = (uint32_t)(kmaj_row(0) * ld_elems * 2) + 16u * kmaj_chunk();
+    step = (uint32_t)(64 * ld_elems * 2);
+    valid = (rows + 63) / 64;
+  }
+  MOE_DEV void issue(int kt, char* st) const {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      dma16(base + (size_t)kt * 128 + off + (s < valid ? s * step : 0u), kmaj_dst(st, s));
+  }
+};
+
+MOE_DEV bf16x8_t frag_k(const char* st, int r0, int ks) {
+  return *(const bf16x8_t*)(st + swz(r0 + (lane() & 31), 2 * ks + (lane() >> 5)));
+}
+
+// ----------------------------------------------------------- MN-major operand
+// Stage: 64 K rows x 256 columns; chunk c of K row k at k * 512 + 16 (c ^ mnswz(k)).
+// The swizzle spreads the eight K rows x four chunks that one transposing read
+// touches over distinct banks.
+MOE_DEV int mnswz(int k) { return ((k & 3) << 2) | ((k >> 3) & 1); }
+// Instruction s of wavefront w fills K rows 16 s + 2 w and +1: lane L brings K row
+// mn_row(s) = 16 s + 2 w + L / 32 into physical chunk L % 32 (the swizzle depends on
+// k % 16 only: the same logical chunk for the four instructions).
+MOE_DEV int mn_row(int s) { return 16 * s + 2 * wave() + (lane() >> 5); }
+MOE_DEV char* mn_dst(char* st, int s) { return st + (8 * s + wave()) * 1024; }
+
+struct DmaMN {
+  const char* base;  // element (K row 0, column 0) of this tile
+  uint32_t off;      // this lane's offset for instruction 0
+  uint32_t sstep;    // 16 K rows, bytes
+  long kstep;        // 64 K rows, bytes
+  // ncols valid columns (>= 8); columns past them read chunk 0 (never stored)
+  MOE_DEV void set(const bf16_t* b, size_t ld_elems, int ncols) {
+    base = (const char*)b;
+    int c = (lane() & 31) ^ mnswz(mn_row(0));
+    if (8 * c >= ncols) c = 0;
+    off = (uint32_t)(mn_row(0) * ld_elems * 2) + 16u * c;
+    sstep = (uint32_t)(16 * ld_elems * 2);
+    kstep = (long)(64 * ld_elems * 2);
+  }
+  MOE_DEV void issue(int kt, char* st) const {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dma16(base + kt * kstep + off + s * sstep, mn_dst(st, s));
+  }
+};
+
+// Fragment of columns c0 .. c0 + 31 (c0 a multiple of 32) at K step ks: lane l gets
+// column c0 + (l & 31), K values 16 ks + 8 (l >> 5) + 0..7 (the MFMA operand
+// layout).  Lane l = 16 g + 4 a + j' addresses K row 16 ks + 8 (g >> 1) + j' (and
+// +4 for the second read), columns c0 + 16 (g & 1) + 4 a .. +3.  The swizzle of
+// those rows does not depend on ks, and the column chunk splits into the block's
+// part (c0 / 8, a multiple of 4) and the lane's (2 (g & 1) + a / 2 < 4), so the
+// address is a lane constant plus 16 * ((c0 / 8) ^ (swizzle & 12)) plus immediates.
+MOE_DEV int mn_lane_ofs() {
+  const int l = lane(), g = l >> 4, a = l & 3, j = (l >> 2) & 3;
+  const int k = 8 * (g >> 1) + j;
+  const int sw = mnswz(k);
+  return k * 512 + (((2 * (g & 1) + (a >> 1)) ^ (sw & 3)) << 4) + (a & 1) * 8;
+}
+MOE_DEV int mn_blk_ofs(int c0) {
+  const int l = lane(), g = l >> 4, j = (l >> 2) & 3;
+  const int sw = mnswz(8 * (g >> 1) + j);
+  return (((c0 >> 3) ^ (sw & 12)) << 4);
+}
+MOE_DEV bf16x8_t frag_mn(const char* st, int c0, int ks) {
+  const char* p = st + mn_lane_ofs() + mn_blk_ofs(c0) + ks * 16 * 512;
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p + 4 * 512));
+  const s16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// ------------------------------------------------------------------ main loop
+// A: blocks i = 0..3 at rows 128 wm + 32 i; B: blocks j = 0..1 at columns
+// 64 wn + 32 j.  ma / mb: number of leading blocks with any valid row / column
+// (wave-uniform); the others are not multiplied.
+struct Acc {
+  f32x16_t c[4][2];
+};
+
+// Operand adaptors: issue(kt, stage) and frag(stage, block, ks, kt).
+struct OpKG {  // K-major gathered rows
+  DmaKG d;
+  MOE_DEV void issue(int kt, char* st) const { d.issue(kt, st); }
+  MOE_DEV bf16x8_t frag(const char* st, int r0, int ks, int) const { return frag_k(st, r0, ks); }
+};
+struct OpK {  // K-major strided rows
+  DmaKS d;
+  MOE_DEV void issue(int kt, char* st) const { d.issue(kt, st); }
+  MOE_DEV bf16x8_t frag(const char* st, int r0, int ks, int) const { return frag_k(st, r0, ks); }
+};
+// GEMM1 weights: B-tile row 64 s + m (instruction s) is W_g (m < 32) or W_u
+// (m >= 32) row 32 s + (m & 31) of this column tile.
+struct OpUpW {
+  const char* g;
+  const char* u;
+  uint32_t off;   // row (m & 31) + chunk, for instruction 0
+  uint32_t step;  // 32 rows, bytes
+  bool up;        // this lane's m >= 32
+  MOE_DEV void set(const bf16_t* wg_tile, const bf16_t* wu_tile, int H) {
+    const int m = kmaj_row(0);  // 0..63
+    g = (const char*)wg_tile;
+    u = (const char*)wu_tile;
+    up = m >= 32;
+    off = (uint32_t)((m & 31) * H * 2) + 16u * kmaj_chunk();
+    step = (uint32_t)(32 * H * 2);
+  }
+  MOE_DEV void issue(int kt, char* st) const {
+    const char* b = up ? u : g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dma16(b + (size_t)kt * 128 + off + s * step, kmaj_dst(st, s));
+  }
+  MOE_DEV bf16x8_t frag(const char* st, int r0, int ks, int) const { return frag_k(st, r0, ks); }
+};
+struct OpMN {  // MN-major, full K tiles
+  DmaMN d;
+  MOE_DEV void issue(int kt, char* st) const { d.issue(kt, st); }
+  MOE_DEV bf16x8_t frag(const char* st, int c0, int ks, int) const { return frag_mn(st, c0, ks); }
+};
+struct OpMNCat {  // dgrad-up weights: K rows < I from W_g[e], the rest from W_u[e]
+  DmaMN g, u;
+  int kI;  // K tiles in W_g
+  MOE_DEV void issue(int kt, char* st) const {
+    if (kt < kI) g.issue(kt, st);
+    else u.issue(kt - kI, st);
+  }
+  MOE_DEV bf16x8_t frag(const char* st, int c0, int ks, int) const { return frag_mn(st, c0, ks); }
+};
+
+template <class OA, class OB>
+MOE_DEV void load_frags(const OA& A, const OB& B, const char* st, int kt, int ks, int wm, int wn,
+                        int ma, int mb, bf16x8_t (&a)[4], bf16x8_t (&b)[2]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i < ma) a[i] = A.frag(st, 128 * wm + 32 * i, ks, kt);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    if (j < mb) b[j] = B.frag(st + STAGE, 64 * wn + 32 * j, ks, kt);
+}
+
+MOE_DEV void mma(Acc& acc, const bf16x8_t (&a)[4], const bf16x8_t (&b)[2], int ma, int mb) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (i < ma && j < mb)
+        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc.c[i][j], 0, 0, 0);
+}
+
+template <class OA, class OB>
+MOE_DEV void main_loop(char* lds, const OA& A, const OB& B, int nk, int ma, int mb, Acc& acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc.c[i][j][v] = 0.0f;
+  if (nk <= 0) return;
+  const int wm = wave() >> 2, wn = wave() & 3;
+  A.issue(0, lds);
+  B.issue(0, lds + STAGE);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  bf16x8_t a0[4], b0[2], a1[4], b1[2];
+  load_frags(A, B, lds, 0, 0, wm, wn, ma, mb, a0, b0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const char* cur = lds + (kt & 1) * 2 * STAGE;
+    char* nxt = lds + ((kt + 1) & 1) * 2 * STAGE;
+    // the last iteration reloads its own K tile into the idle stage (never read)
+    const int kn = kt + 1 < nk ? kt + 1 : kt;
+    A.issue(kn, nxt);
+    B.issue(kn, nxt + STAGE);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(A, B, cur, kt, 1, wm, wn, ma, mb, a1, b1);
+    mma(acc, a0, b0, ma, mb);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(A, B, cur, kt, 2, wm, wn, ma, mb, a0, b0);
+    mma(acc, a1, b1, ma, mb);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(A, B, cur, kt, 3, wm, wn, ma, mb, a1, b1);
+    mma(acc, a0, b0, ma, mb);
+    __builtin_amdgcn_sched_barrier(0);
+    // this wavefront's reads of `cur` and its loads into `nxt` are complete; after
+    // the barrier every wavefront's are: `nxt` is readable, `cur` reusable
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(A, B, nxt, kt + 1, 0, wm, wn, ma, mb, a0, b0);
+    mma(acc, a1, b1, ma, mb);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // LDS free for an epilogue
+}
+
+// Output position of register v of block (i, j): row 128 wm + 32 i + 8 (v >> 2) +
+// 4 (l >> 5) + (v & 3), column 64 wn + 32 j + (l & 31).
+MOE_DEV int out_row(int i, int v) {
+  return 128 * (wave() >> 2) + 32 * i + 8 * (v >> 2) + 4 * (lane() >> 5) + (v & 3);
+}
+MOE_DEV int out_col(int j) { return 64 * (wave() & 3) + 32 * j + (lane() & 31); }
+
+// Leading A blocks of this wavefront with a row below `rows`, B blocks with a
+// column below `cols`.
+MOE_DEV int blocks_a(int rows) { return min(4, max(0, (rows - 128 * (wave() >> 2) + 31) / 32)); }
+MOE_DEV int blocks_b(int cols) { return min(2, max(0, (cols - 64 * (wave() & 3) + 31) / 32)); }
+
+// ------------------------------------------------------------ tile decode
+struct Tile {
+  int e, row0, row_end;
+};
+
+// Rows-grouped launches: a 1-D grid over (256-row tile, column tile) pairs,
+// renumbered so that the workgroups of one XCD (ids x, x + 8, ...) take a
+// contiguous run of pairs, column tile fastest (as in gemm_common.hpp).
+MOE_DEV bool row_tile(const GroupInfo& g, int nt_count, Tile& t, int& nt) {
+  const int n_row_tiles = g.wtiles ? g.n_wtiles[0] : (g.dense_rows + TILE - 1) / TILE;
+  const int total = n_row_tiles * nt_count;
+  const int id = blockIdx.x;
+  if (id >= total) return false;
+  const int per = total / N_XCD, rem = total % N_XCD, x = id % N_XCD, local = id / N_XCD;
+  const int L = x < rem ? x * (per + 1) + local : rem * (per + 1) + (x - rem) * per + local;
+  const int mt = L / nt_count;
+  nt = L - mt * nt_count;
+  if (g.wtiles) {
+    t.e = g.wtiles[2 * mt];
+    t.row0 = g.wtiles[2 * mt + 1];
+    t.row_end = min(t.row0 + TILE, g.offsets[t.e + 1]);
+  } else {
+    t.e = 0;
+    t.row0 = mt * TILE;
+    t.row_end = min(t.row0 + TILE, g.dense_rows);
+  }
+  return true;
+}
+
+MOE_DEV int row_of_tile(const Tile& t, int r) {  // clamp rows past the tile's end
+  return t.row0 + r < t.row_end ? t.row0 + r : t.row0;
+}
+
+// ---------------------------------------------------------------- kernels
+// GEMM1 + SwiGLU.  Column tile nt covers i in [128 nt, 128 nt + 128): B-tile rows
+// 64 wn + rr (rr < 32) are W_g[e] row 128 nt + 32 wn + rr and rows 64 wn + 32 + rr
+// the W_u[e] row of the same i, so gate and up of one (row, i) are the same
+// register of blocks 0 and 1 of one lane and the SwiGLU is formed in registers.
+// Z (fp32) keeps the pre-activations for the backward; h = silu(A) B rounds once.
+__global__ __launch_bounds__(NTH, 1) void k_up_swiglu(GroupInfo g, const bf16_t* __restrict__ x,
+                                                      const bf16_t* __restrict__ wg,
+                                                      const bf16_t* __restrict__ wu, int H, int I,
+                                                      float* __restrict__ Z,
+                                                      bf16_t* __restrict__ hout) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS];
+  Tile t;
+  int nt;
+  if (!row_tile(g, I / 128, t, nt)) return;
+  const size_t wofs = (size_t)t.e * I * H;
+  OpKG A;
+  OpUpW B;
+  A.d.set(x, t.row_end - t.row0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int r = row_of_tile(t, kmaj_row(s));
+    A.d.row(s, (size_t)(g.src_token ? g.src_token[r] : r) * H);
+  }
+  B.set(wg + wofs + (size_t)128 * nt * H, wu + wofs + (size_t)128 * nt * H, H);
+  Acc acc;
+  main_loop(lds, A, B, H / 64, blocks_a(t.row_end - t.row0), 2, acc);
+  const int i = 128 * nt + 32 * (wave() & 3) + (lane() & 31);
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = t.row0 + out_row(bi, v);
+      if (r < t.row_end) {
+        const float a = acc.c[bi][0][v], b = acc.c[bi][1][v];
+        float* zr = Z + (size_t)r * (2 * I);
+        zr[i] = a;
+        zr[I + i] = b;
+        hout[(size_t)r * I + i] = f32_to_bf16(silu_f(a) * b);
+      }
+    }
+}
+
+// GEMM2: Y[r, n] = sum_i h[r, i] W_d[e][n, i]
+__global__ __launch_bounds__(NTH, 1) void k_down(GroupInfo g, const bf16_t* __restrict__ h,
+                                                 const bf16_t* __restrict__ wd, int H, int I,
+                                                 bf16_t* __restrict__ Y) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS];
+  Tile t;
+  int nt;
+  if (!row_tile(g, (H + TILE - 1) / TILE, t, nt)) return;
+  const int n0 = nt * TILE;
+  OpKG A;
+  OpK B;
+  A.d.set(h, t.row_end - t.row0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) A.d.row(s, (size_t)row_of_tile(t, kmaj_row(s)) * I);
+  B.d.set(wd + (size_t)t.e * H * I + (size_t)n0 * I, (size_t)I, H - n0);
+  Acc acc;
+  main_loop(lds, A, B, I / 64, blocks_a(t.row_end - t.row0), blocks_b(H - n0), acc);
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) {
+      const int n = n0 + out_col(bj);
+      if (n < H)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = t.row0 + out_row(bi, v);
+          if (r < t.row_end) Y[(size_t)r * H + n] = f32_to_bf16(acc.c[bi][bj][v]);
+        }
+    }
+}
+
+// dgrad-up: dX[r, n] = sum_{k < 2I} dZ[r, k] Wcat[k, n], Wcat = [W_g[e]; W_u[e]]
+__global__ __launch_bounds__(NTH, 1) void k_dgrad_up(GroupInfo g, const bf16_t* __restrict__ dZ,
+                                                     const bf16_t* __restrict__ wg,
+                                                     const bf16_t* __restrict__ wu, int H, int I,
+                                                     bf16_t* __restrict__ dX) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS];
+  Tile t;
+  int nt;
+  if (!row_tile(g, (H + TILE - 1) / TILE, t, nt)) return;
+  const int n0 = nt * TILE, ncols = min(TILE, H - n0);
+  const size_t wofs = (size_t)t.e * I * H + n0;
+  OpKG A;
+  OpMNCat B;
+  A.d.set(dZ, t.row_end - t.row0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) A.d.row(s, (size_t)row_of_tile(t, kmaj_row(s)) * (2 * I));
+  B.g.set(wg + wofs, (size_t)H, ncols);
+  B.u.set(wu + wofs, (size_t)H, ncols);
+  B.kI = I / 64;
+  Acc acc;
+  main_loop(lds, A, B, (2 * I) / 64, blocks_a(t.row_end - t.row0), blocks_b(ncols), acc);
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) {
+      const int n = n0 + out_col(bj);
+      if (n < H)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = t.row0 + out_row(bi, v);
+          if (r < t.row_end) dX[(size_t)r * H + n] = f32_to_bf16(acc.c[bi][bj][v]);
+        }
+    }
+}
+
+}  // namespace big
+
+// ------------------------------------------------------------------ launchers
+static unsigned big_row_tiles(const GroupInfo& g) {
+  return g.wtiles ? (unsigned)g.max_wtiles
+                  : (unsigned)((g.dense_rows + big::TILE - 1) / big::TILE);
+}
+
+hipError_t launch_big_up_swiglu(const GroupInfo& g, const void* x, const void* wg, const void* wu,
+                                int H, int I, void* Z, void* h, hipStream_t s) {
+  const unsigned ty = big_row_tiles(g);
+  if (ty == 0) return hipSuccess;
+  return MOE_LAUNCH(g.wtiles ? "gemm_up_swiglu" : "gemm_up_swiglu_shared", s,
+                    big::k_up_swiglu<<<ty * (I / 128), big::NTH, 0, s>>>(
+                        g, (const bf16_t*)x, (const bf16_t*)wg, (const bf16_t*)wu, H, I,
+                        (float*)Z, (bf16_t*)h));
+}
+
+hipError_t launch_big_down(const GroupInfo& g, const void* h, const void* wd, int H, int I,
+                           void* Y, hipStream_t s) {
+  const unsigned ty = big_row_tiles(g);
+  if (ty == 0) return hipSuccess;
+  return MOE_LAUNCH(g.wtiles ? "gemm_down" : "gemm_down_shared", s,
+                    big::k_down<<<ty * ((H + big::TILE - 1) / big::TILE), big::NTH, 0, s>>>(
+                        g, (const bf16_t*)h, (const bf16_t*)wd, H, I, (bf16_t*)Y));
+}
+
+hipError_t launch_big_dgrad_up(const GroupInfo& g, const void* dZ, const void* wg, const void* wu,
+                               int H, int I, void* dX, hipStream_t s) {
+  const unsigned ty = big_row_tiles(g);
+  if (ty == 0) return hipSuccess;
+  return MOE_LAUNCH(g.wtiles ? "gemm_dgrad_up" : "gemm_dgrad_up_shared", s,
+                    big::k_dgrad_up<<<ty * ((H + big::TILE - 1) / big::TILE), big::NTH, 0, s>>>(
+                        g, (const bf16_t*)dZ, (const bf16_t*)wg, (const bf16_t*)wu, H, I,
+                        (bf16_t*)dX));
+}
+
+}  // namespace moe

@@ -25,6 +25,7 @@ void trace_after(hipStream_t s);
 // plan construction
 constexpr int PLAN_CHUNK = 512;      // pairs per wavefront chunk
 constexpr int GEMM_TILE_M = 128;     // rows per grouped-GEMM tile (plan tile list)
+constexpr int GEMM_WTILE_M = 256;    // rows per wide tile (second plan tile list)
 
 // router
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* w,
@@ -49,6 +50,8 @@ struct PlanPtrs {
   int32_t* active;         // [E] experts with rows, ascending
   int32_t* n_active;
   int32_t* tile_first;     // [E + 1] first tile of each expert in the tile list
+  int32_t* wtiles;         // wide-tile list and its length
+  int32_t* n_wtiles;
   int32_t* chunk_hist;     // [n_chunks, E]
   int32_t* chunk_invalid;  // [n_chunks]
   int n_chunks;
@@ -81,10 +84,21 @@ struct GroupInfo {
   const int32_t* active;     // K-grouped: experts with rows (NULL: dense)
   const int32_t* n_active;
   const int32_t* counts;     // rows per expert (zero-fill of empty experts)
+  const int32_t* wtiles;     // rows-grouped, wide kernels: 256-row tile list
+  const int32_t* n_wtiles;
   int max_tiles;             // grid bound for rows-grouped launches
+  int max_wtiles;
   int dense_rows;            // row count in dense mode
   int E;
 };
+
+// bf16 large-tile kernels (gemm_big.hip) behind the launch_gemm_* entry points
+hipError_t launch_big_up_swiglu(const GroupInfo& g, const void* x, const void* wg, const void* wu,
+                                int H, int I, void* Z, void* h, hipStream_t s);
+hipError_t launch_big_down(const GroupInfo& g, const void* h, const void* wd, int H, int I,
+                           void* Y, hipStream_t s);
+hipError_t launch_big_dgrad_up(const GroupInfo& g, const void* dZ, const void* wg, const void* wu,
+                               int H, int I, void* dX, hipStream_t s);
 
 // GEMM1 + SwiGLU: Z (fp32) [:, i] = A, Z[:, I + i] = B, h = silu(A) * B, with
 // A = X W_g[e]^T, B = X W_u[e]^T and X rows gathered from x through src_token.

@@ -168,7 +168,6 @@ hipError_t launch_dg_reduce(const float* dgp, const int32_t* pos, int R, int n_p
 
 namespace moe {
 
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 struct ZeroBufs {
   u32x4_t* p[3];

@@ -85,9 +85,10 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
     int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles, int32_t* __restrict__ err_flag,
     int32_t* __restrict__ src_token, int32_t* __restrict__ src_slot,
     int32_t* __restrict__ active, int32_t* __restrict__ n_active,
-    int32_t* __restrict__ tile_first) {
+    int32_t* __restrict__ tile_first, int wtile_m, int32_t* __restrict__ wtiles,
+    int32_t* __restrict__ n_wtiles) {
   __shared__ int32_t s_rows[1];
-  __shared__ int32_t s_wave[3][16];
+  __shared__ int32_t s_wave[4][16];
   __shared__ int32_t s_bad;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   if (tid == 0) s_bad = 0;
@@ -95,19 +96,24 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
   if (tid < E)
     for (int c = 0; c < n_chunks; ++c) n += hist[(size_t)c * E + tid];
   const int nt = (n + tile_m - 1) / tile_m;
+  const int nw = (n + wtile_m - 1) / wtile_m;
   const int act = n > 0 ? 1 : 0;
   // inclusive scans inside each wavefront (Hillis-Steele over shuffles)
-  int a = n, b = nt, c3 = act;
+  int a = n, b = nt, c3 = act, d = nw;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int ua = __shfl_up(a, o, 64), ub = __shfl_up(b, o, 64), uc = __shfl_up(c3, o, 64);
-    if (lane >= o) { a += ua; b += ub; c3 += uc; }
+    const int ud = __shfl_up(d, o, 64);
+    if (lane >= o) { a += ua; b += ub; c3 += uc; d += ud; }
   }
-  if (lane == 63) { s_wave[0][wv] = a; s_wave[1][wv] = b; s_wave[2][wv] = c3; }
+  if (lane == 63) { s_wave[0][wv] = a; s_wave[1][wv] = b; s_wave[2][wv] = c3; s_wave[3][wv] = d; }
   __syncthreads();
-  int base_a = 0, base_b = 0, base_c = 0;
-  for (int i = 0; i < wv; ++i) { base_a += s_wave[0][i]; base_b += s_wave[1][i]; base_c += s_wave[2][i]; }
+  int base_a = 0, base_b = 0, base_c = 0, base_d = 0;
+  for (int i = 0; i < wv; ++i) {
+    base_a += s_wave[0][i]; base_b += s_wave[1][i]; base_c += s_wave[2][i]; base_d += s_wave[3][i];
+  }
   const int excl_rows = base_a + a - n, excl_tiles = base_b + b - nt, excl_act = base_c + c3 - act;
+  const int excl_w = base_d + d - nw;
   if (tid < E) {
     counts[tid] = n;
     tile_first[tid] = excl_tiles;
@@ -124,10 +130,15 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
       tiles[2 * (excl_tiles + m)] = tid;
       tiles[2 * (excl_tiles + m) + 1] = excl_rows + m * tile_m;
     }
+    for (int m = 0; m < nw; ++m) {
+      wtiles[2 * (excl_w + m)] = tid;
+      wtiles[2 * (excl_w + m) + 1] = excl_rows + m * wtile_m;
+    }
   }
   if (tid == E - 1) {
     offsets[E] = excl_rows + n;
     n_tiles[0] = excl_tiles + nt;
+    n_wtiles[0] = excl_w + nw;
     n_active[0] = excl_act + act;
     tile_first[E] = excl_tiles + nt;
     s_rows[0] = excl_rows + n;
@@ -196,7 +207,7 @@ hipError_t launch_plan(const int32_t* topk_idx, int T, int k, int E, const PlanP
                                   p.chunk_hist, p.chunk_invalid, p.n_chunks, E, R, GEMM_TILE_M,
                                   p.counts, p.offsets, p.tiles, p.n_tiles, p.err_flag,
                                   p.src_token, p.src_slot, p.active, p.n_active,
-                                  p.tile_first));
+                                  p.tile_first, GEMM_WTILE_M, p.wtiles, p.n_wtiles));
   if (err != hipSuccess || p.n_chunks == 0) return err;
   return MOE_LAUNCH("plan_scatter", s,
                     plan_scatter_kernel<<<blocks, 256, lds, s>>>(topk_idx, R, E, k, nbits,

@@ -96,8 +96,9 @@ def test_layout_functions(lib):
     assert L.tile_m == 128 and L.chunk_pairs == 512
     assert L.n_chunks == (300 * 4 + 511) // 512
     assert L.max_tiles >= 300 * 4 // 128 + 16
+    assert L.wtile_m == 256 and L.max_wtiles >= 300 * 4 // 256 + 16
     offs = [L.counts, L.offsets, L.src_token, L.src_slot, L.pos, L.tiles, L.n_tiles, L.err_flag,
-            L.scratch]
+            L.active, L.n_active, L.tile_first, L.wtiles, L.n_wtiles, L.scratch]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert B.moe_plan_bytes(s) == L.total_bytes >= L.scratch + 4 * (L.n_chunks * 16 + L.n_chunks)
     R, I, H = 1200, 128, 256

@@ -65,6 +65,9 @@ def check_plan(B, idx, E):
     tl = oracle.tile_list(ref["counts"], ref["offsets"], got["tile_m"])
     assert got["n_tiles"][0] == len(tl)
     np.testing.assert_array_equal(got["tiles"][:len(tl)], tl)
+    wl = oracle.tile_list(ref["counts"], ref["offsets"], got["wtile_m"])
+    assert got["n_wtiles"][0] == len(wl)
+    np.testing.assert_array_equal(got["wtiles"][:len(wl)], wl)
     assert got["err_flag"][0] == int(ref["err"])
     act = np.nonzero(ref["counts"])[0]
     assert got["n_active"][0] == len(act)
@@ -139,3 +142,5 @@ def test_plan_is_deterministic(B):
     for key in ("counts", "offsets", "src_token", "src_slot", "pos", "n_tiles", "err_flag"):
         np.testing.assert_array_equal(a[key], b[key])
     np.testing.assert_array_equal(a["tiles"][:n], b["tiles"][:n])
+    nw = int(a["n_wtiles"][0])
+    np.testing.assert_array_equal(a["wtiles"][:nw], b["wtiles"][:nw])
