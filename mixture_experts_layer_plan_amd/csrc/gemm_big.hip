@@ -51,8 +51,6 @@ constexpr int LDS = 4 * STAGE;   // two stages of (A, B)
 
 typedef __attribute__((address_space(3))) void* lds_vptr;
 typedef const __attribute__((address_space(1))) void* gbl_vptr;
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef short s16x8_t __attribute__((ext_vector_type(8)));
 
 MOE_DEV void dma16(const char* src, char* dst) {
   __builtin_amdgcn_global_load_lds((gbl_vptr)src, (lds_vptr)dst, 16, 0, 0);
@@ -126,7 +124,7 @@ MOE_DEV bf16x8_t frag_k(const char* st, int r0, int ks) {
 // Stage: 64 K rows x 256 columns; chunk c of K row k at k * 512 + 16 (c ^ mnswz(k)).
 // The swizzle spreads the eight K rows x four chunks that one transposing read
 // touches over distinct banks.
-MOE_DEV int mnswz(int k) { return ((k & 3) << 2) | ((k >> 3) & 1); }
+MOE_DEV int mnswz(int k) { return mn_swz(k); }  // as for the 128-column tiles
 // Instruction s of wavefront w fills K rows 16 s + 2 w and +1: lane L brings K row
 // mn_row(s) = 16 s + 2 w + L / 32 into physical chunk L % 32 (the swizzle depends on
 // k % 16 only: the same logical chunk for the four instructions).

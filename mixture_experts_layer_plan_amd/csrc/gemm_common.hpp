@@ -33,6 +33,7 @@ MOE_DEV uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 // wait the branches cause.)
 template <typename T>
 struct KLoad {
+  static constexpr bool kmajor = true;  // LDS tile is K-major (rows of K)
   const T* rp[4];
   MOE_DEV void set(int s, const T* p, bool valid) { rp[s] = valid ? p : nullptr; }
   MOE_DEV void load(int kt, uint4 (&r)[4]) const {
@@ -47,12 +48,23 @@ struct KLoad {
   }
 };
 
+// Swizzle of the MN-major bf16 LDS tile (64 K rows x 128 columns, 256 bytes per K
+// row): 16-byte chunk c of K row k sits at k * 256 + 16 (c ^ mn_swz(k)).  One
+// transposing fragment read touches eight K rows (four consecutive, then four
+// more 8 rows down) x four consecutive chunks; the swizzle gives each of the four
+// rows a different group of four bank-chunks and the other four rows the
+// complementary order, so the read needs the minimum two LDS cycles.
+MOE_DEV int mn_swz(int k) { return ((k & 3) << 2) | ((k >> 3) & 1); }
+
 // MN-major operand: element (k, i) of the tile at kr(k)[i]; kr returns nullptr
 // for K rows outside the operand (they load as zeros).
-// bf16: thread t owns k = 4 (t >> 4) .. +3, i = 8 (t & 15) .. +7.
-// fp32: thread t owns k = 4 (t >> 5) .. +3, i = 4 (t & 31) .. +3.
+// bf16: thread t owns k = 4 (t >> 4) .. +3, i = 8 (t & 15) .. +7, stored as it
+//       lies in memory (MN-major LDS tile, read back by transposing LDS reads).
+// fp32: thread t owns k = 4 (t >> 5) .. +3, i = 4 (t & 31) .. +3, transposed in
+//       registers into the K-major tile (there is no 32-bit transposing read).
 template <typename T, class KR>
 struct MNLoad {
+  static constexpr bool kmajor = sizeof(T) != 2;
   KR kr;
   static constexpr int IB = 128 / Tr<T>::VEC;  // i-blocks per row of 128
   MOE_DEV void load(int kt, uint4 (&r)[4]) const {
@@ -75,16 +87,11 @@ template <typename T, class KR>
 MOE_DEV void MNLoad<T, KR>::store(char* t, const uint4 (&r)[4]) const {
   const int kb = threadIdx.x / IB, ib = threadIdx.x % IB;
   if constexpr (sizeof(T) == 2) {
-    // 4 k x 8 i bf16 -> 8 rows (i) of 4 k values (8 bytes)
+    // K rows 4 kb .. +3, chunk ib of each, as stored in memory
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int sh = (i & 1) * 16;
-      const uint32_t e0 = (u4_word(r[0], i >> 1) >> sh) & 0xffffu;
-      const uint32_t e1 = (u4_word(r[1], i >> 1) >> sh) & 0xffffu;
-      const uint32_t e2 = (u4_word(r[2], i >> 1) >> sh) & 0xffffu;
-      const uint32_t e3 = (u4_word(r[3], i >> 1) >> sh) & 0xffffu;
-      const int row = ib * 8 + i;
-      *(uint2*)(t + swz(row, kb >> 1) + (kb & 1) * 8) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+    for (int kk = 0; kk < 4; ++kk) {
+      const int k = 4 * kb + kk;
+      *(uint4*)(t + k * 256 + ((ib ^ mn_swz(k)) << 4)) = r[kk];
     }
   } else {
     // 4 k x 4 i fp32 -> 4 rows (i) of 4 k values (16 bytes)
@@ -98,15 +105,62 @@ MOE_DEV void MNLoad<T, KR>::store(char* t, const uint4 (&r)[4]) const {
 }
 
 // ------------------------------------------------------------- MFMA on a tile
-// acc[mb][nb]: wave rows arow + 32 mb, B-tile rows brow[nb]; lane l supplies row
-// (l & 31) and the 8 K values of chunk half (l >> 5) of each 16-deep step.
-template <typename T>
+// Fragment of tile rows (K-major) or columns (MN-major) c0 .. c0 + 31 at 16-deep K
+// step ks: lane l supplies row/column c0 + (l & 31) and K values 16 ks + 8 (l >> 5)
+// + 0..7.  K-major: one 16-byte read.  MN-major: two ds_read_b64_tr_b16 (gfx950:
+// within each 16-lane group, lane 4a + b receives element b of the 8-byte rows
+// addressed by lanes a, a + 4, a + 8, a + 12), so lane 16 g + 4 a + j addresses K row
+// 16 ks + 8 (g >> 1) + j (+4 for the second read) at columns c0 + 16 (g & 1) + 4 a.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+
+template <bool KMAJOR>
+MOE_DEV bf16x8_t frag16(const char* t, int c0, int ks, int lane) {
+  if constexpr (KMAJOR) {
+    return *(const bf16x8_t*)(t + swz(c0 + (lane & 31), 2 * ks + (lane >> 5)));
+  } else {
+    const int g = lane >> 4, a = lane & 3, j = (lane >> 2) & 3;
+    const int k = 16 * ks + 8 * (g >> 1) + j;  // K row k + 4 has the same swizzle
+    const int col = c0 + 16 * (g & 1) + 4 * a;
+    const char* p = t + k * 256 + (((col >> 3) ^ mn_swz(k)) << 4) + (col & 7) * 2;
+    typedef __attribute__((address_space(3))) s16x4_t* lp;
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(p));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(p + 4 * 256));
+    return __builtin_bit_cast(bf16x8_t, (s16x8_t)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4,
+                                                                          5, 6, 7));
+  }
+}
+
+// acc[mb][nb]: wave rows arow + 32 mb, B-tile rows brow[nb]; AK / BK: the A / B
+// LDS tile is K-major (else MN-major, bf16 only).
+template <typename T, bool AK = true, bool BK = true>
 MOE_DEV void mma_tile(const char* ta, const char* tb, f32x16_t (&acc)[2][2], int arow,
                       const int (&brow)[2], int lane);
 
 template <>
-MOE_DEV void mma_tile<bf16_t>(const char* ta, const char* tb, f32x16_t (&acc)[2][2], int arow,
-                              const int (&brow)[2], int lane) {
+MOE_DEV void mma_tile<bf16_t, true, true>(const char* ta, const char* tb, f32x16_t (&acc)[2][2],
+                                          int arow, const int (&brow)[2], int lane);
+
+template <typename T, bool AK, bool BK>
+MOE_DEV void mma_tile(const char* ta, const char* tb, f32x16_t (&acc)[2][2], int arow,
+                      const int (&brow)[2], int lane) {
+  static_assert(sizeof(T) == 2, "MN-major LDS tiles are bf16 only");
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const bf16x8_t a0 = frag16<AK>(ta, arow, ks, lane);
+    const bf16x8_t a1 = frag16<AK>(ta, arow + 32, ks, lane);
+    const bf16x8_t b0 = frag16<BK>(tb, brow[0], ks, lane);
+    const bf16x8_t b1 = frag16<BK>(tb, brow[1], ks, lane);
+    acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
+    acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
+    acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
+    acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
+  }
+}
+
+template <>
+MOE_DEV void mma_tile<bf16_t, true, true>(const char* ta, const char* tb, f32x16_t (&acc)[2][2],
+                                          int arow, const int (&brow)[2], int lane) {
   const int r = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -123,8 +177,8 @@ MOE_DEV void mma_tile<bf16_t>(const char* ta, const char* tb, f32x16_t (&acc)[2]
 }
 
 template <>
-MOE_DEV void mma_tile<float>(const char* ta, const char* tb, f32x16_t (&acc)[2][2], int arow,
-                             const int (&brow)[2], int lane) {
+MOE_DEV void mma_tile<float, true, true>(const char* ta, const char* tb, f32x16_t (&acc)[2][2],
+                                         int arow, const int (&brow)[2], int lane) {
   const int r = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
@@ -180,7 +234,7 @@ MOE_DEV void gemm_main(char* lds, const LA& la, const LB& lb, int nk, f32x16_t (
         la.load(kt + 1, ra);
         lb.load(kt + 1, rb);
       }
-      mma_tile<T>(cur, cur + TILEB, acc, arow, brow, lane);
+      mma_tile<T, LA::kmajor, LB::kmajor>(cur, cur + TILEB, acc, arow, brow, lane);
       if (more) {
         la.store(nxt, ra);
         lb.store(nxt + TILEB, rb);
@@ -206,7 +260,7 @@ MOE_DEV void gemm_main(char* lds, const LA& la, const LB& lb, int nk, f32x16_t (
       la.load(kt + 2, ra0);
       lb.load(kt + 2, rb0);
     }
-    mma_tile<T>(buf0, buf0 + TILEB, acc, arow, brow, lane);
+    mma_tile<T, LA::kmajor, LB::kmajor>(buf0, buf0 + TILEB, acc, arow, brow, lane);
     if (kt + 1 < nk) {
       la.store(buf1, ra1);
       lb.store(buf1 + TILEB, rb1);
@@ -217,7 +271,7 @@ MOE_DEV void gemm_main(char* lds, const LA& la, const LB& lb, int nk, f32x16_t (
       la.load(kt + 3, ra1);
       lb.load(kt + 3, rb1);
     }
-    mma_tile<T>(buf1, buf1 + TILEB, acc, arow, brow, lane);
+    mma_tile<T, LA::kmajor, LB::kmajor>(buf1, buf1 + TILEB, acc, arow, brow, lane);
     if (kt + 2 < nk) {
       la.store(buf0, ra0);
       lb.store(buf0 + TILEB, rb0);
