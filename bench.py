@@ -46,9 +46,10 @@ def kernel_work(name, sh, counts, es=2):
                             + R * (I // 128) * 4, 2 * R * H * I),
         "dg_reduce": (R * (I // 128) * 4 + R * 8, 0),
         "zero_empty_experts": ((E - Et) * 3 * I * H * es, 0),
-        "gemm_wgrad_down": (R * H * es + R * I * es + Et * H * I * es, 2 * R * H * I),
+        # the wgrads also store the zero gradients of the E - Et experts without rows
+        "gemm_wgrad_down": (R * H * es + R * I * es + E * H * I * es, 2 * R * H * I),
         "gemm_dgrad_up": (Et * 2 * I * H * es + R * 2 * I * es + R * H * es, 2 * R * 2 * I * H),
-        "gemm_wgrad_up": (R * 2 * I * es + R * H * es + Et * 2 * I * H * es, 2 * R * 2 * I * H),
+        "gemm_wgrad_up": (R * 2 * I * es + R * H * es + E * 2 * I * H * es, 2 * R * 2 * I * H),
         "gemm_dgrad_down_shared": (Is * H * es + T * H * es + T * 2 * Is * 4 + T * 3 * Is * es,
                                    2 * T * H * Is),
         "gemm_wgrad_down_shared": (T * H * es + T * Is * es + H * Is * es, 2 * T * H * Is),

@@ -338,12 +338,7 @@ moe_status backward_impl(moe_dtype dt, const moe_shape* s, const void* plan, con
   // dgrad-down + SwiGLU backward + router-weight-gradient partials
   MOE_TRY(launch_gemm_dgrad_down(d, g, dYu, wd, Z, topk_w, H, I, s->k, dZ, gh, dgp, st));
   MOE_TRY(launch_dg_reduce(dgp, v.pos, R, I / 128, d_topk_w, st));
-  {
-    const size_t es = dt == MOE_BF16 ? 2 : 4;
-    void* bufs[3] = {dwg, dwu, dwd};
-    const size_t stride[3] = {(size_t)I * H * es, (size_t)I * H * es, (size_t)H * I * es};
-    MOE_TRY(launch_zero_empty_experts(v.counts, s->E, bufs, stride, st));
-  }
+  // the wgrads also write the zero gradients of experts without rows
   MOE_TRY(launch_gemm_wgrad_down(d, g, dYu, gh, H, I, dwd, st));
   MOE_TRY(launch_gemm_dgrad_up(d, g, dZ, wg, wu, H, I, dX, st));
   MOE_TRY(launch_gemm_wgrad_up(d, g, dZ, X, H, I, dwg, dwu, st));

@@ -220,8 +220,8 @@ __global__ __launch_bounds__(NTHR, 2) void k_dgrad_up(GroupInfo g, const T* __re
 }
 
 // wgrad-down: dW_d[e][m, n] = sum_r dYu[r, m] gh[r, n]  (M = H, N = I, K = rows of e).
-// Persistent: each workgroup walks work items blockIdx.x, + gridDim.x, ...; experts
-// without rows are not visited (their gradients are zeroed by a separate fill).
+// Persistent: each workgroup walks work items blockIdx.x, + gridDim.x, ...; the
+// tiles of experts without rows are stored as zeros.
 template <typename T>
 __global__ __launch_bounds__(NTHR, 2) void k_wgrad_down(GroupInfo g, const T* __restrict__ dYu,
                                                         const T* __restrict__ gh, int H, int I,
@@ -234,6 +234,10 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_down(GroupInfo g, const T* __
   const int lane = threadIdx.x & 63;
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
     const KTile t = k_tile(g, w, MT, NT);
+    if (k_empty(g, t.e)) {
+      zero_tile<T>(dwd + (size_t)t.e * H * I + (size_t)t.m0 * I + t.n0, (size_t)I);
+      continue;
+    }
     int seg0, seg1;
     k_segment(g, t.e, seg0, seg1);
     MNLoad<T, KRowSeg<T>> la{{dYu + t.m0, nullptr, (size_t)H, seg0, seg1}};
@@ -252,7 +256,8 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_down(GroupInfo g, const T* __
 }
 
 // wgrad-up: [dW_g; dW_u][e][m, n] = sum_r dZ[r, m] X[r, n] with X[r] = x[tok(r)] (the
-// dispatched rows, replayed)  (M = 2I, N = H); persistent.
+// dispatched rows, replayed)  (M = 2I, N = H); persistent, zeros for experts
+// without rows.
 template <typename T>
 __global__ __launch_bounds__(NTHR, 2) void k_wgrad_up(GroupInfo g, const T* __restrict__ dZ,
                                                       const T* __restrict__ X, int H, int I,
@@ -265,6 +270,12 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_up(GroupInfo g, const T* __re
   const int lane = threadIdx.x & 63;
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
     const KTile t = k_tile(g, w, MT, NT);
+    if (k_empty(g, t.e)) {
+      zero_tile<T>((t.m0 < I ? dwg + (size_t)t.e * I * H + (size_t)t.m0 * H
+                             : dwu + (size_t)t.e * I * H + (size_t)(t.m0 - I) * H) + t.n0,
+                   (size_t)H);
+      continue;
+    }
     int seg0, seg1;
     k_segment(g, t.e, seg0, seg1);
     MNLoad<T, KRowSeg<T>> la{{dZ + t.m0, nullptr, (size_t)(2 * I), seg0, seg1}};

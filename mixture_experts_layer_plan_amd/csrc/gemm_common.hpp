@@ -420,23 +420,42 @@ MOE_DEV void k_segment(const GroupInfo& g, int e, int& seg0, int& seg1) {
 }
 
 // Work item w of a K-grouped GEMM over an M_tiles x N_tiles output per expert:
-// experts with rows only (the plan's active list), tiles in row-major order.
+// every expert in id order (the single dense "expert" in dense mode), tiles in
+// row-major order.  Items of experts without rows store zeros (the weight
+// gradients are overwritten), so those writes interleave with the multiplying
+// items of the other experts instead of running as a separate pass.
 struct KTile {
   int e, m0, n0;
 };
 MOE_DEV KTile k_tile(const GroupInfo& g, int w, int mt_count, int nt_count) {
   const int per = mt_count * nt_count;
-  const int a = w / per, rem = w - a * per;
+  const int e = w / per, rem = w - e * per;
   const int mt = rem / nt_count;
   KTile t;
-  t.e = g.active ? g.active[a] : 0;
+  t.e = e;
   t.m0 = mt * TM;
   t.n0 = (rem - mt * nt_count) * TN;
   return t;
 }
 
 MOE_DEV int k_work_items(const GroupInfo& g, int mt_count, int nt_count) {
-  return (g.active ? g.n_active[0] : 1) * mt_count * nt_count;
+  return (g.offsets ? g.E : 1) * mt_count * nt_count;
+}
+
+MOE_DEV bool k_empty(const GroupInfo& g, int e) { return g.counts && g.counts[e] == 0; }
+
+// Zero a TM x TN tile of T at out (row stride ld elements) with 16-byte
+// non-temporal stores.
+template <typename T>
+MOE_DEV void zero_tile(T* out, size_t ld) {
+  constexpr int CPR = TN * (int)sizeof(T) / 16;  // 16-byte chunks per row
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < TM * CPR / NTHR; ++i) {
+    const int c = (int)threadIdx.x + i * NTHR;
+    const int r = c / CPR, q = c - r * CPR;
+    __builtin_nontemporal_store(z, (u32x4_t*)(out + (size_t)r * ld) + q);
+  }
 }
 
 // Persistent grid: two resident workgroups per compute unit, at most one per item.
