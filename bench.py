@@ -1,11 +1,18 @@
-"""Throughput of the deterministic MoE layer (forward + backward) on one MI355X.
+"""Throughput of the deterministic MoE layer on one MI355X.
 
-One step = route -> plan -> forward -> backward -> router backward over one batch of
-the bf16 workload T=4096, H=7168, I=2048, E=256, k=8 with a shared expert
-(I_shared=2048) and Zipf(1.2)-skewed routing; all inputs are synthetic and already
-resident in HBM.  Prints ONE JSON line with tokens/s, the roofline of the dominant
-kernel (timed live with HIP events around each launch over the timed region) and
-the fp64 oracle's throughput on a bounded sample of the same workload on the host.
+Default workload (the headline): one step = route -> plan -> forward -> backward ->
+router backward over one batch of the bf16 workload T=4096, H=7168, I=2048, E=256,
+k=8 with a shared expert (I_shared=2048) and Zipf(1.2)-skewed routing; all inputs
+are synthetic and already resident in HBM.  Prints ONE JSON line with tokens/s,
+the roofline of the dominant kernel (timed live with HIP events around each launch
+over the timed region), per-kernel MFMA / HBM / roofline fractions, and the fp64
+oracle's throughput on a bounded sample of the same workload on the host.
+
+`--config` selects another workload of synth.CONFIGS: forward-only configs time
+route -> plan -> forward; the MXFP8 ring config times the MX layer with its
+weights quantised once before the timed region (the weight conversion runs once
+per weight update and is reported on its own); `ep_share_bf16` is one GPU's share
+of an expert-parallel layer (4 local experts x 4096 rows), compute-bound.
 """
 from __future__ import annotations
 
@@ -23,43 +30,78 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "mxfp8": 5000.0}
 METRIC = "MoE layer tokens/s fwd+bwd @H7168 I2048 E256 top8, 1 GPU; % MFMA/HBM peak"
 
 
-def kernel_work(name, sh, counts, es=2):
-    """Algorithmic (bytes, flops) of one launch of kernel `name` for this routing.
+def kernel_work(name, sh, counts_mb, es=2):
+    """Algorithmic (bytes, flops) of kernel `name` summed over its launches in one
+    step, for the realised routing (counts_mb: per-minibatch expert row counts).
 
-    Bytes count every operand once: weights of the touched experts, activation
-    rows read and written, gradients written; flops count 2 per multiply-add."""
+    Bytes count every operand once per launch: weights of the touched experts,
+    activation rows read and written, gradients written; flops count 2 per
+    multiply-add.  MXFP8 operands are 1 byte per element plus one scale byte per
+    32."""
     T, H, I, E, k, Is = sh.T, sh.H, sh.I, sh.E, sh.k, sh.I_shared
-    R = int(sum(counts))
-    Et = int(sum(1 for c in counts if c > 0))
+    q = 1 + 1 / 32  # MXFP8 bytes per element with its scale
+    mbs = [(sum(c), sum(1 for v in c if v > 0)) for c in counts_mb]  # (R_m, Et_m)
+    n_mb = len(mbs)
+    Tm = [min(sh.T_minibatch or T, T - m * (sh.T_minibatch or T)) for m in range(n_mb)]
+    R = sum(r for r, _ in mbs)
+    union = [sum(c[e] for c in counts_mb) for e in range(E)]
+    Et = sum(1 for v in union if v > 0)
+
+    def over_mb(f):
+        b = fl = 0.0
+        for (Rm, Etm), tm in zip(mbs, Tm):
+            x, y = f(Rm, Etm, tm)
+            b += x
+            fl += y
+        return int(b), int(fl)
+
     w = {
-        "route": (T * E * 4 + T * k * 8, 0),
-        "plan_hist": (R * 4, 0), "plan_scan": (E * 12, 0), "plan_scatter": (R * 16, 0),
-        # saved pre-activations Z are fp32 (4 bytes), h bf16
-        "gemm_up_swiglu": (Et * 2 * I * H * es + R * H * es + R * 2 * I * 4 + R * I * es,
-                           2 * R * H * 2 * I),
-        "gemm_down": (Et * H * I * es + R * I * es + R * H * es, 2 * R * I * H),
-        "gemm_up_swiglu_shared": (2 * Is * H * es + T * H * es + T * 2 * Is * 4 + T * Is * es,
-                                  2 * T * H * 2 * Is),
-        "gemm_down_shared": (Is * H * es + T * Is * es + T * H * es, 2 * T * Is * H),
-        "combine_bf16": (R * H * es + 2 * T * H * es + T * k * 8, 0),
-        "gemm_dgrad_down": (Et * H * I * es + R * H * es + R * 2 * I * 4 + R * 3 * I * es
-                            + R * (I // 128) * 4, 2 * R * H * I),
-        "dg_reduce": (R * (I // 128) * 4 + R * 8, 0),
-        "zero_empty_experts": ((E - Et) * 3 * I * H * es, 0),
+        "route": lambda: (T * E * 4 + T * k * 8, 0),
+        "route_backward": lambda: (T * k * 12 + T * E * 4, 0),
+        "plan_hist": lambda: over_mb(lambda Rm, Etm, tm: (Rm * 4, 0)),
+        "plan_scan": lambda: over_mb(lambda Rm, Etm, tm: (E * 12, 0)),
+        "plan_scatter": lambda: over_mb(lambda Rm, Etm, tm: (Rm * 16, 0)),
+        "dg_reduce": lambda: over_mb(lambda Rm, Etm, tm: (Rm * (I // 128) * 4 + Rm * 8, 0)),
+        "gather_rows": lambda: (2 * (2 * R * H * es + R * 4), 0),  # X and dYu replays
+        "combine_bf16": lambda: over_mb(lambda Rm, Etm, tm: (Rm * H * 2 + 2 * tm * H * 2 + tm * k * 8, 0)),
+        "reverse_dispatch_bf16": lambda: over_mb(lambda Rm, Etm, tm: (Rm * H * 2 + 2 * tm * H * 2, 0)),
+        # saved pre-activations Z are fp32 (4 bytes), h in the layer's dtype
+        "gemm_up_swiglu": lambda: (Et * 2 * I * H * es + R * H * es + R * 2 * I * 4 + R * I * es,
+                                   2 * R * H * 2 * I),
+        "gemm_down": lambda: (Et * H * I * es + R * I * es + R * H * es, 2 * R * I * H),
+        "gemm_dgrad_down": lambda: (Et * H * I * es + R * H * es + R * 2 * I * 4 + R * 3 * I * es
+                                    + R * (I // 128) * 4, 2 * R * H * I),
         # the wgrads also store the zero gradients of the E - Et experts without rows
-        "gemm_wgrad_down": (R * H * es + R * I * es + E * H * I * es, 2 * R * H * I),
-        "gemm_dgrad_up": (Et * 2 * I * H * es + R * 2 * I * es + R * H * es, 2 * R * 2 * I * H),
-        "gemm_wgrad_up": (R * 2 * I * es + R * H * es + E * 2 * I * H * es, 2 * R * 2 * I * H),
-        "gemm_dgrad_down_shared": (Is * H * es + T * H * es + T * 2 * Is * 4 + T * 3 * Is * es,
-                                   2 * T * H * Is),
-        "gemm_wgrad_down_shared": (T * H * es + T * Is * es + H * Is * es, 2 * T * H * Is),
-        "gemm_dgrad_up_shared": (2 * Is * H * es + T * 2 * Is * es + T * H * es, 2 * T * 2 * Is * H),
-        "gemm_wgrad_up_shared": (T * 2 * Is * es + T * H * es + 2 * Is * H * es, 2 * T * 2 * Is * H),
-        "reverse_dispatch_bf16": (R * H * es + 2 * T * H * es, 0),
-        "gather_rows": (2 * R * H * es + R * 4, 0),
-        "route_backward": (T * k * 12 + T * E * 4, 0),
+        "gemm_wgrad_down": lambda: (R * H * es + R * I * es + E * H * I * es, 2 * R * H * I),
+        "gemm_dgrad_up": lambda: (Et * 2 * I * H * es + R * 2 * I * es + R * H * es, 2 * R * 2 * I * H),
+        "gemm_wgrad_up": lambda: (R * 2 * I * es + R * H * es + E * 2 * I * H * es, 2 * R * 2 * I * H),
+        "gemm_up_swiglu_shared": lambda: (2 * Is * H * 2 + T * H * 2 + T * 2 * Is * 4 + T * Is * 2,
+                                          2 * T * H * 2 * Is),
+        "gemm_down_shared": lambda: (Is * H * 2 + T * Is * 2 + T * H * 2, 2 * T * Is * H),
+        "gemm_dgrad_down_shared": lambda: (Is * H * 2 + T * H * 2 + T * 2 * Is * 4 + T * 3 * Is * 2,
+                                           2 * T * H * Is),
+        "gemm_wgrad_down_shared": lambda: (T * H * 2 + T * Is * 2 + H * Is * 2, 2 * T * H * Is),
+        "gemm_dgrad_up_shared": lambda: (2 * Is * H * 2 + T * 2 * Is * 2 + T * H * 2, 2 * T * 2 * Is * H),
+        "gemm_wgrad_up_shared": lambda: (T * 2 * Is * 2 + T * H * 2 + 2 * Is * H * 2, 2 * T * 2 * Is * H),
+        # MXFP8 path (per minibatch unless noted)
+        "mx_quant_rows": lambda: over_mb(lambda Rm, Etm, tm: (2 * Rm * H * (2 + q), 0)),  # x, dy
+        "mx_quant_tokens": lambda: over_mb(lambda Rm, Etm, tm: (Rm * (2 * H * (2 + q) + I * (4 + q)
+                                                                      + 2 * I * (4 + q)), 0)),
+        "mx_gemm_up_swiglu": lambda: over_mb(lambda Rm, Etm, tm: (
+            Etm * 2 * I * H * q + Rm * H * q + Rm * 2 * I * 4 + Rm * I * q, 2 * Rm * H * 2 * I)),
+        "mx_gemm_down": lambda: over_mb(lambda Rm, Etm, tm: (
+            Etm * H * I * q + Rm * I * q + Rm * H * 2, 2 * Rm * I * H)),
+        "mx_gemm_dgrad_down": lambda: over_mb(lambda Rm, Etm, tm: (
+            Etm * H * I * q + Rm * H * q + Rm * 2 * I * 4 + Rm * 2 * I * 4 + Rm * I * 4
+            + Rm * 2 * I * q + Rm * (I // 128) * 4, 2 * Rm * H * I)),
+        "mx_gemm_dgrad_up": lambda: over_mb(lambda Rm, Etm, tm: (
+            Etm * 2 * I * H * q + Rm * 2 * I * q + Rm * H * 2, 2 * Rm * 2 * I * H)),
+        "mx_gemm_wgrad_down": lambda: (int(R * (H + I) * q + Et * H * I * 2), 2 * R * H * I),
+        "mx_gemm_wgrad_up": lambda: (int(R * (2 * I + H) * q + Et * 2 * I * H * 2), 2 * R * 2 * I * H),
+        "zero_empty_experts": lambda: ((E - Et) * 3 * I * H * es, 0),
     }
-    return w.get(name, (0, 0))
+    f = w.get(name)
+    return f() if f else (0, 0)
 
 
 def kernel_sources_sha256() -> str:
@@ -136,18 +178,17 @@ def main():
 
     import torch
 
-    from mixture_experts_layer_plan_amd import LayerBuffers, binding
+    from mixture_experts_layer_plan_amd import LayerBuffers, binding, layer
     from mixture_experts_layer_plan_amd.layer import run_layer
     from synth import CONFIGS, make_inputs
 
     sh = CONFIGS[args.config]
-    if sh.dtype != "bf16" or not sh.backward:
-        raise SystemExit(f"bench config {args.config} is not a bf16 forward+backward workload")
     torch.cuda.set_device(0)
     log = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
     log(f"[bench] generating {args.config} inputs on the device")
-    inp = make_inputs(sh, seed=0, device="cuda", with_dy=True)
-    b = LayerBuffers(sh.T, sh.H, sh.I, sh.E, sh.k, sh.I_shared, "bf16", backward=True)
+    inp = make_inputs(sh, seed=0, device="cuda", with_dy=sh.backward)
+    b = LayerBuffers(sh.T, sh.H, sh.I, sh.E, sh.k, sh.I_shared, sh.dtype, backward=sh.backward,
+                     router_gemm=sh.router == "gemm", T_minibatch=sh.T_minibatch)
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -155,14 +196,33 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    stream = torch.cuda.current_stream()
+    mx = sh.dtype == "mxfp8"
+    quant_ms = None
+    if mx:
+        # weights change once per optimiser step, not per layer pass: convert them
+        # once here and time that conversion on its own
+        layer.quantize_weights(b, inp)
+        torch.cuda.synchronize()
+        q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        q0.record(stream)
+        layer.quantize_weights(b, inp)
+        q1.record(stream)
+        torch.cuda.synchronize()
+        quant_ms = q0.elapsed_time(q1)
+
+    def step():
+        run_layer(b, inp, backward=sh.backward, quantize=False)
+
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
-        run_layer(b, inp, backward=True)
+        step()
     torch.cuda.synchronize()
-    counts = b.plan_views()["counts"].cpu().tolist()
+    n_mb = max(1, binding.moe_plan_layout_of(b.s).n_minibatch)
+    counts_mb = [binding.plan_views(b.s, b.plan, m)["counts"].cpu().tolist() for m in range(n_mb)]
+    counts = [sum(c[e] for c in counts_mb) for e in range(sh.E)]
 
-    trace = binding.KernelTrace(capacity=64 * max(args.steps, 1))
-    stream = torch.cuda.current_stream()
+    trace = binding.KernelTrace(capacity=96 * max(args.steps, 1))
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
@@ -170,7 +230,7 @@ def main():
     ev0.record(stream)
     with trace:
         for _ in range(args.steps):
-            run_layer(b, inp, backward=True)
+            step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -180,7 +240,9 @@ def main():
     ms_per_step = ms_total / max(args.steps, 1)
     tokens_per_s = sh.T / (ms_per_step / 1e3)
 
-    # per-kernel averages over the timed region
+    # per-kernel averages over the timed region; work per step from the routing
+    es = 4 if sh.dtype == "f32" else 2
+    peak_flops = MFMA_PEAK_TFLOPS["mxfp8" if mx else sh.dtype] * 1e12
     agg = {}
     for name, ms in recs:
         a = agg.setdefault(name, [0.0, 0])
@@ -188,19 +250,29 @@ def main():
         a[1] += 1
     kernels = {}
     for name, (tot, n) in sorted(agg.items(), key=lambda kv: -kv[1][0]):
-        byt, flop = kernel_work(name, sh, counts)
-        avg_s = tot / n / 1e3
-        kernels[name] = {"avg_ms": round(tot / n, 4), "launches": n,
+        byt, flop = kernel_work(name, sh, counts_mb, es)
+        pk = peak_flops if name.startswith("mx_gemm") else MFMA_PEAK_TFLOPS[
+            "f32" if sh.dtype == "f32" else "bf16"] * 1e12
+        t_step = tot / max(args.steps, 1) / 1e3  # seconds per step
+        t_roof = max(byt / (HBM_PEAK_GBS * 1e9), flop / pk)
+        kernels[name] = {"avg_ms": round(tot / n, 4), "launches_per_step": n // max(args.steps, 1),
                          "share": round(tot / max(ms_total, 1e-9), 4),
-                         "GB_s": round(byt / avg_s / 1e9, 1) if byt else None,
-                         "TFLOP_s": round(flop / avg_s / 1e12, 1) if flop else None}
+                         "GB_s": round(byt / t_step / 1e9, 1) if byt else None,
+                         "TFLOP_s": round(flop / t_step / 1e12, 1) if flop else None,
+                         "hbm_frac": round(byt / t_step / (HBM_PEAK_GBS * 1e9), 4) if byt else None,
+                         "mfma_frac": round(flop / t_step / pk, 4) if flop else None,
+                         "roof_frac": round(t_roof / t_step, 4) if t_roof else None}
     dom = max(agg, key=lambda n: agg[n][0])
-    byt, flop = kernel_work(dom, sh, counts)
+    byt, flop = kernel_work(dom, sh, counts_mb, es)
+    n_launch = agg[dom][1] // max(args.steps, 1)
+    byt, flop = byt // max(n_launch, 1), flop // max(n_launch, 1)  # per launch
     avg_s = agg[dom][0] / agg[dom][1] / 1e3
-    t_hbm, t_mfma = byt / (HBM_PEAK_GBS * 1e9), flop / (MFMA_PEAK_TFLOPS["bf16"] * 1e12)
+    pk = peak_flops if dom.startswith("mx_gemm") else MFMA_PEAK_TFLOPS[
+        "f32" if sh.dtype == "f32" else "bf16"] * 1e12
+    t_hbm, t_mfma = byt / (HBM_PEAK_GBS * 1e9), flop / pk
     if t_mfma > t_hbm:
         roof = {"bound": "mfma", "achieved": round(flop / avg_s / 1e12, 2),
-                "peak": MFMA_PEAK_TFLOPS["bf16"], "unit": "TFLOP/s"}
+                "peak": pk / 1e12, "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": round(byt / avg_s / 1e9, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
@@ -211,18 +283,25 @@ def main():
     roof["algorithmic_flops"] = flop
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.config == "kimi_bf16_fwdbwd":
         log(f"[bench] oracle on {args.cpu_tokens} tokens (cpu baseline)")
         cpu = cpu_baseline(sh, inp, args.cpu_tokens)
 
+    passes = "fwd+bwd" if sh.backward else "fwd"
+    metric = METRIC if args.config == "kimi_bf16_fwdbwd" else (
+        f"MoE layer tokens/s {passes} @H{sh.H} I{sh.I} E{sh.E} top{sh.k}, 1 GPU; "
+        f"% MFMA/HBM peak")
+    desc = (f"{args.config}: {sh.dtype} MoE layer {passes}, T={sh.T} H={sh.H} I={sh.I} E={sh.E} "
+            f"top-{sh.k}" + (f", shared expert I={sh.I_shared}" if sh.I_shared else "")
+            + (f", Zipf({sh.zipf_s}) routing" if sh.zipf_s else "")
+            + (f", minibatches of {sh.T_minibatch}" if sh.T_minibatch else ""))
     out = {
-        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": metric, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "f32": "f32", "mxfp8": "fp8-e4m3 (MX) + bf16"}[sh.dtype],
         "data": "synthetic",
-        "config": {"workload": f"{args.config}: bf16 MoE layer fwd+bwd, T={sh.T} H={sh.H} "
-                               f"I={sh.I} E={sh.E} top-{sh.k}, shared expert I={sh.I_shared}, "
-                               f"Zipf({sh.zipf_s}) routing", "T": sh.T, "H": sh.H, "I": sh.I,
+        "config": {"workload": desc, "T": sh.T, "H": sh.H, "I": sh.I,
                    "E": sh.E, "k": sh.k, "I_shared": sh.I_shared, "parallelism": "single GPU",
                    "experts_touched": int(sum(1 for c in counts if c > 0)),
                    "max_rows_per_expert": int(max(counts))},
@@ -231,6 +310,9 @@ def main():
         "kernels": kernels,
         "wall_s_timed": round(wall, 3),
     }
+    if quant_ms is not None:
+        out["config"]["T_minibatch"] = sh.T_minibatch
+        out["mx_weight_quantisation_ms"] = round(quant_ms, 4)
     print(json.dumps(out), flush=True)
 
 

@@ -2,7 +2,8 @@
 
 ``LayerBuffers`` allocates (through torch, on the current device) every output,
 the plan, the saved activations and the workspaces that the C-ABI asks for.
-``run_layer`` enqueues route -> plan -> [MX weight quantisation ->] forward [-> backward -> router backward]
+``run_layer`` enqueues route -> plan -> [MX weight quantisation ->] forward [-> backward ->
+router backward]
 on the current stream.  Both only move pointers; the arithmetic is in libmoe.so.
 """
 from __future__ import annotations
@@ -53,7 +54,14 @@ class LayerBuffers:
         return B.plan_views(self.s, self.plan)
 
 
-def run_forward(b: LayerBuffers, inp: dict, stream=None):
+def quantize_weights(b: LayerBuffers, inp: dict, stream=None):
+    """MXFP8 weights in the six orientations the MX GEMMs read (once per weight update)."""
+    B.moe_quantize_weights_mxfp8(b.s, inp["w_gate"], inp["w_up"], inp["w_down"], b.wq, stream)
+
+
+def run_forward(b: LayerBuffers, inp: dict, stream=None, quantize=True):
+    """route -> plan -> forward; for MXFP8 also the weight quantisation unless
+    ``quantize`` is False (weights already quantised into ``b.wq``)."""
     s = b.s
     if "w_router" in inp:
         B.moe_router_logits_f32(s, inp["x"], inp["w_router"], b.logits, stream)
@@ -63,7 +71,8 @@ def run_forward(b: LayerBuffers, inp: dict, stream=None):
     B.moe_route(s, logits, b.topk_idx, b.topk_w, stream)
     B.moe_plan(s, b.topk_idx, b.plan, stream)
     if b.dtype == "mxfp8":
-        B.moe_quantize_weights_mxfp8(s, inp["w_gate"], inp["w_up"], inp["w_down"], b.wq, stream)
+        if quantize:
+            quantize_weights(b, inp, stream)
         B.moe_forward_mxfp8(s, b.plan, inp["x"], b.topk_w, b.wq, inp.get("s_gate"),
                             inp.get("s_up"), inp.get("s_down"), b.y, b.saved, b.ws_fwd, stream)
         return
@@ -91,7 +100,7 @@ def run_backward(b: LayerBuffers, inp: dict, stream=None):
                                   stream)
 
 
-def run_layer(b: LayerBuffers, inp: dict, backward: bool = True, stream=None):
-    run_forward(b, inp, stream)
+def run_layer(b: LayerBuffers, inp: dict, backward: bool = True, stream=None, quantize=True):
+    run_forward(b, inp, stream, quantize)
     if backward:
         run_backward(b, inp, stream)

@@ -58,6 +58,9 @@ CONFIGS: dict[str, Shape] = {
     # MXFP8 forward+backward over 4 minibatches of 2048 tokens through a ring buffer
     "kimi_mxfp8_ring": Shape(T=8192, H=7168, I=2048, E=256, k=8, I_shared=2048,
                              T_minibatch=2048, dtype="mxfp8", zipf_s=1.2),
+    # one GPU's share of an expert-parallel layer: 4 local experts, every token on all
+    # four (k = E), so each expert gets exactly 4096 rows; bf16 forward+backward
+    "ep_share_bf16": Shape(T=4096, H=7168, I=2048, E=4, k=4),
 }
 
 
