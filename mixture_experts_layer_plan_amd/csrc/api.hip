@@ -448,11 +448,12 @@ MxFwdWs mx_fwd_ws(const moe_shape* s) {
 
 // Backward workspace: per-minibatch buffers (dYu ring, dZ fp32 and MX, g h fp32,
 // dg partials, dX) and the token-quantised wgrad operands of all minibatches
-// (transposed, tile-padded token axis of Kp = n_mb * max_tiles * 128 bytes).
+// (the transposed token axis of the wgrads: Kp = n_mb * max_tiles * 128 bytes per row,
+// of which the experts' padded segments use at most all but 97).
 struct MxBwdWs {
   size_t ring8[2], rings[2], dZ, dZ8, dZs, gh, dgp, dX;
   size_t dYuT8, dYuTs, ghT8, ghTs, dZT8, dZTs, XT8, XTs;
-  size_t counts_all, active, n_active;
+  size_t counts_all, active, n_active, kseg, kpos;
   size_t dZs_sh, hs_sh, dxs, total;
   size_t Kp;
 };
@@ -479,6 +480,8 @@ MxBwdWs mx_bwd_ws(const moe_shape* s) {
   L.counts_all = c.take(sizeof(int32_t) * s->E);
   L.active = c.take(sizeof(int32_t) * s->E);
   L.n_active = c.take(sizeof(int32_t));
+  L.kseg = c.take(sizeof(int32_t) * (size_t)n_minibatches(s) * s->E);
+  L.kpos = c.take(sizeof(int32_t) * (s->E + 1));
   L.dZs_sh = c.take(T * 2 * s->I_shared * 2);
   L.hs_sh = c.take(T * s->I_shared * 2);
   L.dxs = c.take(s->I_shared ? T * H * 2 : 0);
@@ -575,15 +578,23 @@ moe_status backward_mx_impl(const moe_shape* s, const void* plan, const void* x,
     MOE_TRY(launch_gemm_dgrad_up(1, gs, dZs, sg, su, H, Is, dxs, st));
     MOE_TRY(launch_gemm_wgrad_up(1, gs, dZs, x, H, Is, dsg, dsu, st));
   }
+  // the wgrads' token axis over all minibatches (offsets per expert and minibatch)
   const int32_t* counts[MX_MAX_MB];
+  for (int m = 0; m < nmb; ++m) counts[m] = view_plan(s, plan, m).counts;
+  int32_t* counts_all = at<int32_t>(ws, W.counts_all);
+  int32_t* active = at<int32_t>(ws, W.active);
+  int32_t* n_active = at<int32_t>(ws, W.n_active);
+  int32_t* kseg = at<int32_t>(ws, W.kseg);
+  int32_t* kpos = at<int32_t>(ws, W.kpos);
+  MOE_TRY(launch_mb_union(counts, nmb, s->E, counts_all, active, n_active, kseg, kpos, st));
   MbPlans mp;
   mp.n_mb = nmb;
-  mp.max_tiles = P.max_tiles;
+  mp.kpos = kpos;
+  mp.active = active;
+  mp.n_active = n_active;
   for (int m = nmb - 1; m >= 0; --m) {
     const int T_m = std::min(Tmb, s->T - m * Tmb), R_m = T_m * k;
     const PlanView v = view_plan(s, plan, m);
-    counts[m] = v.counts;
-    mp.tile_first[m] = v.tile_first;
     if (T_m <= 0) continue;
     const GroupInfo g = grouped(s, v);
     const size_t tok0 = (size_t)m * Tmb;
@@ -598,35 +609,31 @@ moe_status backward_mx_impl(const moe_shape* s, const void* plan, const void* x,
     void* gh = at<char>(ws, W.gh);
     float* dgp = at<float>(ws, W.dgp);
     void* dX = at<char>(ws, W.dX);
-    const size_t kofs = (size_t)m * P.max_tiles * 128;
+    const int32_t* ksm = kseg + (size_t)m * s->E;
     // reverse-combine into the ring slot, quantised along H
     MOE_TRY(launch_quant_rows(1, dym, v.src_token, v.offsets + s->E, R_m, H, dYu8, dYus, st));
     MOE_TRY(launch_mx_dgrad_down(g, dYu8, dYus, q + Q.wdT8, q + Q.wdTs, Z, topk_w + tok0 * k, H,
                                  I, k, dZ, dZ8, dZsc, gh, dgp, st));
     MOE_TRY(launch_dg_reduce(dgp, v.pos, R_m, I / 128, d_topk_w + tok0 * k, st));
     // wgrad operands of this minibatch, quantised along its tokens
-    MOE_TRY(launch_quant_tokens(1, dym, v.src_token, H, v.tiles, v.n_tiles, v.offsets, P.max_tiles,
-                                H, W.Kp, kofs, at<uint8_t>(ws, W.dYuT8), at<uint8_t>(ws, W.dYuTs),
-                                st));
-    MOE_TRY(launch_quant_tokens(1, xm, v.src_token, H, v.tiles, v.n_tiles, v.offsets, P.max_tiles, H,
-                                W.Kp, kofs, at<uint8_t>(ws, W.XT8), at<uint8_t>(ws, W.XTs), st));
-    MOE_TRY(launch_quant_tokens(0, gh, nullptr, I, v.tiles, v.n_tiles, v.offsets, P.max_tiles, I,
-                                W.Kp, kofs, at<uint8_t>(ws, W.ghT8), at<uint8_t>(ws, W.ghTs), st));
-    MOE_TRY(launch_quant_tokens(0, dZ, nullptr, 2 * I, v.tiles, v.n_tiles, v.offsets, P.max_tiles,
-                                2 * I, W.Kp, kofs, at<uint8_t>(ws, W.dZT8), at<uint8_t>(ws, W.dZTs),
-                                st));
+    MOE_TRY(launch_quant_tokens(1, dym, v.src_token, H, v.tiles, v.n_tiles, v.offsets, kpos, ksm,
+                                P.max_tiles, H, W.Kp, at<uint8_t>(ws, W.dYuT8),
+                                at<uint8_t>(ws, W.dYuTs), st));
+    MOE_TRY(launch_quant_tokens(1, xm, v.src_token, H, v.tiles, v.n_tiles, v.offsets, kpos, ksm,
+                                P.max_tiles, H, W.Kp, at<uint8_t>(ws, W.XT8),
+                                at<uint8_t>(ws, W.XTs), st));
+    MOE_TRY(launch_quant_tokens(0, gh, nullptr, I, v.tiles, v.n_tiles, v.offsets, kpos, ksm,
+                                P.max_tiles, I, W.Kp, at<uint8_t>(ws, W.ghT8),
+                                at<uint8_t>(ws, W.ghTs), st));
+    MOE_TRY(launch_quant_tokens(0, dZ, nullptr, 2 * I, v.tiles, v.n_tiles, v.offsets, kpos, ksm,
+                                P.max_tiles, 2 * I, W.Kp, at<uint8_t>(ws, W.dZT8),
+                                at<uint8_t>(ws, W.dZTs), st));
     MOE_TRY(launch_mx_dgrad_up(g, dZ8, dZsc, q + Q.wgT8, q + Q.wgTs, q + Q.wuT8, q + Q.wuTs, H, I,
                                dX, st));
     MOE_TRY(launch_combine_bf16(dX, v.pos, nullptr,
                                 dxs ? (const bf16_t_host*)dxs + tok0 * H : nullptr,
                                 (bf16_t_host*)dx + tok0 * H, T_m, k, H, st));
   }
-  int32_t* counts_all = at<int32_t>(ws, W.counts_all);
-  int32_t* active = at<int32_t>(ws, W.active);
-  int32_t* n_active = at<int32_t>(ws, W.n_active);
-  MOE_TRY(launch_mb_union(counts, nmb, s->E, counts_all, active, n_active, st));
-  mp.active = active;
-  mp.n_active = n_active;
   {
     void* bufs[3] = {dwg, dwu, dwd};
     const size_t stride[3] = {(size_t)I * H * 2, (size_t)I * H * 2, (size_t)H * I * 2};
@@ -634,10 +641,10 @@ moe_status backward_mx_impl(const moe_shape* s, const void* plan, const void* x,
   }
   MOE_TRY(launch_mx_wgrad("mx_gemm_wgrad_down", mp, s->E, at<uint8_t>(ws, W.dYuT8),
                           at<uint8_t>(ws, W.dYuTs), at<uint8_t>(ws, W.ghT8),
-                          at<uint8_t>(ws, W.ghTs), H, I, H, dwd, nullptr, st));
+                          at<uint8_t>(ws, W.ghTs), H, I, H, W.Kp, dwd, nullptr, st));
   MOE_TRY(launch_mx_wgrad("mx_gemm_wgrad_up", mp, s->E, at<uint8_t>(ws, W.dZT8),
                           at<uint8_t>(ws, W.dZTs), at<uint8_t>(ws, W.XT8), at<uint8_t>(ws, W.XTs),
-                          2 * I, H, I, dwg, dwu, st));
+                          2 * I, H, I, W.Kp, dwg, dwu, st));
   return MOE_OK;
 }
 

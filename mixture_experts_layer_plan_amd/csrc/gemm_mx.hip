@@ -30,39 +30,53 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 constexpr int MX_BK = 128;  // K bytes per tile row (4 scale blocks)
 
 // One K-major MX operand as seen by one thread: data rows for its loads (rows
-// (t >> 3) + 32 s of the tile), scale rows for its MFMA fragments (two 32-row
-// blocks).  A second source can take over at K >= ksplit (dgrad-up weights); its
-// pointers are pre-offset by -ksplit so that the same K offset applies.
-// Rows outside the operand (dok / sok false) load as zeros.
+// (t >> 3) + 32 s of the tile) and scale rows for its MFMA fragments (two 32-row
+// blocks), as 32-bit byte offsets from wave-uniform bases.  Source 1 replaces
+// source 0 for the rows flagged in `sel` (bit s: loader row s, bit 4 + q: scale row
+// q) and for all rows at K >= ksplit (dgrad-up's second weight; its bases are then
+// pre-offset by -ksplit so that the same K offset applies).  Rows with their bit
+// clear in `ok` (same bit positions) load as zeros, and so do the K bytes at or past
+// kend (a multiple of 32): their 16-byte chunks are zeroed and their blocks' scale
+// bytes set to 0 (2^-127), so no stale scale byte (0xFF is NaN in E8M0) reaches the
+// MFMA.
 struct MxOp {
-  const uint8_t* d[4];
-  const uint8_t* d_hi[4];
-  const uint8_t* sc[2];
-  const uint8_t* sc_hi[2];
-  bool dok[4], sok[2];
-  long ksplit;
+  const uint8_t* d[2];   // data bases of source 0 and 1
+  const uint8_t* s[2];   // scale bases
+  uint32_t off[4];       // data row offsets (bytes)
+  uint32_t soff[2];      // scale row offsets (bytes)
+  uint32_t sel, ok;
+  long ksplit, kend;
 };
 
 MOE_DEV void mx_op_clear(MxOp& o) {
+  o.d[0] = o.d[1] = nullptr;
+  o.s[0] = o.s[1] = nullptr;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    o.d[s] = o.d_hi[s] = nullptr;
-    o.dok[s] = true;
-  }
-  o.sc[0] = o.sc[1] = o.sc_hi[0] = o.sc_hi[1] = nullptr;
-  o.sok[0] = o.sok[1] = true;
+  for (int i = 0; i < 4; ++i) o.off[i] = 0;
+  o.soff[0] = o.soff[1] = 0;
+  o.sel = 0;
+  o.ok = 0x3fu;
   o.ksplit = 1L << 62;
+  o.kend = 1L << 62;
 }
 
 MOE_DEV void mx_load(const MxOp& o, long koff, uint4 (&r)[4], uint32_t (&sw)[2]) {
   const bool hi = koff >= o.ksplit;
   const int ch = (threadIdx.x & 7) * 16;
+  const bool kin = koff + ch < o.kend;
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
-    r[s] = o.dok[s] ? *(const uint4*)((hi ? o.d_hi[s] : o.d[s]) + koff + ch) : zero4();
+  for (int q = 0; q < 4; ++q) {
+    const uint8_t* b = (hi || ((o.sel >> q) & 1u)) ? o.d[1] : o.d[0];
+    r[q] = ((o.ok >> q) & 1u) && kin ? *(const uint4*)(b + o.off[q] + koff + ch) : zero4();
+  }
+  // scale byte b of a word is block koff / 32 + b; keep the blocks below kend
+  const long nb = (o.kend - koff) / 32;
+  const uint32_t keep = nb >= 4 ? 0xffffffffu : (nb <= 0 ? 0u : (1u << (8 * nb)) - 1u);
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
-    sw[q] = o.sok[q] ? *(const uint32_t*)((hi ? o.sc_hi[q] : o.sc[q]) + koff / 32) : 0u;
+  for (int q = 0; q < 2; ++q) {
+    const uint8_t* b = (hi || ((o.sel >> (4 + q)) & 1u)) ? o.s[1] : o.s[0];
+    sw[q] = ((o.ok >> (4 + q)) & 1u) ? *(const uint32_t*)(b + o.soff[q] + koff / 32) & keep : 0u;
+  }
 }
 
 MOE_DEV void mx_store(char* t, const uint4 (&r)[4]) {
@@ -117,42 +131,29 @@ MOE_DEV void gemm_main_mx(char* lds, const MxOp& A, const MxOp& B, const KM& km,
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   if (nk <= 0) return;
-  char* buf0 = lds;
-  char* buf1 = lds + 2 * TILEB;
-  uint4 ra0[4], rb0[4], ra1[4], rb1[4];
-  uint32_t sa0[2], sb0[2], sa1[2], sb1[2], ca0[2], cb0[2], ca1[2], cb1[2];
-  mx_load(A, km(0), ra0, sa0);
-  mx_load(B, km(0), rb0, sb0);
-  if (nk > 1) {
-    mx_load(A, km(1), ra1, sa1);
-    mx_load(B, km(1), rb1, sb1);
-  }
-  mx_store(buf0, ra0);
-  mx_store(buf0 + TILEB, rb0);
-  ca0[0] = sa0[0]; ca0[1] = sa0[1]; cb0[0] = sb0[0]; cb0[1] = sb0[1];
+  // two LDS stages, one register stage: tile kt + 1 is loaded into registers
+  // while tile kt is multiplied, then stored into the other LDS stage
+  uint4 ra[4], rb[4];
+  uint32_t sa[2], sb[2], ca[2], cb[2];
+  mx_load(A, km(0), ra, sa);
+  mx_load(B, km(0), rb, sb);
+  mx_store(lds, ra);
+  mx_store(lds + TILEB, rb);
+  ca[0] = sa[0]; ca[1] = sa[1]; cb[0] = sb[0]; cb[1] = sb[1];
   __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    if (kt + 2 < nk) {
-      mx_load(A, km(kt + 2), ra0, sa0);
-      mx_load(B, km(kt + 2), rb0, sb0);
+  for (int kt = 0; kt < nk; ++kt) {
+    char* cur = lds + (kt & 1) * 2 * TILEB;
+    char* nxt = lds + ((kt + 1) & 1) * 2 * TILEB;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      mx_load(A, km(kt + 1), ra, sa);
+      mx_load(B, km(kt + 1), rb, sb);
     }
-    mma_tile_mx(buf0, buf0 + TILEB, ca0, cb0, acc, arow, brow, lane);
-    if (kt + 1 < nk) {
-      mx_store(buf1, ra1);
-      mx_store(buf1 + TILEB, rb1);
-      ca1[0] = sa1[0]; ca1[1] = sa1[1]; cb1[0] = sb1[0]; cb1[1] = sb1[1];
-    }
-    __syncthreads();
-    if (kt + 1 >= nk) break;
-    if (kt + 3 < nk) {
-      mx_load(A, km(kt + 3), ra1, sa1);
-      mx_load(B, km(kt + 3), rb1, sb1);
-    }
-    mma_tile_mx(buf1, buf1 + TILEB, ca1, cb1, acc, arow, brow, lane);
-    if (kt + 2 < nk) {
-      mx_store(buf0, ra0);
-      mx_store(buf0 + TILEB, rb0);
-      ca0[0] = sa0[0]; ca0[1] = sa0[1]; cb0[0] = sb0[0]; cb0[1] = sb0[1];
+    mma_tile_mx(cur, cur + TILEB, ca, cb, acc, arow, brow, lane);
+    if (more) {
+      mx_store(nxt, ra);
+      mx_store(nxt + TILEB, rb);
+      ca[0] = sa[0]; ca[1] = sa[1]; cb[0] = sb[0]; cb[1] = sb[1];
     }
     __syncthreads();
   }
@@ -192,21 +193,32 @@ __global__ __launch_bounds__(NTHR, 2) void k_up_swiglu_mx(
   MxOp A, B;
   mx_op_clear(A);
   mx_op_clear(B);
-  const size_t we = (size_t)t.e * I;
+  const size_t we = (size_t)t.e * I + i0;  // first weight row of this column tile
+  A.d[0] = X8;
+  A.s[0] = Xs;
+  B.d[0] = wg8 + we * H;
+  B.d[1] = wu8 + we * H;
+  B.s[0] = wgs + we * HS;
+  B.s[1] = wus + we * HS;
+  A.ok = 0;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int rr = (threadIdx.x >> 3) + 32 * s, r = t.row0 + rr;
-    A.dok[s] = r < t.row_end;
-    A.d[s] = X8 + (size_t)(A.dok[s] ? r : t.row0) * H;
-    B.d[s] = rr < 64 ? wg8 + (we + i0 + rr) * H : wu8 + (we + i0 + rr - 64) * H;
+    const bool ok = r < t.row_end;
+    A.ok |= (uint32_t)ok << s;
+    A.off[s] = (uint32_t)((ok ? r : t.row0) * H);
+    B.off[s] = (uint32_t)((rr & 63) * H);
+    B.sel |= (uint32_t)(rr >= 64) << s;
   }
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int r = t.row0 + arow + 32 * q + (lane & 31);
-    A.sok[q] = r < t.row_end;
-    A.sc[q] = Xs + (size_t)(A.sok[q] ? r : t.row0) * HS;
+    const bool ok = r < t.row_end;
+    A.ok |= (uint32_t)ok << (4 + q);
+    A.soff[q] = (uint32_t)((ok ? r : t.row0) * HS);
     const int n = brow[q] + (lane & 31);
-    B.sc[q] = n < 64 ? wgs + (we + i0 + n) * HS : wus + (we + i0 + n - 64) * HS;
+    B.soff[q] = (uint32_t)((n & 63) * HS);
+    B.sel |= (uint32_t)(n >= 64) << (4 + q);
   }
   f32x16_t acc[2][2];
   gemm_main_mx(lds, A, B, KLinear(), H / MX_BK, acc, arow, brow, lane);
@@ -250,20 +262,27 @@ __global__ __launch_bounds__(NTHR, 2) void k_down_mx(GroupInfo g, const uint8_t*
   MxOp A, B;
   mx_op_clear(A);
   mx_op_clear(B);
-  const size_t we = (size_t)t.e * H;
+  const size_t we = (size_t)t.e * H + n0;
+  A.d[0] = hq;
+  A.s[0] = hs;
+  B.d[0] = wd8 + we * I;
+  B.s[0] = wds + we * IS;
+  A.ok = 0;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int rr = (threadIdx.x >> 3) + 32 * s, r = t.row0 + rr;
-    A.dok[s] = r < t.row_end;
-    A.d[s] = hq + (size_t)(A.dok[s] ? r : t.row0) * I;
-    B.d[s] = wd8 + (we + n0 + rr) * I;
+    const bool ok = r < t.row_end;
+    A.ok |= (uint32_t)ok << s;
+    A.off[s] = (uint32_t)((ok ? r : t.row0) * I);
+    B.off[s] = (uint32_t)(rr * I);
   }
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int r = t.row0 + arow + 32 * q + (lane & 31);
-    A.sok[q] = r < t.row_end;
-    A.sc[q] = hs + (size_t)(A.sok[q] ? r : t.row0) * IS;
-    B.sc[q] = wds + (we + n0 + brow[q] + (lane & 31)) * IS;
+    const bool ok = r < t.row_end;
+    A.ok |= (uint32_t)ok << (4 + q);
+    A.soff[q] = (uint32_t)((ok ? r : t.row0) * IS);
+    B.soff[q] = (uint32_t)((brow[q] + (lane & 31)) * IS);
   }
   f32x16_t acc[2][2];
   gemm_main_mx(lds, A, B, KLinear(), I / MX_BK, acc, arow, brow, lane);
@@ -294,20 +313,27 @@ __global__ __launch_bounds__(NTHR, 2) void k_dgrad_down_mx(
   MxOp A, B;
   mx_op_clear(A);
   mx_op_clear(B);
-  const size_t we = (size_t)t.e * I;
+  const size_t we = (size_t)t.e * I + i0;
+  A.d[0] = dYu8;
+  A.s[0] = dYus;
+  B.d[0] = wdT8 + we * H;
+  B.s[0] = wdTs + we * HS;
+  A.ok = 0;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int rr = (threadIdx.x >> 3) + 32 * s, r = t.row0 + rr;
-    A.dok[s] = r < t.row_end;
-    A.d[s] = dYu8 + (size_t)(A.dok[s] ? r : t.row0) * H;
-    B.d[s] = wdT8 + (we + i0 + rr) * H;
+    const bool ok = r < t.row_end;
+    A.ok |= (uint32_t)ok << s;
+    A.off[s] = (uint32_t)((ok ? r : t.row0) * H);
+    B.off[s] = (uint32_t)(rr * H);
   }
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int r = t.row0 + arow + 32 * q + (lane & 31);
-    A.sok[q] = r < t.row_end;
-    A.sc[q] = dYus + (size_t)(A.sok[q] ? r : t.row0) * HS;
-    B.sc[q] = wdTs + (we + i0 + brow[q] + (lane & 31)) * HS;
+    const bool ok = r < t.row_end;
+    A.ok |= (uint32_t)ok << (4 + q);
+    A.soff[q] = (uint32_t)((ok ? r : t.row0) * HS);
+    B.soff[q] = (uint32_t)((brow[q] + (lane & 31)) * HS);
   }
   f32x16_t acc[2][2];
   gemm_main_mx(lds, A, B, KLinear(), H / MX_BK, acc, arow, brow, lane);
@@ -375,24 +401,30 @@ __global__ __launch_bounds__(NTHR, 2) void k_dgrad_up_mx(
   MxOp A, B;
   mx_op_clear(A);
   mx_op_clear(B);
-  const size_t we = (size_t)t.e * H;
+  const size_t we = (size_t)t.e * H + n0;
+  A.d[0] = dZ8;
+  A.s[0] = dZs;
   B.ksplit = I;
+  B.d[0] = wgT8 + we * I;
+  B.d[1] = wuT8 + we * I - I;
+  B.s[0] = wgTs + we * IS;
+  B.s[1] = wuTs + we * IS - IS;
+  A.ok = 0;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int rr = (threadIdx.x >> 3) + 32 * s, r = t.row0 + rr;
-    A.dok[s] = r < t.row_end;
-    A.d[s] = dZ8 + (size_t)(A.dok[s] ? r : t.row0) * (2 * I);
-    B.d[s] = wgT8 + (we + n0 + rr) * I;
-    B.d_hi[s] = wuT8 + (we + n0 + rr) * I - I;
+    const bool ok = r < t.row_end;
+    A.ok |= (uint32_t)ok << s;
+    A.off[s] = (uint32_t)((ok ? r : t.row0) * (2 * I));
+    B.off[s] = (uint32_t)(rr * I);
   }
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int r = t.row0 + arow + 32 * q + (lane & 31);
-    A.sok[q] = r < t.row_end;
-    A.sc[q] = dZs + (size_t)(A.sok[q] ? r : t.row0) * S2;
-    const size_t n = we + n0 + brow[q] + (lane & 31);
-    B.sc[q] = wgTs + n * IS;
-    B.sc_hi[q] = wuTs + n * IS - IS;
+    const bool ok = r < t.row_end;
+    A.ok |= (uint32_t)ok << (4 + q);
+    A.soff[q] = (uint32_t)((ok ? r : t.row0) * S2);
+    B.soff[q] = (uint32_t)((brow[q] + (lane & 31)) * IS);
   }
   f32x16_t acc[2][2];
   gemm_main_mx(lds, A, B, KLinear(), (2 * I) / MX_BK, acc, arow, brow, lane);
@@ -405,86 +437,67 @@ __global__ __launch_bounds__(NTHR, 2) void k_dgrad_up_mx(
 
 // K tiles of one expert in the tile-padded token axis of all minibatches: tile j
 // of expert e in minibatch m sits at K offset (m * max_tiles + first_m[e] + j) * 128.
-struct KMinibatch {
-  int n_mb, max_tiles;
-  int first[MX_MAX_MB], cnt[MX_MAX_MB];
-  MOE_DEV long operator()(int kt) const {
-    long base = 0;
-#pragma unroll
-    for (int m = 0; m < MX_MAX_MB; ++m) {
-      if (m < n_mb) {
-        if (kt >= 0 && kt < cnt[m]) base = ((long)m * max_tiles + first[m] + kt) * MX_BK;
-        kt -= cnt[m];
-      }
-    }
-    return base;
-  }
+// K offset (bytes) of K tile kt in an expert's region of the token axis
+struct KFrom {
+  long k0;
+  MOE_DEV long operator()(int kt) const { return k0 + (long)kt * MX_BK; }
 };
 
-MOE_DEV KMinibatch k_minibatch(const MbPlans& mp, int e, int& nk) {
-  KMinibatch km;
-  km.n_mb = mp.n_mb;
-  km.max_tiles = mp.max_tiles;
-  nk = 0;
-#pragma unroll
-  for (int m = 0; m < MX_MAX_MB; ++m) {
-    km.first[m] = 0;
-    km.cnt[m] = 0;
-    if (m < mp.n_mb) {
-      km.first[m] = mp.tile_first[m][e];
-      km.cnt[m] = mp.tile_first[m][e + 1] - km.first[m];
-      nk += km.cnt[m];
-    }
-  }
-  return km;
-}
-
-// wgrad, MX: out[e][m, n] = sum over the expert's padded token axis of
-// Q_t(A)[m, k] Q_t(B)[n, k]; A [M, Kp], B [N, Kp] (Kp = n_mb * max_tiles * 128).
-// Persistent over (expert with rows in some minibatch, output tile).  Output rows
+// wgrad, MX: out[e][m, n] = sum over the expert's columns [kpos[e], kpos[e + 1]) of
+// the token axis of Q_t(A)[m, k] Q_t(B)[n, k]; A [M, Kp], B [N, Kp] (Kp: the axis
+// length).  The last K tile's bytes past the expert's columns load as zeros.
+// One workgroup per (expert with rows in some minibatch, output tile).  Output rows
 // m < split go to out0[e], the rest to out1[e] (dW_g / dW_u); split = M for one.
 __global__ __launch_bounds__(NTHR, 2) void k_wgrad_mx(MbPlans mp, const uint8_t* __restrict__ A8,
                                                       const uint8_t* __restrict__ As,
                                                       const uint8_t* __restrict__ B8,
                                                       const uint8_t* __restrict__ Bs, int M, int N,
-                                                      int split, bf16_t* __restrict__ out0,
+                                                      int split, long Kp,
+                                                      bf16_t* __restrict__ out0,
                                                       bf16_t* __restrict__ out1) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   const int MT = M / TM, NT = N / TN, lane = threadIdx.x & 63;
-  const long Kp = (long)mp.n_mb * mp.max_tiles * MX_BK, KS = Kp / 32;
-  const int total = mp.n_active[0] * MT * NT;
+  const long KS = Kp / 32;
+  // one workgroup per item; the realised items are renumbered so that the
+  // workgroups of one XCD take a contiguous run of them
+  const int total = mp.n_active[0] * MT * NT, id = blockIdx.x;
+  if (id >= total) return;
+  const int q8 = total / N_XCD, rem8 = total % N_XCD, x = id % N_XCD, local = id / N_XCD;
+  const int w = x < rem8 ? x * (q8 + 1) + local : rem8 * (q8 + 1) + (x - rem8) * q8 + local;
   int arow, brow[2];
   wave_coords(arow, brow, false);
-  for (int w = blockIdx.x; w < total; w += gridDim.x) {
-    const int a = w / (MT * NT), rem = w - a * (MT * NT);
-    const int e = mp.active[a], mt = rem / NT, m0 = mt * TM, n0 = (rem - mt * NT) * TN;
-    int nk;
-    const KMinibatch km = k_minibatch(mp, e, nk);
-    MxOp oa, ob;
-    mx_op_clear(oa);
-    mx_op_clear(ob);
+  const int a = w / (MT * NT), rem = w - a * (MT * NT);
+  const int e = mp.active[a], mt = rem / NT, m0 = mt * TM, n0 = (rem - mt * NT) * TN;
+  const KFrom km{mp.kpos[e]};
+  const long kend = mp.kpos[e + 1];
+  const int nk = (int)((kend - km.k0 + MX_BK - 1) / MX_BK);
+  MxOp oa, ob;
+  mx_op_clear(oa);
+  mx_op_clear(ob);
+  oa.kend = ob.kend = kend;
+  oa.d[0] = A8 + (size_t)m0 * Kp;
+  ob.d[0] = B8 + (size_t)n0 * Kp;
+  oa.s[0] = As + (size_t)m0 * KS;
+  ob.s[0] = Bs + (size_t)n0 * KS;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int rr = (threadIdx.x >> 3) + 32 * s;
-      oa.d[s] = A8 + (size_t)(m0 + rr) * Kp;
-      ob.d[s] = B8 + (size_t)(n0 + rr) * Kp;
-    }
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      oa.sc[q] = As + (size_t)(m0 + arow + 32 * q + (lane & 31)) * KS;
-      ob.sc[q] = Bs + (size_t)(n0 + brow[q] + (lane & 31)) * KS;
-    }
-    f32x16_t acc[2][2];
-    gemm_main_mx(lds, oa, ob, km, nk, acc, arow, brow, lane);
-    float* C = (float*)lds;
-    stage_acc(C, acc, arow, brow, lane);
-    __syncthreads();
-    bf16_t* base = (m0 < split ? out0 + (size_t)e * split * N + (size_t)m0 * N
-                               : out1 + (size_t)e * (M - split) * N + (size_t)(m0 - split) * N) + n0;
-    auto out = [&](int r) { return base + (size_t)r * N; };
-    epi_store<bf16_t>(C, out, TM);
-    __syncthreads();
+  for (int s = 0; s < 4; ++s) {
+    const int rr = (threadIdx.x >> 3) + 32 * s;
+    oa.off[s] = ob.off[s] = (uint32_t)(rr * Kp);
   }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    oa.soff[q] = (uint32_t)((arow + 32 * q + (lane & 31)) * KS);
+    ob.soff[q] = (uint32_t)((brow[q] + (lane & 31)) * KS);
+  }
+  f32x16_t acc[2][2];
+  gemm_main_mx(lds, oa, ob, km, nk, acc, arow, brow, lane);
+  float* C = (float*)lds;
+  stage_acc(C, acc, arow, brow, lane);
+  __syncthreads();
+  bf16_t* base = (m0 < split ? out0 + (size_t)e * split * N + (size_t)m0 * N
+                             : out1 + (size_t)e * (M - split) * N + (size_t)(m0 - split) * N) + n0;
+  auto out = [&](int r) { return base + (size_t)r * N; };
+  epi_store<bf16_t>(C, out, TM);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -533,10 +546,10 @@ hipError_t launch_mx_dgrad_up(const GroupInfo& g, const uint8_t* dZ8, const uint
 
 hipError_t launch_mx_wgrad(const char* name, const MbPlans& mp, int E, const uint8_t* A8,
                            const uint8_t* As, const uint8_t* B8, const uint8_t* Bs, int M, int N,
-                           int split, void* out0, void* out1, hipStream_t s) {
-  const unsigned grid = persistent_grid((long)E * (M / TM) * (N / TN));
+                           int split, size_t Kp, void* out0, void* out1, hipStream_t s) {
+  const unsigned grid = (unsigned)E * (M / TM) * (N / TN);  // bound on the realised items
   return MOE_LAUNCH(name, s,
-                    k_wgrad_mx<<<grid, NTHR, 0, s>>>(mp, A8, As, B8, Bs, M, N, split,
+                    k_wgrad_mx<<<grid, NTHR, 0, s>>>(mp, A8, As, B8, Bs, M, N, split, (long)Kp,
                                                      (bf16_t*)out0, (bf16_t*)out1));
 }
 

@@ -133,26 +133,33 @@ hipError_t launch_quant_rows(int dt, const void* src, const int32_t* gather,
 // Column quantisation of batch x [rows, cols] into batch x [cols, rows] (blocks along rows).
 hipError_t launch_quant_cols(int dt, const void* src, int batch, int rows, int cols, uint8_t* q,
                              uint8_t* sc, hipStream_t s);
-// Token quantisation of plan tiles into the transposed, tile-padded token axis
-// (dt 1: bf16 source, 0: fp32 source).
+// Token quantisation of one minibatch's plan tiles into the transposed token axis
+// of the wgrads (dt 1: bf16 source, 0: fp32 source).  Expert e's rows of this
+// minibatch go to columns kpos[e] + kseg[e] + (row - offsets[e]), in blocks of 32
+// rows from the segment's first row (the last block zero-padded); blocks without a
+// row are not written.  kpad_total: the axis length (row pitch of q).
 hipError_t launch_quant_tokens(int dt, const void* src, const int32_t* gather, int ld,
                                const int32_t* tiles, const int32_t* n_tiles,
-                               const int32_t* offsets, int max_tiles, int cols,
-                               size_t kpad_total, size_t kofs, uint8_t* q, uint8_t* sc,
-                               hipStream_t s);
+                               const int32_t* offsets, const int32_t* kpos,
+                               const int32_t* kseg, int max_tiles, int cols, size_t kpad_total,
+                               uint8_t* q, uint8_t* sc, hipStream_t s);
 
-// Tile lists of the minibatch plans, for the wgrads that span all of them.
+// The wgrads' token axis over all minibatches: expert e owns columns
+// [kpos[e], kpos[e + 1]), its minibatch segments one after the other, each padded to
+// a multiple of 32 rows.
 struct MbPlans {
-  const int32_t* tile_first[MX_MAX_MB];
-  int n_mb, max_tiles;
+  int n_mb;
+  const int32_t* kpos;       // [E + 1]
   const int32_t* active;     // union over minibatches of the experts with rows
   const int32_t* n_active;
 };
 
 // counts_all[e] = sum over minibatch plans of counts[e]; active / n_active list the
-// experts with counts_all > 0 in ascending order.
+// experts with counts_all > 0 in ascending order; kseg[m * E + e] = sum over m' < m of
+// pad32(counts_m'[e]) and kpos = exclusive prefix over e of sum_m pad32(counts_m[e]).
 hipError_t launch_mb_union(const int32_t* const* counts, int n_mb, int E, int32_t* counts_all,
-                           int32_t* active, int32_t* n_active, hipStream_t s);
+                           int32_t* active, int32_t* n_active, int32_t* kseg, int32_t* kpos,
+                           hipStream_t s);
 
 hipError_t launch_mx_up_swiglu(const GroupInfo& g, const uint8_t* X8, const uint8_t* Xs,
                                const uint8_t* wg8, const uint8_t* wgs, const uint8_t* wu8,
@@ -170,6 +177,6 @@ hipError_t launch_mx_dgrad_up(const GroupInfo& g, const uint8_t* dZ8, const uint
                               const uint8_t* wuTs, int H, int I, void* dX, hipStream_t s);
 hipError_t launch_mx_wgrad(const char* name, const MbPlans& mp, int E, const uint8_t* A8,
                            const uint8_t* As, const uint8_t* B8, const uint8_t* Bs, int M, int N,
-                           int split, void* out0, void* out1, hipStream_t s);
+                           int split, size_t Kp, void* out0, void* out1, hipStream_t s);
 
 }  // namespace moe

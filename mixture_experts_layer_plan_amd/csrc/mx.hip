@@ -13,8 +13,8 @@
 // Kernels here: row quantisation (blocks along the contiguous axis, optionally
 // pulling rows through the plan's src_token list: the MX dispatch), column
 // quantisation with a transposed output (weights blocked along their outer
-// axis), and token quantisation (blocks of 32 rows inside each 128-row tile of
-// the plan, written transposed for the wgrad GEMMs).
+// axis), and token quantisation (blocks of 32 rows from each expert segment's
+// first row, written transposed for the wgrad GEMMs).
 #include "common.hpp"
 #include "internal.hpp"
 #include "mx_common.hpp"
@@ -82,16 +82,20 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const T* __restrict__ s
 
 // ------------------------------------------------------------- tokens
 // For plan tile t (expert e, rows row0 .. row_end-1, at most 128) and column c:
-// blocks of 32 rows from row0; the output is transposed into the tile-padded token
-// axis: q[c, kofs + 128 t + j] for local row j (rows past row_end are zero), with
-// scales s[c, (kofs + 128 t) / 32 + j / 32].  src rows are pulled through gather
-// when given.  One workgroup per (tile, 64 columns).
+// blocks of 32 rows from row0 (a multiple of 32 rows after the segment's first row,
+// so the blocks start at the segment's first row); the output is transposed into
+// the wgrads' token axis: q[c, kbase + j] for local row j with
+// kbase = kpos[e] + kseg[e] + (row0 - offsets[e]) (rows past row_end inside a block
+// are zero), scales s[c, kbase / 32 + j / 32].  Blocks without a row are not
+// written: those columns belong to the next segment.  src rows are pulled through
+// gather when given.  One workgroup per (tile, 64 columns).
 template <typename T>
 __global__ __launch_bounds__(256) void quant_tokens_kernel(
     const T* __restrict__ src, const int32_t* __restrict__ gather, int ld,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
-    const int32_t* __restrict__ offsets, int cols, size_t kpad_total, size_t kofs,
-    uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ kpos,
+    const int32_t* __restrict__ kseg, int cols, size_t kpad_total, uint8_t* __restrict__ q,
+    uint8_t* __restrict__ sc) {
   __shared__ float tile[128][65];
   const int t = blockIdx.x, c0 = blockIdx.y * 64;
   if (t >= n_tiles[0]) return;
@@ -104,13 +108,14 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
   }
   __syncthreads();
   const int cc = threadIdx.x & 63, blk = threadIdx.x >> 6;
+  if (row0 + 32 * blk >= row_end) return;  // no row in this block
   float v[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) v[i] = tile[32 * blk + i][cc];
   const int X = mx_scale_exp(v);
   uint4 lo, hi;
   mx_encode32(v, X, lo, hi);
-  const size_t k = kofs + (size_t)128 * t + 32 * blk;
+  const size_t k = (size_t)kpos[e] + kseg[e] + (row0 - offsets[e]) + 32 * blk;
   uint4* qd = (uint4*)(q + (size_t)(c0 + cc) * kpad_total + k);
   qd[0] = lo;
   qd[1] = hi;
@@ -147,20 +152,20 @@ hipError_t launch_quant_cols(int dt, const void* src, int batch, int rows, int c
 
 hipError_t launch_quant_tokens(int dt, const void* src, const int32_t* gather, int ld,
                                const int32_t* tiles, const int32_t* n_tiles,
-                               const int32_t* offsets, int max_tiles, int cols,
-                               size_t kpad_total, size_t kofs, uint8_t* q, uint8_t* sc,
-                               hipStream_t s) {
+                               const int32_t* offsets, const int32_t* kpos,
+                               const int32_t* kseg, int max_tiles, int cols, size_t kpad_total,
+                               uint8_t* q, uint8_t* sc, hipStream_t s) {
   if (max_tiles == 0) return hipSuccess;
   const dim3 grid(max_tiles, cols / 64);
   if (dt)
     return MOE_LAUNCH("mx_quant_tokens", s,
                       quant_tokens_kernel<bf16_t><<<grid, 256, 0, s>>>(
-                          (const bf16_t*)src, gather, ld, tiles, n_tiles, offsets, cols,
-                          kpad_total, kofs, q, sc));
+                          (const bf16_t*)src, gather, ld, tiles, n_tiles, offsets, kpos, kseg,
+                          cols, kpad_total, q, sc));
   return MOE_LAUNCH("mx_quant_tokens", s,
                     quant_tokens_kernel<float><<<grid, 256, 0, s>>>(
-                        (const float*)src, gather, ld, tiles, n_tiles, offsets, cols, kpad_total,
-                        kofs, q, sc));
+                        (const float*)src, gather, ld, tiles, n_tiles, offsets, kpos, kseg, cols,
+                        kpad_total, q, sc));
 }
 
 }  // namespace moe

@@ -219,42 +219,56 @@ hipError_t launch_plan(const int32_t* topk_idx, int T, int k, int E, const PlanP
 
 namespace moe {
 
-// Union of the minibatch plans' expert lists (one workgroup of 1024 threads).
+// Union of the minibatch plans' expert lists and the wgrads' token-axis offsets
+// (one workgroup of 1024 threads; thread e owns expert e).
 __global__ __launch_bounds__(1024) void mb_union_kernel(MbCounts mc, int E,
                                                         int32_t* __restrict__ counts_all,
                                                         int32_t* __restrict__ active,
-                                                        int32_t* __restrict__ n_active) {
-  __shared__ int32_t s_wave[16];
+                                                        int32_t* __restrict__ n_active,
+                                                        int32_t* __restrict__ kseg,
+                                                        int32_t* __restrict__ kpos) {
+  __shared__ int32_t s_wave[2][16];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int n = 0;
+  int n = 0, len = 0;
   if (tid < E)
-    for (int m = 0; m < mc.n_mb; ++m) n += mc.counts[m][tid];
+    for (int m = 0; m < mc.n_mb; ++m) {
+      const int c = mc.counts[m][tid];
+      kseg[m * E + tid] = len;
+      n += c;
+      len += (c + 31) & ~31;
+    }
   const int act = n > 0 ? 1 : 0;
-  int c = act;
+  int c = act, p = len;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(c, o, 64);
-    if (lane >= o) c += u;
+    const int u = __shfl_up(c, o, 64), v = __shfl_up(p, o, 64);
+    if (lane >= o) { c += u; p += v; }
   }
-  if (lane == 63) s_wave[wv] = c;
+  if (lane == 63) { s_wave[0][wv] = c; s_wave[1][wv] = p; }
   __syncthreads();
-  int base = 0;
-  for (int i = 0; i < wv; ++i) base += s_wave[i];
+  int base = 0, pbase = 0;
+  for (int i = 0; i < wv; ++i) { base += s_wave[0][i]; pbase += s_wave[1][i]; }
   const int excl = base + c - act;
   if (tid < E) {
     counts_all[tid] = n;
     if (act) active[excl] = tid;
+    kpos[tid] = pbase + p - len;
   }
-  if (tid == E - 1) n_active[0] = excl + act;
+  if (tid == E - 1) {
+    n_active[0] = excl + act;
+    kpos[E] = pbase + p;
+  }
 }
 
 hipError_t launch_mb_union(const int32_t* const* counts, int n_mb, int E, int32_t* counts_all,
-                           int32_t* active, int32_t* n_active, hipStream_t s) {
+                           int32_t* active, int32_t* n_active, int32_t* kseg, int32_t* kpos,
+                           hipStream_t s) {
   MbCounts mc;
   mc.n_mb = n_mb;
   for (int m = 0; m < MX_MAX_MB; ++m) mc.counts[m] = m < n_mb ? counts[m] : nullptr;
   return MOE_LAUNCH("mb_union", s,
-                    mb_union_kernel<<<1, 1024, 0, s>>>(mc, E, counts_all, active, n_active));
+                    mb_union_kernel<<<1, 1024, 0, s>>>(mc, E, counts_all, active, n_active,
+                                                       kseg, kpos));
 }
 
 }  // namespace moe
