@@ -319,7 +319,7 @@ struct Tile {
 
 // Rows-grouped launches: a 1-D grid over (256-row tile, column tile) pairs,
 // renumbered so that the workgroups of one XCD (ids x, x + 8, ...) take a
-// contiguous run of pairs, column tile fastest (as in gemm_common.hpp).
+// contiguous run of pairs ordered by group_rows in groups of 4 row tiles.
 MOE_DEV bool row_tile(const GroupInfo& g, int nt_count, Tile& t, int& nt) {
   const int n_row_tiles = g.wtiles ? g.n_wtiles[0] : (g.dense_rows + TILE - 1) / TILE;
   const int total = n_row_tiles * nt_count;
@@ -327,8 +327,8 @@ MOE_DEV bool row_tile(const GroupInfo& g, int nt_count, Tile& t, int& nt) {
   if (id >= total) return false;
   const int per = total / N_XCD, rem = total % N_XCD, x = id % N_XCD, local = id / N_XCD;
   const int L = x < rem ? x * (per + 1) + local : rem * (per + 1) + (x - rem) * per + local;
-  const int mt = L / nt_count;
-  nt = L - mt * nt_count;
+  int mt;
+  group_rows(g.wtiles, g.offsets, g.dense_rows, TILE, nt_count, 4, L, mt, nt);  // 32 per XCD
   if (g.wtiles) {
     t.e = g.wtiles[2 * mt];
     t.row0 = g.wtiles[2 * mt + 1];

@@ -334,11 +334,47 @@ struct RowTile {
 
 constexpr int N_XCD = 8;  // MI355X: workgroup i is dispatched to XCD i mod 8
 
+// Wave-uniform read of plan data that no kernel of this launch writes, through the
+// constant address space so that it compiles to a scalar load (lgkmcnt).  A vector
+// load here would make its wait vmcnt(0), which also waits for every global store
+// of the previous work item of a persistent loop.
+MOE_DEV int32_t ld_uniform(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
+// Pair L of a rows-grouped launch -> (row tile mt, column tile nt).  The row tiles
+// of one expert (contiguous and in row order in the plan's tile list; the dense
+// launch is one "expert") are taken in groups of up to G, and inside a group the
+// column tile is outer and the row tile inner.  The workgroups an XCD runs at one
+// time (a window of consecutive pairs) then form a G x (window / G) block: each
+// weight panel is fetched into that XCD's L2 once per group of row tiles instead
+// of once per row tile, and each row tile once per window / G column tiles.
+MOE_DEV void group_rows(const int32_t* tiles, const int32_t* offsets, int dense_rows, int tile_m,
+                        int nt_count, int G, int L, int& mt, int& nt) {
+  const int mt0 = L / nt_count;
+  int i, m_e;
+  if (tiles) {
+    const int e = ld_uniform(tiles + 2 * mt0), row0 = ld_uniform(tiles + 2 * mt0 + 1);
+    const int s0 = ld_uniform(offsets + e), s1 = ld_uniform(offsets + e + 1);
+    i = (row0 - s0) / tile_m;
+    m_e = (s1 - s0 + tile_m - 1) / tile_m;
+  } else {
+    i = mt0;
+    m_e = (dense_rows + tile_m - 1) / tile_m;
+  }
+  const int gf = mt0 - i % G, gsz = min(G, m_e - (i - i % G));
+  const int j = L - gf * nt_count;
+  nt = j / gsz;
+  mt = gf + (j - nt * gsz);
+}
+
+constexpr int ROW_GROUP = 8;  // 64 workgroups per XCD at a time: 8 x 8 blocks
+
 // Rows-grouped launches use a 1-D grid over (row tile, column tile) pairs.  The
 // pairs that exist (n_tiles of the plan x nt_count) are renumbered so that the
 // workgroups one XCD receives (ids x, x + 8, x + 16, ...) cover a contiguous run
-// of pairs with the column tile fastest: a row tile's activations and an expert's
-// weight columns are then fetched into that XCD's L2 once, not once per XCD.
+// of pairs, ordered by group_rows: a row tile's activations and an expert's weight
+// columns are then fetched into that XCD's L2, not into every XCD's.
 // Returns false for workgroups past the last pair.
 MOE_DEV bool rows_tile(const GroupInfo& g, int nt_count, RowTile& t, int& nt) {
   const int n_row_tiles = g.tiles ? g.n_tiles[0] : (g.dense_rows + TM - 1) / TM;
@@ -347,8 +383,8 @@ MOE_DEV bool rows_tile(const GroupInfo& g, int nt_count, RowTile& t, int& nt) {
   if (id >= total) return false;
   const int per = total / N_XCD, rem = total % N_XCD, x = id % N_XCD, local = id / N_XCD;
   const int L = x < rem ? x * (per + 1) + local : rem * (per + 1) + (x - rem) * per + local;
-  const int mt = L / nt_count;
-  nt = L - mt * nt_count;
+  int mt;
+  group_rows(g.tiles, g.offsets, g.dense_rows, TM, nt_count, ROW_GROUP, L, mt, nt);
   if (g.tiles) {
     t.e = g.tiles[2 * mt];
     t.row0 = g.tiles[2 * mt + 1];
@@ -411,8 +447,8 @@ struct KRowSeg {
 
 MOE_DEV void k_segment(const GroupInfo& g, int e, int& seg0, int& seg1) {
   if (g.offsets) {
-    seg0 = g.offsets[e];
-    seg1 = g.offsets[e + 1];
+    seg0 = ld_uniform(g.offsets + e);
+    seg1 = ld_uniform(g.offsets + e + 1);
   } else {
     seg0 = 0;
     seg1 = g.dense_rows;
@@ -442,7 +478,7 @@ MOE_DEV int k_work_items(const GroupInfo& g, int mt_count, int nt_count) {
   return (g.offsets ? g.E : 1) * mt_count * nt_count;
 }
 
-MOE_DEV bool k_empty(const GroupInfo& g, int e) { return g.counts && g.counts[e] == 0; }
+MOE_DEV bool k_empty(const GroupInfo& g, int e) { return g.counts && ld_uniform(g.counts + e) == 0; }
 
 // Zero a TM x TN tile of T at out (row stride ld elements) with 16-byte
 // non-temporal stores.
