@@ -34,28 +34,46 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restric
 
 // y[t, :] = round( sum_j w[t, j] * Y[pos[t, j], :] + shared[t, :] ), fp32 from zero,
 // j ascending, shared last.  WEIGHTED = false sums with weight 1 (reverse-dispatch).
+// One 128-thread workgroup per (token, slice of 128 16-byte chunks); each thread
+// issues the loads of up to 8 slots and of the shared row together, then adds them
+// in slot order.
+constexpr int CMB_THREADS = 128;
 template <bool WEIGHTED>
-__global__ __launch_bounds__(256) void combine_bf16_kernel(const uint4* __restrict__ Y,
-                                                           const int32_t* __restrict__ pos,
-                                                           const float* __restrict__ w,
-                                                           const uint4* __restrict__ shared,
-                                                           uint4* __restrict__ y, int k,
-                                                           int row_chunks) {
-  const int t = blockIdx.x;
-  __shared__ int s_pos[MOE_MAX_K];
-  __shared__ float s_w[MOE_MAX_K];
-  if (threadIdx.x < k) {
-    s_pos[threadIdx.x] = pos[(size_t)t * k + threadIdx.x];
-    s_w[threadIdx.x] = WEIGHTED ? w[(size_t)t * k + threadIdx.x] : 1.0f;
-  }
-  __syncthreads();
-  for (int c = threadIdx.x; c < row_chunks; c += 256) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int r = s_pos[j];
-      if (r < 0) continue;
+__global__ __launch_bounds__(CMB_THREADS) void combine_bf16_kernel(
+    const uint4* __restrict__ Y, const int32_t* __restrict__ pos, const float* __restrict__ w,
+    const uint4* __restrict__ shared, uint4* __restrict__ y, int k, int row_chunks, int slices) {
+  const int t = blockIdx.x / slices;
+  const int c = (blockIdx.x - t * slices) * CMB_THREADS + threadIdx.x;
+  if (c >= row_chunks) return;
+  // the token's slots and weights: wave-uniform reads of data no kernel of this
+  // launch writes, through the constant address space (scalar loads)
+  typedef const __attribute__((address_space(4))) int32_t* cpos_t;
+  typedef const __attribute__((address_space(4))) float* cw_t;
+  const cpos_t s_pos = (cpos_t)(pos + (size_t)t * k);
+  const cw_t s_w = WEIGHTED ? (cw_t)(w + (size_t)t * k) : nullptr;
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    const bool last = j0 + 8 >= k;
+    int rr[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) rr[jj] = s_pos[min(j0 + jj, k - 1)];  // issued together
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+      if (j0 + jj >= k) rr[jj] = -1;
+    uint4 raw[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)  // each Y row is read once: bypass-friendly loads
+      raw[jj] = rr[jj] >= 0 ? __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                                  (const u32x4_t*)(Y + (size_t)rr[jj] * row_chunks + c)))
+                            : z;
+    const uint4 sh = shared && last ? shared[(size_t)t * row_chunks + c] : z;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = j0 + jj;
+      if (rr[jj] < 0) continue;
       float v[8];
-      unpack8(Y[(size_t)r * row_chunks + c], v);
+      unpack8(raw[jj], v);
       if (WEIGHTED) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = fmaf(s_w[j], v[i], acc[i]);
@@ -64,14 +82,21 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint4* __restri
         for (int i = 0; i < 8; ++i) acc[i] += v[i];
       }
     }
-    if (shared) {
+    if (shared && last) {
       float v[8];
-      unpack8(shared[(size_t)t * row_chunks + c], v);
+      unpack8(sh, v);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += v[i];
     }
-    y[(size_t)t * row_chunks + c] = pack8(acc);
   }
+  if (shared && k == 0) {
+    float v[8];
+    unpack8(shared[(size_t)t * row_chunks + c], v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += v[i];
+  }
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, pack8(acc)),
+                              (u32x4_t*)(y + (size_t)t * row_chunks + c));
 }
 
 template <bool WEIGHTED>
@@ -134,13 +159,18 @@ hipError_t launch_gather_rows(const void* src, void* dst, const int32_t* src_tok
 hipError_t launch_combine_bf16(const void* Y, const int32_t* pos, const float* w,
                                const void* shared, void* y, int T, int k, int H, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  const int chunks = H / 8, slices = (chunks + CMB_THREADS - 1) / CMB_THREADS;
+  if ((long)T * slices > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  const unsigned grid = (unsigned)((long)T * slices);
   if (w)
     return MOE_LAUNCH("combine_bf16", s,
-                      combine_bf16_kernel<true><<<T, 256, 0, s>>>(
-                          (const uint4*)Y, pos, w, (const uint4*)shared, (uint4*)y, k, H / 8));
+                      combine_bf16_kernel<true><<<grid, CMB_THREADS, 0, s>>>(
+                          (const uint4*)Y, pos, w, (const uint4*)shared, (uint4*)y, k, chunks,
+                          slices));
   return MOE_LAUNCH("reverse_dispatch_bf16", s,
-                    combine_bf16_kernel<false><<<T, 256, 0, s>>>(
-                        (const uint4*)Y, pos, nullptr, (const uint4*)shared, (uint4*)y, k, H / 8));
+                    combine_bf16_kernel<false><<<grid, CMB_THREADS, 0, s>>>(
+                        (const uint4*)Y, pos, nullptr, (const uint4*)shared, (uint4*)y, k, chunks,
+                        slices));
 }
 
 hipError_t launch_combine_f32(const float* Y, const int32_t* pos, const float* w,

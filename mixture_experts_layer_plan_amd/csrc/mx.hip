@@ -88,7 +88,10 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const T* __restrict__ s
 // kbase = kpos[e] + kseg[e] + (row0 - offsets[e]) (rows past row_end inside a block
 // are zero), scales s[c, kbase / 32 + j / 32].  Blocks without a row are not
 // written: those columns belong to the next segment.  src rows are pulled through
-// gather when given.  One workgroup per (tile, 64 columns).
+// gather when given.  One workgroup per (tile, 64 columns): 16-byte row loads into
+// an fp32 LDS tile, one thread per (column, block) for the scale and the codes,
+// which are staged in LDS as [column][row] so that 8 lanes store each column's
+// 128 codes as one contiguous run.
 template <typename T>
 __global__ __launch_bounds__(256) void quant_tokens_kernel(
     const T* __restrict__ src, const int32_t* __restrict__ gather, int ld,
@@ -96,30 +99,54 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ kpos,
     const int32_t* __restrict__ kseg, int cols, size_t kpad_total, uint8_t* __restrict__ q,
     uint8_t* __restrict__ sc) {
+  constexpr int VEC = 16 / (int)sizeof(T), VPR = 64 / VEC;  // elements per load, loads per row
+  constexpr int CROW = 128 + 16;  // bytes per staged column (padded against bank conflicts)
   __shared__ float tile[128][65];
+  __shared__ __attribute__((aligned(16))) uint8_t codes[64 * CROW];
   const int t = blockIdx.x, c0 = blockIdx.y * 64;
   if (t >= n_tiles[0]) return;
   const int e = tiles[2 * t], row0 = tiles[2 * t + 1];
-  const int row_end = min(row0 + 128, offsets[e + 1]);
-  for (int i = threadIdx.x; i < 128 * 64; i += 256) {
-    const int j = i / 64, cc = i % 64;
-    const int r = row0 + j;
-    tile[j][cc] = (r < row_end) ? to_f32(src[(size_t)(gather ? gather[r] : r) * ld + c0 + cc]) : 0.0f;
+  const int nrows = min(row0 + 128, offsets[e + 1]) - row0;
+  for (int i = threadIdx.x; i < 128 * VPR; i += 256) {
+    const int j = i / VPR, v = i - j * VPR;
+    float f[VEC];
+    if (j < nrows) {
+      const int r = row0 + j;
+      const uint4 raw = *(const uint4*)(src + (size_t)(gather ? gather[r] : r) * ld + c0 + v * VEC);
+      if constexpr (sizeof(T) == 2) {
+        unpack8(raw, f);
+      } else {
+        f[0] = __uint_as_float(raw.x); f[1] = __uint_as_float(raw.y);
+        f[2] = __uint_as_float(raw.z); f[3] = __uint_as_float(raw.w);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < VEC; ++u) f[u] = 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < VEC; ++u) tile[j][v * VEC + u] = f[u];
   }
   __syncthreads();
   const int cc = threadIdx.x & 63, blk = threadIdx.x >> 6;
-  if (row0 + 32 * blk >= row_end) return;  // no row in this block
-  float v[32];
+  const size_t kbase = (size_t)kpos[e] + kseg[e] + (row0 - offsets[e]);
+  if (32 * blk < nrows) {
+    float v[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = tile[32 * blk + i][cc];
-  const int X = mx_scale_exp(v);
-  uint4 lo, hi;
-  mx_encode32(v, X, lo, hi);
-  const size_t k = (size_t)kpos[e] + kseg[e] + (row0 - offsets[e]) + 32 * blk;
-  uint4* qd = (uint4*)(q + (size_t)(c0 + cc) * kpad_total + k);
-  qd[0] = lo;
-  qd[1] = hi;
-  sc[(size_t)(c0 + cc) * (kpad_total / 32) + k / 32] = (uint8_t)(X + 127);
+    for (int i = 0; i < 32; ++i) v[i] = tile[32 * blk + i][cc];
+    const int X = mx_scale_exp(v);
+    uint4 lo, hi;
+    mx_encode32(v, X, lo, hi);
+    *(uint4*)(codes + cc * CROW + 32 * blk) = lo;
+    *(uint4*)(codes + cc * CROW + 32 * blk + 16) = hi;
+    sc[(size_t)(c0 + cc) * (kpad_total / 32) + kbase / 32 + blk] = (uint8_t)(X + 127);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
+    const int col = i >> 3, ch = i & 7;
+    if (16 * ch >= ((nrows + 31) & ~31)) continue;  // 16-byte chunk of a block without rows
+    *(uint4*)(q + (size_t)(c0 + col) * kpad_total + kbase + 16 * ch) =
+        *(const uint4*)(codes + col * CROW + 16 * ch);
+  }
 }
 
 // ----------------------------------------------------------- launchers
