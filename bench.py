@@ -96,9 +96,9 @@ def kernel_work(name, sh, counts_mb, es=2):
             + Rm * 2 * I * q + Rm * (I // 128) * 4, 2 * Rm * H * I)),
         "mx_gemm_dgrad_up": lambda: over_mb(lambda Rm, Etm, tm: (
             Etm * 2 * I * H * q + Rm * 2 * I * q + Rm * H * 2, 2 * Rm * 2 * I * H)),
-        "mx_gemm_wgrad_down": lambda: (int(R * (H + I) * q + Et * H * I * 2), 2 * R * H * I),
-        "mx_gemm_wgrad_up": lambda: (int(R * (2 * I + H) * q + Et * 2 * I * H * 2), 2 * R * 2 * I * H),
-        "zero_empty_experts": lambda: ((E - Et) * 3 * I * H * es, 0),
+        # the MX wgrads also store the zero gradients of the E - Et experts without rows
+        "mx_gemm_wgrad_down": lambda: (int(R * (H + I) * q + E * H * I * 2), 2 * R * H * I),
+        "mx_gemm_wgrad_up": lambda: (int(R * (2 * I + H) * q + E * 2 * I * H * 2), 2 * R * 2 * I * H),
     }
     f = w.get(name)
     return f() if f else (0, 0)

@@ -634,11 +634,7 @@ moe_status backward_mx_impl(const moe_shape* s, const void* plan, const void* x,
                                 dxs ? (const bf16_t_host*)dxs + tok0 * H : nullptr,
                                 (bf16_t_host*)dx + tok0 * H, T_m, k, H, st));
   }
-  {
-    void* bufs[3] = {dwg, dwu, dwd};
-    const size_t stride[3] = {(size_t)I * H * 2, (size_t)I * H * 2, (size_t)H * I * 2};
-    MOE_TRY(launch_zero_empty_experts(counts_all, s->E, bufs, stride, st));
-  }
+  // the wgrads also store the zero gradients of experts without rows
   MOE_TRY(launch_mx_wgrad("mx_gemm_wgrad_down", mp, s->E, at<uint8_t>(ws, W.dYuT8),
                           at<uint8_t>(ws, W.dYuTs), at<uint8_t>(ws, W.ghT8),
                           at<uint8_t>(ws, W.ghTs), H, I, H, W.Kp, dwd, nullptr, st));

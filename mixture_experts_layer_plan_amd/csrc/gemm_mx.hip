@@ -446,9 +446,11 @@ struct KFrom {
 // wgrad, MX: out[e][m, n] = sum over the expert's columns [kpos[e], kpos[e + 1]) of
 // the token axis of Q_t(A)[m, k] Q_t(B)[n, k]; A [M, Kp], B [N, Kp] (Kp: the axis
 // length).  The last K tile's bytes past the expert's columns load as zeros.
-// One workgroup per (expert with rows in some minibatch, output tile).  Output rows
-// m < split go to out0[e], the rest to out1[e] (dW_g / dW_u); split = M for one.
-__global__ __launch_bounds__(NTHR, 2) void k_wgrad_mx(MbPlans mp, const uint8_t* __restrict__ A8,
+// One workgroup per (expert, output tile); experts without rows in any minibatch
+// get zero tiles.  Output rows m < split go to out0[e], the rest to out1[e] (dW_g /
+// dW_u); split = M for one.
+__global__ __launch_bounds__(NTHR, 2) void k_wgrad_mx(MbPlans mp, int E,
+                                                      const uint8_t* __restrict__ A8,
                                                       const uint8_t* __restrict__ As,
                                                       const uint8_t* __restrict__ B8,
                                                       const uint8_t* __restrict__ Bs, int M, int N,
@@ -458,18 +460,23 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_mx(MbPlans mp, const uint8_t*
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   const int MT = M / TM, NT = N / TN, lane = threadIdx.x & 63;
   const long KS = Kp / 32;
-  // one workgroup per item; the realised items are renumbered so that the
-  // workgroups of one XCD take a contiguous run of them
-  const int total = mp.n_active[0] * MT * NT, id = blockIdx.x;
-  if (id >= total) return;
-  const int q8 = total / N_XCD, rem8 = total % N_XCD, x = id % N_XCD, local = id / N_XCD;
-  const int w = x < rem8 ? x * (q8 + 1) + local : rem8 * (q8 + 1) + (x - rem8) * q8 + local;
+  // one workgroup per (expert, tile) over all E experts, in id order and spread over
+  // the XCDs round-robin; the tiles of an expert with no row in any minibatch (an
+  // empty run of the token axis) are stored as zeros
+  const int id = blockIdx.x;
+  if (id >= E * MT * NT) return;
   int arow, brow[2];
   wave_coords(arow, brow, false);
-  const int a = w / (MT * NT), rem = w - a * (MT * NT);
-  const int e = mp.active[a], mt = rem / NT, m0 = mt * TM, n0 = (rem - mt * NT) * TN;
-  const KFrom km{mp.kpos[e]};
-  const long kend = mp.kpos[e + 1];
+  const int e = id / (MT * NT), rem = id - e * (MT * NT);
+  const int mt = rem / NT, m0 = mt * TM, n0 = (rem - mt * NT) * TN;
+  bf16_t* base = (m0 < split ? out0 + (size_t)e * split * N + (size_t)m0 * N
+                             : out1 + (size_t)e * (M - split) * N + (size_t)(m0 - split) * N) + n0;
+  if (ld_uniform(mp.kpos + e + 1) == ld_uniform(mp.kpos + e)) {
+    zero_tile<bf16_t>(base, (size_t)N);
+    return;
+  }
+  const KFrom km{ld_uniform(mp.kpos + e)};
+  const long kend = ld_uniform(mp.kpos + e + 1);
   const int nk = (int)((kend - km.k0 + MX_BK - 1) / MX_BK);
   MxOp oa, ob;
   mx_op_clear(oa);
@@ -494,8 +501,6 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_mx(MbPlans mp, const uint8_t*
   float* C = (float*)lds;
   stage_acc(C, acc, arow, brow, lane);
   __syncthreads();
-  bf16_t* base = (m0 < split ? out0 + (size_t)e * split * N + (size_t)m0 * N
-                             : out1 + (size_t)e * (M - split) * N + (size_t)(m0 - split) * N) + n0;
   auto out = [&](int r) { return base + (size_t)r * N; };
   epi_store<bf16_t>(C, out, TM);
 }
@@ -547,9 +552,9 @@ hipError_t launch_mx_dgrad_up(const GroupInfo& g, const uint8_t* dZ8, const uint
 hipError_t launch_mx_wgrad(const char* name, const MbPlans& mp, int E, const uint8_t* A8,
                            const uint8_t* As, const uint8_t* B8, const uint8_t* Bs, int M, int N,
                            int split, size_t Kp, void* out0, void* out1, hipStream_t s) {
-  const unsigned grid = (unsigned)E * (M / TM) * (N / TN);  // bound on the realised items
+  const unsigned grid = (unsigned)E * (M / TM) * (N / TN);
   return MOE_LAUNCH(name, s,
-                    k_wgrad_mx<<<grid, NTHR, 0, s>>>(mp, A8, As, B8, Bs, M, N, split, (long)Kp,
+                    k_wgrad_mx<<<grid, NTHR, 0, s>>>(mp, E, A8, As, B8, Bs, M, N, split, (long)Kp,
                                                      (bf16_t*)out0, (bf16_t*)out1));
 }
 

@@ -67,10 +67,6 @@ hipError_t launch_combine_bf16(const void* Y, const int32_t* pos, const float* w
                                const void* shared, void* y, int T, int k, int H, hipStream_t s);
 hipError_t launch_combine_f32(const float* Y, const int32_t* pos, const float* w,
                               const float* shared, float* y, int T, int k, int H, hipStream_t s);
-// Zero the weight gradients of experts that received no rows: for each e with
-// counts[e] == 0, bytes [e * stride[i], (e + 1) * stride[i]) of buffer i (i < 3).
-hipError_t launch_zero_empty_experts(const int32_t* counts, int E, void* const* bufs,
-                                     const size_t* stride, hipStream_t s);
 hipError_t launch_dg_reduce(const float* dgp, const int32_t* pos, int R, int n_parts,
                             float* d_topk_w, hipStream_t s);
 

@@ -195,39 +195,3 @@ hipError_t launch_dg_reduce(const float* dgp, const int32_t* pos, int R, int n_p
 }
 
 }  // namespace moe
-
-namespace moe {
-
-
-struct ZeroBufs {
-  u32x4_t* p[3];
-  size_t chunks[3];  // 16-byte chunks per expert
-};
-
-// Grid-stride zero fill of the per-expert regions of experts without rows.
-__global__ __launch_bounds__(256) void zero_empty_kernel(const int32_t* __restrict__ counts, int E,
-                                                         ZeroBufs z) {
-  const size_t tid = (size_t)blockIdx.x * 256 + threadIdx.x, nth = (size_t)gridDim.x * 256;
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
-  for (int e = 0; e < E; ++e) {
-    if (counts[e] != 0) continue;
-#pragma unroll
-    for (int b = 0; b < 3; ++b) {
-      if (!z.p[b]) continue;
-      u32x4_t* base = z.p[b] + (size_t)e * z.chunks[b];
-      for (size_t c = tid; c < z.chunks[b]; c += nth) __builtin_nontemporal_store(zero, base + c);
-    }
-  }
-}
-
-hipError_t launch_zero_empty_experts(const int32_t* counts, int E, void* const* bufs,
-                                     const size_t* stride, hipStream_t s) {
-  ZeroBufs z;
-  for (int b = 0; b < 3; ++b) {
-    z.p[b] = (u32x4_t*)bufs[b];
-    z.chunks[b] = stride[b] / 16;
-  }
-  return MOE_LAUNCH("zero_empty_experts", s, zero_empty_kernel<<<2048, 256, 0, s>>>(counts, E, z));
-}
-
-}  // namespace moe
