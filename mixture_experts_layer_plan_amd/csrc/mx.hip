@@ -89,9 +89,9 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const T* __restrict__ s
 // are zero), scales s[c, kbase / 32 + j / 32].  Blocks without a row are not
 // written: those columns belong to the next segment.  src rows are pulled through
 // gather when given.  One workgroup per (tile, 64 columns): 16-byte row loads into
-// an fp32 LDS tile, one thread per (column, block) for the scale and the codes,
-// which are staged in LDS as [column][row] so that 8 lanes store each column's
-// 128 codes as one contiguous run.
+// an LDS tile in the input type, one thread per (column, block) for the scale and
+// the codes, which are staged in the same LDS as [column][row] so that 8 lanes store
+// each column's 128 codes as one contiguous run.
 template <typename T>
 __global__ __launch_bounds__(256) void quant_tokens_kernel(
     const T* __restrict__ src, const int32_t* __restrict__ gather, int ld,
@@ -100,39 +100,35 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
     const int32_t* __restrict__ kseg, int cols, size_t kpad_total, uint8_t* __restrict__ q,
     uint8_t* __restrict__ sc) {
   constexpr int VEC = 16 / (int)sizeof(T), VPR = 64 / VEC;  // elements per load, loads per row
-  constexpr int CROW = 128 + 16;  // bytes per staged column (padded against bank conflicts)
-  __shared__ float tile[128][65];
-  __shared__ __attribute__((aligned(16))) uint8_t codes[64 * CROW];
+  constexpr int TROW = 64 + VEC;  // tile row in elements (padded by one 16-byte piece)
+  constexpr int CROW = 128 + 16;  // bytes per staged code column (padded)
+  static_assert(64 * CROW <= 128 * TROW * (int)sizeof(T), "codes fit in the tile");
+  // the tile in the input type; after every thread has read its 32 values it is
+  // reused for the codes
+  __shared__ __attribute__((aligned(16))) T tile[128 * TROW];
+  uint8_t* codes = (uint8_t*)tile;
   const int t = blockIdx.x, c0 = blockIdx.y * 64;
   if (t >= n_tiles[0]) return;
   const int e = tiles[2 * t], row0 = tiles[2 * t + 1];
   const int nrows = min(row0 + 128, offsets[e + 1]) - row0;
   for (int i = threadIdx.x; i < 128 * VPR; i += 256) {
     const int j = i / VPR, v = i - j * VPR;
-    float f[VEC];
+    uint4 raw = make_uint4(0u, 0u, 0u, 0u);
     if (j < nrows) {
       const int r = row0 + j;
-      const uint4 raw = *(const uint4*)(src + (size_t)(gather ? gather[r] : r) * ld + c0 + v * VEC);
-      if constexpr (sizeof(T) == 2) {
-        unpack8(raw, f);
-      } else {
-        f[0] = __uint_as_float(raw.x); f[1] = __uint_as_float(raw.y);
-        f[2] = __uint_as_float(raw.z); f[3] = __uint_as_float(raw.w);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < VEC; ++u) f[u] = 0.0f;
+      raw = *(const uint4*)(src + (size_t)(gather ? gather[r] : r) * ld + c0 + v * VEC);
     }
-#pragma unroll
-    for (int u = 0; u < VEC; ++u) tile[j][v * VEC + u] = f[u];
+    *(uint4*)(tile + j * TROW + v * VEC) = raw;
   }
   __syncthreads();
   const int cc = threadIdx.x & 63, blk = threadIdx.x >> 6;
-  const size_t kbase = (size_t)kpos[e] + kseg[e] + (row0 - offsets[e]);
-  if (32 * blk < nrows) {
-    float v[32];
+  const bool has = 32 * blk < nrows;
+  float v[32];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = tile[32 * blk + i][cc];
+  for (int i = 0; i < 32; ++i) v[i] = to_f32(tile[(32 * blk + i) * TROW + cc]);
+  __syncthreads();  // the tile is now free for the codes
+  const size_t kbase = (size_t)kpos[e] + kseg[e] + (row0 - offsets[e]);
+  if (has) {
     const int X = mx_scale_exp(v);
     uint4 lo, hi;
     mx_encode32(v, X, lo, hi);
