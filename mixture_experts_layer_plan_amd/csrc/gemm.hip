@@ -233,7 +233,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_down(GroupInfo g, const T* __
   wave_coords(arow, brow, false);
   const int lane = threadIdx.x & 63;
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
-    const KTile t = k_tile(g, w, MT, NT);
+    const KTile t = k_tile(g, w, MT, NT, true);
     if (k_empty(g, t.e)) {
       zero_tile<T>(dwd + (size_t)t.e * H * I + (size_t)t.m0 * I + t.n0, (size_t)I);
       continue;
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_up(GroupInfo g, const T* __re
   wave_coords(arow, brow, false);
   const int lane = threadIdx.x & 63;
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
-    const KTile t = k_tile(g, w, MT, NT);
+    const KTile t = k_tile(g, w, MT, NT, false);
     if (k_empty(g, t.e)) {
       zero_tile<T>((t.m0 < I ? dwg + (size_t)t.e * I * H + (size_t)t.m0 * H
                              : dwu + (size_t)t.e * I * H + (size_t)(t.m0 - I) * H) + t.n0,

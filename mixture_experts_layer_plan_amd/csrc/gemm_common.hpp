@@ -456,21 +456,30 @@ MOE_DEV void k_segment(const GroupInfo& g, int e, int& seg0, int& seg1) {
 }
 
 // Work item w of a K-grouped GEMM over an M_tiles x N_tiles output per expert:
-// every expert in id order (the single dense "expert" in dense mode), tiles in
-// row-major order.  Items of experts without rows store zeros (the weight
-// gradients are overwritten), so those writes interleave with the multiplying
-// items of the other experts instead of running as a separate pass.
+// every expert in id order (the single dense "expert" in dense mode), the tiles of
+// an expert with the M index fastest when m_fast, else the N index.  The wgrads
+// put the index that runs along H fastest (measured on MI355X: 2.91 against
+// 3.19 ms for wgrad-down, 5.67 against 6.13 ms for wgrad-up).  Items of experts
+// without rows store zeros (the weight gradients are overwritten), so those writes
+// interleave with the multiplying items of the other experts instead of running as
+// a separate pass.
 struct KTile {
   int e, m0, n0;
 };
-MOE_DEV KTile k_tile(const GroupInfo& g, int w, int mt_count, int nt_count) {
+MOE_DEV KTile k_tile(const GroupInfo& g, int w, int mt_count, int nt_count, bool m_fast) {
   const int per = mt_count * nt_count;
   const int e = w / per, rem = w - e * per;
-  const int mt = rem / nt_count;
   KTile t;
   t.e = e;
-  t.m0 = mt * TM;
-  t.n0 = (rem - mt * nt_count) * TN;
+  if (m_fast) {
+    const int nt = rem / mt_count;
+    t.m0 = (rem - nt * mt_count) * TM;
+    t.n0 = nt * TN;
+  } else {
+    const int mt = rem / nt_count;
+    t.m0 = mt * TM;
+    t.n0 = (rem - mt * nt_count) * TN;
+  }
   return t;
 }
 

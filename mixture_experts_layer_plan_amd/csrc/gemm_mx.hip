@@ -449,7 +449,7 @@ struct KFrom {
 // One workgroup per (expert, output tile); experts without rows in any minibatch
 // get zero tiles.  Output rows m < split go to out0[e], the rest to out1[e] (dW_g /
 // dW_u); split = M for one.
-__global__ __launch_bounds__(NTHR, 2) void k_wgrad_mx(MbPlans mp, int E,
+__global__ __launch_bounds__(NTHR, 2) void k_wgrad_mx(MbPlans mp, int E, bool m_fast,
                                                       const uint8_t* __restrict__ A8,
                                                       const uint8_t* __restrict__ As,
                                                       const uint8_t* __restrict__ B8,
@@ -468,7 +468,9 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_mx(MbPlans mp, int E,
   int arow, brow[2];
   wave_coords(arow, brow, false);
   const int e = id / (MT * NT), rem = id - e * (MT * NT);
-  const int mt = rem / NT, m0 = mt * TM, n0 = (rem - mt * NT) * TN;
+  // the tile index along H runs fastest (M for wgrad-down, N for wgrad-up)
+  const int mt = m_fast ? rem % MT : rem / NT, nt = m_fast ? rem / MT : rem % NT;
+  const int m0 = mt * TM, n0 = nt * TN;
   bf16_t* base = (m0 < split ? out0 + (size_t)e * split * N + (size_t)m0 * N
                              : out1 + (size_t)e * (M - split) * N + (size_t)(m0 - split) * N) + n0;
   if (ld_uniform(mp.kpos + e + 1) == ld_uniform(mp.kpos + e)) {
@@ -553,9 +555,11 @@ hipError_t launch_mx_wgrad(const char* name, const MbPlans& mp, int E, const uin
                            const uint8_t* As, const uint8_t* B8, const uint8_t* Bs, int M, int N,
                            int split, size_t Kp, void* out0, void* out1, hipStream_t s) {
   const unsigned grid = (unsigned)E * (M / TM) * (N / TN);
+  // one output (split == M) is wgrad-down, whose M runs along H
   return MOE_LAUNCH(name, s,
-                    k_wgrad_mx<<<grid, NTHR, 0, s>>>(mp, E, A8, As, B8, Bs, M, N, split, (long)Kp,
-                                                     (bf16_t*)out0, (bf16_t*)out1));
+                    k_wgrad_mx<<<grid, NTHR, 0, s>>>(mp, E, split == M, A8, As, B8, Bs, M, N,
+                                                     split, (long)Kp, (bf16_t*)out0,
+                                                     (bf16_t*)out1));
 }
 
 }  // namespace moe
