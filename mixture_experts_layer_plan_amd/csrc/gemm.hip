@@ -240,8 +240,9 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_down(GroupInfo g, const T* __
     }
     int seg0, seg1;
     k_segment(g, t.e, seg0, seg1);
-    MNLoad<T, KRowSeg<T>> la{{dYu + t.m0, nullptr, (size_t)H, seg0, seg1}};
-    MNLoad<T, KRowSeg<T>> lb{{gh + t.n0, nullptr, (size_t)I, seg0, seg1}};
+    MNSeg<T> la, lb;
+    la.set(dYu + (size_t)seg0 * H + t.m0, (size_t)H, seg1 - seg0);
+    lb.set(gh + (size_t)seg0 * I + t.n0, (size_t)I, seg1 - seg0);
     f32x16_t acc[2][2];
     const int nk = (seg1 - seg0 + Tr<T>::BK - 1) / Tr<T>::BK;
     gemm_main<T, 1>(lds, la, lb, nk, acc, arow, brow, lane);
@@ -278,8 +279,9 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_up(GroupInfo g, const T* __re
     }
     int seg0, seg1;
     k_segment(g, t.e, seg0, seg1);
-    MNLoad<T, KRowSeg<T>> la{{dZ + t.m0, nullptr, (size_t)(2 * I), seg0, seg1}};
-    MNLoad<T, KRowSeg<T>> lb{{X + t.n0, nullptr, (size_t)H, seg0, seg1}};
+    MNSeg<T> la, lb;
+    la.set(dZ + (size_t)seg0 * (2 * I) + t.m0, (size_t)(2 * I), seg1 - seg0);
+    lb.set(X + (size_t)seg0 * H + t.n0, (size_t)H, seg1 - seg0);
     f32x16_t acc[2][2];
     const int nk = (seg1 - seg0 + Tr<T>::BK - 1) / Tr<T>::BK;
     gemm_main<T, 1>(lds, la, lb, nk, acc, arow, brow, lane);

@@ -104,6 +104,42 @@ MOE_DEV void MNLoad<T, KR>::store(char* t, const uint4 (&r)[4]) const {
   }
 }
 
+// MN-major operand over the K rows 0 .. n-1 of a row-major matrix whose row 0 is at
+// base (row stride ld elements), columns c0 .. c0 + 127 (base points at column c0):
+// the K-grouped operands of the wgrads (an expert's segment of rows).  Addresses are
+// the wave-uniform row base of K tile kt plus a 32-bit per-thread offset, and a row
+// is valid below one per-thread limit: no per-row pointers or branches on them.
+// Same thread-to-element map and LDS layout as MNLoad.
+template <typename T>
+struct MNSeg {
+  static constexpr bool kmajor = sizeof(T) != 2;
+  static constexpr int IB = 128 / Tr<T>::VEC;
+  const T* base;
+  size_t ld;
+  int n;         // valid K rows
+  uint32_t off;  // element offset of this thread's first row and column group
+  int k4;        // this thread's first K row within a tile
+  MOE_DEV void set(const T* b, size_t ld_elems, int rows) {
+    base = b;
+    ld = ld_elems;
+    n = rows;
+    const int kb = threadIdx.x / IB, ib = threadIdx.x % IB;
+    k4 = 4 * kb;
+    off = (uint32_t)(k4 * ld_elems + ib * Tr<T>::VEC);
+  }
+  MOE_DEV void load(int kt, uint4 (&r)[4]) const {
+    const T* b = base + (size_t)kt * Tr<T>::BK * ld;
+    const int lim = n - kt * Tr<T>::BK - k4;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      r[kk] = kk < lim ? *(const uint4*)(b + off + (uint32_t)kk * (uint32_t)ld) : zero4();
+  }
+  struct NoRows {  // MNLoad's store does not use its row functor
+    MOE_DEV const T* operator()(int) const { return nullptr; }
+  };
+  MOE_DEV void store(char* t, const uint4 (&r)[4]) const { MNLoad<T, NoRows>{}.store(t, r); }
+};
+
 // ------------------------------------------------------------- MFMA on a tile
 // Fragment of tile rows (K-major) or columns (MN-major) c0 .. c0 + 31 at 16-deep K
 // step ks: lane l supplies row/column c0 + (l & 31) and K values 16 ks + 8 (l >> 5)
@@ -427,21 +463,6 @@ struct KRowCat {
   int I, H;
   MOE_DEV const T* operator()(int k) const {
     return k < I ? wg + (size_t)k * H : wu + (size_t)(k - I) * H;
-  }
-};
-
-// K rows of a K-grouped operand: segment row seg0 + k (valid below seg1) of a
-// row-major matrix, optionally gathered through src_token.
-template <typename T>
-struct KRowSeg {
-  const T* base;
-  const int32_t* gather;
-  size_t ld;
-  int seg0, seg1;
-  MOE_DEV const T* operator()(int k) const {
-    const int r = seg0 + k;
-    if (r >= seg1) return nullptr;
-    return base + (size_t)(gather ? gather[r] : r) * ld;
   }
 };
 
