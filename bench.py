@@ -105,14 +105,21 @@ def kernel_work(name, sh, counts_mb, es=2):
 
 
 def kernel_sources_sha256() -> str:
-    """Hash of the HIP sources of the library (kernels and their headers)."""
+    """Hash of the HIP sources of the library (kernels and their headers) with their
+    comments removed and whitespace collapsed, so that editing a comment does not
+    invalidate the measurements keyed by it."""
     import hashlib
+    import re
     d = os.path.join(ROOT, "mixture_experts_layer_plan_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(d)):
         if f.endswith((".hip", ".hpp")):
+            text = open(os.path.join(d, f), encoding="utf-8").read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", "", text)
+            text = re.sub(r"\s+", " ", text)
             h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
+            h.update(text.encode())
     return h.hexdigest()
 
 

@@ -16,17 +16,19 @@
 // and a register prefetch overlap the next tile's global loads with the current
 // tile's MFMAs.  An operand stored K-contiguous ("K-major") is copied chunk by
 // chunk; one stored with K as the outer dimension ("MN-major": the wgrad operands
-// and the weights of the dgrad GEMMs) is loaded as 4 x VEC blocks and transposed
-// in registers on its way into LDS.
+// and the weights of the dgrad GEMMs) is stored into LDS as it lies in memory and
+// read back with the transposing LDS read ds_read_b64_tr_b16 (bf16), or loaded as
+// 4 x VEC blocks and transposed in registers on its way into LDS (fp32).
 //
 // Grouping: a "rows-grouped" GEMM (forward GEMMs and dgrads) walks the plan's
 // tile list (expert, first row) so a tile never mixes experts; a "K-grouped" GEMM
-// (wgrads) is persistent: its workgroups walk (expert with rows, output tile) items
-// and run K over that expert's rows; experts without rows get zeros from a
-// separate full-bandwidth fill.  The dispatch gather of x happens in the A loader
-// of GEMM1 through the plan's src_token list (X is not written in the forward);
-// the backward replays the gathers of x and dy once into row-major buffers so that
-// the K rows of the wgrad operands are plain strided addresses.  Every output
+// (wgrads) is persistent: its workgroups walk (expert, output tile) items over all
+// E experts and run K over that expert's rows; the items of experts without rows
+// store zero tiles, interleaved with the multiplying items.  The dispatch gather of
+// x happens in the A loader of GEMM1 through the plan's src_token list (X is not
+// written in the forward); the backward replays the gathers of x and dy once into
+// row-major buffers so that the K rows of the wgrad operands are plain strided
+// addresses.  Every output
 // element is produced by one workgroup with a fixed K order: results are bitwise
 // reproducible and independent of the grid.
 //
