@@ -104,6 +104,8 @@ SMALL_MX = {
     "ring3_ragged": (Shape(T=300, H=256, I=256, E=8, k=2, I_shared=128, dtype="mxfp8"), 128),
     "skew_ring": (Shape(T=512, H=384, I=256, E=16, k=4, I_shared=256, zipf_s=1.2, dtype="mxfp8"), 128),
     "one_minibatch": (Shape(T=200, H=256, I=128, E=6, k=3, dtype="mxfp8"), 0),
+    # most experts receive no row in any of the three minibatches
+    "sparse_experts": (Shape(T=96, H=256, I=128, E=16, k=2, zipf_s=3.0, dtype="mxfp8"), 32),
 }
 
 
@@ -129,6 +131,27 @@ def test_mx_layer_small_all_outputs(name):
     if shape.I_shared:
         for n in ("ds_gate", "ds_up", "ds_down"):
             check(getattr(b, n), g[n], "bf16", n)
+
+
+def test_mx_experts_without_rows_get_zero_gradients():
+    shape, T_mb = SMALL_MX["sparse_experts"]
+    say("mx: weight gradients of experts without rows are overwritten with zeros")
+    from mixture_experts_layer_plan_amd import LayerBuffers, run_layer
+    inp = to_dev(make_inputs(shape, seed=6, device="cpu", with_dy=True))
+    b = LayerBuffers(shape.T, shape.H, shape.I, shape.E, shape.k, shape.I_shared, "mxfp8",
+                     backward=True, T_minibatch=T_mb)
+    for t in (b.dw_gate, b.dw_up, b.dw_down):
+        t.fill_(1.0)
+    run_layer(b, inp, backward=True)
+    torch.cuda.synchronize()
+    used = set(int(e) for e in np_(b.topk_idx).ravel())
+    empty = [e for e in range(shape.E) if e not in used]
+    assert empty and used, (empty, used)
+    for e in empty:
+        for t in (b.dw_gate, b.dw_up, b.dw_down):
+            assert not t[e].any(), e
+    for e in used:
+        assert b.dw_gate[e].any() and b.dw_up[e].any() and b.dw_down[e].any(), e
 
 
 def test_mx_row_local_outputs_bitwise_independent_of_minibatch_size():
