@@ -119,8 +119,9 @@ struct KLinear {
   MOE_DEV long operator()(int kt) const { return (long)kt * MX_BK; }
 };
 
-// Main loop, prefetch distance 2 (as gemm_main); scale words travel with their
-// data: sX0/sX1 with the register sets, cX0/cX1 with the LDS buffers.
+// Main loop: two LDS stages and one register stage (tile kt + 1 is loaded while
+// tile kt is multiplied); scale words travel with their data, sX with the register
+// stage and cX with the LDS stage being multiplied.
 template <class KM>
 MOE_DEV void gemm_main_mx(char* lds, const MxOp& A, const MxOp& B, const KM& km, int nk,
                           f32x16_t (&acc)[2][2], int arow, const int (&brow)[2], int lane) {
