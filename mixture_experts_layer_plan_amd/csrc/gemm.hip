@@ -370,7 +370,7 @@ hipError_t launch_gemm_up_swiglu(int dt, const GroupInfo& g, const void* x, cons
 }
 hipError_t launch_gemm_down(int dt, const GroupInfo& g, const void* h, const void* wd, int H,
                             int I, void* Y, hipStream_t s) {
-  if (dt && !g.tiles) return launch_big_down(g, h, wd, H, I, Y, s);
+  if (dt) return launch_big_down(g, h, wd, H, I, Y, s);
   return dt ? down_t<bf16_t>(g, h, wd, H, I, Y, s) : down_t<float>(g, h, wd, H, I, Y, s);
 }
 hipError_t launch_gemm_dgrad_down(int dt, const GroupInfo& g, const void* dy, const void* wd,
