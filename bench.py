@@ -179,8 +179,9 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU's share of the layer; runs on more than one GPU are "
-              "not part of this build (see the sharding design notes).", file=sys.stderr)
+        print("bench.py measures one GPU's share of the layer; multi-GPU runs are not "
+              "implemented (expert-parallel sharding is described in the design notes).",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

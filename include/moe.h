@@ -54,7 +54,7 @@ typedef enum {
   MOE_E_SHAPE = 2,       /* a size is out of range or not a supported multiple */
   MOE_E_ALIGN = 3,       /* a pointer is not 16-byte aligned */
   MOE_E_WORKSPACE = 4,   /* workspace smaller than moe_workspace_bytes() */
-  MOE_E_UNSUPPORTED = 5, /* valid request that this build does not implement */
+  MOE_E_UNSUPPORTED = 5, /* valid request that the library does not implement */
   MOE_E_HIP = 6          /* a HIP launch failed (hipGetLastError) */
 } moe_status;
 

@@ -657,7 +657,7 @@ const char* moe_status_str(moe_status s) {
     case MOE_E_SHAPE: return "shape out of range or not a supported multiple";
     case MOE_E_ALIGN: return "pointer not 16-byte aligned";
     case MOE_E_WORKSPACE: return "workspace too small";
-    case MOE_E_UNSUPPORTED: return "not supported by this build";
+    case MOE_E_UNSUPPORTED: return "valid request that the library does not implement";
     case MOE_E_HIP: return "HIP launch failed";
   }
   return "unknown status";

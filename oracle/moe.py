@@ -18,7 +18,7 @@ them [STA §Outras características].  The plan, dispatch and combine reorder ro
 without changing this value: the pull schedule's order follows from the routing
 [SEB §Das Scheduling] and needs no sort [STA §Escolha da direção de comunicação].
 
-Readings taken where the pages are silent (each is also listed in the design doc):
+Readings taken where the pages are silent:
   * score function: softmax; gates renormalised over the selected k;
   * selection on raw logits, order (logit desc, expert id asc), ties to the lower id;
   * rows of an expert in ascending flat pair index t*k+j (= ascending token);
