@@ -221,6 +221,146 @@ __global__ __launch_bounds__(NTHR, 2) void k_dgrad_up(GroupInfo g, const T* __re
   epi_store<T>(C, out, t.row_end - t.row0);
 }
 
+// ------------------------------------------------------- DMA-fed wgrad loop (bf16)
+// The K-grouped wgrad operands reach LDS by the direct-to-LDS load
+// (global_load_lds_dwordx4: lane L's 16 bytes land at the wavefront's LDS base +
+// 16 L), so no registers stage them and three 32-deep K stages are in flight while
+// a fourth is multiplied: a ring of 4 x 16 KiB (two MN-major operand tiles of 32 K
+// rows x 256 bytes each, the same swizzled layout as the register-staged tiles).
+// Against one register-staged 64-deep tile in flight this keeps 1.5x the bytes in
+// flight per workgroup.  K rows past the expert's segment read a 256-byte zero row
+// in device memory, so they add exactly zero and never leave the operands.
+__device__ __attribute__((aligned(16))) uint4 g_zero_krow[16];
+
+namespace wdma {
+constexpr int BK = 32;          // K rows per stage
+constexpr int OPB = BK * 256;   // bytes of one operand tile in a stage
+constexpr int STB = 2 * OPB;    // stage bytes
+static_assert(4 * STB == LDS_BYTES, "the ring fills the LDS of the staged C tile");
+
+typedef __attribute__((address_space(3))) void* lds_vptr;
+typedef const __attribute__((address_space(1))) void* gbl_vptr;
+
+// MN-major operand: K row k = row seg0 + k of a row-major bf16 matrix, columns
+// c0 .. c0 + 127.  Instruction q (0, 1) of wavefront w fills K rows 8 w + 4 q ..
+// + 3 of a stage: lane L brings K row r = 8 w + 4 q + L / 16 into physical chunk
+// L % 16, i.e. its logical chunk (L % 16) ^ mn_swz(r).
+struct Opnd {
+  const char* base;  // element (seg0, c0)
+  uint32_t ldb;      // row stride, bytes
+  int n;             // rows in the segment
+  int r[2];
+  uint32_t col[2];
+  MOE_DEV void set(const bf16_t* b, size_t ld, int rows) {
+    base = (const char*)b;
+    ldb = (uint32_t)(ld * 2);
+    n = rows;
+    const int w = threadIdx.x >> 6, L = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      r[q] = 8 * w + 4 * q + (L >> 4);
+      col[q] = (uint32_t)(((L & 15) ^ mn_swz(r[q])) << 4);
+    }
+  }
+  MOE_DEV void issue(int kt, char* tile) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int t = kt * BK + r[q];
+      const char* src = t < n ? base + (size_t)t * ldb + col[q] : (const char*)g_zero_krow + col[q];
+      __builtin_amdgcn_global_load_lds((gbl_vptr)src, (lds_vptr)(tile + (8 * w + 4 * q) * 256), 16,
+                                       0, 0);
+    }
+  }
+};
+
+// The MFMAs of one 32-deep stage (two 16-deep steps) on two MN-major tiles.  The
+// transposing LDS reads are issued from inline assembly: for the
+// ds_read_b64_tr_b16 builtin the compiler waits for every outstanding
+// direct-to-LDS load first (vmcnt(0)), which would drain the ring on every stage.
+// Each step's eight reads and their lgkmcnt(0) wait form one asm block, so no
+// fragment register is used before its data is in.
+MOE_DEV uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+MOE_DEV uint32_t mn_frag_addr(const char* t, int c0, int ks, int lane) {
+  const int g = lane >> 4, a = lane & 3, j = (lane >> 2) & 3;
+  const int k = 16 * ks + 8 * (g >> 1) + j;  // K row k + 4 has the same swizzle
+  const int col = c0 + 16 * (g & 1) + 4 * a;
+  return lds_addr(t + k * 256 + (((col >> 3) ^ mn_swz(k)) << 4) + (col & 7) * 2);
+}
+MOE_DEV bf16x8_t join_tr(const s16x4_t& lo, const s16x4_t& hi) {
+  return __builtin_bit_cast(bf16x8_t, (s16x8_t)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5,
+                                                                        6, 7));
+}
+MOE_DEV void mma_stage(const char* ta, const char* tb, f32x16_t (&acc)[2][2], int arow,
+                       const int (&brow)[2], int lane) {
+#pragma unroll
+  for (int ks = 0; ks < BK / 16; ++ks) {
+    const uint32_t pa0 = mn_frag_addr(ta, arow, ks, lane), pa1 = mn_frag_addr(ta, arow + 32, ks, lane);
+    const uint32_t pb0 = mn_frag_addr(tb, brow[0], ks, lane);
+    const uint32_t pb1 = mn_frag_addr(tb, brow[1], ks, lane);
+    s16x4_t a0l, a0h, a1l, a1h, b0l, b0h, b1l, b1h;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %2, %9\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %4, %10\n\t"
+        "ds_read_b64_tr_b16 %5, %10 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %6, %11\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:1024\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a0l), "=&v"(a0h), "=&v"(a1l), "=&v"(a1h), "=&v"(b0l), "=&v"(b0h), "=&v"(b1l),
+          "=&v"(b1h)
+        : "v"(pa0), "v"(pa1), "v"(pb0), "v"(pb1)
+        : "memory");
+    const bf16x8_t a0 = join_tr(a0l, a0h), a1 = join_tr(a1l, a1h);
+    const bf16x8_t b0 = join_tr(b0l, b0h), b1 = join_tr(b1l, b1h);
+    acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
+    acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
+    acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
+    acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
+  }
+}
+
+// Wait until at most `ahead` stages of this wavefront's loads (4 instructions each)
+// are outstanding and its LDS reads are done, then meet the workgroup.
+MOE_DEV void ring_wait(int ahead) {
+  if (ahead >= 2) __builtin_amdgcn_s_waitcnt(0x0078);       // vmcnt(8) lgkmcnt(0)
+  else if (ahead == 1) __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
+  else __builtin_amdgcn_s_waitcnt(0x0070);                  // vmcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
+MOE_DEV void main_loop(char* lds, const Opnd& A, const Opnd& B, int n, f32x16_t (&acc)[2][2],
+                       int arow, const int (&brow)[2], int lane) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  const int nk = (n + BK - 1) / BK;
+  for (int s = 0; s < 3 && s < nk; ++s) {
+    A.issue(s, lds + s * STB);
+    B.issue(s, lds + s * STB + OPB);
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    ring_wait(min(2, nk - 1 - kt));  // stage kt is in; stage kt - 1 is no longer read
+    if (kt + 3 < nk) {
+      char* slot = lds + ((kt + 3) & 3) * STB;
+      A.issue(kt + 3, slot);
+      B.issue(kt + 3, slot + OPB);
+    }
+    const char* cur = lds + (kt & 3) * STB;
+    mma_stage(cur, cur + OPB, acc, arow, brow, lane);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  __builtin_amdgcn_s_barrier();  // every wavefront is done with the ring
+}
+}  // namespace wdma
+
 // wgrad-down: dW_d[e][m, n] = sum_r dYu[r, m] gh[r, n]  (M = H, N = I, K = rows of e).
 // Persistent: each workgroup walks work items blockIdx.x, + gridDim.x, ...; the
 // tiles of experts without rows are stored as zeros.
@@ -242,12 +382,19 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_down(GroupInfo g, const T* __
     }
     int seg0, seg1;
     k_segment(g, t.e, seg0, seg1);
-    MNSeg<T> la, lb;
-    la.set(dYu + (size_t)seg0 * H + t.m0, (size_t)H, seg1 - seg0);
-    lb.set(gh + (size_t)seg0 * I + t.n0, (size_t)I, seg1 - seg0);
     f32x16_t acc[2][2];
-    const int nk = (seg1 - seg0 + Tr<T>::BK - 1) / Tr<T>::BK;
-    gemm_main<T, 1>(lds, la, lb, nk, acc, arow, brow, lane);
+    if constexpr (sizeof(T) == 2) {
+      wdma::Opnd la, lb;
+      la.set(dYu + (size_t)seg0 * H + t.m0, (size_t)H, seg1 - seg0);
+      lb.set(gh + (size_t)seg0 * I + t.n0, (size_t)I, seg1 - seg0);
+      wdma::main_loop(lds, la, lb, seg1 - seg0, acc, arow, brow, lane);
+    } else {
+      MNSeg<T> la, lb;
+      la.set(dYu + (size_t)seg0 * H + t.m0, (size_t)H, seg1 - seg0);
+      lb.set(gh + (size_t)seg0 * I + t.n0, (size_t)I, seg1 - seg0);
+      const int nk = (seg1 - seg0 + Tr<T>::BK - 1) / Tr<T>::BK;
+      gemm_main<T, 1>(lds, la, lb, nk, acc, arow, brow, lane);
+    }
     float* C = (float*)lds;
     stage_acc(C, acc, arow, brow, lane);
     __syncthreads();
@@ -281,12 +428,19 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_up(GroupInfo g, const T* __re
     }
     int seg0, seg1;
     k_segment(g, t.e, seg0, seg1);
-    MNSeg<T> la, lb;
-    la.set(dZ + (size_t)seg0 * (2 * I) + t.m0, (size_t)(2 * I), seg1 - seg0);
-    lb.set(X + (size_t)seg0 * H + t.n0, (size_t)H, seg1 - seg0);
     f32x16_t acc[2][2];
-    const int nk = (seg1 - seg0 + Tr<T>::BK - 1) / Tr<T>::BK;
-    gemm_main<T, 1>(lds, la, lb, nk, acc, arow, brow, lane);
+    if constexpr (sizeof(T) == 2) {
+      wdma::Opnd la, lb;
+      la.set(dZ + (size_t)seg0 * (2 * I) + t.m0, (size_t)(2 * I), seg1 - seg0);
+      lb.set(X + (size_t)seg0 * H + t.n0, (size_t)H, seg1 - seg0);
+      wdma::main_loop(lds, la, lb, seg1 - seg0, acc, arow, brow, lane);
+    } else {
+      MNSeg<T> la, lb;
+      la.set(dZ + (size_t)seg0 * (2 * I) + t.m0, (size_t)(2 * I), seg1 - seg0);
+      lb.set(X + (size_t)seg0 * H + t.n0, (size_t)H, seg1 - seg0);
+      const int nk = (seg1 - seg0 + Tr<T>::BK - 1) / Tr<T>::BK;
+      gemm_main<T, 1>(lds, la, lb, nk, acc, arow, brow, lane);
+    }
     float* C = (float*)lds;
     stage_acc(C, acc, arow, brow, lane);
     __syncthreads();

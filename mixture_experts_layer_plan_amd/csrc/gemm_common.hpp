@@ -169,7 +169,7 @@ MOE_DEV bf16x8_t frag16(const char* t, int c0, int ks, int lane) {
 
 // acc[mb][nb]: wave rows arow + 32 mb, B-tile rows brow[nb]; AK / BK: the A / B
 // LDS tile is K-major (else MN-major, bf16 only).
-template <typename T, bool AK = true, bool BK = true>
+template <typename T, bool AK = true, bool BK = true, int NKS = 4>
 MOE_DEV void mma_tile(const char* ta, const char* tb, f32x16_t (&acc)[2][2], int arow,
                       const int (&brow)[2], int lane);
 
@@ -177,12 +177,14 @@ template <>
 MOE_DEV void mma_tile<bf16_t, true, true>(const char* ta, const char* tb, f32x16_t (&acc)[2][2],
                                           int arow, const int (&brow)[2], int lane);
 
-template <typename T, bool AK, bool BK>
+// NKS: 16-deep K steps in the tile (4 for the 64-deep register-staged tiles, 2 for
+// the 32-deep stages of the DMA-fed wgrads).
+template <typename T, bool AK, bool BK, int NKS>
 MOE_DEV void mma_tile(const char* ta, const char* tb, f32x16_t (&acc)[2][2], int arow,
                       const int (&brow)[2], int lane) {
   static_assert(sizeof(T) == 2, "MN-major LDS tiles are bf16 only");
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
+  for (int ks = 0; ks < NKS; ++ks) {
     const bf16x8_t a0 = frag16<AK>(ta, arow, ks, lane);
     const bf16x8_t a1 = frag16<AK>(ta, arow + 32, ks, lane);
     const bf16x8_t b0 = frag16<BK>(tb, brow[0], ks, lane);
