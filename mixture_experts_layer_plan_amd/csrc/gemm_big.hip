@@ -169,10 +169,21 @@ MOE_DEV int mn_blk_ofs(int c0) {
   const int sw = mnswz(8 * (g >> 1) + j);
   return (((c0 >> 3) ^ (sw & 12)) << 4);
 }
+// The two reads are issued from inline assembly together with their lgkmcnt(0)
+// wait: for the ds_read_b64_tr_b16 builtin the compiler first waits for every
+// outstanding direct-to-LDS load (vmcnt(0)), i.e. for the next K tile's loads that
+// were just issued, which would serialise the loads with the MFMAs.
 MOE_DEV bf16x8_t frag_mn(const char* st, int c0, int ks) {
   const char* p = st + mn_lane_ofs() + mn_blk_ofs(c0) + ks * 16 * 512;
-  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
-  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p + 4 * 512));
+  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+  s16x4_t lo, hi;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %2\n\t"
+      "ds_read_b64_tr_b16 %1, %2 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lo), "=&v"(hi)
+      : "v"(a)
+      : "memory");
   const s16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8_t, v);
 }
