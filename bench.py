@@ -27,6 +27,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "mxfp8": 5000.0}
+# rows from which an expert's bf16 weight gradients run on the 256 x 256 tiles (the
+# library's split of the K-grouped wgrads)
+WGRAD_HOT_ROWS = 256
 METRIC = "MoE layer tokens/s fwd+bwd @H7168 I2048 E256 top8, 1 GPU; % MFMA/HBM peak"
 
 
@@ -46,6 +49,12 @@ def kernel_work(name, sh, counts_mb, es=2):
     R = sum(r for r, _ in mbs)
     union = [sum(c[e] for c in counts_mb) for e in range(E)]
     Et = sum(1 for v in union if v > 0)
+    # bf16 wgrads: experts with >= WGRAD_HOT_ROWS rows go to the 256-tile kernel when H
+    # and I are multiples of 256; the 128-tile kernel keeps the rest and the zero
+    # gradients of the experts without rows
+    hot_split = es == 2 and H % 256 == 0 and I % 256 == 0 and not sh.T_minibatch
+    Eh = sum(1 for v in union if v >= WGRAD_HOT_ROWS) if hot_split else 0
+    Rh = sum(v for v in union if v >= WGRAD_HOT_ROWS) if hot_split else 0
 
     def over_mb(f):
         b = fl = 0.0
@@ -72,9 +81,14 @@ def kernel_work(name, sh, counts_mb, es=2):
         "gemm_dgrad_down": lambda: (Et * H * I * es + R * H * es + R * 2 * I * 4 + R * 3 * I * es
                                     + R * (I // 128) * 4, 2 * R * H * I),
         # the wgrads also store the zero gradients of the E - Et experts without rows
-        "gemm_wgrad_down": lambda: (R * H * es + R * I * es + E * H * I * es, 2 * R * H * I),
+        "gemm_wgrad_down": lambda: ((R - Rh) * (H + I) * es + (E - Eh) * H * I * es,
+                                    2 * (R - Rh) * H * I),
+        "gemm_wgrad_down_hot": lambda: (Rh * (H + I) * es + Eh * H * I * es, 2 * Rh * H * I),
         "gemm_dgrad_up": lambda: (Et * 2 * I * H * es + R * 2 * I * es + R * H * es, 2 * R * 2 * I * H),
-        "gemm_wgrad_up": lambda: (R * 2 * I * es + R * H * es + E * 2 * I * H * es, 2 * R * 2 * I * H),
+        "gemm_wgrad_up": lambda: ((R - Rh) * (2 * I + H) * es + (E - Eh) * 2 * I * H * es,
+                                  2 * (R - Rh) * 2 * I * H),
+        "gemm_wgrad_up_hot": lambda: (Rh * (2 * I + H) * es + Eh * 2 * I * H * es,
+                                      2 * Rh * 2 * I * H),
         "gemm_up_swiglu_shared": lambda: (2 * Is * H * 2 + T * H * 2 + T * 2 * Is * 4 + T * Is * 2,
                                           2 * T * H * 2 * Is),
         "gemm_down_shared": lambda: (Is * H * 2 + T * Is * 2 + T * H * 2, 2 * T * Is * H),

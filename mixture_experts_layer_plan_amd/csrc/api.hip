@@ -169,6 +169,7 @@ GroupInfo grouped(const moe_shape* s, const PlanView& v) {
   g.max_wtiles = v.max_wtiles;
   g.dense_rows = 0;
   g.E = s->E;
+  g.hot_rows = INT_MAX;
   return g;
 }
 
@@ -177,6 +178,7 @@ GroupInfo dense(int rows) {
   memset(&g, 0, sizeof(g));
   g.dense_rows = rows;
   g.E = 1;
+  g.hot_rows = INT_MAX;
   return g;
 }
 

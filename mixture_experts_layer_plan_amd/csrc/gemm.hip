@@ -376,7 +376,12 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_down(GroupInfo g, const T* __
   const int lane = threadIdx.x & 63;
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
     const KTile t = k_tile(g, w, MT, NT, true);
-    if (k_empty(g, t.e)) {
+    const int kind = k_item_kind(g, t.e);
+    if (kind == 2) {
+      w = k_skip_expert(w, t.e, MT * NT);
+      continue;
+    }
+    if (kind == 1) {
       zero_tile<T>(dwd + (size_t)t.e * H * I + (size_t)t.m0 * I + t.n0, (size_t)I);
       continue;
     }
@@ -420,7 +425,12 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_up(GroupInfo g, const T* __re
   const int lane = threadIdx.x & 63;
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
     const KTile t = k_tile(g, w, MT, NT, false);
-    if (k_empty(g, t.e)) {
+    const int kind = k_item_kind(g, t.e);
+    if (kind == 2) {
+      w = k_skip_expert(w, t.e, MT * NT);
+      continue;
+    }
+    if (kind == 1) {
       zero_tile<T>((t.m0 < I ? dwg + (size_t)t.e * I * H + (size_t)t.m0 * H
                              : dwu + (size_t)t.e * I * H + (size_t)(t.m0 - I) * H) + t.n0,
                    (size_t)H);
@@ -538,15 +548,31 @@ hipError_t launch_gemm_dgrad_up(int dt, const GroupInfo& g, const void* dZ, cons
   return dt ? launch_big_dgrad_up(g, dZ, wg, wu, H, I, dX, s)
             : dgrad_up_t<float>(g, dZ, wg, wu, H, I, dX, s);
 }
+// Grouped bf16 wgrads: the experts with at least WGRAD_HOT_ROWS rows run on the
+// 256 x 256 core; the 128 x 128 kernel takes the experts with fewer rows (short K,
+// bound by their output writes) and stores the zero gradients of the experts
+// without rows.
+constexpr int WGRAD_HOT_ROWS = 256;
+
 hipError_t launch_gemm_wgrad_down(int dt, const GroupInfo& g, const void* dy, const void* gh,
                                   int H, int I, void* dwd, hipStream_t s) {
-  return dt ? wgrad_down_t<bf16_t>(g, dy, gh, H, I, dwd, s)
-            : wgrad_down_t<float>(g, dy, gh, H, I, dwd, s);
+  if (!dt) return wgrad_down_t<float>(g, dy, gh, H, I, dwd, s);
+  const hipError_t e = launch_big_wgrad_down_hot(g, dy, gh, H, I, dwd, WGRAD_HOT_ROWS, s);
+  if (e == hipErrorNotSupported) return wgrad_down_t<bf16_t>(g, dy, gh, H, I, dwd, s);
+  if (e != hipSuccess) return e;
+  GroupInfo rest = g;
+  rest.hot_rows = WGRAD_HOT_ROWS;
+  return wgrad_down_t<bf16_t>(rest, dy, gh, H, I, dwd, s);
 }
 hipError_t launch_gemm_wgrad_up(int dt, const GroupInfo& g, const void* dZ, const void* x,
                                 int H, int I, void* dwg, void* dwu, hipStream_t s) {
-  return dt ? wgrad_up_t<bf16_t>(g, dZ, x, H, I, dwg, dwu, s)
-            : wgrad_up_t<float>(g, dZ, x, H, I, dwg, dwu, s);
+  if (!dt) return wgrad_up_t<float>(g, dZ, x, H, I, dwg, dwu, s);
+  const hipError_t e = launch_big_wgrad_up_hot(g, dZ, x, H, I, dwg, dwu, WGRAD_HOT_ROWS, s);
+  if (e == hipErrorNotSupported) return wgrad_up_t<bf16_t>(g, dZ, x, H, I, dwg, dwu, s);
+  if (e != hipSuccess) return e;
+  GroupInfo rest = g;
+  rest.hot_rows = WGRAD_HOT_ROWS;
+  return wgrad_up_t<bf16_t>(rest, dZ, x, H, I, dwg, dwu, s);
 }
 
 }  // namespace moe

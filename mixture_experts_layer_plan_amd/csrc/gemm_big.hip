@@ -245,6 +245,85 @@ struct OpMNCat {  // dgrad-up weights: K rows < I from W_g[e], the rest from W_u
   MOE_DEV bf16x8_t frag(const char* st, int c0, int ks, int) const { return frag_mn(st, c0, ks); }
 };
 
+// K-grouped MN-major operand (the wgrads): K row k is row seg0 + k of a row-major
+// matrix, columns c0 .. c0 + 255 (all valid).  K rows at or past the segment's
+// `n` rows read a 512-byte zero row in device memory, so the last K tile adds
+// exactly zero and never reads another expert's rows.
+__device__ __attribute__((aligned(16))) uint4 g_zero_row512[32];
+
+struct OpMNSeg {
+  const char* base;  // element (K row 0, column c0): wave-uniform
+  size_t ldb;        // row stride, bytes
+  uint32_t off;      // this lane's offset for instruction 0 (K row r0, its chunk)
+  uint32_t sstep;    // 16 K rows, bytes
+  uint32_t col;      // this lane's chunk offset
+  int r0, n;         // this lane's K row for instruction 0; rows in the segment
+  MOE_DEV void set(const bf16_t* b, size_t ld_elems, int rows) {
+    base = (const char*)b;
+    ldb = ld_elems * 2;
+    r0 = mn_row(0);
+    n = rows;
+    col = 16u * (uint32_t)((lane() & 31) ^ mnswz(r0));
+    off = (uint32_t)(r0 * ldb) + col;
+    sstep = (uint32_t)(16 * ldb);
+  }
+  MOE_DEV void issue(int kt, char* st) const {
+    const char* b = base + (size_t)kt * 64 * ldb;
+    if (64 * kt + 64 <= n) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) dma16(b + off + s * sstep, mn_dst(st, s));
+    } else {  // the segment's last K tile
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const char* src = 64 * kt + r0 + 16 * s < n ? b + off + s * sstep
+                                                      : (const char*)g_zero_row512 + col;
+        dma16(src, mn_dst(st, s));
+      }
+    }
+  }
+  MOE_DEV bf16x8_t frag(const char* st, int c0, int ks, int) const { return frag_mn(st, c0, ks); }
+};
+
+// Both operands MN-major (the wgrads): the twelve transposing reads of one 16-deep
+// step are issued as one block with a single wait, instead of six waits.
+MOE_DEV uint32_t lds_u32(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+MOE_DEV bf16x8_t join_tr(const s16x4_t& lo, const s16x4_t& hi) {
+  return __builtin_bit_cast(bf16x8_t, (s16x8_t)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5,
+                                                                        6, 7));
+}
+MOE_DEV void load_frags(const OpMNSeg&, const OpMNSeg&, const char* st, int, int ks, int wm, int wn,
+                        int, int, bf16x8_t (&a)[4], bf16x8_t (&b)[2]) {
+  const uint32_t base = lds_u32(st) + (uint32_t)(mn_lane_ofs() + ks * 16 * 512);
+  const uint32_t a0 = base + mn_blk_ofs(128 * wm), a1 = base + mn_blk_ofs(128 * wm + 32);
+  const uint32_t a2 = base + mn_blk_ofs(128 * wm + 64), a3 = base + mn_blk_ofs(128 * wm + 96);
+  const uint32_t b0 = base + STAGE + mn_blk_ofs(64 * wn), b1 = base + STAGE + mn_blk_ofs(64 * wn + 32);
+  s16x4_t r[12];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %12\n\t"
+      "ds_read_b64_tr_b16 %1, %12 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %2, %13\n\t"
+      "ds_read_b64_tr_b16 %3, %13 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %4, %14\n\t"
+      "ds_read_b64_tr_b16 %5, %14 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %6, %15\n\t"
+      "ds_read_b64_tr_b16 %7, %15 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %8, %16\n\t"
+      "ds_read_b64_tr_b16 %9, %16 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %10, %17\n\t"
+      "ds_read_b64_tr_b16 %11, %17 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11])
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(b0), "v"(b1)
+      : "memory");
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = join_tr(r[2 * i], r[2 * i + 1]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) b[j] = join_tr(r[8 + 2 * j], r[9 + 2 * j]);
+}
+
 template <class OA, class OB>
 MOE_DEV void load_frags(const OA& A, const OB& B, const char* st, int kt, int ks, int wm, int wn,
                         int ma, int mb, bf16x8_t (&a)[4], bf16x8_t (&b)[2]) {
@@ -469,6 +548,106 @@ __global__ __launch_bounds__(NTH, 1) void k_dgrad_up(GroupInfo g, const bf16_t* 
     }
 }
 
+// ------------------------------------------------------- K-grouped wgrads
+// Weight gradients of the experts with many rows, on this core: out[e][m, n] =
+// sum over the expert's rows r of A[r, m] B[r, n] (wgrad-up: A = dZ, B = X, M = 2I,
+// N = H, rows m < I to dW_g and the rest to dW_u; wgrad-down: A = dYu, B = g h,
+// M = H, N = I), K running over the expert's segment of the plan in row order.
+// Both operands are K-outer (MN-major) and read as they lie, no transposes.  The
+// experts with fewer rows and the zero gradients of the experts without rows stay
+// on the 128 x 128 kernel, whose two workgroups per CU overlap those short,
+// write-bound items.  (Measured on MI355X: storing the zero gradients from this
+// kernel, inside its K loop or from workgroups of their own, overlapped nothing.)
+//
+// Persistent grid (a multiple of 8 workgroups, one per CU); workgroup b runs on XCD
+// b mod 8.  Each expert's PM x PN-tile output is cut into 8 rectangles of tiles, one
+// per XCD, along M or N (equal when that count is a multiple of 8), and an XCD's
+// workgroups walk its rectangles of all hot experts in id order, M index fastest:
+// the workgroups an XCD runs at once share a few operand panels in its L2.  Every
+// output element is produced by one workgroup with a fixed K order.
+struct WgradArgs {
+  const int32_t* counts;
+  const int32_t* offsets;
+  int E, hot_rows;
+  const bf16_t* A;
+  const bf16_t* B;
+  int lda, ldb;          // row strides (elements)
+  bf16_t* out0;          // output rows m < half_rows
+  bf16_t* out1;          // output rows m >= half_rows (wgrad-up: dW_u)
+  int M, N, half_rows;   // per-expert output
+  int PM, PN, split_m;   // 256-tiles per expert along M and N; the axis split over XCDs
+};
+
+// wave 0 lists, in id order, the experts with >= hot_rows rows
+MOE_DEV int list_hot(const int32_t* counts, int E, int hot_rows, int* hot, int* n) {
+  if (wave() == 0) {
+    int nh = 0;
+    const uint64_t below = (1ull << lane()) - 1ull;
+    for (int b = 0; b < E; b += 64) {
+      const int e = b + lane();
+      const bool h = e < E && counts[e] >= hot_rows;
+      const uint64_t mh = __ballot(h);
+      if (h) hot[nh + __popcll(mh & below)] = e;
+      nh += __popcll(mh);
+    }
+    if (lane() == 0) n[0] = nh;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(n[0]);
+}
+
+__global__ __launch_bounds__(NTH, 1) void k_wgrad_hot(WgradArgs p) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS];
+  __shared__ int s_hot[MOE_MAX_E], s_n[1];
+  const int n_hot = list_hot(p.counts, p.E, p.hot_rows, s_hot, s_n);
+  const int x = blockIdx.x % N_XCD, slot = blockIdx.x / N_XCD, nslot = gridDim.x / N_XCD;
+  // this XCD's rectangle: tiles [m_lo, m_lo + pm) x [n_lo, n_lo + pn)
+  int m_lo = 0, n_lo = 0, pm = p.PM, pn = p.PN;
+  if (p.split_m) {
+    const int w = (p.PM + N_XCD - 1) / N_XCD;
+    m_lo = x * w;
+    pm = max(0, min(w, p.PM - m_lo));
+  } else {
+    const int w = (p.PN + N_XCD - 1) / N_XCD;
+    n_lo = x * w;
+    pn = max(0, min(w, p.PN - n_lo));
+  }
+  const int per = pm * pn;
+  const int nq = per * n_hot;  // tiles of this XCD
+  const long part0 = (long)p.half_rows * p.N, part1 = (long)(p.M - p.half_rows) * p.N;
+  for (int q = slot; q < nq; q += nslot) {
+    const int h = q / per, j = q - h * per;
+    const int e = __builtin_amdgcn_readfirstlane(s_hot[h]);
+    const int m0 = (m_lo + j % pm) * TILE, n0 = (n_lo + j / pm) * TILE;
+    const int seg0 = ld_uniform(p.offsets + e), n = ld_uniform(p.offsets + e + 1) - seg0;
+    OpMNSeg A, B;
+    A.set(p.A + (size_t)seg0 * p.lda + m0, (size_t)p.lda, n);
+    B.set(p.B + (size_t)seg0 * p.ldb + n0, (size_t)p.ldb, n);
+    Acc acc;
+    main_loop(lds, A, B, (n + 63) / 64, 4, 2, acc);
+    bf16_t* base = m0 < p.half_rows
+                       ? p.out0 + (size_t)e * part0 + (size_t)m0 * p.N + n0
+                       : p.out1 + (size_t)e * part1 + (size_t)(m0 - p.half_rows) * p.N + n0;
+    // row stride made opaque per tile: otherwise the 64 row offsets of the stores
+    // below are hoisted out of the tile loop and held in registers (spills)
+    int ld = p.N;
+    asm volatile("" : "+s"(ld));
+    bf16_t* lp = base + (size_t)out_row(0, 0) * ld + out_col(0);
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16_t* rp = lp + (size_t)(32 * bi + 8 * g4) * ld;
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            rp[(size_t)r * ld + 32 * bj] = f32_to_bf16(acc.c[bi][bj][4 * g4 + r]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  }
+}
+
 }  // namespace big
 
 // ------------------------------------------------------------------ launchers
@@ -504,6 +683,49 @@ hipError_t launch_big_dgrad_up(const GroupInfo& g, const void* dZ, const void* w
                     big::k_dgrad_up<<<ty * ((H + big::TILE - 1) / big::TILE), big::NTH, 0, s>>>(
                         g, (const bf16_t*)dZ, (const bf16_t*)wg, (const bf16_t*)wu, H, I,
                         (bf16_t*)dX));
+}
+
+// Wgrads of the experts with >= hot_rows rows (see k_wgrad_hot).
+// Returns hipErrorNotSupported, with nothing enqueued, for shapes this core does
+// not tile (the caller then runs the 128 x 128 kernel over every expert).
+static hipError_t wgrad_hot(const char* name, const GroupInfo& g, const void* A, int lda,
+                            const void* B, int ldb, void* out0, void* out1, int M, int N,
+                            int half_rows, int hot_rows, hipStream_t s) {
+  if (!g.offsets || !g.counts || M % big::TILE || N % big::TILE || half_rows % big::TILE ||
+      g.E > MOE_MAX_E || hot_rows < 1)
+    return hipErrorNotSupported;
+  big::WgradArgs p;
+  p.counts = g.counts;
+  p.offsets = g.offsets;
+  p.E = g.E;
+  p.hot_rows = hot_rows;
+  p.A = (const bf16_t*)A;
+  p.B = (const bf16_t*)B;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.out0 = (bf16_t*)out0;
+  p.out1 = (bf16_t*)out1;
+  p.M = M;
+  p.N = N;
+  p.half_rows = half_rows;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const unsigned grid = (unsigned)(cus >= N_XCD ? cus - cus % N_XCD : N_XCD);
+  p.PM = M / big::TILE;
+  p.PN = N / big::TILE;
+  p.split_m = p.PM % N_XCD == 0 ? 1 : p.PN % N_XCD == 0 ? 0 : (p.PM >= p.PN ? 1 : 0);
+  return MOE_LAUNCH(name, s, big::k_wgrad_hot<<<grid, big::NTH, 0, s>>>(p));
+}
+
+hipError_t launch_big_wgrad_up_hot(const GroupInfo& g, const void* dZ, const void* X, int H,
+                                   int I, void* dwg, void* dwu, int hot_rows, hipStream_t s) {
+  return wgrad_hot("gemm_wgrad_up_hot", g, dZ, 2 * I, X, H, dwg, dwu, 2 * I, H, I, hot_rows, s);
+}
+
+hipError_t launch_big_wgrad_down_hot(const GroupInfo& g, const void* dYu, const void* gh, int H,
+                                     int I, void* dwd, int hot_rows, hipStream_t s) {
+  return wgrad_hot("gemm_wgrad_down_hot", g, dYu, H, gh, I, dwd, nullptr, H, I, H, hot_rows, s);
 }
 
 }  // namespace moe

@@ -512,6 +512,22 @@ MOE_DEV int k_work_items(const GroupInfo& g, int mt_count, int nt_count) {
 
 MOE_DEV bool k_empty(const GroupInfo& g, int e) { return g.counts && ld_uniform(g.counts + e) == 0; }
 
+// What a K-grouped wgrad item of expert e does: 0 multiply, 1 store a zero tile,
+// 2 nothing (the large-tile kernel owns the expert's output).
+MOE_DEV int k_item_kind(const GroupInfo& g, int e) {
+  if (!g.counts) return 0;
+  const int c = ld_uniform(g.counts + e);
+  if (c == 0) return 1;
+  return c >= g.hot_rows ? 2 : 0;
+}
+
+// For an item w of expert e that is skipped: advance w so that the loop's next
+// step (w += gridDim.x) lands on this workgroup's first item of expert e + 1 or later.
+MOE_DEV int k_skip_expert(int w, int e, int per) {
+  const int nxt = (e + 1) * per;  // > w
+  return w + ((nxt - w - 1) / (int)gridDim.x) * (int)gridDim.x;
+}
+
 // Zero a TM x TN tile of T at out (row stride ld elements) with 16-byte
 // non-temporal stores.
 template <typename T>

@@ -86,6 +86,9 @@ struct GroupInfo {
   int max_wtiles;
   int dense_rows;            // row count in dense mode
   int E;
+  // K-grouped 128 x 128 wgrads: experts with >= hot_rows rows are left to the
+  // large-tile kernel (INT_MAX: this kernel takes every expert)
+  int hot_rows;
 };
 
 // bf16 large-tile kernels (gemm_big.hip) behind the launch_gemm_* entry points
@@ -95,6 +98,12 @@ hipError_t launch_big_down(const GroupInfo& g, const void* h, const void* wd, in
                            void* Y, hipStream_t s);
 hipError_t launch_big_dgrad_up(const GroupInfo& g, const void* dZ, const void* wg, const void* wu,
                                int H, int I, void* dX, hipStream_t s);
+// bf16 wgrads of the experts with >= hot_rows rows on the large tiles;
+// hipErrorNotSupported (nothing enqueued) for shapes the large tiles do not cover
+hipError_t launch_big_wgrad_up_hot(const GroupInfo& g, const void* dZ, const void* X, int H,
+                                   int I, void* dwg, void* dwu, int hot_rows, hipStream_t s);
+hipError_t launch_big_wgrad_down_hot(const GroupInfo& g, const void* dYu, const void* gh, int H,
+                                     int I, void* dwd, int hot_rows, hipStream_t s);
 
 // GEMM1 + SwiGLU: Z (fp32) [:, i] = A, Z[:, I + i] = B, h = silu(A) * B, with
 // A = X W_g[e]^T, B = X W_u[e]^T and X rows gathered from x through src_token.

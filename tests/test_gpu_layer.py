@@ -22,6 +22,9 @@ SMALL = {
     "k_eq_E_bf16": Shape(T=70, H=128, I=128, E=4, k=4),
     "one_token_bf16": Shape(T=1, H=128, I=128, E=8, k=2, I_shared=128),
     "hot_expert_bf16": Shape(T=700, H=256, I=256, E=32, k=2, zipf_s=4.0),
+    # two experts past the large-tile wgrad threshold (987 and 593 rows: ragged last
+    # K tiles), one just under it (255), small ones and six without rows; M / 256 = 8
+    "hot_wgrad_bf16": Shape(T=1024, H=2048, I=1024, E=16, k=2, zipf_s=2.0),
     "tiny_f32": CONFIGS["tiny_f32"],
     "ragged_f32": Shape(T=200, H=256, I=256, E=6, k=3, I_shared=128, dtype="f32"),
 }
