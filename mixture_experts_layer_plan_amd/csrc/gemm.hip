@@ -551,15 +551,18 @@ hipError_t launch_gemm_dgrad_up(int dt, const GroupInfo& g, const void* dZ, cons
 // Grouped bf16 wgrads: the experts with at least WGRAD_HOT_ROWS rows run on the
 // 256 x 256 core; the 128 x 128 kernel takes the experts with fewer rows (short K,
 // bound by their output writes) and stores the zero gradients of the experts
-// without rows.
+// without rows.  A dense operand pair (the shared expert) with at least that many
+// rows runs on the 256 x 256 core alone.
 constexpr int WGRAD_HOT_ROWS = 256;
 
 hipError_t launch_gemm_wgrad_down(int dt, const GroupInfo& g, const void* dy, const void* gh,
                                   int H, int I, void* dwd, hipStream_t s) {
   if (!dt) return wgrad_down_t<float>(g, dy, gh, H, I, dwd, s);
+  if (!g.offsets && g.dense_rows < WGRAD_HOT_ROWS)  // a short dense operand
+    return wgrad_down_t<bf16_t>(g, dy, gh, H, I, dwd, s);
   const hipError_t e = launch_big_wgrad_down_hot(g, dy, gh, H, I, dwd, WGRAD_HOT_ROWS, s);
   if (e == hipErrorNotSupported) return wgrad_down_t<bf16_t>(g, dy, gh, H, I, dwd, s);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !g.offsets) return e;
   GroupInfo rest = g;
   rest.hot_rows = WGRAD_HOT_ROWS;
   return wgrad_down_t<bf16_t>(rest, dy, gh, H, I, dwd, s);
@@ -567,9 +570,11 @@ hipError_t launch_gemm_wgrad_down(int dt, const GroupInfo& g, const void* dy, co
 hipError_t launch_gemm_wgrad_up(int dt, const GroupInfo& g, const void* dZ, const void* x,
                                 int H, int I, void* dwg, void* dwu, hipStream_t s) {
   if (!dt) return wgrad_up_t<float>(g, dZ, x, H, I, dwg, dwu, s);
+  if (!g.offsets && g.dense_rows < WGRAD_HOT_ROWS)  // a short dense operand
+    return wgrad_up_t<bf16_t>(g, dZ, x, H, I, dwg, dwu, s);
   const hipError_t e = launch_big_wgrad_up_hot(g, dZ, x, H, I, dwg, dwu, WGRAD_HOT_ROWS, s);
   if (e == hipErrorNotSupported) return wgrad_up_t<bf16_t>(g, dZ, x, H, I, dwg, dwu, s);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !g.offsets) return e;
   GroupInfo rest = g;
   rest.hot_rows = WGRAD_HOT_ROWS;
   return wgrad_up_t<bf16_t>(rest, dZ, x, H, I, dwg, dwu, s);

@@ -566,9 +566,9 @@ __global__ __launch_bounds__(NTH, 1) void k_dgrad_up(GroupInfo g, const bf16_t* 
 // the workgroups an XCD runs at once share a few operand panels in its L2.  Every
 // output element is produced by one workgroup with a fixed K order.
 struct WgradArgs {
-  const int32_t* counts;
+  const int32_t* counts;   // NULL: dense, one "expert" of dense_rows rows
   const int32_t* offsets;
-  int E, hot_rows;
+  int E, hot_rows, dense_rows;
   const bf16_t* A;
   const bf16_t* B;
   int lda, ldb;          // row strides (elements)
@@ -599,7 +599,7 @@ MOE_DEV int list_hot(const int32_t* counts, int E, int hot_rows, int* hot, int* 
 __global__ __launch_bounds__(NTH, 1) void k_wgrad_hot(WgradArgs p) {
   __shared__ __attribute__((aligned(16))) char lds[LDS];
   __shared__ int s_hot[MOE_MAX_E], s_n[1];
-  const int n_hot = list_hot(p.counts, p.E, p.hot_rows, s_hot, s_n);
+  const int n_hot = p.counts ? list_hot(p.counts, p.E, p.hot_rows, s_hot, s_n) : 1;
   const int x = blockIdx.x % N_XCD, slot = blockIdx.x / N_XCD, nslot = gridDim.x / N_XCD;
   // this XCD's rectangle: tiles [m_lo, m_lo + pm) x [n_lo, n_lo + pn)
   int m_lo = 0, n_lo = 0, pm = p.PM, pn = p.PN;
@@ -617,9 +617,10 @@ __global__ __launch_bounds__(NTH, 1) void k_wgrad_hot(WgradArgs p) {
   const long part0 = (long)p.half_rows * p.N, part1 = (long)(p.M - p.half_rows) * p.N;
   for (int q = slot; q < nq; q += nslot) {
     const int h = q / per, j = q - h * per;
-    const int e = __builtin_amdgcn_readfirstlane(s_hot[h]);
+    const int e = p.counts ? __builtin_amdgcn_readfirstlane(s_hot[h]) : 0;
     const int m0 = (m_lo + j % pm) * TILE, n0 = (n_lo + j / pm) * TILE;
-    const int seg0 = ld_uniform(p.offsets + e), n = ld_uniform(p.offsets + e + 1) - seg0;
+    const int seg0 = p.counts ? ld_uniform(p.offsets + e) : 0;
+    const int n = p.counts ? ld_uniform(p.offsets + e + 1) - seg0 : p.dense_rows;
     OpMNSeg A, B;
     A.set(p.A + (size_t)seg0 * p.lda + m0, (size_t)p.lda, n);
     B.set(p.B + (size_t)seg0 * p.ldb + n0, (size_t)p.ldb, n);
@@ -685,20 +686,23 @@ hipError_t launch_big_dgrad_up(const GroupInfo& g, const void* dZ, const void* w
                         (bf16_t*)dX));
 }
 
-// Wgrads of the experts with >= hot_rows rows (see k_wgrad_hot).
-// Returns hipErrorNotSupported, with nothing enqueued, for shapes this core does
-// not tile (the caller then runs the 128 x 128 kernel over every expert).
+// Wgrads of the experts with >= hot_rows rows (see k_wgrad_hot); in dense mode (the
+// shared expert) the one dense operand pair.  Returns hipErrorNotSupported, with
+// nothing enqueued, for shapes this core does not tile (the caller then runs the
+// 128 x 128 kernel over every expert).
 static hipError_t wgrad_hot(const char* name, const GroupInfo& g, const void* A, int lda,
                             const void* B, int ldb, void* out0, void* out1, int M, int N,
                             int half_rows, int hot_rows, hipStream_t s) {
-  if (!g.offsets || !g.counts || M % big::TILE || N % big::TILE || half_rows % big::TILE ||
+  const bool dense = !g.offsets;
+  if ((!dense && !g.counts) || M % big::TILE || N % big::TILE || half_rows % big::TILE ||
       g.E > MOE_MAX_E || hot_rows < 1)
     return hipErrorNotSupported;
   big::WgradArgs p;
-  p.counts = g.counts;
+  p.counts = dense ? nullptr : g.counts;
   p.offsets = g.offsets;
   p.E = g.E;
   p.hot_rows = hot_rows;
+  p.dense_rows = g.dense_rows;
   p.A = (const bf16_t*)A;
   p.B = (const bf16_t*)B;
   p.lda = lda;
@@ -720,12 +724,14 @@ static hipError_t wgrad_hot(const char* name, const GroupInfo& g, const void* A,
 
 hipError_t launch_big_wgrad_up_hot(const GroupInfo& g, const void* dZ, const void* X, int H,
                                    int I, void* dwg, void* dwu, int hot_rows, hipStream_t s) {
-  return wgrad_hot("gemm_wgrad_up_hot", g, dZ, 2 * I, X, H, dwg, dwu, 2 * I, H, I, hot_rows, s);
+  return wgrad_hot(g.offsets ? "gemm_wgrad_up_hot" : "gemm_wgrad_up_shared", g, dZ, 2 * I, X, H,
+                   dwg, dwu, 2 * I, H, I, hot_rows, s);
 }
 
 hipError_t launch_big_wgrad_down_hot(const GroupInfo& g, const void* dYu, const void* gh, int H,
                                      int I, void* dwd, int hot_rows, hipStream_t s) {
-  return wgrad_hot("gemm_wgrad_down_hot", g, dYu, H, gh, I, dwd, nullptr, H, I, H, hot_rows, s);
+  return wgrad_hot(g.offsets ? "gemm_wgrad_down_hot" : "gemm_wgrad_down_shared", g, dYu, H, gh, I,
+                   dwd, nullptr, H, I, H, hot_rows, s);
 }
 
 }  // namespace moe
