@@ -30,6 +30,9 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "mxfp8": 5000.0}
 # rows from which an expert's bf16 weight gradients run on the 256 x 256 tiles (the
 # library's split of the K-grouped wgrads)
 WGRAD_HOT_ROWS = 256
+# bytes of packed token range from which an expert's MXFP8 weight gradients run on the
+# 256 x 256 tiles
+MX_WGRAD_HOT_BYTES = 256
 METRIC = "MoE layer tokens/s fwd+bwd @H7168 I2048 E256 top8, 1 GPU; % MFMA/HBM peak"
 
 
@@ -55,6 +58,13 @@ def kernel_work(name, sh, counts_mb, es=2):
     hot_split = es == 2 and H % 256 == 0 and I % 256 == 0 and not sh.T_minibatch
     Eh = sum(1 for v in union if v >= WGRAD_HOT_ROWS) if hot_split else 0
     Rh = sum(v for v in union if v >= WGRAD_HOT_ROWS) if hot_split else 0
+    # MXFP8 wgrads: experts whose packed token range (each minibatch segment padded to
+    # 32 rows) has >= MX_WGRAD_HOT_BYTES bytes go to the 256-tile kernel
+    packed = [sum(-(-c[e] // 32) * 32 for c in counts_mb) for e in range(E)]
+    mx_hot = [e for e in range(E) if packed[e] >= MX_WGRAD_HOT_BYTES] \
+        if H % 256 == 0 and I % 256 == 0 else []
+    Emx = len(mx_hot)
+    Rmx = sum(union[e] for e in mx_hot)
 
     def over_mb(f):
         b = fl = 0.0
@@ -111,8 +121,14 @@ def kernel_work(name, sh, counts_mb, es=2):
         "mx_gemm_dgrad_up": lambda: over_mb(lambda Rm, Etm, tm: (
             Etm * 2 * I * H * q + Rm * 2 * I * q + Rm * H * 2, 2 * Rm * 2 * I * H)),
         # the MX wgrads also store the zero gradients of the E - Et experts without rows
-        "mx_gemm_wgrad_down": lambda: (int(R * (H + I) * q + E * H * I * 2), 2 * R * H * I),
-        "mx_gemm_wgrad_up": lambda: (int(R * (2 * I + H) * q + E * 2 * I * H * 2), 2 * R * 2 * I * H),
+        "mx_gemm_wgrad_down": lambda: (int((R - Rmx) * (H + I) * q + (E - Emx) * H * I * 2),
+                                       2 * (R - Rmx) * H * I),
+        "mx_gemm_wgrad_up": lambda: (int((R - Rmx) * (2 * I + H) * q + (E - Emx) * 2 * I * H * 2),
+                                     2 * (R - Rmx) * 2 * I * H),
+        "mx_gemm_wgrad_down_hot": lambda: (int(Rmx * (H + I) * q + Emx * H * I * 2), 2 * Rmx * H * I),
+        "mx_gemm_wgrad_up_hot": lambda: (int(Rmx * (2 * I + H) * q + Emx * 2 * I * H * 2),
+                                         2 * Rmx * 2 * I * H),
+        "mx_zero_tail": lambda: ((2 * H + I + 2 * I) * 128, 0),  # both wgrads' operand rows
     }
     f = w.get(name)
     return f() if f else (0, 0)

@@ -636,13 +636,26 @@ moe_status backward_mx_impl(const moe_shape* s, const void* plan, const void* x,
                                 dxs ? (const bf16_t_host*)dxs + tok0 * H : nullptr,
                                 (bf16_t_host*)dx + tok0 * H, T_m, k, H, st));
   }
-  // the wgrads also store the zero gradients of experts without rows
+  // Experts with a long packed token range run on the 256-tile kernel; the 128-tile
+  // kernel takes the others and stores the zero gradients of experts without rows.
+  int hot = MX_WGRAD_HOT_BYTES;
+  hipError_t e1 = launch_mx_wgrad_hot("mx_gemm_wgrad_down_hot", mp, s->E, at<uint8_t>(ws, W.dYuT8),
+                                      at<uint8_t>(ws, W.dYuTs), at<uint8_t>(ws, W.ghT8),
+                                      at<uint8_t>(ws, W.ghTs), H, I, H, W.Kp, dwd, nullptr, hot, st);
+  if (e1 == hipErrorNotSupported) hot = 0;
+  else if (e1 != hipSuccess) return hip_status(e1);
   MOE_TRY(launch_mx_wgrad("mx_gemm_wgrad_down", mp, s->E, at<uint8_t>(ws, W.dYuT8),
                           at<uint8_t>(ws, W.dYuTs), at<uint8_t>(ws, W.ghT8),
-                          at<uint8_t>(ws, W.ghTs), H, I, H, W.Kp, dwd, nullptr, st));
+                          at<uint8_t>(ws, W.ghTs), H, I, H, W.Kp, dwd, nullptr, hot, st));
+  hot = MX_WGRAD_HOT_BYTES;
+  e1 = launch_mx_wgrad_hot("mx_gemm_wgrad_up_hot", mp, s->E, at<uint8_t>(ws, W.dZT8),
+                           at<uint8_t>(ws, W.dZTs), at<uint8_t>(ws, W.XT8), at<uint8_t>(ws, W.XTs),
+                           2 * I, H, I, W.Kp, dwg, dwu, hot, st);
+  if (e1 == hipErrorNotSupported) hot = 0;
+  else if (e1 != hipSuccess) return hip_status(e1);
   MOE_TRY(launch_mx_wgrad("mx_gemm_wgrad_up", mp, s->E, at<uint8_t>(ws, W.dZT8),
                           at<uint8_t>(ws, W.dZTs), at<uint8_t>(ws, W.XT8), at<uint8_t>(ws, W.XTs),
-                          2 * I, H, I, W.Kp, dwg, dwu, st));
+                          2 * I, H, I, W.Kp, dwg, dwu, hot, st));
   return MOE_OK;
 }
 

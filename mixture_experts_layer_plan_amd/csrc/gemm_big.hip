@@ -649,6 +649,239 @@ __global__ __launch_bounds__(NTH, 1) void k_wgrad_hot(WgradArgs p) {
   }
 }
 
+// ------------------------------------------------------- MXFP8 K-grouped wgrads
+// The MXFP8 weight gradients of the experts with many rows, on this core.  Both
+// operands are the token-axis-transposed E4M3 rows of the MX path (A: rows of M,
+// B: rows of N, each Kp bytes long, one E8M0 scale byte per 32 along the packed
+// token axis; expert e owns bytes [kpos[e], kpos[e + 1]) of every row, a multiple of
+// 32).  A stage is a 128-byte K piece of 256 rows per operand, in the K-major layout
+// of the bf16 kernels (bytes are bytes), and feeds two 64-deep steps of the scaled
+// MFMA v_mfma_scale_f32_32x32x64_f8f6f4.  In that instruction lane i + 32 h holds
+// row i and takes bytes 0-15 from K block 0 and 16-31 from K block 1 of its step,
+// and the scale of (row i, block c) comes from lane i + 32 c: lane (i, h) reads the
+// 16-byte chunks 4 ks + h and 4 ks + 2 + h of its row, and uses byte 2 ks + h of its
+// row's scale word.  Scale words of the stage after the current one are loaded with
+// its data; the bytes of blocks at or past the expert's end are set to 0 (2^-127),
+// so those blocks' products (next expert's codes, or the zero tail written after
+// the packed axis) vanish.
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+struct DmaKB {  // K-major byte rows at a fixed stride
+  const char* base;  // row 0, K byte 0 of this expert's range
+  uint32_t off;      // this lane's row for instruction 0, chunk included
+  uint32_t step;     // 64 rows, bytes
+  MOE_DEV void set(const uint8_t* b, size_t ld) {
+    base = (const char*)b;
+    off = (uint32_t)(kmaj_row(0) * ld) + 16u * kmaj_chunk();
+    step = (uint32_t)(64 * ld);
+  }
+  MOE_DEV void issue(int kt, char* st) const {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dma16(base + (size_t)kt * 128 + off + s * step, kmaj_dst(st, s));
+  }
+};
+
+// this lane's scale words of one stage: A blocks 0..3, B blocks 0..1
+struct MxScales {
+  uint32_t a[4], b[2];
+};
+struct MxScaleRows {
+  const uint8_t* as;  // scale byte (row of A block 0 for this lane, K block of k0)
+  const uint8_t* bs;
+  uint32_t astep;     // 32 rows of A scales, bytes
+  uint32_t bstep;     // 32 rows of B scales
+  long kbytes;        // bytes of the expert's range
+  MOE_DEV void load(int kt, MxScales& sc) const {
+    const long nb = (kbytes - (long)kt * 128) / 32;  // blocks of this stage inside the range
+    const uint32_t keep = nb >= 4 ? 0xffffffffu : (nb <= 0 ? 0u : (1u << (8 * nb)) - 1u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      sc.a[i] = *(const uint32_t*)(as + i * astep + 4 * kt) & keep;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      sc.b[j] = *(const uint32_t*)(bs + j * bstep + 4 * kt) & keep;
+  }
+};
+
+MOE_DEV i32x8_t frag_mx(const char* st, int r0, int ks) {
+  const int r = r0 + (lane() & 31), h = lane() >> 5;
+  const uint4 x = *(const uint4*)(st + swz(r, 4 * ks + h));
+  const uint4 y = *(const uint4*)(st + swz(r, 4 * ks + 2 + h));
+  i32x8_t v;
+  v[0] = (int)x.x; v[1] = (int)x.y; v[2] = (int)x.z; v[3] = (int)x.w;
+  v[4] = (int)y.x; v[5] = (int)y.y; v[6] = (int)y.z; v[7] = (int)y.w;
+  return v;
+}
+
+MOE_DEV void mma_stage_mx(const char* st, const MxScales& sc, int wm, int wn, Acc& acc) {
+  const int h = lane() >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int sh = 8 * (2 * ks + h);
+    i32x8_t a[4], b[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = frag_mx(st, 128 * wm + 32 * i, ks);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[j] = frag_mx(st + STAGE, 64 * wn + 32 * j, ks);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc.c[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            a[i], b[j], acc.c[i][j], 0, 0, 0, (int)((sc.a[i] >> sh) & 0xffu), 0,
+            (int)((sc.b[j] >> sh) & 0xffu));
+  }
+}
+
+// One K stage: issue stage kn's data into `nxt` and its scale words into sn, multiply
+// stage `cur` with sc, wait for this wavefront's loads, meet the workgroup.
+MOE_DEV void stage_mx(const DmaKB& A, const DmaKB& B, const MxScaleRows& S, int kn,
+                      const char* cur, char* nxt, const MxScales& sc, MxScales& sn, int wm, int wn,
+                      Acc& acc) {
+  A.issue(kn, nxt);
+  B.issue(kn, nxt + STAGE);
+  S.load(kn, sn);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_stage_mx(cur, sc, wm, wn, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Two LDS stages: stage kt + 1 (data and scale words) loads while stage kt
+// multiplies.  The loop is unrolled by two with the scale words in two fixed sets
+// (no copy from "next" to "current"): with a copy the compiler waits for the next
+// stage's scale loads, and so for every load in flight, before the current stage's
+// MFMAs.
+MOE_DEV void main_loop_mx(char* lds, const DmaKB& A, const DmaKB& B, const MxScaleRows& S, int nk,
+                          Acc& acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc.c[i][j][v] = 0.0f;
+  if (nk <= 0) return;
+  const int wm = wave() >> 2, wn = wave() & 3;
+  char* b0 = lds;
+  char* b1 = lds + 2 * STAGE;
+  MxScales s0, s1;
+  A.issue(0, b0);
+  B.issue(0, b0 + STAGE);
+  S.load(0, s0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // the last stage reloads itself into the idle buffer (never read)
+  for (int kt = 0; kt < nk; kt += 2) {
+    stage_mx(A, B, S, kt + 1 < nk ? kt + 1 : kt, b0, b1, s0, s1, wm, wn, acc);
+    if (kt + 1 < nk) stage_mx(A, B, S, kt + 2 < nk ? kt + 2 : kt + 1, b1, b0, s1, s0, wm, wn, acc);
+  }
+  __syncthreads();  // LDS free for another tile
+}
+
+struct MxWgradArgs {
+  const int32_t* kpos;  // [E + 1] packed token-axis offsets (bytes)
+  int E, hot_bytes;
+  const uint8_t* A8;
+  const uint8_t* As;
+  const uint8_t* B8;
+  const uint8_t* Bs;
+  long Kp;              // row length of A8, B8 (bytes); scale rows are Kp / 32
+  bf16_t* out0;
+  bf16_t* out1;
+  int M, N, half_rows;
+  int PM, PN, split_m;
+};
+
+// wave 0 lists, in id order, the experts whose packed range has >= hot_bytes bytes
+MOE_DEV int list_hot_kpos(const int32_t* kpos, int E, int hot_bytes, int* hot, int* n) {
+  if (wave() == 0) {
+    int nh = 0;
+    const uint64_t below = (1ull << lane()) - 1ull;
+    for (int b = 0; b < E; b += 64) {
+      const int e = b + lane();
+      const bool h = e < E && kpos[e + 1] - kpos[e] >= hot_bytes;
+      const uint64_t mh = __ballot(h);
+      if (h) hot[nh + __popcll(mh & below)] = e;
+      nh += __popcll(mh);
+    }
+    if (lane() == 0) n[0] = nh;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(n[0]);
+}
+
+__global__ __launch_bounds__(NTH, 1) void k_wgrad_hot_mx(MxWgradArgs p) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS];
+  __shared__ int s_hot[MOE_MAX_E], s_n[1];
+  const int n_hot = list_hot_kpos(p.kpos, p.E, p.hot_bytes, s_hot, s_n);
+  const int x = blockIdx.x % N_XCD, slot = blockIdx.x / N_XCD, nslot = gridDim.x / N_XCD;
+  int m_lo = 0, n_lo = 0, pm = p.PM, pn = p.PN;
+  if (p.split_m) {
+    const int w = (p.PM + N_XCD - 1) / N_XCD;
+    m_lo = x * w;
+    pm = max(0, min(w, p.PM - m_lo));
+  } else {
+    const int w = (p.PN + N_XCD - 1) / N_XCD;
+    n_lo = x * w;
+    pn = max(0, min(w, p.PN - n_lo));
+  }
+  const int per = pm * pn;
+  const int nq = per * n_hot;
+  const long KS = p.Kp / 32;
+  const long part0 = (long)p.half_rows * p.N, part1 = (long)(p.M - p.half_rows) * p.N;
+  const int wm = wave() >> 2, wn = wave() & 3;
+  for (int q = slot; q < nq; q += nslot) {
+    const int h = q / per, j = q - h * per;
+    const int e = __builtin_amdgcn_readfirstlane(s_hot[h]);
+    const int m0 = (m_lo + j % pm) * TILE, n0 = (n_lo + j / pm) * TILE;
+    const long k0 = ld_uniform(p.kpos + e), kb = ld_uniform(p.kpos + e + 1) - k0;
+    DmaKB A, B;
+    A.set(p.A8 + (size_t)m0 * p.Kp + k0, (size_t)p.Kp);
+    B.set(p.B8 + (size_t)n0 * p.Kp + k0, (size_t)p.Kp);
+    MxScaleRows S;
+    S.as = p.As + (size_t)(m0 + 128 * wm + (lane() & 31)) * KS + k0 / 32;
+    S.bs = p.Bs + (size_t)(n0 + 64 * wn + (lane() & 31)) * KS + k0 / 32;
+    S.astep = (uint32_t)(32 * KS);
+    S.bstep = (uint32_t)(32 * KS);
+    S.kbytes = kb;
+    Acc acc;
+    main_loop_mx(lds, A, B, S, (int)((kb + 127) / 128), acc);
+    bf16_t* base = m0 < p.half_rows
+                       ? p.out0 + (size_t)e * part0 + (size_t)m0 * p.N + n0
+                       : p.out1 + (size_t)e * part1 + (size_t)(m0 - p.half_rows) * p.N + n0;
+    int ld = p.N;  // opaque per tile (see k_wgrad_hot)
+    asm volatile("" : "+s"(ld));
+    bf16_t* lp = base + (size_t)out_row(0, 0) * ld + out_col(0);
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16_t* rp = lp + (size_t)(32 * bi + 8 * g4) * ld;
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            rp[(size_t)r * ld + 32 * bj] = f32_to_bf16(acc.c[bi][bj][4 * g4 + r]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  }
+}
+
+// Zero the 128 bytes after the packed token axis of every row (stages of the last
+// expert read up to 96 bytes past its range; those bytes are otherwise never written).
+__global__ __launch_bounds__(256) void mx_zero_tail_kernel(uint8_t* __restrict__ q, int rows,
+                                                           long Kp,
+                                                           const int32_t* __restrict__ kend) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;  // 16-byte piece
+  if (i >= (long)rows * 8) return;
+  const long row = i / 8, b = kend[0] + 16 * (i % 8);
+  if (b + 16 > Kp) return;  // the row ends first (at least 96 bytes follow kpos[E])
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  *(u32x4_t*)(q + row * Kp + b) = z;
+}
+
 }  // namespace big
 
 // ------------------------------------------------------------------ launchers
@@ -732,6 +965,48 @@ hipError_t launch_big_wgrad_down_hot(const GroupInfo& g, const void* dYu, const 
                                      int I, void* dwd, int hot_rows, hipStream_t s) {
   return wgrad_hot(g.offsets ? "gemm_wgrad_down_hot" : "gemm_wgrad_down_shared", g, dYu, H, gh, I,
                    dwd, nullptr, H, I, H, hot_rows, s);
+}
+
+// MXFP8 wgrads of the experts whose packed token range has >= hot_bytes bytes
+// (k_wgrad_hot_mx), after zeroing the tails of both operands past kpos[E];
+// hipErrorNotSupported (nothing enqueued) for shapes the 256-tiles do not cover.
+hipError_t launch_mx_wgrad_hot(const char* name, const MbPlans& mp, int E, uint8_t* A8,
+                               const uint8_t* As, uint8_t* B8, const uint8_t* Bs, int M, int N,
+                               int split, size_t Kp, void* out0, void* out1, int hot_bytes,
+                               hipStream_t s) {
+  if (M % big::TILE || N % big::TILE || split % big::TILE || E > MOE_MAX_E || hot_bytes < 128 ||
+      Kp % 128)
+    return hipErrorNotSupported;
+  big::MxWgradArgs p;
+  p.kpos = mp.kpos;
+  p.E = E;
+  p.hot_bytes = hot_bytes;
+  p.A8 = A8;
+  p.As = As;
+  p.B8 = B8;
+  p.Bs = Bs;
+  p.Kp = (long)Kp;
+  p.out0 = (bf16_t*)out0;
+  p.out1 = (bf16_t*)out1;
+  p.M = M;
+  p.N = N;
+  p.half_rows = split;
+  p.PM = M / big::TILE;
+  p.PN = N / big::TILE;
+  p.split_m = p.PM % N_XCD == 0 ? 1 : p.PN % N_XCD == 0 ? 0 : (p.PM >= p.PN ? 1 : 0);
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const unsigned grid = (unsigned)(cus >= N_XCD ? cus - cus % N_XCD : N_XCD);
+  hipError_t err = MOE_LAUNCH("mx_zero_tail", s,
+                              big::mx_zero_tail_kernel<<<(M * 8 + 255) / 256, 256, 0, s>>>(
+                                  A8, M, (long)Kp, mp.kpos + E));
+  if (err != hipSuccess) return err;
+  err = MOE_LAUNCH("mx_zero_tail", s,
+                   big::mx_zero_tail_kernel<<<(N * 8 + 255) / 256, 256, 0, s>>>(
+                       B8, N, (long)Kp, mp.kpos + E));
+  if (err != hipSuccess) return err;
+  return MOE_LAUNCH(name, s, big::k_wgrad_hot_mx<<<grid, big::NTH, 0, s>>>(p));
 }
 
 }  // namespace moe

@@ -457,13 +457,15 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_mx(MbPlans mp, int E, bool m_
                                                       const uint8_t* __restrict__ Bs, int M, int N,
                                                       int split, long Kp,
                                                       bf16_t* __restrict__ out0,
-                                                      bf16_t* __restrict__ out1) {
+                                                      bf16_t* __restrict__ out1, int hot_bytes) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   const int MT = M / TM, NT = N / TN, lane = threadIdx.x & 63;
   const long KS = Kp / 32;
   // one workgroup per (expert, tile) over all E experts, in id order and spread over
   // the XCDs round-robin; the tiles of an expert with no row in any minibatch (an
-  // empty run of the token axis) are stored as zeros
+  // empty run of the token axis) are stored as zeros; the experts whose range has
+  // >= hot_bytes bytes belong to the large-tile kernel (a persistent form of this
+  // loop spilled 68 registers and measured slower)
   const int id = blockIdx.x;
   if (id >= E * MT * NT) return;
   int arow, brow[2];
@@ -480,6 +482,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_mx(MbPlans mp, int E, bool m_
   }
   const KFrom km{ld_uniform(mp.kpos + e)};
   const long kend = ld_uniform(mp.kpos + e + 1);
+  if (hot_bytes > 0 && kend - km.k0 >= hot_bytes) return;
   const int nk = (int)((kend - km.k0 + MX_BK - 1) / MX_BK);
   MxOp oa, ob;
   mx_op_clear(oa);
@@ -554,13 +557,14 @@ hipError_t launch_mx_dgrad_up(const GroupInfo& g, const uint8_t* dZ8, const uint
 
 hipError_t launch_mx_wgrad(const char* name, const MbPlans& mp, int E, const uint8_t* A8,
                            const uint8_t* As, const uint8_t* B8, const uint8_t* Bs, int M, int N,
-                           int split, size_t Kp, void* out0, void* out1, hipStream_t s) {
+                           int split, size_t Kp, void* out0, void* out1, int hot_bytes,
+                           hipStream_t s) {
   const unsigned grid = (unsigned)E * (M / TM) * (N / TN);
   // one output (split == M) is wgrad-down, whose M runs along H
   return MOE_LAUNCH(name, s,
                     k_wgrad_mx<<<grid, NTHR, 0, s>>>(mp, E, split == M, A8, As, B8, Bs, M, N,
                                                      split, (long)Kp, (bf16_t*)out0,
-                                                     (bf16_t*)out1));
+                                                     (bf16_t*)out1, hot_bytes));
 }
 
 }  // namespace moe

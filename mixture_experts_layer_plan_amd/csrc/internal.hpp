@@ -129,6 +129,9 @@ hipError_t launch_gemm_wgrad_up(int dt, const GroupInfo& g, const void* dZ, cons
 
 // ------------------------------------------------------------------ MXFP8
 #define MX_MAX_MB 8  // minibatches per macro batch in the MX path
+// MX wgrads: experts whose packed token range (all minibatches, each segment padded
+// to 32) has at least this many bytes run on the 256 x 256 core
+constexpr int MX_WGRAD_HOT_BYTES = 256;
 
 // Row quantisation: q[r] = E4M3 of src[gather ? gather[r] : r] (cols values) with
 // one scale per 32; rows r < min(n_rows, *n_rows_dev) (n_rows_dev may be NULL).
@@ -180,8 +183,17 @@ hipError_t launch_mx_dgrad_down(const GroupInfo& g, const uint8_t* dYu8, const u
 hipError_t launch_mx_dgrad_up(const GroupInfo& g, const uint8_t* dZ8, const uint8_t* dZs,
                               const uint8_t* wgT8, const uint8_t* wgTs, const uint8_t* wuT8,
                               const uint8_t* wuTs, int H, int I, void* dX, hipStream_t s);
+// experts whose packed range has >= hot_bytes bytes are skipped (0: none)
 hipError_t launch_mx_wgrad(const char* name, const MbPlans& mp, int E, const uint8_t* A8,
                            const uint8_t* As, const uint8_t* B8, const uint8_t* Bs, int M, int N,
-                           int split, size_t Kp, void* out0, void* out1, hipStream_t s);
+                           int split, size_t Kp, void* out0, void* out1, int hot_bytes,
+                           hipStream_t s);
+// The same wgrads for the experts whose packed range has >= hot_bytes bytes on the
+// 256 x 256 core (zeroes the operands' bytes past kpos[E] first); hipErrorNotSupported
+// (nothing enqueued) for shapes the 256-tiles do not cover.
+hipError_t launch_mx_wgrad_hot(const char* name, const MbPlans& mp, int E, uint8_t* A8,
+                               const uint8_t* As, uint8_t* B8, const uint8_t* Bs, int M, int N,
+                               int split, size_t Kp, void* out0, void* out1, int hot_bytes,
+                               hipStream_t s);
 
 }  // namespace moe

@@ -57,3 +57,13 @@ def check(got, ref, kind="bf16", what="", allowance=None):
     assert not bad.any(), (f"{what}: {bad.sum()} of {r.size} elements out of tolerance; worst "
                            f"{np.max(np.abs(d) / bound):.2f}x the bound")
     return rel
+
+
+def check_norm(got, ref, kind="bf16", what=""):
+    """The normwise bound alone (see test_mx_hot_expert_weight_gradients)."""
+    g, r = f64(got), f64(ref)
+    assert g.shape == r.shape, f"{what}: shape {g.shape} vs {r.shape}"
+    nr = np.linalg.norm(r)
+    rel = np.linalg.norm(g - r) / nr if nr else np.linalg.norm(g)
+    assert rel <= TOL[kind][0], f"{what}: normwise rel err {rel:.3e} > {TOL[kind][0]}"
+    return rel
