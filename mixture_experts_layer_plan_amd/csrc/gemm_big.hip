@@ -560,11 +560,22 @@ __global__ __launch_bounds__(NTH, 1) void k_dgrad_up(GroupInfo g, const bf16_t* 
 // kernel, inside its K loop or from workgroups of their own, overlapped nothing.)
 //
 // Persistent grid (a multiple of 8 workgroups, one per CU); workgroup b runs on XCD
-// b mod 8.  Each expert's PM x PN-tile output is cut into 8 rectangles of tiles, one
-// per XCD, along M or N (equal when that count is a multiple of 8), and an XCD's
-// workgroups walk its rectangles of all hot experts in id order, M index fastest:
-// the workgroups an XCD runs at once share a few operand panels in its L2.  Every
+// b mod 8.  Each expert's PM x PN-tile output is cut into a GM x (8 / GM) grid of
+// rectangles, one per XCD, chosen as square as the counts allow (fewest operand
+// panels per XCD: each panel an XCD reads comes from the Infinity Cache or HBM), and
+// an XCD's workgroups walk its rectangles of all hot experts in id order, M index
+// fastest: the workgroups an XCD runs at once share a few panels in its L2.  Every
 // output element is produced by one workgroup with a fixed K order.
+// XCD x's rectangle of an expert's PM x PN output tiles: the 8 XCDs form a GM x
+// (8 / GM) grid over the tiles (XCD x at row x / (8 / GM), column x % (8 / GM)).
+MOE_DEV void xcd_rect(int PM, int PN, int GM, int x, int& m_lo, int& n_lo, int& pm, int& pn) {
+  const int GN = N_XCD / GM, wm = (PM + GM - 1) / GM, wn = (PN + GN - 1) / GN;
+  m_lo = (x / GN) * wm;
+  n_lo = (x % GN) * wn;
+  pm = max(0, min(wm, PM - m_lo));
+  pn = max(0, min(wn, PN - n_lo));
+}
+
 struct WgradArgs {
   const int32_t* counts;   // NULL: dense, one "expert" of dense_rows rows
   const int32_t* offsets;
@@ -575,7 +586,7 @@ struct WgradArgs {
   bf16_t* out0;          // output rows m < half_rows
   bf16_t* out1;          // output rows m >= half_rows (wgrad-up: dW_u)
   int M, N, half_rows;   // per-expert output
-  int PM, PN, split_m;   // 256-tiles per expert along M and N; the axis split over XCDs
+  int PM, PN, GM;        // 256-tiles per expert along M and N; XCD groups along M
 };
 
 // wave 0 lists, in id order, the experts with >= hot_rows rows
@@ -601,17 +612,8 @@ __global__ __launch_bounds__(NTH, 1) void k_wgrad_hot(WgradArgs p) {
   __shared__ int s_hot[MOE_MAX_E], s_n[1];
   const int n_hot = p.counts ? list_hot(p.counts, p.E, p.hot_rows, s_hot, s_n) : 1;
   const int x = blockIdx.x % N_XCD, slot = blockIdx.x / N_XCD, nslot = gridDim.x / N_XCD;
-  // this XCD's rectangle: tiles [m_lo, m_lo + pm) x [n_lo, n_lo + pn)
-  int m_lo = 0, n_lo = 0, pm = p.PM, pn = p.PN;
-  if (p.split_m) {
-    const int w = (p.PM + N_XCD - 1) / N_XCD;
-    m_lo = x * w;
-    pm = max(0, min(w, p.PM - m_lo));
-  } else {
-    const int w = (p.PN + N_XCD - 1) / N_XCD;
-    n_lo = x * w;
-    pn = max(0, min(w, p.PN - n_lo));
-  }
+  int m_lo, n_lo, pm, pn;  // this XCD's rectangle: tiles [m_lo, +pm) x [n_lo, +pn)
+  xcd_rect(p.PM, p.PN, p.GM, x, m_lo, n_lo, pm, pn);
   const int per = pm * pn;
   const int nq = per * n_hot;  // tiles of this XCD
   const long part0 = (long)p.half_rows * p.N, part1 = (long)(p.M - p.half_rows) * p.N;
@@ -791,7 +793,7 @@ struct MxWgradArgs {
   bf16_t* out0;
   bf16_t* out1;
   int M, N, half_rows;
-  int PM, PN, split_m;
+  int PM, PN, GM;
 };
 
 // wave 0 lists, in id order, the experts whose packed range has >= hot_bytes bytes
@@ -817,16 +819,8 @@ __global__ __launch_bounds__(NTH, 1) void k_wgrad_hot_mx(MxWgradArgs p) {
   __shared__ int s_hot[MOE_MAX_E], s_n[1];
   const int n_hot = list_hot_kpos(p.kpos, p.E, p.hot_bytes, s_hot, s_n);
   const int x = blockIdx.x % N_XCD, slot = blockIdx.x / N_XCD, nslot = gridDim.x / N_XCD;
-  int m_lo = 0, n_lo = 0, pm = p.PM, pn = p.PN;
-  if (p.split_m) {
-    const int w = (p.PM + N_XCD - 1) / N_XCD;
-    m_lo = x * w;
-    pm = max(0, min(w, p.PM - m_lo));
-  } else {
-    const int w = (p.PN + N_XCD - 1) / N_XCD;
-    n_lo = x * w;
-    pn = max(0, min(w, p.PN - n_lo));
-  }
+  int m_lo, n_lo, pm, pn;
+  xcd_rect(p.PM, p.PN, p.GM, x, m_lo, n_lo, pm, pn);
   const int per = pm * pn;
   const int nq = per * n_hot;
   const long KS = p.Kp / 32;
@@ -919,6 +913,21 @@ hipError_t launch_big_dgrad_up(const GroupInfo& g, const void* dZ, const void* w
                         (bf16_t*)dX));
 }
 
+// GM for xcd_rect: the XCD grid (GM x 8 / GM) whose rectangles need the fewest panels
+// (rows + columns of tiles), ties to the more even split
+static int xcd_grid_rows(int PM, int PN) {
+  int best = 1, cost = 1 << 30;
+  for (int gm = 1; gm <= N_XCD; gm *= 2) {
+    const int gn = N_XCD / gm, wm = (PM + gm - 1) / gm, wn = (PN + gn - 1) / gn;
+    const int c = wm + wn;
+    if (c < cost) {
+      cost = c;
+      best = gm;
+    }
+  }
+  return best;
+}
+
 // Wgrads of the experts with >= hot_rows rows (see k_wgrad_hot); in dense mode (the
 // shared expert) the one dense operand pair.  Returns hipErrorNotSupported, with
 // nothing enqueued, for shapes this core does not tile (the caller then runs the
@@ -951,7 +960,7 @@ static hipError_t wgrad_hot(const char* name, const GroupInfo& g, const void* A,
   const unsigned grid = (unsigned)(cus >= N_XCD ? cus - cus % N_XCD : N_XCD);
   p.PM = M / big::TILE;
   p.PN = N / big::TILE;
-  p.split_m = p.PM % N_XCD == 0 ? 1 : p.PN % N_XCD == 0 ? 0 : (p.PM >= p.PN ? 1 : 0);
+  p.GM = xcd_grid_rows(p.PM, p.PN);
   return MOE_LAUNCH(name, s, big::k_wgrad_hot<<<grid, big::NTH, 0, s>>>(p));
 }
 
@@ -993,7 +1002,7 @@ hipError_t launch_mx_wgrad_hot(const char* name, const MbPlans& mp, int E, uint8
   p.half_rows = split;
   p.PM = M / big::TILE;
   p.PN = N / big::TILE;
-  p.split_m = p.PM % N_XCD == 0 ? 1 : p.PN % N_XCD == 0 ? 0 : (p.PM >= p.PN ? 1 : 0);
+  p.GM = xcd_grid_rows(p.PM, p.PN);
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess)
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
