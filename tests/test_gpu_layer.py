@@ -205,6 +205,42 @@ def test_full_size_forward_backward_sampled():
     assert digest(b.y, b.dx, b.d_topk_w, b.dw_gate, b.dw_down) == d1
 
 
+def test_ep_share_forward_backward_sampled():
+    """One GPU's share of an expert-parallel layer: 4 experts x 4096 rows (every token on
+    every expert), so every weight gradient runs on the large-tile wgrad kernel with
+    K = 4096; sampled tokens and weight-gradient slices of every expert."""
+    name = "ep_share_bf16"
+    shape, inp, b = full_size(name, backward=True)
+    L = np_(inp["logits"])
+    idx, w = oracle.route(L, shape.k)
+    np.testing.assert_array_equal(np_(b.topk_idx), idx)
+    plan = oracle.build_plan(idx, shape.E)
+    assert (plan["counts"] == shape.T).all()
+    Wg, Wu, Wd = ExpertCache(inp["w_gate"]), ExpertCache(inp["w_up"]), ExpertCache(inp["w_down"])
+    toks = sampled_tokens(shape.T, 6)
+    say(f"{name}: oracle on {len(toks)} sampled tokens")
+    y_ref, dx_ref, dg_ref = [], [], []
+    for t in toks:
+        y_ref.append(oracle.token_forward(inp["x"][t], idx[t], w[t], Wg, Wu, Wd))
+        dx_t, dg_t = oracle.token_backward(inp["x"][t], idx[t], w[t], inp["dy"][t], Wg, Wu, Wd)
+        dx_ref.append(dx_t)
+        dg_ref.append(dg_t)
+    check(np_(b.y.double())[toks], np.stack(y_ref), "bf16", "y (sampled)")
+    check(np_(b.dx.double())[toks], np.stack(dx_ref), "bf16", "dx (sampled)")
+    check(np_(b.d_topk_w)[toks], np.stack(dg_ref), "bf16", "d_topk_w (sampled)")
+    cols = [0, 1500, shape.I - 1]
+    for e in range(shape.E):
+        seg = slice(plan["offsets"][e], plan["offsets"][e + 1])
+        tok, slot = plan["src_token"][seg], plan["src_slot"][seg]
+        say(f"{name}: dW slices of expert {e}")
+        ti = torch.as_tensor(tok, device="cuda")
+        dg_, du_, dd_ = oracle.expert_weight_grad_slices(
+            inp["x"][ti], inp["dy"][ti], w[tok, slot], Wg[e], Wu[e], Wd[e], cols)
+        check(np_(b.dw_gate[e].double())[cols], dg_, "bf16", f"dw_gate[{e}] rows")
+        check(np_(b.dw_up[e].double())[cols], du_, "bf16", f"dw_up[{e}] rows")
+        check(np_(b.dw_down[e].double())[:, cols], dd_, "bf16", f"dw_down[{e}] cols")
+
+
 def test_empty_batch_zeroes_weight_gradients():
     say("layer T=0: forward is a no-op, backward overwrites dW with zeros")
     from mixture_experts_layer_plan_amd import LayerBuffers, run_layer
