@@ -1,5 +1,6 @@
-// Large-tile bf16 grouped GEMMs for gfx950 (MI355X): GEMM1 + SwiGLU, GEMM2 and
-// dgrad-up, with their epilogues fused.
+// Large-tile grouped GEMMs for gfx950 (MI355X): bf16 GEMM1 + SwiGLU, GEMM2 and
+// dgrad-up with their epilogues fused, and the weight gradients (bf16 and MXFP8) of
+// the experts with many rows.
 //
 // The experts are SwiGLU feed-forward nets run as grouped GEMMs over all experts
 // at once (sebask.de, "Mixture-of-Kittens: Cursors Open-Source-Ansatz für
@@ -17,21 +18,23 @@
 // barrier sits before the last step's MFMAs so that the next tile's first
 // fragments load underneath them.  Against a 128 x 128 tile with register-staged
 // loads this halves LDS traffic per flop (32 flops per LDS byte) and frees the
-// registers that made the loop wait on every fragment read.  (The K-grouped
-// wgrads and dgrad-down stay on the 128 x 128 kernels of gemm.hip: with one
-// workgroup per CU their write-heavy epilogues no longer overlap other tiles'
-// loads, and they measured slower.)
+// registers that made the loop wait on every fragment read.  (dgrad-down, and the
+// wgrads of experts with few rows and of experts without rows, stay on the 128 x 128
+// kernels of gemm.hip: short-K, write-heavy items overlap better two workgroups per
+// CU, and dgrad-down's 256-wide column tiles are too few.)
 //
 // Operand layouts in LDS (one stage = 32 KiB per operand):
 //  * K-major (rows of K-contiguous data: tokens, and the weights of the forward
 //    GEMMs): 256 rows x 128 bytes, 16-byte chunks XOR-swizzled by row; fragments
 //    by 16-byte reads.
-//  * MN-major (K is the outer dimension: the weights of dgrad-up): 64 K rows x
-//    512 bytes as stored in memory, 16-byte chunks XOR-swizzled by K row;
-//    fragments by the gfx950 transposing LDS read ds_read_b64_tr_b16 (within each
-//    16-lane group, lane 4a + b receives element b of the 8-byte rows addressed by
-//    lanes a, a + 4, a + 8, a + 12), two reads per fragment.  No register
-//    transpose, no bank conflicts.
+//  * MN-major (K is the outer dimension: the weights of dgrad-up, both bf16 wgrad
+//    operands): 64 K rows x 512 bytes as stored in memory, 16-byte chunks
+//    XOR-swizzled by K row; fragments by the gfx950 transposing LDS read
+//    ds_read_b64_tr_b16 (within each 16-lane group, lane 4a + b receives element b
+//    of the 8-byte rows addressed by lanes a, a + 4, a + 8, a + 12), two reads per
+//    fragment.  No register transpose, no bank conflicts.
+//  * MXFP8 wgrad operands: K-major, 128-byte K pieces (128 E4M3 values) in the
+//    K-major layout above.
 //
 // Grouping: the kernels walk the plan's 256-row tile list (expert, first row); a
 // wavefront skips the MFMAs of 32-row blocks that lie past the expert's rows and

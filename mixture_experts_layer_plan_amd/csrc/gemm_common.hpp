@@ -510,8 +510,6 @@ MOE_DEV int k_work_items(const GroupInfo& g, int mt_count, int nt_count) {
   return (g.offsets ? g.E : 1) * mt_count * nt_count;
 }
 
-MOE_DEV bool k_empty(const GroupInfo& g, int e) { return g.counts && ld_uniform(g.counts + e) == 0; }
-
 // What a K-grouped wgrad item of expert e does: 0 multiply, 1 store a zero tile,
 // 2 nothing (the large-tile kernel owns the expert's output).
 MOE_DEV int k_item_kind(const GroupInfo& g, int e) {
