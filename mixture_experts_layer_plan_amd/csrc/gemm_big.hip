@@ -39,7 +39,9 @@
 // Grouping: the kernels walk the plan's 256-row tile list (expert, first row); a
 // wavefront skips the MFMAs of 32-row blocks that lie past the expert's rows and
 // the token loads skip whole 64-row groups past them, so a tile of a small expert
-// costs what its rows need and is bound by its weight reads.  Every output element
+// costs what its rows need and is bound by its weight reads.  Such a tile (at most
+// 64 or 128 rows) runs K through a deeper ring whose stages hold only the A rows
+// that exist, so more of its weight panel is in flight.  Every output element
 // is produced by one workgroup with a fixed K order: bitwise reproducible and
 // independent of the grid.
 #include "gemm_common.hpp"
@@ -51,6 +53,7 @@ constexpr int TILE = 256;
 constexpr int NTH = 512;
 constexpr int STAGE = 32768;     // one operand, one 64-deep K tile
 constexpr int LDS = 4 * STAGE;   // two stages of (A, B)
+constexpr int LDS_ROWS = 163840; // the row-grouped kernels: also the small-tile ring
 
 typedef __attribute__((address_space(3))) void* lds_vptr;
 typedef const __attribute__((address_space(1))) void* gbl_vptr;
@@ -329,13 +332,13 @@ MOE_DEV void load_frags(const OpMNSeg&, const OpMNSeg&, const char* st, int, int
 
 template <class OA, class OB>
 MOE_DEV void load_frags(const OA& A, const OB& B, const char* st, int kt, int ks, int wm, int wn,
-                        int ma, int mb, bf16x8_t (&a)[4], bf16x8_t (&b)[2]) {
+                        int ma, int mb, bf16x8_t (&a)[4], bf16x8_t (&b)[2], int boff = STAGE) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (i < ma) a[i] = A.frag(st, 128 * wm + 32 * i, ks, kt);
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-    if (j < mb) b[j] = B.frag(st + STAGE, 64 * wn + 32 * j, ks, kt);
+    if (j < mb) b[j] = B.frag(st + boff, 64 * wn + 32 * j, ks, kt);
 }
 
 MOE_DEV void mma(Acc& acc, const bf16x8_t (&a)[4], const bf16x8_t (&b)[2], int ma, int mb) {
@@ -391,6 +394,80 @@ MOE_DEV void main_loop(char* lds, const OA& A, const OB& B, int nk, int ma, int 
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();  // LDS free for an epilogue
+}
+
+// Tiles with at most RA rows (RA = 64 or 128; a small expert's single tile) run K
+// through a ring of NS stages instead: a stage holds only the RA rows of A that
+// exist (RA * 128 bytes) and the full B part (32 KiB), so RA = 64 fits four stages
+// (three in flight, 120 KiB against the 64 KiB of the two-stage loop) and RA = 128
+// three.  These tiles are bound by streaming their weights; with more bytes in flight
+// a CU streams faster while other CUs run the MFMA-bound tiles of larger experts
+// (a CU alone pulls ~40 GB/s, ~20 GB/s when every CU streams).  The A loads of such
+// a tile are RA / 64 instructions per lane and the B loads four: the ring's waits
+// count (RA / 64 + 4) per stage.
+template <int RA>
+MOE_DEV void ring_wait_small(int ahead) {
+  constexpr int L = RA / 64 + 4;  // loads per stage per lane
+  static_assert(2 * L < 16, "vmcnt field");
+  if (ahead >= 2) __builtin_amdgcn_s_waitcnt((2 * L) | 0x70);
+  else if (ahead == 1) __builtin_amdgcn_s_waitcnt(L | 0x70);
+  else __builtin_amdgcn_s_waitcnt(0x70);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");  // no LDS read of the stage moves above the barrier
+}
+
+template <int RA, int NS, class OA, class OB>
+MOE_DEV void main_loop_small(char* lds, const OA& A, const OB& B, int nk, int ma, int mb,
+                             Acc& acc) {
+  constexpr int SA = RA * 128, SST = SA + STAGE;
+  static_assert(NS * SST <= 163840 && NS >= 2 && NS <= 4, "ring fits the LDS");
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc.c[i][j][v] = 0.0f;
+  if (nk <= 0) return;
+  const int wm = wave() >> 2, wn = wave() & 3;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) {
+      A.issue(s, lds + s * SST);
+      B.issue(s, lds + s * SST + SA);
+    }
+  int slot = 0;  // kt % NS
+  for (int kt = 0; kt < nk; ++kt) {
+    ring_wait_small<RA>(min(NS - 2, nk - 1 - kt));  // stage kt in; kt - 1 no longer read
+    if (kt + NS - 1 < nk) {  // into the slot of stage kt - 1
+      char* st = lds + (slot == 0 ? NS - 1 : slot - 1) * SST;
+      A.issue(kt + NS - 1, st);
+      B.issue(kt + NS - 1, st + SA);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const char* cur = lds + slot * SST;
+    bf16x8_t a0[4], b0[2], a1[4], b1[2];
+    load_frags(A, B, cur, kt, 0, wm, wn, ma, mb, a0, b0, SA);
+    load_frags(A, B, cur, kt, 1, wm, wn, ma, mb, a1, b1, SA);
+    mma(acc, a0, b0, ma, mb);
+    load_frags(A, B, cur, kt, 2, wm, wn, ma, mb, a0, b0, SA);
+    mma(acc, a1, b1, ma, mb);
+    load_frags(A, B, cur, kt, 3, wm, wn, ma, mb, a1, b1, SA);
+    mma(acc, a0, b0, ma, mb);
+    mma(acc, a1, b1, ma, mb);
+    slot = slot == NS - 1 ? 0 : slot + 1;
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // LDS free for an epilogue
+}
+
+// The K loop of a row-grouped tile: the two-stage loop, or the ring for a tile with
+// at most 128 rows.
+template <class OA, class OB>
+MOE_DEV void main_loop_rows(char* lds, const OA& A, const OB& B, int nk, int rows, int ma, int mb,
+                            Acc& acc) {
+  if (rows <= 64) main_loop_small<64, 4>(lds, A, B, nk, ma, mb, acc);
+  else if (rows <= 128) main_loop_small<128, 3>(lds, A, B, nk, ma, mb, acc);
+  else main_loop(lds, A, B, nk, ma, mb, acc);
 }
 
 // Output position of register v of block (i, j): row 128 wm + 32 i + 8 (v >> 2) +
@@ -451,7 +528,7 @@ __global__ __launch_bounds__(NTH, 1) void k_up_swiglu(GroupInfo g, const bf16_t*
                                                       const bf16_t* __restrict__ wu, int H, int I,
                                                       float* __restrict__ Z,
                                                       bf16_t* __restrict__ hout) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS];
+  __shared__ __attribute__((aligned(16))) char lds[LDS_ROWS];
   Tile t;
   int nt;
   if (!row_tile(g, I / 128, t, nt)) return;
@@ -466,7 +543,7 @@ __global__ __launch_bounds__(NTH, 1) void k_up_swiglu(GroupInfo g, const bf16_t*
   }
   B.set(wg + wofs + (size_t)128 * nt * H, wu + wofs + (size_t)128 * nt * H, H);
   Acc acc;
-  main_loop(lds, A, B, H / 64, blocks_a(t.row_end - t.row0), 2, acc);
+  main_loop_rows(lds, A, B, H / 64, t.row_end - t.row0, blocks_a(t.row_end - t.row0), 2, acc);
   const int i = 128 * nt + 32 * (wave() & 3) + (lane() & 31);
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
@@ -489,7 +566,7 @@ __global__ __launch_bounds__(NTH, 1) void k_up_swiglu(GroupInfo g, const bf16_t*
 __global__ __launch_bounds__(NTH, 1) void k_down(GroupInfo g, const bf16_t* __restrict__ h,
                                                  const bf16_t* __restrict__ wd, int H, int I,
                                                  bf16_t* __restrict__ Y) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS];
+  __shared__ __attribute__((aligned(16))) char lds[LDS_ROWS];
   Tile t;
   int nt;
   if (!row_tile(g, (H + TILE - 1) / TILE, t, nt)) return;
@@ -501,7 +578,8 @@ __global__ __launch_bounds__(NTH, 1) void k_down(GroupInfo g, const bf16_t* __re
   for (int s = 0; s < 4; ++s) A.d.row(s, (size_t)row_of_tile(t, kmaj_row(s)) * I);
   B.d.set(wd + (size_t)t.e * H * I + (size_t)n0 * I, (size_t)I, H - n0);
   Acc acc;
-  main_loop(lds, A, B, I / 64, blocks_a(t.row_end - t.row0), blocks_b(H - n0), acc);
+  main_loop_rows(lds, A, B, I / 64, t.row_end - t.row0, blocks_a(t.row_end - t.row0),
+                 blocks_b(H - n0), acc);
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
@@ -521,7 +599,7 @@ __global__ __launch_bounds__(NTH, 1) void k_dgrad_up(GroupInfo g, const bf16_t* 
                                                      const bf16_t* __restrict__ wg,
                                                      const bf16_t* __restrict__ wu, int H, int I,
                                                      bf16_t* __restrict__ dX) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS];
+  __shared__ __attribute__((aligned(16))) char lds[LDS_ROWS];
   Tile t;
   int nt;
   if (!row_tile(g, (H + TILE - 1) / TILE, t, nt)) return;
@@ -536,7 +614,8 @@ __global__ __launch_bounds__(NTH, 1) void k_dgrad_up(GroupInfo g, const bf16_t* 
   B.u.set(wu + wofs, (size_t)H, ncols);
   B.kI = I / 64;
   Acc acc;
-  main_loop(lds, A, B, (2 * I) / 64, blocks_a(t.row_end - t.row0), blocks_b(ncols), acc);
+  main_loop_rows(lds, A, B, (2 * I) / 64, t.row_end - t.row0, blocks_a(t.row_end - t.row0),
+                 blocks_b(ncols), acc);
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
