@@ -382,7 +382,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_down(GroupInfo g, const T* __
       continue;
     }
     if (kind == 1) {
-      zero_tile<T>(dwd + (size_t)t.e * H * I + (size_t)t.m0 * I + t.n0, (size_t)I);
+      zero_span<T>(dwd + (size_t)t.e * H * I + ((size_t)(t.m0 / TM) * NT + t.n0 / TN) * (TM * TN));
       continue;
     }
     int seg0, seg1;
@@ -431,9 +431,9 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_up(GroupInfo g, const T* __re
       continue;
     }
     if (kind == 1) {
-      zero_tile<T>((t.m0 < I ? dwg + (size_t)t.e * I * H + (size_t)t.m0 * H
-                             : dwu + (size_t)t.e * I * H + (size_t)(t.m0 - I) * H) + t.n0,
-                   (size_t)H);
+      const int mg = t.m0 < I ? t.m0 : t.m0 - I;  // row tile within dW_g or dW_u
+      zero_span<T>((t.m0 < I ? dwg : dwu) + (size_t)t.e * I * H +
+                   ((size_t)(mg / TM) * NT + t.n0 / TN) * (TM * TN));
       continue;
     }
     int seg0, seg1;

@@ -526,18 +526,18 @@ MOE_DEV int k_skip_expert(int w, int e, int per) {
   return w + ((nxt - w - 1) / (int)gridDim.x) * (int)gridDim.x;
 }
 
-// Zero a TM x TN tile of T at out (row stride ld elements) with 16-byte
-// non-temporal stores.
+// Zero TM * TN consecutive elements of T at out with 16-byte non-temporal stores.
+// An expert without rows gets its whole gradient block zeroed: its tile (mt, nt)
+// takes the block's (mt * NT + nt)-th span of TM * TN elements, not the tile's own
+// rows, so every workgroup writes one contiguous 32 KiB (bf16) run instead of TM
+// rows of TN elements each.
 template <typename T>
-MOE_DEV void zero_tile(T* out, size_t ld) {
-  constexpr int CPR = TN * (int)sizeof(T) / 16;  // 16-byte chunks per row
+MOE_DEV void zero_span(T* out) {
+  constexpr int CH = TM * TN * (int)sizeof(T) / 16;
   const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int i = 0; i < TM * CPR / NTHR; ++i) {
-    const int c = (int)threadIdx.x + i * NTHR;
-    const int r = c / CPR, q = c - r * CPR;
-    __builtin_nontemporal_store(z, (u32x4_t*)(out + (size_t)r * ld) + q);
-  }
+  for (int i = 0; i < CH / NTHR; ++i)
+    __builtin_nontemporal_store(z, (u32x4_t*)out + (int)threadIdx.x + i * NTHR);
 }
 
 // Persistent grid: two resident workgroups per compute unit, at most one per item.

@@ -477,7 +477,10 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_mx(MbPlans mp, int E, bool m_
   bf16_t* base = (m0 < split ? out0 + (size_t)e * split * N + (size_t)m0 * N
                              : out1 + (size_t)e * (M - split) * N + (size_t)(m0 - split) * N) + n0;
   if (ld_uniform(mp.kpos + e + 1) == ld_uniform(mp.kpos + e)) {
-    zero_tile<bf16_t>(base, (size_t)N);
+    const int mg = m0 < split ? m0 : m0 - split;  // row tile within its output block
+    zero_span<bf16_t>((m0 < split ? out0 + (size_t)e * split * N
+                                  : out1 + (size_t)e * (M - split) * N) +
+                      ((size_t)(mg / TM) * NT + nt) * (TM * TN));
     return;
   }
   const KFrom km{ld_uniform(mp.kpos + e)};

@@ -253,3 +253,28 @@ def test_empty_batch_zeroes_weight_gradients():
     torch.cuda.synchronize()
     for t in (b.dw_gate, b.dw_up, b.dw_down, b.ds_gate, b.ds_up, b.ds_down):
         assert not t.any()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_experts_without_rows_get_zero_gradients(dtype):
+    # a Zipf(2.0) routing over 64 experts: a hot expert (>= 256 rows, the large-tile
+    # wgrads), small ones, and experts without rows, whose gradient blocks the
+    # small-tile wgrads overwrite with zeros in contiguous spans
+    shape = Shape(T=512, H=256, I=128, E=64, k=2, zipf_s=2.0, dtype=dtype)
+    say(f"layer {dtype}: dW of experts without rows overwritten with zeros, others written")
+    from mixture_experts_layer_plan_amd import LayerBuffers, run_layer
+    inp = to_dev(make_inputs(shape, seed=3, device="cpu", with_dy=True))
+    b = LayerBuffers(shape.T, shape.H, shape.I, shape.E, shape.k, 0, dtype, backward=True)
+    for t in (b.dw_gate, b.dw_up, b.dw_down):
+        t.fill_(1.0)
+    run_layer(b, inp, backward=True)
+    torch.cuda.synchronize()
+    counts = np.bincount(np_(b.topk_idx).ravel(), minlength=shape.E)
+    empty = [e for e in range(shape.E) if counts[e] == 0]
+    assert empty and counts.max() >= 256, counts
+    for e in range(shape.E):
+        for t in (b.dw_gate, b.dw_up, b.dw_down):
+            if counts[e] == 0:
+                assert not t[e].any(), e
+            else:
+                assert not (t[e] == 1.0).all(dim=-1).any(), e  # no row left as filled
