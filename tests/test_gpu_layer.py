@@ -51,9 +51,38 @@ def router_margin_ok(L, k):
 @pytest.mark.parametrize("name", list(SMALL))
 def test_layer_small_all_outputs(name):
     shape = SMALL[name]
-    kind = shape.dtype
     say(f"layer {name}: {shape}")
     inp = make_inputs(shape, seed=0, device="cpu", with_dy=True)
+    check_all_outputs(shape, inp)
+
+
+# Row counts around the K-loop variants of the 256-row GEMMs (a tile of at most 64
+# rows, at most 128, more) and the large-tile wgrad threshold (256), plus an expert
+# without rows; with H = 128 the K loop is shorter than the deepest ring's prologue.
+EXACT_COUNTS = [0, 1, 63, 64, 65, 127, 128, 129, 255, 256, 257, 320]
+
+
+@pytest.mark.parametrize("H", [128, 768])
+def test_layer_exact_row_counts(H):
+    counts = np.array(EXACT_COUNTS)
+    shape = Shape(T=int(counts.sum()), H=H, I=256, E=len(counts), k=1)
+    say(f"layer exact counts {EXACT_COUNTS}: {shape}")
+    inp = make_inputs(shape, seed=5, device="cpu", with_dy=True)
+    # top-1 expert of token t fixed by a margin of 8 over N(0, 0.25) logits, the
+    # experts' tokens interleaved in a seeded order
+    rng = np.random.default_rng(5)
+    choice = rng.permutation(np.repeat(np.arange(shape.E), counts))
+    L = 0.5 * rng.standard_normal((shape.T, shape.E)).astype(np.float32)
+    L[np.arange(shape.T), choice] = 8.0
+    inp["logits"] = torch.from_numpy(L)
+    c = check_all_outputs(shape, inp)
+    np.testing.assert_array_equal(np.bincount(c["topk_idx"].ravel(), minlength=shape.E), counts)
+
+
+def check_all_outputs(shape: Shape, inp: dict):
+    """Run the layer forward + backward on the GPU and compare every output with
+    the oracle; returns the oracle's forward cache."""
+    kind = shape.dtype
     b = gpu_run(shape, to_dev(inp))
     c = oracle.layer_forward(inp["x"], inp.get("logits"), shape.k, inp["w_gate"], inp["w_up"],
                              inp["w_down"], shared=shared_of(inp), w_router=inp.get("w_router"))
@@ -83,6 +112,7 @@ def test_layer_small_all_outputs(name):
             check(getattr(b, n), g[n], kind, n)
     if shape.router == "gemm":
         check(b.dw_router, g["dw_router"], kind, "dw_router")
+    return c
 
 
 def test_layer_bitwise_repeatable_and_buffer_independent():
