@@ -168,6 +168,44 @@ def test_mx_hot_expert_weight_gradients(I):
         check(getattr(b, n), g[n], "bf16", n)
 
 
+# Row counts around the 32-token blocks of the packed token axis, the 128-row tiles and
+# the large-tile wgrad threshold (256 packed tokens), plus an expert without rows.
+MX_EXACT_COUNTS = [0, 1, 31, 32, 33, 127, 128, 129, 255, 256, 257, 300]
+
+
+@pytest.mark.parametrize("T_mb", [0, 512])
+def test_mx_layer_exact_row_counts(T_mb):
+    """Every weight gradient element by element; y, dx and dg normwise only, as in
+    test_mx_hot_expert_weight_gradients: here two rows of the 300-row expert hold two
+    E4M3 codes of h each that differ between the kernel's fp32 pre-activations and the
+    oracle's fp64 ones (same E8M0 scales; the pre-activations agree to 1.1e-5 and
+    straddle a rounding midpoint), which moves those rows of y by 1.5 % and 3.6 %."""
+    counts = np.array(MX_EXACT_COUNTS)
+    shape = Shape(T=int(counts.sum()), H=256, I=256, E=len(counts), k=1, dtype="mxfp8")
+    say(f"mx layer exact counts {MX_EXACT_COUNTS}: {shape} T_mb={T_mb}")
+    inp = make_inputs(shape, seed=7, device="cpu", with_dy=True)
+    # top-1 expert of token t fixed by a margin of 8 over N(0, 0.25) logits
+    rng = np.random.default_rng(7)
+    choice = rng.permutation(np.repeat(np.arange(shape.E), counts))
+    L = 0.5 * rng.standard_normal((shape.T, shape.E)).astype(np.float32)
+    L[np.arange(shape.T), choice] = 8.0
+    inp["logits"] = torch.from_numpy(L)
+    b = gpu_mx(shape, to_dev(inp), T_mb)
+    c = moe_mx.layer_forward_mx(inp["x"], inp["logits"], shape.k, inp["w_gate"], inp["w_up"],
+                                inp["w_down"], shared=None, T_mb=T_mb)
+    g = moe_mx.layer_backward_mx(c, inp["dy"], keep_operands=True)
+    np.testing.assert_array_equal(np_(b.topk_idx), c["topk_idx"])
+    np.testing.assert_array_equal(np.bincount(c["topk_idx"].ravel(), minlength=shape.E), counts)
+    check_norm(b.y, c["y"], "mxfp8", "y")
+    check_norm(b.dx, g["dx"], "mxfp8", "dx")
+    check_norm(b.d_topk_w, g["dg"], "mxfp8", "d_topk_w")
+    for e in range(shape.E):
+        for n in ("dw_gate", "dw_up", "dw_down"):
+            ops = g["wgrad_operands"].get(e, {}).get(n)
+            allow = one_flip_allowance(ops) if ops else None
+            check(getattr(b, n)[e], g[n][e], "mxfp8", f"{n}[{e}]", allowance=allow)
+
+
 def test_mx_experts_without_rows_get_zero_gradients():
     shape, T_mb = SMALL_MX["sparse_experts"]
     say("mx: weight gradients of experts without rows are overwritten with zeros")
