@@ -494,10 +494,24 @@ struct Tile {
 // weight-bound tiles; dealt round-robin, every XCD gets a share of both, and the
 // tiles that share a weight panel run at the same time on neighbouring XCDs
 // (dgrad-up 4.10 -> 3.84 ms, GEMM1 + SwiGLU 3.24 -> 3.10 ms measured on MI355X).
+//
+// GEMM1 + SwiGLU deals blocks of XCD_BLOCK consecutive pairs instead (block j to XCD
+// j mod 8, the launch rounded up to whole rounds of 8 blocks): a block covers 4 row
+// tiles x 4 column tiles of a group, so the workgroups an XCD runs at once share
+// their token rows and weight panels in its L2 (measured on MI355X at T = 4096,
+// Zipf(1.2): GEMM1 2.97 -> 2.90 ms over three runs each; the same dealing made
+// dgrad-up slower, 3.26 -> 3.29 ms, and left GEMM2 unchanged, so those keep single
+// pairs).
+constexpr int XCD_BLOCK = 16;
+template <bool BLOCKS>
 MOE_DEV bool row_tile(const GroupInfo& g, int nt_count, Tile& t, int& nt) {
   const int n_row_tiles = g.wtiles ? g.n_wtiles[0] : (g.dense_rows + TILE - 1) / TILE;
   const int total = n_row_tiles * nt_count;
-  const int L = blockIdx.x;
+  int L = blockIdx.x;
+  if (BLOCKS) {
+    const int x = L % N_XCD, q = L / N_XCD;
+    L = ((q / XCD_BLOCK) * N_XCD + x) * XCD_BLOCK + q % XCD_BLOCK;
+  }
   if (L >= total) return false;
   int mt;
   group_rows(g.wtiles, g.offsets, g.dense_rows, TILE, nt_count, 4, L, mt, nt);
@@ -531,7 +545,7 @@ __global__ __launch_bounds__(NTH, 1) void k_up_swiglu(GroupInfo g, const bf16_t*
   __shared__ __attribute__((aligned(16))) char lds[LDS_ROWS];
   Tile t;
   int nt;
-  if (!row_tile(g, I / 128, t, nt)) return;
+  if (!row_tile<true>(g, I / 128, t, nt)) return;
   const size_t wofs = (size_t)t.e * I * H;
   OpKG A;
   OpUpW B;
@@ -569,7 +583,7 @@ __global__ __launch_bounds__(NTH, 1) void k_down(GroupInfo g, const bf16_t* __re
   __shared__ __attribute__((aligned(16))) char lds[LDS_ROWS];
   Tile t;
   int nt;
-  if (!row_tile(g, (H + TILE - 1) / TILE, t, nt)) return;
+  if (!row_tile<false>(g, (H + TILE - 1) / TILE, t, nt)) return;
   const int n0 = nt * TILE;
   OpKG A;
   OpK B;
@@ -602,7 +616,7 @@ __global__ __launch_bounds__(NTH, 1) void k_dgrad_up(GroupInfo g, const bf16_t* 
   __shared__ __attribute__((aligned(16))) char lds[LDS_ROWS];
   Tile t;
   int nt;
-  if (!row_tile(g, (H + TILE - 1) / TILE, t, nt)) return;
+  if (!row_tile<false>(g, (H + TILE - 1) / TILE, t, nt)) return;
   const int n0 = nt * TILE, ncols = min(TILE, H - n0);
   const size_t wofs = (size_t)t.e * I * H + n0;
   OpKG A;
@@ -965,13 +979,18 @@ static unsigned big_row_tiles(const GroupInfo& g) {
   return g.wtiles ? (unsigned)g.max_wtiles
                   : (unsigned)((g.dense_rows + big::TILE - 1) / big::TILE);
 }
+// grid of a launch that deals blocks of pairs: whole rounds of 8 blocks
+static unsigned big_row_grid(unsigned pairs) {
+  const unsigned r = N_XCD * big::XCD_BLOCK;
+  return (pairs + r - 1) / r * r;
+}
 
 hipError_t launch_big_up_swiglu(const GroupInfo& g, const void* x, const void* wg, const void* wu,
                                 int H, int I, void* Z, void* h, hipStream_t s) {
   const unsigned ty = big_row_tiles(g);
   if (ty == 0) return hipSuccess;
   return MOE_LAUNCH(g.wtiles ? "gemm_up_swiglu" : "gemm_up_swiglu_shared", s,
-                    big::k_up_swiglu<<<ty * (I / 128), big::NTH, 0, s>>>(
+                    big::k_up_swiglu<<<big_row_grid(ty * (I / 128)), big::NTH, 0, s>>>(
                         g, (const bf16_t*)x, (const bf16_t*)wg, (const bf16_t*)wu, H, I,
                         (float*)Z, (bf16_t*)h));
 }
