@@ -405,7 +405,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_down(GroupInfo g, const T* __
     __syncthreads();
     T* base = dwd + (size_t)t.e * H * I + (size_t)t.m0 * I + t.n0;
     auto out = [&](int r) { return base + (size_t)r * I; };
-    epi_store<T>(C, out, TM);
+    epi_store<T, true>(C, out, TM);
     __syncthreads();
   }
 }
@@ -457,7 +457,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_up(GroupInfo g, const T* __re
     T* base = (t.m0 < I ? dwg + (size_t)t.e * I * H + (size_t)t.m0 * H
                         : dwu + (size_t)t.e * I * H + (size_t)(t.m0 - I) * H) + t.n0;
     auto out = [&](int r) { return base + (size_t)r * H; };
-    epi_store<T>(C, out, TM);
+    epi_store<T, true>(C, out, TM);
     __syncthreads();
   }
 }

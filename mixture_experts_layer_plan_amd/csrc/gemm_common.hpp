@@ -351,8 +351,23 @@ MOE_DEV void load8(const float* p, float* f) {
   f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
-// Plain epilogue: the 128 x 128 tile to out_row(r) + n0 for valid rows.
-template <typename T, class RowPtr>
+// Plain epilogue: the 128 x 128 tile to out_row(r) + n0 for valid rows.  NT: with
+// non-temporal stores, for outputs no kernel of the step reads again (the weight
+// gradients; measured on MI355X: wgrad-up 2.96 -> 2.84 ms at T = 4096, Zipf(1.2)).
+MOE_DEV void store8_nt(bf16_t* p, const float* f) {
+  const uint4 v = pack8(f);
+  const u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, (u32x4_t*)p);
+}
+MOE_DEV void store8_nt(float* p, const float* f) {
+  const u32x4_t a = {__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                     __float_as_uint(f[3])};
+  const u32x4_t b = {__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]),
+                     __float_as_uint(f[7])};
+  __builtin_nontemporal_store(a, (u32x4_t*)p);
+  __builtin_nontemporal_store(b, (u32x4_t*)(p + 4));
+}
+template <typename T, bool NT = false, class RowPtr>
 MOE_DEV void epi_store(const float* C, const RowPtr& out_row, int n_valid_rows) {
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
@@ -360,7 +375,8 @@ MOE_DEV void epi_store(const float* C, const RowPtr& out_row, int n_valid_rows) 
     if (r < n_valid_rows) {
       float f[8];
       read8(C, r, 8 * c, f);
-      store8(out_row(r) + 8 * c, f);
+      if (NT) store8_nt(out_row(r) + 8 * c, f);
+      else store8(out_row(r) + 8 * c, f);
     }
   }
 }

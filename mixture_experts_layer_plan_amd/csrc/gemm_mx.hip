@@ -511,7 +511,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_mx(MbPlans mp, int E, bool m_
   stage_acc(C, acc, arow, brow, lane);
   __syncthreads();
   auto out = [&](int r) { return base + (size_t)r * N; };
-  epi_store<bf16_t>(C, out, TM);
+  epi_store<bf16_t, true>(C, out, TM);
 }
 
 // ------------------------------------------------------------------ launchers
