@@ -567,8 +567,9 @@ __global__ __launch_bounds__(NTH, 1) void k_up_swiglu(GroupInfo g, const bf16_t*
       if (r < t.row_end) {
         const float a = acc.c[bi][0][v], b = acc.c[bi][1][v];
         float* zr = Z + (size_t)r * (2 * I);
-        zr[i] = a;
-        zr[I + i] = b;
+        // Z is read back only by the backward: non-temporal (GEMM1 2.91 -> 2.87 ms)
+        __builtin_nontemporal_store(a, zr + i);
+        __builtin_nontemporal_store(b, zr + I + i);
         hout[(size_t)r * I + i] = f32_to_bf16(silu_f(a) * b);
       }
     }
