@@ -111,14 +111,22 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
   if (t >= n_tiles[0]) return;
   const int e = tiles[2 * t], row0 = tiles[2 * t + 1];
   const int nrows = min(row0 + 128, offsets[e + 1]) - row0;
-  for (int i = threadIdx.x; i < 128 * VPR; i += 256) {
-    const int j = i / VPR, v = i - j * VPR;
-    uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+  // every lane issues all its loads before the first LDS store
+  constexpr int NL = 128 * VPR / 256;
+  uint4 raw[NL];
+#pragma unroll
+  for (int k = 0; k < NL; ++k) {
+    const int i = (int)threadIdx.x + 256 * k, j = i / VPR, v = i - j * VPR;
+    raw[k] = make_uint4(0u, 0u, 0u, 0u);
     if (j < nrows) {
       const int r = row0 + j;
-      raw = *(const uint4*)(src + (size_t)(gather ? gather[r] : r) * ld + c0 + v * VEC);
+      raw[k] = *(const uint4*)(src + (size_t)(gather ? gather[r] : r) * ld + c0 + v * VEC);
     }
-    *(uint4*)(tile + j * TROW + v * VEC) = raw;
+  }
+#pragma unroll
+  for (int k = 0; k < NL; ++k) {
+    const int i = (int)threadIdx.x + 256 * k, j = i / VPR, v = i - j * VPR;
+    *(uint4*)(tile + j * TROW + v * VEC) = raw[k];
   }
   __syncthreads();
   const int cc = threadIdx.x & 63, blk = threadIdx.x >> 6;
