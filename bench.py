@@ -81,7 +81,9 @@ def kernel_work(name, sh, counts_mb, es=2):
         "plan_scan": lambda: over_mb(lambda Rm, Etm, tm: (E * 12, 0)),
         "plan_scatter": lambda: over_mb(lambda Rm, Etm, tm: (Rm * 16, 0)),
         "dg_reduce": lambda: over_mb(lambda Rm, Etm, tm: (Rm * (I // 128) * 4 + Rm * 8, 0)),
-        "gather_rows": lambda: (2 * (2 * R * H * es + R * 4), 0),  # X and dYu replays
+        # X and dYu replays: each source row is read once and written to its k rows,
+        # (1 + k) H b bytes per token, plus the pull list
+        "gather_rows": lambda: (2 * ((T + R) * H * es + R * 4), 0),
         "combine_bf16": lambda: over_mb(lambda Rm, Etm, tm: (Rm * H * 2 + 2 * tm * H * 2 + tm * k * 8, 0)),
         "reverse_dispatch_bf16": lambda: over_mb(lambda Rm, Etm, tm: (Rm * H * 2 + 2 * tm * H * 2, 0)),
         # saved pre-activations Z are fp32 (4 bytes), h in the layer's dtype
@@ -108,7 +110,9 @@ def kernel_work(name, sh, counts_mb, es=2):
         "gemm_dgrad_up_shared": lambda: (2 * Is * H * 2 + T * 2 * Is * 2 + T * H * 2, 2 * T * 2 * Is * H),
         "gemm_wgrad_up_shared": lambda: (T * 2 * Is * 2 + T * H * 2 + 2 * Is * H * 2, 2 * T * 2 * Is * H),
         # MXFP8 path (per minibatch unless noted)
-        "mx_quant_rows": lambda: over_mb(lambda Rm, Etm, tm: (2 * Rm * H * (2 + q), 0)),  # x, dy
+        # x (forward) and dy (backward) gathered into the ring and quantised: each
+        # source row read once, its k rows written as E4M3 codes with scales
+        "mx_quant_rows": lambda: over_mb(lambda Rm, Etm, tm: (2 * (tm * H * 2 + Rm * H * q + Rm * 4), 0)),
         "mx_quant_tokens": lambda: over_mb(lambda Rm, Etm, tm: (Rm * (2 * H * (2 + q) + I * (4 + q)
                                                                       + 2 * I * (4 + q)), 0)),
         "mx_gemm_up_swiglu": lambda: over_mb(lambda Rm, Etm, tm: (

@@ -67,7 +67,11 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2 } moe_dtype;
  * H, I and I_shared multiples of 128 for the expert GEMMs; the bf16 and fp32
  * layer calls take one minibatch (T_minibatch 0 or >= T), the MXFP8 calls at
  * most 8.  The bf16 layer calls also need T*k*max(H, 2I, 2 I_shared)*2 bytes and
- * I*H*2, I_shared*H*2 bytes below 4 GiB (MOE_E_UNSUPPORTED otherwise). */
+ * I*H*2, I_shared*H*2 bytes below 4 GiB (MOE_E_UNSUPPORTED otherwise).  The MXFP8
+ * layer calls need T_minibatch*k*max(H, 2I) below 2^31 (T*k when T_minibatch is 0),
+ * T*max(H, 2 I_shared)*2 and I_shared*H*2 below 2^32, and 256 times the packed
+ * token-axis length (n_minibatch * max_tiles * 128, see moe_plan_layout) below 2^32
+ * (MOE_E_UNSUPPORTED otherwise; the size queries then return 0). */
 typedef struct {
   int32_t T, H, I, E, k;
   int32_t I_shared;

@@ -114,7 +114,10 @@ def shape(T, H, I, E, k, I_shared=0, T_minibatch=0) -> moe_shape:
     return moe_shape(int(T), int(H), int(I), int(E), int(k), int(I_shared), int(T_minibatch))
 
 
-def _ptr(t):
+def _ptr(t, dtype=None, numel=None):
+    """Device pointer of a contiguous tensor (None -> NULL).  ``dtype`` and ``numel``,
+    when given, are checked: the library reads and writes through raw pointers, so a
+    tensor of another element type or size would be over-read or overrun."""
     if t is None:
         return None
     if isinstance(t, int):
@@ -123,7 +126,23 @@ def _ptr(t):
         raise ValueError("expected a device tensor")
     if not t.is_contiguous():
         raise ValueError("expected a contiguous tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"expected a {dtype} tensor, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"expected {numel} elements, got {t.numel()}")
     return t.data_ptr()
+
+
+_F32 = torch.float32
+_BF16 = torch.bfloat16
+
+
+def _f32(t, numel=None):
+    return _ptr(t, _F32, numel)
+
+
+def _bf16(t, numel=None):
+    return _ptr(t, _BF16, numel)
 
 
 def _stream(stream):
@@ -161,23 +180,25 @@ def moe_workspace_bytes(s: moe_shape, dtype: int, backward: bool) -> int:
 
 
 def moe_router_logits_f32(s, x, w_router, logits, stream=None):
-    _call("moe_router_logits_f32", ctypes.byref(s), _ptr(x), _ptr(w_router), _ptr(logits),
-          _stream(stream))
+    _call("moe_router_logits_f32", ctypes.byref(s), _f32(x, s.T * s.H), _f32(w_router, s.E * s.H),
+          _f32(logits, s.T * s.E), _stream(stream))
 
 
 def moe_route(s, logits, topk_idx, topk_w, stream=None):
-    _call("moe_route", ctypes.byref(s), _ptr(logits), _ptr(topk_idx), _ptr(topk_w),
-          _stream(stream))
+    _call("moe_route", ctypes.byref(s), _f32(logits, s.T * s.E), _ptr(topk_idx, torch.int32, s.T * s.k),
+          _f32(topk_w, s.T * s.k), _stream(stream))
 
 
 def moe_route_backward(s, topk_idx, topk_w, d_topk_w, d_logits, stream=None):
-    _call("moe_route_backward", ctypes.byref(s), _ptr(topk_idx), _ptr(topk_w), _ptr(d_topk_w),
-          _ptr(d_logits), _stream(stream))
+    _call("moe_route_backward", ctypes.byref(s), _ptr(topk_idx, torch.int32, s.T * s.k),
+          _f32(topk_w, s.T * s.k), _f32(d_topk_w, s.T * s.k), _f32(d_logits, s.T * s.E),
+          _stream(stream))
 
 
 def moe_router_backward_f32(s, x, w_router, d_logits, dw_router, dx, stream=None):
-    _call("moe_router_backward_f32", ctypes.byref(s), _ptr(x), _ptr(w_router), _ptr(d_logits),
-          _ptr(dw_router), _ptr(dx), _stream(stream))
+    _call("moe_router_backward_f32", ctypes.byref(s), _f32(x, s.T * s.H), _f32(w_router, s.E * s.H),
+          _f32(d_logits, s.T * s.E), _f32(dw_router, s.E * s.H), _f32(dx, s.T * s.H),
+          _stream(stream))
 
 
 def moe_plan(s, topk_idx, plan, stream=None):
@@ -189,7 +210,8 @@ def moe_dispatch_bf16(s, plan, x, X, stream=None):
 
 
 def moe_dispatch_f32(s, plan, x, X, stream=None):
-    _call("moe_dispatch_f32", ctypes.byref(s), _ptr(plan), _ptr(x), _ptr(X), _stream(stream))
+    _call("moe_dispatch_f32", ctypes.byref(s), _ptr(plan), _f32(x, s.T * s.H), _f32(X, s.T * s.k * s.H),
+          _stream(stream))
 
 
 def moe_combine_bf16(s, plan, Y, topk_w, shared_out, y, stream=None):
@@ -198,8 +220,8 @@ def moe_combine_bf16(s, plan, Y, topk_w, shared_out, y, stream=None):
 
 
 def moe_combine_f32(s, plan, Y, topk_w, shared_out, y, stream=None):
-    _call("moe_combine_f32", ctypes.byref(s), _ptr(plan), _ptr(Y), _ptr(topk_w),
-          _ptr(shared_out), _ptr(y), _stream(stream))
+    _call("moe_combine_f32", ctypes.byref(s), _ptr(plan), _f32(Y, s.T * s.k * s.H),
+          _f32(topk_w, s.T * s.k), _f32(shared_out, s.T * s.H), _f32(y, s.T * s.H), _stream(stream))
 
 
 def moe_reverse_combine_bf16(s, plan, dy, dYu, stream=None):
@@ -214,8 +236,11 @@ def moe_reverse_dispatch_bf16(s, plan, dX, shared_dx, dx, stream=None):
 
 def _fwd(name, s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down, y, saved, ws,
          stream):
-    _call(name, ctypes.byref(s), _ptr(plan), _ptr(x), _ptr(topk_w), _ptr(w_gate), _ptr(w_up),
-          _ptr(w_down), _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(y), _ptr(saved), _ptr(ws),
+    dt = _F32 if name.endswith("_f32") else _BF16
+    nw, ns = s.E * s.I * s.H, s.I_shared * s.H
+    _call(name, ctypes.byref(s), _ptr(plan), _ptr(x, dt, s.T * s.H), _f32(topk_w, s.T * s.k),
+          _ptr(w_gate, dt, nw), _ptr(w_up, dt, nw), _ptr(w_down, dt, nw), _ptr(s_gate, dt, ns),
+          _ptr(s_up, dt, ns), _ptr(s_down, dt, ns), _ptr(y, dt, s.T * s.H), _ptr(saved), _ptr(ws),
           0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
 
 
@@ -233,11 +258,14 @@ def moe_forward_f32(s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_do
 
 def _bwd(name, s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down, saved, dy, dx,
          dw_gate, dw_up, dw_down, ds_gate, ds_up, ds_down, d_topk_w, ws, stream):
-    _call(name, ctypes.byref(s), _ptr(plan), _ptr(x), _ptr(topk_w), _ptr(w_gate), _ptr(w_up),
-          _ptr(w_down), _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(saved), _ptr(dy), _ptr(dx),
-          _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _ptr(ds_gate), _ptr(ds_up), _ptr(ds_down),
-          _ptr(d_topk_w), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
-          _stream(stream))
+    dt = _F32 if name.endswith("_f32") else _BF16
+    nw, ns, nt = s.E * s.I * s.H, s.I_shared * s.H, s.T * s.H
+    _call(name, ctypes.byref(s), _ptr(plan), _ptr(x, dt, nt), _f32(topk_w, s.T * s.k),
+          _ptr(w_gate, dt, nw), _ptr(w_up, dt, nw), _ptr(w_down, dt, nw), _ptr(s_gate, dt, ns),
+          _ptr(s_up, dt, ns), _ptr(s_down, dt, ns), _ptr(saved), _ptr(dy, dt, nt), _ptr(dx, dt, nt),
+          _ptr(dw_gate, dt, nw), _ptr(dw_up, dt, nw), _ptr(dw_down, dt, nw), _ptr(ds_gate, dt, ns),
+          _ptr(ds_up, dt, ns), _ptr(ds_down, dt, ns), _f32(d_topk_w, s.T * s.k), _ptr(ws),
+          0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
 
 
 def moe_backward_bf16(s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down, saved, dy,
@@ -259,8 +287,9 @@ def moe_mx_weights_bytes(s: moe_shape) -> int:
 
 
 def moe_quantize_weights_mxfp8(s, w_gate, w_up, w_down, wq, stream=None):
-    _call("moe_quantize_weights_mxfp8", ctypes.byref(s), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
-          _ptr(wq), _stream(stream))
+    nw = s.E * s.I * s.H
+    _call("moe_quantize_weights_mxfp8", ctypes.byref(s), _bf16(w_gate, nw), _bf16(w_up, nw),
+          _bf16(w_down, nw), _ptr(wq, torch.uint8, moe_mx_weights_bytes(s)), _stream(stream))
 
 
 def moe_quantize_mxfp8(src, rows, cols, axis, q, scales, stream=None):
@@ -269,17 +298,21 @@ def moe_quantize_mxfp8(src, rows, cols, axis, q, scales, stream=None):
 
 
 def moe_forward_mxfp8(s, plan, x, topk_w, wq, s_gate, s_up, s_down, y, saved, ws, stream=None):
-    _call("moe_forward_mxfp8", ctypes.byref(s), _ptr(plan), _ptr(x), _ptr(topk_w), _ptr(wq),
-          _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(y), _ptr(saved), _ptr(ws),
+    ns, nt = s.I_shared * s.H, s.T * s.H
+    _call("moe_forward_mxfp8", ctypes.byref(s), _ptr(plan), _bf16(x, nt), _f32(topk_w, s.T * s.k),
+          _ptr(wq, torch.uint8, moe_mx_weights_bytes(s)), _bf16(s_gate, ns), _bf16(s_up, ns),
+          _bf16(s_down, ns), _bf16(y, nt), _ptr(saved), _ptr(ws),
           0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
 
 
 def moe_backward_mxfp8(s, plan, x, topk_w, wq, s_gate, s_up, s_down, saved, dy, dx, dw_gate,
                        dw_up, dw_down, ds_gate, ds_up, ds_down, d_topk_w, ws, stream=None):
-    _call("moe_backward_mxfp8", ctypes.byref(s), _ptr(plan), _ptr(x), _ptr(topk_w), _ptr(wq),
-          _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(saved), _ptr(dy), _ptr(dx), _ptr(dw_gate),
-          _ptr(dw_up), _ptr(dw_down), _ptr(ds_gate), _ptr(ds_up), _ptr(ds_down), _ptr(d_topk_w),
-          _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    nw, ns, nt = s.E * s.I * s.H, s.I_shared * s.H, s.T * s.H
+    _call("moe_backward_mxfp8", ctypes.byref(s), _ptr(plan), _bf16(x, nt), _f32(topk_w, s.T * s.k),
+          _ptr(wq, torch.uint8, moe_mx_weights_bytes(s)), _bf16(s_gate, ns), _bf16(s_up, ns),
+          _bf16(s_down, ns), _ptr(saved), _bf16(dy, nt), _bf16(dx, nt), _bf16(dw_gate, nw),
+          _bf16(dw_up, nw), _bf16(dw_down, nw), _bf16(ds_gate, ns), _bf16(ds_up, ns),
+          _bf16(ds_down, ns), _f32(d_topk_w, s.T * s.k), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
 
 
 # ------------------------------------------------------------ kernel timing

@@ -492,10 +492,27 @@ MxBwdWs mx_bwd_ws(const moe_shape* s) {
   return L;
 }
 
+// The MX GEMMs address a minibatch's E4M3 activation rows with 32-bit signed
+// products row * width (width = H or 2I bytes), the wgrads a packed token-axis row
+// with 32-bit offsets below 256 rows * Kp, and the shared expert's bf16 GEMMs run
+// densely over all T tokens with the 32-bit byte offsets of the bf16 kernels.
+bool mx_offsets_fit(const moe_shape* s) {
+  const uint64_t R = (uint64_t)minibatch_tokens(s) * s->k;
+  const uint64_t w = std::max<uint64_t>((uint64_t)s->H, 2ull * s->I);
+  if (R * w >= (1ull << 31)) return false;
+  const uint64_t ws = std::max<uint64_t>((uint64_t)s->H, 2ull * s->I_shared);
+  if ((uint64_t)s->T * ws * 2 >= (1ull << 32) || (uint64_t)s->I_shared * s->H * 2 >= (1ull << 32))
+    return false;
+  const moe_plan_layout P = plan_layout(s);
+  const uint64_t Kp = (uint64_t)n_minibatches(s) * P.max_tiles * 128;
+  return 256 * Kp < (1ull << 32);
+}
+
 moe_status check_mx(const moe_shape* s) {
   moe_status rc = check_shape(s, true);
   if (rc != MOE_OK) return rc;
   if (n_minibatches(s) > MX_MAX_MB) return MOE_E_SHAPE;
+  if (!mx_offsets_fit(s)) return MOE_E_UNSUPPORTED;
   return MOE_OK;
 }
 

@@ -18,6 +18,9 @@ class LayerBuffers:
                  router_gemm=False, device="cuda", T_minibatch=0):
         if dtype not in ("bf16", "f32", "mxfp8"):
             raise ValueError(f"unsupported dtype {dtype}")
+        if router_gemm and dtype != "f32":
+            # the router GEMM calls take fp32 x and accumulate into an fp32 dx
+            raise ValueError("router_gemm needs dtype 'f32'")
         self.dtype = dtype
         self.dt = B.DTYPES[dtype]
         self.s = B.shape(T, H, I, E, k, I_shared, T_minibatch)
@@ -64,6 +67,8 @@ def run_forward(b: LayerBuffers, inp: dict, stream=None, quantize=True):
     ``quantize`` is False (weights already quantised into ``b.wq``)."""
     s = b.s
     if "w_router" in inp:
+        if b.logits is None:
+            raise ValueError("inputs carry w_router but the buffers have no router GEMM")
         B.moe_router_logits_f32(s, inp["x"], inp["w_router"], b.logits, stream)
         logits = b.logits
     else:

@@ -54,32 +54,46 @@ def q_tokens(a) -> np.ndarray:
     return mx_roundtrip(a, axis=0)[:n]
 
 
+# Axis of the 32-element blocks at each quantisation point: every operand is
+# blocked along the contraction axis of its own GEMM (module docstring).  The tables
+# name each point so that a test can put one point on the wrong axis and show that
+# a pin fails.  Activations: "x", "h", "dy", "dA", "dB" are blocked along the row
+# (q_rows); the wgrad operands along the tokens of an expert's segment (q_tokens).
+ACT_AXIS = {"x": "rows", "h": "rows", "dy": "rows", "dA": "rows", "dB": "rows",
+            "wgrad": "tokens"}
+# Weights: (which weight, axis).  W_g, W_u [I, H] and W_d [H, I] per expert; "rows"
+# blocks along the last axis, "cols" along the first.
+WEIGHT_AXIS = {
+    "g_H": ("gate", "rows"),   # GEMM1: K = H
+    "u_H": ("up", "rows"),
+    "d_I": ("down", "rows"),   # GEMM2: K = I
+    "d_H": ("down", "cols"),   # dgrad-down: K = H
+    "g_I": ("gate", "cols"),   # dgrad-up: K = I
+    "u_I": ("up", "cols"),
+}
+
+
+def _q_axis(axis: str, a) -> np.ndarray:
+    return {"rows": q_rows, "cols": q_cols, "tokens": q_tokens}[axis](a)
+
+
+def q_act(point: str, a) -> np.ndarray:
+    """dequant(Q(a)) of the activation operand at quantisation point ``point``."""
+    return _q_axis(ACT_AXIS[point], a)
+
+
 class _QuantCache:
     """Per-expert quantised weights, each orientation computed once."""
 
     def __init__(self, w_gate, w_up, w_down):
-        self.w = (w_gate, w_up, w_down)
+        self.w = {"gate": w_gate, "up": w_up, "down": w_down}
         self.c = {}
 
     def get(self, kind, e):
         key = (kind, int(e))
         if key not in self.c:
-            wg, wu, wd = self.w
-            if kind == "g_H":
-                v = q_rows(wg[e])            # [I, H] along H
-            elif kind == "u_H":
-                v = q_rows(wu[e])
-            elif kind == "d_I":
-                v = q_rows(wd[e])            # [H, I] along I
-            elif kind == "d_H":
-                v = q_cols(wd[e])            # [H, I] along H
-            elif kind == "g_I":
-                v = q_cols(wg[e])            # [I, H] along I
-            elif kind == "u_I":
-                v = q_cols(wu[e])
-            else:
-                raise KeyError(kind)
-            self.c[key] = v
+            which, axis = WEIGHT_AXIS[kind]
+            self.c[key] = _q_axis(axis, self.w[which][e])
         return self.c[key]
 
 
@@ -101,7 +115,7 @@ def layer_forward_mx(x, logits, k, w_gate, w_up, w_down, shared=None, T_mb=0,
     mbs = []
     for sl in minibatch_slices(T, T_mb):
         plan = build_plan(idx[sl], E)
-        xq = q_rows(xf[sl])
+        xq = q_act("x", xf[sl])
         n_rows = int(plan["offsets"][E])
         X = xq[plan["src_token"][:n_rows]]
         Y = np.zeros((n_rows, H))
@@ -117,7 +131,7 @@ def layer_forward_mx(x, logits, k, w_gate, w_up, w_down, shared=None, T_mb=0,
                 I = Ae.shape[1]
                 A, B, h = np.zeros((n_rows, I)), np.zeros((n_rows, I)), np.zeros((n_rows, I))
             A[r0:r1], B[r0:r1], h[r0:r1] = Ae, Be, he
-            Y[r0:r1] = q_rows(he) @ qc.get("d_I", e).T
+            Y[r0:r1] = q_act("h", he) @ qc.get("d_I", e).T
         shared_out = dense_swiglu(xf[sl], *shared)[3] if shared is not None else None
         y[sl] = combine(Y, plan["pos"], g[sl], shared_out)
         mbs.append({"slice": sl, "plan": plan, "A": A, "B": B, "h": h, "Y": Y})
@@ -131,7 +145,8 @@ def layer_backward_mx(cache: dict, dy, keep_operands: bool = False) -> dict:
     weight-gradient products, ``wgrad_operands[e][name]`` = list over minibatches
     of (a, b) with dW[e] = sum a^T b (names dw_down: (dYu, g h), dw_gate: (dA, X),
     dw_up: (dB, X)), from which a test bounds what one quantisation step of a
-    single product term can move an element."""
+    single product term can move an element, and ``row_values[m]`` = the
+    unquantised dh', dA and dB of minibatch m's rows (in plan order)."""
     dyf = _f64(dy)
     xf = cache["x"]
     T, H = xf.shape
@@ -145,17 +160,23 @@ def layer_backward_mx(cache: dict, dy, keep_operands: bool = False) -> dict:
     dx = np.zeros((T, H))
     dg = np.zeros((T, k))
     operands = {}
+    row_values = []
     for mb in cache["minibatches"]:
         sl, plan = mb["slice"], mb["plan"]
         n_rows = int(plan["offsets"][E])
         st = plan["src_token"][:n_rows]
         ss = plan["src_slot"][:n_rows]
-        dyq = q_rows(dyf[sl])
+        dyq = q_act("dy", dyf[sl])
         dY_rows = dyf[sl][st]
         X_rows = xf[sl][st]
         g_rows = g[sl][st, ss]
         dX = np.zeros((n_rows, H))
         dg_rows = np.zeros(n_rows)
+        if keep_operands:
+            I = mb["h"].shape[1] if mb["h"] is not None else 0
+            rv = {"dhp": np.zeros((n_rows, I)), "dA": np.zeros((n_rows, I)),
+                  "dB": np.zeros((n_rows, I))}
+            row_values.append(rv)
         for e in range(E):
             r0, r1 = int(plan["offsets"][e]), int(plan["offsets"][e + 1])
             if r1 == r0:
@@ -167,10 +188,12 @@ def layer_backward_mx(cache: dict, dy, keep_operands: bool = False) -> dict:
             dh = gr * dhp
             dA = dh * B * dsilu(A)
             dB = dh * silu(A)
-            dX[r0:r1] = q_rows(dA) @ qc.get("g_I", e) + q_rows(dB) @ qc.get("u_I", e)
-            Xt = q_tokens(X_rows[r0:r1])
-            ops = ((q_tokens(dY_rows[r0:r1]), q_tokens(gr * h)),
-                   (q_tokens(dA), Xt), (q_tokens(dB), Xt))
+            if keep_operands:
+                rv["dhp"][r0:r1], rv["dA"][r0:r1], rv["dB"][r0:r1] = dhp, dA, dB
+            dX[r0:r1] = q_act("dA", dA) @ qc.get("g_I", e) + q_act("dB", dB) @ qc.get("u_I", e)
+            Xt = q_act("wgrad", X_rows[r0:r1])
+            ops = ((q_act("wgrad", dY_rows[r0:r1]), q_act("wgrad", gr * h)),
+                   (q_act("wgrad", dA), Xt), (q_act("wgrad", dB), Xt))
             for store, name, (a, b) in zip((dWd, dWg, dWu), ("dw_down", "dw_gate", "dw_up"), ops):
                 p = a.T @ b
                 store[e] = p if store[e] is None else store[e] + p
@@ -191,6 +214,7 @@ def layer_backward_mx(cache: dict, dy, keep_operands: bool = False) -> dict:
     out = {"dg": dg, "dw_gate": np.stack(dWg), "dw_up": np.stack(dWu), "dw_down": np.stack(dWd)}
     if keep_operands:
         out["wgrad_operands"] = operands
+        out["row_values"] = row_values
     if cache["shared"] is not None:
         Sg, Su, Sd = (_f64(a) for a in cache["shared"])
         As, Bs = xf @ Sg.T, xf @ Su.T
@@ -212,24 +236,25 @@ def token_mx(x_t, idx_t, w_t, dy_t, qc: _QuantCache, shared=None, backward=True)
     (y_t, dx_t, dg_t); dx_t and dg_t are None without ``backward``.  The
     row-local quantisations (x and dy along H, h along I, dA and dB along I) do not
     depend on the minibatch, so these equal the planned results row for row."""
-    v = q_rows(_f64(x_t)[None])[0]
+    v = q_act("x", _f64(x_t)[None])[0]
     g = _f64(w_t)
     y = np.zeros_like(v)
     dx = np.zeros_like(v) if backward else None
     dg = np.zeros(len(idx_t)) if backward else None
-    d = q_rows(_f64(dy_t)[None])[0] if backward else None
+    d = q_act("dy", _f64(dy_t)[None])[0] if backward else None
     for j, e in enumerate(np.asarray(idx_t).astype(int)):
         A = qc.get("g_H", e) @ v
         B = qc.get("u_H", e) @ v
         h = silu(A) * B
-        y += g[j] * (qc.get("d_I", e) @ q_rows(h[None])[0])
+        y += g[j] * (qc.get("d_I", e) @ q_act("h", h[None])[0])
         if backward:
             dhp = qc.get("d_H", e).T @ d
             dg[j] = float(dhp @ h)
             dh = g[j] * dhp
             dA = dh * B * dsilu(A)
             dB = dh * silu(A)
-            dx += qc.get("g_I", e).T @ q_rows(dA[None])[0] + qc.get("u_I", e).T @ q_rows(dB[None])[0]
+            dx += (qc.get("g_I", e).T @ q_act("dA", dA[None])[0]
+                   + qc.get("u_I", e).T @ q_act("dB", dB[None])[0])
     if shared is not None:
         Sg, Su, Sd = (_f64(a) for a in shared)
         xf = _f64(x_t)

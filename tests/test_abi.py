@@ -106,3 +106,25 @@ def test_layout_functions(lib):
     assert B.moe_saved_bytes(s, B.MOE_F32) >= R * 2 * I * 4
     assert B.moe_workspace_bytes(s, B.MOE_BF16, True) >= R * (2 * I + I + H) * 2
     assert B.moe_plan_bytes(s_(E=0)) == 0
+
+
+def test_mx_rejects_shapes_whose_offsets_overflow(lib):
+    """MXFP8 calls refuse shapes whose 32-bit row offsets would overflow: one
+    minibatch of T*k rows of H = 7168 bytes reaches 2^31 at T = 37450 with k = 8."""
+    ok = s_(T=8192, H=7168, I=2048, E=256, k=8, T_minibatch=2048)
+    assert B.moe_workspace_bytes(ok, B.MOE_MXFP8, True) > 0
+    big = s_(T=37450, H=7168, I=2048, E=256, k=8, T_minibatch=0)
+    assert B.moe_workspace_bytes(big, B.MOE_MXFP8, True) == 0
+    assert B.moe_saved_bytes(big, B.MOE_MXFP8) == 0
+    rc = B.lib().moe_forward_mxfp8(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, None, None, None,
+                                   FAKE, FAKE, FAKE, 1 << 40, None)
+    assert rc == 5
+    # in minibatches of 8192 tokens the same T fits
+    assert B.moe_workspace_bytes(s_(T=37450, H=7168, I=2048, E=256, k=8, T_minibatch=8192),
+                                 B.MOE_MXFP8, True) > 0
+
+
+def test_router_gemm_needs_fp32_buffers():
+    from mixture_experts_layer_plan_amd import LayerBuffers
+    with pytest.raises(ValueError):
+        LayerBuffers(8, 256, 128, 4, 2, dtype="bf16", router_gemm=True, device="cpu")

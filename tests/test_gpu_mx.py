@@ -12,7 +12,7 @@ from gpu_util import digest, np_, say, shared_of, to_dev
 from oracle import moe_mx
 from oracle.mx import mx_quantize
 from synth import CONFIGS, Shape, make_inputs
-from tolerance import check, check_norm, one_flip_allowance
+from tolerance import check, mx_layer_allowances, one_flip_allowance
 
 pytestmark = pytest.mark.gpu
 
@@ -91,6 +91,16 @@ def test_weight_quantisation_all_orientations(B):
         np.testing.assert_array_equal(scales, rs.reshape(-1))
 
 
+def check_layer_outputs(b, inp, c, g, E):
+    """y, dx, d_topk_w and d_logits element by element; y and dx with the allowance
+    for the E4M3 codes of h and dZ that fp32 and fp64 values may round differently."""
+    y_al, dx_al = mx_layer_allowances(inp["x"], inp["dy"], c, g, E)
+    check(b.y, c["y"], "mxfp8", "y", allowance=y_al)
+    check(b.dx, g["dx"], "mxfp8", "dx", allowance=dx_al)
+    check(b.d_topk_w, g["dg"], "mxfp8", "d_topk_w")
+    check(b.d_logits, g["dlogits"], "mxfp8", "d_logits")
+
+
 def gpu_mx(shape, inp, T_mb):
     from mixture_experts_layer_plan_amd import LayerBuffers, run_layer
     b = LayerBuffers(shape.T, shape.H, shape.I, shape.E, shape.k, shape.I_shared, "mxfp8",
@@ -119,10 +129,7 @@ def test_mx_layer_small_all_outputs(name):
                                 inp["w_down"], shared=shared_of(inp), T_mb=T_mb)
     g = moe_mx.layer_backward_mx(c, inp["dy"], keep_operands=True)
     np.testing.assert_array_equal(np_(b.topk_idx), c["topk_idx"])
-    check(b.y, c["y"], "mxfp8", "y")
-    check(b.dx, g["dx"], "mxfp8", "dx")
-    check(b.d_topk_w, g["dg"], "mxfp8", "d_topk_w")
-    check(b.d_logits, g["dlogits"], "mxfp8", "d_logits")
+    check_layer_outputs(b, inp, c, g, shape.E)
     for e in range(shape.E):
         for n in ("dw_gate", "dw_up", "dw_down"):
             ops = g["wgrad_operands"].get(e, {}).get(n)
@@ -137,11 +144,7 @@ def test_mx_layer_small_all_outputs(name):
 def test_mx_hot_expert_weight_gradients(I):
     """Three experts whose packed token range reaches the large-tile wgrad threshold
     (256 bytes; one exactly at it), the others short, over four minibatches: every
-    weight gradient element by element.  y, dx and dg are held to the normwise bound
-    only: at these shapes a handful of their elements (4-5 of 524288) land 1.1-1.3x
-    past the per-element bound where an E4M3 code of h or dZ flips between the
-    kernel's fp32 and the oracle's fp64 values (an intermediate the weight-gradient
-    allowance does not cover; the same elements, independent of the wgrad kernels)."""
+    output element by element."""
     shape, T_mb = Shape(T=1024, H=512, I=I, E=12, k=2, I_shared=256, zipf_s=2.0,
                         dtype="mxfp8"), 256
     say(f"mx hot-expert wgrads: {shape} T_mb={T_mb}")
@@ -156,9 +159,7 @@ def test_mx_hot_expert_weight_gradients(I):
         for e in range(shape.E) for m in range(shape.T // T_mb)]
     per_e = np.array(packed).reshape(shape.E, -1).sum(axis=1)
     assert (per_e >= 256).sum() == 3 and (per_e == 256).any(), per_e
-    check_norm(b.y, c["y"], "mxfp8", "y")
-    check_norm(b.dx, g["dx"], "mxfp8", "dx")
-    check_norm(b.d_topk_w, g["dg"], "mxfp8", "d_topk_w")
+    check_layer_outputs(b, inp, c, g, shape.E)
     for e in range(shape.E):
         for n in ("dw_gate", "dw_up", "dw_down"):
             ops = g["wgrad_operands"].get(e, {}).get(n)
@@ -175,11 +176,11 @@ MX_EXACT_COUNTS = [0, 1, 31, 32, 33, 127, 128, 129, 255, 256, 257, 300]
 
 @pytest.mark.parametrize("T_mb", [0, 512])
 def test_mx_layer_exact_row_counts(T_mb):
-    """Every weight gradient element by element; y, dx and dg normwise only, as in
-    test_mx_hot_expert_weight_gradients: here two rows of the 300-row expert hold two
-    E4M3 codes of h each that differ between the kernel's fp32 pre-activations and the
-    oracle's fp64 ones (same E8M0 scales; the pre-activations agree to 1.1e-5 and
-    straddle a rounding midpoint), which moves those rows of y by 1.5 % and 3.6 %."""
+    """Every output element by element.  Two rows of the 300-row expert hold E4M3
+    codes of h that differ between the kernel's fp32 pre-activations and the oracle's
+    fp64 ones (the pre-activations agree to 1.1e-5 and straddle a rounding midpoint),
+    which moves those rows of y by up to 3.6 %: the allowance for such code choices
+    covers them."""
     counts = np.array(MX_EXACT_COUNTS)
     shape = Shape(T=int(counts.sum()), H=256, I=256, E=len(counts), k=1, dtype="mxfp8")
     say(f"mx layer exact counts {MX_EXACT_COUNTS}: {shape} T_mb={T_mb}")
@@ -196,9 +197,7 @@ def test_mx_layer_exact_row_counts(T_mb):
     g = moe_mx.layer_backward_mx(c, inp["dy"], keep_operands=True)
     np.testing.assert_array_equal(np_(b.topk_idx), c["topk_idx"])
     np.testing.assert_array_equal(np.bincount(c["topk_idx"].ravel(), minlength=shape.E), counts)
-    check_norm(b.y, c["y"], "mxfp8", "y")
-    check_norm(b.dx, g["dx"], "mxfp8", "dx")
-    check_norm(b.d_topk_w, g["dg"], "mxfp8", "d_topk_w")
+    check_layer_outputs(b, inp, c, g, shape.E)
     for e in range(shape.E):
         for n in ("dw_gate", "dw_up", "dw_down"):
             ops = g["wgrad_operands"].get(e, {}).get(n)

@@ -145,3 +145,120 @@ def test_per_token_mx_equals_planned_rows():
         np.testing.assert_allclose(y_t, c["y"][t], rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(dx_t, g["dx"][t], rtol=1e-11, atol=1e-12)
         np.testing.assert_allclose(dg_t, g["dg"][t], rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------
+# One pin per remaining quantisation point.  Each builds an operand whose slices
+# differ by 2^20 across the axis that must NOT be blocked, checks the MX layer per
+# slice against the exact layer, and, with the point moved to the other axis (a
+# mistake planted in the oracle for the test), checks that the same comparison
+# fails: the pin would catch a shared wrong axis in the oracle and the kernels.
+
+def _swap(monkeypatch, point):
+    """Put quantisation point `point` on the other axis."""
+    if point is None:
+        return
+    if point in moe_mx.WEIGHT_AXIS:
+        which, axis = moe_mx.WEIGHT_AXIS[point]
+        monkeypatch.setitem(moe_mx.WEIGHT_AXIS, point, (which, "cols" if axis == "rows" else "rows"))
+    else:
+        monkeypatch.setitem(moe_mx.ACT_AXIS, point, "tokens")
+
+
+def _exact(d, k=1):
+    ce = oracle.layer_forward(d["x"], d["logits"], k, d["w_gate"], d["w_up"], d["w_down"])
+    return ce, oracle.layer_backward(ce, d["dy"])
+
+
+def _worst(a, ref, axis):
+    """Largest relative error over the slices along `axis` (norms over the other axis)."""
+    return np.max(np.linalg.norm(a - ref, axis=axis) / np.linalg.norm(ref, axis=axis))
+
+
+def _small_layer(seed):
+    rng = np.random.default_rng(seed)
+    return rng, rand_layer(rng, 40, 64, 64, 1, shared=False)
+
+
+@pytest.mark.parametrize("swap", [None, "d_I"])
+def test_down_weights_are_blocked_along_I_in_the_forward(monkeypatch, swap):
+    """W_d rows alternate by 2^20: Y = Q_I(h) Q_I(W_d)^T keeps every column of y only
+    with W_d blocked along I (per row of W_d)."""
+    _swap(monkeypatch, swap)
+    rng, d = _small_layer(10)
+    d["w_down"][0] = binade_scaled(rng, d["w_down"][0].shape, 0)
+    c, _ = run_mx(d, 1, 0)
+    ce, _ = _exact(d)
+    worst = _worst(c["y"], ce["y"], 0)
+    assert (worst < 0.3) if swap is None else (worst > 0.6), worst
+
+
+@pytest.mark.parametrize("swap", [None, "d_H"])
+def test_down_weights_are_blocked_along_H_in_dgrad_down(monkeypatch, swap):
+    """W_d columns alternate by 2^20: dh' = Q_H(dy) Q_H(W_d) keeps every column of dh'
+    (seen through the rows of dW_g = Q_t(dA)^T Q_t(X), dA ~ dh') only with W_d blocked
+    along H (per column of W_d)."""
+    _swap(monkeypatch, swap)
+    rng, d = _small_layer(11)
+    d["w_down"][0] = binade_scaled(rng, d["w_down"][0].shape, 1)
+    _, g = run_mx(d, 1, 0)
+    _, ge = _exact(d)
+    worst = _worst(g["dw_gate"][0], ge["dw_gate"][0], 1)
+    assert (worst < 0.3) if swap is None else (worst > 0.6), worst
+
+
+@pytest.mark.parametrize("swap", [None, "h"])
+def test_h_is_blocked_along_I(monkeypatch, swap):
+    """Tokens alternate by 2^20 (so rows of h by about 2^40): Y = Q_I(h) W_d^T keeps
+    every row of y only with h blocked along I (per row)."""
+    _swap(monkeypatch, swap)
+    rng, d = _small_layer(12)
+    d["x"] = binade_scaled(rng, d["x"].shape, 0)
+    c, _ = run_mx(d, 1, 0)
+    ce, _ = _exact(d)
+    worst = _worst(c["y"], ce["y"], 1)
+    assert (worst < 0.3) if swap is None else (worst > 0.6), worst
+
+
+@pytest.mark.parametrize("swap", [None, "dy", "dA", "dB"])
+def test_dy_and_dgrad_up_activations_are_blocked_along_their_rows(monkeypatch, swap):
+    """Rows of dy alternate by 2^20, and so do the rows of dh', dA and dB:
+    dh' = Q_H(dy) Q_H(W_d) and dX = Q_I(dA) Q_I(W_g) + Q_I(dB) Q_I(W_u) keep every row
+    of dx only with dy blocked along H and dA, dB each blocked along I (per row)."""
+    _swap(monkeypatch, swap)
+    rng, d = _small_layer(13)
+    d["dy"] = binade_scaled(rng, d["dy"].shape, 0)
+    _, g = run_mx(d, 1, 0)
+    _, ge = _exact(d)
+    worst = _worst(g["dx"], ge["dx"], 1)
+    assert (worst < 0.3) if swap is None else (worst > 0.6), worst
+
+
+@pytest.mark.parametrize("swap", [None, "g_H", "x"])
+def test_forward_blocking_pins_fail_when_swapped(monkeypatch, swap):
+    """The earlier forward pins (W_g along H; x along H) with their point swapped."""
+    _swap(monkeypatch, swap)
+    rng = np.random.default_rng(2)
+    d = rand_layer(rng, 40, 64, 64, 1, shared=False)
+    if swap == "x":
+        d["x"] = binade_scaled(rng, (40, 64), 0)
+    else:
+        d["w_gate"][0] = binade_scaled(rng, (64, 64), 0)
+    c, _ = run_mx(d, 1, 0)
+    A_exact = d["x"] @ d["w_gate"][0].T
+    A_mx = c["minibatches"][0]["A"]
+    worst = _worst(A_mx, A_exact, 1 if swap == "x" else 0)
+    assert (worst < 0.3) if swap is None else (worst > 0.6), worst
+
+
+@pytest.mark.parametrize("swap", ["g_I", "u_I"])
+def test_dgrad_up_weight_pin_fails_when_swapped(monkeypatch, swap):
+    """test_dgrad_up_weights_are_blocked_along_I with one weight on the other axis."""
+    _swap(monkeypatch, swap)
+    rng = np.random.default_rng(4)
+    d = rand_layer(rng, 40, 64, 64, 1, shared=False)
+    d["w_gate"][0] = binade_scaled(rng, (64, 64), 1)
+    d["w_up"][0] = binade_scaled(rng, (64, 64), 1)
+    _, g = run_mx(d, 1, 0)
+    _, ge = _exact(d)
+    assert _worst(g["dx"], ge["dx"], 0) > 0.5
