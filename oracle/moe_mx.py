@@ -18,13 +18,16 @@ rule in ``oracle.mx``), and everything else is the fp64 definition of
             dX = Q_2I(dA|dB) [Q_I(W_g); Q_I(W_u)]      (weights blocked along I)
             dW_d[e] = Q_t(dYu)^T Q_t(g h), dW_g[e] = Q_t(dA)^T Q_t(X),
             dW_u[e] = Q_t(dB)^T Q_t(X)
-where Q_t blocks along the tokens of one expert's segment in one minibatch,
-32 rows at a time from the segment's first row, the last block zero-padded.
+where Q_t blocks along the tokens of expert e: its rows of the whole macro batch
+(every minibatch, in token order), 32 rows at a time from its first row, the
+last block zero-padded.
 
 Tokens are processed in consecutive minibatches of T_mb (the ring-buffer macro
 batch, stamatios.com § Ring token buffers); each minibatch has its own plan.
-Weight gradients sum the per-minibatch products (in fp64 the order is
-immaterial).  The shared expert is the exact bf16-input definition.
+The weight-gradient blocks span minibatches so that the gradients do not depend
+on T_mb: the pages state that the fixed order makes results independent of the
+batch size (sebask.de, § Determinismus und MXFP8-Unterstützung).  The shared
+expert is the exact bf16-input definition.
 """
 from __future__ import annotations
 
@@ -142,8 +145,8 @@ def layer_forward_mx(x, logits, k, w_gate, w_up, w_down, shared=None, T_mb=0,
 def layer_backward_mx(cache: dict, dy, keep_operands: bool = False) -> dict:
     """Backward of ``layer_forward_mx`` (selection held fixed).  With
     ``keep_operands`` the result also holds the quantised operands of the three
-    weight-gradient products, ``wgrad_operands[e][name]`` = list over minibatches
-    of (a, b) with dW[e] = sum a^T b (names dw_down: (dYu, g h), dw_gate: (dA, X),
+    weight-gradient products, ``wgrad_operands[e][name]`` = [(a, b)] with
+    dW[e] = a^T b (names dw_down: (dYu, g h), dw_gate: (dA, X),
     dw_up: (dB, X)), from which a test bounds what one quantisation step of a
     single product term can move an element, and ``row_values[m]`` = the
     unquantised dh', dA and dB of minibatch m's rows (in plan order)."""
@@ -161,6 +164,7 @@ def layer_backward_mx(cache: dict, dy, keep_operands: bool = False) -> dict:
     dg = np.zeros((T, k))
     operands = {}
     row_values = []
+    wrows = {}
     for mb in cache["minibatches"]:
         sl, plan = mb["slice"], mb["plan"]
         n_rows = int(plan["offsets"][E])
@@ -191,14 +195,11 @@ def layer_backward_mx(cache: dict, dy, keep_operands: bool = False) -> dict:
             if keep_operands:
                 rv["dhp"][r0:r1], rv["dA"][r0:r1], rv["dB"][r0:r1] = dhp, dA, dB
             dX[r0:r1] = q_act("dA", dA) @ qc.get("g_I", e) + q_act("dB", dB) @ qc.get("u_I", e)
-            Xt = q_act("wgrad", X_rows[r0:r1])
-            ops = ((q_act("wgrad", dY_rows[r0:r1]), q_act("wgrad", gr * h)),
-                   (q_act("wgrad", dA), Xt), (q_act("wgrad", dB), Xt))
-            for store, name, (a, b) in zip((dWd, dWg, dWu), ("dw_down", "dw_gate", "dw_up"), ops):
-                p = a.T @ b
-                store[e] = p if store[e] is None else store[e] + p
-                if keep_operands:
-                    operands.setdefault(e, {}).setdefault(name, []).append((a, b))
+            # this minibatch's rows of the weight-gradient operands, in token order
+            rows_e = wrows.setdefault(e, {"dYu": [], "gh": [], "dA": [], "dB": [], "X": []})
+            for name, v in (("dYu", dY_rows[r0:r1]), ("gh", gr * h), ("dA", dA), ("dB", dB),
+                            ("X", X_rows[r0:r1])):
+                rows_e[name].append(v)
         P = plan["pos"]
         Tm = P.shape[0]
         for t in range(Tm):
@@ -206,6 +207,15 @@ def layer_backward_mx(cache: dict, dy, keep_operands: bool = False) -> dict:
                 if P[t, j] >= 0:
                     dx[sl.start + t] += dX[P[t, j]]
                     dg[sl.start + t, j] = dg_rows[P[t, j]]
+    # weight gradients: each expert's rows of all minibatches, quantised along those
+    # tokens in blocks of 32 from the first
+    for e, rows_e in wrows.items():
+        q = {name: q_act("wgrad", np.concatenate(v)) for name, v in rows_e.items()}
+        ops = ((q["dYu"], q["gh"]), (q["dA"], q["X"]), (q["dB"], q["X"]))
+        for store, name, (a, b) in zip((dWd, dWg, dWu), ("dw_down", "dw_gate", "dw_up"), ops):
+            store[e] = a.T @ b
+            if keep_operands:
+                operands.setdefault(e, {})[name] = [(a, b)]
     for e in range(E):
         if dWg[e] is None:
             dWg[e] = np.zeros(tuple(w_gate[e].shape))

@@ -24,7 +24,9 @@ def run_mx(d, k, T_mb):
     return c, moe_mx.layer_backward_mx(c, d["dy"])
 
 
-def test_row_local_outputs_do_not_depend_on_minibatch_size():
+def test_outputs_do_not_depend_on_minibatch_size():
+    """Row-local outputs, and the weight gradients (whose token blocks run over each
+    expert's rows of the whole macro batch), are the same for every minibatch size."""
     rng = np.random.default_rng(0)
     d = rand_layer(rng, 96, 64, 64, 6)
     ref_c, ref_g = run_mx(d, 2, 0)
@@ -33,6 +35,27 @@ def test_row_local_outputs_do_not_depend_on_minibatch_size():
         np.testing.assert_allclose(c["y"], ref_c["y"], rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(g["dx"], ref_g["dx"], rtol=1e-11, atol=1e-12)
         np.testing.assert_allclose(g["dg"], ref_g["dg"], rtol=1e-11, atol=1e-12)
+        for n in ("dw_gate", "dw_up", "dw_down"):
+            np.testing.assert_array_equal(g[n], ref_g[n])
+
+
+def test_weight_gradient_blocks_span_minibatches():
+    """An expert's first 32 rows form one block even when a minibatch boundary falls
+    inside them: one token among the first 32 scaled by 2^12 flushes the small rows
+    of its block (an effect of MX blocking the oracle keeps), and moving the boundary
+    to T_mb = 10 changes nothing."""
+    rng = np.random.default_rng(8)
+    d = rand_layer(rng, 64, 64, 64, 1, shared=False)
+    d["x"][20] *= 2.0 ** 12
+    _, g0 = run_mx(d, 1, 0)
+    _, g1 = run_mx(d, 1, 10)
+    np.testing.assert_array_equal(g0["dw_gate"], g1["dw_gate"])
+    # per-minibatch blocks (rows 0-9, 10-19, 20-29, ...) would keep row 5's small
+    # values: the shared-block result differs from that blocking
+    X = d["x"]
+    blk = moe_mx.q_tokens(X[:32])
+    per_mb = np.concatenate([moe_mx.q_tokens(X[i:i + 10]) for i in (0, 10, 20)])[:30]
+    assert not np.array_equal(blk[:30], per_mb)
 
 
 def rel(a, b):
