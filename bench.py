@@ -58,9 +58,9 @@ def kernel_work(name, sh, counts_mb, es=2):
     hot_split = es == 2 and H % 256 == 0 and I % 256 == 0 and not sh.T_minibatch
     Eh = sum(1 for v in union if v >= WGRAD_HOT_ROWS) if hot_split else 0
     Rh = sum(v for v in union if v >= WGRAD_HOT_ROWS) if hot_split else 0
-    # MXFP8 wgrads: experts whose packed token range (each minibatch segment padded to
-    # 32 rows) has >= MX_WGRAD_HOT_BYTES bytes go to the 256-tile kernel
-    packed = [sum(-(-c[e] // 32) * 32 for c in counts_mb) for e in range(E)]
+    # MXFP8 wgrads: experts whose packed token range (their rows of all minibatches,
+    # padded to 32) has >= MX_WGRAD_HOT_BYTES bytes go to the 256-tile kernel
+    packed = [-(-union[e] // 32) * 32 for e in range(E)]
     mx_hot = [e for e in range(E) if packed[e] >= MX_WGRAD_HOT_BYTES] \
         if H % 256 == 0 and I % 256 == 0 else []
     Emx = len(mx_hot)
@@ -113,8 +113,12 @@ def kernel_work(name, sh, counts_mb, es=2):
         # x (forward) and dy (backward) gathered into the ring and quantised: each
         # source row read once, its k rows written as E4M3 codes with scales
         "mx_quant_rows": lambda: over_mb(lambda Rm, Etm, tm: (2 * (tm * H * 2 + Rm * H * q + Rm * 4), 0)),
-        "mx_quant_tokens": lambda: over_mb(lambda Rm, Etm, tm: (Rm * (2 * H * (2 + q) + I * (4 + q)
-                                                                      + 2 * I * (4 + q)), 0)),
+        # the wgrad operands of the macro batch, quantised along each expert's tokens:
+        # dy and x (bf16 sources read once per token), g h and dZ (fp32 rows), the
+        # row maps
+        "mx_quant_tokens": lambda: (int(2 * (T * H * 2 + R * H * q) + R * I * (4 + q)
+                                        + R * 2 * I * (4 + q) + 4 * R * 4), 0),
+        "mb_rows": lambda: (R * 20, 0),
         "mx_gemm_up_swiglu": lambda: over_mb(lambda Rm, Etm, tm: (
             Etm * 2 * I * H * q + Rm * H * q + Rm * 2 * I * 4 + Rm * I * q, 2 * Rm * H * 2 * I)),
         "mx_gemm_down": lambda: over_mb(lambda Rm, Etm, tm: (

@@ -128,6 +128,17 @@ typedef struct moe_trace {
 
 void moe_trace_set(moe_trace* trace);
 
+/* Compute units that the persistent kernels of calls from this host thread size
+ * their grids for (the weight-gradient kernels run a fixed number of workgroups
+ * that walk their work items): 0 (the default) = every CU of the device, otherwise
+ * min(cus, the device's CUs).  For callers that keep CUs busy with other work on
+ * another stream, as the pages partition SMs in software between communication and
+ * computation (stamatios.com, § Granularidade do overlap).  Outputs do not depend
+ * on it: every output element is produced by one workgroup with a fixed K order
+ * (sebask.de, § Determinismus und MXFP8-Unterstützung).  Per host thread, like the
+ * trace. */
+void moe_set_cu_budget(int32_t cus);
+
 /* Layout and size of the plan buffer for `shape` (T, k, E are used). */
 moe_status moe_plan_layout_of(const moe_shape* shape, moe_plan_layout* out);
 size_t moe_plan_bytes(const moe_shape* shape);

@@ -61,6 +61,7 @@ class moe_trace(ctypes.Structure):
 _SIGS = {
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_trace_set": (None, [ctypes.POINTER(moe_trace)]),
+    "moe_set_cu_budget": (None, [ctypes.c_int32]),
     "moe_plan_layout_of": (ctypes.c_int, [_S, ctypes.POINTER(moe_plan_layout)]),
     "moe_plan_bytes": (_Z, [_S]),
     "moe_saved_bytes": (_Z, [_S, _I]),
@@ -155,6 +156,10 @@ def _call(name, *args):
     rc = getattr(lib(), name)(*args)
     if rc != 0:
         raise MoeError(name, rc, lib().moe_status_str(rc).decode())
+
+
+def moe_set_cu_budget(cus: int) -> None:
+    lib().moe_set_cu_budget(int(cus))
 
 
 def moe_status_str(code: int) -> str:

@@ -16,6 +16,15 @@ typedef uint16_t bf16_t_host;  // bfloat16 bits on the host side
 namespace moe {
 
 thread_local ::moe_trace* tls_trace = nullptr;
+thread_local int tls_cu_budget = 0;
+
+int device_cus() {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (cus <= 0) cus = 256;
+  return tls_cu_budget > 0 && tls_cu_budget < cus ? tls_cu_budget : cus;
+}
 
 void trace_before(hipStream_t s, const char* name) {
   moe_trace* t = tls_trace;
@@ -448,42 +457,55 @@ MxFwdWs mx_fwd_ws(const moe_shape* s) {
   return L;
 }
 
-// Backward workspace: per-minibatch buffers (dYu ring, dZ fp32 and MX, g h fp32,
-// dg partials, dX) and the token-quantised wgrad operands of all minibatches
-// (the transposed token axis of the wgrads: Kp = n_mb * max_tiles * 128 bytes per row,
-// of which the experts' padded segments use at most all but 97).
+// Backward workspace: per-minibatch buffers (dYu ring, dZ MX, dg partials, dX), the
+// fp32 dZ and g h of every minibatch (minibatch m's rows at m * R_mb), the
+// token-quantised wgrad operands on the packed token axis of the macro batch (Kp
+// bytes per row: each expert's rows of all minibatches padded to 32, plus at least
+// 128 bytes of tail that the large-tile wgrad may read past the last expert) and the
+// arrays that map that axis to the minibatch plans.
 struct MxBwdWs {
   size_t ring8[2], rings[2], dZ, dZ8, dZs, gh, dgp, dX;
   size_t dYuT8, dYuTs, ghT8, ghTs, dZT8, dZTs, XT8, XTs;
-  size_t counts_all, active, n_active, kseg, kpos;
+  size_t counts_all, active, n_active, cum, kpos, goff, gtiles, n_gtiles, grow, gtok;
   size_t dZs_sh, hs_sh, dxs, total;
   size_t Kp;
+  int max_gtiles;
 };
+size_t mx_token_axis_bytes(const moe_shape* s) {
+  const size_t R = (size_t)s->T * s->k;
+  return (R + 32 * (size_t)std::min<size_t>(s->E, R) + 127) / 128 * 128 + 128;
+}
 MxBwdWs mx_bwd_ws(const moe_shape* s) {
-  const moe_plan_layout P = plan_layout(s);
   const size_t Tm = minibatch_tokens(s), R = Tm * s->k, H = s->H, I = s->I, T = s->T;
-  const size_t Kp = (size_t)n_minibatches(s) * P.max_tiles * 128;
+  const size_t nmb = n_minibatches(s), Rall = nmb * R, Rtot = T * s->k;
+  const size_t Kp = mx_token_axis_bytes(s);
   Carve c;
   MxBwdWs L;
   for (int i = 0; i < 2; ++i) {
     L.ring8[i] = c.take(R * H);
     L.rings[i] = c.take(R * H / 32);
   }
-  L.dZ = c.take(R * 2 * I * sizeof(float));
+  L.dZ = c.take(Rall * 2 * I * sizeof(float));
   L.dZ8 = c.take(R * 2 * I);
   L.dZs = c.take(R * 2 * I / 32);
-  L.gh = c.take(R * I * sizeof(float));
+  L.gh = c.take(Rall * I * sizeof(float));
   L.dgp = c.take(R * (I / 128) * sizeof(float));
   L.dX = c.take(R * H * 2);
   L.dYuT8 = c.take(H * Kp); L.dYuTs = c.take(H * Kp / 32);
   L.ghT8 = c.take(I * Kp); L.ghTs = c.take(I * Kp / 32);
   L.dZT8 = c.take(2 * I * Kp); L.dZTs = c.take(2 * I * Kp / 32);
   L.XT8 = c.take(H * Kp); L.XTs = c.take(H * Kp / 32);
+  L.max_gtiles = (int)(Rtot / 128 + std::min<size_t>(s->E, Rtot) + 1);
   L.counts_all = c.take(sizeof(int32_t) * s->E);
   L.active = c.take(sizeof(int32_t) * s->E);
   L.n_active = c.take(sizeof(int32_t));
-  L.kseg = c.take(sizeof(int32_t) * (size_t)n_minibatches(s) * s->E);
+  L.cum = c.take(sizeof(int32_t) * nmb * s->E);
   L.kpos = c.take(sizeof(int32_t) * (s->E + 1));
+  L.goff = c.take(sizeof(int32_t) * (s->E + 1));
+  L.gtiles = c.take(sizeof(int32_t) * 2 * (size_t)L.max_gtiles);
+  L.n_gtiles = c.take(sizeof(int32_t));
+  L.grow = c.take(sizeof(int32_t) * Rtot);
+  L.gtok = c.take(sizeof(int32_t) * Rtot);
   L.dZs_sh = c.take(T * 2 * s->I_shared * 2);
   L.hs_sh = c.take(T * s->I_shared * 2);
   L.dxs = c.take(s->I_shared ? T * H * 2 : 0);
@@ -503,9 +525,7 @@ bool mx_offsets_fit(const moe_shape* s) {
   const uint64_t ws = std::max<uint64_t>((uint64_t)s->H, 2ull * s->I_shared);
   if ((uint64_t)s->T * ws * 2 >= (1ull << 32) || (uint64_t)s->I_shared * s->H * 2 >= (1ull << 32))
     return false;
-  const moe_plan_layout P = plan_layout(s);
-  const uint64_t Kp = (uint64_t)n_minibatches(s) * P.max_tiles * 128;
-  return 256 * Kp < (1ull << 32);
+  return 256 * (uint64_t)mx_token_axis_bytes(s) < (1ull << 32);
 }
 
 moe_status check_mx(const moe_shape* s) {
@@ -597,20 +617,37 @@ moe_status backward_mx_impl(const moe_shape* s, const void* plan, const void* x,
     MOE_TRY(launch_gemm_dgrad_up(1, gs, dZs, sg, su, H, Is, dxs, st));
     MOE_TRY(launch_gemm_wgrad_up(1, gs, dZs, x, H, Is, dsg, dsu, st));
   }
-  // the wgrads' token axis over all minibatches (offsets per expert and minibatch)
-  const int32_t* counts[MX_MAX_MB];
-  for (int m = 0; m < nmb; ++m) counts[m] = view_plan(s, plan, m).counts;
-  int32_t* counts_all = at<int32_t>(ws, W.counts_all);
-  int32_t* active = at<int32_t>(ws, W.active);
-  int32_t* n_active = at<int32_t>(ws, W.n_active);
-  int32_t* kseg = at<int32_t>(ws, W.kseg);
-  int32_t* kpos = at<int32_t>(ws, W.kpos);
-  MOE_TRY(launch_mb_union(counts, nmb, s->E, counts_all, active, n_active, kseg, kpos, st));
+  // the wgrads' token axis over all minibatches: each expert's rows of the macro batch
+  // in token order (global rows), their packed columns and plan rows
+  MbPlanViews pv;
+  memset(&pv, 0, sizeof(pv));
+  pv.n_mb = nmb;
+  for (int m = 0; m < nmb; ++m) {
+    const PlanView v = view_plan(s, plan, m);
+    pv.counts[m] = v.counts;
+    pv.offsets[m] = v.offsets;
+    pv.tiles[m] = v.tiles;
+    pv.n_tiles[m] = v.n_tiles;
+    pv.src_token[m] = v.src_token;
+  }
+  MbAxis ax;
+  ax.counts_all = at<int32_t>(ws, W.counts_all);
+  ax.active = at<int32_t>(ws, W.active);
+  ax.n_active = at<int32_t>(ws, W.n_active);
+  ax.cum = at<int32_t>(ws, W.cum);
+  ax.kpos = at<int32_t>(ws, W.kpos);
+  ax.goff = at<int32_t>(ws, W.goff);
+  ax.gtiles = at<int32_t>(ws, W.gtiles);
+  ax.n_gtiles = at<int32_t>(ws, W.n_gtiles);
+  ax.grow = at<int32_t>(ws, W.grow);
+  ax.gtok = at<int32_t>(ws, W.gtok);
+  MOE_TRY(launch_mb_union(pv, s->E, ax, st));
+  MOE_TRY(launch_mb_rows(pv, s->E, P.max_tiles, Tmb * k, Tmb, ax, st));
   MbPlans mp;
   mp.n_mb = nmb;
-  mp.kpos = kpos;
-  mp.active = active;
-  mp.n_active = n_active;
+  mp.kpos = ax.kpos;
+  mp.active = ax.active;
+  mp.n_active = ax.n_active;
   for (int m = nmb - 1; m >= 0; --m) {
     const int T_m = std::min(Tmb, s->T - m * Tmb), R_m = T_m * k;
     const PlanView v = view_plan(s, plan, m);
@@ -618,41 +655,41 @@ moe_status backward_mx_impl(const moe_shape* s, const void* plan, const void* x,
     const GroupInfo g = grouped(s, v);
     const size_t tok0 = (size_t)m * Tmb;
     const bf16_t_host* dym = (const bf16_t_host*)dy + tok0 * H;
-    const bf16_t_host* xm = (const bf16_t_host*)x + tok0 * H;
     uint8_t* dYu8 = at<uint8_t>(ws, W.ring8[m & 1]);
     uint8_t* dYus = at<uint8_t>(ws, W.rings[m & 1]);
     const float* Z = at<float>(saved, S.Z) + tok0 * k * 2 * I;
-    void* dZ = at<char>(ws, W.dZ);
+    float* dZ = at<float>(ws, W.dZ) + tok0 * k * 2 * I;
     uint8_t* dZ8 = at<uint8_t>(ws, W.dZ8);
     uint8_t* dZsc = at<uint8_t>(ws, W.dZs);
-    void* gh = at<char>(ws, W.gh);
+    float* gh = at<float>(ws, W.gh) + tok0 * k * I;
     float* dgp = at<float>(ws, W.dgp);
     void* dX = at<char>(ws, W.dX);
-    const int32_t* ksm = kseg + (size_t)m * s->E;
     // reverse-combine into the ring slot, quantised along H
     MOE_TRY(launch_quant_rows(1, dym, v.src_token, v.offsets + s->E, R_m, H, dYu8, dYus, st));
     MOE_TRY(launch_mx_dgrad_down(g, dYu8, dYus, q + Q.wdT8, q + Q.wdTs, Z, topk_w + tok0 * k, H,
                                  I, k, dZ, dZ8, dZsc, gh, dgp, st));
     MOE_TRY(launch_dg_reduce(dgp, v.pos, R_m, I / 128, d_topk_w + tok0 * k, st));
-    // wgrad operands of this minibatch, quantised along its tokens
-    MOE_TRY(launch_quant_tokens(1, dym, v.src_token, H, v.tiles, v.n_tiles, v.offsets, kpos, ksm,
-                                P.max_tiles, H, W.Kp, at<uint8_t>(ws, W.dYuT8),
-                                at<uint8_t>(ws, W.dYuTs), st));
-    MOE_TRY(launch_quant_tokens(1, xm, v.src_token, H, v.tiles, v.n_tiles, v.offsets, kpos, ksm,
-                                P.max_tiles, H, W.Kp, at<uint8_t>(ws, W.XT8),
-                                at<uint8_t>(ws, W.XTs), st));
-    MOE_TRY(launch_quant_tokens(0, gh, nullptr, I, v.tiles, v.n_tiles, v.offsets, kpos, ksm,
-                                P.max_tiles, I, W.Kp, at<uint8_t>(ws, W.ghT8),
-                                at<uint8_t>(ws, W.ghTs), st));
-    MOE_TRY(launch_quant_tokens(0, dZ, nullptr, 2 * I, v.tiles, v.n_tiles, v.offsets, kpos, ksm,
-                                P.max_tiles, 2 * I, W.Kp, at<uint8_t>(ws, W.dZT8),
-                                at<uint8_t>(ws, W.dZTs), st));
     MOE_TRY(launch_mx_dgrad_up(g, dZ8, dZsc, q + Q.wgT8, q + Q.wgTs, q + Q.wuT8, q + Q.wuTs, H, I,
                                dX, st));
     MOE_TRY(launch_combine_bf16(dX, v.pos, nullptr,
                                 dxs ? (const bf16_t_host*)dxs + tok0 * H : nullptr,
                                 (bf16_t_host*)dx + tok0 * H, T_m, k, H, st));
   }
+  // wgrad operands of the macro batch, quantised along each expert's tokens (blocks
+  // from its first row, spanning minibatches): dy and x pulled by token, g h and dZ
+  // from the rows the minibatches stored
+  MOE_TRY(launch_quant_tokens(1, dy, ax.gtok, H, ax.gtiles, ax.n_gtiles, ax.goff, ax.kpos, nullptr,
+                              W.max_gtiles, H, W.Kp, at<uint8_t>(ws, W.dYuT8),
+                              at<uint8_t>(ws, W.dYuTs), st));
+  MOE_TRY(launch_quant_tokens(1, x, ax.gtok, H, ax.gtiles, ax.n_gtiles, ax.goff, ax.kpos, nullptr,
+                              W.max_gtiles, H, W.Kp, at<uint8_t>(ws, W.XT8),
+                              at<uint8_t>(ws, W.XTs), st));
+  MOE_TRY(launch_quant_tokens(0, at<float>(ws, W.gh), ax.grow, I, ax.gtiles, ax.n_gtiles, ax.goff,
+                              ax.kpos, nullptr, W.max_gtiles, I, W.Kp, at<uint8_t>(ws, W.ghT8),
+                              at<uint8_t>(ws, W.ghTs), st));
+  MOE_TRY(launch_quant_tokens(0, at<float>(ws, W.dZ), ax.grow, 2 * I, ax.gtiles, ax.n_gtiles,
+                              ax.goff, ax.kpos, nullptr, W.max_gtiles, 2 * I, W.Kp,
+                              at<uint8_t>(ws, W.dZT8), at<uint8_t>(ws, W.dZTs), st));
   // Experts with a long packed token range run on the 256-tile kernel; the 128-tile
   // kernel takes the others and stores the zero gradients of experts without rows.
   int hot = MX_WGRAD_HOT_BYTES;
@@ -681,6 +718,8 @@ moe_status backward_mx_impl(const moe_shape* s, const void* plan, const void* x,
 extern "C" {
 
 void moe_trace_set(moe_trace* trace) { moe::tls_trace = trace; }
+
+void moe_set_cu_budget(int32_t cus) { moe::tls_cu_budget = cus > 0 ? cus : 0; }
 
 const char* moe_status_str(moe_status s) {
   switch (s) {

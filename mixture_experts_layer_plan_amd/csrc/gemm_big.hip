@@ -1056,9 +1056,7 @@ static hipError_t wgrad_hot(const char* name, const GroupInfo& g, const void* A,
   p.M = M;
   p.N = N;
   p.half_rows = half_rows;
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess)
-    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int cus = device_cus();
   const unsigned grid = (unsigned)(cus >= N_XCD ? cus - cus % N_XCD : N_XCD);
   p.PM = M / big::TILE;
   p.PN = N / big::TILE;
@@ -1105,9 +1103,7 @@ hipError_t launch_mx_wgrad_hot(const char* name, const MbPlans& mp, int E, uint8
   p.PM = M / big::TILE;
   p.PN = N / big::TILE;
   p.GM = xcd_grid_rows(p.PM, p.PN);
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess)
-    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int cus = device_cus();
   const unsigned grid = (unsigned)(cus >= N_XCD ? cus - cus % N_XCD : N_XCD);
   hipError_t err = MOE_LAUNCH("mx_zero_tail", s,
                               big::mx_zero_tail_kernel<<<(M * 8 + 255) / 256, 256, 0, s>>>(

@@ -558,10 +558,7 @@ MOE_DEV void zero_span(T* out) {
 
 // Persistent grid: two resident workgroups per compute unit, at most one per item.
 inline unsigned persistent_grid(long items) {
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess)
-    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  const long g = 2L * (cus > 0 ? cus : 256);
+  const long g = 2L * device_cus();
   return (unsigned)(items < g ? (items > 0 ? items : 1) : g);
 }
 

@@ -17,6 +17,10 @@ extern thread_local ::moe_trace* tls_trace;
 void trace_before(hipStream_t s, const char* name);
 void trace_after(hipStream_t s);
 
+// Compute units that persistent launches size their grids for: the current
+// device's CU count, capped by the calling thread's moe_set_cu_budget.
+int device_cus();
+
 // Enqueue one kernel launch between trace events; evaluates to hipGetLastError().
 #define MOE_LAUNCH(name, stream, ...)   \
   (::moe::trace_before((stream), (name)), (__VA_ARGS__), ::moe::trace_after(stream), \
@@ -129,7 +133,7 @@ hipError_t launch_gemm_wgrad_up(int dt, const GroupInfo& g, const void* dZ, cons
 
 // ------------------------------------------------------------------ MXFP8
 #define MX_MAX_MB 8  // minibatches per macro batch in the MX path
-// MX wgrads: experts whose packed token range (all minibatches, each segment padded
+// MX wgrads: experts whose packed token range (their rows of all minibatches, padded
 // to 32) has at least this many bytes run on the 256 x 256 core
 constexpr int MX_WGRAD_HOT_BYTES = 256;
 
@@ -141,20 +145,50 @@ hipError_t launch_quant_rows(int dt, const void* src, const int32_t* gather,
 // Column quantisation of batch x [rows, cols] into batch x [cols, rows] (blocks along rows).
 hipError_t launch_quant_cols(int dt, const void* src, int batch, int rows, int cols, uint8_t* q,
                              uint8_t* sc, hipStream_t s);
-// Token quantisation of one minibatch's plan tiles into the transposed token axis
-// of the wgrads (dt 1: bf16 source, 0: fp32 source).  Expert e's rows of this
-// minibatch go to columns kpos[e] + kseg[e] + (row - offsets[e]), in blocks of 32
-// rows from the segment's first row (the last block zero-padded); blocks without a
-// row are not written.  kpad_total: the axis length (row pitch of q).
+// Token quantisation into the transposed token axis of the wgrads (dt 1: bf16
+// source, 0: fp32 source) over a tile list of 128-row tiles (expert, first row) of
+// a row space with expert offsets `offsets`.  Expert e's rows go to columns
+// kpos[e] + (kseg ? kseg[e] : 0) + (row - offsets[e]), in blocks of 32 rows from
+// its first row (the last block zero-padded); blocks without a row are not written.
+// Row r is read from src row gather ? gather[r] : r.  kpad_total: the axis length
+// (row pitch of q).
 hipError_t launch_quant_tokens(int dt, const void* src, const int32_t* gather, int ld,
                                const int32_t* tiles, const int32_t* n_tiles,
                                const int32_t* offsets, const int32_t* kpos,
                                const int32_t* kseg, int max_tiles, int cols, size_t kpad_total,
                                uint8_t* q, uint8_t* sc, hipStream_t s);
 
-// The wgrads' token axis over all minibatches: expert e owns columns
-// [kpos[e], kpos[e + 1]), its minibatch segments one after the other, each padded to
-// a multiple of 32 rows.
+// The minibatch plans of one macro batch (device pointers into the plan buffer).
+struct MbPlanViews {
+  int n_mb;
+  const int32_t* counts[MX_MAX_MB];
+  const int32_t* offsets[MX_MAX_MB];
+  const int32_t* tiles[MX_MAX_MB];
+  const int32_t* n_tiles[MX_MAX_MB];
+  const int32_t* src_token[MX_MAX_MB];
+};
+
+// The wgrads' token axis over all minibatches (device arrays in the workspace):
+// expert e's rows of the macro batch in token order are its global rows
+// [goff[e], goff[e + 1]) (minibatch m's segment from goff[e] + cum[m * E + e]) and
+// take the packed columns [kpos[e], kpos[e] + n_e), kpos advancing by n_e rounded
+// up to 32; gtiles / n_gtiles: (expert, first global row) per 128 global rows;
+// grow / gtok: per global row, its row in the per-minibatch arrays stored one
+// minibatch after the other (m * R_mb + r) and its token.
+struct MbAxis {
+  int32_t* counts_all;
+  int32_t* active;
+  int32_t* n_active;
+  int32_t* cum;     // [n_mb * E]
+  int32_t* kpos;    // [E + 1]
+  int32_t* goff;    // [E + 1]
+  int32_t* gtiles;  // [max_gtiles * 2]
+  int32_t* n_gtiles;
+  int32_t* grow;    // [T * k]
+  int32_t* gtok;    // [T * k]
+};
+
+// What the wgrad kernels read of the axis.
 struct MbPlans {
   int n_mb;
   const int32_t* kpos;       // [E + 1]
@@ -162,12 +196,9 @@ struct MbPlans {
   const int32_t* n_active;
 };
 
-// counts_all[e] = sum over minibatch plans of counts[e]; active / n_active list the
-// experts with counts_all > 0 in ascending order; kseg[m * E + e] = sum over m' < m of
-// pad32(counts_m'[e]) and kpos = exclusive prefix over e of sum_m pad32(counts_m[e]).
-hipError_t launch_mb_union(const int32_t* const* counts, int n_mb, int E, int32_t* counts_all,
-                           int32_t* active, int32_t* n_active, int32_t* kseg, int32_t* kpos,
-                           hipStream_t s);
+hipError_t launch_mb_union(const MbPlanViews& v, int E, const MbAxis& ax, hipStream_t s);
+hipError_t launch_mb_rows(const MbPlanViews& v, int E, int max_tiles, int R_mb, int T_mb,
+                          const MbAxis& ax, hipStream_t s);
 
 hipError_t launch_mx_up_swiglu(const GroupInfo& g, const uint8_t* X8, const uint8_t* Xs,
                                const uint8_t* wg8, const uint8_t* wgs, const uint8_t* wu8,

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const T* __restrict__ s
 // blocks of 32 rows from row0 (a multiple of 32 rows after the segment's first row,
 // so the blocks start at the segment's first row); the output is transposed into
 // the wgrads' token axis: q[c, kbase + j] for local row j with
-// kbase = kpos[e] + kseg[e] + (row0 - offsets[e]) (rows past row_end inside a block
+// kbase = kpos[e] + kseg[e] + (row0 - offsets[e]) (kseg NULL: 0; rows past row_end inside a block
 // are zero), scales s[c, kbase / 32 + j / 32].  Blocks without a row are not
 // written: those columns belong to the next segment.  src rows are pulled through
 // gather when given.  One workgroup per (tile, 64 columns): 16-byte row loads into
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
 #pragma unroll
   for (int i = 0; i < 32; ++i) v[i] = to_f32(tile[(32 * blk + i) * TROW + cc]);
   __syncthreads();  // the tile is now free for the codes
-  const size_t kbase = (size_t)kpos[e] + kseg[e] + (row0 - offsets[e]);
+  const size_t kbase = (size_t)kpos[e] + (kseg ? kseg[e] : 0) + (row0 - offsets[e]);
   if (has) {
     const int X = mx_scale_exp(v);
     uint4 lo, hi;

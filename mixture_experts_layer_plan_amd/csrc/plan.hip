@@ -27,8 +27,12 @@ namespace moe {
 
 constexpr int PLAN_WAVES = 4;  // wavefronts (chunks) per workgroup
 
-struct MbCounts {
+struct MbPlanPtrs {
   const int32_t* counts[MX_MAX_MB];
+  const int32_t* offsets[MX_MAX_MB];
+  const int32_t* tiles[MX_MAX_MB];
+  const int32_t* n_tiles[MX_MAX_MB];
+  const int32_t* src_token[MX_MAX_MB];
   int n_mb;
 };
 constexpr int PLAN_STEPS = PLAN_CHUNK / 64;
@@ -219,56 +223,119 @@ hipError_t launch_plan(const int32_t* topk_idx, int T, int k, int E, const PlanP
 
 namespace moe {
 
-// Union of the minibatch plans' expert lists and the wgrads' token-axis offsets
-// (one workgroup of 1024 threads; thread e owns expert e).
-__global__ __launch_bounds__(1024) void mb_union_kernel(MbCounts mc, int E,
+// The weight gradients' token axis over the minibatches of one macro batch (one
+// workgroup of 1024 threads; thread e owns expert e).  Expert e's rows of all
+// minibatches, in token order, are its global rows goff[e] .. goff[e + 1] - 1
+// (minibatch m's segment starts at goff[e] + cum[m * E + e]); on the packed token
+// axis they take the byte columns kpos[e] .. kpos[e] + n_e - 1, kpos advancing by
+// n_e rounded up to 32 (the MX blocks run from each expert's first row); gtiles lists
+// (expert, first global row) per 128 global rows of each expert.
+MOE_DEV int block_excl_scan(int v, int* s_wave, int& total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int c = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(c, o, 64);
+    if (lane >= o) c += u;
+  }
+  __syncthreads();  // s_wave free from a previous scan
+  if (lane == 63) s_wave[wv] = c;
+  __syncthreads();
+  int base = 0;
+  total = 0;
+  for (int i = 0; i < nw; ++i) {
+    if (i < wv) base += s_wave[i];
+    total += s_wave[i];
+  }
+  return base + c - v;
+}
+
+__global__ __launch_bounds__(1024) void mb_union_kernel(MbPlanPtrs mc, int E,
                                                         int32_t* __restrict__ counts_all,
                                                         int32_t* __restrict__ active,
                                                         int32_t* __restrict__ n_active,
-                                                        int32_t* __restrict__ kseg,
-                                                        int32_t* __restrict__ kpos) {
-  __shared__ int32_t s_wave[2][16];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int n = 0, len = 0;
+                                                        int32_t* __restrict__ cum,
+                                                        int32_t* __restrict__ kpos,
+                                                        int32_t* __restrict__ goff,
+                                                        int32_t* __restrict__ gtiles,
+                                                        int32_t* __restrict__ n_gtiles) {
+  __shared__ int s_wave[16];
+  const int tid = threadIdx.x;
+  int n = 0;
   if (tid < E)
     for (int m = 0; m < mc.n_mb; ++m) {
-      const int c = mc.counts[m][tid];
-      kseg[m * E + tid] = len;
-      n += c;
-      len += (c + 31) & ~31;
+      cum[m * E + tid] = n;
+      n += mc.counts[m][tid];
     }
-  const int act = n > 0 ? 1 : 0;
-  int c = act, p = len;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(c, o, 64), v = __shfl_up(p, o, 64);
-    if (lane >= o) { c += u; p += v; }
-  }
-  if (lane == 63) { s_wave[0][wv] = c; s_wave[1][wv] = p; }
-  __syncthreads();
-  int base = 0, pbase = 0;
-  for (int i = 0; i < wv; ++i) { base += s_wave[0][i]; pbase += s_wave[1][i]; }
-  const int excl = base + c - act;
+  const int act = n > 0 ? 1 : 0, ntile = (n + 127) / 128;
+  int tot_act, tot_k, tot_n, tot_t;
+  const int e_act = block_excl_scan(act, s_wave, tot_act);
+  const int e_k = block_excl_scan((n + 31) & ~31, s_wave, tot_k);
+  const int e_n = block_excl_scan(n, s_wave, tot_n);
+  const int e_t = block_excl_scan(ntile, s_wave, tot_t);
   if (tid < E) {
     counts_all[tid] = n;
-    if (act) active[excl] = tid;
-    kpos[tid] = pbase + p - len;
+    if (act) active[e_act] = tid;
+    kpos[tid] = e_k;
+    goff[tid] = e_n;
+    for (int i = 0; i < ntile; ++i) {
+      gtiles[2 * (e_t + i)] = tid;
+      gtiles[2 * (e_t + i) + 1] = e_n + 128 * i;
+    }
   }
-  if (tid == E - 1) {
-    n_active[0] = excl + act;
-    kpos[E] = pbase + p;
+  if (tid == 0) {
+    n_active[0] = tot_act;
+    kpos[E] = tot_k;
+    goff[E] = tot_n;
+    n_gtiles[0] = tot_t;
   }
 }
 
-hipError_t launch_mb_union(const int32_t* const* counts, int n_mb, int E, int32_t* counts_all,
-                           int32_t* active, int32_t* n_active, int32_t* kseg, int32_t* kpos,
-                           hipStream_t s) {
-  MbCounts mc;
-  mc.n_mb = n_mb;
-  for (int m = 0; m < MX_MAX_MB; ++m) mc.counts[m] = m < n_mb ? counts[m] : nullptr;
+// Global row p of a macro batch (see mb_union_kernel) of minibatch m's plan row r:
+// grow[p] = m * R_mb + r (rows of per-minibatch arrays stored one minibatch after
+// the other) and gtok[p] = m * T_mb + src_token_m[r] (its token).  One workgroup of
+// 128 threads per (plan tile, minibatch).
+__global__ __launch_bounds__(128) void mb_rows_kernel(MbPlanPtrs mc, int E, int R_mb, int T_mb,
+                                                      const int32_t* __restrict__ cum,
+                                                      const int32_t* __restrict__ goff,
+                                                      int32_t* __restrict__ grow,
+                                                      int32_t* __restrict__ gtok) {
+  const int m = blockIdx.y, t = blockIdx.x;
+  if (m >= mc.n_mb || t >= mc.n_tiles[m][0]) return;
+  const int e = mc.tiles[m][2 * t], row = mc.tiles[m][2 * t + 1] + (int)threadIdx.x;
+  const int32_t* off = mc.offsets[m];
+  if (row >= off[e + 1]) return;
+  const int p = goff[e] + cum[m * E + e] + (row - off[e]);
+  grow[p] = m * R_mb + row;
+  gtok[p] = m * T_mb + mc.src_token[m][row];
+}
+
+static MbPlanPtrs mb_ptrs(const MbPlanViews& v) {
+  MbPlanPtrs mc = {};
+  mc.n_mb = v.n_mb;
+  for (int m = 0; m < v.n_mb && m < MX_MAX_MB; ++m) {
+    mc.counts[m] = v.counts[m];
+    mc.offsets[m] = v.offsets[m];
+    mc.tiles[m] = v.tiles[m];
+    mc.n_tiles[m] = v.n_tiles[m];
+    mc.src_token[m] = v.src_token[m];
+  }
+  return mc;
+}
+
+hipError_t launch_mb_union(const MbPlanViews& v, int E, const MbAxis& ax, hipStream_t s) {
   return MOE_LAUNCH("mb_union", s,
-                    mb_union_kernel<<<1, 1024, 0, s>>>(mc, E, counts_all, active, n_active,
-                                                       kseg, kpos));
+                    mb_union_kernel<<<1, 1024, 0, s>>>(mb_ptrs(v), E, ax.counts_all, ax.active,
+                                                       ax.n_active, ax.cum, ax.kpos, ax.goff,
+                                                       ax.gtiles, ax.n_gtiles));
+}
+
+hipError_t launch_mb_rows(const MbPlanViews& v, int E, int max_tiles, int R_mb, int T_mb,
+                          const MbAxis& ax, hipStream_t s) {
+  if (max_tiles == 0 || v.n_mb == 0) return hipSuccess;
+  return MOE_LAUNCH("mb_rows", s,
+                    mb_rows_kernel<<<dim3(max_tiles, v.n_mb), 128, 0, s>>>(
+                        mb_ptrs(v), E, R_mb, T_mb, ax.cum, ax.goff, ax.grow, ax.gtok));
 }
 
 }  // namespace moe

@@ -128,6 +128,28 @@ def test_layer_bitwise_repeatable_and_buffer_independent():
     assert outs[0] == outs[1] == outs[2]
 
 
+@pytest.mark.parametrize("name", ["hot_wgrad_bf16", "skew_shared_bf16"])
+def test_layer_bitwise_independent_of_persistent_grid(name):
+    """Every output is bitwise the same whether the persistent kernels (the weight
+    gradients) run one workgroup per CU of the whole chip or far fewer: each output
+    element comes from one workgroup with a fixed K order."""
+    from mixture_experts_layer_plan_amd import binding
+    shape = SMALL[name]
+    say(f"determinism over persistent grid sizes: {name}")
+    inp = to_dev(make_inputs(shape, seed=2, device="cpu", with_dy=True))
+    outs = []
+    try:
+        for cus in (0, 8, 40, 128):
+            binding.moe_set_cu_budget(cus)
+            b = gpu_run(shape, inp)
+            outs.append(digest(b.y, b.dx, b.dw_gate, b.dw_up, b.dw_down, b.ds_gate, b.ds_up,
+                               b.ds_down, b.d_topk_w, b.d_logits))
+            del b
+    finally:
+        binding.moe_set_cu_budget(0)
+    assert len(set(outs)) == 1, outs
+
+
 # --------------------------------------------------------------- full sizes
 class ExpertCache:
     """fp64 host copies of single experts of a device weight stack, on demand."""

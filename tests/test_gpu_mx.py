@@ -226,15 +226,68 @@ def test_mx_experts_without_rows_get_zero_gradients():
         assert b.dw_gate[e].any() and b.dw_up[e].any() and b.dw_down[e].any(), e
 
 
-def test_mx_row_local_outputs_bitwise_independent_of_minibatch_size():
+def test_mx_outputs_bitwise_independent_of_minibatch_size():
+    """y, dx, d_topk_w (row-local) and the weight gradients (token blocks over each
+    expert's rows of the macro batch, one fixed K order) are bitwise the same for
+    every minibatch size, ragged last minibatch included."""
     shape, _ = SMALL_MX["skew_ring"]
-    say("mx minibatch-size invariance of y, dx, d_topk_w")
+    say("mx minibatch-size invariance of every output")
     inp = to_dev(make_inputs(shape, seed=4, device="cpu", with_dy=True))
     outs = []
-    for T_mb in (0, 256, 128):
+    for T_mb in (0, 256, 128, 96):
         b = gpu_mx(shape, inp, T_mb)
-        outs.append(digest(b.y, b.dx, b.d_topk_w))
-    assert outs[0] == outs[1] == outs[2]
+        outs.append(digest(b.y, b.dx, b.d_topk_w, b.dw_gate, b.dw_up, b.dw_down, b.ds_gate,
+                           b.ds_up, b.ds_down))
+    assert len(set(outs)) == 1, outs
+
+
+def test_mx_bitwise_independent_of_persistent_grid():
+    from mixture_experts_layer_plan_amd import binding
+    shape, T_mb = Shape(T=1024, H=512, I=256, E=12, k=2, I_shared=256, zipf_s=2.0,
+                        dtype="mxfp8"), 256
+    say("mx determinism over persistent grid sizes")
+    inp = to_dev(make_inputs(shape, seed=3, device="cpu", with_dy=True))
+    outs = []
+    try:
+        for cus in (0, 8, 72):
+            binding.moe_set_cu_budget(cus)
+            b = gpu_mx(shape, inp, T_mb)
+            outs.append(digest(b.y, b.dx, b.d_topk_w, b.dw_gate, b.dw_up, b.dw_down))
+            del b
+    finally:
+        binding.moe_set_cu_budget(0)
+    assert len(set(outs)) == 1, outs
+
+
+def test_mx_full_size_weight_gradients_independent_of_minibatch_size():
+    """At the MXFP8 workload's shape (T = 8192, H = 7168, I = 2048, E = 256, k = 8):
+    every output is bitwise the same for minibatches of 2048, 1024 and one minibatch
+    of all 8192 tokens (compared on the device)."""
+    from mixture_experts_layer_plan_amd import LayerBuffers, layer, run_layer
+    shape = CONFIGS["kimi_mxfp8_ring"]
+    say("mx full size: inputs on the device")
+    inp = make_inputs(shape, seed=1, device="cuda", with_dy=True)
+    ref = None
+    names = ("y", "dx", "d_topk_w", "dw_gate", "dw_up", "dw_down", "ds_gate", "ds_up", "ds_down")
+    wq = None
+    for T_mb in (2048, 1024, 0):
+        say(f"mx full size: T_minibatch = {T_mb}")
+        b = LayerBuffers(shape.T, shape.H, shape.I, shape.E, shape.k, shape.I_shared, "mxfp8",
+                         backward=True, T_minibatch=T_mb)
+        if wq is None:
+            layer.quantize_weights(b, inp)
+            wq = b.wq
+        else:
+            b.wq = wq
+        run_layer(b, inp, backward=True, quantize=False)
+        torch.cuda.synchronize()
+        if ref is None:
+            ref = {n: getattr(b, n) for n in names}
+        else:
+            for n in names:
+                assert torch.equal(getattr(b, n), ref[n]), (T_mb, n)
+        del b
+        torch.cuda.empty_cache()
 
 
 def test_mx_bitwise_repeatable():
