@@ -254,6 +254,24 @@ moe_status moe_forward_bf16(const moe_shape* shape, const void* plan, const void
                             const void* s_down, void* y, void* saved, void* ws,
                             size_t ws_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): moe_forward_bf16 with its workspace in a
+ * static device array of the library instead of a caller buffer.  It allocates
+ * nothing and calls no allocating routine; the caller passes inputs and outputs as
+ * for moe_forward_bf16 (y, saved).  The array holds MOE_NOALLOC_SCRATCH_BYTES per
+ * GPU, from the library's first use of a GPU until the process ends; shapes whose
+ * forward workspace, moe_workspace_bytes(shape, MOE_BF16, 0), is larger return
+ * MOE_E_WORKSPACE (at H = 7168, I = I_shared = 2048, k = 8: up to 404 tokens).
+ * Every call on one GPU uses that GPU's one array: calls that overlap on a GPU (on
+ * different streams, or from different threads without ordering) race.  Nothing
+ * in the array needs to start at zero: every workspace element the forward reads
+ * it has written earlier in the same call. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_forward_bf16_noalloc(const moe_shape* shape, const void* plan, const void* x,
+                                    const float* topk_w, const void* w_gate, const void* w_up,
+                                    const void* w_down, const void* s_gate, const void* s_up,
+                                    const void* s_down, void* y, void* saved, hipStream_t stream);
+
 /* Backward, the mirror of the forward (sebask.de, § Push oder Pull: reverse-combine
  * and reverse-dispatch; stamatios.com, § Outras características: router-weight
  * gradient fused into the SwiGLU backward):

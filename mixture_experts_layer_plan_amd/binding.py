@@ -79,6 +79,7 @@ _SIGS = {
     "moe_reverse_dispatch_bf16": (_I, [_S, _P, _P, _P, _P, _P]),
     "moe_forward_bf16": (_I, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "moe_forward_f32": (_I, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "moe_forward_bf16_noalloc": (_I, [_S] + [_P] * 12),
     "moe_backward_bf16": (_I, [_S] + [_P] * 20 + [_Z, _P]),
     "moe_backward_f32": (_I, [_S] + [_P] * 20 + [_Z, _P]),
     "moe_mx_weights_bytes": (_Z, [_S]),
@@ -253,6 +254,18 @@ def moe_forward_bf16(s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_d
                      ws, stream=None):
     _fwd("moe_forward_bf16", s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down, y,
          saved, ws, stream)
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_forward_bf16_noalloc(s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down, y,
+                             saved, stream=None):
+    nw, ns, nt = s.E * s.I * s.H, s.I_shared * s.H, s.T * s.H
+    _call("moe_forward_bf16_noalloc", ctypes.byref(s), _ptr(plan), _bf16(x, nt),
+          _f32(topk_w, s.T * s.k), _bf16(w_gate, nw), _bf16(w_up, nw), _bf16(w_down, nw),
+          _bf16(s_gate, ns), _bf16(s_up, ns), _bf16(s_down, ns), _bf16(y, nt), _ptr(saved),
+          _stream(stream))
 
 
 def moe_forward_f32(s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down, y, saved,

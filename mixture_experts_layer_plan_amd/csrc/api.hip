@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "internal.hpp"
@@ -713,6 +714,29 @@ moe_status backward_mx_impl(const moe_shape* s, const void* plan, const void* x,
   return MOE_OK;
 }
 
+// Workspace of moe_forward_bf16_noalloc: one static device array per GPU (each
+// device that loads the library holds its own copy until the process ends).  In
+// host code `scratch` names a host-side stand-in, not the device address: the
+// address comes from hipGetSymbolAddress, once per device with that device current.
+__device__ __attribute__((aligned(256))) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[MAX_DEVICES] = {};
+
+moe_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return MOE_E_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_E_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -937,6 +961,20 @@ moe_status moe_forward_bf16(const moe_shape* s, const void* plan, const void* x,
                             hipStream_t st) {
   return forward_impl(MOE_BF16, s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down, y,
                       saved, ws, ws_bytes, st);
+}
+
+moe_status moe_forward_bf16_noalloc(const moe_shape* s, const void* plan, const void* x,
+                                    const float* topk_w, const void* w_gate, const void* w_up,
+                                    const void* w_down, const void* s_gate, const void* s_up,
+                                    const void* s_down, void* y, void* saved, hipStream_t st) {
+  moe_status rc = check_shape(s, true);
+  if (rc != MOE_OK) return rc;
+  if (fwd_ws(s, MOE_BF16).total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_E_WORKSPACE;
+  void* ws = nullptr;
+  rc = scratch_of_current_device(&ws);
+  if (rc != MOE_OK) return rc;
+  return forward_impl(MOE_BF16, s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down, y,
+                      saved, ws, MOE_NOALLOC_SCRATCH_BYTES, st);
 }
 
 moe_status moe_forward_f32(const moe_shape* s, const void* plan, const float* x,
