@@ -66,12 +66,15 @@ def kernel_work(name, sh, counts_mb, es=2):
     Emx = len(mx_hot)
     Rmx = sum(union[e] for e in mx_hot)
 
-    def over_mb(f):
+    def over_mb(f, replayed=False):
+        # replayed: the launch runs once more in the backward for every minibatch but
+        # the last when the activations are replayed instead of kept
         b = fl = 0.0
-        for (Rm, Etm), tm in zip(mbs, Tm):
+        for m, ((Rm, Etm), tm) in enumerate(zip(mbs, Tm)):
             x, y = f(Rm, Etm, tm)
-            b += x
-            fl += y
+            n = 2 if replayed and sh.replay and m < n_mb - 1 else 1
+            b += n * x
+            fl += n * y
         return int(b), int(fl)
 
     w = {
@@ -112,7 +115,9 @@ def kernel_work(name, sh, counts_mb, es=2):
         # MXFP8 path (per minibatch unless noted)
         # x (forward) and dy (backward) gathered into the ring and quantised: each
         # source row read once, its k rows written as E4M3 codes with scales
-        "mx_quant_rows": lambda: over_mb(lambda Rm, Etm, tm: (2 * (tm * H * 2 + Rm * H * q + Rm * 4), 0)),
+        "mx_quant_rows": lambda: tuple(a + b for a, b in zip(
+            over_mb(lambda Rm, Etm, tm: (tm * H * 2 + Rm * H * q + Rm * 4, 0), replayed=True),
+            over_mb(lambda Rm, Etm, tm: (tm * H * 2 + Rm * H * q + Rm * 4, 0)))),
         # the wgrad operands of the macro batch, quantised along each expert's tokens:
         # dy and x (bf16 sources read once per token), g h and dZ (fp32 rows), the
         # row maps
@@ -120,7 +125,8 @@ def kernel_work(name, sh, counts_mb, es=2):
                                         + R * 2 * I * (4 + q) + 4 * R * 4), 0),
         "mb_rows": lambda: (R * 20, 0),
         "mx_gemm_up_swiglu": lambda: over_mb(lambda Rm, Etm, tm: (
-            Etm * 2 * I * H * q + Rm * H * q + Rm * 2 * I * 4 + Rm * I * q, 2 * Rm * H * 2 * I)),
+            Etm * 2 * I * H * q + Rm * H * q + Rm * 2 * I * 4 + Rm * I * q, 2 * Rm * H * 2 * I),
+            replayed=True),
         "mx_gemm_down": lambda: over_mb(lambda Rm, Etm, tm: (
             Etm * H * I * q + Rm * I * q + Rm * H * 2, 2 * Rm * I * H)),
         "mx_gemm_dgrad_down": lambda: over_mb(lambda Rm, Etm, tm: (
@@ -214,6 +220,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (counter calibration)")
+    ap.add_argument("--dump-launches", default=None,
+                    help="write the library's launch names of one timed step, in order, to this "
+                         "file (to name the kernels of a profiler trace)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -234,7 +243,8 @@ def main():
     log(f"[bench] generating {args.config} inputs on the device")
     inp = make_inputs(sh, seed=0, device="cuda", with_dy=sh.backward)
     b = LayerBuffers(sh.T, sh.H, sh.I, sh.E, sh.k, sh.I_shared, sh.dtype, backward=sh.backward,
-                     router_gemm=sh.router == "gemm", T_minibatch=sh.T_minibatch)
+                     router_gemm=sh.router == "gemm", T_minibatch=sh.T_minibatch,
+                     replay=sh.replay)
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -283,6 +293,10 @@ def main():
     ms_total = ev0.elapsed_time(ev1)
     recs = trace.records()
     trace.close()
+    if args.dump_launches:
+        per_step = len(recs) // max(args.steps, 1)
+        with open(args.dump_launches, "w") as f:
+            f.write("\n".join(n for n, _ in recs[:per_step]) + "\n")
     ms_per_step = ms_total / max(args.steps, 1)
     tokens_per_s = sh.T / (ms_per_step / 1e3)
 
@@ -340,7 +354,8 @@ def main():
     desc = (f"{args.config}: {sh.dtype} MoE layer {passes}, T={sh.T} H={sh.H} I={sh.I} E={sh.E} "
             f"top-{sh.k}" + (f", shared expert I={sh.I_shared}" if sh.I_shared else "")
             + (f", Zipf({sh.zipf_s}) routing" if sh.zipf_s else "")
-            + (f", minibatches of {sh.T_minibatch}" if sh.T_minibatch else ""))
+            + (f", minibatches of {sh.T_minibatch}" if sh.T_minibatch else "")
+            + (", activations of all but the last minibatch replayed" if sh.replay else ""))
     out = {
         "metric": metric, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),

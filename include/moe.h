@@ -76,7 +76,18 @@ typedef struct {
   int32_t T, H, I, E, k;
   int32_t I_shared;
   int32_t T_minibatch;
+  int32_t flags; /* MOE_REPLAY or 0; other bits: MOE_E_SHAPE */
 } moe_shape;
+
+/* MXFP8 calls with several minibatches: the forward keeps the pre-activations of
+ * the last minibatch only (the one still in the ring when the forward ends, which
+ * the backward, walking the minibatches in reverse, needs first) and the backward
+ * replays the dispatch and the up/gate GEMM of the others (stamatios.com, § Ring
+ * token buffers: a reverse ring in the forward keeps the activation replay of the
+ * backward small).  Outputs are bitwise the same as without it; moe_saved_bytes
+ * shrinks by a factor of n_minibatch for the routed experts.  No effect on the bf16
+ * and fp32 calls (one minibatch). */
+#define MOE_REPLAY 1
 
 /* Where each array of the schedule table sits inside the plan buffer (byte
  * offsets from its start; all 256-byte aligned).  With R = T*k:
@@ -317,8 +328,10 @@ moe_status moe_backward_f32(const moe_shape* shape, const void* plan, const floa
  * x and dy along H (quantised while they are gathered into the ring of minibatch
  * slots), h along I, dZ = (dA | dB) along 2I, the weights along H or I (both
  * orientations, from moe_quantize_weights_mxfp8), and the wgrad operands along
- * the tokens of each expert's segment in each minibatch (blocks of 32 rows from
- * the segment's first row, zero-padded).  Tokens run in minibatches of
+ * the tokens of each expert: its rows of the whole call in token order, in blocks
+ * of 32 from its first row (zero-padded), whatever the minibatch size, so that the
+ * weight gradients are bitwise the same for every T_minibatch (sebask.de,
+ * § Determinismus und MXFP8-Unterstützung).  Tokens run in minibatches of
  * shape->T_minibatch (at most 8 per call; 0 = one minibatch) through a ring of two
  * slots of T_minibatch * k dispatched rows (stamatios.com, § Ring token buffers
  * and § Granularidade do overlap); the plan must come from moe_plan with the same

@@ -32,7 +32,7 @@ class MoeError(RuntimeError):
 class moe_shape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("I_shared", ctypes.c_int32),
-                ("T_minibatch", ctypes.c_int32)]
+                ("T_minibatch", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 class moe_plan_layout(ctypes.Structure):
@@ -112,8 +112,12 @@ def exported_names() -> list[str]:
     return list(_SIGS)
 
 
-def shape(T, H, I, E, k, I_shared=0, T_minibatch=0) -> moe_shape:
-    return moe_shape(int(T), int(H), int(I), int(E), int(k), int(I_shared), int(T_minibatch))
+MOE_REPLAY = 1
+
+
+def shape(T, H, I, E, k, I_shared=0, T_minibatch=0, flags=0) -> moe_shape:
+    return moe_shape(int(T), int(H), int(I), int(E), int(k), int(I_shared), int(T_minibatch),
+                     int(flags))
 
 
 def _ptr(t, dtype=None, numel=None):

@@ -77,6 +77,7 @@ moe_status check_shape(const moe_shape* s, bool need_gemm_dims) {
     return MOE_E_SHAPE;
   if ((int64_t)s->T * s->k >= (int64_t)1 << 31) return MOE_E_SHAPE;
   if (s->H < 128 || s->H % 128) return MOE_E_SHAPE;
+  if (s->flags & ~MOE_REPLAY) return MOE_E_SHAPE;
   if (need_gemm_dims) {
     if (s->I < 128 || s->I % 128) return MOE_E_SHAPE;
     if (s->I_shared < 0 || s->I_shared % 128) return MOE_E_SHAPE;
@@ -422,15 +423,18 @@ MxWeights mx_weights_layout(const moe_shape* s) {
 }
 
 // Saved by the MX forward: Z fp32 of every minibatch (minibatch m's rows at
-// m * R_mb) and Zs fp32 [T, 2 Is].
+// m * R_mb; with MOE_REPLAY the last minibatch's only) and Zs fp32 [T, 2 Is].
 struct MxSaved {
   size_t Z, Zs, total;
 };
+bool mx_replay(const moe_shape* s) { return (s->flags & MOE_REPLAY) && n_minibatches(s) > 1; }
+
 MxSaved mx_saved_layout(const moe_shape* s) {
   const size_t R_mb = (size_t)minibatch_tokens(s) * s->k;
+  const size_t n_saved = mx_replay(s) ? 1 : (size_t)n_minibatches(s);
   Carve c;
   MxSaved L;
-  L.Z = c.take((size_t)n_minibatches(s) * R_mb * 2 * s->I * sizeof(float));
+  L.Z = c.take(n_saved * R_mb * 2 * s->I * sizeof(float));
   L.Zs = c.take((size_t)s->T * 2 * s->I_shared * sizeof(float));
   L.total = c.off;
   return L;
@@ -439,7 +443,7 @@ MxSaved mx_saved_layout(const moe_shape* s) {
 // Forward workspace: the ring of two minibatch slots of dispatched MX rows, the
 // quantised h, Y, and the shared expert's h and output of one minibatch.
 struct MxFwdWs {
-  size_t ring8[2], rings[2], hq, hs, Y, hs_sh, ys, total;
+  size_t ring8[2], rings[2], hq, hs, Y, hs_sh, ys, Zr, total;
 };
 MxFwdWs mx_fwd_ws(const moe_shape* s) {
   const size_t Tm = minibatch_tokens(s), R = Tm * s->k, H = s->H, I = s->I;
@@ -454,6 +458,8 @@ MxFwdWs mx_fwd_ws(const moe_shape* s) {
   L.Y = c.take(R * H * 2);
   L.hs_sh = c.take(Tm * s->I_shared * 2);
   L.ys = c.take(s->I_shared ? Tm * H * 2 : 0);
+  // with MOE_REPLAY: Z of the minibatches before the last (not kept)
+  L.Zr = c.take(mx_replay(s) ? R * 2 * I * sizeof(float) : 0);
   L.total = c.off;
   return L;
 }
@@ -468,6 +474,7 @@ struct MxBwdWs {
   size_t ring8[2], rings[2], dZ, dZ8, dZs, gh, dgp, dX;
   size_t dYuT8, dYuTs, ghT8, ghTs, dZT8, dZTs, XT8, XTs;
   size_t counts_all, active, n_active, cum, kpos, goff, gtiles, n_gtiles, grow, gtok;
+  size_t rX8, rXs, rZ, rhq, rhs;  // MOE_REPLAY: replayed dispatch, Z and (unused) h
   size_t dZs_sh, hs_sh, dxs, total;
   size_t Kp;
   int max_gtiles;
@@ -507,6 +514,12 @@ MxBwdWs mx_bwd_ws(const moe_shape* s) {
   L.n_gtiles = c.take(sizeof(int32_t));
   L.grow = c.take(sizeof(int32_t) * Rtot);
   L.gtok = c.take(sizeof(int32_t) * Rtot);
+  const size_t rp = mx_replay(s) ? 1 : 0;
+  L.rX8 = c.take(rp * R * H);
+  L.rXs = c.take(rp * R * H / 32);
+  L.rZ = c.take(rp * R * 2 * I * sizeof(float));
+  L.rhq = c.take(rp * R * I);
+  L.rhs = c.take(rp * R * I / 32);
   L.dZs_sh = c.take(T * 2 * s->I_shared * 2);
   L.hs_sh = c.take(T * s->I_shared * 2);
   L.dxs = c.take(s->I_shared ? T * H * 2 : 0);
@@ -560,7 +573,8 @@ moe_status forward_mx_impl(const moe_shape* s, const void* plan, const void* x,
     const bf16_t_host* xm = (const bf16_t_host*)x + (size_t)m * Tmb * H;
     uint8_t* X8 = at<uint8_t>(ws, W.ring8[m & 1]);
     uint8_t* Xs = at<uint8_t>(ws, W.rings[m & 1]);
-    float* Z = at<float>(saved, S.Z) + (size_t)m * Tmb * k * 2 * I;
+    float* Z = !mx_replay(s) ? at<float>(saved, S.Z) + (size_t)m * Tmb * k * 2 * I
+                             : (m == nmb - 1 ? at<float>(saved, S.Z) : at<float>(ws, W.Zr));
     uint8_t* hq = at<uint8_t>(ws, W.hq);
     uint8_t* hs = at<uint8_t>(ws, W.hs);
     void* Y = at<char>(ws, W.Y);
@@ -659,6 +673,21 @@ moe_status backward_mx_impl(const moe_shape* s, const void* plan, const void* x,
     uint8_t* dYu8 = at<uint8_t>(ws, W.ring8[m & 1]);
     uint8_t* dYus = at<uint8_t>(ws, W.rings[m & 1]);
     const float* Z = at<float>(saved, S.Z) + tok0 * k * 2 * I;
+    if (mx_replay(s)) {
+      if (m == nmb - 1) {
+        Z = at<float>(saved, S.Z);
+      } else {
+        // replay this minibatch's dispatch and up/gate GEMM for its pre-activations
+        const bf16_t_host* xm = (const bf16_t_host*)x + tok0 * H;
+        uint8_t* X8 = at<uint8_t>(ws, W.rX8);
+        uint8_t* Xs = at<uint8_t>(ws, W.rXs);
+        float* rZ = at<float>(ws, W.rZ);
+        MOE_TRY(launch_quant_rows(1, xm, v.src_token, v.offsets + s->E, R_m, H, X8, Xs, st));
+        MOE_TRY(launch_mx_up_swiglu(g, X8, Xs, q + Q.wg8, q + Q.wgs, q + Q.wu8, q + Q.wus, H, I,
+                                    rZ, at<uint8_t>(ws, W.rhq), at<uint8_t>(ws, W.rhs), st));
+        Z = rZ;
+      }
+    }
     float* dZ = at<float>(ws, W.dZ) + tok0 * k * 2 * I;
     uint8_t* dZ8 = at<uint8_t>(ws, W.dZ8);
     uint8_t* dZsc = at<uint8_t>(ws, W.dZs);

@@ -40,6 +40,7 @@ class Shape:
     router: str = "logits"       # "logits": logits are an input; "gemm": logits = x W_r^T
     zipf_s: float = 0.0
     backward: bool = True
+    replay: bool = False         # MXFP8: keep the last minibatch's activations only
 
     @property
     def R(self) -> int:
@@ -58,6 +59,10 @@ CONFIGS: dict[str, Shape] = {
     # MXFP8 forward+backward over 4 minibatches of 2048 tokens through a ring buffer
     "kimi_mxfp8_ring": Shape(T=8192, H=7168, I=2048, E=256, k=8, I_shared=2048,
                              T_minibatch=2048, dtype="mxfp8", zipf_s=1.2),
+    # the same with the activations of all but the last minibatch replayed in the
+    # backward instead of kept
+    "kimi_mxfp8_ring_replay": Shape(T=8192, H=7168, I=2048, E=256, k=8, I_shared=2048,
+                                    T_minibatch=2048, dtype="mxfp8", zipf_s=1.2, replay=True),
     # one GPU's share of an expert-parallel layer: 4 local experts, every token on all
     # four (k = E), so each expert gets exactly 4096 rows; bf16 forward+backward
     "ep_share_bf16": Shape(T=4096, H=7168, I=2048, E=4, k=4),

@@ -128,3 +128,17 @@ def test_router_gemm_needs_fp32_buffers():
     from mixture_experts_layer_plan_amd import LayerBuffers
     with pytest.raises(ValueError):
         LayerBuffers(8, 256, 128, 4, 2, dtype="bf16", router_gemm=True, device="cpu")
+
+
+def test_replay_flag_shrinks_saved_activations(lib):
+    kept = s_(T=300, T_minibatch=128)
+    rep = s_(T=300, T_minibatch=128, flags=B.MOE_REPLAY)
+    R_mb, I = 128 * 2, 128
+    assert B.moe_saved_bytes(kept, B.MOE_MXFP8) - B.moe_saved_bytes(rep, B.MOE_MXFP8) == \
+        2 * R_mb * 2 * I * 4                    # two of three minibatches' Z not kept
+    assert B.moe_workspace_bytes(rep, B.MOE_MXFP8, True) > B.moe_workspace_bytes(kept, B.MOE_MXFP8, True)
+    # one minibatch: nothing to replay
+    assert B.moe_saved_bytes(s_(T=300, flags=B.MOE_REPLAY), B.MOE_MXFP8) == \
+        B.moe_saved_bytes(s_(T=300), B.MOE_MXFP8)
+    assert B.moe_saved_bytes(s_(flags=2), B.MOE_MXFP8) == 0   # unknown flag bits
+    assert rc_route(s_(flags=4)) == 2

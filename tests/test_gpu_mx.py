@@ -241,6 +241,30 @@ def test_mx_outputs_bitwise_independent_of_minibatch_size():
     assert len(set(outs)) == 1, outs
 
 
+@pytest.mark.parametrize("name", ["ring3_ragged", "skew_ring"])
+def test_mx_replayed_activations_bitwise_equal_kept(name):
+    """With MOE_REPLAY the forward keeps the last minibatch's pre-activations only and
+    the backward replays the dispatch and up/gate GEMM of the others: every output
+    is bitwise what the layer gives with all pre-activations kept."""
+    from mixture_experts_layer_plan_amd import LayerBuffers, run_layer
+    shape, T_mb = SMALL_MX[name]
+    say(f"mx replay vs kept activations: {name}")
+    inp = to_dev(make_inputs(shape, seed=8, device="cpu", with_dy=True))
+    names = ("y", "dx", "d_topk_w", "d_logits", "dw_gate", "dw_up", "dw_down", "ds_gate",
+             "ds_up", "ds_down")
+    outs, saved = [], []
+    for replay in (False, True):
+        b = LayerBuffers(shape.T, shape.H, shape.I, shape.E, shape.k, shape.I_shared, "mxfp8",
+                         backward=True, T_minibatch=T_mb, replay=replay)
+        run_layer(b, inp, backward=True)
+        torch.cuda.synchronize()
+        outs.append(digest(*(getattr(b, n) for n in names)))
+        saved.append(b.saved.numel())
+    assert outs[0] == outs[1]
+    n_mb = -(-shape.T // T_mb)
+    assert saved[1] < saved[0] and n_mb > 1
+
+
 def test_mx_bitwise_independent_of_persistent_grid():
     from mixture_experts_layer_plan_amd import binding
     shape, T_mb = Shape(T=1024, H=512, I=256, E=12, k=2, I_shared=256, zipf_s=2.0,
@@ -262,7 +286,8 @@ def test_mx_bitwise_independent_of_persistent_grid():
 def test_mx_full_size_weight_gradients_independent_of_minibatch_size():
     """At the MXFP8 workload's shape (T = 8192, H = 7168, I = 2048, E = 256, k = 8):
     every output is bitwise the same for minibatches of 2048, 1024 and one minibatch
-    of all 8192 tokens (compared on the device)."""
+    of all 8192 tokens, and with the activations of minibatches of 2048 replayed
+    (compared on the device)."""
     from mixture_experts_layer_plan_amd import LayerBuffers, layer, run_layer
     shape = CONFIGS["kimi_mxfp8_ring"]
     say("mx full size: inputs on the device")
@@ -270,10 +295,10 @@ def test_mx_full_size_weight_gradients_independent_of_minibatch_size():
     ref = None
     names = ("y", "dx", "d_topk_w", "dw_gate", "dw_up", "dw_down", "ds_gate", "ds_up", "ds_down")
     wq = None
-    for T_mb in (2048, 1024, 0):
-        say(f"mx full size: T_minibatch = {T_mb}")
+    for T_mb, replay in ((2048, False), (1024, False), (0, False), (2048, True)):
+        say(f"mx full size: T_minibatch = {T_mb}, replay = {replay}")
         b = LayerBuffers(shape.T, shape.H, shape.I, shape.E, shape.k, shape.I_shared, "mxfp8",
-                         backward=True, T_minibatch=T_mb)
+                         backward=True, T_minibatch=T_mb, replay=replay)
         if wq is None:
             layer.quantize_weights(b, inp)
             wq = b.wq
