@@ -95,9 +95,10 @@ struct DmaKG {
   MOE_DEV void row(int s, size_t row_elem_offset) {
     off[s] = (uint32_t)(row_elem_offset * 2) + 16u * kmaj_chunk();
   }
+  template <int S0 = 0, int S1 = 4>
   MOE_DEV void issue(int kt, char* st) const {
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = S0; s < S1; ++s)
       if (s < n) dma16(base + (size_t)kt * 128 + off[s], kmaj_dst(st, s));
   }
 };
@@ -115,9 +116,10 @@ struct DmaKS {
     step = (uint32_t)(64 * ld_elems * 2);
     valid = (rows + 63) / 64;
   }
+  template <int S0 = 0, int S1 = 4>
   MOE_DEV void issue(int kt, char* st) const {
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = S0; s < S1; ++s)
       dma16(base + (size_t)kt * 128 + off + (s < valid ? s * step : 0u), kmaj_dst(st, s));
   }
 };
@@ -151,9 +153,10 @@ struct DmaMN {
     sstep = (uint32_t)(16 * ld_elems * 2);
     kstep = (long)(64 * ld_elems * 2);
   }
+  template <int S0 = 0, int S1 = 4>
   MOE_DEV void issue(int kt, char* st) const {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) dma16(base + kt * kstep + off + s * sstep, mn_dst(st, s));
+    for (int s = S0; s < S1; ++s) dma16(base + kt * kstep + off + s * sstep, mn_dst(st, s));
   }
 };
 
@@ -205,12 +208,14 @@ struct Acc {
 // Operand adaptors: issue(kt, stage) and frag(stage, block, ks, kt).
 struct OpKG {  // K-major gathered rows
   DmaKG d;
-  MOE_DEV void issue(int kt, char* st) const { d.issue(kt, st); }
+  template <int S0 = 0, int S1 = 4>
+  MOE_DEV void issue(int kt, char* st) const { d.template issue<S0, S1>(kt, st); }
   MOE_DEV bf16x8_t frag(const char* st, int r0, int ks, int) const { return frag_k(st, r0, ks); }
 };
 struct OpK {  // K-major strided rows
   DmaKS d;
-  MOE_DEV void issue(int kt, char* st) const { d.issue(kt, st); }
+  template <int S0 = 0, int S1 = 4>
+  MOE_DEV void issue(int kt, char* st) const { d.template issue<S0, S1>(kt, st); }
   MOE_DEV bf16x8_t frag(const char* st, int r0, int ks, int) const { return frag_k(st, r0, ks); }
 };
 // GEMM1 weights: B-tile row 64 s + m (instruction s) is W_g (m < 32) or W_u
@@ -229,24 +234,27 @@ struct OpUpW {
     off = (uint32_t)((m & 31) * H * 2) + 16u * kmaj_chunk();
     step = (uint32_t)(32 * H * 2);
   }
+  template <int S0 = 0, int S1 = 4>
   MOE_DEV void issue(int kt, char* st) const {
     const char* b = up ? u : g;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) dma16(b + (size_t)kt * 128 + off + s * step, kmaj_dst(st, s));
+    for (int s = S0; s < S1; ++s) dma16(b + (size_t)kt * 128 + off + s * step, kmaj_dst(st, s));
   }
   MOE_DEV bf16x8_t frag(const char* st, int r0, int ks, int) const { return frag_k(st, r0, ks); }
 };
 struct OpMN {  // MN-major, full K tiles
   DmaMN d;
-  MOE_DEV void issue(int kt, char* st) const { d.issue(kt, st); }
+  template <int S0 = 0, int S1 = 4>
+  MOE_DEV void issue(int kt, char* st) const { d.template issue<S0, S1>(kt, st); }
   MOE_DEV bf16x8_t frag(const char* st, int c0, int ks, int) const { return frag_mn(st, c0, ks); }
 };
 struct OpMNCat {  // dgrad-up weights: K rows < I from W_g[e], the rest from W_u[e]
   DmaMN g, u;
   int kI;  // K tiles in W_g
+  template <int S0 = 0, int S1 = 4>
   MOE_DEV void issue(int kt, char* st) const {
-    if (kt < kI) g.issue(kt, st);
-    else u.issue(kt - kI, st);
+    if (kt < kI) g.template issue<S0, S1>(kt, st);
+    else u.template issue<S0, S1>(kt - kI, st);
   }
   MOE_DEV bf16x8_t frag(const char* st, int c0, int ks, int) const { return frag_mn(st, c0, ks); }
 };
@@ -273,14 +281,15 @@ struct OpMNSeg {
     off = (uint32_t)(r0 * ldb) + col;
     sstep = (uint32_t)(16 * ldb);
   }
+  template <int S0 = 0, int S1 = 4>
   MOE_DEV void issue(int kt, char* st) const {
     const char* b = base + (size_t)kt * 64 * ldb;
     if (64 * kt + 64 <= n) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) dma16(b + off + s * sstep, mn_dst(st, s));
+      for (int s = S0; s < S1; ++s) dma16(b + off + s * sstep, mn_dst(st, s));
     } else {  // the segment's last K tile
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = S0; s < S1; ++s) {
         const char* src = 64 * kt + r0 + 16 * s < n ? b + off + s * sstep
                                                       : (const char*)g_zero_row512 + col;
         dma16(src, mn_dst(st, s));
@@ -350,7 +359,12 @@ MOE_DEV void mma(Acc& acc, const bf16x8_t (&a)[4], const bf16x8_t (&b)[2], int m
         acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc.c[i][j], 0, 0, 0);
 }
 
-template <class OA, class OB>
+// LATE_B: the next K tile's B loads are issued after the first step's MFMAs instead
+// of together with its A loads (the row-grouped kernels: measured on MI355X at
+// T = 4096, Zipf(1.2), dgrad-up 3.12 -> 2.97 ms, GEMM2 1.76 -> 1.67 ms, GEMM1
+// unchanged, the step 18.64 -> 18.45 ms; the wgrads, whose K loops are short and
+// read both operands MN-major, measured 3 % slower with it)
+template <bool LATE_B = false, class OA, class OB>
 MOE_DEV void main_loop(char* lds, const OA& A, const OB& B, int nk, int ma, int mb, Acc& acc) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -372,11 +386,15 @@ MOE_DEV void main_loop(char* lds, const OA& A, const OB& B, int nk, int ma, int 
     // the last iteration reloads its own K tile into the idle stage (never read)
     const int kn = kt + 1 < nk ? kt + 1 : kt;
     A.issue(kn, nxt);
-    B.issue(kn, nxt + STAGE);
+    if (!LATE_B) B.issue(kn, nxt + STAGE);
     __builtin_amdgcn_sched_barrier(0);
     load_frags(A, B, cur, kt, 1, wm, wn, ma, mb, a1, b1);
     mma(acc, a0, b0, ma, mb);
     __builtin_amdgcn_sched_barrier(0);
+    if (LATE_B) {
+      B.issue(kn, nxt + STAGE);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     load_frags(A, B, cur, kt, 2, wm, wn, ma, mb, a0, b0);
     mma(acc, a1, b1, ma, mb);
     __builtin_amdgcn_sched_barrier(0);
@@ -467,7 +485,7 @@ MOE_DEV void main_loop_rows(char* lds, const OA& A, const OB& B, int nk, int row
                             Acc& acc) {
   if (rows <= 64) main_loop_small<64, 4>(lds, A, B, nk, ma, mb, acc);
   else if (rows <= 128) main_loop_small<128, 3>(lds, A, B, nk, ma, mb, acc);
-  else main_loop(lds, A, B, nk, ma, mb, acc);
+  else main_loop<true>(lds, A, B, nk, ma, mb, acc);
 }
 
 // Output position of register v of block (i, j): row 128 wm + 32 i + 8 (v >> 2) +
