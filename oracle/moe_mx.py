@@ -241,11 +241,14 @@ def layer_backward_mx(cache: dict, dy, keep_operands: bool = False) -> dict:
     return out
 
 
-def token_mx(x_t, idx_t, w_t, dy_t, qc: _QuantCache, shared=None, backward=True):
+def token_mx(x_t, idx_t, w_t, dy_t, qc: _QuantCache, shared=None, backward=True, rows_out=None):
     """One token straight from the MX definition (no plan, no minibatch): returns
     (y_t, dx_t, dg_t); dx_t and dg_t are None without ``backward``.  The
     row-local quantisations (x and dy along H, h along I, dA and dB along I) do not
-    depend on the minibatch, so these equal the planned results row for row."""
+    depend on the minibatch, so these equal the planned results row for row.  With a
+    list ``rows_out``, each of the token's k rows appends its unquantised values
+    (dict: e, g, A, B, h and, with ``backward``, dhp, dA, dB) and the quantised token
+    rows xq, dyq."""
     v = q_act("x", _f64(x_t)[None])[0]
     g = _f64(w_t)
     y = np.zeros_like(v)
@@ -257,6 +260,7 @@ def token_mx(x_t, idx_t, w_t, dy_t, qc: _QuantCache, shared=None, backward=True)
         B = qc.get("u_H", e) @ v
         h = silu(A) * B
         y += g[j] * (qc.get("d_I", e) @ q_act("h", h[None])[0])
+        row = {"e": int(e), "g": g[j], "A": A, "B": B, "h": h, "xq": v, "dyq": d}
         if backward:
             dhp = qc.get("d_H", e).T @ d
             dg[j] = float(dhp @ h)
@@ -265,6 +269,9 @@ def token_mx(x_t, idx_t, w_t, dy_t, qc: _QuantCache, shared=None, backward=True)
             dB = dh * silu(A)
             dx += (qc.get("g_I", e).T @ q_act("dA", dA[None])[0]
                    + qc.get("u_I", e).T @ q_act("dB", dB[None])[0])
+            row.update(dhp=dhp, dA=dA, dB=dB)
+        if rows_out is not None:
+            rows_out.append(row)
     if shared is not None:
         Sg, Su, Sd = (_f64(a) for a in shared)
         xf = _f64(x_t)
@@ -275,3 +282,62 @@ def token_mx(x_t, idx_t, w_t, dy_t, qc: _QuantCache, shared=None, backward=True)
             dh = Sd.T @ _f64(dy_t)
             dx += Sg.T @ (dh * B * dsilu(A)) + Su.T @ (dh * silu(A))
     return y, dx, dg
+
+
+def _weight_rows(kind, W, rows):
+    """Rows ``rows`` of quantisation point ``kind`` of weight W (blocks along each row
+    need only those rows)."""
+    W = _f64(W)
+    return q_rows(W[rows]) if WEIGHT_AXIS[kind][1] == "rows" else q_cols(W)[rows]
+
+
+def _weight_cols(kind, W, cols):
+    """Columns ``cols`` of quantisation point ``kind`` of weight W (blocks along each
+    column need only those columns)."""
+    W = _f64(W)
+    return q_cols(W[:, cols]) if WEIGHT_AXIS[kind][1] == "cols" else q_rows(W)[:, cols]
+
+
+def expert_weight_grad_slices_mx(x, dy, topk_idx, topk_w, e, cols, w_gate_e, w_up_e, w_down_e,
+                                 keep_operands=False):
+    """Slices of one expert's MX weight gradients straight from the definition:
+    (dW_g[cols, :], dW_u[cols, :], dW_d[:, cols]) for the intermediate indices
+    ``cols``.  The expert's rows are its pairs (t, j) with topk_idx[t, j] = e in
+    ascending t (its rows of every minibatch, in order); the token-axis operands are
+    blocked along those rows from the first (module docstring).  Everything used is
+    column- or row-local: the rows ``cols`` of W_g, W_u quantised along H, the columns
+    ``cols`` of W_d quantised along H, x and dy rows quantised along H.  Cost is
+    linear in the expert's rows.  With ``keep_operands`` also returns the quantised
+    (a, b) pairs of the three products (dW = a^T b) for the one-flip allowance."""
+    xf, dyf = _f64(x), _f64(dy)
+    idx = np.asarray(topk_idx)
+    g_all = _f64(topk_w)
+    ts, js = np.nonzero(idx == e)            # row-major: ascending t, then j
+    order = np.lexsort((js, ts))
+    ts, js = ts[order], js[order]
+    H = xf.shape[1]
+    cols = np.asarray(cols)
+    if len(ts) == 0:
+        z = np.zeros((len(cols), H))
+        return (z, z.copy(), np.zeros((H, len(cols)))) + (({},) if keep_operands else ())
+    Xq = q_act("x", xf[ts])                  # along H, per row
+    Dq = q_act("dy", dyf[ts])
+    g = g_all[ts, js][:, None]
+    Wg_c = _weight_rows("g_H", w_gate_e, cols)   # [c, H]
+    Wu_c = _weight_rows("u_H", w_up_e, cols)
+    Wd_c = _weight_cols("d_H", w_down_e, cols)   # [H, c]
+    A = Xq @ Wg_c.T
+    B = Xq @ Wu_c.T
+    h = silu(A) * B
+    dhp = Dq @ Wd_c
+    dh = g * dhp
+    dA = dh * B * dsilu(A)
+    dB = dh * silu(A)
+    Xt = q_act("wgrad", xf[ts])
+    ops = ((q_act("wgrad", dA), Xt), (q_act("wgrad", dB), Xt),
+           (q_act("wgrad", dyf[ts]), q_act("wgrad", g * h)))
+    dWg, dWu = ops[0][0].T @ ops[0][1], ops[1][0].T @ ops[1][1]
+    dWd = ops[2][0].T @ ops[2][1]
+    if keep_operands:
+        return dWg, dWu, dWd, {"dw_gate": [ops[0]], "dw_up": [ops[1]], "dw_down": [ops[2]]}
+    return dWg, dWu, dWd

@@ -52,15 +52,25 @@ def e4m3_encode(v) -> np.ndarray:
     return (code | (sign.astype(np.int64) << 7)).astype(np.uint8)
 
 
-def e4m3_decode(code) -> np.ndarray:
-    c = np.asarray(code, dtype=np.int64)
+def _e4m3_value(c: np.ndarray) -> np.ndarray:
+    """Value of each code from its bit fields (NaN codes give NaN)."""
+    c = np.asarray(c, dtype=np.int64)
     s = np.where(c & 0x80, -1.0, 1.0)
     E = (c >> 3) & 0xF
     m = (c & 0x7).astype(np.float64)
-    if np.any((E == 15) & (m == 7)):
-        raise ValueError("NaN code")
     val = np.where(E == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(E - 7.0))
-    return s * val
+    return np.where((E == 15) & (m == 7), np.nan, s * val)
+
+
+# the 256 code values, looked up by code (the same bit-field rule, evaluated once)
+_E4M3_TABLE = _e4m3_value(np.arange(256))
+
+
+def e4m3_decode(code) -> np.ndarray:
+    v = _E4M3_TABLE[np.asarray(code, dtype=np.uint8)]
+    if np.isnan(v).any():
+        raise ValueError("NaN code")
+    return v
 
 
 def _blocks(a: np.ndarray, axis: int):

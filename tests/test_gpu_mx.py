@@ -324,7 +324,25 @@ def test_mx_bitwise_repeatable():
     assert d[0] == d[1] == d[2]
 
 
+def _warm(qc, experts, kinds=("g_H", "u_H", "d_I", "d_H", "g_I", "u_I")):
+    """Quantise the sampled experts' weights in threads (numpy releases the GIL in its
+    array operations), each orientation once."""
+    import concurrent.futures as cf
+    import os
+    jobs = [(k, e) for e in sorted(experts) for k in kinds]
+    with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4)) as ex:
+        list(ex.map(lambda j: qc.get(*j), jobs))
+
+
 def test_mx_full_size_sampled():
+    """The MXFP8 workload at full size (T = 8192 in minibatches of 2048, H = 7168,
+    I = 2048, E = 256, k = 8, Zipf(1.2)): y, dx, d_topk_w and d_logits of six tokens
+    (one from each minibatch and two more; chosen among the tokens whose experts are
+    the most frequent ones, which keeps the oracle's weight quantisation bounded),
+    element by element against the oracle's per-token MX definition; and column
+    slices of the weight gradients of the expert with the most rows, a median one, one
+    with a single row and one without rows."""
+    from tolerance import mx_token_allowances
     name = "kimi_mxfp8_ring"
     shape = CONFIGS[name]
     say(f"{name}: inputs on the device")
@@ -334,17 +352,50 @@ def test_mx_full_size_sampled():
     L = np_(inp["logits"])
     idx, w = oracle.route(L, shape.k)
     np.testing.assert_array_equal(np_(b.topk_idx), idx)
+    counts = np.bincount(idx.ravel(), minlength=shape.E)
+    hot = set(np.argsort(-counts, kind="stable")[:16].tolist())
+    overlap = lambda t: sum(int(e) in hot for e in idx[t])  # noqa: E731
+    toks = []
+    for m in range(shape.T // shape.T_minibatch):
+        sl = range(m * shape.T_minibatch, (m + 1) * shape.T_minibatch)
+        toks.append(max(sl, key=lambda t: (overlap(t), -t)))
+    for t in sorted(range(shape.T), key=lambda t: (-overlap(t), -t)):
+        if len(toks) == 6:
+            break
+        if t not in toks:
+            toks.append(t)
     qc = moe_mx._QuantCache(inp["w_gate"], inp["w_up"], inp["w_down"])
     sh = shared_of(inp)
-    toks = [5, shape.T - 3]
-    say(f"{name}: oracle on tokens {toks}")
-    y_ref, dx_ref, dg_ref = [], [], []
+    experts = set(int(e) for t in toks for e in idx[t])
+    say(f"{name}: oracle weights of {len(experts)} experts for tokens {toks}")
+    _warm(qc, experts)
+    y_g, dx_g, dg_g, dl_g = (np_(b.y.double()), np_(b.dx.double()), np_(b.d_topk_w),
+                             np_(b.d_logits))
     for t in toks:
+        say(f"{name}: token {t}")
+        rows = []
         y_t, dx_t, dg_t = moe_mx.token_mx(inp["x"][t], idx[t], w[t], inp["dy"][t], qc, shared=sh,
-                                          backward=(t == toks[0]))
-        y_ref.append(y_t)
-        dx_ref.append(dx_t)
-        dg_ref.append(dg_t)
-    check(np_(b.y.double())[toks], np.stack(y_ref), "mxfp8", "y (sampled)")
-    check(np_(b.dx.double())[toks[0]], dx_ref[0], "mxfp8", "dx (sampled)")
-    check(np_(b.d_topk_w)[toks[0]], dg_ref[0], "mxfp8", "d_topk_w (sampled)")
+                                          rows_out=rows)
+        y_al, dx_al = mx_token_allowances(rows, qc)
+        check(y_g[t], y_t, "mxfp8", f"y[{t}]", allowance=y_al)
+        check(dx_g[t], dx_t, "mxfp8", f"dx[{t}]", allowance=dx_al)
+        check(dg_g[t], dg_t, "mxfp8", f"d_topk_w[{t}]")
+        dl_t = oracle.route_backward(idx[t:t + 1], w[t:t + 1], dg_t[None], shape.E)[0]
+        check(dl_g[t], dl_t, "mxfp8", f"d_logits[{t}]")
+    # weight-gradient slices of four experts
+    pos = np.nonzero(counts)[0]
+    chosen = {"most rows": int(np.argmax(counts)),
+              "median": int(pos[np.argsort(counts[pos], kind="stable")[len(pos) // 2]]),
+              "one row": int(pos[np.argmin(counts[pos])]),
+              "no rows": int(np.nonzero(counts == 0)[0][0])}
+    cols = [0, 777, shape.I - 1]
+    for what, e in chosen.items():
+        say(f"{name}: weight-gradient slices of expert {e} ({what}, {counts[e]} rows)")
+        dWg, dWu, dWd, ops = moe_mx.expert_weight_grad_slices_mx(
+            inp["x"], inp["dy"], idx, w, e, cols, inp["w_gate"][e], inp["w_up"][e],
+            inp["w_down"][e], keep_operands=True)
+        for n, ref, got in (("dw_gate", dWg, b.dw_gate[e][cols]), ("dw_up", dWu, b.dw_up[e][cols]),
+                            ("dw_down", dWd, b.dw_down[e][:, cols])):
+            allow = one_flip_allowance(ops[n]) if ops else None
+            check(np_(got.double()), ref, "mxfp8", f"{n}[{e}] ({what})", allowance=allow)
+    assert counts[chosen["one row"]] == 1 or counts[pos].min() > 1

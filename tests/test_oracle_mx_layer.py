@@ -285,3 +285,35 @@ def test_dgrad_up_weight_pin_fails_when_swapped(monkeypatch, swap):
     _, g = run_mx(d, 1, 0)
     _, ge = _exact(d)
     assert _worst(g["dx"], ge["dx"], 0) > 0.5
+
+
+@pytest.mark.parametrize("T_mb", [0, 24])
+def test_expert_weight_grad_slices_mx_equal_the_full_backward(T_mb):
+    rng = np.random.default_rng(9)
+    d = rand_layer(rng, 72, 64, 96, 5, shared=False)
+    c, g = run_mx(d, 2, T_mb)
+    cols = [0, 17, 95]
+    for e in range(5):
+        dWg, dWu, dWd = moe_mx.expert_weight_grad_slices_mx(
+            d["x"], d["dy"], c["topk_idx"], c["topk_w"], e, cols, d["w_gate"][e], d["w_up"][e],
+            d["w_down"][e])
+        np.testing.assert_allclose(dWg, g["dw_gate"][e][cols], rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(dWu, g["dw_up"][e][cols], rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(dWd, g["dw_down"][e][:, cols], rtol=1e-11, atol=1e-13)
+
+
+def test_token_rows_out_match_the_planned_rows():
+    rng = np.random.default_rng(10)
+    d = rand_layer(rng, 40, 64, 64, 4, shared=False)
+    c, g = run_mx(d, 2, 0)
+    g2 = moe_mx.layer_backward_mx(c, d["dy"], keep_operands=True)
+    plan = c["minibatches"][0]["plan"]
+    t = 7
+    rows = []
+    moe_mx.token_mx(d["x"][t], c["topk_idx"][t], c["topk_w"][t], d["dy"][t], c["qcache"],
+                    rows_out=rows)
+    for j, row in enumerate(rows):
+        r = plan["pos"][t, j]
+        assert row["e"] == c["topk_idx"][t, j]
+        np.testing.assert_allclose(row["h"], c["minibatches"][0]["h"][r], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(row["dA"], g2["row_values"][0]["dA"][r], rtol=1e-12, atol=1e-14)

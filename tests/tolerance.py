@@ -167,6 +167,21 @@ def mx_layer_allowances(inp_x, inp_dy, c, g, E):
     return y_al, dx_al
 
 
+def mx_token_allowances(rows, qc):
+    """The y and dx allowances of one token from its rows (``token_mx(...,
+    rows_out=rows)``) and the oracle's quantised weights ``qc``."""
+    y_al = dx_al = 0.0
+    for row in rows:
+        e = row["e"]
+        one = lambda k: np.asarray(row[k])[None]  # noqa: E731
+        sp = mx_row_spreads(one("xq"), one("A"), one("B"), one("h"), qc.get("g_H", e),
+                            qc.get("u_H", e), one("dyq"), qc.get("d_H", e), one("dhp"),
+                            np.array([row["g"]]))
+        y_al = y_al + abs(row["g"]) * (sp["h"] @ np.abs(qc.get("d_I", e)).T)[0]
+        dx_al = dx_al + (sp["dA"] @ np.abs(qc.get("g_I", e)) + sp["dB"] @ np.abs(qc.get("u_I", e)))[0]
+    return y_al, dx_al
+
+
 def check(got, ref, kind="bf16", what="", allowance=None):
     g, r = f64(got), f64(ref)
     assert g.shape == r.shape, f"{what}: shape {g.shape} vs {r.shape}"
