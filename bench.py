@@ -93,6 +93,10 @@ def kernel_work(name, sh, counts_mb, es=2):
         "gemm_up_swiglu": lambda: (Et * 2 * I * H * es + R * H * es + R * 2 * I * 4 + R * I * es,
                                    2 * R * H * 2 * I),
         "gemm_down": lambda: (Et * H * I * es + R * I * es + R * H * es, 2 * R * I * H),
+        "gemm_forward_fused": lambda: tuple(a + b for a, b in zip(
+            kernel_work("gemm_up_swiglu", sh, counts_mb, es),
+            kernel_work("gemm_down", sh, counts_mb, es))),
+        "fused_zero": lambda: (0, 0),
         "gemm_dgrad_down": lambda: (Et * H * I * es + R * H * es + R * 2 * I * 4 + R * 3 * I * es
                                     + R * (I // 128) * 4, 2 * R * H * I),
         # the wgrads also store the zero gradients of the E - Et experts without rows
@@ -244,7 +248,7 @@ def main():
     inp = make_inputs(sh, seed=0, device="cuda", with_dy=sh.backward)
     b = LayerBuffers(sh.T, sh.H, sh.I, sh.E, sh.k, sh.I_shared, sh.dtype, backward=sh.backward,
                      router_gemm=sh.router == "gemm", T_minibatch=sh.T_minibatch,
-                     replay=sh.replay)
+                     replay=sh.replay, fused_forward=sh.fused_forward)
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -355,7 +359,8 @@ def main():
             f"top-{sh.k}" + (f", shared expert I={sh.I_shared}" if sh.I_shared else "")
             + (f", Zipf({sh.zipf_s}) routing" if sh.zipf_s else "")
             + (f", minibatches of {sh.T_minibatch}" if sh.T_minibatch else "")
-            + (", activations of all but the last minibatch replayed" if sh.replay else ""))
+            + (", activations of all but the last minibatch replayed" if sh.replay else "")
+            + (", up/gate and down GEMMs in one persistent launch" if sh.fused_forward else ""))
     out = {
         "metric": metric, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),

@@ -76,7 +76,7 @@ typedef struct {
   int32_t T, H, I, E, k;
   int32_t I_shared;
   int32_t T_minibatch;
-  int32_t flags; /* MOE_REPLAY or 0; other bits: MOE_E_SHAPE */
+  int32_t flags; /* MOE_REPLAY | MOE_FUSED_FORWARD or 0; other bits: MOE_E_SHAPE */
 } moe_shape;
 
 /* MXFP8 calls with several minibatches: the forward keeps the pre-activations of
@@ -89,6 +89,16 @@ typedef struct {
  * and fp32 calls (one minibatch). */
 #define MOE_REPLAY 1
 
+/* bf16 forward: the up/gate GEMM with SwiGLU and the down GEMM of the routed experts
+ * run as one persistent kernel, each down-GEMM tile starting as soon as the
+ * up/gate tiles of its rows have signalled through a device counter (stamatios.com,
+ * § Granularidade do overlap and § Outras características: one kernel whose units
+ * signal each other through counters).  Outputs are bitwise the same as without it.
+ * A tile gives up waiting after about two seconds, which can only happen when other
+ * work keeps the GPU's compute units from the kernel that long; bit 1 (value 2) of
+ * the plan's err_flag is then set and y is not valid. */
+#define MOE_FUSED_FORWARD 2
+
 /* Where each array of the schedule table sits inside the plan buffer (byte
  * offsets from its start; all 256-byte aligned).  With R = T*k:
  *   counts    int32 [E]      rows routed to each expert
@@ -99,7 +109,8 @@ typedef struct {
  *   tiles     int32 [max_tiles, 2]  (expert, first row) per tile_m rows of each
  *                            expert, experts in id order; n_tiles entries valid
  *   n_tiles   int32 [1]
- *   err_flag  int32 [1]      1 if some expert id was outside [0, E), else 0
+ *   err_flag  int32 [1]      bit 0: some expert id was outside [0, E); bit 1: a
+ *                            MOE_FUSED_FORWARD wait gave up (see there)
  *   active    int32 [E]      ids of the experts with rows, ascending; n_active valid
  *   n_active  int32 [1]
  *   tile_first int32 [E+1]   index of each expert's first entry in `tiles`

@@ -113,6 +113,7 @@ def exported_names() -> list[str]:
 
 
 MOE_REPLAY = 1
+MOE_FUSED_FORWARD = 2
 
 
 def shape(T, H, I, E, k, I_shared=0, T_minibatch=0, flags=0) -> moe_shape:

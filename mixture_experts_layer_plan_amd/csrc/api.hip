@@ -77,7 +77,7 @@ moe_status check_shape(const moe_shape* s, bool need_gemm_dims) {
     return MOE_E_SHAPE;
   if ((int64_t)s->T * s->k >= (int64_t)1 << 31) return MOE_E_SHAPE;
   if (s->H < 128 || s->H % 128) return MOE_E_SHAPE;
-  if (s->flags & ~MOE_REPLAY) return MOE_E_SHAPE;
+  if (s->flags & ~(MOE_REPLAY | MOE_FUSED_FORWARD)) return MOE_E_SHAPE;
   if (need_gemm_dims) {
     if (s->I < 128 || s->I % 128) return MOE_E_SHAPE;
     if (s->I_shared < 0 || s->I_shared % 128) return MOE_E_SHAPE;
@@ -209,9 +209,10 @@ SavedLayout saved_layout(const moe_shape* s, moe_dtype) {
   return L;
 }
 
-// forward workspace: h [R, I], Y [R, H], hs [T, Is], ys [T, H]
+// forward workspace: h [R, I], Y [R, H], hs [T, Is], ys [T, H], and the row-tile
+// counters of the fused forward
 struct FwdWs {
-  size_t h, Y, hs, ys, total;
+  size_t h, Y, hs, ys, ready, total;
 };
 FwdWs fwd_ws(const moe_shape* s, moe_dtype dt) {
   const size_t R = (size_t)s->T * s->k, es = esize(dt), T = s->T;
@@ -221,6 +222,8 @@ FwdWs fwd_ws(const moe_shape* s, moe_dtype dt) {
   L.Y = c.take(R * s->H * es);
   L.hs = c.take(T * s->I_shared * es);
   L.ys = c.take(s->I_shared ? T * s->H * es : 0);
+  L.ready = c.take((s->flags & MOE_FUSED_FORWARD)
+                       ? sizeof(int32_t) * (plan_layout(s).max_wtiles + 8) : 0);
   L.total = c.off;
   return L;
 }
@@ -294,8 +297,17 @@ moe_status forward_impl(moe_dtype dt, const moe_shape* s, const void* plan, cons
   void* Z = at<char>(saved, S.Z);
   void* h = at<char>(ws, W.h);
   void* Y = at<char>(ws, W.Y);
-  MOE_TRY(launch_gemm_up_swiglu(d, g, x, wg, wu, s->H, s->I, Z, h, st));
-  MOE_TRY(launch_gemm_down(d, g, h, wd, s->H, s->I, Y, st));
+  hipError_t fe = hipErrorNotSupported;
+  if (d && (s->flags & MOE_FUSED_FORWARD)) {
+    const moe_plan_layout P = plan_layout(s);
+    fe = launch_big_forward_fused(g, x, wg, wu, wd, s->H, s->I, Z, h, Y, at<int32_t>(ws, W.ready),
+                                  (int32_t*)((char*)const_cast<void*>(plan) + P.err_flag), st);
+    if (fe != hipSuccess && fe != hipErrorNotSupported) return MOE_E_HIP;
+  }
+  if (fe == hipErrorNotSupported) {
+    MOE_TRY(launch_gemm_up_swiglu(d, g, x, wg, wu, s->H, s->I, Z, h, st));
+    MOE_TRY(launch_gemm_down(d, g, h, wd, s->H, s->I, Y, st));
+  }
   void* ys = nullptr;
   if (s->I_shared) {
     const GroupInfo gs = dense(s->T);

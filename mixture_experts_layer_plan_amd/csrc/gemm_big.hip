@@ -58,9 +58,13 @@ constexpr int LDS_ROWS = 163840; // the row-grouped kernels: also the small-tile
 typedef __attribute__((address_space(3))) void* lds_vptr;
 typedef const __attribute__((address_space(1))) void* gbl_vptr;
 
+// AUX: cache policy of the load (0; or 16 = sc1, coherent at device scope: reads
+// data that another XCD wrote through, not a stale line of this XCD's L2)
+template <int AUX = 0>
 MOE_DEV void dma16(const char* src, char* dst) {
-  __builtin_amdgcn_global_load_lds((gbl_vptr)src, (lds_vptr)dst, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((gbl_vptr)src, (lds_vptr)dst, 16, 0, AUX);
 }
+constexpr int CPOL_DEVICE = 16;
 
 MOE_DEV int wave() { return threadIdx.x >> 6; }
 MOE_DEV int lane() { return threadIdx.x & 63; }
@@ -84,7 +88,8 @@ MOE_DEV char* kmaj_dst(char* st, int s) { return st + (8 * s + wave()) * 1024; }
 // whose 64 rows all lie past the tile's `rows` are not issued: those LDS rows keep
 // stale data and feed only output rows that are neither multiplied (blocks_a) nor
 // stored.
-struct DmaKG {
+template <int AUX = 0>
+struct DmaKGT {
   const char* base;
   uint32_t off[4];  // byte offset of this lane's row for instruction s, chunk included
   int n;            // instructions issued
@@ -99,9 +104,10 @@ struct DmaKG {
   MOE_DEV void issue(int kt, char* st) const {
 #pragma unroll
     for (int s = S0; s < S1; ++s)
-      if (s < n) dma16(base + (size_t)kt * 128 + off[s], kmaj_dst(st, s));
+      if (s < n) dma16<AUX>(base + (size_t)kt * 128 + off[s], kmaj_dst(st, s));
   }
 };
+using DmaKG = DmaKGT<0>;
 
 // Rows at a fixed stride (weights): row r at base + r * ld; rows past `rows` read
 // row 0 (only whole 64-row groups can lie past the operand, as rows % 64 == 0).
@@ -206,12 +212,14 @@ struct Acc {
 };
 
 // Operand adaptors: issue(kt, stage) and frag(stage, block, ks, kt).
-struct OpKG {  // K-major gathered rows
-  DmaKG d;
+template <int AUX = 0>
+struct OpKGT {  // K-major gathered rows
+  DmaKGT<AUX> d;
   template <int S0 = 0, int S1 = 4>
   MOE_DEV void issue(int kt, char* st) const { d.template issue<S0, S1>(kt, st); }
   MOE_DEV bf16x8_t frag(const char* st, int r0, int ks, int) const { return frag_k(st, r0, ks); }
 };
+using OpKG = OpKGT<0>;
 struct OpK {  // K-major strided rows
   DmaKS d;
   template <int S0 = 0, int S1 = 4>
@@ -503,6 +511,7 @@ MOE_DEV int blocks_b(int cols) { return min(2, max(0, (cols - 64 * (wave() & 3) 
 // ------------------------------------------------------------ tile decode
 struct Tile {
   int e, row0, row_end;
+  int mt;  // index of the row tile in the plan's wide-tile list (dense: the tile)
 };
 
 // Rows-grouped launches: a 1-D grid over (256-row tile, column tile) pairs in the
@@ -522,10 +531,10 @@ struct Tile {
 // pairs).
 constexpr int XCD_BLOCK = 16;
 template <bool BLOCKS>
-MOE_DEV bool row_tile(const GroupInfo& g, int nt_count, Tile& t, int& nt) {
+MOE_DEV bool row_tile_at(const GroupInfo& g, int nt_count, int id, Tile& t, int& nt) {
   const int n_row_tiles = g.wtiles ? g.n_wtiles[0] : (g.dense_rows + TILE - 1) / TILE;
   const int total = n_row_tiles * nt_count;
-  int L = blockIdx.x;
+  int L = id;
   if (BLOCKS) {
     const int x = L % N_XCD, q = L / N_XCD;
     L = ((q / XCD_BLOCK) * N_XCD + x) * XCD_BLOCK + q % XCD_BLOCK;
@@ -533,6 +542,7 @@ MOE_DEV bool row_tile(const GroupInfo& g, int nt_count, Tile& t, int& nt) {
   if (L >= total) return false;
   int mt;
   group_rows(g.wtiles, g.offsets, g.dense_rows, TILE, nt_count, 4, L, mt, nt);
+  t.mt = mt;
   if (g.wtiles) {
     t.e = g.wtiles[2 * mt];
     t.row0 = g.wtiles[2 * mt + 1];
@@ -545,6 +555,11 @@ MOE_DEV bool row_tile(const GroupInfo& g, int nt_count, Tile& t, int& nt) {
   return true;
 }
 
+template <bool BLOCKS>
+MOE_DEV bool row_tile(const GroupInfo& g, int nt_count, Tile& t, int& nt) {
+  return row_tile_at<BLOCKS>(g, nt_count, blockIdx.x, t, nt);
+}
+
 MOE_DEV int row_of_tile(const Tile& t, int r) {  // clamp rows past the tile's end
   return t.row0 + r < t.row_end ? t.row0 + r : t.row0;
 }
@@ -555,15 +570,12 @@ MOE_DEV int row_of_tile(const Tile& t, int r) {  // clamp rows past the tile's e
 // the W_u[e] row of the same i, so gate and up of one (row, i) are the same
 // register of blocks 0 and 1 of one lane and the SwiGLU is formed in registers.
 // Z (fp32) keeps the pre-activations for the backward; h = silu(A) B rounds once.
-__global__ __launch_bounds__(NTH, 1) void k_up_swiglu(GroupInfo g, const bf16_t* __restrict__ x,
-                                                      const bf16_t* __restrict__ wg,
-                                                      const bf16_t* __restrict__ wu, int H, int I,
-                                                      float* __restrict__ Z,
-                                                      bf16_t* __restrict__ hout) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_ROWS];
-  Tile t;
-  int nt;
-  if (!row_tile<true>(g, I / 128, t, nt)) return;
+// COHERENT_H: h is stored through to device scope (for a consumer on another XCD)
+template <bool COHERENT_H = false>
+MOE_DEV void up_swiglu_tile(char* lds, const GroupInfo& g, const Tile& t, int nt,
+                            const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg,
+                            const bf16_t* __restrict__ wu, int H, int I, float* __restrict__ Z,
+                            bf16_t* __restrict__ hout) {
   const size_t wofs = (size_t)t.e * I * H;
   OpKG A;
   OpUpW B;
@@ -588,23 +600,37 @@ __global__ __launch_bounds__(NTH, 1) void k_up_swiglu(GroupInfo g, const bf16_t*
         // Z is read back only by the backward: non-temporal (GEMM1 2.91 -> 2.87 ms)
         __builtin_nontemporal_store(a, zr + i);
         __builtin_nontemporal_store(b, zr + I + i);
-        hout[(size_t)r * I + i] = f32_to_bf16(silu_f(a) * b);
+        const bf16_t hv = f32_to_bf16(silu_f(a) * b);
+        if (COHERENT_H)
+          __hip_atomic_store((uint16_t*)(hout + (size_t)r * I + i), __builtin_bit_cast(uint16_t, hv),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          hout[(size_t)r * I + i] = hv;
       }
     }
+}
+
+__global__ __launch_bounds__(NTH, 1) void k_up_swiglu(GroupInfo g, const bf16_t* __restrict__ x,
+                                                      const bf16_t* __restrict__ wg,
+                                                      const bf16_t* __restrict__ wu, int H, int I,
+                                                      float* __restrict__ Z,
+                                                      bf16_t* __restrict__ hout) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_ROWS];
+  Tile t;
+  int nt;
+  if (!row_tile<true>(g, I / 128, t, nt)) return;
+  up_swiglu_tile(lds, g, t, nt, x, wg, wu, H, I, Z, hout);
 }
 
 // GEMM2: Y[r, n] = sum_i h[r, i] W_d[e][n, i] (grouped and the dense shared expert;
 // against the 128 x 128 kernel: 1.86 -> 1.81 ms at the skewed E = 256 workload,
 // 0.65 -> 0.55 ms at four experts of 4096 rows)
-__global__ __launch_bounds__(NTH, 1) void k_down(GroupInfo g, const bf16_t* __restrict__ h,
-                                                 const bf16_t* __restrict__ wd, int H, int I,
-                                                 bf16_t* __restrict__ Y) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_ROWS];
-  Tile t;
-  int nt;
-  if (!row_tile<false>(g, (H + TILE - 1) / TILE, t, nt)) return;
+// AUX: cache policy of the h loads
+template <int AUX = 0>
+MOE_DEV void down_tile(char* lds, const Tile& t, int nt, const bf16_t* __restrict__ h,
+                       const bf16_t* __restrict__ wd, int H, int I, bf16_t* __restrict__ Y) {
   const int n0 = nt * TILE;
-  OpKG A;
+  OpKGT<AUX> A;
   OpK B;
   A.d.set(h, t.row_end - t.row0);
 #pragma unroll
@@ -625,6 +651,101 @@ __global__ __launch_bounds__(NTH, 1) void k_down(GroupInfo g, const bf16_t* __re
           if (r < t.row_end) Y[(size_t)r * H + n] = f32_to_bf16(acc.c[bi][bj][v]);
         }
     }
+}
+
+__global__ __launch_bounds__(NTH, 1) void k_down(GroupInfo g, const bf16_t* __restrict__ h,
+                                                 const bf16_t* __restrict__ wd, int H, int I,
+                                                 bf16_t* __restrict__ Y) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_ROWS];
+  Tile t;
+  int nt;
+  if (!row_tile<false>(g, (H + TILE - 1) / TILE, t, nt)) return;
+  down_tile(lds, t, nt, h, wd, H, I, Y);
+}
+
+// ----------------------------------------------- forward GEMMs in one launch
+// GEMM1 + SwiGLU and GEMM2 of the routed experts as one persistent kernel, the
+// producer / consumer form of the pages' megakernel on one GPU (stamatios.com,
+// "Cursor abre código de megakernel MoE para GPUs NVL72", § Granularidade do overlap:
+// units signal each other through local counters; § Outras características: one
+// kernel).  The work items are the GEMM1 pairs (in the order and XCD dealing of
+// k_up_swiglu) followed by the GEMM2 pairs (those of k_down), item q on XCD q mod 8
+// as in the separate launches; the workgroups of one XCD (workgroup b runs on XCD
+// b mod 8) take that XCD's items in order from a counter, so that work balances
+// as it does when the dispatcher hands out a launch's workgroups.  A GEMM1 pair
+// stores h with device-coherent stores (written through to the device's coherence
+// point, not left in its XCD's L2), waits for them, and adds one to ready[row
+// tile]; a GEMM2 pair waits until its row tile's counter has all I / 128 column
+// tiles and then reads h with device-coherent loads (no stale line of its own
+// XCD's L2; measured on MI355X against an acquire / release pair, which invalidates
+// and writes back the whole L2: 5.08 -> 4.96 ms before the queues).  Each XCD's
+// queue hands out all its GEMM1 items before any GEMM2 item and GEMM1 items never
+// wait, so every wait ends once the workgroups holding the producers run.  A wait gives up after about two seconds (err bit 2:
+// possible only if other work keeps CUs from this grid that long); the pair then
+// reads whatever h holds.  The arithmetic of every tile is that of the two kernels.
+struct FusedFwd {
+  GroupInfo g;
+  const bf16_t* x;
+  const bf16_t* wg;
+  const bf16_t* wu;
+  const bf16_t* wd;
+  int H, I;
+  float* Z;
+  bf16_t* h;
+  bf16_t* Y;
+  int32_t* ready;   // [max_wtiles], zero at launch
+  int32_t* next;    // [8] per-XCD item counters, zero at launch
+  int32_t* err;
+  int n1, n2;       // item counts of the two phases (virtual grids of the kernels)
+};
+
+constexpr int FUSED_SPIN_LIMIT = 1 << 20;  // waits of ~4096 cycles each
+
+__global__ __launch_bounds__(NTH, 1) void k_forward_fused(FusedFwd p) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_ROWS];
+  int* s_item = (int*)lds;  // LDS is free between items
+  const int nt1 = p.I / 128, nt2 = (p.H + TILE - 1) / TILE, x = blockIdx.x % N_XCD;
+  for (;;) {
+    // next item of this XCD's queue (items x, x + 8, ... in order)
+    if (threadIdx.x == 0)
+      *s_item = __hip_atomic_fetch_add(p.next + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int q = *s_item * N_XCD + x;
+    __syncthreads();  // read by every thread before the tile overwrites the LDS
+    if (q >= p.n1 + p.n2) break;
+    Tile t;
+    int nt;
+    if (q < p.n1) {
+      if (!row_tile_at<true>(p.g, nt1, q, t, nt)) continue;
+      up_swiglu_tile<true>(lds, p.g, t, nt, p.x, p.wg, p.wu, p.H, p.I, p.Z, p.h);
+      // every lane's h stores have reached device scope, then one count for the
+      // workgroup
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(p.ready + t.mt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      if (!row_tile_at<false>(p.g, nt2, q - p.n1, t, nt)) continue;
+      if (threadIdx.x == 0) {
+        int spins = 0;
+        while (__hip_atomic_load(p.ready + t.mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+               nt1) {
+          if (++spins > FUSED_SPIN_LIMIT) {
+            __hip_atomic_fetch_or(p.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(64);
+        }
+      }
+      __syncthreads();
+      down_tile<CPOL_DEVICE>(lds, t, nt, p.h, p.wd, p.H, p.I, p.Y);
+    }
+  }
+}
+
+__global__ void zero_i32_kernel(int32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
 }
 
 // dgrad-up: dX[r, n] = sum_{k < 2I} dZ[r, k] Wcat[k, n], Wcat = [W_g[e]; W_u[e]]
@@ -1012,6 +1133,38 @@ hipError_t launch_big_up_swiglu(const GroupInfo& g, const void* x, const void* w
                     big::k_up_swiglu<<<big_row_grid(ty * (I / 128)), big::NTH, 0, s>>>(
                         g, (const bf16_t*)x, (const bf16_t*)wg, (const bf16_t*)wu, H, I,
                         (float*)Z, (bf16_t*)h));
+}
+
+// GEMM1 + SwiGLU and GEMM2 in one persistent launch (k_forward_fused); `ready` holds
+// max_wtiles + 8 int32 counters (zeroed here by a small kernel), err the plan's err
+// flag.
+hipError_t launch_big_forward_fused(const GroupInfo& g, const void* x, const void* wg,
+                                    const void* wu, const void* wd, int H, int I, void* Z, void* h,
+                                    void* Y, int32_t* ready, int32_t* err, hipStream_t s) {
+  if (!g.wtiles || g.max_wtiles == 0) return hipErrorNotSupported;
+  const int n_cnt = g.max_wtiles + N_XCD;  // ready counters, then the queue counters
+  hipError_t e = MOE_LAUNCH("fused_zero", s,
+                            big::zero_i32_kernel<<<(n_cnt + 255) / 256, 256, 0, s>>>(ready, n_cnt));
+  if (e != hipSuccess) return e;
+  big::FusedFwd p;
+  p.g = g;
+  p.x = (const bf16_t*)x;
+  p.wg = (const bf16_t*)wg;
+  p.wu = (const bf16_t*)wu;
+  p.wd = (const bf16_t*)wd;
+  p.H = H;
+  p.I = I;
+  p.Z = (float*)Z;
+  p.h = (bf16_t*)h;
+  p.Y = (bf16_t*)Y;
+  p.ready = ready;
+  p.next = ready + g.max_wtiles;
+  p.err = err;
+  p.n1 = (int)big_row_grid((unsigned)g.max_wtiles * (I / 128));
+  p.n2 = g.max_wtiles * ((H + big::TILE - 1) / big::TILE);
+  const int cus = device_cus();
+  const unsigned grid = (unsigned)(cus >= N_XCD ? cus - cus % N_XCD : N_XCD);
+  return MOE_LAUNCH("gemm_forward_fused", s, big::k_forward_fused<<<grid, big::NTH, 0, s>>>(p));
 }
 
 hipError_t launch_big_down(const GroupInfo& g, const void* h, const void* wd, int H, int I,

@@ -100,6 +100,13 @@ hipError_t launch_big_up_swiglu(const GroupInfo& g, const void* x, const void* w
                                 int H, int I, void* Z, void* h, hipStream_t s);
 hipError_t launch_big_down(const GroupInfo& g, const void* h, const void* wd, int H, int I,
                            void* Y, hipStream_t s);
+// GEMM1 + SwiGLU and GEMM2 of the routed experts in one persistent launch with
+// device-counter hand-off between them (ready: max_wtiles + 8 int32 of workspace; err:
+// the plan's err flag, bit 2 set if a wait gave up); hipErrorNotSupported without
+// the plan's wide-tile list
+hipError_t launch_big_forward_fused(const GroupInfo& g, const void* x, const void* wg,
+                                    const void* wu, const void* wd, int H, int I, void* Z, void* h,
+                                    void* Y, int32_t* ready, int32_t* err, hipStream_t s);
 hipError_t launch_big_dgrad_up(const GroupInfo& g, const void* dZ, const void* wg, const void* wu,
                                int H, int I, void* dX, hipStream_t s);
 // bf16 wgrads of the experts with >= hot_rows rows on the large tiles;

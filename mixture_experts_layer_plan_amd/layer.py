@@ -15,7 +15,8 @@ from . import binding as B
 
 class LayerBuffers:
     def __init__(self, T, H, I, E, k, I_shared=0, dtype="bf16", backward=True,
-                 router_gemm=False, device="cuda", T_minibatch=0, replay=False):
+                 router_gemm=False, device="cuda", T_minibatch=0, replay=False,
+                 fused_forward=False):
         if dtype not in ("bf16", "f32", "mxfp8"):
             raise ValueError(f"unsupported dtype {dtype}")
         if router_gemm and dtype != "f32":
@@ -23,7 +24,8 @@ class LayerBuffers:
             raise ValueError("router_gemm needs dtype 'f32'")
         self.dtype = dtype
         self.dt = B.DTYPES[dtype]
-        self.s = B.shape(T, H, I, E, k, I_shared, T_minibatch, B.MOE_REPLAY if replay else 0)
+        flags = (B.MOE_REPLAY if replay else 0) | (B.MOE_FUSED_FORWARD if fused_forward else 0)
+        self.s = B.shape(T, H, I, E, k, I_shared, T_minibatch, flags)
         tdt = torch.float32 if dtype == "f32" else torch.bfloat16
         dev = torch.device(device)
         u8 = dict(dtype=torch.uint8, device=dev)

@@ -41,6 +41,7 @@ class Shape:
     zipf_s: float = 0.0
     backward: bool = True
     replay: bool = False         # MXFP8: keep the last minibatch's activations only
+    fused_forward: bool = False  # bf16: up/gate and down GEMMs in one launch
 
     @property
     def R(self) -> int:
@@ -56,6 +57,9 @@ CONFIGS: dict[str, Shape] = {
     "kimi_bf16_fwd": Shape(T=2048, H=7168, I=2048, E=256, k=8, zipf_s=1.1, backward=False),
     # bf16 forward+backward with a shared expert, Zipf(1.2) skew
     "kimi_bf16_fwdbwd": Shape(T=4096, H=7168, I=2048, E=256, k=8, I_shared=2048, zipf_s=1.2),
+    # the same with the forward's two expert GEMMs in one persistent launch
+    "kimi_bf16_fwdbwd_fused": Shape(T=4096, H=7168, I=2048, E=256, k=8, I_shared=2048,
+                                    zipf_s=1.2, fused_forward=True),
     # MXFP8 forward+backward over 4 minibatches of 2048 tokens through a ring buffer
     "kimi_mxfp8_ring": Shape(T=8192, H=7168, I=2048, E=256, k=8, I_shared=2048,
                              T_minibatch=2048, dtype="mxfp8", zipf_s=1.2),

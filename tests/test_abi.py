@@ -140,5 +140,5 @@ def test_replay_flag_shrinks_saved_activations(lib):
     # one minibatch: nothing to replay
     assert B.moe_saved_bytes(s_(T=300, flags=B.MOE_REPLAY), B.MOE_MXFP8) == \
         B.moe_saved_bytes(s_(T=300), B.MOE_MXFP8)
-    assert B.moe_saved_bytes(s_(flags=2), B.MOE_MXFP8) == 0   # unknown flag bits
-    assert rc_route(s_(flags=4)) == 2
+    assert B.moe_saved_bytes(s_(flags=4), B.MOE_MXFP8) == 0   # unknown flag bits
+    assert rc_route(s_(flags=8)) == 2

@@ -150,6 +150,47 @@ def test_layer_bitwise_independent_of_persistent_grid(name):
     assert len(set(outs)) == 1, outs
 
 
+@pytest.mark.parametrize("name", ["hot_wgrad_bf16", "skew_shared_bf16", "ragged_bf16",
+                                  "hot_expert_bf16"])
+def test_fused_forward_bitwise_equal_separate_launches(name):
+    """MOE_FUSED_FORWARD (the two expert GEMMs in one persistent launch with counter
+    hand-off) gives bitwise the outputs of the two launches, backward included (the
+    saved pre-activations are the same), and leaves the plan's err flag at 0."""
+    from mixture_experts_layer_plan_amd import LayerBuffers, run_layer
+    shape = SMALL[name]
+    say(f"fused forward vs two launches: {name}")
+    inp = to_dev(make_inputs(shape, seed=3, device="cpu", with_dy=True))
+    outs = []
+    for fused in (False, True):
+        b = LayerBuffers(shape.T, shape.H, shape.I, shape.E, shape.k, shape.I_shared, "bf16",
+                         backward=True, fused_forward=fused)
+        run_layer(b, inp, backward=True)
+        torch.cuda.synchronize()
+        outs.append(digest(b.y, b.saved, b.dx, b.dw_gate, b.dw_up, b.dw_down, b.d_topk_w))
+        assert int(b.plan_views()["err_flag"].item()) == 0
+    assert outs[0] == outs[1]
+
+
+def test_fused_forward_full_size_bitwise_equal():
+    from mixture_experts_layer_plan_amd import LayerBuffers, run_layer
+    shape = CONFIGS["kimi_bf16_fwd"]
+    say("fused forward at full size: inputs on the device")
+    inp = make_inputs(shape, seed=4, device="cuda", with_dy=False)
+    ref = None
+    for fused in (False, True, True):
+        say(f"fused forward at full size: fused = {fused}")
+        b = LayerBuffers(shape.T, shape.H, shape.I, shape.E, shape.k, shape.I_shared, "bf16",
+                         backward=False, fused_forward=fused)
+        run_layer(b, inp, backward=False)
+        torch.cuda.synchronize()
+        assert int(b.plan_views()["err_flag"].item()) == 0
+        if ref is None:
+            ref = (b.y.clone(), b.saved.clone())
+        else:
+            assert torch.equal(b.y, ref[0]) and torch.equal(b.saved, ref[1])
+        del b
+
+
 # --------------------------------------------------------------- full sizes
 class ExpertCache:
     """fp64 host copies of single experts of a device weight stack, on demand."""
