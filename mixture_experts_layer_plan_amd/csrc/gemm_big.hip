@@ -1,6 +1,6 @@
 // Large-tile grouped GEMMs for gfx950 (MI355X): bf16 GEMM1 + SwiGLU, GEMM2 and
-// dgrad-up with their epilogues fused, and the weight gradients (bf16 and MXFP8) of
-// the experts with many rows.
+// dgrad-up with their epilogues fused, MXFP8 GEMM2 and dgrad-up, and the weight
+// gradients (bf16 and MXFP8) of the experts with many rows.
 //
 // The experts are SwiGLU feed-forward nets run as grouped GEMMs over all experts
 // at once (sebask.de, "Mixture-of-Kittens: Cursors Open-Source-Ansatz für
@@ -33,8 +33,8 @@
 //    ds_read_b64_tr_b16 (within each 16-lane group, lane 4a + b receives element b
 //    of the 8-byte rows addressed by lanes a, a + 4, a + 8, a + 12), two reads per
 //    fragment.  No register transpose, no bank conflicts.
-//  * MXFP8 wgrad operands: K-major, 128-byte K pieces (128 E4M3 values) in the
-//    K-major layout above.
+//  * MXFP8 operands (wgrads, and the row-grouped GEMM2 and dgrad-up): K-major,
+//    128-byte K pieces (128 E4M3 values) in the K-major layout above.
 //
 // Grouping: the kernels walk the plan's 256-row tile list (expert, first row); a
 // wavefront skips the MFMAs of 32-row blocks that lie past the expert's rows and
@@ -1099,6 +1099,261 @@ __global__ __launch_bounds__(NTH, 1) void k_wgrad_hot_mx(MxWgradArgs p) {
   }
 }
 
+// ------------------------------------------------------- MXFP8 row-grouped GEMMs
+// GEMM2 and dgrad-up of the MX path on this core.  Every operand is a
+// K-major E4M3 byte row with one E8M0 scale byte per 32 (the activations of a
+// minibatch's ring slot and the quantised weights, in the orientation whose rows run
+// along the GEMM's K).  A stage is a 128-byte K piece of the tile's 256 A and 256 B
+// rows in the K-major layout of the bf16 kernels (128 codes: two 64-deep scaled MFMA
+// steps).  The scale bytes of four stages (16 per row) reach the LDS with one
+// direct-to-LDS load per lane: lane q of the workgroup loads row q of the 512 tile
+// rows (A rows, then B rows), one group ahead of its use, into one of two 8 KiB
+// buffers; each stage then reads its lane's six scale words from the LDS.  Loading
+// the words per stage from global memory instead (six 4-byte loads per lane, each
+// instruction touching 32 rows' cache lines) cost about 30 % of these kernels' time.
+// The K order of every output element is that of the 128 x 128 MX kernels (64-deep
+// steps from K = 0), so the results are the same.  Needs H and I multiples of 512, so
+// that scale groups and dgrad-up's W_g / W_u split align.  Measured on MI355X at T =
+// 8192 in minibatches of 2048 (H = 7168, I = 2048, E = 256, k = 8, Zipf(1.2)), per
+// minibatch launch against the 128 x 128 MX kernels: GEMM2 0.73 -> 0.66 ms, dgrad-up
+// 1.34 -> 1.21 ms.  GEMM1 + SwiGLU on this core took 1.58 against 1.54 ms and stays on
+// the 128 x 128 kernel; issuing the B loads after the first MFMA step (as the bf16
+// kernels do) made all three slower (GEMM2 0.70, dgrad-up 1.32 ms).
+constexpr int MX_GROUP = 4;                                  // K stages per scale load
+constexpr int MX_SBUF = 2 * TILE * 16;                       // scale bytes of one group
+static_assert(4 * STAGE + 2 * MX_SBUF <= LDS_ROWS, "MX stages and scale groups fit");
+
+// A rows row0 .. row0 + rows - 1 of a K-major byte matrix (row stride ld): only the
+// instructions whose 64 rows include one of the tile's are issued; rows past the
+// tile inside an issued instruction read row 0 of the tile (their outputs are not
+// stored).
+struct MxDmaA {
+  const char* base;
+  uint32_t off[4];
+  int n;
+  MOE_DEV void set(const uint8_t* b, size_t ld, int rows) {
+    base = (const char*)b;
+    n = (rows + 63) / 64;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int r = kmaj_row(s);
+      off[s] = (uint32_t)((r < rows ? r : 0) * ld) + 16u * kmaj_chunk();
+    }
+  }
+  MOE_DEV void issue(int kt, char* st) const {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      if (s < n) dma16(base + (size_t)kt * 128 + off[s], kmaj_dst(st, s));
+  }
+};
+
+// B: 256 weight rows at a fixed stride, K stages from kI on from a second matrix
+// (dgrad-up's W_u^T after W_g^T; base1 pre-offset by -128 kI bytes)
+struct MxDmaB {
+  const char* base0;
+  const char* base1;
+  uint32_t off, step;
+  int kI;
+  MOE_DEV void set(const uint8_t* b0, const uint8_t* b1, size_t ld, int k_split) {
+    base0 = (const char*)b0;
+    base1 = (const char*)b1 - (size_t)k_split * 128;
+    off = (uint32_t)(kmaj_row(0) * ld) + 16u * kmaj_chunk();
+    step = (uint32_t)(64 * ld);
+    kI = k_split;
+  }
+  MOE_DEV void issue(int kt, char* st) const {
+    const char* b = kt >= kI ? base1 : base0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dma16(b + (size_t)kt * 128 + off + s * step, kmaj_dst(st, s));
+  }
+};
+
+// Scale bytes of one group for this lane's tile row q = 64 wave + lane (A rows 0..255,
+// then B rows): 16 bytes at src0 + 16 g, or at src1 + 16 g from group g1 on (src1
+// pre-offset by -16 g1), into row q of an 8 KiB buffer.
+struct MxScaleDma {
+  const char* src0;
+  const char* src1;
+  int g1;
+  MOE_DEV void issue(int g, char* sb) const {
+    dma16((g >= g1 ? src1 : src0) + 16 * g, sb + wave() * 1024);
+  }
+};
+
+// this lane's scale words of stage u of the group in sb: A blocks 0..3 of rows
+// 128 wm + 32 i + (lane & 31), B blocks 0..1 of rows 64 wn + 32 j + (lane & 31)
+MOE_DEV void mx_stage_scales(const char* sb, int u, int wm, int wn, MxScales& sc) {
+  const int l = lane() & 31;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sc.a[i] = *(const uint32_t*)(sb + 16 * (128 * wm + 32 * i + l) + 4 * u);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    sc.b[j] = *(const uint32_t*)(sb + 16 * (TILE + 64 * wn + 32 * j + l) + 4 * u);
+}
+
+// one stage of scaled MFMAs: A blocks below ma, B blocks below mb (B at st + boff);
+// the B fragments of a step first, then the A fragments one block at a time with
+// the next block's read in flight during the current block's MFMAs
+MOE_DEV void mma_stage_mx_m(const char* st, int boff, const MxScales& sc, int wm, int wn, int ma,
+                            int mb, Acc& acc) {
+  const int h = lane() >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int sh = 8 * (2 * ks + h);
+    i32x8_t b[2], a[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (j < mb) b[j] = frag_mx(st + boff, 64 * wn + 32 * j, ks);
+    if (ma > 0) a[0] = frag_mx(st, 128 * wm, ks);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i + 1 < ma) a[(i + 1) & 1] = frag_mx(st, 128 * wm + 32 * (i + 1), ks);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (i < ma && j < mb)
+          acc.c[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              a[i & 1], b[j], acc.c[i][j], 0, 0, 0, (int)((sc.a[i] >> sh) & 0xffu), 0,
+              (int)((sc.b[j] >> sh) & 0xffu));
+    }
+  }
+}
+
+// Two LDS data stages (stage kt + 1 loads while stage kt multiplies) and two scale
+// buffers: group G's scale bytes are issued with the data of stage 4 G, i.e. during
+// stage 4 G - 1, into buffer G mod 2, which group G - 2 used.  Every stage ends with
+// the whole workgroup's loads in and a barrier, so each buffer is full before it is
+// read and no longer read when it is loaded again.
+template <class OA, class OB>
+MOE_DEV void main_loop_rows_mx(char* lds, const OA& A, const OB& B, const MxScaleDma& S, int nk,
+                               int ma, int mb, Acc& acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc.c[i][j][v] = 0.0f;
+  if (nk > 0) {
+    const int wm = wave() >> 2, wn = wave() & 3;
+    char* const sb = lds + 4 * STAGE;
+    A.issue(0, lds);
+    B.issue(0, lds + STAGE);
+    S.issue(0, sb);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* cur = lds + (kt & 1) * 2 * STAGE;
+      const int kn = kt + 1;
+      if (kn < nk) {
+        char* nxt = lds + (kn & 1) * 2 * STAGE;
+        A.issue(kn, nxt);
+        B.issue(kn, nxt + STAGE);
+        if (kn % MX_GROUP == 0) S.issue(kn / MX_GROUP, sb + ((kn / MX_GROUP) & 1) * MX_SBUF);
+      }
+      MxScales sc;
+      mx_stage_scales(sb + ((kt / MX_GROUP) & 1) * MX_SBUF, kt % MX_GROUP, wm, wn, sc);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_stage_mx_m(cur, STAGE, sc, wm, wn, ma, mb, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // LDS free for an epilogue or the next tile
+}
+
+// Scale source of this lane's tile row when it is an A row (q < 256): the tile's row
+// q (rows past the tile: its row 0); sc_tile is the scale row of the tile's row 0,
+// ks the scale row stride.  Returns NULL for a B row.
+MOE_DEV const char* mx_scale_src_a(const uint8_t* sc_tile, size_t ks, int rows) {
+  const int q = 64 * wave() + lane();
+  if (q >= TILE) return nullptr;
+  return (const char*)sc_tile + (size_t)(q < rows ? q : 0) * ks;
+}
+
+// GEMM2, MX: Y = Q_I(h) Q_I(W_d)^T in bf16
+__global__ __launch_bounds__(NTH, 1) void k_down_mx(GroupInfo g, const uint8_t* __restrict__ hq,
+                                                    const uint8_t* __restrict__ hsc,
+                                                    const uint8_t* __restrict__ wd8,
+                                                    const uint8_t* __restrict__ wds, int H, int I,
+                                                    bf16_t* __restrict__ Y) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_ROWS];
+  Tile t;
+  int nt;
+  if (!row_tile<false>(g, H / TILE, t, nt)) return;
+  const int rows = t.row_end - t.row0, n0 = nt * TILE, IS = I / 32;
+  const size_t wrow = (size_t)t.e * H + n0;
+  MxDmaA A;
+  A.set(hq + (size_t)t.row0 * I, (size_t)I, rows);
+  MxDmaB B;
+  B.set(wd8 + wrow * I, wd8 + wrow * I, (size_t)I, 1 << 30);
+  MxScaleDma S;
+  S.src0 = mx_scale_src_a(hsc + (size_t)t.row0 * IS, (size_t)IS, rows);
+  if (!S.src0) S.src0 = (const char*)wds + (wrow + (64 * wave() + lane() - TILE)) * IS;
+  S.src1 = S.src0;
+  S.g1 = 1 << 30;
+  Acc acc;
+  main_loop_rows_mx(lds, A, B, S, I / 128, blocks_a(rows), 2, acc);
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) {
+      const int n = n0 + out_col(bj);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = t.row0 + out_row(bi, v);
+        if (r < t.row_end) Y[(size_t)r * H + n] = f32_to_bf16(acc.c[bi][bj][v]);
+      }
+    }
+}
+
+// dgrad-up, MX: dX = Q_2I(dZ) [Q_I(W_g); Q_I(W_u)] with the weights stored transposed
+// [E, H, I]: B row n takes W_g^T[e][n] for K < I and W_u^T[e][n] after
+__global__ __launch_bounds__(NTH, 1) void k_dgrad_up_mx(GroupInfo g, const uint8_t* __restrict__ dZ8,
+                                                        const uint8_t* __restrict__ dZs,
+                                                        const uint8_t* __restrict__ wgT8,
+                                                        const uint8_t* __restrict__ wgTs,
+                                                        const uint8_t* __restrict__ wuT8,
+                                                        const uint8_t* __restrict__ wuTs, int H,
+                                                        int I, bf16_t* __restrict__ dX) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_ROWS];
+  Tile t;
+  int nt;
+  if (!row_tile<false>(g, H / TILE, t, nt)) return;
+  const int rows = t.row_end - t.row0, n0 = nt * TILE, IS = I / 32, S2 = (2 * I) / 32;
+  const int kI = I / 128;
+  const size_t wrow = (size_t)t.e * H + n0;
+  MxDmaA A;
+  A.set(dZ8 + (size_t)t.row0 * (2 * I), (size_t)(2 * I), rows);
+  MxDmaB B;
+  B.set(wgT8 + wrow * I, wuT8 + wrow * I, (size_t)I, kI);
+  MxScaleDma S;
+  S.src0 = mx_scale_src_a(dZs + (size_t)t.row0 * S2, (size_t)S2, rows);
+  S.g1 = 1 << 30;
+  if (S.src0) {
+    S.src1 = S.src0;
+  } else {
+    const size_t n = wrow + (64 * wave() + lane() - TILE);
+    S.src0 = (const char*)wgTs + n * IS;
+    S.g1 = kI / MX_GROUP;
+    S.src1 = (const char*)wuTs + n * IS - 16 * S.g1;
+  }
+  Acc acc;
+  main_loop_rows_mx(lds, A, B, S, (2 * I) / 128, blocks_a(rows), 2, acc);
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) {
+      const int n = n0 + out_col(bj);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = t.row0 + out_row(bi, v);
+        if (r < t.row_end) dX[(size_t)r * H + n] = f32_to_bf16(acc.c[bi][bj][v]);
+      }
+    }
+}
+
 // Zero the 128 bytes after the packed token axis of every row (stages of the last
 // expert read up to 96 bytes past its range; those bytes are otherwise never written).
 __global__ __launch_bounds__(256) void mx_zero_tail_kernel(uint8_t* __restrict__ q, int rows,
@@ -1184,6 +1439,35 @@ hipError_t launch_big_dgrad_up(const GroupInfo& g, const void* dZ, const void* w
                     big::k_dgrad_up<<<ty * ((H + big::TILE - 1) / big::TILE), big::NTH, 0, s>>>(
                         g, (const bf16_t*)dZ, (const bf16_t*)wg, (const bf16_t*)wu, H, I,
                         (bf16_t*)dX));
+}
+
+// MX GEMM2 and dgrad-up on this core: H and I multiples of 512 (scale groups of 512
+// bytes of K) and the plan's wide-tile list present; hipErrorNotSupported (nothing
+// enqueued) otherwise
+static bool big_mx_ok(const GroupInfo& g, int H, int I) {
+  return g.wtiles && H % 512 == 0 && I % 512 == 0;
+}
+
+hipError_t launch_big_mx_down(const GroupInfo& g, const uint8_t* hq, const uint8_t* hs,
+                              const uint8_t* wd8, const uint8_t* wds, int H, int I, void* Y,
+                              hipStream_t s) {
+  if (!big_mx_ok(g, H, I)) return hipErrorNotSupported;
+  const unsigned ty = big_row_tiles(g);
+  if (ty == 0) return hipSuccess;
+  return MOE_LAUNCH("mx_gemm_down", s,
+                    big::k_down_mx<<<ty * (H / big::TILE), big::NTH, 0, s>>>(
+                        g, hq, hs, wd8, wds, H, I, (bf16_t*)Y));
+}
+
+hipError_t launch_big_mx_dgrad_up(const GroupInfo& g, const uint8_t* dZ8, const uint8_t* dZs,
+                                  const uint8_t* wgT8, const uint8_t* wgTs, const uint8_t* wuT8,
+                                  const uint8_t* wuTs, int H, int I, void* dX, hipStream_t s) {
+  if (!big_mx_ok(g, H, I)) return hipErrorNotSupported;
+  const unsigned ty = big_row_tiles(g);
+  if (ty == 0) return hipSuccess;
+  return MOE_LAUNCH("mx_gemm_dgrad_up", s,
+                    big::k_dgrad_up_mx<<<ty * (H / big::TILE), big::NTH, 0, s>>>(
+                        g, dZ8, dZs, wgT8, wgTs, wuT8, wuTs, H, I, (bf16_t*)dX));
 }
 
 // GM for xcd_rect: the XCD grid (GM x 8 / GM) whose rectangles need the fewest panels

@@ -529,6 +529,8 @@ hipError_t launch_mx_up_swiglu(const GroupInfo& g, const uint8_t* X8, const uint
 hipError_t launch_mx_down(const GroupInfo& g, const uint8_t* hq, const uint8_t* hs,
                           const uint8_t* wd8, const uint8_t* wds, int H, int I, void* Y,
                           hipStream_t s) {
+  const hipError_t e = launch_big_mx_down(g, hq, hs, wd8, wds, H, I, Y, s);
+  if (e != hipErrorNotSupported) return e;
   const unsigned ty = (unsigned)g.max_tiles;
   if (ty == 0) return hipSuccess;
   return MOE_LAUNCH("mx_gemm_down", s,
@@ -551,6 +553,8 @@ hipError_t launch_mx_dgrad_down(const GroupInfo& g, const uint8_t* dYu8, const u
 hipError_t launch_mx_dgrad_up(const GroupInfo& g, const uint8_t* dZ8, const uint8_t* dZs,
                               const uint8_t* wgT8, const uint8_t* wgTs, const uint8_t* wuT8,
                               const uint8_t* wuTs, int H, int I, void* dX, hipStream_t s) {
+  const hipError_t e = launch_big_mx_dgrad_up(g, dZ8, dZs, wgT8, wgTs, wuT8, wuTs, H, I, dX, s);
+  if (e != hipErrorNotSupported) return e;
   const unsigned ty = (unsigned)g.max_tiles;
   if (ty == 0) return hipSuccess;
   return MOE_LAUNCH("mx_gemm_dgrad_up", s,

@@ -107,6 +107,15 @@ hipError_t launch_big_down(const GroupInfo& g, const void* h, const void* wd, in
 hipError_t launch_big_forward_fused(const GroupInfo& g, const void* x, const void* wg,
                                     const void* wu, const void* wd, int H, int I, void* Z, void* h,
                                     void* Y, int32_t* ready, int32_t* err, hipStream_t s);
+// MXFP8 GEMM2 and dgrad-up on the 256 x 256 core (gemm_big.hip); hipErrorNotSupported
+// (nothing enqueued) unless H and I are multiples of 512 and the plan has its
+// wide-tile list, and the launch_mx_* entry points then use the 128 x 128 kernels
+hipError_t launch_big_mx_down(const GroupInfo& g, const uint8_t* hq, const uint8_t* hs,
+                              const uint8_t* wd8, const uint8_t* wds, int H, int I, void* Y,
+                              hipStream_t s);
+hipError_t launch_big_mx_dgrad_up(const GroupInfo& g, const uint8_t* dZ8, const uint8_t* dZs,
+                                  const uint8_t* wgT8, const uint8_t* wgTs, const uint8_t* wuT8,
+                                  const uint8_t* wuTs, int H, int I, void* dX, hipStream_t s);
 hipError_t launch_big_dgrad_up(const GroupInfo& g, const void* dZ, const void* wg, const void* wu,
                                int H, int I, void* dX, hipStream_t s);
 // bf16 wgrads of the experts with >= hot_rows rows on the large tiles;

@@ -175,14 +175,17 @@ MX_EXACT_COUNTS = [0, 1, 31, 32, 33, 127, 128, 129, 255, 256, 257, 300]
 
 
 @pytest.mark.parametrize("T_mb", [0, 512])
-def test_mx_layer_exact_row_counts(T_mb):
+@pytest.mark.parametrize("HI", [(256, 256), (512, 512)])
+def test_mx_layer_exact_row_counts(HI, T_mb):
     """Every output element by element.  Two rows of the 300-row expert hold E4M3
     codes of h that differ between the kernel's fp32 pre-activations and the oracle's
     fp64 ones (the pre-activations agree to 1.1e-5 and straddle a rounding midpoint),
     which moves those rows of y by up to 3.6 %: the allowance for such code choices
-    covers them."""
+    covers them.  H = I = 256 runs the row-grouped MX GEMMs on the 128-row kernels,
+    H = I = 512 on the 256-row kernels (K a multiple of 512)."""
     counts = np.array(MX_EXACT_COUNTS)
-    shape = Shape(T=int(counts.sum()), H=256, I=256, E=len(counts), k=1, dtype="mxfp8")
+    H, I = HI
+    shape = Shape(T=int(counts.sum()), H=H, I=I, E=len(counts), k=1, dtype="mxfp8")
     say(f"mx layer exact counts {MX_EXACT_COUNTS}: {shape} T_mb={T_mb}")
     inp = make_inputs(shape, seed=7, device="cpu", with_dy=True)
     # top-1 expert of token t fixed by a margin of 8 over N(0, 0.25) logits
