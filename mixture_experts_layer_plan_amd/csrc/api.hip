@@ -358,8 +358,8 @@ moe_status backward_impl(moe_dtype dt, const moe_shape* s, const void* plan, con
   void* dYu = at<char>(ws, W.dYu);
   const int es = d ? 2 : 4;
   // reverse-combine: pull dy rows into expert order; replay the dispatch of x
-  MOE_TRY(launch_gather_rows(dy, dYu, v.src_token, v.offsets + s->E, R, H * es, st));
-  MOE_TRY(launch_gather_rows(x, X, v.src_token, v.offsets + s->E, R, H * es, st));
+  MOE_TRY(launch_scatter_rows(dy, dYu, v.pos, s->T, s->k, H * es, st));
+  MOE_TRY(launch_scatter_rows(x, X, v.pos, s->T, s->k, H * es, st));
   // dgrad-down + SwiGLU backward + router-weight-gradient partials
   MOE_TRY(launch_gemm_dgrad_down(d, g, dYu, wd, Z, topk_w, H, I, s->k, dZ, gh, dgp, st));
   MOE_TRY(launch_dg_reduce(dgp, v.pos, R, I / 128, d_topk_w, st));

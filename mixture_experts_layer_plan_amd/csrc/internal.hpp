@@ -67,6 +67,9 @@ hipError_t launch_plan(const int32_t* topk_idx, int T, int k, int E, const PlanP
 // row movement
 hipError_t launch_gather_rows(const void* src, void* dst, const int32_t* src_token,
                               const int32_t* n_valid, int R, int row_bytes, hipStream_t s);
+// the same rows written from the source side: dst[pos[t, j]] = src[t] (pos < 0 skipped)
+hipError_t launch_scatter_rows(const void* src, void* dst, const int32_t* pos, int T, int k,
+                               int row_bytes, hipStream_t s);
 hipError_t launch_combine_bf16(const void* Y, const int32_t* pos, const float* w,
                                const void* shared, void* y, int T, int k, int H, hipStream_t s);
 hipError_t launch_combine_f32(const float* Y, const int32_t* pos, const float* w,

@@ -39,6 +39,38 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restric
   for (; c < row_chunks; c += 256) nts(d + c, s[c]);
 }
 
+// The same copy walked by source token: dst[pos[t, j], :] = src[t, :] for every pair
+// with pos[t, j] >= 0 (the rows r < n_valid, each written once), so that each source
+// row is read once and written to its k rows.  One workgroup per token; the token's
+// slots are wave-uniform reads through the constant address space.
+__global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4* __restrict__ src,
+                                                           uint4* __restrict__ dst,
+                                                           const int32_t* __restrict__ pos, int k,
+                                                           int row_chunks) {
+  const int t = blockIdx.x;
+  typedef const __attribute__((address_space(4))) int32_t* cpos_t;
+  const cpos_t s_pos = (cpos_t)(pos + (size_t)t * k);
+  const uint4* s = src + (size_t)t * row_chunks;
+  for (int c0 = 0; c0 < row_chunks; c0 += 4 * 256) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + u * 256 + (int)threadIdx.x;
+      if (c < row_chunks) v[u] = s[c];
+    }
+    for (int j = 0; j < k; ++j) {
+      const int r = s_pos[j];
+      if (r < 0) continue;
+      uint4* d = dst + (size_t)r * row_chunks;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + u * 256 + (int)threadIdx.x;
+        if (c < row_chunks) nts(d + c, v[u]);
+      }
+    }
+  }
+}
+
 // y[t, :] = round( sum_j w[t, j] * Y[pos[t, j], :] + shared[t, :] ), fp32 from zero,
 // j ascending, shared last.  WEIGHTED = false sums with weight 1 (reverse-dispatch).
 // One 128-thread workgroup per (token, slice of 128 16-byte chunks); each thread
@@ -161,6 +193,14 @@ hipError_t launch_gather_rows(const void* src, void* dst, const int32_t* src_tok
   return MOE_LAUNCH("gather_rows", s,
                     gather_rows_kernel<<<R, 256, 0, s>>>((const uint4*)src, (uint4*)dst,
                                                          src_token, n_valid, row_bytes / 16));
+}
+
+hipError_t launch_scatter_rows(const void* src, void* dst, const int32_t* pos, int T, int k,
+                               int row_bytes, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  return MOE_LAUNCH("gather_rows", s,
+                    scatter_rows_kernel<<<T, 256, 0, s>>>((const uint4*)src, (uint4*)dst, pos, k,
+                                                          row_bytes / 16));
 }
 
 hipError_t launch_combine_bf16(const void* Y, const int32_t* pos, const float* w,
