@@ -591,7 +591,7 @@ moe_status forward_mx_impl(const moe_shape* s, const void* plan, const void* x,
     uint8_t* hs = at<uint8_t>(ws, W.hs);
     void* Y = at<char>(ws, W.Y);
     // dispatch into the ring slot, quantised along H on the way
-    MOE_TRY(launch_quant_rows(1, xm, v.src_token, v.offsets + s->E, R_m, H, X8, Xs, st));
+    MOE_TRY(launch_quant_scatter_rows(1, xm, v.pos, T_m, k, H, X8, Xs, st));
     MOE_TRY(launch_mx_up_swiglu(g, X8, Xs, q + Q.wg8, q + Q.wgs, q + Q.wu8, q + Q.wus, H, I, Z,
                                 hq, hs, st));
     MOE_TRY(launch_mx_down(g, hq, hs, q + Q.wd8, q + Q.wds, H, I, Y, st));
@@ -694,7 +694,7 @@ moe_status backward_mx_impl(const moe_shape* s, const void* plan, const void* x,
         uint8_t* X8 = at<uint8_t>(ws, W.rX8);
         uint8_t* Xs = at<uint8_t>(ws, W.rXs);
         float* rZ = at<float>(ws, W.rZ);
-        MOE_TRY(launch_quant_rows(1, xm, v.src_token, v.offsets + s->E, R_m, H, X8, Xs, st));
+        MOE_TRY(launch_quant_scatter_rows(1, xm, v.pos, T_m, k, H, X8, Xs, st));
         MOE_TRY(launch_mx_up_swiglu(g, X8, Xs, q + Q.wg8, q + Q.wgs, q + Q.wu8, q + Q.wus, H, I,
                                     rZ, at<uint8_t>(ws, W.rhq), at<uint8_t>(ws, W.rhs), st));
         Z = rZ;
@@ -707,7 +707,7 @@ moe_status backward_mx_impl(const moe_shape* s, const void* plan, const void* x,
     float* dgp = at<float>(ws, W.dgp);
     void* dX = at<char>(ws, W.dX);
     // reverse-combine into the ring slot, quantised along H
-    MOE_TRY(launch_quant_rows(1, dym, v.src_token, v.offsets + s->E, R_m, H, dYu8, dYus, st));
+    MOE_TRY(launch_quant_scatter_rows(1, dym, v.pos, T_m, k, H, dYu8, dYus, st));
     MOE_TRY(launch_mx_dgrad_down(g, dYu8, dYus, q + Q.wdT8, q + Q.wdTs, Z, topk_w + tok0 * k, H,
                                  I, k, dZ, dZ8, dZsc, gh, dgp, st));
     MOE_TRY(launch_dg_reduce(dgp, v.pos, R_m, I / 128, d_topk_w + tok0 * k, st));

@@ -161,6 +161,10 @@ constexpr int MX_WGRAD_HOT_BYTES = 256;
 hipError_t launch_quant_rows(int dt, const void* src, const int32_t* gather,
                              const int32_t* n_rows_dev, int n_rows, int cols, uint8_t* q,
                              uint8_t* sc, hipStream_t s);
+// The same rows written from the source side (the dispatch of tokens into expert
+// rows): q[pos[t, j]] = Q(src[t]) for t < n_tok, j < k, pos >= 0.
+hipError_t launch_quant_scatter_rows(int dt, const void* src, const int32_t* pos, int n_tok, int k,
+                                     int cols, uint8_t* q, uint8_t* sc, hipStream_t s);
 // Column quantisation of batch x [rows, cols] into batch x [cols, rows] (blocks along rows).
 hipError_t launch_quant_cols(int dt, const void* src, int batch, int rows, int cols, uint8_t* q,
                              uint8_t* sc, hipStream_t s);

@@ -50,6 +50,40 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ s
   }
 }
 
+// The dispatch form of the same quantisation, walked by source token: row src[t]
+// (t < n_tok) is quantised once and its codes and scales go to every destination row
+// pos[t, j] >= 0, i.e. q[pos[t, j]] = Q(src[t]), the rows that the pull form
+// q[r] = Q(src[src_token[r]]) writes.  One wavefront per token; lane j < k holds
+// slot j and the others read it by lane exchange.
+template <typename T>
+__global__ __launch_bounds__(256) void quant_scatter_rows_kernel(const T* __restrict__ src,
+                                                                 const int32_t* __restrict__ pos,
+                                                                 int n_tok, int k, int cols,
+                                                                 uint8_t* __restrict__ q,
+                                                                 uint8_t* __restrict__ sc) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= n_tok) return;
+  const int my_row = lane < k ? pos[(size_t)t * k + lane] : -1;
+  const T* row = src + (size_t)t * cols;
+  const int nb = cols / 32;
+  for (int b = lane; b < nb; b += 64) {
+    float v[32];
+    load32(row + 32 * b, v);
+    const int X = mx_scale_exp(v);
+    uint4 lo, hi;
+    mx_encode32(v, X, lo, hi);
+    for (int j = 0; j < k; ++j) {
+      const int r = __shfl(my_row, j, 64);
+      if (r < 0) continue;
+      uint4* qd = (uint4*)(q + (size_t)r * cols + 32 * b);
+      qd[0] = lo;
+      qd[1] = hi;
+      sc[(size_t)r * nb + b] = (uint8_t)(X + 127);
+    }
+  }
+}
+
 // ------------------------------------------------------------ columns
 // Batched [batch, rows, cols] -> q [batch, cols, rows] with blocks of 32 along
 // rows: q[b, c, r] = E4M3(src[b, r, c] / 2^X(b, c, r / 32)).  A workgroup takes a
@@ -166,6 +200,19 @@ hipError_t launch_quant_rows(int dt, const void* src, const int32_t* gather,
   return MOE_LAUNCH("mx_quant_rows", s,
                     quant_rows_kernel<float><<<grid, 256, 0, s>>>(
                         (const float*)src, gather, n_rows_dev, n_rows, cols, q, sc));
+}
+
+hipError_t launch_quant_scatter_rows(int dt, const void* src, const int32_t* pos, int n_tok, int k,
+                                     int cols, uint8_t* q, uint8_t* sc, hipStream_t s) {
+  if (n_tok == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((n_tok + 3) / 4);
+  if (dt)
+    return MOE_LAUNCH("mx_quant_rows", s,
+                      quant_scatter_rows_kernel<bf16_t><<<grid, 256, 0, s>>>(
+                          (const bf16_t*)src, pos, n_tok, k, cols, q, sc));
+  return MOE_LAUNCH("mx_quant_rows", s,
+                    quant_scatter_rows_kernel<float><<<grid, 256, 0, s>>>(
+                        (const float*)src, pos, n_tok, k, cols, q, sc));
 }
 
 hipError_t launch_quant_cols(int dt, const void* src, int batch, int rows, int cols, uint8_t* q,
