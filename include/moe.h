@@ -364,6 +364,11 @@ moe_status moe_quantize_weights_mxfp8(const moe_shape* shape, const void* w_gate
 moe_status moe_quantize_mxfp8(const void* src, int64_t rows, int64_t cols, int axis, uint8_t* q,
                               uint8_t* scales, hipStream_t stream);
 
+/* The same for an fp32 matrix, as the MXFP8 backward quantises its fp32
+ * intermediates (dZ and g h along the tokens): the rule applied to the fp32 value. */
+moe_status moe_quantize_mxfp8_f32(const float* src, int64_t rows, int64_t cols, int axis,
+                                  uint8_t* q, uint8_t* scales, hipStream_t stream);
+
 /* As moe_forward_bf16 with the expert weights replaced by `wq`; the shared-expert
  * weights s_* stay bf16.  saved: moe_saved_bytes(shape, MOE_MXFP8); ws:
  * moe_workspace_bytes(shape, MOE_MXFP8, 0). */

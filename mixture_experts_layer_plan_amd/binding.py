@@ -85,6 +85,7 @@ _SIGS = {
     "moe_mx_weights_bytes": (_Z, [_S]),
     "moe_quantize_weights_mxfp8": (_I, [_S, _P, _P, _P, _P, _P]),
     "moe_quantize_mxfp8": (_I, [_P, ctypes.c_int64, ctypes.c_int64, _I, _P, _P, _P]),
+    "moe_quantize_mxfp8_f32": (_I, [_P, ctypes.c_int64, ctypes.c_int64, _I, _P, _P, _P]),
     "moe_forward_mxfp8": (_I, [_S] + [_P] * 10 + [_Z, _P]),
     "moe_backward_mxfp8": (_I, [_S] + [_P] * 18 + [_Z, _P]),
 }
@@ -318,6 +319,12 @@ def moe_quantize_weights_mxfp8(s, w_gate, w_up, w_down, wq, stream=None):
 def moe_quantize_mxfp8(src, rows, cols, axis, q, scales, stream=None):
     _call("moe_quantize_mxfp8", _ptr(src), int(rows), int(cols), int(axis), _ptr(q), _ptr(scales),
           _stream(stream))
+
+
+def moe_quantize_mxfp8_f32(src, rows, cols, axis, q, scales, stream=None):
+    n = int(rows) * int(cols)
+    _call("moe_quantize_mxfp8_f32", _f32(src, n), int(rows), int(cols), int(axis),
+          _ptr(q, torch.uint8, n), _ptr(scales, torch.uint8, n // 32), _stream(stream))
 
 
 def moe_forward_mxfp8(s, plan, x, topk_w, wq, s_gate, s_up, s_down, y, saved, ws, stream=None):

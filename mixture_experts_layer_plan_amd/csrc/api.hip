@@ -579,7 +579,7 @@ moe_status forward_mx_impl(const moe_shape* s, const void* plan, const void* x,
   const int H = s->H, I = s->I, k = s->k, nmb = n_minibatches(s), Tmb = minibatch_tokens(s);
   const uint8_t* q = (const uint8_t*)wq;
   for (int m = 0; m < nmb; ++m) {
-    const int T_m = std::min(Tmb, s->T - m * Tmb), R_m = T_m * k;
+    const int T_m = std::min(Tmb, s->T - m * Tmb);
     const PlanView v = view_plan(s, plan, m);
     const GroupInfo g = grouped(s, v);
     const bf16_t_host* xm = (const bf16_t_host*)x + (size_t)m * Tmb * H;
@@ -850,21 +850,31 @@ moe_status moe_quantize_weights_mxfp8(const moe_shape* s, const void* w_gate, co
   return MOE_OK;
 }
 
-moe_status moe_quantize_mxfp8(const void* src, int64_t rows, int64_t cols, int axis, uint8_t* q,
-                              uint8_t* scales, hipStream_t st) {
+static moe_status quantize_mxfp8(int dt, const void* src, int64_t rows, int64_t cols, int axis,
+                                 uint8_t* q, uint8_t* scales, hipStream_t st) {
   if (any_null({src, q, scales}) && rows * cols > 0) return MOE_E_NULL;
   if (!all_aligned({src, q})) return MOE_E_ALIGN;
   if (rows < 0 || cols < 0 || rows > INT32_MAX || cols > INT32_MAX) return MOE_E_SHAPE;
   if (rows * cols == 0) return MOE_OK;
   if (axis == 1) {
     if (cols % 32) return MOE_E_SHAPE;
-    return hip_status(launch_quant_rows(1, src, nullptr, nullptr, (int)rows, (int)cols, q, scales, st));
+    return hip_status(launch_quant_rows(dt, src, nullptr, nullptr, (int)rows, (int)cols, q, scales, st));
   }
   if (axis == 0) {
     if (rows % 32) return MOE_E_SHAPE;
-    return hip_status(launch_quant_cols(1, src, 1, (int)rows, (int)cols, q, scales, st));
+    return hip_status(launch_quant_cols(dt, src, 1, (int)rows, (int)cols, q, scales, st));
   }
   return MOE_E_SHAPE;
+}
+
+moe_status moe_quantize_mxfp8(const void* src, int64_t rows, int64_t cols, int axis, uint8_t* q,
+                              uint8_t* scales, hipStream_t st) {
+  return quantize_mxfp8(1, src, rows, cols, axis, q, scales, st);
+}
+
+moe_status moe_quantize_mxfp8_f32(const float* src, int64_t rows, int64_t cols, int axis,
+                                  uint8_t* q, uint8_t* scales, hipStream_t st) {
+  return quantize_mxfp8(0, src, rows, cols, axis, q, scales, st);
 }
 
 moe_status moe_forward_mxfp8(const moe_shape* s, const void* plan, const void* x,

@@ -59,6 +59,49 @@ def test_quantise_cols_transposed_bitexact(B, rows, cols):
     np.testing.assert_array_equal(np_(s), rs.T)
 
 
+def rounding_edges_f32(n_blocks, seed):
+    """fp32 blocks of 32 whose scaled values sit on the E4M3 grid, on every midpoint
+    between neighbouring codes and one fp32 step either side of it, and between 448
+    and 480 (saturated): block b has scale exponent X_b (its first value fixes amax
+    in [2^8, 2^9) 2^X_b), including X_b = -125, whose smaller values are fp32
+    subnormals."""
+    rng = np.random.default_rng(seed)
+    grid = oracle.mx.e4m3_decode(np.arange(127))            # codes 0 .. 126: 0 .. 448
+    mids = (grid[:-1] + grid[1:]) / 2
+    m32 = mids.astype(np.float32)
+    cand = np.concatenate([grid, mids, np.nextafter(m32, np.float32(np.inf)).astype(np.float64),
+                           np.nextafter(m32, np.float32(0)).astype(np.float64),
+                           np.float32([450.0, 463.99, 464.0, 479.9]).astype(np.float64)])
+    X = rng.integers(-30, 30, n_blocks)
+    X[:4] = [-125, -120, 100, 0]
+    blocks = rng.choice(cand, (n_blocks, 32)) * rng.choice([-1.0, 1.0], (n_blocks, 32))
+    blocks[:, 0] = rng.choice(np.float32([256.0, 300.0, 448.0, 479.9]).astype(np.float64), n_blocks)
+    a = (blocks * np.exp2(X.astype(np.float64))[:, None]).astype(np.float32)
+    assert np.array_equal(a.astype(np.float64)[4:], (blocks * np.exp2(X[:, None]))[4:])
+    return a
+
+
+@pytest.mark.parametrize("axis", [1, 0])
+def test_quantise_f32_rounding_edges_bitexact(B, axis):
+    """The fp32 quantiser (the MXFP8 backward's dZ and g h) on values at and beside every
+    E4M3 rounding midpoint, saturated values and fp32 subnormals, bit for bit."""
+    say(f"mx quantise fp32 rounding edges, axis {axis}")
+    a = rounding_edges_f32(4096, 11).reshape(64, 2048)   # blocks along the columns
+    if axis == 0:
+        a = np.ascontiguousarray(a.T)                     # blocks along the rows
+    rows, cols = a.shape
+    qs = (cols, rows) if axis == 0 else (rows, cols)
+    q = torch.empty(qs, dtype=torch.uint8, device="cuda")
+    s = torch.empty((qs[0], qs[1] // 32), dtype=torch.uint8, device="cuda")
+    B.moe_quantize_mxfp8_f32(torch.from_numpy(a).cuda(), rows, cols, axis, q, s)
+    torch.cuda.synchronize()
+    rq, rs = mx_quantize(a.astype(np.float64), axis=axis)
+    if axis == 0:
+        rq, rs = rq.T, rs.T
+    np.testing.assert_array_equal(np_(s), rs)
+    np.testing.assert_array_equal(np_(q), rq)
+
+
 def test_weight_quantisation_all_orientations(B):
     say("mx weight quantisation")
     E, I, H = 3, 128, 256
