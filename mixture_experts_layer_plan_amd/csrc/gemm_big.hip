@@ -898,10 +898,10 @@ __global__ __launch_bounds__(NTH, 1) void k_wgrad_hot(WgradArgs p) {
 // row i and takes bytes 0-15 from K block 0 and 16-31 from K block 1 of its step,
 // and the scale of (row i, block c) comes from lane i + 32 c: lane (i, h) reads the
 // 16-byte chunks 4 ks + h and 4 ks + 2 + h of its row, and uses byte 2 ks + h of its
-// row's scale word.  Scale words of the stage after the current one are loaded with
-// its data; the bytes of blocks at or past the expert's end are set to 0 (2^-127),
-// so those blocks' products (next expert's codes, or the zero tail written after
-// the packed axis) vanish.
+// row's scale word.  The scale words reach the LDS four pieces at a time (MxScaleLds);
+// the bytes of blocks at or past the expert's end are set to 0 (2^-127), so those
+// blocks' products (next expert's codes, or the zero tail written after the packed
+// axis) vanish.
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 struct DmaKB {  // K-major byte rows at a fixed stride
@@ -923,21 +923,53 @@ struct DmaKB {  // K-major byte rows at a fixed stride
 struct MxScales {
   uint32_t a[4], b[2];
 };
-struct MxScaleRows {
-  const uint8_t* as;  // scale byte (row of A block 0 for this lane, K block of k0)
+
+// Scale bytes of the 256 A and 256 B rows of a wgrad tile, four K pieces (16 bytes
+// of each row) at a time, through the LDS: thread t loads, in the stage of part u
+// (kt % 4) of the next group, the 4-byte word t % 4 of row u * 128 + t / 4 of the
+// 512 (A rows, then B rows), and stores it to that group's LDS buffer after the
+// stage's wait.  Each load instruction then covers 16 rows' contiguous bytes, where
+// one 4-byte word per fragment row per stage (six loads per lane, each touching 32
+// rows' cache lines) cost about a third of the kernel's time.
+struct MxScaleLds {
+  const uint8_t* as;  // A scale rows (row stride ks bytes)
   const uint8_t* bs;
-  uint32_t astep;     // 32 rows of A scales, bytes
-  uint32_t bstep;     // 32 rows of B scales
+  uint32_t offa;      // this thread's A row of part 0, its K byte of the range start
+  uint32_t offb;
+  uint32_t step;      // 128 rows
+  int lim;            // largest in-row offset past the range start that keeps a word
+                      // inside the row
   long kbytes;        // bytes of the expert's range
-  MOE_DEV void load(int kt, MxScales& sc) const {
-    const long nb = (kbytes - (long)kt * 128) / 32;  // blocks of this stage inside the range
+  MOE_DEV void set(const uint8_t* a_rows, const uint8_t* b_rows, long ks, long k0, long kb) {
+    const int t = threadIdx.x;
+    as = a_rows;
+    bs = b_rows;
+    offa = (uint32_t)((t >> 2) * ks + k0 / 32);
+    offb = offa;
+    step = (uint32_t)(128 * ks);
+    lim = (int)(ks - 4 - k0 / 32);
+    kbytes = kb;
+  }
+  // part u of group G (pieces 4 G .. 4 G + 3)
+  MOE_DEV uint32_t load(int G, int u) const {
+    const uint32_t o = (u < 2 ? offa : offb) + (u & 1) * step +
+                       (uint32_t)min(16 * G + 4 * (int)(threadIdx.x & 3), lim);
+    return *(const uint32_t*)((u < 2 ? as : bs) + o);
+  }
+  MOE_DEV void put(char* sb, int u, uint32_t w) const {
+    *(uint32_t*)(sb + 16 * (128 * u + (threadIdx.x >> 2)) + 4 * (threadIdx.x & 3)) = w;
+  }
+  // this lane's words of piece kt from the group buffer sb, blocks past the range zero
+  MOE_DEV void words(const char* sb, int kt, int wm, int wn, MxScales& sc) const {
+    const long nb = (kbytes - (long)kt * 128) / 32;  // blocks of this piece inside the range
     const uint32_t keep = nb >= 4 ? 0xffffffffu : (nb <= 0 ? 0u : (1u << (8 * nb)) - 1u);
+    const int l = lane() & 31, u = kt & 3;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      sc.a[i] = *(const uint32_t*)(as + i * astep + 4 * kt) & keep;
+      sc.a[i] = *(const uint32_t*)(sb + 16 * (128 * wm + 32 * i + l) + 4 * u) & keep;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      sc.b[j] = *(const uint32_t*)(bs + j * bstep + 4 * kt) & keep;
+      sc.b[j] = *(const uint32_t*)(sb + 16 * (TILE + 64 * wn + 32 * j + l) + 4 * u) & keep;
   }
 };
 
@@ -951,48 +983,42 @@ MOE_DEV i32x8_t frag_mx(const char* st, int r0, int ks) {
   return v;
 }
 
-MOE_DEV void mma_stage_mx(const char* st, const MxScales& sc, int wm, int wn, Acc& acc) {
+// one stage of scaled MFMAs: A blocks below ma, B blocks below mb (B at st + boff);
+// the B fragments of a step first, then the A fragments one block at a time with
+// the next block's read in flight during the current block's MFMAs
+MOE_DEV void mma_stage_mx_m(const char* st, int boff, const MxScales& sc, int wm, int wn, int ma,
+                            int mb, Acc& acc) {
   const int h = lane() >> 5;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     const int sh = 8 * (2 * ks + h);
-    i32x8_t a[4], b[2];
+    i32x8_t b[2], a[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = frag_mx(st, 128 * wm + 32 * i, ks);
+    for (int j = 0; j < 2; ++j)
+      if (j < mb) b[j] = frag_mx(st + boff, 64 * wn + 32 * j, ks);
+    if (ma > 0) a[0] = frag_mx(st, 128 * wm, ks);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) b[j] = frag_mx(st + STAGE, 64 * wn + 32 * j, ks);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      if (i + 1 < ma) a[(i + 1) & 1] = frag_mx(st, 128 * wm + 32 * (i + 1), ks);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        acc.c[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            a[i], b[j], acc.c[i][j], 0, 0, 0, (int)((sc.a[i] >> sh) & 0xffu), 0,
-            (int)((sc.b[j] >> sh) & 0xffu));
+        if (i < ma && j < mb)
+          acc.c[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              a[i & 1], b[j], acc.c[i][j], 0, 0, 0, (int)((sc.a[i] >> sh) & 0xffu), 0,
+              (int)((sc.b[j] >> sh) & 0xffu));
+    }
   }
 }
 
-// One K stage: issue stage kn's data into `nxt` and its scale words into sn, multiply
-// stage `cur` with sc, wait for this wavefront's loads, meet the workgroup.
-MOE_DEV void stage_mx(const DmaKB& A, const DmaKB& B, const MxScaleRows& S, int kn,
-                      const char* cur, char* nxt, const MxScales& sc, MxScales& sn, int wm, int wn,
-                      Acc& acc) {
-  A.issue(kn, nxt);
-  B.issue(kn, nxt + STAGE);
-  S.load(kn, sn);
-  __builtin_amdgcn_sched_barrier(0);
-  mma_stage_mx(cur, sc, wm, wn, acc);
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
+constexpr int MX_WSBUF = 2 * TILE * 16;  // scale bytes of one group of four pieces
 
-// Two LDS stages: stage kt + 1 (data and scale words) loads while stage kt
-// multiplies.  The loop is unrolled by two with the scale words in two fixed sets
-// (no copy from "next" to "current"): with a copy the compiler waits for the next
-// stage's scale loads, and so for every load in flight, before the current stage's
-// MFMAs.
-MOE_DEV void main_loop_mx(char* lds, const DmaKB& A, const DmaKB& B, const MxScaleRows& S, int nk,
+// Two LDS data stages (piece kt + 1 loads while piece kt multiplies) and two scale
+// group buffers after them (group G read in pieces 4 G .. 4 G + 3 from buffer G mod 2,
+// written during pieces 4 G - 4 .. 4 G - 1; past the last group the words loaded and
+// stored are unused, which keeps the loop free of branches: with a branch around
+// them the compiler spilled registers).  Every piece ends with the whole workgroup's
+// loads and LDS stores done and a barrier.
+MOE_DEV void main_loop_mx(char* lds, const DmaKB& A, const DmaKB& B, const MxScaleLds& S, int nk,
                           Acc& acc) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -1002,18 +1028,35 @@ MOE_DEV void main_loop_mx(char* lds, const DmaKB& A, const DmaKB& B, const MxSca
       for (int v = 0; v < 16; ++v) acc.c[i][j][v] = 0.0f;
   if (nk <= 0) return;
   const int wm = wave() >> 2, wn = wave() & 3;
-  char* b0 = lds;
-  char* b1 = lds + 2 * STAGE;
-  MxScales s0, s1;
-  A.issue(0, b0);
-  B.issue(0, b0 + STAGE);
-  S.load(0, s0);
+  char* const sb = lds + 4 * STAGE;
+  A.issue(0, lds);
+  B.issue(0, lds + STAGE);
+  uint32_t w0 = S.load(0, 0), w1 = S.load(0, 1), w2 = S.load(0, 2), w3 = S.load(0, 3);
   __builtin_amdgcn_s_waitcnt(0);
+  S.put(sb, 0, w0);
+  S.put(sb, 1, w1);
+  S.put(sb, 2, w2);
+  S.put(sb, 3, w3);
   __syncthreads();
-  // the last stage reloads itself into the idle buffer (never read)
-  for (int kt = 0; kt < nk; kt += 2) {
-    stage_mx(A, B, S, kt + 1 < nk ? kt + 1 : kt, b0, b1, s0, s1, wm, wn, acc);
-    if (kt + 1 < nk) stage_mx(A, B, S, kt + 2 < nk ? kt + 2 : kt + 1, b1, b0, s1, s0, wm, wn, acc);
+  for (int kt = 0; kt < nk; ++kt) {
+    const char* cur = lds + (kt & 1) * 2 * STAGE;
+    const int kn = kt + 1, gn = (kt >> 2) + 1, u = kt & 3;
+    if (kn < nk) {
+      char* nxt = lds + (kn & 1) * 2 * STAGE;
+      A.issue(kn, nxt);
+      B.issue(kn, nxt + STAGE);
+    }
+    const uint32_t w = S.load(gn, u);  // past the last group: an unused word
+    MxScales sc;
+    S.words(sb + ((kt >> 2) & 1) * MX_WSBUF, kt, wm, wn, sc);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_stage_mx_m(cur, STAGE, sc, wm, wn, 4, 2, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    S.put(sb + (gn & 1) * MX_WSBUF, u, w);  // never the buffer being read
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   }
   __syncthreads();  // LDS free for another tile
 }
@@ -1051,7 +1094,7 @@ MOE_DEV int list_hot_kpos(const int32_t* kpos, int E, int hot_bytes, int* hot, i
 }
 
 __global__ __launch_bounds__(NTH, 1) void k_wgrad_hot_mx(MxWgradArgs p) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS];
+  __shared__ __attribute__((aligned(16))) char lds[LDS + 2 * MX_WSBUF];
   __shared__ int s_hot[MOE_MAX_E], s_n[1];
   const int n_hot = list_hot_kpos(p.kpos, p.E, p.hot_bytes, s_hot, s_n);
   const int x = blockIdx.x % N_XCD, slot = blockIdx.x / N_XCD, nslot = gridDim.x / N_XCD;
@@ -1061,8 +1104,7 @@ __global__ __launch_bounds__(NTH, 1) void k_wgrad_hot_mx(MxWgradArgs p) {
   const int nq = per * n_hot;
   const long KS = p.Kp / 32;
   const long part0 = (long)p.half_rows * p.N, part1 = (long)(p.M - p.half_rows) * p.N;
-  const int wm = wave() >> 2, wn = wave() & 3;
-  for (int q = slot; q < nq; q += nslot) {
+    for (int q = slot; q < nq; q += nslot) {
     const int h = q / per, j = q - h * per;
     const int e = __builtin_amdgcn_readfirstlane(s_hot[h]);
     const int m0 = (m_lo + j % pm) * TILE, n0 = (n_lo + j / pm) * TILE;
@@ -1070,12 +1112,8 @@ __global__ __launch_bounds__(NTH, 1) void k_wgrad_hot_mx(MxWgradArgs p) {
     DmaKB A, B;
     A.set(p.A8 + (size_t)m0 * p.Kp + k0, (size_t)p.Kp);
     B.set(p.B8 + (size_t)n0 * p.Kp + k0, (size_t)p.Kp);
-    MxScaleRows S;
-    S.as = p.As + (size_t)(m0 + 128 * wm + (lane() & 31)) * KS + k0 / 32;
-    S.bs = p.Bs + (size_t)(n0 + 64 * wn + (lane() & 31)) * KS + k0 / 32;
-    S.astep = (uint32_t)(32 * KS);
-    S.bstep = (uint32_t)(32 * KS);
-    S.kbytes = kb;
+    MxScaleLds S;
+    S.set(p.As + (size_t)m0 * KS, p.Bs + (size_t)n0 * KS, KS, k0, kb);
     Acc acc;
     main_loop_mx(lds, A, B, S, (int)((kb + 127) / 128), acc);
     bf16_t* base = m0 < p.half_rows
@@ -1189,33 +1227,6 @@ MOE_DEV void mx_stage_scales(const char* sb, int u, int wm, int wn, MxScales& sc
 #pragma unroll
   for (int j = 0; j < 2; ++j)
     sc.b[j] = *(const uint32_t*)(sb + 16 * (TILE + 64 * wn + 32 * j + l) + 4 * u);
-}
-
-// one stage of scaled MFMAs: A blocks below ma, B blocks below mb (B at st + boff);
-// the B fragments of a step first, then the A fragments one block at a time with
-// the next block's read in flight during the current block's MFMAs
-MOE_DEV void mma_stage_mx_m(const char* st, int boff, const MxScales& sc, int wm, int wn, int ma,
-                            int mb, Acc& acc) {
-  const int h = lane() >> 5;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const int sh = 8 * (2 * ks + h);
-    i32x8_t b[2], a[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      if (j < mb) b[j] = frag_mx(st + boff, 64 * wn + 32 * j, ks);
-    if (ma > 0) a[0] = frag_mx(st, 128 * wm, ks);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (i + 1 < ma) a[(i + 1) & 1] = frag_mx(st, 128 * wm + 32 * (i + 1), ks);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        if (i < ma && j < mb)
-          acc.c[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              a[i & 1], b[j], acc.c[i][j], 0, 0, 0, (int)((sc.a[i] >> sh) & 0xffu), 0,
-              (int)((sc.b[j] >> sh) & 0xffu));
-    }
-  }
 }
 
 // Two LDS data stages (stage kt + 1 loads while stage kt multiplies) and two scale
