@@ -29,23 +29,25 @@ namespace moe {
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 constexpr int MX_BK = 128;  // K bytes per tile row (4 scale blocks)
 
-// One K-major MX operand as seen by one thread: data rows for its loads (rows
-// (t >> 3) + 32 s of the tile) and scale rows for its MFMA fragments (two 32-row
-// blocks), as 32-bit byte offsets from wave-uniform bases.  Source 1 replaces
-// source 0 for the rows flagged in `sel` (bit s: loader row s, bit 4 + q: scale row
-// q) and for all rows at K >= ksplit (dgrad-up's second weight; its bases are then
-// pre-offset by -ksplit so that the same K offset applies).  Rows with their bit
-// clear in `ok` (same bit positions) load as zeros, and so do the K bytes at or past
-// kend (a multiple of 32): their 16-byte chunks are zeroed and their blocks' scale
-// bytes set to 0 (2^-127), so no stale scale byte (0xFF is NaN in E8M0) reaches the
-// MFMA.
+// One K-major MX operand as seen by one thread: the rows of its loads (rows
+// (t >> 3) + 32 s of the tile) as 32-bit byte offsets from wave-uniform bases; the
+// same rows' scale bytes sit at offset / 32 from the scale bases (a data row is K
+// bytes, its scale row K / 32).  Source 1 replaces source 0 for the rows flagged in
+// `sel` (bit s: row s) and for all rows at K >= ksplit (dgrad-up's second weight;
+// its bases are then pre-offset by -ksplit so that the same K offset applies).  Rows
+// with their bit clear in `ok` load as zeros, and so do the K bytes at or past kend
+// (a multiple of 32): their 16-byte chunks are zeroed and their blocks' scale bytes
+// set to 0 (2^-127), so no stale scale byte (0xFF is NaN in E8M0) reaches the MFMA.
+// klen: bytes of K in a row of source 1 (of source 0 below ksplit), which bounds the
+// scale loads.  soff: the scale rows of this lane's two MFMA fragment blocks, for
+// the loop that loads their words directly (bits 4 + q of ok flag them valid).
 struct MxOp {
   const uint8_t* d[2];   // data bases of source 0 and 1
   const uint8_t* s[2];   // scale bases
   uint32_t off[4];       // data row offsets (bytes)
-  uint32_t soff[2];      // scale row offsets (bytes)
+  uint32_t soff[2];      // fragment scale rows (bytes), direct loads only
   uint32_t sel, ok;
-  long ksplit, kend;
+  long ksplit, kend, klen;
 };
 
 MOE_DEV void mx_op_clear(MxOp& o) {
@@ -58,9 +60,10 @@ MOE_DEV void mx_op_clear(MxOp& o) {
   o.ok = 0x3fu;
   o.ksplit = 1L << 62;
   o.kend = 1L << 62;
+  o.klen = 0;
 }
 
-MOE_DEV void mx_load(const MxOp& o, long koff, uint4 (&r)[4], uint32_t (&sw)[2]) {
+MOE_DEV void mx_load(const MxOp& o, long koff, uint4 (&r)[4]) {
   const bool hi = koff >= o.ksplit;
   const int ch = (threadIdx.x & 7) * 16;
   const bool kin = koff + ch < o.kend;
@@ -69,14 +72,65 @@ MOE_DEV void mx_load(const MxOp& o, long koff, uint4 (&r)[4], uint32_t (&sw)[2])
     const uint8_t* b = (hi || ((o.sel >> q) & 1u)) ? o.d[1] : o.d[0];
     r[q] = ((o.ok >> q) & 1u) && kin ? *(const uint4*)(b + o.off[q] + koff + ch) : zero4();
   }
-  // scale byte b of a word is block koff / 32 + b; keep the blocks below kend
+}
+
+// Scale words through the LDS.  A group is MX_SG K tiles: word j (tile j of the
+// group, four blocks) of each of the 256 tile rows (A rows 0..127, B rows 128..255)
+// at 4 (256 j + row) of a group buffer.  Thread t loads, in the tile of part p of the
+// current group, word t & 7 of row (t >> 3) + 32 (p & 3) of A (p < 4) or B of the
+// next group, and stores it after the tile's wait; eight threads then cover a
+// row's 32 contiguous scale bytes.  Loading the words of the MFMA fragments' rows
+// directly (four loads per lane per tile, each touching 32 rows' cache lines) cost
+// about a quarter of these kernels' time.
+constexpr int MX_SG = 8;
+constexpr int MX_SGB = MX_SG * 256 * 4;
+constexpr int MX_LDS = LDS_BYTES + 2 * MX_SGB;
+
+// this thread's word of row s of operand o at K offset kw; 0 for rows outside the
+// tile; K offsets past the operand read an unused word inside the row
+template <int S>
+MOE_DEV uint32_t mx_sword_of(const MxOp& o, long kw) {
+  const bool hi = kw >= o.ksplit;
+  const long lim = (hi ? o.klen : min(o.ksplit, o.klen)) - MX_BK;
+  if (kw > lim) kw = lim;
+  // the source as a uniform byte distance from source 0 (selecting between the two
+  // 64-bit bases per lane kept both in registers and spilled them)
+  const long delta = (long)((uintptr_t)o.s[1] - (uintptr_t)o.s[0]);
+  const bool one = hi || ((o.sel >> S) & 1u);
+  const uint8_t* p = o.s[0] + (one ? delta : 0L) + (o.off[S] >> 5) + kw / 32;
+  return ((o.ok >> S) & 1u) ? *(const uint32_t*)p : 0u;
+}
+
+// the word of part p (row p & 3 of A for p < 4, of B after); p is the same for the
+// whole workgroup, and the branches keep every register index a constant (a
+// runtime index into the row offsets put them in scratch memory)
+MOE_DEV uint32_t mx_sword(const MxOp& A, const MxOp& B, int p, long kw) {
+  switch (p) {
+    case 0: return mx_sword_of<0>(A, kw);
+    case 1: return mx_sword_of<1>(A, kw);
+    case 2: return mx_sword_of<2>(A, kw);
+    case 3: return mx_sword_of<3>(A, kw);
+    case 4: return mx_sword_of<0>(B, kw);
+    case 5: return mx_sword_of<1>(B, kw);
+    case 6: return mx_sword_of<2>(B, kw);
+    default: return mx_sword_of<3>(B, kw);
+  }
+}
+
+MOE_DEV void mx_sput(char* buf, int p, uint32_t w) {
+  const int t = threadIdx.x;
+  *(uint32_t*)(buf + 4 * (256 * (t & 7) + (t >> 3) + 32 * (p & 3) + (p >= 4 ? 128 : 0))) = w;
+}
+
+// the direct form: this lane's words of its fragment rows at K offset koff, blocks
+// at or past kend zero (single-source operands)
+MOE_DEV void mx_load_words(const MxOp& o, long koff, uint32_t (&sw)[2]) {
   const long nb = (o.kend - koff) / 32;
   const uint32_t keep = nb >= 4 ? 0xffffffffu : (nb <= 0 ? 0u : (1u << (8 * nb)) - 1u);
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const uint8_t* b = (hi || ((o.sel >> (4 + q)) & 1u)) ? o.s[1] : o.s[0];
-    sw[q] = ((o.ok >> (4 + q)) & 1u) ? *(const uint32_t*)(b + o.soff[q] + koff / 32) & keep : 0u;
-  }
+  for (int q = 0; q < 2; ++q)
+    sw[q] = ((o.ok >> (4 + q)) & 1u) ? *(const uint32_t*)(o.s[0] + o.soff[q] + koff / 32) & keep
+                                     : 0u;
 }
 
 MOE_DEV void mx_store(char* t, const uint4 (&r)[4]) {
@@ -120,9 +174,14 @@ struct KLinear {
 };
 
 // Main loop: two LDS stages and one register stage (tile kt + 1 is loaded while
-// tile kt is multiplied); scale words travel with their data, sX with the register
-// stage and cX with the LDS stage being multiplied.
-template <class KM>
+// tile kt is multiplied), and two scale group buffers after the stages (group G,
+// tiles 8 G .. 8 G + 7, read from buffer G mod 2 and written during the tiles of
+// group G - 1; the words of tiles past the last one are loaded but unused).  `lds`
+// holds MX_LDS bytes.  The weight gradients' K loops are short (an expert's tokens,
+// mostly one or two tiles), where a group load costs more than it saves: they load
+// each tile's words for the fragment rows directly (LDS_SCALES = false; `lds` then
+// holds LDS_BYTES).
+template <bool LDS_SCALES = true, class KM>
 MOE_DEV void gemm_main_mx(char* lds, const MxOp& A, const MxOp& B, const KM& km, int nk,
                           f32x16_t (&acc)[2][2], int arow, const int (&brow)[2], int lane) {
 #pragma unroll
@@ -132,30 +191,77 @@ MOE_DEV void gemm_main_mx(char* lds, const MxOp& A, const MxOp& B, const KM& km,
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   if (nk <= 0) return;
-  // two LDS stages, one register stage: tile kt + 1 is loaded into registers
-  // while tile kt is multiplied, then stored into the other LDS stage
+  if constexpr (!LDS_SCALES) {
+    uint4 ra[4], rb[4];
+    uint32_t sa[2], sb[2], ca[2], cb[2];
+    mx_load(A, km(0), ra);
+    mx_load(B, km(0), rb);
+    mx_load_words(A, km(0), ca);
+    mx_load_words(B, km(0), cb);
+    mx_store(lds, ra);
+    mx_store(lds + TILEB, rb);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      char* cur = lds + (kt & 1) * 2 * TILEB;
+      char* nxt = lds + ((kt + 1) & 1) * 2 * TILEB;
+      const bool more = kt + 1 < nk;
+      if (more) {
+        mx_load(A, km(kt + 1), ra);
+        mx_load(B, km(kt + 1), rb);
+        mx_load_words(A, km(kt + 1), sa);
+        mx_load_words(B, km(kt + 1), sb);
+      }
+      mma_tile_mx(cur, cur + TILEB, ca, cb, acc, arow, brow, lane);
+      if (more) {
+        mx_store(nxt, ra);
+        mx_store(nxt + TILEB, rb);
+        ca[0] = sa[0]; ca[1] = sa[1]; cb[0] = sb[0]; cb[1] = sb[1];
+      }
+      __syncthreads();
+    }
+    return;
+  }
+  char* const sg = lds + LDS_BYTES;
+  const int tj = threadIdx.x & 7, l = lane & 31;
   uint4 ra[4], rb[4];
-  uint32_t sa[2], sb[2], ca[2], cb[2];
-  mx_load(A, km(0), ra, sa);
-  mx_load(B, km(0), rb, sb);
+  mx_load(A, km(0), ra);
+  mx_load(B, km(0), rb);
+  uint32_t w0[MX_SG];  // group 0; only the words of tiles that exist (short K loops)
+#pragma unroll
+  for (int p = 0; p < MX_SG; ++p) w0[p] = tj < nk ? mx_sword(A, B, p, km(tj)) : 0u;
   mx_store(lds, ra);
   mx_store(lds + TILEB, rb);
-  ca[0] = sa[0]; ca[1] = sa[1]; cb[0] = sb[0]; cb[1] = sb[1];
+#pragma unroll
+  for (int p = 0; p < MX_SG; ++p) mx_sput(sg, p, w0[p]);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     char* cur = lds + (kt & 1) * 2 * TILEB;
     char* nxt = lds + ((kt + 1) & 1) * 2 * TILEB;
     const bool more = kt + 1 < nk;
     if (more) {
-      mx_load(A, km(kt + 1), ra, sa);
-      mx_load(B, km(kt + 1), rb, sb);
+      mx_load(A, km(kt + 1), ra);
+      mx_load(B, km(kt + 1), rb);
+    }
+    const int p = kt & 7, g1 = (kt >> 3) + 1;
+    const bool next = MX_SG * g1 < nk;  // a next group exists
+    const uint32_t w = next ? mx_sword(A, B, p, km(MX_SG * g1 + tj)) : 0u;
+    // this lane's words of tile kt: fragment rows arow + 32 q + l (A), brow[q] + l (B);
+    // blocks at or past kend zero
+    const char* gb = sg + ((kt >> 3) & 1) * MX_SGB + 4 * 256 * p;
+    const long nb = (A.kend - km(kt)) / 32;
+    const uint32_t keep = nb >= 4 ? 0xffffffffu : (nb <= 0 ? 0u : (1u << (8 * nb)) - 1u);
+    uint32_t ca[2], cb[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      ca[q] = *(const uint32_t*)(gb + 4 * (arow + 32 * q + l)) & keep;
+      cb[q] = *(const uint32_t*)(gb + 4 * (128 + brow[q] + l)) & keep;
     }
     mma_tile_mx(cur, cur + TILEB, ca, cb, acc, arow, brow, lane);
     if (more) {
       mx_store(nxt, ra);
       mx_store(nxt + TILEB, rb);
-      ca[0] = sa[0]; ca[1] = sa[1]; cb[0] = sb[0]; cb[1] = sb[1];
     }
+    if (next) mx_sput(sg + (g1 & 1) * MX_SGB, p, w);  // never the buffer being read
     __syncthreads();
   }
 }
@@ -184,7 +290,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_up_swiglu_mx(
     const uint8_t* __restrict__ wg8, const uint8_t* __restrict__ wgs,
     const uint8_t* __restrict__ wu8, const uint8_t* __restrict__ wus, int H, int I,
     float* __restrict__ Z, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds[MX_LDS];
   RowTile t;
   int nt;
   if (!rows_tile(g, I / 64, t, nt)) return;
@@ -211,17 +317,8 @@ __global__ __launch_bounds__(NTHR, 2) void k_up_swiglu_mx(
     B.off[s] = (uint32_t)((rr & 63) * H);
     B.sel |= (uint32_t)(rr >= 64) << s;
   }
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int r = t.row0 + arow + 32 * q + (lane & 31);
-    const bool ok = r < t.row_end;
-    A.ok |= (uint32_t)ok << (4 + q);
-    A.soff[q] = (uint32_t)((ok ? r : t.row0) * HS);
-    const int n = brow[q] + (lane & 31);
-    B.soff[q] = (uint32_t)((n & 63) * HS);
-    B.sel |= (uint32_t)(n >= 64) << (4 + q);
-  }
   f32x16_t acc[2][2];
+  A.klen = B.klen = H;
   gemm_main_mx(lds, A, B, KLinear(), H / MX_BK, acc, arow, brow, lane);
   float* C = (float*)lds;
   stage_acc(C, acc, arow, brow, lane);
@@ -253,7 +350,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_down_mx(GroupInfo g, const uint8_t*
                                                      const uint8_t* __restrict__ wd8,
                                                      const uint8_t* __restrict__ wds, int H, int I,
                                                      bf16_t* __restrict__ Y) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds[MX_LDS];
   RowTile t;
   int nt;
   if (!rows_tile(g, H / TN, t, nt)) return;
@@ -277,15 +374,8 @@ __global__ __launch_bounds__(NTHR, 2) void k_down_mx(GroupInfo g, const uint8_t*
     A.off[s] = (uint32_t)((ok ? r : t.row0) * I);
     B.off[s] = (uint32_t)(rr * I);
   }
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int r = t.row0 + arow + 32 * q + (lane & 31);
-    const bool ok = r < t.row_end;
-    A.ok |= (uint32_t)ok << (4 + q);
-    A.soff[q] = (uint32_t)((ok ? r : t.row0) * IS);
-    B.soff[q] = (uint32_t)((brow[q] + (lane & 31)) * IS);
-  }
   f32x16_t acc[2][2];
+  A.klen = B.klen = I;
   gemm_main_mx(lds, A, B, KLinear(), I / MX_BK, acc, arow, brow, lane);
   float* C = (float*)lds;
   stage_acc(C, acc, arow, brow, lane);
@@ -304,7 +394,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_dgrad_down_mx(
     const float* __restrict__ Z, const float* __restrict__ topk_w, int H, int I, int k,
     float* __restrict__ dZ, uint8_t* __restrict__ dZ8, uint8_t* __restrict__ dZs,
     float* __restrict__ gh, float* __restrict__ dgp) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds[MX_LDS];
   RowTile t;
   int nt;
   if (!rows_tile(g, I / TN, t, nt)) return;
@@ -328,15 +418,8 @@ __global__ __launch_bounds__(NTHR, 2) void k_dgrad_down_mx(
     A.off[s] = (uint32_t)((ok ? r : t.row0) * H);
     B.off[s] = (uint32_t)(rr * H);
   }
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int r = t.row0 + arow + 32 * q + (lane & 31);
-    const bool ok = r < t.row_end;
-    A.ok |= (uint32_t)ok << (4 + q);
-    A.soff[q] = (uint32_t)((ok ? r : t.row0) * HS);
-    B.soff[q] = (uint32_t)((brow[q] + (lane & 31)) * HS);
-  }
   f32x16_t acc[2][2];
+  A.klen = B.klen = H;
   gemm_main_mx(lds, A, B, KLinear(), H / MX_BK, acc, arow, brow, lane);
   float* C = (float*)lds;
   stage_acc(C, acc, arow, brow, lane);
@@ -392,11 +475,11 @@ __global__ __launch_bounds__(NTHR, 2) void k_dgrad_up_mx(
     const uint8_t* __restrict__ wgT8, const uint8_t* __restrict__ wgTs,
     const uint8_t* __restrict__ wuT8, const uint8_t* __restrict__ wuTs, int H, int I,
     bf16_t* __restrict__ dX) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds[MX_LDS];
   RowTile t;
   int nt;
   if (!rows_tile(g, H / TN, t, nt)) return;
-  const int n0 = nt * TN, lane = threadIdx.x & 63, IS = I / 32, S2 = (2 * I) / 32;
+  const int n0 = nt * TN, lane = threadIdx.x & 63, IS = I / 32;
   int arow, brow[2];
   wave_coords(arow, brow, false);
   MxOp A, B;
@@ -419,15 +502,8 @@ __global__ __launch_bounds__(NTHR, 2) void k_dgrad_up_mx(
     A.off[s] = (uint32_t)((ok ? r : t.row0) * (2 * I));
     B.off[s] = (uint32_t)(rr * I);
   }
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int r = t.row0 + arow + 32 * q + (lane & 31);
-    const bool ok = r < t.row_end;
-    A.ok |= (uint32_t)ok << (4 + q);
-    A.soff[q] = (uint32_t)((ok ? r : t.row0) * S2);
-    B.soff[q] = (uint32_t)((brow[q] + (lane & 31)) * IS);
-  }
   f32x16_t acc[2][2];
+  A.klen = B.klen = 2 * I;
   gemm_main_mx(lds, A, B, KLinear(), (2 * I) / MX_BK, acc, arow, brow, lane);
   float* C = (float*)lds;
   stage_acc(C, acc, arow, brow, lane);
@@ -500,13 +576,13 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_mx(MbPlans mp, int E, bool m_
     const int rr = (threadIdx.x >> 3) + 32 * s;
     oa.off[s] = ob.off[s] = (uint32_t)(rr * Kp);
   }
+  f32x16_t acc[2][2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     oa.soff[q] = (uint32_t)((arow + 32 * q + (lane & 31)) * KS);
     ob.soff[q] = (uint32_t)((brow[q] + (lane & 31)) * KS);
   }
-  f32x16_t acc[2][2];
-  gemm_main_mx(lds, oa, ob, km, nk, acc, arow, brow, lane);
+  gemm_main_mx<false>(lds, oa, ob, km, nk, acc, arow, brow, lane);
   float* C = (float*)lds;
   stage_acc(C, acc, arow, brow, lane);
   __syncthreads();
