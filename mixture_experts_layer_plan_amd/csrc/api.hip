@@ -468,8 +468,9 @@ MxFwdWs mx_fwd_ws(const moe_shape* s) {
   L.hq = c.take(R * I);
   L.hs = c.take(R * I / 32);
   L.Y = c.take(R * H * 2);
-  L.hs_sh = c.take(Tm * s->I_shared * 2);
-  L.ys = c.take(s->I_shared ? Tm * H * 2 : 0);
+  // the shared expert runs once over all T tokens: h_s and its output for every token
+  L.hs_sh = c.take((size_t)s->T * s->I_shared * 2);
+  L.ys = c.take(s->I_shared ? (size_t)s->T * H * 2 : 0);
   // with MOE_REPLAY: Z of the minibatches before the last (not kept)
   L.Zr = c.take(mx_replay(s) ? R * 2 * I * sizeof(float) : 0);
   L.total = c.off;
@@ -578,6 +579,17 @@ moe_status forward_mx_impl(const moe_shape* s, const void* plan, const void* x,
   const MxSaved S = mx_saved_layout(s);
   const int H = s->H, I = s->I, k = s->k, nmb = n_minibatches(s), Tmb = minibatch_tokens(s);
   const uint8_t* q = (const uint8_t*)wq;
+  // the shared expert (bf16, dense, per token) once over all tokens: 256-row tiles of
+  // the whole batch fill the chip where a 2048-token minibatch gives 128 workgroups
+  const bf16_t_host* ys_all = nullptr;
+  if (s->I_shared) {
+    const GroupInfo gs = dense(s->T);
+    MOE_TRY(launch_gemm_up_swiglu(1, gs, x, sg, su, H, s->I_shared, at<float>(saved, S.Zs),
+                                  at<char>(ws, W.hs_sh), st));
+    MOE_TRY(launch_gemm_down(1, gs, at<char>(ws, W.hs_sh), sd, H, s->I_shared,
+                             at<char>(ws, W.ys), st));
+    ys_all = at<bf16_t_host>(ws, W.ys);
+  }
   for (int m = 0; m < nmb; ++m) {
     const int T_m = std::min(Tmb, s->T - m * Tmb);
     const PlanView v = view_plan(s, plan, m);
@@ -595,15 +607,7 @@ moe_status forward_mx_impl(const moe_shape* s, const void* plan, const void* x,
     MOE_TRY(launch_mx_up_swiglu(g, X8, Xs, q + Q.wg8, q + Q.wgs, q + Q.wu8, q + Q.wus, H, I, Z,
                                 hq, hs, st));
     MOE_TRY(launch_mx_down(g, hq, hs, q + Q.wd8, q + Q.wds, H, I, Y, st));
-    void* ys = nullptr;
-    if (s->I_shared) {
-      const GroupInfo gs = dense(T_m);
-      float* Zs = at<float>(saved, S.Zs) + (size_t)m * Tmb * 2 * s->I_shared;
-      void* hsh = at<char>(ws, W.hs_sh);
-      ys = at<char>(ws, W.ys);
-      MOE_TRY(launch_gemm_up_swiglu(1, gs, xm, sg, su, H, s->I_shared, Zs, hsh, st));
-      MOE_TRY(launch_gemm_down(1, gs, hsh, sd, H, s->I_shared, ys, st));
-    }
+    const void* ys = ys_all ? ys_all + (size_t)m * Tmb * H : nullptr;
     MOE_TRY(launch_combine_bf16(Y, v.pos, topk_w + (size_t)m * Tmb * k, ys,
                                 (bf16_t_host*)y + (size_t)m * Tmb * H, T_m, k, H, st));
   }
