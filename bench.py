@@ -95,9 +95,11 @@ def kernel_work(name, sh, counts_mb, es=2):
         "gemm_up_swiglu": lambda: (Et * 2 * I * H * es + R * H * es + R * 2 * I * 4 + R * I * es,
                                    2 * R * H * 2 * I),
         "gemm_down": lambda: (Et * H * I * es + R * I * es + R * H * es, 2 * R * I * H),
-        "gemm_forward_fused": lambda: tuple(a + b for a, b in zip(
-            kernel_work("gemm_up_swiglu", sh, counts_mb, es),
-            kernel_work("gemm_down", sh, counts_mb, es))),
+        # the persistent forward: routed and shared GEMM1 + SwiGLU and GEMM2, combine
+        "gemm_forward_fused": lambda: tuple(map(sum, zip(*(
+            kernel_work(n, sh, counts_mb, es)
+            for n in ("gemm_up_swiglu", "gemm_down", "combine_bf16")
+            + (("gemm_up_swiglu_shared", "gemm_down_shared") if Is else ()))))),
         "fused_zero": lambda: (0, 0),
         "gemm_dgrad_down": lambda: (Et * H * I * es + R * H * es + R * 2 * I * 4 + R * 3 * I * es
                                     + R * (I // 128) * 4, 2 * R * H * I),

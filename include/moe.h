@@ -89,11 +89,13 @@ typedef struct {
  * and fp32 calls (one minibatch). */
 #define MOE_REPLAY 1
 
-/* bf16 forward: the up/gate GEMM with SwiGLU and the down GEMM of the routed experts
- * run as one persistent kernel, each down-GEMM tile starting as soon as the
- * up/gate tiles of its rows have signalled through a device counter (stamatios.com,
- * § Granularidade do overlap and § Outras características: one kernel whose units
- * signal each other through counters).  Outputs are bitwise the same as without it.
+/* bf16 forward: everything after the plan (the up/gate GEMMs with SwiGLU and the
+ * down GEMMs of the routed and the shared experts, and the combine) runs as one
+ * persistent kernel; each down-GEMM tile starts as soon as the up/gate tiles of its
+ * rows have signalled through a device counter, and the combine once every down-GEMM
+ * tile has (stamatios.com, § Granularidade do overlap and § Outras características:
+ * one kernel whose units signal each other through counters).  Outputs are bitwise
+ * the same as without it.
  * A tile gives up waiting after about two seconds, which can only happen when other
  * work keeps the GPU's compute units from the kernel that long; bit 1 (value 2) of
  * the plan's err_flag is then set and y is not valid. */

@@ -223,7 +223,8 @@ FwdWs fwd_ws(const moe_shape* s, moe_dtype dt) {
   L.hs = c.take(T * s->I_shared * es);
   L.ys = c.take(s->I_shared ? T * s->H * es : 0);
   L.ready = c.take((s->flags & MOE_FUSED_FORWARD)
-                       ? sizeof(int32_t) * (plan_layout(s).max_wtiles + 8) : 0);
+                       ? sizeof(int32_t) * fused_counters(plan_layout(s).max_wtiles, s->T)
+                       : 0);
   L.total = c.off;
   return L;
 }
@@ -297,23 +298,45 @@ moe_status forward_impl(moe_dtype dt, const moe_shape* s, const void* plan, cons
   void* Z = at<char>(saved, S.Z);
   void* h = at<char>(ws, W.h);
   void* Y = at<char>(ws, W.Y);
-  hipError_t fe = hipErrorNotSupported;
+  void* ys = s->I_shared ? at<char>(ws, W.ys) : nullptr;
   if (d && (s->flags & MOE_FUSED_FORWARD)) {
     const moe_plan_layout P = plan_layout(s);
-    fe = launch_big_forward_fused(g, x, wg, wu, wd, s->H, s->I, Z, h, Y, at<int32_t>(ws, W.ready),
-                                  (int32_t*)((char*)const_cast<void*>(plan) + P.err_flag), st);
-    if (fe != hipSuccess && fe != hipErrorNotSupported) return MOE_E_HIP;
+    FusedForwardArgs a;
+    a.g = g;
+    a.gs = dense(s->T);
+    a.T = s->T;
+    a.k = s->k;
+    a.H = s->H;
+    a.I = s->I;
+    a.Is = s->I_shared;
+    a.x = x;
+    a.wg = wg;
+    a.wu = wu;
+    a.wd = wd;
+    a.sg = sg;
+    a.su = su;
+    a.sd = sd;
+    a.Z = Z;
+    a.h = h;
+    a.Y = Y;
+    a.Zs = s->I_shared ? at<char>(saved, S.Zs) : nullptr;
+    a.hs = s->I_shared ? at<char>(ws, W.hs) : nullptr;
+    a.ys = ys;
+    a.pos = v.pos;
+    a.w = topk_w;
+    a.y = y;
+    a.ready = at<int32_t>(ws, W.ready);
+    a.err = (int32_t*)((char*)const_cast<void*>(plan) + P.err_flag);
+    const hipError_t fe = launch_big_forward_fused(a, st);
+    if (fe == hipSuccess) return MOE_OK;
+    if (fe != hipErrorNotSupported) return MOE_E_HIP;
   }
-  if (fe == hipErrorNotSupported) {
-    MOE_TRY(launch_gemm_up_swiglu(d, g, x, wg, wu, s->H, s->I, Z, h, st));
-    MOE_TRY(launch_gemm_down(d, g, h, wd, s->H, s->I, Y, st));
-  }
-  void* ys = nullptr;
+  MOE_TRY(launch_gemm_up_swiglu(d, g, x, wg, wu, s->H, s->I, Z, h, st));
+  MOE_TRY(launch_gemm_down(d, g, h, wd, s->H, s->I, Y, st));
   if (s->I_shared) {
     const GroupInfo gs = dense(s->T);
     void* Zs = at<char>(saved, S.Zs);
     void* hs = at<char>(ws, W.hs);
-    ys = at<char>(ws, W.ys);
     MOE_TRY(launch_gemm_up_swiglu(d, gs, x, sg, su, s->H, s->I_shared, Zs, hs, st));
     MOE_TRY(launch_gemm_down(d, gs, hs, sd, s->H, s->I_shared, ys, st));
   }

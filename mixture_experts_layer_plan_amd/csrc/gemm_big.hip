@@ -45,11 +45,13 @@
 // is produced by one workgroup with a fixed K order: bitwise reproducible and
 // independent of the grid.
 #include "gemm_common.hpp"
+#include "move_common.hpp"
 
 namespace moe {
 namespace big {
 
 constexpr int TILE = 256;
+static_assert(TILE == 256, "fused_counters counts 256-row tiles");
 constexpr int NTH = 512;
 constexpr int STAGE = 32768;     // one operand, one 64-deep K tile
 constexpr int LDS = 4 * STAGE;   // two stages of (A, B)
@@ -502,6 +504,15 @@ MOE_DEV int out_row(int i, int v) {
   return 128 * (wave() >> 2) + 32 * i + 8 * (v >> 2) + 4 * (lane() >> 5) + (v & 3);
 }
 MOE_DEV int out_col(int j) { return 64 * (wave() & 3) + 32 * j + (lane() & 31); }
+// out_row(i, v) - out_row(0, 0), and out_row(0, 0) hidden from loop-invariant code
+// motion: in a persistent kernel the compiler otherwise computes the 64 row indices of
+// the epilogue once before the item loop and keeps (or spills) them across the GEMM
+MOE_DEV int out_row_rel(int i, int v) { return 32 * i + 8 * (v >> 2) + (v & 3); }
+MOE_DEV int out_row_base() {
+  int r = out_row(0, 0);
+  asm volatile("" : "+v"(r));
+  return r;
+}
 
 // Leading A blocks of this wavefront with a row below `rows`, B blocks with a
 // column below `cols`.
@@ -589,11 +600,12 @@ MOE_DEV void up_swiglu_tile(char* lds, const GroupInfo& g, const Tile& t, int nt
   Acc acc;
   main_loop_rows(lds, A, B, H / 64, t.row_end - t.row0, blocks_a(t.row_end - t.row0), 2, acc);
   const int i = 128 * nt + 32 * (wave() & 3) + (lane() & 31);
+  const int rb = t.row0 + out_row_base();
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int r = t.row0 + out_row(bi, v);
+      const int r = rb + out_row_rel(bi, v);
       if (r < t.row_end) {
         const float a = acc.c[bi][0][v], b = acc.c[bi][1][v];
         float* zr = Z + (size_t)r * (2 * I);
@@ -625,8 +637,9 @@ __global__ __launch_bounds__(NTH, 1) void k_up_swiglu(GroupInfo g, const bf16_t*
 // GEMM2: Y[r, n] = sum_i h[r, i] W_d[e][n, i] (grouped and the dense shared expert;
 // against the 128 x 128 kernel: 1.86 -> 1.81 ms at the skewed E = 256 workload,
 // 0.65 -> 0.55 ms at four experts of 4096 rows)
-// AUX: cache policy of the h loads
-template <int AUX = 0>
+// AUX: cache policy of the h loads; COHERENT_Y: Y is stored through to device scope
+// (for a consumer on another XCD)
+template <int AUX = 0, bool COHERENT_Y = false>
 MOE_DEV void down_tile(char* lds, const Tile& t, int nt, const bf16_t* __restrict__ h,
                        const bf16_t* __restrict__ wd, int H, int I, bf16_t* __restrict__ Y) {
   const int n0 = nt * TILE;
@@ -639,6 +652,7 @@ MOE_DEV void down_tile(char* lds, const Tile& t, int nt, const bf16_t* __restric
   Acc acc;
   main_loop_rows(lds, A, B, I / 64, t.row_end - t.row0, blocks_a(t.row_end - t.row0),
                  blocks_b(H - n0), acc);
+  const int rb = t.row0 + out_row_base();
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
@@ -647,8 +661,16 @@ MOE_DEV void down_tile(char* lds, const Tile& t, int nt, const bf16_t* __restric
       if (n < H)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int r = t.row0 + out_row(bi, v);
-          if (r < t.row_end) Y[(size_t)r * H + n] = f32_to_bf16(acc.c[bi][bj][v]);
+          const int r = rb + out_row_rel(bi, v);
+          if (r < t.row_end) {
+            const bf16_t yv = f32_to_bf16(acc.c[bi][bj][v]);
+            if (COHERENT_Y)
+              __hip_atomic_store((uint16_t*)(Y + (size_t)r * H + n),
+                                 __builtin_bit_cast(uint16_t, yv), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+            else
+              Y[(size_t)r * H + n] = yv;
+          }
         }
     }
 }
@@ -663,82 +685,161 @@ __global__ __launch_bounds__(NTH, 1) void k_down(GroupInfo g, const bf16_t* __re
   down_tile(lds, t, nt, h, wd, H, I, Y);
 }
 
-// ----------------------------------------------- forward GEMMs in one launch
-// GEMM1 + SwiGLU and GEMM2 of the routed experts as one persistent kernel, the
-// producer / consumer form of the pages' megakernel on one GPU (stamatios.com,
-// "Cursor abre código de megakernel MoE para GPUs NVL72", § Granularidade do overlap:
-// units signal each other through local counters; § Outras características: one
-// kernel).  The work items are the GEMM1 pairs (in the order and XCD dealing of
-// k_up_swiglu) followed by the GEMM2 pairs (those of k_down), item q on XCD q mod 8
-// as in the separate launches; the workgroups of one XCD (workgroup b runs on XCD
-// b mod 8) take that XCD's items in order from a counter, so that work balances
-// as it does when the dispatcher hands out a launch's workgroups.  A GEMM1 pair
-// stores h with device-coherent stores (written through to the device's coherence
-// point, not left in its XCD's L2), waits for them, and adds one to ready[row
-// tile]; a GEMM2 pair waits until its row tile's counter has all I / 128 column
-// tiles and then reads h with device-coherent loads (no stale line of its own
+// ------------------------------------------------ the forward in one launch
+// GEMM1 + SwiGLU and GEMM2 of the routed and the shared experts and the combine as
+// one persistent kernel, the producer / consumer form of the pages' megakernel on one
+// GPU (stamatios.com, "Cursor abre código de megakernel MoE para GPUs NVL72",
+// § Granularidade do overlap: units signal each other through local counters;
+// § Outras características: one kernel).  The work items, in order, are the routed
+// GEMM1 pairs (in the order and XCD dealing of k_up_swiglu), the shared expert's
+// GEMM1 pairs, the routed GEMM2 pairs (those of k_down), the shared GEMM2 pairs and
+// the combine items (FUSED_CMB_TOKENS tokens each); item q goes to XCD q mod 8 as
+// in the separate launches, and the workgroups of one XCD (workgroup b runs on XCD
+// b mod 8) take that XCD's items in order from a counter, so that work balances as
+// it does when the dispatcher hands out a launch's workgroups.
+//   A GEMM1 pair stores h with device-coherent stores (written through to the
+// device's coherence point, not left in its XCD's L2), waits for them, and adds one
+// to its row tile's counter; a GEMM2 pair waits until that counter has all I / 128
+// column tiles and then reads h with device-coherent loads (no stale line of its own
 // XCD's L2; measured on MI355X against an acquire / release pair, which invalidates
-// and writes back the whole L2: 5.08 -> 4.96 ms before the queues).  Each XCD's
-// queue hands out all its GEMM1 items before any GEMM2 item and GEMM1 items never
-// wait, so every wait ends once the workgroups holding the producers run.  A wait gives up after about two seconds (err bit 2:
-// possible only if other work keeps CUs from this grid that long); the pair then
-// reads whatever h holds.  The arithmetic of every tile is that of the two kernels.
+// and writes back the whole L2: 5.08 -> 4.96 ms before the queues).  A GEMM2 pair
+// stores Y the same way and adds one to `done`; a combine item waits until `done`
+// holds every GEMM2 pair, then reads Y and the shared rows at device scope.  Each
+// XCD's queue hands out all its GEMM1 items before any GEMM2 item and all those
+// before any combine item, and GEMM1 items never wait, so every wait ends once the
+// workgroups holding the producers run.  A wait gives up after about two seconds
+// (err bit 2: possible only if other work keeps CUs from this grid that long); the
+// item then reads whatever its input holds.  The arithmetic of every tile and chunk
+// is that of the separate kernels, so the outputs are bitwise theirs.
 struct FusedFwd {
-  GroupInfo g;
+  GroupInfo g;      // routed rows (wide-tile list)
+  GroupInfo gs;     // the shared expert: dense over the T tokens
   const bf16_t* x;
   const bf16_t* wg;
   const bf16_t* wu;
   const bf16_t* wd;
-  int H, I;
+  const bf16_t* sg;  // shared expert weights (NULL: none)
+  const bf16_t* su;
+  const bf16_t* sd;
+  int H, I, Is, T, k;
   float* Z;
   bf16_t* h;
   bf16_t* Y;
-  int32_t* ready;   // [max_wtiles], zero at launch
+  float* Zs;
+  bf16_t* hs;
+  bf16_t* ys;
+  const int32_t* pos;   // [T, k] row of each (token, slot)
+  const float* w;       // [T, k] combine weights
+  bf16_t* y;            // [T, H] layer output
+  int32_t* ready;   // [max_wtiles] routed row-tile counters, zero at launch
+  int32_t* readys;  // [n_rts] shared row-tile counters, zero at launch
+  int32_t* done;    // [1] GEMM2 pairs finished, zero at launch
   int32_t* next;    // [8] per-XCD item counters, zero at launch
   int32_t* err;
-  int n1, n2;       // item counts of the two phases (virtual grids of the kernels)
+  // item counts of the phases (the virtual grids of the separate kernels), n_rts the
+  // shared expert's row tiles
+  int n1, n1s, n2, n2s, nc, n_rts;
 };
 
 constexpr int FUSED_SPIN_LIMIT = 1 << 20;  // waits of ~4096 cycles each
+constexpr int FUSED_CMB_TOKENS = 4;
 
-__global__ __launch_bounds__(NTH, 1) void k_forward_fused(FusedFwd p) {
+// thread 0 waits until *c >= target (bounded: err bit 2 on giving up); then the
+// workgroup goes on
+MOE_DEV void fused_wait(const int32_t* c, int target, int32_t* err) {
+  if (threadIdx.x == 0) {
+    int spins = 0;
+    while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if (++spins > FUSED_SPIN_LIMIT) {
+        __hip_atomic_fetch_or(err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(64);
+    }
+  }
+  __syncthreads();
+}
+
+// thread 0 claims the workgroup's next item of queue `next` (its index lands in
+// `claimed`); then every lane's coherent stores have completed, then one count on c
+// for the workgroup.  The claim goes out first so that its round trip overlaps the
+// wait for the stores.
+MOE_DEV void fused_signal(int32_t* c, int32_t* next, int& claimed) {
+  if (threadIdx.x == 0)
+    claimed = __hip_atomic_fetch_add(next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The launch's fields are read through a pointer that an empty asm statement hides
+// from the compiler at every item, so that each phase loads the few it uses from the
+// kernel arguments instead of keeping all of them in scalar registers across the loop
+// (with them held, the kernel spilled scalar registers into vector registers).
+__global__ __launch_bounds__(NTH, 1) void k_forward_fused(FusedFwd arg) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_ROWS];
   int* s_item = (int*)lds;  // LDS is free between items
-  const int nt1 = p.I / 128, nt2 = (p.H + TILE - 1) / TILE, x = blockIdx.x % N_XCD;
+  // the launch's only argument, at the start of the kernel-argument segment (taking
+  // arg's address would copy it to private memory)
+  const FusedFwd* pa = (const FusedFwd*)__builtin_amdgcn_kernarg_segment_ptr();
+  const int x = blockIdx.x % N_XCD;
+  int claimed = -1;  // thread 0: the next item, if already claimed
   for (;;) {
-    // next item of this XCD's queue (items x, x + 8, ... in order)
-    if (threadIdx.x == 0)
-      *s_item = __hip_atomic_fetch_add(p.next + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const FusedFwd* pp = pa;
+    asm volatile("" : "+s"(pp));
+    const FusedFwd& p = *pp;
+    // next item of this XCD's queue (items x, x + 8, ... in order), claimed here or
+    // already at the end of the previous tile
+    if (threadIdx.x == 0) {
+      if (claimed < 0)
+        claimed = __hip_atomic_fetch_add(p.next + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *s_item = claimed;
+      claimed = -1;
+    }
     __syncthreads();
     const int q = *s_item * N_XCD + x;
     __syncthreads();  // read by every thread before the tile overwrites the LDS
-    if (q >= p.n1 + p.n2) break;
+    const int q1s = p.n1, q2 = q1s + p.n1s, q2s = q2 + p.n2, qc = q2s + p.n2s;
+    if (q >= qc + p.nc) break;
+    const int nt2 = (p.H + TILE - 1) / TILE;
     Tile t;
     int nt;
-    if (q < p.n1) {
-      if (!row_tile_at<true>(p.g, nt1, q, t, nt)) continue;
-      up_swiglu_tile<true>(lds, p.g, t, nt, p.x, p.wg, p.wu, p.H, p.I, p.Z, p.h);
-      // every lane's h stores have reached device scope, then one count for the
-      // workgroup
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (threadIdx.x == 0)
-        __hip_atomic_fetch_add(p.ready + t.mt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // routed and shared items of one GEMM share one inlined tile body (two bodies
+    // per GEMM left the routed tiles 5% slower); the operands are picked per item
+    if (q < q2) {
+      const bool sh = q >= q1s;
+      const GroupInfo& g = sh ? p.gs : p.g;
+      const int I = sh ? p.Is : p.I;
+      if (!row_tile_at<true>(g, I / 128, sh ? q - q1s : q, t, nt)) continue;
+      up_swiglu_tile<true>(lds, g, t, nt, p.x, sh ? p.sg : p.wg, sh ? p.su : p.wu, p.H, I,
+                           sh ? p.Zs : p.Z, sh ? p.hs : p.h);
+      fused_signal((sh ? p.readys : p.ready) + t.mt, p.next + x, claimed);
+    } else if (q < qc) {
+      const bool sh = q >= q2s;
+      const GroupInfo& g = sh ? p.gs : p.g;
+      const int I = sh ? p.Is : p.I;
+      if (!row_tile_at<false>(g, nt2, sh ? q - q2s : q - q2, t, nt)) continue;
+      fused_wait((sh ? p.readys : p.ready) + t.mt, I / 128, p.err);
+      down_tile<CPOL_DEVICE, true>(lds, t, nt, sh ? p.hs : p.h, sh ? p.sd : p.wd, p.H, I,
+                                   sh ? p.ys : p.Y);
+      fused_signal(p.done, p.next + x, claimed);
     } else {
-      if (!row_tile_at<false>(p.g, nt2, q - p.n1, t, nt)) continue;
-      if (threadIdx.x == 0) {
-        int spins = 0;
-        while (__hip_atomic_load(p.ready + t.mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-               nt1) {
-          if (++spins > FUSED_SPIN_LIMIT) {
-            __hip_atomic_fetch_or(p.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(64);
-        }
+      // every routed and shared GEMM2 pair: n_wtiles x nt2 + n_rts x nt2
+      fused_wait(p.done, (p.g.n_wtiles[0] + p.n_rts) * nt2, p.err);
+      const int rc = p.H / 8, sl = (rc + 63) / 64, t0 = (q - qc) * FUSED_CMB_TOKENS;
+      const int ntok = min(FUSED_CMB_TOKENS, p.T - t0);
+      const uint4* Y = (const uint4*)p.Y;
+      const uint4* ys = (const uint4*)p.ys;
+      uint4* y = (uint4*)p.y;
+      // one wave per (token, 64 chunks): the token, and so its pos and w, are
+      // wave-uniform
+      for (int u = wave(); u < ntok * sl; u += NTH / 64) {
+        const int tk = t0 + u / sl, c = (u % sl) * 64 + lane();
+        if (c < rc)
+          combine_chunk<true, true>(Y, p.pos + (size_t)tk * p.k, p.w + (size_t)tk * p.k,
+                                    ys ? ys + (size_t)tk * rc : nullptr, y + (size_t)tk * rc,
+                                    p.k, rc, c);
       }
-      __syncthreads();
-      down_tile<CPOL_DEVICE>(lds, t, nt, p.h, p.wd, p.H, p.I, p.Y);
     }
   }
 }
@@ -1401,33 +1502,54 @@ hipError_t launch_big_up_swiglu(const GroupInfo& g, const void* x, const void* w
                         (float*)Z, (bf16_t*)h));
 }
 
-// GEMM1 + SwiGLU and GEMM2 in one persistent launch (k_forward_fused); `ready` holds
-// max_wtiles + 8 int32 counters (zeroed here by a small kernel), err the plan's err
-// flag.
-hipError_t launch_big_forward_fused(const GroupInfo& g, const void* x, const void* wg,
-                                    const void* wu, const void* wd, int H, int I, void* Z, void* h,
-                                    void* Y, int32_t* ready, int32_t* err, hipStream_t s) {
+// The bf16 forward after the plan in one persistent launch (k_forward_fused); the
+// counters (fused_counters(g.max_wtiles, T) int32) are zeroed here by a small kernel.
+hipError_t launch_big_forward_fused(const FusedForwardArgs& a, hipStream_t s) {
+  const GroupInfo& g = a.g;
   if (!g.wtiles || g.max_wtiles == 0) return hipErrorNotSupported;
-  const int n_cnt = g.max_wtiles + N_XCD;  // ready counters, then the queue counters
-  hipError_t e = MOE_LAUNCH("fused_zero", s,
-                            big::zero_i32_kernel<<<(n_cnt + 255) / 256, 256, 0, s>>>(ready, n_cnt));
+  if (a.T <= 0) return hipSuccess;
+  const int n_rts = a.Is ? (a.T + big::TILE - 1) / big::TILE : 0;
+  const int n_cnt = fused_counters(g.max_wtiles, a.T);
+  hipError_t e = MOE_LAUNCH(
+      "fused_zero", s, big::zero_i32_kernel<<<(n_cnt + 255) / 256, 256, 0, s>>>(a.ready, n_cnt));
   if (e != hipSuccess) return e;
   big::FusedFwd p;
   p.g = g;
-  p.x = (const bf16_t*)x;
-  p.wg = (const bf16_t*)wg;
-  p.wu = (const bf16_t*)wu;
-  p.wd = (const bf16_t*)wd;
-  p.H = H;
-  p.I = I;
-  p.Z = (float*)Z;
-  p.h = (bf16_t*)h;
-  p.Y = (bf16_t*)Y;
-  p.ready = ready;
-  p.next = ready + g.max_wtiles;
-  p.err = err;
-  p.n1 = (int)big_row_grid((unsigned)g.max_wtiles * (I / 128));
-  p.n2 = g.max_wtiles * ((H + big::TILE - 1) / big::TILE);
+  p.gs = a.gs;
+  if (a.Is && (a.gs.wtiles || a.gs.dense_rows != a.T)) return hipErrorInvalidValue;
+  p.x = (const bf16_t*)a.x;
+  p.wg = (const bf16_t*)a.wg;
+  p.wu = (const bf16_t*)a.wu;
+  p.wd = (const bf16_t*)a.wd;
+  p.sg = (const bf16_t*)a.sg;
+  p.su = (const bf16_t*)a.su;
+  p.sd = (const bf16_t*)a.sd;
+  p.H = a.H;
+  p.I = a.I;
+  p.Is = a.Is;
+  p.T = a.T;
+  p.k = a.k;
+  p.Z = (float*)a.Z;
+  p.h = (bf16_t*)a.h;
+  p.Y = (bf16_t*)a.Y;
+  p.Zs = (float*)a.Zs;
+  p.hs = (bf16_t*)a.hs;
+  p.ys = a.Is ? (bf16_t*)a.ys : nullptr;
+  p.pos = a.pos;
+  p.w = a.w;
+  p.y = (bf16_t*)a.y;
+  p.ready = a.ready;
+  p.readys = a.ready + g.max_wtiles;
+  p.done = p.readys + n_rts;
+  p.next = p.done + 1;
+  p.err = a.err;
+  const int nt2 = (a.H + big::TILE - 1) / big::TILE;
+  p.n1 = (int)big_row_grid((unsigned)g.max_wtiles * (a.I / 128));
+  p.n1s = a.Is ? (int)big_row_grid((unsigned)n_rts * (a.Is / 128)) : 0;
+  p.n2 = g.max_wtiles * nt2;
+  p.n2s = n_rts * nt2;
+  p.nc = (a.T + big::FUSED_CMB_TOKENS - 1) / big::FUSED_CMB_TOKENS;
+  p.n_rts = n_rts;
   const int cus = device_cus();
   const unsigned grid = (unsigned)(cus >= N_XCD ? cus - cus % N_XCD : N_XCD);
   return MOE_LAUNCH("gemm_forward_fused", s, big::k_forward_fused<<<grid, big::NTH, 0, s>>>(p));

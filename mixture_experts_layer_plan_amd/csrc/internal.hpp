@@ -103,13 +103,26 @@ hipError_t launch_big_up_swiglu(const GroupInfo& g, const void* x, const void* w
                                 int H, int I, void* Z, void* h, hipStream_t s);
 hipError_t launch_big_down(const GroupInfo& g, const void* h, const void* wd, int H, int I,
                            void* Y, hipStream_t s);
-// GEMM1 + SwiGLU and GEMM2 of the routed experts in one persistent launch with
-// device-counter hand-off between them (ready: max_wtiles + 8 int32 of workspace; err:
-// the plan's err flag, bit 2 set if a wait gave up); hipErrorNotSupported without
-// the plan's wide-tile list
-hipError_t launch_big_forward_fused(const GroupInfo& g, const void* x, const void* wg,
-                                    const void* wu, const void* wd, int H, int I, void* Z, void* h,
-                                    void* Y, int32_t* ready, int32_t* err, hipStream_t s);
+// The bf16 forward after the plan in one persistent launch: GEMM1 + SwiGLU and GEMM2
+// of the routed and the shared experts and the combine, with device-counter hand-off
+// between them (gemm_big.hip); outputs bitwise those of the separate launches.
+struct FusedForwardArgs {
+  GroupInfo g;                      // routed rows; needs the plan's wide-tile list
+  GroupInfo gs;                     // the shared expert: dense over the T tokens
+  int T, k, H, I, Is;               // Is = 0: no shared expert (sg, su, sd, Zs, hs, ys unused)
+  const void *x, *wg, *wu, *wd;     // bf16 tokens and routed weights
+  const void *sg, *su, *sd;         // bf16 shared expert weights
+  void *Z, *h, *Y;                  // routed pre-activations (fp32), h and Y (bf16)
+  void *Zs, *hs, *ys;               // the shared expert's
+  const int32_t* pos;               // [T, k] plan inverse
+  const float* w;                   // [T, k] combine weights
+  void* y;                          // [T, H] bf16 output
+  int32_t* ready;                   // fused_counters(g.max_wtiles, T) int32 of workspace
+  int32_t* err;                     // the plan's err flag: bit 2 set if a wait gave up
+};
+inline int fused_counters(int max_wtiles, int T) { return max_wtiles + (T + 255) / 256 + 1 + 8; }
+// hipErrorNotSupported (nothing enqueued) without the plan's wide-tile list
+hipError_t launch_big_forward_fused(const FusedForwardArgs& a, hipStream_t s);
 // MXFP8 GEMM2 and dgrad-up on the 256 x 256 core (gemm_big.hip); hipErrorNotSupported
 // (nothing enqueued) unless H and I are multiples of 512 and the plan has its
 // wide-tile list, and the launch_mx_* entry points then use the 128 x 128 kernels

@@ -11,6 +11,7 @@
 // workgroup per destination row.
 #include "common.hpp"
 #include "internal.hpp"
+#include "move_common.hpp"
 
 namespace moe {
 
@@ -84,58 +85,9 @@ __global__ __launch_bounds__(CMB_THREADS) void combine_bf16_kernel(
   const int t = blockIdx.x / slices;
   const int c = (blockIdx.x - t * slices) * CMB_THREADS + threadIdx.x;
   if (c >= row_chunks) return;
-  // the token's slots and weights: wave-uniform reads of data no kernel of this
-  // launch writes, through the constant address space (scalar loads)
-  typedef const __attribute__((address_space(4))) int32_t* cpos_t;
-  typedef const __attribute__((address_space(4))) float* cw_t;
-  const cpos_t s_pos = (cpos_t)(pos + (size_t)t * k);
-  const cw_t s_w = WEIGHTED ? (cw_t)(w + (size_t)t * k) : nullptr;
-  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j0 = 0; j0 < k; j0 += 8) {
-    const bool last = j0 + 8 >= k;
-    int rr[8];
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) rr[jj] = s_pos[min(j0 + jj, k - 1)];  // issued together
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj)
-      if (j0 + jj >= k) rr[jj] = -1;
-    uint4 raw[8];
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj)  // each Y row is read once: bypass-friendly loads
-      raw[jj] = rr[jj] >= 0 ? __builtin_bit_cast(uint4, __builtin_nontemporal_load(
-                                  (const u32x4_t*)(Y + (size_t)rr[jj] * row_chunks + c)))
-                            : z;
-    const uint4 sh = shared && last ? shared[(size_t)t * row_chunks + c] : z;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int j = j0 + jj;
-      if (rr[jj] < 0) continue;
-      float v[8];
-      unpack8(raw[jj], v);
-      if (WEIGHTED) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(s_w[j], v[i], acc[i]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += v[i];
-      }
-    }
-    if (shared && last) {
-      float v[8];
-      unpack8(sh, v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += v[i];
-    }
-  }
-  if (shared && k == 0) {
-    float v[8];
-    unpack8(shared[(size_t)t * row_chunks + c], v);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += v[i];
-  }
-  __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, pack8(acc)),
-                              (u32x4_t*)(y + (size_t)t * row_chunks + c));
+  combine_chunk<WEIGHTED>(Y, pos + (size_t)t * k, WEIGHTED ? w + (size_t)t * k : nullptr,
+                          shared ? shared + (size_t)t * row_chunks : nullptr,
+                          y + (size_t)t * row_chunks, k, row_chunks, c);
 }
 
 template <bool WEIGHTED>

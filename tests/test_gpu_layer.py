@@ -30,10 +30,11 @@ SMALL = {
 }
 
 
-def gpu_run(shape: Shape, inp_dev: dict, backward=True):
+def gpu_run(shape: Shape, inp_dev: dict, backward=True, fused_forward=False):
     from mixture_experts_layer_plan_amd import LayerBuffers, run_layer
     b = LayerBuffers(shape.T, shape.H, shape.I, shape.E, shape.k, shape.I_shared,
-                     dtype=shape.dtype, backward=backward, router_gemm=shape.router == "gemm")
+                     dtype=shape.dtype, backward=backward, router_gemm=shape.router == "gemm",
+                     fused_forward=fused_forward)
     run_layer(b, inp_dev, backward=backward)
     torch.cuda.synchronize()
     return b
@@ -79,11 +80,11 @@ def test_layer_exact_row_counts(H):
     np.testing.assert_array_equal(np.bincount(c["topk_idx"].ravel(), minlength=shape.E), counts)
 
 
-def check_all_outputs(shape: Shape, inp: dict):
+def check_all_outputs(shape: Shape, inp: dict, fused_forward=False):
     """Run the layer forward + backward on the GPU and compare every output with
     the oracle; returns the oracle's forward cache."""
     kind = shape.dtype
-    b = gpu_run(shape, to_dev(inp))
+    b = gpu_run(shape, to_dev(inp), fused_forward=fused_forward)
     c = oracle.layer_forward(inp["x"], inp.get("logits"), shape.k, inp["w_gate"], inp["w_up"],
                              inp["w_down"], shared=shared_of(inp), w_router=inp.get("w_router"))
     g = oracle.layer_backward(c, inp["dy"])
@@ -112,6 +113,7 @@ def check_all_outputs(shape: Shape, inp: dict):
             check(getattr(b, n), g[n], kind, n)
     if shape.router == "gemm":
         check(b.dw_router, g["dw_router"], kind, "dw_router")
+    assert int(b.plan_views()["err_flag"].item()) == 0
     return c
 
 
@@ -150,12 +152,22 @@ def test_layer_bitwise_independent_of_persistent_grid(name):
     assert len(set(outs)) == 1, outs
 
 
+@pytest.mark.parametrize("name", ["skew_shared_bf16", "one_token_bf16", "hot_expert_bf16"])
+def test_fused_forward_small_all_outputs(name):
+    """MOE_FUSED_FORWARD (routed and shared expert GEMMs and the combine in one
+    persistent launch with counter hand-off) against the oracle, every output."""
+    shape = SMALL[name]
+    say(f"fused forward, layer {name}: {shape}")
+    inp = make_inputs(shape, seed=0, device="cpu", with_dy=True)
+    check_all_outputs(shape, inp, fused_forward=True)
+
+
 @pytest.mark.parametrize("name", ["hot_wgrad_bf16", "skew_shared_bf16", "ragged_bf16",
-                                  "hot_expert_bf16"])
+                                  "hot_expert_bf16", "one_token_bf16", "k_eq_E_bf16"])
 def test_fused_forward_bitwise_equal_separate_launches(name):
-    """MOE_FUSED_FORWARD (the two expert GEMMs in one persistent launch with counter
-    hand-off) gives bitwise the outputs of the two launches, backward included (the
-    saved pre-activations are the same), and leaves the plan's err flag at 0."""
+    """MOE_FUSED_FORWARD gives bitwise the outputs of the separate launches, backward
+    included (the saved pre-activations are the same), and leaves the plan's err flag
+    at 0."""
     from mixture_experts_layer_plan_amd import LayerBuffers, run_layer
     shape = SMALL[name]
     say(f"fused forward vs two launches: {name}")
@@ -171,10 +183,13 @@ def test_fused_forward_bitwise_equal_separate_launches(name):
     assert outs[0] == outs[1]
 
 
-def test_fused_forward_full_size_bitwise_equal():
+@pytest.mark.parametrize("name", ["kimi_bf16_fwd", "kimi_bf16_fwdbwd"])
+def test_fused_forward_full_size_bitwise_equal(name):
+    """At the full sizes (the second with the shared expert), forward only: y and
+    the saved pre-activations bitwise those of the separate launches, twice."""
     from mixture_experts_layer_plan_amd import LayerBuffers, run_layer
-    shape = CONFIGS["kimi_bf16_fwd"]
-    say("fused forward at full size: inputs on the device")
+    shape = CONFIGS[name]
+    say(f"fused forward at full size {name}: inputs on the device")
     inp = make_inputs(shape, seed=4, device="cuda", with_dy=False)
     ref = None
     for fused in (False, True, True):
