@@ -228,9 +228,9 @@ __global__ __launch_bounds__(NTHR, 2) void k_dgrad_up(GroupInfo g, const T* __re
 // a fourth is multiplied: a ring of 4 x 16 KiB (two MN-major operand tiles of 32 K
 // rows x 256 bytes each, the same swizzled layout as the register-staged tiles).
 // Against one register-staged 64-deep tile in flight this keeps 1.5x the bytes in
-// flight per workgroup.  K rows past the expert's segment read a 256-byte zero row
-// in device memory, so they add exactly zero and never leave the operands.
-__device__ __attribute__((aligned(16))) uint4 g_zero_krow[16];
+// flight per workgroup.  The loads go through a buffer resource whose range is the
+// expert's segment: K rows past it lie out of range and load as zeros, so they add
+// exactly zero and never leave the operands.
 
 namespace wdma {
 constexpr int BK = 32;          // K rows per stage
@@ -238,23 +238,19 @@ constexpr int OPB = BK * 256;   // bytes of one operand tile in a stage
 constexpr int STB = 2 * OPB;    // stage bytes
 static_assert(4 * STB == LDS_BYTES, "the ring fills the LDS of the staged C tile");
 
-typedef __attribute__((address_space(3))) void* lds_vptr;
-typedef const __attribute__((address_space(1))) void* gbl_vptr;
 
 // MN-major operand: K row k = row seg0 + k of a row-major bf16 matrix, columns
 // c0 .. c0 + 127.  Instruction q (0, 1) of wavefront w fills K rows 8 w + 4 q ..
 // + 3 of a stage: lane L brings K row r = 8 w + 4 q + L / 16 into physical chunk
 // L % 16, i.e. its logical chunk (L % 16) ^ mn_swz(r).
 struct Opnd {
-  const char* base;  // element (seg0, c0)
+  rsrc_t rs;         // element (seg0, c0); range: the segment's rows
   uint32_t ldb;      // row stride, bytes
-  int n;             // rows in the segment
   int r[2];
   uint32_t col[2];
   MOE_DEV void set(const bf16_t* b, size_t ld, int rows) {
-    base = (const char*)b;
     ldb = (uint32_t)(ld * 2);
-    n = rows;
+    rs = make_rsrc(b, (uint32_t)rows * ldb);
     const int w = threadIdx.x >> 6, L = threadIdx.x & 63;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -265,12 +261,9 @@ struct Opnd {
   MOE_DEV void issue(int kt, char* tile) const {
     const int w = threadIdx.x >> 6;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int t = kt * BK + r[q];
-      const char* src = t < n ? base + (size_t)t * ldb + col[q] : (const char*)g_zero_krow + col[q];
-      __builtin_amdgcn_global_load_lds((gbl_vptr)src, (lds_vptr)(tile + (8 * w + 4 * q) * 256), 16,
-                                       0, 0);
-    }
+    for (int q = 0; q < 2; ++q)  // K rows past the segment lie past the range: zeros
+      dma16_buf(rs, (uint32_t)(kt * BK + r[q]) * ldb + col[q], 0u,
+                tile + (8 * w + 4 * q) * 256);
   }
 };
 

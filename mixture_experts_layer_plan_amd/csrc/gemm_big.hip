@@ -68,19 +68,11 @@ MOE_DEV void dma16(const char* src, char* dst) {
 }
 constexpr int CPOL_DEVICE = 16;
 
-// The same load through a buffer resource (buffer_load_dwordx4 ... lds): the operand's
-// wave-uniform base in scalar registers, a 32-bit per-lane offset and a wave-uniform
-// scalar offset.  Measured on MI355X against the global_load_lds form, with this
-// core's K loop on a dense 4096 x 4096 x 7168 bf16 product: 229 -> 201 us (8192 x 4096
-// x 7168: 467 -> 414 us); the counters showed half the address-unit stall cycles.
-// The range covers 4 GiB from the base: offsets are 32-bit sums as before.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-MOE_DEV rsrc_t make_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, 0x00020000);
-}
+// The operand loaders below use the buffer-resource form of this load (dma16_buf,
+// gemm_common.hpp); dma16 is left for the scale bytes and the zero-row tails.
 template <int AUX = 0>
 MOE_DEV void dmab(rsrc_t r, uint32_t voff, uint32_t soff, char* dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)dst, 16, voff, soff, 0, AUX);
+  dma16_buf<AUX>(r, voff, soff, dst);
 }
 // the wavefront's index as a scalar (wave-uniform by construction)
 MOE_DEV int wave_s() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
@@ -1021,17 +1013,17 @@ __global__ __launch_bounds__(NTH, 1) void k_wgrad_hot(WgradArgs p) {
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 struct DmaKB {  // K-major byte rows at a fixed stride
-  const char* base;  // row 0, K byte 0 of this expert's range
+  rsrc_t r;          // row 0, K byte 0 of this expert's range
   uint32_t off;      // this lane's row for instruction 0, chunk included
   uint32_t step;     // 64 rows, bytes
   MOE_DEV void set(const uint8_t* b, size_t ld) {
-    base = (const char*)b;
+    r = make_rsrc(b);
     off = (uint32_t)(kmaj_row(0) * ld) + 16u * kmaj_chunk();
     step = (uint32_t)(64 * ld);
   }
   MOE_DEV void issue(int kt, char* st) const {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) dma16(base + (size_t)kt * 128 + off + s * step, kmaj_dst(st, s));
+    for (int s = 0; s < 4; ++s) dmab(r, off, (uint32_t)kt * 128u + s * step, kmaj_dst(st, s));
   }
 };
 
@@ -1282,11 +1274,11 @@ static_assert(4 * STAGE + 2 * MX_SBUF <= LDS_ROWS, "MX stages and scale groups f
 // tile inside an issued instruction read row 0 of the tile (their outputs are not
 // stored).
 struct MxDmaA {
-  const char* base;
+  rsrc_t r;
   uint32_t off[4];
   int n;
   MOE_DEV void set(const uint8_t* b, size_t ld, int rows) {
-    base = (const char*)b;
+    r = make_rsrc(b);
     n = (rows + 63) / 64;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -1297,28 +1289,29 @@ struct MxDmaA {
   MOE_DEV void issue(int kt, char* st) const {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      if (s < n) dma16(base + (size_t)kt * 128 + off[s], kmaj_dst(st, s));
+      if (s < n) dmab(r, off[s], (uint32_t)kt * 128u, kmaj_dst(st, s));
   }
 };
 
 // B: 256 weight rows at a fixed stride, K stages from kI on from a second matrix
-// (dgrad-up's W_u^T after W_g^T; base1 pre-offset by -128 kI bytes)
+// (dgrad-up's W_u^T after W_g^T)
 struct MxDmaB {
-  const char* base0;
-  const char* base1;
+  rsrc_t r0, r1;
   uint32_t off, step;
   int kI;
   MOE_DEV void set(const uint8_t* b0, const uint8_t* b1, size_t ld, int k_split) {
-    base0 = (const char*)b0;
-    base1 = (const char*)b1 - (size_t)k_split * 128;
+    r0 = make_rsrc(b0);
+    r1 = make_rsrc(b1);
     off = (uint32_t)(kmaj_row(0) * ld) + 16u * kmaj_chunk();
     step = (uint32_t)(64 * ld);
     kI = k_split;
   }
   MOE_DEV void issue(int kt, char* st) const {
-    const char* b = kt >= kI ? base1 : base0;
+    const bool hi = kt >= kI;
+    const rsrc_t r = hi ? r1 : r0;
+    const uint32_t k0 = (uint32_t)(hi ? kt - kI : kt) * 128u;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) dma16(b + (size_t)kt * 128 + off + s * step, kmaj_dst(st, s));
+    for (int s = 0; s < 4; ++s) dmab(r, off, k0 + s * step, kmaj_dst(st, s));
   }
 };
 
