@@ -63,14 +63,25 @@ MOE_DEV void mx_op_clear(MxOp& o) {
   o.klen = 0;
 }
 
+// Data loads through buffer resources over 2 GiB from each source base: the source of
+// row q (sel bit q, the same in every lane, or the second source from ksplit on) is
+// a scalar choice, and rows outside the operand (ok) or K bytes at or past kend take
+// an offset past the range, which loads zeros (MI355X: buffer loads issue faster than
+// 64-bit per-lane addresses; the 256 x 256 core's direct-to-LDS loads went 229 -> 201
+// us on a dense product).  Every source's offsets stay below 2 GiB.
+constexpr uint32_t MX_RANGE = 0x80000000u;
 MOE_DEV void mx_load(const MxOp& o, long koff, uint4 (&r)[4]) {
   const bool hi = koff >= o.ksplit;
   const int ch = (threadIdx.x & 7) * 16;
   const bool kin = koff + ch < o.kend;
+  const uint32_t sel = __builtin_amdgcn_readfirstlane(o.sel);
+  const rsrc_t r0 = make_rsrc(o.d[0], MX_RANGE), r1 = make_rsrc(o.d[1], MX_RANGE);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint8_t* b = (hi || ((o.sel >> q) & 1u)) ? o.d[1] : o.d[0];
-    r[q] = ((o.ok >> q) & 1u) && kin ? *(const uint4*)(b + o.off[q] + koff + ch) : zero4();
+    const uint32_t voff = ((o.ok >> q) & 1u) && kin ? o.off[q] + (uint32_t)ch : MX_RANGE;
+    r[q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         (hi || ((sel >> q) & 1u)) ? r1 : r0, voff,
+                                         (uint32_t)koff, 0));
   }
 }
 
