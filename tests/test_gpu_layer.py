@@ -206,6 +206,36 @@ def test_fused_forward_full_size_bitwise_equal(name):
         del b
 
 
+def test_fused_forward_reused_buffers_fresh_tokens():
+    """The fused forward run twice on the same buffers, the second time with every
+    token's x moved to the next token (same routing, so the same rows, but new h and Y
+    values in every row): bitwise the separate launches on the second input.  A GEMM2
+    tile or combine item that read a line of h, Y or the shared rows left in its XCD's
+    cache by the first launch would differ."""
+    from mixture_experts_layer_plan_amd import LayerBuffers, run_layer
+    shape = CONFIGS["kimi_bf16_fwdbwd"]
+    say("fused forward, reused buffers, fresh tokens: inputs on the device")
+    inp = make_inputs(shape, seed=6, device="cuda", with_dy=False)
+    inp2 = dict(inp)
+    inp2["x"] = torch.roll(inp["x"], 1, dims=0)
+    outs = []
+    for fused in (True, False):
+        say(f"fused = {fused}")
+        b = LayerBuffers(shape.T, shape.H, shape.I, shape.E, shape.k, shape.I_shared, "bf16",
+                         backward=False, fused_forward=fused)
+        if fused:
+            run_layer(b, inp, backward=False)
+            torch.cuda.synchronize()
+            y1 = b.y.clone()
+        run_layer(b, inp2, backward=False)
+        torch.cuda.synchronize()
+        assert int(b.plan_views()["err_flag"].item()) == 0
+        outs.append((b.y.clone(), b.saved.clone()))
+        del b
+    assert not torch.equal(y1, outs[0][0])
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
 # --------------------------------------------------------------- full sizes
 class ExpertCache:
     """fp64 host copies of single experts of a device weight stack, on demand."""
