@@ -748,6 +748,30 @@ struct FusedFwd {
   int n1, n1s, n2, n2s, nc, n_rts;
 };
 
+// A GroupInfo of the kernel arguments copied field by field from the constant address
+// space (each field a scalar load); the copy constructor does not bind to it.
+MOE_DEV GroupInfo group_from_args(const __attribute__((address_space(4))) GroupInfo& s) {
+  GroupInfo g;
+  g.tiles = s.tiles;
+  g.n_tiles = s.n_tiles;
+  g.offsets = s.offsets;
+  g.src_token = s.src_token;
+  g.src_slot = s.src_slot;
+  g.active = s.active;
+  g.n_active = s.n_active;
+  g.counts = s.counts;
+  g.wtiles = s.wtiles;
+  g.n_wtiles = s.n_wtiles;
+  g.max_tiles = s.max_tiles;
+  g.max_wtiles = s.max_wtiles;
+  g.dense_rows = s.dense_rows;
+  g.E = s.E;
+  g.hot_rows = s.hot_rows;
+  return g;
+}
+static_assert(sizeof(GroupInfo) == 10 * sizeof(void*) + 5 * sizeof(int) + 4,
+              "group_from_args copies every field of GroupInfo");
+
 constexpr int FUSED_SPIN_LIMIT = 1 << 20;  // waits of ~4096 cycles each
 constexpr int FUSED_CMB_TOKENS = 4;
 
@@ -787,14 +811,18 @@ __global__ __launch_bounds__(NTH, 1) void k_forward_fused(FusedFwd arg) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_ROWS];
   int* s_item = (int*)lds;  // LDS is free between items
   // the launch's only argument, at the start of the kernel-argument segment (taking
-  // arg's address would copy it to private memory)
-  const FusedFwd* pa = (const FusedFwd*)__builtin_amdgcn_kernarg_segment_ptr();
+  // arg's address would copy it to private memory), read through the constant address
+  // space: its fields load as scalars (through a generic pointer they came back in
+  // vector registers, and every buffer resource built from them was wrapped in a loop
+  // over distinct values)
+  typedef const __attribute__((address_space(4))) FusedFwd kfused_t;
+  kfused_t* pa = (kfused_t*)__builtin_amdgcn_kernarg_segment_ptr();
   const int x = blockIdx.x % N_XCD;
   int claimed = -1;  // thread 0: the next item, if already claimed
   for (;;) {
-    const FusedFwd* pp = pa;
+    kfused_t* pp = pa;
     asm volatile("" : "+s"(pp));
-    const FusedFwd& p = *pp;
+    kfused_t& p = *pp;
     // next item of this XCD's queue (items x, x + 8, ... in order), claimed here or
     // already at the end of the previous tile
     if (threadIdx.x == 0) {
@@ -804,28 +832,42 @@ __global__ __launch_bounds__(NTH, 1) void k_forward_fused(FusedFwd arg) {
       claimed = -1;
     }
     __syncthreads();
-    const int q = *s_item * N_XCD + x;
+    // the same in every lane: scalar, so that the tile's operand bases (buffer
+    // resources) are scalar too
+    const int q = __builtin_amdgcn_readfirstlane(*s_item * N_XCD + x);
     __syncthreads();  // read by every thread before the tile overwrites the LDS
     const int q1s = p.n1, q2 = q1s + p.n1s, q2s = q2 + p.n2, qc = q2s + p.n2s;
     if (q >= qc + p.nc) break;
     const int nt2 = (p.H + TILE - 1) / TILE;
     Tile t;
     int nt;
+    // the tile's coordinates as scalars (they come from loads of the tile list, which
+    // the compiler cannot take as uniform here: with them in vector registers every
+    // buffer load was wrapped in a loop over distinct resources)
+    auto uniform = [](Tile& tt, int& n) {
+      tt.e = __builtin_amdgcn_readfirstlane(tt.e);
+      tt.mt = __builtin_amdgcn_readfirstlane(tt.mt);
+      tt.row0 = __builtin_amdgcn_readfirstlane(tt.row0);
+      tt.row_end = __builtin_amdgcn_readfirstlane(tt.row_end);
+      n = __builtin_amdgcn_readfirstlane(n);
+    };
     // routed and shared items of one GEMM share one inlined tile body (two bodies
     // per GEMM left the routed tiles 5% slower); the operands are picked per item
     if (q < q2) {
       const bool sh = q >= q1s;
-      const GroupInfo& g = sh ? p.gs : p.g;
+      const GroupInfo g = group_from_args(sh ? p.gs : p.g);
       const int I = sh ? p.Is : p.I;
       if (!row_tile_at<true>(g, I / 128, sh ? q - q1s : q, t, nt)) continue;
+      uniform(t, nt);
       up_swiglu_tile<true>(lds, g, t, nt, p.x, sh ? p.sg : p.wg, sh ? p.su : p.wu, p.H, I,
                            sh ? p.Zs : p.Z, sh ? p.hs : p.h);
       fused_signal((sh ? p.readys : p.ready) + t.mt, p.next + x, claimed);
     } else if (q < qc) {
       const bool sh = q >= q2s;
-      const GroupInfo& g = sh ? p.gs : p.g;
+      const GroupInfo g = group_from_args(sh ? p.gs : p.g);
       const int I = sh ? p.Is : p.I;
       if (!row_tile_at<false>(g, nt2, sh ? q - q2s : q - q2, t, nt)) continue;
+      uniform(t, nt);
       fused_wait((sh ? p.readys : p.ready) + t.mt, I / 128, p.err);
       down_tile<CPOL_DEVICE, true>(lds, t, nt, sh ? p.hs : p.h, sh ? p.sd : p.wd, p.H, I,
                                    sh ? p.ys : p.Y);
