@@ -223,7 +223,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_dgrad_up(GroupInfo g, const T* __re
 
 // ------------------------------------------------------- DMA-fed wgrad loop (bf16)
 // The K-grouped wgrad operands reach LDS by the direct-to-LDS load
-// (global_load_lds_dwordx4: lane L's 16 bytes land at the wavefront's LDS base +
+// (buffer_load_dwordx4 ... lds: lane L's 16 bytes land at the wavefront's LDS base +
 // 16 L), so no registers stage them and three 32-deep K stages are in flight while
 // a fourth is multiplied: a ring of 4 x 16 KiB (two MN-major operand tiles of 32 K
 // rows x 256 bytes each, the same swizzled layout as the register-staged tiles).

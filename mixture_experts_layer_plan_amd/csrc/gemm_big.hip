@@ -11,8 +11,9 @@
 // (two per SIMD) computes a 256 x 256 output tile; wavefront (wm, wn) owns rows
 // 128 wm .. +127 and columns 64 wn .. +63 as 4 x 2 blocks of
 // v_mfma_f32_32x32x16_bf16.  Both operands travel global -> LDS by the gfx950
-// direct-to-LDS load (global_load_lds_dwordx4: each lane's 16 bytes land at the
-// wavefront's LDS base + 16 * lane), so no registers stage them; two LDS stages of
+// direct-to-LDS load (buffer_load_dwordx4 ... lds through a buffer resource: each
+// lane's 16 bytes land at the wavefront's LDS base + 16 * lane; the scale bytes and
+// zero-row tails keep the global_load_lds form), so no registers stage them; two LDS stages of
 // 64 KiB each: the next K tile (64 deep) streams in while the current one is
 // multiplied.  MFMA fragments are read one 16-deep step ahead, and the tile
 // barrier sits before the last step's MFMAs so that the next tile's first
