@@ -34,9 +34,206 @@
 //
 // Epilogues stage the fp32 accumulator tile in LDS (64 KiB, swizzled) and then
 // work on rows of 8 consecutive columns with 16-byte global accesses.
+#include <type_traits>
+
 #include "gemm_common.hpp"
 
 namespace moe {
+
+// ------------------------------------------------ DMA-fed loop (bf16 wgrads, dgrad-down)
+// The K-grouped wgrad operands and dgrad-down's operands reach LDS by the direct-to-LDS load
+// (buffer_load_dwordx4 ... lds: lane L's 16 bytes land at the wavefront's LDS base +
+// 16 L), so no registers stage them and three 32-deep K stages are in flight while
+// a fourth is multiplied: a ring of 4 x 16 KiB (two MN-major operand tiles of 32 K
+// rows x 256 bytes each, the same swizzled layout as the register-staged tiles).
+// Against one register-staged 64-deep tile in flight this keeps 1.5x the bytes in
+// flight per workgroup.  The loads go through a buffer resource whose range is the
+// expert's segment: K rows past it lie out of range and load as zeros, so they add
+// exactly zero and never leave the operands.
+
+namespace wdma {
+constexpr int BK = 32;          // K rows per stage
+constexpr int OPB = BK * 256;   // bytes of one operand tile in a stage
+constexpr int STB = 2 * OPB;    // stage bytes
+static_assert(4 * STB == LDS_BYTES, "the ring fills the LDS of the staged C tile");
+
+
+// MN-major operand: K row k = row seg0 + k of a row-major bf16 matrix, columns
+// c0 .. c0 + 127.  Instruction q (0, 1) of wavefront w fills K rows 8 w + 4 q ..
+// + 3 of a stage: lane L brings K row r = 8 w + 4 q + L / 16 into physical chunk
+// L % 16, i.e. its logical chunk (L % 16) ^ mn_swz(r).
+struct Opnd {
+  rsrc_t rs;         // element (seg0, c0); range: the segment's rows
+  uint32_t ldb;      // row stride, bytes
+  int r[2];
+  uint32_t col[2];
+  MOE_DEV void set(const bf16_t* b, size_t ld, int rows) {
+    ldb = (uint32_t)(ld * 2);
+    rs = make_rsrc(b, (uint32_t)rows * ldb);
+    const int w = threadIdx.x >> 6, L = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      r[q] = 8 * w + 4 * q + (L >> 4);
+      col[q] = (uint32_t)(((L & 15) ^ mn_swz(r[q])) << 4);
+    }
+  }
+  MOE_DEV void issue(int kt, char* tile) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)  // K rows past the segment lie past the range: zeros
+      dma16_buf(rs, (uint32_t)(kt * BK + r[q]) * ldb + col[q], 0u,
+                tile + (8 * w + 4 * q) * 256);
+  }
+};
+
+// K-major operand (dgrad-down's rows of dYu, K = H along each row): 128 rows x 32 K
+// per stage, 64-byte rows, chunk c (K values 8 c .. 8 c + 7) of row r at r * 64 +
+// 16 (c ^ ((r >> 2) & 3)), so that the 16 lanes of a fragment read that share a chunk
+// index hit 16 different 16-byte bank groups.  Instruction q of wavefront w fills rows
+// 16 (2 w + q) .. + 15: lane L brings row 16 (2 w + q) + L / 4, physical chunk L % 4.
+MOE_DEV int km_chunk(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+struct KOpnd {
+  rsrc_t rs;  // row 0 of the tile; range: its valid rows (rows past them load zeros)
+  uint32_t off[2];
+  MOE_DEV void set(const bf16_t* rows, size_t ld, int nrows) {
+    const uint32_t ldb = (uint32_t)(ld * 2);
+    rs = make_rsrc(rows, (uint32_t)nrows * ldb);
+    const int w = threadIdx.x >> 6, L = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r = 16 * (2 * w + q) + (L >> 2);
+      off[q] = (uint32_t)r * ldb + (uint32_t)(((L & 3) ^ ((r >> 2) & 3)) << 4);
+    }
+  }
+  MOE_DEV void issue(int kt, char* tile) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      dma16_buf(rs, off[q], (uint32_t)(kt * BK * 2), tile + (2 * w + q) * 1024);
+  }
+};
+
+// The MFMAs of one 32-deep stage (two 16-deep steps) on two MN-major tiles.  The
+// transposing LDS reads are issued from inline assembly: for the
+// ds_read_b64_tr_b16 builtin the compiler waits for every outstanding
+// direct-to-LDS load first (vmcnt(0)), which would drain the ring on every stage.
+// Each step's eight reads and their lgkmcnt(0) wait form one asm block, so no
+// fragment register is used before its data is in.
+MOE_DEV uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+MOE_DEV uint32_t mn_frag_addr(const char* t, int c0, int ks, int lane) {
+  const int g = lane >> 4, a = lane & 3, j = (lane >> 2) & 3;
+  const int k = 16 * ks + 8 * (g >> 1) + j;  // K row k + 4 has the same swizzle
+  const int col = c0 + 16 * (g & 1) + 4 * a;
+  return lds_addr(t + k * 256 + (((col >> 3) ^ mn_swz(k)) << 4) + (col & 7) * 2);
+}
+MOE_DEV bf16x8_t join_tr(const s16x4_t& lo, const s16x4_t& hi) {
+  return __builtin_bit_cast(bf16x8_t, (s16x8_t)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5,
+                                                                        6, 7));
+}
+// A K-major (KOpnd): its two fragments are plain 16-byte reads.
+MOE_DEV void mma_stage_km(const char* ta, const char* tb, f32x16_t (&acc)[2][2], int arow,
+                          const int (&brow)[2], int lane) {
+#pragma unroll
+  for (int ks = 0; ks < BK / 16; ++ks) {
+    const int ch = 2 * ks + (lane >> 5);
+    const uint32_t pa0 = lds_addr(ta + km_chunk(arow + (lane & 31), ch));
+    const uint32_t pa1 = lds_addr(ta + km_chunk(arow + 32 + (lane & 31), ch));
+    const uint32_t pb0 = mn_frag_addr(tb, brow[0], ks, lane);
+    const uint32_t pb1 = mn_frag_addr(tb, brow[1], ks, lane);
+    s16x8_t a0, a1;
+    s16x4_t b0l, b0h, b1l, b1h;
+    asm volatile(
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %1, %7\n\t"
+        "ds_read_b64_tr_b16 %2, %8\n\t"
+        "ds_read_b64_tr_b16 %3, %8 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %4, %9\n\t"
+        "ds_read_b64_tr_b16 %5, %9 offset:1024\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a0), "=&v"(a1), "=&v"(b0l), "=&v"(b0h), "=&v"(b1l), "=&v"(b1h)
+        : "v"(pa0), "v"(pa1), "v"(pb0), "v"(pb1)
+        : "memory");
+    const bf16x8_t fa0 = __builtin_bit_cast(bf16x8_t, a0), fa1 = __builtin_bit_cast(bf16x8_t, a1);
+    const bf16x8_t b0 = join_tr(b0l, b0h), b1 = join_tr(b1l, b1h);
+    acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0, b0, acc[0][0], 0, 0, 0);
+    acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0, b1, acc[0][1], 0, 0, 0);
+    acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1, b0, acc[1][0], 0, 0, 0);
+    acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1, b1, acc[1][1], 0, 0, 0);
+  }
+}
+
+MOE_DEV void mma_stage(const char* ta, const char* tb, f32x16_t (&acc)[2][2], int arow,
+                       const int (&brow)[2], int lane) {
+#pragma unroll
+  for (int ks = 0; ks < BK / 16; ++ks) {
+    const uint32_t pa0 = mn_frag_addr(ta, arow, ks, lane), pa1 = mn_frag_addr(ta, arow + 32, ks, lane);
+    const uint32_t pb0 = mn_frag_addr(tb, brow[0], ks, lane);
+    const uint32_t pb1 = mn_frag_addr(tb, brow[1], ks, lane);
+    s16x4_t a0l, a0h, a1l, a1h, b0l, b0h, b1l, b1h;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %2, %9\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %4, %10\n\t"
+        "ds_read_b64_tr_b16 %5, %10 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %6, %11\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:1024\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a0l), "=&v"(a0h), "=&v"(a1l), "=&v"(a1h), "=&v"(b0l), "=&v"(b0h), "=&v"(b1l),
+          "=&v"(b1h)
+        : "v"(pa0), "v"(pa1), "v"(pb0), "v"(pb1)
+        : "memory");
+    const bf16x8_t a0 = join_tr(a0l, a0h), a1 = join_tr(a1l, a1h);
+    const bf16x8_t b0 = join_tr(b0l, b0h), b1 = join_tr(b1l, b1h);
+    acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
+    acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
+    acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
+    acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
+  }
+}
+
+// Wait until at most `ahead` stages of this wavefront's loads (4 instructions each)
+// are outstanding and its LDS reads are done, then meet the workgroup.
+MOE_DEV void ring_wait(int ahead) {
+  if (ahead >= 2) __builtin_amdgcn_s_waitcnt(0x0078);       // vmcnt(8) lgkmcnt(0)
+  else if (ahead == 1) __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
+  else __builtin_amdgcn_s_waitcnt(0x0070);                  // vmcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
+// OA: Opnd (MN-major A, the wgrads) or KOpnd (K-major A, dgrad-down); n: K.
+template <class OA>
+MOE_DEV void main_loop(char* lds, const OA& A, const Opnd& B, int n, f32x16_t (&acc)[2][2],
+                       int arow, const int (&brow)[2], int lane) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  const int nk = (n + BK - 1) / BK;
+  for (int s = 0; s < 3 && s < nk; ++s) {
+    A.issue(s, lds + s * STB);
+    B.issue(s, lds + s * STB + OPB);
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    ring_wait(min(2, nk - 1 - kt));  // stage kt is in; stage kt - 1 is no longer read
+    if (kt + 3 < nk) {
+      char* slot = lds + ((kt + 3) & 3) * STB;
+      A.issue(kt + 3, slot);
+      B.issue(kt + 3, slot + OPB);
+    }
+    const char* cur = lds + (kt & 3) * STB;
+    if constexpr (std::is_same<OA, KOpnd>::value) mma_stage_km(cur, cur + OPB, acc, arow, brow, lane);
+    else mma_stage(cur, cur + OPB, acc, arow, brow, lane);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  __builtin_amdgcn_s_barrier();  // every wavefront is done with the ring
+}
+}  // namespace wdma
 
 // ------------------------------------------------------------------ kernels
 // GEMM1 + SwiGLU.  Tile n covers i in [64 n, 64 n + 64): B-tile rows 0..63 are
@@ -123,7 +320,9 @@ __global__ __launch_bounds__(NTHR, 2) void k_down(GroupInfo g, const T* __restri
 
 // dgrad-down: dh'[r, i] = sum_n dYu[r, n] W_d[e][n, i] with dYu[r] = dy[tok(r)] (the
 // reverse-combined rows); epilogue: SwiGLU backward and the router-weight-gradient
-// partial of this tile's 128 columns.
+// partial of this tile's 128 columns.  bf16 runs K through the direct-to-LDS ring
+// (dYu rows K-major, W_d MN-major; three 32-deep stages in flight); fp32 through the
+// register-staged loop.
 template <typename T>
 __global__ __launch_bounds__(NTHR, 2) void k_dgrad_down(GroupInfo g, const T* __restrict__ dYu,
                                                         const T* __restrict__ wd,
@@ -137,18 +336,26 @@ __global__ __launch_bounds__(NTHR, 2) void k_dgrad_down(GroupInfo g, const T* __
   int nt;
   if (!rows_tile(g, I / TN, t, nt)) return;
   const int i0 = nt * TN;
-  KLoad<T> la;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int r = t.row0 + (threadIdx.x >> 3) + 32 * s;
-    la.set(s, dYu + (size_t)r * H, r < t.row_end);
-  }
-  MNLoad<T, KRowPlain<T>> lb{{wd + (size_t)t.e * H * I + i0, (size_t)I}};
   int arow, brow[2];
   wave_coords(arow, brow, false);
   const int lane = threadIdx.x & 63;
   f32x16_t acc[2][2];
-  gemm_main<T>(lds, la, lb, H / Tr<T>::BK, acc, arow, brow, lane);
+  if constexpr (sizeof(T) == 2) {  // the direct-to-LDS ring
+    wdma::KOpnd la;
+    la.set(dYu + (size_t)t.row0 * H, (size_t)H, t.row_end - t.row0);
+    wdma::Opnd lb;
+    lb.set(wd + (size_t)t.e * H * I + i0, (size_t)I, H);
+    wdma::main_loop(lds, la, lb, H, acc, arow, brow, lane);
+  } else {
+    KLoad<T> la;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int r = t.row0 + (threadIdx.x >> 3) + 32 * s;
+      la.set(s, dYu + (size_t)r * H, r < t.row_end);
+    }
+    MNLoad<T, KRowPlain<T>> lb{{wd + (size_t)t.e * H * I + i0, (size_t)I}};
+    gemm_main<T>(lds, la, lb, H / Tr<T>::BK, acc, arow, brow, lane);
+  }
   float* C = (float*)lds;
   stage_acc(C, acc, arow, brow, lane);
   __syncthreads();
@@ -221,138 +428,6 @@ __global__ __launch_bounds__(NTHR, 2) void k_dgrad_up(GroupInfo g, const T* __re
   epi_store<T>(C, out, t.row_end - t.row0);
 }
 
-// ------------------------------------------------------- DMA-fed wgrad loop (bf16)
-// The K-grouped wgrad operands reach LDS by the direct-to-LDS load
-// (buffer_load_dwordx4 ... lds: lane L's 16 bytes land at the wavefront's LDS base +
-// 16 L), so no registers stage them and three 32-deep K stages are in flight while
-// a fourth is multiplied: a ring of 4 x 16 KiB (two MN-major operand tiles of 32 K
-// rows x 256 bytes each, the same swizzled layout as the register-staged tiles).
-// Against one register-staged 64-deep tile in flight this keeps 1.5x the bytes in
-// flight per workgroup.  The loads go through a buffer resource whose range is the
-// expert's segment: K rows past it lie out of range and load as zeros, so they add
-// exactly zero and never leave the operands.
-
-namespace wdma {
-constexpr int BK = 32;          // K rows per stage
-constexpr int OPB = BK * 256;   // bytes of one operand tile in a stage
-constexpr int STB = 2 * OPB;    // stage bytes
-static_assert(4 * STB == LDS_BYTES, "the ring fills the LDS of the staged C tile");
-
-
-// MN-major operand: K row k = row seg0 + k of a row-major bf16 matrix, columns
-// c0 .. c0 + 127.  Instruction q (0, 1) of wavefront w fills K rows 8 w + 4 q ..
-// + 3 of a stage: lane L brings K row r = 8 w + 4 q + L / 16 into physical chunk
-// L % 16, i.e. its logical chunk (L % 16) ^ mn_swz(r).
-struct Opnd {
-  rsrc_t rs;         // element (seg0, c0); range: the segment's rows
-  uint32_t ldb;      // row stride, bytes
-  int r[2];
-  uint32_t col[2];
-  MOE_DEV void set(const bf16_t* b, size_t ld, int rows) {
-    ldb = (uint32_t)(ld * 2);
-    rs = make_rsrc(b, (uint32_t)rows * ldb);
-    const int w = threadIdx.x >> 6, L = threadIdx.x & 63;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      r[q] = 8 * w + 4 * q + (L >> 4);
-      col[q] = (uint32_t)(((L & 15) ^ mn_swz(r[q])) << 4);
-    }
-  }
-  MOE_DEV void issue(int kt, char* tile) const {
-    const int w = threadIdx.x >> 6;
-#pragma unroll
-    for (int q = 0; q < 2; ++q)  // K rows past the segment lie past the range: zeros
-      dma16_buf(rs, (uint32_t)(kt * BK + r[q]) * ldb + col[q], 0u,
-                tile + (8 * w + 4 * q) * 256);
-  }
-};
-
-// The MFMAs of one 32-deep stage (two 16-deep steps) on two MN-major tiles.  The
-// transposing LDS reads are issued from inline assembly: for the
-// ds_read_b64_tr_b16 builtin the compiler waits for every outstanding
-// direct-to-LDS load first (vmcnt(0)), which would drain the ring on every stage.
-// Each step's eight reads and their lgkmcnt(0) wait form one asm block, so no
-// fragment register is used before its data is in.
-MOE_DEV uint32_t lds_addr(const char* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-MOE_DEV uint32_t mn_frag_addr(const char* t, int c0, int ks, int lane) {
-  const int g = lane >> 4, a = lane & 3, j = (lane >> 2) & 3;
-  const int k = 16 * ks + 8 * (g >> 1) + j;  // K row k + 4 has the same swizzle
-  const int col = c0 + 16 * (g & 1) + 4 * a;
-  return lds_addr(t + k * 256 + (((col >> 3) ^ mn_swz(k)) << 4) + (col & 7) * 2);
-}
-MOE_DEV bf16x8_t join_tr(const s16x4_t& lo, const s16x4_t& hi) {
-  return __builtin_bit_cast(bf16x8_t, (s16x8_t)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5,
-                                                                        6, 7));
-}
-MOE_DEV void mma_stage(const char* ta, const char* tb, f32x16_t (&acc)[2][2], int arow,
-                       const int (&brow)[2], int lane) {
-#pragma unroll
-  for (int ks = 0; ks < BK / 16; ++ks) {
-    const uint32_t pa0 = mn_frag_addr(ta, arow, ks, lane), pa1 = mn_frag_addr(ta, arow + 32, ks, lane);
-    const uint32_t pb0 = mn_frag_addr(tb, brow[0], ks, lane);
-    const uint32_t pb1 = mn_frag_addr(tb, brow[1], ks, lane);
-    s16x4_t a0l, a0h, a1l, a1h, b0l, b0h, b1l, b1h;
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8\n\t"
-        "ds_read_b64_tr_b16 %1, %8 offset:1024\n\t"
-        "ds_read_b64_tr_b16 %2, %9\n\t"
-        "ds_read_b64_tr_b16 %3, %9 offset:1024\n\t"
-        "ds_read_b64_tr_b16 %4, %10\n\t"
-        "ds_read_b64_tr_b16 %5, %10 offset:1024\n\t"
-        "ds_read_b64_tr_b16 %6, %11\n\t"
-        "ds_read_b64_tr_b16 %7, %11 offset:1024\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a0l), "=&v"(a0h), "=&v"(a1l), "=&v"(a1h), "=&v"(b0l), "=&v"(b0h), "=&v"(b1l),
-          "=&v"(b1h)
-        : "v"(pa0), "v"(pa1), "v"(pb0), "v"(pb1)
-        : "memory");
-    const bf16x8_t a0 = join_tr(a0l, a0h), a1 = join_tr(a1l, a1h);
-    const bf16x8_t b0 = join_tr(b0l, b0h), b1 = join_tr(b1l, b1h);
-    acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
-    acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
-    acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
-    acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
-  }
-}
-
-// Wait until at most `ahead` stages of this wavefront's loads (4 instructions each)
-// are outstanding and its LDS reads are done, then meet the workgroup.
-MOE_DEV void ring_wait(int ahead) {
-  if (ahead >= 2) __builtin_amdgcn_s_waitcnt(0x0078);       // vmcnt(8) lgkmcnt(0)
-  else if (ahead == 1) __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
-  else __builtin_amdgcn_s_waitcnt(0x0070);                  // vmcnt(0) lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-}
-
-MOE_DEV void main_loop(char* lds, const Opnd& A, const Opnd& B, int n, f32x16_t (&acc)[2][2],
-                       int arow, const int (&brow)[2], int lane) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-  const int nk = (n + BK - 1) / BK;
-  for (int s = 0; s < 3 && s < nk; ++s) {
-    A.issue(s, lds + s * STB);
-    B.issue(s, lds + s * STB + OPB);
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    ring_wait(min(2, nk - 1 - kt));  // stage kt is in; stage kt - 1 is no longer read
-    if (kt + 3 < nk) {
-      char* slot = lds + ((kt + 3) & 3) * STB;
-      A.issue(kt + 3, slot);
-      B.issue(kt + 3, slot + OPB);
-    }
-    const char* cur = lds + (kt & 3) * STB;
-    mma_stage(cur, cur + OPB, acc, arow, brow, lane);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0070);
-  __builtin_amdgcn_s_barrier();  // every wavefront is done with the ring
-}
-}  // namespace wdma
 
 // wgrad-down: dW_d[e][m, n] = sum_r dYu[r, m] gh[r, n]  (M = H, N = I, K = rows of e).
 // Persistent: each workgroup walks work items blockIdx.x, + gridDim.x, ...; the
