@@ -498,11 +498,16 @@ MOE_DEV void main_loop_small(char* lds, const OA& A, const OB& B, int nk, int ma
 
 // The K loop of a row-grouped tile: the two-stage loop, or the ring for a tile with
 // at most 128 rows.
+// A wavefront with all its blocks (ma = 4, mb = 2: every wavefront of a full tile) runs
+// a copy of the two-stage loop compiled for them, free of the per-block guards, which
+// otherwise split the loop body into a branch around every fragment read and MFMA pair.
+// Both copies meet the same barriers, one per K tile.
 template <class OA, class OB>
 MOE_DEV void main_loop_rows(char* lds, const OA& A, const OB& B, int nk, int rows, int ma, int mb,
                             Acc& acc) {
   if (rows <= 64) main_loop_small<64, 4>(lds, A, B, nk, ma, mb, acc);
   else if (rows <= 128) main_loop_small<128, 3>(lds, A, B, nk, ma, mb, acc);
+  else if (ma == 4 && mb == 2) main_loop<true>(lds, A, B, nk, 4, 2, acc);
   else main_loop<true>(lds, A, B, nk, ma, mb, acc);
 }
 
@@ -524,8 +529,14 @@ MOE_DEV int out_row_base() {
 
 // Leading A blocks of this wavefront with a row below `rows`, B blocks with a
 // column below `cols`.
-MOE_DEV int blocks_a(int rows) { return min(4, max(0, (rows - 128 * (wave() >> 2) + 31) / 32)); }
-MOE_DEV int blocks_b(int cols) { return min(2, max(0, (cols - 64 * (wave() & 3) + 31) / 32)); }
+// (read back as wave-uniform values: the block guards of the K loops are then scalar
+// branches, and the full case below is recognised as such)
+MOE_DEV int blocks_a(int rows) {
+  return __builtin_amdgcn_readfirstlane(min(4, max(0, (rows - 128 * (wave() >> 2) + 31) / 32)));
+}
+MOE_DEV int blocks_b(int cols) {
+  return __builtin_amdgcn_readfirstlane(min(2, max(0, (cols - 64 * (wave() & 3) + 31) / 32)));
+}
 
 // ------------------------------------------------------------ tile decode
 struct Tile {
