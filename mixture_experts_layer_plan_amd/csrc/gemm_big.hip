@@ -501,7 +501,9 @@ MOE_DEV void main_loop_small(char* lds, const OA& A, const OB& B, int nk, int ma
 // A wavefront with all its blocks (ma = 4, mb = 2: every wavefront of a full tile) runs
 // a copy of the two-stage loop compiled for them, free of the per-block guards, which
 // otherwise split the loop body into a branch around every fragment read and MFMA pair.
-// Both copies meet the same barriers, one per K tile.
+// Both copies meet the same barriers, one per K tile.  (The same copies of the small-
+// tile rings, for their wavefronts with all blocks, made GEMM2 and dgrad-up slower on
+// MI355X: 1.60 -> 1.65 and 2.88 -> 3.00 ms at T = 4096.)
 template <class OA, class OB>
 MOE_DEV void main_loop_rows(char* lds, const OA& A, const OB& B, int nk, int rows, int ma, int mb,
                             Acc& acc) {
@@ -1398,8 +1400,8 @@ MOE_DEV void mx_stage_scales(const char* sb, int u, int wm, int wn, MxScales& sc
 // the whole workgroup's loads in and a barrier, so each buffer is full before it is
 // read and no longer read when it is loaded again.
 template <class OA, class OB>
-MOE_DEV void main_loop_rows_mx(char* lds, const OA& A, const OB& B, const MxScaleDma& S, int nk,
-                               int ma, int mb, Acc& acc) {
+MOE_DEV void main_loop_rows_mx_body(char* lds, const OA& A, const OB& B, const MxScaleDma& S,
+                                    int nk, int ma, int mb, Acc& acc) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1435,6 +1437,15 @@ MOE_DEV void main_loop_rows_mx(char* lds, const OA& A, const OB& B, const MxScal
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();  // LDS free for an epilogue or the next tile
+}
+
+// As main_loop_rows: a wavefront with all its blocks runs a copy of the loop free of
+// the per-block guards.
+template <class OA, class OB>
+MOE_DEV void main_loop_rows_mx(char* lds, const OA& A, const OB& B, const MxScaleDma& S, int nk,
+                               int ma, int mb, Acc& acc) {
+  if (ma == 4 && mb == 2) main_loop_rows_mx_body(lds, A, B, S, nk, 4, 2, acc);
+  else main_loop_rows_mx_body(lds, A, B, S, nk, ma, mb, acc);
 }
 
 // Scale source of this lane's tile row when it is an A row (q < 256): the tile's row
