@@ -481,6 +481,71 @@ MOE_DEV void step_kmn(const OA& A, const char* st, int kt, int ks, int wm, int w
   bn[1] = join_tr(l1, h1);
 }
 
+// Both operands MN-major (the hot wgrads): two blocks per step, each with six of the
+// next step's twelve transposing reads and four of the current step's MFMAs (measured
+// on MI355X against one block of twelve reads and its wait before the MFMAs: hot
+// wgrad-up 2.00 -> 1.98 ms, wgrad-down 1.02 -> 1.00 ms at T = 4096).
+MOE_DEV void step_mnmn(const char* st, int ks, int wm, int wn, const bf16x8_t (&ac)[4],
+                       const bf16x8_t (&bc)[2], bf16x8_t (&an)[4], bf16x8_t (&bn)[2], Acc& acc) {
+  const uint32_t base = lds_u32(st) + (uint32_t)(mn_lane_ofs() + ks * 16 * 512);
+  const uint32_t pa0 = base + mn_blk_ofs(128 * wm), pa1 = base + mn_blk_ofs(128 * wm + 32);
+  const uint32_t pa2 = base + mn_blk_ofs(128 * wm + 64), pa3 = base + mn_blk_ofs(128 * wm + 96);
+  const uint32_t pb0 = base + STAGE + mn_blk_ofs(64 * wn);
+  const uint32_t pb1 = base + STAGE + mn_blk_ofs(64 * wn + 32);
+  s16x4_t r[12];
+  asm volatile(
+      "s_nop 2\n\t"
+      "ds_read_b64_tr_b16 %0, %14\n\t"
+      "ds_read_b64_tr_b16 %1, %14 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %2, %15\n\t"
+      "ds_read_b64_tr_b16 %3, %15 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %4, %16\n\t"
+      "ds_read_b64_tr_b16 %5, %16 offset:2048\n\t"
+      "v_mfma_f32_32x32x16_bf16 %6, %10, %12, %6\n\t"
+      "v_mfma_f32_32x32x16_bf16 %7, %10, %13, %7\n\t"
+      "v_mfma_f32_32x32x16_bf16 %8, %11, %12, %8\n\t"
+      "v_mfma_f32_32x32x16_bf16 %9, %11, %13, %9\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "+v"(acc.c[0][0]), "+v"(acc.c[0][1]), "+v"(acc.c[1][0]), "+v"(acc.c[1][1])
+      : "v"(ac[0]), "v"(ac[1]), "v"(bc[0]), "v"(bc[1]), "v"(pa0), "v"(pa1), "v"(pa2)
+      : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile(
+      "s_nop 2\n\t"
+      "ds_read_b64_tr_b16 %0, %14\n\t"
+      "ds_read_b64_tr_b16 %1, %14 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %2, %15\n\t"
+      "ds_read_b64_tr_b16 %3, %15 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %4, %16\n\t"
+      "ds_read_b64_tr_b16 %5, %16 offset:2048\n\t"
+      "v_mfma_f32_32x32x16_bf16 %6, %10, %12, %6\n\t"
+      "v_mfma_f32_32x32x16_bf16 %7, %10, %13, %7\n\t"
+      "v_mfma_f32_32x32x16_bf16 %8, %11, %12, %8\n\t"
+      "v_mfma_f32_32x32x16_bf16 %9, %11, %13, %9\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
+        "+v"(acc.c[2][0]), "+v"(acc.c[2][1]), "+v"(acc.c[3][0]), "+v"(acc.c[3][1])
+      : "v"(ac[2]), "v"(ac[3]), "v"(bc[0]), "v"(bc[1]), "v"(pa3), "v"(pb0), "v"(pb1)
+      : "memory");
+#pragma unroll
+  for (int i = 0; i < 4; ++i) an[i] = join_tr(r[2 * i], r[2 * i + 1]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) bn[j] = join_tr(r[8 + 2 * j], r[9 + 2 * j]);
+}
+
+template <class OA, class OB>
+MOE_DEV void step_asm(const OA& A, const OB&, const char* st, int kt, int ks, int wm, int wn,
+                      const bf16x8_t (&ac)[4], const bf16x8_t (&bc)[2], bf16x8_t (&an)[4],
+                      bf16x8_t (&bn)[2], Acc& acc) {
+  step_kmn(A, st, kt, ks, wm, wn, ac, bc, an, bn, acc);
+}
+MOE_DEV void step_asm(const OpMNSeg&, const OpMNSeg&, const char* st, int, int ks, int wm, int wn,
+                      const bf16x8_t (&ac)[4], const bf16x8_t (&bc)[2], bf16x8_t (&an)[4],
+                      bf16x8_t (&bn)[2], Acc& acc) {
+  step_mnmn(st, ks, wm, wn, ac, bc, an, bn, acc);
+}
+
 // The two-stage loop of main_loop<LATE_B> for such tiles, with the steps above.
 template <bool LATE_B, class OA, class OB>
 MOE_DEV void main_loop_kmn(char* lds, const OA& A, const OB& B, int nk, Acc& acc) {
@@ -505,20 +570,20 @@ MOE_DEV void main_loop_kmn(char* lds, const OA& A, const OB& B, int nk, Acc& acc
     A.issue(kn, nxt);
     if (!LATE_B) B.issue(kn, nxt + STAGE);
     __builtin_amdgcn_sched_barrier(0);
-    step_kmn(A, cur, kt, 1, wm, wn, a0, b0, a1, b1, acc);
+    step_asm(A, B, cur, kt, 1, wm, wn, a0, b0, a1, b1, acc);
     __builtin_amdgcn_sched_barrier(0);
     if (LATE_B) {
       B.issue(kn, nxt + STAGE);
       __builtin_amdgcn_sched_barrier(0);
     }
-    step_kmn(A, cur, kt, 2, wm, wn, a1, b1, a0, b0, acc);
+    step_asm(A, B, cur, kt, 2, wm, wn, a1, b1, a0, b0, acc);
     __builtin_amdgcn_sched_barrier(0);
-    step_kmn(A, cur, kt, 3, wm, wn, a0, b0, a1, b1, acc);
+    step_asm(A, B, cur, kt, 3, wm, wn, a0, b0, a1, b1, acc);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    step_kmn(A, nxt, kt + 1, 0, wm, wn, a1, b1, a0, b0, acc);
+    step_asm(A, B, nxt, kt + 1, 0, wm, wn, a1, b1, a0, b0, acc);
     __builtin_amdgcn_sched_barrier(0);
   }
   // wait states between the last MFMAs of the assembly blocks and reads of their
@@ -1128,7 +1193,7 @@ __global__ __launch_bounds__(NTH, 1) void k_wgrad_hot(WgradArgs p) {
     A.set(p.A + (size_t)seg0 * p.lda + m0, (size_t)p.lda, n);
     B.set(p.B + (size_t)seg0 * p.ldb + n0, (size_t)p.ldb, n);
     Acc acc;
-    main_loop(lds, A, B, (n + 63) / 64, 4, 2, acc);
+    main_loop_kmn<false>(lds, A, B, (n + 63) / 64, acc);
     bf16_t* base = m0 < p.half_rows
                        ? p.out0 + (size_t)e * part0 + (size_t)m0 * p.N + n0
                        : p.out1 + (size_t)e * part1 + (size_t)(m0 - p.half_rows) * p.N + n0;
