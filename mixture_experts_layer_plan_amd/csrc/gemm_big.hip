@@ -587,9 +587,13 @@ MOE_DEV void main_loop_kmn(char* lds, const OA& A, const OB& B, int nk, Acc& acc
     __builtin_amdgcn_sched_barrier(0);
   }
   // wait states between the last MFMAs of the assembly blocks and reads of their
-  // results by other instructions (not tracked by the compiler across the blocks)
+  // results by other instructions (not tracked by the compiler across the blocks);
+  // every accumulator passes through one of the two blocks, so no read of one can be
+  // placed before them
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                : "+v"(acc.c[0][0]), "+v"(acc.c[0][1]), "+v"(acc.c[1][0]), "+v"(acc.c[1][1]));
+  asm volatile("s_nop 0"
+               : "+v"(acc.c[2][0]), "+v"(acc.c[2][1]), "+v"(acc.c[3][0]), "+v"(acc.c[3][1]));
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();  // LDS free for an epilogue
 }
