@@ -379,9 +379,10 @@ MOE_DEV void mma(Acc& acc, const bf16x8_t (&a)[4], const bf16x8_t (&b)[2], int m
 
 // LATE_B: the next K tile's B loads are issued after the first step's MFMAs instead
 // of together with its A loads (the row-grouped kernels: measured on MI355X at
-// T = 4096, Zipf(1.2), dgrad-up 3.12 -> 2.97 ms, GEMM2 1.76 -> 1.67 ms, GEMM1
-// unchanged, the step 18.64 -> 18.45 ms; the wgrads, whose K loops are short and
-// read both operands MN-major, measured 3 % slower with it)
+// T = 4096, Zipf(1.2), dgrad-up 3.12 -> 2.97 ms, GEMM2 1.76 -> 1.67 ms, the step
+// 18.64 -> 18.45 ms; with the guard-free full-tile loop GEMM1 gains too, 2.72 ->
+// 2.63 ms.  The hot wgrads, 3 % slower with it in this loop, gain with it in the
+// interleaved loop below: 1.94 -> 1.90 ms (up), 0.97 -> 0.94 ms (down))
 template <bool LATE_B = false, class OA, class OB>
 MOE_DEV void main_loop(char* lds, const OA& A, const OB& B, int nk, int ma, int mb, Acc& acc) {
 #pragma unroll
@@ -1197,7 +1198,7 @@ __global__ __launch_bounds__(NTH, 1) void k_wgrad_hot(WgradArgs p) {
     A.set(p.A + (size_t)seg0 * p.lda + m0, (size_t)p.lda, n);
     B.set(p.B + (size_t)seg0 * p.ldb + n0, (size_t)p.ldb, n);
     Acc acc;
-    main_loop_kmn<false>(lds, A, B, (n + 63) / 64, acc);
+    main_loop_kmn<true>(lds, A, B, (n + 63) / 64, acc);
     bf16_t* base = m0 < p.half_rows
                        ? p.out0 + (size_t)e * part0 + (size_t)m0 * p.N + n0
                        : p.out1 + (size_t)e * part1 + (size_t)(m0 - p.half_rows) * p.N + n0;
