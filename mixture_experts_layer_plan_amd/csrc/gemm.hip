@@ -204,10 +204,13 @@ MOE_DEV void ring_wait(int ahead) {
   __builtin_amdgcn_s_barrier();
 }
 
-// OA: Opnd (MN-major A, the wgrads) or KOpnd (K-major A, dgrad-down); n: K.
-template <class OA>
+// OA: Opnd (MN-major A, the wgrads) or KOpnd (K-major A, dgrad-down); n: K.  NS: ring
+// stages (NS - 1 in flight): 4 (64 KiB) for dgrad-down, 3 (48 KiB) for the wgrad
+// remainders, which run three workgroups per CU.
+template <int NS = 4, class OA>
 MOE_DEV void main_loop(char* lds, const OA& A, const Opnd& B, int n, f32x16_t (&acc)[2][2],
                        int arow, const int (&brow)[2], int lane) {
+  static_assert(NS == 3 || NS == 4, "ring depth");
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -215,18 +218,20 @@ MOE_DEV void main_loop(char* lds, const OA& A, const Opnd& B, int n, f32x16_t (&
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   const int nk = (n + BK - 1) / BK;
-  for (int s = 0; s < 3 && s < nk; ++s) {
+  for (int s = 0; s < NS - 1 && s < nk; ++s) {
     A.issue(s, lds + s * STB);
     B.issue(s, lds + s * STB + OPB);
   }
+  int slot = 0;  // kt % NS
   for (int kt = 0; kt < nk; ++kt) {
-    ring_wait(min(2, nk - 1 - kt));  // stage kt is in; stage kt - 1 is no longer read
-    if (kt + 3 < nk) {
-      char* slot = lds + ((kt + 3) & 3) * STB;
-      A.issue(kt + 3, slot);
-      B.issue(kt + 3, slot + OPB);
+    ring_wait(min(NS - 2, nk - 1 - kt));  // stage kt is in; stage kt - 1 is no longer read
+    if (kt + NS - 1 < nk) {  // into the slot of stage kt - 1
+      char* st = lds + (slot == 0 ? NS - 1 : slot - 1) * STB;
+      A.issue(kt + NS - 1, st);
+      B.issue(kt + NS - 1, st + OPB);
     }
-    const char* cur = lds + (kt & 3) * STB;
+    const char* cur = lds + slot * STB;
+    slot = slot == NS - 1 ? 0 : slot + 1;
     if constexpr (std::is_same<OA, KOpnd>::value) mma_stage_km(cur, cur + OPB, acc, arow, brow, lane);
     else mma_stage(cur, cur + OPB, acc, arow, brow, lane);
   }
@@ -429,14 +434,45 @@ __global__ __launch_bounds__(NTHR, 2) void k_dgrad_up(GroupInfo g, const T* __re
 }
 
 
+// stage_acc inside the persistent item loops: the wave's row and column bases are
+// made opaque per item, so that the 64 staging offsets are computed in each item and
+// not once before the loop and held across it (64 registers)
+MOE_DEV void stage_acc_item(float* C, const f32x16_t (&acc)[2][2], int arow,
+                            const int (&brow)[2], int lane) {
+  int r = arow, b[2] = {brow[0], brow[1]};
+  asm volatile("" : "+v"(r), "+v"(b[0]), "+v"(b[1]));
+  stage_acc(C, acc, r, b, lane);
+}
+
+// The wgrad remainders' epilogue through 32 KiB: the C tile in two halves of 64 rows
+// (the wavefronts of row half hf stage theirs at C rows 0..63, then all threads store
+// those rows), so that the LDS is the 48 KiB ring.
+template <typename T, class RowPtr>
+MOE_DEV void epi_halves(float* C, const f32x16_t (&acc)[2][2], int arow, const int (&brow)[2],
+                        int lane, const RowPtr& out_row) {
+#pragma unroll 1
+  for (int hf = 0; hf < 2; ++hf) {
+    if (arow == 64 * hf) stage_acc_item(C, acc, 0, brow, lane);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int r = (threadIdx.x >> 4) + 16 * s, c = threadIdx.x & 15;
+      float f[8];
+      read8(C, r, 8 * c, f);
+      store8_nt(out_row(64 * hf + r) + 8 * c, f);
+    }
+    __syncthreads();
+  }
+}
+
 // wgrad-down: dW_d[e][m, n] = sum_r dYu[r, m] gh[r, n]  (M = H, N = I, K = rows of e).
 // Persistent: each workgroup walks work items blockIdx.x, + gridDim.x, ...; the
 // tiles of experts without rows are stored as zeros.
 template <typename T>
-__global__ __launch_bounds__(NTHR, 2) void k_wgrad_down(GroupInfo g, const T* __restrict__ dYu,
+__global__ __launch_bounds__(NTHR, sizeof(T) == 2 ? 3 : 2) void k_wgrad_down(GroupInfo g, const T* __restrict__ dYu,
                                                         const T* __restrict__ gh, int H, int I,
                                                         T* __restrict__ dwd) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds[sizeof(T) == 2 ? 3 * wdma::STB : LDS_BYTES];
   const int MT = H / TM, NT = I / TN;
   const int total = k_work_items(g, MT, NT);
   int arow, brow[2];
@@ -460,7 +496,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_down(GroupInfo g, const T* __
       wdma::Opnd la, lb;
       la.set(dYu + (size_t)seg0 * H + t.m0, (size_t)H, seg1 - seg0);
       lb.set(gh + (size_t)seg0 * I + t.n0, (size_t)I, seg1 - seg0);
-      wdma::main_loop(lds, la, lb, seg1 - seg0, acc, arow, brow, lane);
+      wdma::main_loop<3>(lds, la, lb, seg1 - seg0, acc, arow, brow, lane);
     } else {
       MNSeg<T> la, lb;
       la.set(dYu + (size_t)seg0 * H + t.m0, (size_t)H, seg1 - seg0);
@@ -469,12 +505,16 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_down(GroupInfo g, const T* __
       gemm_main<T, 1>(lds, la, lb, nk, acc, arow, brow, lane);
     }
     float* C = (float*)lds;
-    stage_acc(C, acc, arow, brow, lane);
-    __syncthreads();
     T* base = dwd + (size_t)t.e * H * I + (size_t)t.m0 * I + t.n0;
     auto out = [&](int r) { return base + (size_t)r * I; };
-    epi_store<T, true>(C, out, TM);
-    __syncthreads();
+    if constexpr (sizeof(T) == 2) {
+      epi_halves<T>(C, acc, arow, brow, lane, out);
+    } else {
+      stage_acc_item(C, acc, arow, brow, lane);
+      __syncthreads();
+      epi_store<T, true>(C, out, TM);
+      __syncthreads();
+    }
   }
 }
 
@@ -482,10 +522,10 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_down(GroupInfo g, const T* __
 // dispatched rows, replayed)  (M = 2I, N = H); persistent, zeros for experts
 // without rows.
 template <typename T>
-__global__ __launch_bounds__(NTHR, 2) void k_wgrad_up(GroupInfo g, const T* __restrict__ dZ,
+__global__ __launch_bounds__(NTHR, sizeof(T) == 2 ? 3 : 2) void k_wgrad_up(GroupInfo g, const T* __restrict__ dZ,
                                                       const T* __restrict__ X, int H, int I,
                                                       T* __restrict__ dwg, T* __restrict__ dwu) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds[sizeof(T) == 2 ? 3 * wdma::STB : LDS_BYTES];
   const int MT = (2 * I) / TM, NT = H / TN;
   const int total = k_work_items(g, MT, NT);
   int arow, brow[2];
@@ -511,7 +551,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_up(GroupInfo g, const T* __re
       wdma::Opnd la, lb;
       la.set(dZ + (size_t)seg0 * (2 * I) + t.m0, (size_t)(2 * I), seg1 - seg0);
       lb.set(X + (size_t)seg0 * H + t.n0, (size_t)H, seg1 - seg0);
-      wdma::main_loop(lds, la, lb, seg1 - seg0, acc, arow, brow, lane);
+      wdma::main_loop<3>(lds, la, lb, seg1 - seg0, acc, arow, brow, lane);
     } else {
       MNSeg<T> la, lb;
       la.set(dZ + (size_t)seg0 * (2 * I) + t.m0, (size_t)(2 * I), seg1 - seg0);
@@ -520,13 +560,17 @@ __global__ __launch_bounds__(NTHR, 2) void k_wgrad_up(GroupInfo g, const T* __re
       gemm_main<T, 1>(lds, la, lb, nk, acc, arow, brow, lane);
     }
     float* C = (float*)lds;
-    stage_acc(C, acc, arow, brow, lane);
-    __syncthreads();
     T* base = (t.m0 < I ? dwg + (size_t)t.e * I * H + (size_t)t.m0 * H
                         : dwu + (size_t)t.e * I * H + (size_t)(t.m0 - I) * H) + t.n0;
     auto out = [&](int r) { return base + (size_t)r * H; };
-    epi_store<T, true>(C, out, TM);
-    __syncthreads();
+    if constexpr (sizeof(T) == 2) {
+      epi_halves<T>(C, acc, arow, brow, lane, out);
+    } else {
+      stage_acc_item(C, acc, arow, brow, lane);
+      __syncthreads();
+      epi_store<T, true>(C, out, TM);
+      __syncthreads();
+    }
   }
 }
 
@@ -580,7 +624,7 @@ static hipError_t dgrad_up_t(const GroupInfo& g, const void* dZ, const void* wg,
 template <typename T>
 static hipError_t wgrad_down_t(const GroupInfo& g, const void* dy, const void* gh, int H, int I,
                                void* dwd, hipStream_t s) {
-  const unsigned grid = persistent_grid((long)g.E * (H / TM) * (I / TN));
+  const unsigned grid = persistent_grid((long)g.E * (H / TM) * (I / TN), sizeof(T) == 2 ? 3 : 2);
   return MOE_LAUNCH(g.offsets ? "gemm_wgrad_down" : "gemm_wgrad_down_shared", s,
                     k_wgrad_down<T><<<grid, NTHR, 0, s>>>(g, (const T*)dy, (const T*)gh, H, I,
                                                           (T*)dwd));
@@ -589,7 +633,7 @@ static hipError_t wgrad_down_t(const GroupInfo& g, const void* dy, const void* g
 template <typename T>
 static hipError_t wgrad_up_t(const GroupInfo& g, const void* dZ, const void* x, int H, int I,
                              void* dwg, void* dwu, hipStream_t s) {
-  const unsigned grid = persistent_grid((long)g.E * ((2 * I) / TM) * (H / TN));
+  const unsigned grid = persistent_grid((long)g.E * ((2 * I) / TM) * (H / TN), sizeof(T) == 2 ? 3 : 2);
   return MOE_LAUNCH(g.offsets ? "gemm_wgrad_up" : "gemm_wgrad_up_shared", s,
                     k_wgrad_up<T><<<grid, NTHR, 0, s>>>(g, (const T*)dZ, (const T*)x, H, I,
                                                         (T*)dwg, (T*)dwu));

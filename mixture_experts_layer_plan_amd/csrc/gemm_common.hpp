@@ -575,9 +575,9 @@ MOE_DEV void zero_span(T* out) {
     __builtin_nontemporal_store(z, (u32x4_t*)out + (int)threadIdx.x + i * NTHR);
 }
 
-// Persistent grid: two resident workgroups per compute unit, at most one per item.
-inline unsigned persistent_grid(long items) {
-  const long g = 2L * device_cus();
+// Persistent grid: per_cu resident workgroups per compute unit, at most one per item.
+inline unsigned persistent_grid(long items, int per_cu = 2) {
+  const long g = (long)per_cu * device_cus();
   return (unsigned)(items < g ? (items > 0 ? items : 1) : g);
 }
 
