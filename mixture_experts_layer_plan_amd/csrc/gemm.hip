@@ -43,13 +43,14 @@ namespace moe {
 // ------------------------------------------------ DMA-fed loop (bf16 wgrads, dgrad-down)
 // The K-grouped wgrad operands and dgrad-down's operands reach LDS by the direct-to-LDS load
 // (buffer_load_dwordx4 ... lds: lane L's 16 bytes land at the wavefront's LDS base +
-// 16 L), so no registers stage them and three 32-deep K stages are in flight while
-// a fourth is multiplied: a ring of 4 x 16 KiB (two MN-major operand tiles of 32 K
-// rows x 256 bytes each, the same swizzled layout as the register-staged tiles).
-// Against one register-staged 64-deep tile in flight this keeps 1.5x the bytes in
-// flight per workgroup.  The loads go through a buffer resource whose range is the
-// expert's segment: K rows past it lie out of range and load as zeros, so they add
-// exactly zero and never leave the operands.
+// 16 L), so no registers stage them.  A ring of 32-deep K stages of 16 KiB (two operand
+// tiles of 32 K rows x 256 bytes each, the same swizzled layout as the register-staged
+// tiles): dgrad-down keeps three stages in flight while a fourth is multiplied (64 KiB,
+// two workgroups per CU); the wgrad remainders, short K loops bound by their output
+// writes, keep two in flight (48 KiB) so that three workgroups fit per CU.  The loads
+// go through a buffer resource whose range is the expert's segment: K rows past it lie
+// out of range and load as zeros, so they add exactly zero and never leave the
+// operands.
 
 namespace wdma {
 constexpr int BK = 32;          // K rows per stage
