@@ -17,9 +17,12 @@
  *
  * Conventions for every entry point
  *  - Every array pointer is a DEVICE pointer owned by the caller.  The library
- *    allocates and frees nothing, keeps no state between calls (apart from
- *    the optional per-thread timing trace below), never synchronises the host
- *    and enqueues all work on `stream` (NULL = the null stream).  Outputs are valid once the caller has synchronised the stream.
+ *    allocates no device memory, keeps no state between calls (apart from
+ *    the optional per-thread timing trace below, and the side stream of
+ *    moe_backward_bf16), never synchronises the host and enqueues all work on
+ *    `stream` (NULL = the null stream), or orders it with `stream` as if it
+ *    were enqueued there.  Outputs are valid once the caller has synchronised
+ *    the stream.
  *  - Matrices are row-major and contiguous.  Per-expert weights are stacked
  *    [E, out, in] (nn.Linear layout): w_gate, w_up [E, I, H]; w_down [E, H, I].
  *    Shared-expert weights: s_gate, s_up [I_shared, H]; s_down [H, I_shared].
@@ -137,12 +140,14 @@ const char* moe_status_str(moe_status s);
 
 /* Per-kernel timing.  While a trace is set on a host thread, every kernel that a
  * call from that thread enqueues is bracketed by events[2 i] (before) and
- * events[2 i + 1] (after), recorded on the call's stream, and names[i] is set to
+ * events[2 i + 1] (after), recorded on the stream the kernel runs on (the call's
+ * stream or the side stream of moe_backward_bf16), and names[i] is set to
  * the kernel's name (a static string); i runs from the trace's `count`, which the
  * library increments, up to `capacity` (later kernels are not recorded).  The
  * caller creates the 2 * capacity events and reads them with hipEventElapsedTime
- * after synchronising.  moe_trace_set(NULL) stops tracing.  This is the only
- * state the library keeps, and it is per host thread. */
+ * after synchronising.  moe_trace_set(NULL) stops tracing.  Apart from the side
+ * stream of moe_backward_bf16, this is the only state the library keeps; both are
+ * per host thread. */
 typedef struct moe_trace {
   hipEvent_t* events;
   const char** names;
@@ -307,7 +312,14 @@ moe_status moe_forward_bf16_noalloc(const moe_shape* shape, const void* plan, co
  * Outputs are overwritten: dx [T, H]; dw_* like the weights (experts with no
  * rows get zeros); ds_* like the shared weights (NULL without a shared expert);
  * d_topk_w fp32 [T, k] (0 for pairs left out of the plan).
- * ws [ws_bytes >= moe_workspace_bytes(.., 1)]. */
+ * ws [ws_bytes >= moe_workspace_bytes(.., 1)].
+ * The dispatch replay of x and the up-projection weight gradients run on a second
+ * stream of default priority that the library makes, once per host thread and
+ * device, on the first call; it waits for the work enqueued on `stream` before the
+ * call, and `stream` waits for it before the call's last kernel, also when a launch
+ * fails. Where that stream cannot be made, and while a kernel trace is set on the
+ * calling thread (so that each kernel's events time it alone), all the work goes
+ * onto `stream`. */
 moe_status moe_backward_bf16(const moe_shape* shape, const void* plan, const void* x,
                              const float* topk_w, const void* w_gate, const void* w_up,
                              const void* w_down, const void* s_gate, const void* s_up,

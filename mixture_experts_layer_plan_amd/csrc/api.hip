@@ -1,6 +1,8 @@
 // C-ABI of the MoE layer (include/moe.h): argument checks, buffer layouts and the
-// enqueue sequences of the forward and backward passes.  Nothing here allocates,
-// synchronises or keeps state; every kernel goes onto the caller's stream.
+// enqueue sequences of the forward and backward passes.  Nothing here allocates device
+// memory or synchronises with the host.  Every kernel goes onto the caller's stream,
+// except in the bf16 backward, which forks independent GEMMs onto a second stream of
+// its own and joins it back before returning (see SideStream).
 #include <stdint.h>
 #include <string.h>
 
@@ -44,6 +46,49 @@ void trace_after(hipStream_t s) {
 }  // namespace moe
 
 namespace {
+
+// A second stream (default priority) per host thread and device, for the part of one
+// call's work that does not depend on the rest. fork() makes it wait for all that the
+// caller's stream holds so far; join() makes the caller's stream wait for all that it
+// holds. Everything a call enqueues thus stays ordered with the caller's stream
+// before and after it, as if it had all gone onto that stream. side_stream() returns
+// null where the stream or its events cannot be made; the caller then enqueues all
+// its work on its own stream. Made on first use, kept until the process ends.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork_ev = nullptr, join_ev = nullptr;
+  hipError_t fork(hipStream_t from) {
+    hipError_t e = hipEventRecord(fork_ev, from);
+    return e != hipSuccess ? e : hipStreamWaitEvent(s, fork_ev, 0);
+  }
+  hipError_t join(hipStream_t to) {
+    hipError_t e = hipEventRecord(join_ev, s);
+    return e != hipSuccess ? e : hipStreamWaitEvent(to, join_ev, 0);
+  }
+};
+
+SideStream* side_stream() {
+  constexpr int MAX_DEV = 64;
+  thread_local SideStream tab[MAX_DEV];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEV) return nullptr;
+  SideStream& x = tab[dev];
+  if (x.s) return &x;
+  hipStream_t s = nullptr;
+  hipEvent_t a = nullptr, b = nullptr;
+  if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) == hipSuccess &&
+      hipEventCreateWithFlags(&a, hipEventDisableTiming) == hipSuccess &&
+      hipEventCreateWithFlags(&b, hipEventDisableTiming) == hipSuccess) {
+    x.fork_ev = a;
+    x.join_ev = b;
+    x.s = s;
+    return &x;
+  }
+  if (b) (void)hipEventDestroy(b);
+  if (a) (void)hipEventDestroy(a);
+  if (s) (void)hipStreamDestroy(s);
+  return nullptr;
+}
 
 constexpr size_t ALIGN = 256;
 
@@ -380,29 +425,57 @@ moe_status backward_impl(moe_dtype dt, const moe_shape* s, const void* plan, con
   void* X = at<char>(ws, W.X);
   void* dYu = at<char>(ws, W.dYu);
   const int es = d ? 2 : 4;
-  // reverse-combine: pull dy rows into expert order; replay the dispatch of x
-  MOE_TRY(launch_scatter_rows(dy, dYu, v.pos, s->T, s->k, H * es, st));
-  MOE_TRY(launch_scatter_rows(x, X, v.pos, s->T, s->k, H * es, st));
-  // dgrad-down + SwiGLU backward + router-weight-gradient partials
-  MOE_TRY(launch_gemm_dgrad_down(d, g, dYu, wd, Z, topk_w, H, I, s->k, dZ, gh, dgp, st));
-  MOE_TRY(launch_dg_reduce(dgp, v.pos, R, I / 128, d_topk_w, st));
-  // the wgrads also write the zero gradients of experts without rows
-  MOE_TRY(launch_gemm_wgrad_down(d, g, dYu, gh, H, I, dwd, st));
-  MOE_TRY(launch_gemm_dgrad_up(d, g, dZ, wg, wu, H, I, dX, st));
-  MOE_TRY(launch_gemm_wgrad_up(d, g, dZ, X, H, I, dwg, dwu, st));
-  void* dxs = nullptr;
-  if (s->I_shared) {
+  // In the bf16 pass the dispatch replay of x and the up-projection wgrads, which only
+  // wgrad-up reads or writes, run on a side stream beside the rest: the GEMMs after
+  // dgrad-down are independent of one another, and each alone leaves the chip's
+  // memory system partly idle. Both streams are joined before the combine.
+  // (not while a kernel trace is set: each kernel's events then time it alone)
+  SideStream* side = d && !tls_trace ? side_stream() : nullptr;
+  const hipStream_t sx = side ? side->s : st;
+  void* dxs = s->I_shared ? at<char>(ws, W.dxs) : nullptr;
+#define HIP_TRY(expr)                    \
+  do {                                   \
+    const hipError_t e_ = (expr);        \
+    if (e_ != hipSuccess) return e_;     \
+  } while (0)
+  // the shared expert's backward: it reads only dy, x and its saved activations
+  const auto shared_expert = [&](hipStream_t ss) -> hipError_t {
+    if (!s->I_shared) return hipSuccess;
     const int Is = s->I_shared;
     const GroupInfo gs = dense(s->T);
     const void* Zs = at<char>(saved, S.Zs);
     void* dZs = at<char>(ws, W.dZs);
     void* hs = at<char>(ws, W.hs);
-    dxs = at<char>(ws, W.dxs);
-    MOE_TRY(launch_gemm_dgrad_down(d, gs, dy, sd, Zs, nullptr, H, Is, 1, dZs, hs, nullptr, st));
-    MOE_TRY(launch_gemm_wgrad_down(d, gs, dy, hs, H, Is, dsd, st));
-    MOE_TRY(launch_gemm_dgrad_up(d, gs, dZs, sg, su, H, Is, dxs, st));
-    MOE_TRY(launch_gemm_wgrad_up(d, gs, dZs, x, H, Is, dsg, dsu, st));
+    HIP_TRY(launch_gemm_dgrad_down(d, gs, dy, sd, Zs, nullptr, H, Is, 1, dZs, hs, nullptr, ss));
+    HIP_TRY(launch_gemm_wgrad_down(d, gs, dy, hs, H, Is, dsd, ss));
+    HIP_TRY(launch_gemm_dgrad_up(d, gs, dZs, sg, su, H, Is, dxs, ss));
+    HIP_TRY(launch_gemm_wgrad_up(d, gs, dZs, x, H, Is, dsg, dsu, ss));
+    return hipSuccess;
+  };
+  // the side stream is joined on every return path, failed launches included
+  const auto enqueue = [&]() -> hipError_t {
+    // reverse-combine: pull dy rows into expert order; replay the dispatch of x
+    HIP_TRY(launch_scatter_rows(dy, dYu, v.pos, s->T, s->k, H * es, st));
+    HIP_TRY(launch_scatter_rows(x, X, v.pos, s->T, s->k, H * es, sx));
+    // dgrad-down + SwiGLU backward + router-weight-gradient partials
+    HIP_TRY(launch_gemm_dgrad_down(d, g, dYu, wd, Z, topk_w, H, I, s->k, dZ, gh, dgp, st));
+    HIP_TRY(launch_dg_reduce(dgp, v.pos, R, I / 128, d_topk_w, st));
+    if (side) HIP_TRY(side->fork(st));  // dZ is written
+    // the wgrads also write the zero gradients of experts without rows
+    HIP_TRY(launch_gemm_wgrad_up(d, g, dZ, X, H, I, dwg, dwu, sx));
+    HIP_TRY(launch_gemm_wgrad_down(d, g, dYu, gh, H, I, dwd, st));
+    HIP_TRY(launch_gemm_dgrad_up(d, g, dZ, wg, wu, H, I, dX, st));
+    HIP_TRY(shared_expert(st));
+#undef HIP_TRY
+    return hipSuccess;
+  };
+  if (side) MOE_TRY(side->fork(st));
+  hipError_t e = enqueue();
+  if (side) {
+    const hipError_t j = side->join(st);
+    if (e == hipSuccess) e = j;
   }
+  MOE_TRY(e);
   if (d)
     MOE_TRY(launch_combine_bf16(dX, v.pos, nullptr, dxs, dx, s->T, s->k, H, st));
   else

@@ -152,6 +152,36 @@ def test_layer_bitwise_independent_of_persistent_grid(name):
     assert len(set(outs)) == 1, outs
 
 
+@pytest.mark.parametrize("name", ["hot_wgrad_bf16", "skew_shared_bf16"])
+def test_backward_side_stream_bitwise_equal_serial(name):
+    """The bf16 backward runs the dispatch replay of x and the up-projection weight
+    gradients on a second stream that it joins back into the caller's stream; while a
+    kernel trace is set it enqueues everything on the caller's stream. Both give
+    bitwise the same outputs, read right after the call on the caller's stream, which
+    the join has to order after the second stream's kernels."""
+    from mixture_experts_layer_plan_amd import binding
+    shape = SMALL[name]
+    say(f"backward on two streams vs one: {name}")
+    inp = to_dev(make_inputs(shape, seed=4, device="cpu", with_dy=True))
+    outs = []
+    b = gpu_run(shape, inp)
+    outs.append(digest(b.dx, b.dw_gate, b.dw_up, b.dw_down, b.ds_gate, b.ds_up, b.ds_down,
+                       b.d_topk_w, b.d_logits))
+    del b
+    tr = binding.KernelTrace(capacity=256)
+    try:
+        with tr:
+            b = gpu_run(shape, inp)
+            outs.append(digest(b.dx, b.dw_gate, b.dw_up, b.dw_down, b.ds_gate, b.ds_up,
+                               b.ds_down, b.d_topk_w, b.d_logits))
+            del b
+        names = [n for n, _ in tr.records()]
+    finally:
+        tr.close()
+    assert any(n.startswith("gemm_wgrad_up") for n in names), names
+    assert outs[0] == outs[1]
+
+
 @pytest.mark.parametrize("name", ["skew_shared_bf16", "one_token_bf16", "hot_expert_bf16"])
 def test_fused_forward_small_all_outputs(name):
     """MOE_FUSED_FORWARD (routed and shared expert GEMMs and the combine in one
