@@ -19,7 +19,8 @@
  *  - Every array pointer is a DEVICE pointer owned by the caller.  The library
  *    allocates no device memory, keeps no state between calls (apart from
  *    the optional per-thread timing trace below, and the side stream of
- *    moe_backward_bf16), never synchronises the host and enqueues all work on
+ *    moe_backward_bf16 and moe_backward_mxfp8), never synchronises the host and
+ *    enqueues all work on
  *    `stream` (NULL = the null stream), or orders it with `stream` as if it
  *    were enqueued there.  Outputs are valid once the caller has synchronised
  *    the stream.
@@ -141,12 +142,12 @@ const char* moe_status_str(moe_status s);
 /* Per-kernel timing.  While a trace is set on a host thread, every kernel that a
  * call from that thread enqueues is bracketed by events[2 i] (before) and
  * events[2 i + 1] (after), recorded on the stream the kernel runs on (the call's
- * stream or the side stream of moe_backward_bf16), and names[i] is set to
+ * stream or the side stream of the backwards), and names[i] is set to
  * the kernel's name (a static string); i runs from the trace's `count`, which the
  * library increments, up to `capacity` (later kernels are not recorded).  The
  * caller creates the 2 * capacity events and reads them with hipEventElapsedTime
  * after synchronising.  moe_trace_set(NULL) stops tracing.  Apart from the side
- * stream of moe_backward_bf16, this is the only state the library keeps; both are
+ * stream of the backwards, this is the only state the library keeps; both are
  * per host thread. */
 typedef struct moe_trace {
   hipEvent_t* events;
@@ -392,7 +393,9 @@ moe_status moe_forward_mxfp8(const moe_shape* shape, const void* plan, const voi
                              size_t ws_bytes, hipStream_t stream);
 
 /* As moe_backward_bf16 with the expert weights replaced by `wq`; weight gradients
- * are bf16 and overwritten. ws: moe_workspace_bytes(shape, MOE_MXFP8, 1). */
+ * are bf16 and overwritten. ws: moe_workspace_bytes(shape, MOE_MXFP8, 1).  The
+ * up-projection weight gradients run on the side stream described at
+ * moe_backward_bf16, beside the down-projection ones, under the same rules. */
 moe_status moe_backward_mxfp8(const moe_shape* shape, const void* plan, const void* x,
                               const float* topk_w, const void* wq, const void* s_gate,
                               const void* s_up, const void* s_down, const void* saved,

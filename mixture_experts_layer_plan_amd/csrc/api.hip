@@ -1,8 +1,8 @@
 // C-ABI of the MoE layer (include/moe.h): argument checks, buffer layouts and the
 // enqueue sequences of the forward and backward passes.  Nothing here allocates device
 // memory or synchronises with the host.  Every kernel goes onto the caller's stream,
-// except in the bf16 backward, which forks independent GEMMs onto a second stream of
-// its own and joins it back before returning (see SideStream).
+// except in the bf16 and MXFP8 backwards, which fork independent GEMMs onto a second
+// stream of their own and join it back before returning (see SideStream).
 #include <stdint.h>
 #include <string.h>
 
@@ -834,24 +834,43 @@ moe_status backward_mx_impl(const moe_shape* s, const void* plan, const void* x,
                               at<uint8_t>(ws, W.dZT8), at<uint8_t>(ws, W.dZTs), st));
   // Experts with a long packed token range run on the 256-tile kernel; the 128-tile
   // kernel takes the others and stores the zero gradients of experts without rows.
-  int hot = MX_WGRAD_HOT_BYTES;
-  hipError_t e1 = launch_mx_wgrad_hot("mx_gemm_wgrad_down_hot", mp, s->E, at<uint8_t>(ws, W.dYuT8),
-                                      at<uint8_t>(ws, W.dYuTs), at<uint8_t>(ws, W.ghT8),
-                                      at<uint8_t>(ws, W.ghTs), H, I, H, W.Kp, dwd, nullptr, hot, st);
-  if (e1 == hipErrorNotSupported) hot = 0;
-  else if (e1 != hipSuccess) return hip_status(e1);
-  MOE_TRY(launch_mx_wgrad("mx_gemm_wgrad_down", mp, s->E, at<uint8_t>(ws, W.dYuT8),
-                          at<uint8_t>(ws, W.dYuTs), at<uint8_t>(ws, W.ghT8),
-                          at<uint8_t>(ws, W.ghTs), H, I, H, W.Kp, dwd, nullptr, hot, st));
-  hot = MX_WGRAD_HOT_BYTES;
-  e1 = launch_mx_wgrad_hot("mx_gemm_wgrad_up_hot", mp, s->E, at<uint8_t>(ws, W.dZT8),
+  // The two projections' weight gradients are independent: the up-projection pair runs
+  // on the side stream beside the down-projection pair (not while a kernel trace is
+  // set, so that each kernel's events time it alone); joined on every return path.
+  SideStream* side = tls_trace ? nullptr : side_stream();
+  const hipStream_t sx = side ? side->s : st;
+  const auto down = [&]() -> hipError_t {
+    int hot = MX_WGRAD_HOT_BYTES;
+    hipError_t e = launch_mx_wgrad_hot("mx_gemm_wgrad_down_hot", mp, s->E,
+                                       at<uint8_t>(ws, W.dYuT8), at<uint8_t>(ws, W.dYuTs),
+                                       at<uint8_t>(ws, W.ghT8), at<uint8_t>(ws, W.ghTs), H, I, H,
+                                       W.Kp, dwd, nullptr, hot, st);
+    if (e == hipErrorNotSupported) hot = 0;
+    else if (e != hipSuccess) return e;
+    return launch_mx_wgrad("mx_gemm_wgrad_down", mp, s->E, at<uint8_t>(ws, W.dYuT8),
+                           at<uint8_t>(ws, W.dYuTs), at<uint8_t>(ws, W.ghT8),
+                           at<uint8_t>(ws, W.ghTs), H, I, H, W.Kp, dwd, nullptr, hot, st);
+  };
+  const auto up = [&]() -> hipError_t {
+    int hot = MX_WGRAD_HOT_BYTES;
+    hipError_t e = launch_mx_wgrad_hot("mx_gemm_wgrad_up_hot", mp, s->E, at<uint8_t>(ws, W.dZT8),
+                                       at<uint8_t>(ws, W.dZTs), at<uint8_t>(ws, W.XT8),
+                                       at<uint8_t>(ws, W.XTs), 2 * I, H, I, W.Kp, dwg, dwu, hot,
+                                       sx);
+    if (e == hipErrorNotSupported) hot = 0;
+    else if (e != hipSuccess) return e;
+    return launch_mx_wgrad("mx_gemm_wgrad_up", mp, s->E, at<uint8_t>(ws, W.dZT8),
                            at<uint8_t>(ws, W.dZTs), at<uint8_t>(ws, W.XT8), at<uint8_t>(ws, W.XTs),
-                           2 * I, H, I, W.Kp, dwg, dwu, hot, st);
-  if (e1 == hipErrorNotSupported) hot = 0;
-  else if (e1 != hipSuccess) return hip_status(e1);
-  MOE_TRY(launch_mx_wgrad("mx_gemm_wgrad_up", mp, s->E, at<uint8_t>(ws, W.dZT8),
-                          at<uint8_t>(ws, W.dZTs), at<uint8_t>(ws, W.XT8), at<uint8_t>(ws, W.XTs),
-                          2 * I, H, I, W.Kp, dwg, dwu, hot, st));
+                           2 * I, H, I, W.Kp, dwg, dwu, hot, sx);
+  };
+  if (side) MOE_TRY(side->fork(st));
+  hipError_t e = up();
+  if (e == hipSuccess) e = down();
+  if (side) {
+    const hipError_t j = side->join(st);
+    if (e == hipSuccess) e = j;
+  }
+  MOE_TRY(e);
   return MOE_OK;
 }
 
