@@ -320,7 +320,9 @@ moe_status moe_forward_bf16_noalloc(const moe_shape* shape, const void* plan, co
  * call, and `stream` waits for it before the call's last kernel, also when a launch
  * fails. Where that stream cannot be made, and while a kernel trace is set on the
  * calling thread (so that each kernel's events time it alone), all the work goes
- * onto `stream`. */
+ * onto `stream`. A caller that captures the backward into a HIP graph makes one
+ * uncaptured call on that thread and device first, so that the stream and its
+ * events exist before the capture. */
 moe_status moe_backward_bf16(const moe_shape* shape, const void* plan, const void* x,
                              const float* topk_w, const void* w_gate, const void* w_up,
                              const void* w_down, const void* s_gate, const void* s_up,
