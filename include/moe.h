@@ -19,8 +19,8 @@
  *  - Every array pointer is a DEVICE pointer owned by the caller.  The library
  *    allocates no device memory, keeps no state between calls (apart from
  *    the optional per-thread timing trace below, and the side stream of
- *    moe_backward_bf16 and moe_backward_mxfp8), never synchronises the host and
- *    enqueues all work on
+ *    moe_forward_bf16, moe_backward_bf16 and moe_backward_mxfp8), never
+ *    synchronises the host and enqueues all work on
  *    `stream` (NULL = the null stream), or orders it with `stream` as if it
  *    were enqueued there.  Outputs are valid once the caller has synchronised
  *    the stream.
@@ -277,7 +277,9 @@ moe_status moe_reverse_dispatch_bf16(const moe_shape* shape, const void* plan, c
  *   x [T, H], topk_w fp32 [T, k], weights as in the conventions
  *   s_gate, s_up, s_down: NULL when shape->I_shared == 0
  *   y [T, H] out; saved [moe_saved_bytes] out; ws [ws_bytes >= moe_workspace_bytes(.., 0)].
- * T_minibatch must be 0 or T in this variant. */
+ * T_minibatch must be 0 or T in this variant.  The shared expert's two GEMMs run on
+ * the side stream described at moe_backward_bf16, under the same rules (not in
+ * moe_forward_bf16_noalloc, nor with MOE_FUSED_FORWARD). */
 moe_status moe_forward_bf16(const moe_shape* shape, const void* plan, const void* x,
                             const float* topk_w, const void* w_gate, const void* w_up,
                             const void* w_down, const void* s_gate, const void* s_up,

@@ -1,8 +1,9 @@
 // C-ABI of the MoE layer (include/moe.h): argument checks, buffer layouts and the
 // enqueue sequences of the forward and backward passes.  Nothing here allocates device
 // memory or synchronises with the host.  Every kernel goes onto the caller's stream,
-// except in the bf16 and MXFP8 backwards, which fork independent GEMMs onto a second
-// stream of their own and join it back before returning (see SideStream).
+// except in moe_forward_bf16 and the bf16 and MXFP8 backwards, which fork independent
+// GEMMs onto a second stream of their own and join it back before returning (see
+// SideStream).
 #include <stdint.h>
 #include <string.h>
 
@@ -324,7 +325,8 @@ bool any_null_rows(const moe_shape* s, std::initializer_list<const void*> ps) {
 moe_status forward_impl(moe_dtype dt, const moe_shape* s, const void* plan, const void* x,
                         const float* topk_w, const void* wg, const void* wu, const void* wd,
                         const void* sg, const void* su, const void* sd, void* y, void* saved,
-                        void* ws, size_t ws_bytes, hipStream_t st) {
+                        void* ws, size_t ws_bytes, hipStream_t st,
+                        bool may_fork = false) {
   moe_status rc = check_shape(s, true);
   if (rc != MOE_OK) return rc;
   if (n_minibatches(s) != 1) return MOE_E_UNSUPPORTED;
@@ -376,15 +378,36 @@ moe_status forward_impl(moe_dtype dt, const moe_shape* s, const void* plan, cons
     if (fe == hipSuccess) return MOE_OK;
     if (fe != hipErrorNotSupported) return MOE_E_HIP;
   }
-  MOE_TRY(launch_gemm_up_swiglu(d, g, x, wg, wu, s->H, s->I, Z, h, st));
-  MOE_TRY(launch_gemm_down(d, g, h, wd, s->H, s->I, Y, st));
-  if (s->I_shared) {
-    const GroupInfo gs = dense(s->T);
-    void* Zs = at<char>(saved, S.Zs);
-    void* hs = at<char>(ws, W.hs);
-    MOE_TRY(launch_gemm_up_swiglu(d, gs, x, sg, su, s->H, s->I_shared, Zs, hs, st));
-    MOE_TRY(launch_gemm_down(d, gs, hs, sd, s->H, s->I_shared, ys, st));
+  // In the bf16 pass of moe_forward_bf16 the shared expert's two GEMMs, which read only
+  // x, run on the side stream beside the routed ones (not while a kernel trace is set,
+  // so that each kernel's events time it alone); joined on every return path.
+  SideStream* side = d && may_fork && s->I_shared && !tls_trace ? side_stream() : nullptr;
+  const hipStream_t sx = side ? side->s : st;
+#define HIP_TRY(expr)                    \
+  do {                                   \
+    const hipError_t e_ = (expr);        \
+    if (e_ != hipSuccess) return e_;     \
+  } while (0)
+  const auto enqueue = [&]() -> hipError_t {
+    if (s->I_shared) {
+      const GroupInfo gs = dense(s->T);
+      void* Zs = at<char>(saved, S.Zs);
+      void* hs = at<char>(ws, W.hs);
+      HIP_TRY(launch_gemm_up_swiglu(d, gs, x, sg, su, s->H, s->I_shared, Zs, hs, sx));
+      HIP_TRY(launch_gemm_down(d, gs, hs, sd, s->H, s->I_shared, ys, sx));
+    }
+    HIP_TRY(launch_gemm_up_swiglu(d, g, x, wg, wu, s->H, s->I, Z, h, st));
+    HIP_TRY(launch_gemm_down(d, g, h, wd, s->H, s->I, Y, st));
+    return hipSuccess;
+  };
+#undef HIP_TRY
+  if (side) MOE_TRY(side->fork(st));
+  hipError_t e = enqueue();
+  if (side) {
+    const hipError_t j = side->join(st);
+    if (e == hipSuccess) e = j;
   }
+  MOE_TRY(e);
   if (d)
     MOE_TRY(launch_combine_bf16(Y, v.pos, topk_w, ys, y, s->T, s->k, s->H, st));
   else
@@ -1130,7 +1153,7 @@ moe_status moe_forward_bf16(const moe_shape* s, const void* plan, const void* x,
                             const void* s_down, void* y, void* saved, void* ws, size_t ws_bytes,
                             hipStream_t st) {
   return forward_impl(MOE_BF16, s, plan, x, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down, y,
-                      saved, ws, ws_bytes, st);
+                      saved, ws, ws_bytes, st, true);
 }
 
 moe_status moe_forward_bf16_noalloc(const moe_shape* s, const void* plan, const void* x,

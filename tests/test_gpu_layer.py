@@ -153,27 +153,28 @@ def test_layer_bitwise_independent_of_persistent_grid(name):
 
 
 @pytest.mark.parametrize("name", ["hot_wgrad_bf16", "skew_shared_bf16"])
-def test_backward_side_stream_bitwise_equal_serial(name):
-    """The bf16 backward runs the dispatch replay of x and the up-projection weight
-    gradients on a second stream that it joins back into the caller's stream; while a
-    kernel trace is set it enqueues everything on the caller's stream. Both give
-    bitwise the same outputs, read right after the call on the caller's stream, which
-    the join has to order after the second stream's kernels."""
+def test_side_stream_bitwise_equal_serial(name):
+    """The bf16 forward runs the shared expert's GEMMs, and the backward the dispatch
+    replay of x and the up-projection weight gradients, on a second stream that each
+    joins back into the caller's stream; while a kernel trace is set they enqueue
+    everything on the caller's stream. Both give bitwise the same outputs, read right
+    after the calls on the caller's stream, which the join has to order after the
+    second stream's kernels."""
     from mixture_experts_layer_plan_amd import binding
     shape = SMALL[name]
-    say(f"backward on two streams vs one: {name}")
+    say(f"forward and backward on two streams vs one: {name}")
     inp = to_dev(make_inputs(shape, seed=4, device="cpu", with_dy=True))
     outs = []
     b = gpu_run(shape, inp)
-    outs.append(digest(b.dx, b.dw_gate, b.dw_up, b.dw_down, b.ds_gate, b.ds_up, b.ds_down,
-                       b.d_topk_w, b.d_logits))
+    outs.append(digest(b.y, b.dx, b.dw_gate, b.dw_up, b.dw_down, b.ds_gate, b.ds_up,
+                       b.ds_down, b.d_topk_w, b.d_logits))
     del b
     tr = binding.KernelTrace(capacity=256)
     try:
         with tr:
             b = gpu_run(shape, inp)
-            outs.append(digest(b.dx, b.dw_gate, b.dw_up, b.dw_down, b.ds_gate, b.ds_up,
-                               b.ds_down, b.d_topk_w, b.d_logits))
+            outs.append(digest(b.y, b.dx, b.dw_gate, b.dw_up, b.dw_down, b.ds_gate,
+                               b.ds_up, b.ds_down, b.d_topk_w, b.d_logits))
             del b
         names = [n for n, _ in tr.records()]
     finally:
